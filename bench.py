@@ -1,0 +1,208 @@
+#!/usr/bin/env python3
+"""Benchmark of the weight-quantized decode linear on one MI355X.
+
+One step is the decode linear at the headline shape M=1, K=3584, N=18944 (the
+gate/up projection of a Qwen-7B-class layer) in both variants: one W4A8 GEMV (with
+its fused activation quantization) and one W8A16 GEMV.  Weight packing is load-time
+work and stays outside the timed region.  The packed weights are replicated into
+enough distinct copies (rotated step by step) that every step reads them from HBM,
+not from the 256 MB last-level cache.
+
+Printed: ONE JSON line with `value` = algorithmic bytes of both GEMVs / time per
+step (GB/s), per-kernel microseconds and GB/s, the roofline of the dominant kernel
+(per-launch algorithmic bytes / average launch time from HIP events), and the CPU
+oracle timed on this host on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "W4A8/W8A16 GEMV µs and HBM GB/s (% of peak), M=1 K=3584 N=18944"
+PEAK_HBM_GBS = 8000.0
+ROTATE_BYTES = 1.5e9  # > 256 MB last-level cache, several times over
+
+
+def bytes_w4a8(M, N, K):
+    """Algorithmic bytes: 0.5 B per INT4 weight, 4 B per scale, X element and Y element."""
+    return N * K // 2 + 4 * N + 4 * M * K + 4 * M * N
+
+
+def bytes_w8a16(M, N, K):
+    """Algorithmic bytes: 1 B per INT8 weight, 2 B per f16 scale, X element and Y element."""
+    return N * K + 2 * N + 2 * M * K + 2 * M * N
+
+
+def kernel_source_hash(kernel: str) -> str:
+    csrc = os.path.join(ROOT, "bit_weight_quantized_load_amd", "csrc")
+    files = ["common.hpp", "kernels.hpp", "api.hip",
+             "gemv_w4a8.hip" if kernel == "gemv_w4a8" else "gemv_w8a16.hip"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, if it was taken on the
+    current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        t = json.load(fh)
+    if t.get("kernel_source_sha") != kernel_source_hash(kernel):
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def host_threads() -> int:
+    n = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS")
+    if env and env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, n)
+
+
+def cpu_baseline(W, X, X16, seconds, b_step):
+    """The oracle, as it stands, on this host: W4A8 (activation quantization, integer
+    GEMV, epilogue) plus the fp64 W8A16 reference, repeated for about `seconds`.
+    Weight quantization is load-time work on both sides and is not timed."""
+    import oracle
+
+    q4, s4 = oracle.quant_w4(W)
+    q8, s8 = oracle.quant_w8(W)
+    nt = host_threads()
+    reps = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.gemv_w4a8(X, q4, s4, nthreads=nt)
+        oracle.gemv_w8a16_ref64(X16, q8, s8, nthreads=nt)
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= seconds:
+            break
+    return {"value": round(reps * b_step / dt / 1e9, 4), "unit": "GB/s", "cores": nt,
+            "kind": "oracle",
+            "sample": "%d repetitions of the full step (W4A8 + fp64 W8A16 reference, M=1 K=3584 "
+                      "N=18944) in %.1f s on %d OpenMP threads" % (reps, dt, nt)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only (the GEMV needs no communication; "
+              "sharding across GPUs is a design note, not built); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from __graft_entry__ import _ensure_built
+
+    _ensure_built()
+    import bit_weight_quantized_load_amd as qw
+    import workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    c = wl.HEADLINE
+    M, K, N = c["M"], c["K"], c["N"]
+    b4, b8 = bytes_w4a8(M, N, K), bytes_w8a16(M, N, K)
+    b_step = b4 + b8
+
+    # synthetic inputs of the Qwen-7B gate/up projection: 1% outlier rows, 4 outlier channels
+    W = wl.weights(1, wl.tensor_id("gate_proj", 0), N, K, outlier_rows=True)
+    X = wl.activations(1, wl.tensor_id("gate_proj", 1), M, K, outlier_channels=4)
+    X16 = X.astype(np.float16)
+    Wd = torch.from_numpy(W).cuda()
+    Wq4, s4 = qw.quantize_pack_w4(Wd)
+    Wq8, s8 = qw.quantize_pack_w8(Wd)
+    del Wd
+    R = max(2, math.ceil(ROTATE_BYTES / (Wq4.numel() + Wq8.numel())))
+    copies = [(Wq4, s4, Wq8, s8)] + [(Wq4.clone(), s4.clone(), Wq8.clone(), s8.clone())
+                                     for _ in range(R - 1)]
+    Xd = torch.from_numpy(X).cuda()
+    X16d = torch.from_numpy(X16).cuda()
+    Y4 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    Y8 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ws4 = qw.make_workspace("w4a8", M, N, K)
+    ws8 = qw.make_workspace("w8a16", M, N, K)
+
+    def step(i, ev=None):
+        w4, sc4, w8, sc8 = copies[i % R]
+        if ev is not None:
+            ev[0].record()
+        qw.gemv_w4a8(Xd, w4, sc4, workspace=ws4, out=Y4)
+        if ev is not None:
+            ev[1].record()
+        qw.gemv_w8a16(X16d, w8, sc8, workspace=ws8, out=Y8)
+        if ev is not None:
+            ev[2].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K_steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t4 = sum(e[0].elapsed_time(e[1]) for e in evs) / K_steps * 1e3  # us per launch
+    t8 = sum(e[1].elapsed_time(e[2]) for e in evs) / K_steps * 1e3
+    ms_per_step = wall * 1e3 / K_steps
+    value = b_step / (ms_per_step * 1e-3) / 1e9
+
+    kernels = {
+        "gemv_w4a8": {"us": round(t4, 3), "algo_bytes": b4, "GB/s": round(b4 / t4 / 1e3, 1),
+                      "frac_of_peak": round(b4 / t4 / 1e3 / PEAK_HBM_GBS, 4)},
+        "gemv_w8a16": {"us": round(t8, 3), "algo_bytes": b8, "GB/s": round(b8 / t8 / 1e3, 1),
+                       "frac_of_peak": round(b8 / t8 / 1e3 / PEAK_HBM_GBS, 4)},
+    }
+    dom = "gemv_w8a16" if t8 >= t4 else "gemv_w4a8"
+    ach = kernels[dom]["GB/s"]
+    traffic = load_traffic(dom, c["workload"])
+    roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(W, X, X16, args.cpu_seconds, b_step)
+
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": K_steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "i8xi8->i32 (W4A8), f16xf16->f32 (W8A16)", "data": "synthetic",
+        "config": {"workload": c["workload"], "M": M, "K": K, "N": N,
+                   "step": "gemv_w4a8 + gemv_w8a16", "weight_copies_rotated": R},
+        "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

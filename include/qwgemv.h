@@ -1,0 +1,152 @@
+/*
+ * qwgemv.h -- C ABI of the weight-quantized decode linear for AMD MI355X (gfx950).
+ *
+ * Two linears of single-batch LLM decode, each behind plain pointers and sizes:
+ *
+ *  W4A8  Row-wise symmetric INT4 weights with one fp32 scale per output row,
+ *        activations quantized dynamically to INT8 per row of X, int8 x int8 dot
+ *        products accumulated in int32, output = acc * w_scale[n] * a_scale[m].
+ *        Source: "Jetson Orin AGX 上的 INT4 量化推理实践：从 9 tok/s 到 19.6 tok/s",
+ *        sections 当前实现方式 (the three formulas) and 正确方向 (int8 dot into int32).
+ *
+ *  W8A16 Per-output-channel INT8 weights with an f16 scale, dequantized in registers
+ *        against f16 activations, fp32 accumulation, f16 output.
+ *        Source: ChatGLM2-6B W8A16 deployment on BM1684X (TPU-MLIR write-up),
+ *        sections 2 (per-channel INT8 storage, F16 compute), 3 (f16 scale vector) and
+ *        4 (load INT8, cast, multiply by the scale, multiply with the activation).
+ *
+ * Conventions for every function below:
+ *  - Pointers are DEVICE pointers (memory of the current HIP device) unless a comment
+ *    says otherwise.  The caller allocates and owns every buffer; the library never
+ *    keeps a pointer past the call.
+ *  - Matrices are row-major and contiguous: W and the packed weights are [N][K]
+ *    (output rows n, input columns k), X is [M][K], Y is [M][N].
+ *  - Every pointer must be 16-byte aligned.  K must be a positive multiple of 32 and
+ *    at most 131072; M and N must be positive (M at most 65535).
+ *  - fp16 values travel as their IEEE binary16 bit patterns in uint16_t.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Work is
+ *    enqueued asynchronously on it and the call returns without synchronising,
+ *    except for the two load-time packers (see below).
+ *  - Arguments are validated on the host before any HIP call.  The return value is
+ *    QW_OK or one of the error codes; nothing is enqueued when validation fails.
+ *    Nothing throws across this interface.
+ *  - Inputs must be finite.  The packers check and report QW_ERR_NONFINITE; for X
+ *    the result of a non-finite activation is unspecified.
+ */
+#ifndef QWGEMV_H
+#define QWGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    QW_OK = 0,
+    QW_ERR_NULL = 1,       /* a required pointer is NULL                        */
+    QW_ERR_SHAPE = 2,      /* M, N or K out of range, or K % 32 != 0            */
+    QW_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                  */
+    QW_ERR_WORKSPACE = 4,  /* ws_bytes below qw_workspace_bytes()               */
+    QW_ERR_NONFINITE = 5,  /* a packer met a non-finite weight or f16 overflow  */
+    QW_ERR_HIP = 6,        /* a HIP runtime call or launch failed               */
+    QW_ERR_TILING = 7      /* tiling arguments of a *_tiled call are invalid    */
+};
+
+/* Bytes of the packed weights: N*K/2 for INT4, N*K for INT8.  The packed buffer is
+   [N][K/2] bytes for INT4 (byte j of a row holds k=2j in its low nibble and k=2j+1
+   in its high nibble, 4-bit two's complement) and [N][K] int8 for INT8.  This
+   layout keeps each row contiguous, so the kernels read it with 128-bit loads that
+   cover 256 contiguous bytes per 16 lanes. */
+size_t qw_w4_packed_bytes(int64_t N, int64_t K);
+size_t qw_w8_packed_bytes(int64_t N, int64_t K);
+
+/* Workspace that gemv_w4a8 (op 0) or gemv_w8a16 (op 1) needs for shape (M, N, K).
+   0 means the call needs none and accepts workspace == NULL.  A workspace must be
+   zero-filled before its first use (qw_workspace_clear does it); every call leaves
+   it zero-filled again, so one workspace serves any number of calls issued in
+   order on one stream, including inside a captured graph.  Calls that run
+   concurrently need separate workspaces. */
+size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
+
+/* Zero-fills a workspace with a kernel (no memset node, safe to capture). */
+int qw_workspace_clear(void* workspace, size_t ws_bytes, void* stream);
+
+/* Row-wise INT4 quantization and packing, done once at weight-load time
+   ("Jetson Orin AGX 上的 INT4 量化推理实践", section 当前实现方式).
+   W fp32 [N][K] -> Wq (qw_w4_packed_bytes) and w_scale fp32 [N] with
+   w_scale[n] = maxabs(W[n,:]) / 7 (fp32 division) and codes
+   clamp(rint(W / w_scale), -7, 7) (round half to even); an all-zero row has scale 0.
+   Synchronises `stream` once to read back a non-finite flag: not capturable. */
+int quantize_pack_w4(const float* W, int64_t N, int64_t K, void* Wq, float* w_scale,
+                     void* stream);
+
+/* Per-output-channel INT8 quantization, done once at load time (ChatGLM2-6B W8A16
+   write-up, sections 2 and 3).  W fp32 [N][K] -> Wq int8 [N][K] and
+   w_scale_f16 [N] = f16(maxabs(W[n,:]) / 127); codes clamp(rint(W / s16), -127, 127)
+   are taken against the stored f16 scale.  A row whose f16 scale is 0 gets zero
+   codes; a scale that overflows f16 is QW_ERR_NONFINITE.  Synchronises once. */
+int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w_scale_f16,
+                     void* stream);
+
+/* Dynamic per-row INT8 activation quantization ("Jetson Orin AGX 上的 INT4 量化推理实践",
+   section 当前实现方式).  X fp32 [M][K] -> Xq int8 [M][K] and a_scale fp32 [M] with
+   a_scale[m] = maxabs(X[m,:]) / 127 and codes clamp(rint(X / a_scale), -127, 127).
+   gemv_w4a8 runs the same computation in its prologue; the codes agree bit for bit. */
+int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scale,
+                 void* stream);
+
+/* W4A8 linear, activation quantization fused into the prologue.
+   X fp32 [M][K], Wq from quantize_pack_w4, w_scale fp32 [N] -> Y fp32 [M][N] with
+   Y[m][n] = ((float)acc[m][n] * w_scale[n]) * a_scale[m] and
+   acc[m][n] = sum_k q[n][k] * xq[m][k] in int32.  workspace/ws_bytes as described at
+   qw_workspace_bytes (op 0).  M >= 16 runs a skinny-GEMM kernel on the matrix cores. */
+int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+              int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
+
+/* W8A16 linear.  X f16 [M][K], Wq int8 [N][K], w_scale_f16 [N] -> Y f16 [M][N] with
+   Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
+   scale is applied after the sum, which equals dequantize-then-multiply up to fp32
+   rounding.  workspace as at qw_workspace_bytes (op 1). */
+int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
+               int64_t N, int64_t K, uint16_t* Y_f16, void* workspace, size_t ws_bytes,
+               void* stream);
+
+/* ---- test and tuning helpers (not on the decode path) ---------------------- */
+
+/* Device layout -> int8 codes [N][K] (device pointer). */
+int qw_w4_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* stream);
+int qw_w8_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* stream);
+
+/* gemv_w4a8 that also writes the int32 accumulators acc [M][N], the activation
+   codes xq [M][K] and scales a_scale [M] its prologue computed.  Any of the three
+   extra pointers may be NULL. */
+int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                       int64_t N, int64_t K, float* Y, int32_t* acc, int8_t* xq,
+                       float* a_scale, void* workspace, size_t ws_bytes, void* stream);
+
+/* The GEMV kernels (M < 16) with an explicit tiling instead of the built-in choice:
+   cpl = 16-byte chunks per lane per row in one K slice (1, 2 or 4), gb = row groups
+   of 4 rows loaded per batch (1, 2, 4 or 8), rows_per_wave = a multiple of 4*gb,
+   slices = K slices (>= 1; the slice length is 16*cpl chunks, so slices must equal
+   ceil(chunks_per_row / (16*cpl))).  Needs qw_tiled_workspace_bytes() of workspace. */
+int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                       int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes,
+                       int cpl, int gb, int rows_per_wave, void* stream);
+int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
+                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, void* workspace,
+                        size_t ws_bytes, int cpl, int gb, int rows_per_wave, void* stream);
+size_t qw_tiled_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int cpl, int gb,
+                                int rows_per_wave);
+
+/* Text for a status code (static storage). */
+const char* qw_status_str(int status);
+/* The hipError_t of the last QW_ERR_HIP returned on this thread (0 if none). */
+int qw_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QWGEMV_H */

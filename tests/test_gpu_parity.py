@@ -1,0 +1,346 @@
+"""Parity of the HIP path with the CPU oracle, through the C ABI, on an MI355X.
+
+Bars: INT4/INT8 codes, packed bytes, fp32/f16 scales and int32 accumulators are
+bit-exact; W4A8 outputs within 1e-6 relative error per element; W8A16 outputs within
+1e-3 relative L2 error of the fp64 dequantize-then-multiply reference.  Inputs are
+the seeded synthetic workloads of the ``workloads`` module.  Full-size shapes that
+the oracle cannot finish in seconds are checked on sampled output rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_load_amd as qw
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+W4A8_RTOL = 1e-6
+W8A16_RL2 = 1e-3
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.set_device(0)
+    qw.lib()
+    yield
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def assert_w4a8_close(y, yo):
+    y = np.asarray(y, np.float64)
+    yo = np.asarray(yo, np.float64)
+    zero = yo == 0
+    assert np.all(y[zero] == 0)
+    rel = np.abs(y[~zero] - yo[~zero]) / np.abs(yo[~zero])
+    assert rel.size == 0 or rel.max() <= W4A8_RTOL, rel.max()
+
+
+def rel_l2(y, y64):
+    y = np.asarray(y, np.float64)
+    return float(np.linalg.norm(y - y64) / max(np.linalg.norm(y64), 1e-300))
+
+
+def pack_w4_and_check(W, rows=None):
+    """GPU pack of W; compares packed bytes, codes and scales with the oracle (on
+    `rows` only when given).  Returns (Wq, s) on the device."""
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    Wsub = W if rows is None else W[rows]
+    q_o, s_o = oracle.quant_w4(Wsub)
+    Wq_h = host(Wq if rows is None else Wq[torch.as_tensor(rows, device="cuda")])
+    s_h = host(s if rows is None else s[torch.as_tensor(rows, device="cuda")])
+    assert np.array_equal(s_h.view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(Wq_h, oracle.pack_w4(q_o))
+    return Wq, s, q_o, s_o
+
+
+# ------------------------------------------------------------------ config 0 --
+
+def test_tiny_w4a8_config_bit_exact():
+    M, K, N = 1, 256, 512
+    say("tiny W4A8 seed 0", M, K, N)
+    W = wl.weights(0, wl.tensor_id("tiny", 0), N, K)
+    X = wl.activations(0, wl.tensor_id("tiny", 1), M, K)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    codes = host(qw.w4_codes(Wq, N, K))
+    assert np.array_equal(codes, q_o)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    ws = qw.make_workspace("w4a8", M, N, K)
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=ws)
+    assert np.array_equal(host(out["xq"]), ref["xq"])
+    assert np.array_equal(host(out["a"]).view(np.uint32), ref["a"].view(np.uint32))
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert_w4a8_close(host(out["Y"]), ref["Y"])
+    # the production entry point, into a NaN-poisoned output with guard canaries
+    buf = torch.full((M * N + 64,), float("nan"), device="cuda")
+    buf[M * N:] = 12345.0
+    Y = buf[:M * N].view(M, N)
+    qw.gemv_w4a8(dev(X), Wq, s, workspace=ws, out=Y)
+    bh = host(buf)
+    assert np.all(bh[M * N:] == 12345.0)
+    assert np.array_equal(bh[:M * N].reshape(M, N), host(out["Y"]))
+    if ws is not None:
+        assert not host(ws).any(), "workspace must be left zero-filled"
+
+
+def test_quant_act_matches_oracle_and_fused_prologue():
+    for (M, K, seed) in [(1, 256, 0), (1, 3584, 1), (4, 4096, 4), (3, 18944, 5), (2, 32, 6)]:
+        say("quant_act", M, K)
+        X = wl.activations(seed, 99, M, K, outlier_channels=4 if K >= 64 else 0)
+        if M > 1:
+            X[1] = 0.0  # an all-zero row
+        xq, a = qw.quant_act_i8(dev(X))
+        xq_o, a_o = oracle.quant_act_i8(X)
+        assert np.array_equal(host(xq), xq_o)
+        assert np.array_equal(host(a).view(np.uint32), a_o.view(np.uint32))
+        N = 64
+        W = wl.weights(seed, 98, N, K)
+        Wq, s = qw.quantize_pack_w4(dev(W))
+        out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+        assert np.array_equal(host(out["xq"]), xq_o)
+        assert np.array_equal(host(out["a"]).view(np.uint32), a_o.view(np.uint32))
+
+
+# ------------------------------------------------------------------ config 1 --
+
+@pytest.mark.parametrize("name,K,N", wl.QWEN7B_LINEARS)
+def test_qwen7b_linear_w4a8(name, K, N):
+    seed = wl.QWEN7B_W4A8["seed"]
+    say("qwen7b W4A8", name, K, N)
+    W = wl.weights(seed, wl.tensor_id(name, 0), N, K, outlier_rows=True)
+    X = wl.activations(seed, wl.tensor_id(name, 1), 1, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", 1, N, K))
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert_w4a8_close(host(out["Y"]), ref["Y"])
+    Y = qw.gemv_w4a8(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", 1, N, K))
+    assert_w4a8_close(host(Y), ref["Y"])
+
+
+# ------------------------------------------------------------------ config 2 --
+
+def _w8a16_case(seed, tid_w, tid_x, M, N, K, rows=None):
+    W = wl.weights(seed, tid_w, N, K)
+    X16 = wl.activations(seed, tid_x, M, K, dtype=np.float16)
+    Wq, s16 = qw.quantize_pack_w8(dev(W))
+    Wsub = W if rows is None else W[rows]
+    q_o, s16_o = oracle.quant_w8(Wsub)
+    ridx = None if rows is None else torch.as_tensor(rows, device="cuda")
+    assert np.array_equal(host(Wq if ridx is None else Wq[ridx]), q_o)
+    assert np.array_equal(host(s16 if ridx is None else s16[ridx]).view(np.uint16), s16_o)
+    y = qw.gemv_w8a16(dev(X16), Wq, s16, workspace=qw.make_workspace("w8a16", M, N, K))
+    y = host(y if ridx is None else y[:, ridx]).astype(np.float64)
+    y64 = oracle.gemv_w8a16_ref64(X16, q_o, s16_o, nthreads=oracle.num_threads())
+    return W if rows is None else Wsub, X16, y, y64
+
+
+def test_chatglm2_w8a16_config():
+    c = wl.CHATGLM2_W8A16
+    say("chatglm2 W8A16", c["K"], c["N"])
+    W, X16, y, y64 = _w8a16_case(c["seed"], wl.tensor_id("chatglm2", 0),
+                                 wl.tensor_id("chatglm2", 1), 1, c["N"], c["K"])
+    assert rel_l2(y, y64) <= W8A16_RL2
+    yf = X16.astype(np.float64) @ W.astype(np.float64).T
+    cos = float((y * yf).sum() / np.linalg.norm(y) / np.linalg.norm(yf))
+    assert cos > 0.99
+
+
+def test_headline_w8a16_shape():
+    c = wl.HEADLINE
+    say("headline W8A16", c["K"], c["N"])
+    _, _, y, y64 = _w8a16_case(7, wl.tensor_id("headline_w8", 0), wl.tensor_id("headline_w8", 1),
+                               1, c["N"], c["K"])
+    assert rel_l2(y, y64) <= W8A16_RL2
+
+
+# ------------------------------------------------------------------ config 3 --
+
+def _sample_rows(N, n=2048, seed=0):
+    r = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(0, 64), np.arange(N - 64, N), r.choice(N, n, replace=False)])
+    return np.unique(rows)
+
+
+def test_lm_head_w4a8_sampled():
+    c = wl.LMHEAD_W4A8
+    K, N = c["K"], c["N"]
+    say("lm_head W4A8", K, N)
+    W = wl.weights(c["seed"], wl.tensor_id("lm_head", 0), N, K)
+    X = wl.activations(c["seed"], wl.tensor_id("lm_head", 1), 1, K)
+    rows = _sample_rows(N)
+    Wq, s, q_o, s_o = pack_w4_and_check(W, rows)
+    del W
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", 1, N, K))
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    ridx = torch.as_tensor(rows, device="cuda")
+    assert np.array_equal(host(out["acc"][:, ridx]), ref["acc"])
+    assert_w4a8_close(host(out["Y"][:, ridx]), ref["Y"])
+    assert torch.isfinite(out["Y"]).all().item()
+
+
+# ------------------------------------------------------------------ config 4 --
+
+@pytest.mark.parametrize("M", wl.SKINNY["Ms"])
+def test_skinny_sweep_sampled(M):
+    c = wl.SKINNY
+    K, N = c["K"], c["N"]
+    say("skinny", M, K, N)
+    rows = _sample_rows(N, 512, seed=M)
+    W = wl.weights(c["seed"], wl.tensor_id("skinny", 0), N, K)
+    X = wl.activations(c["seed"], wl.tensor_id("skinny", 1), M, K)
+    Wq, s, q_o, s_o = pack_w4_and_check(W, rows)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    ridx = torch.as_tensor(rows, device="cuda")
+    Y = qw.gemv_w4a8(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+    assert_w4a8_close(host(Y[:, ridx]), ref["Y"])
+    del Wq, s
+    X16 = X.astype(np.float16)
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    q8, s16_o = oracle.quant_w8(W[rows])
+    assert np.array_equal(host(Wq8[ridx]), q8)
+    y = qw.gemv_w8a16(dev(X16), Wq8, s16, workspace=qw.make_workspace("w8a16", M, N, K))
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    assert rel_l2(host(y[:, ridx]), y64) <= W8A16_RL2
+
+
+# --------------------------------------------------------------- edge cases --
+
+EDGE = [(1, 1, 32), (1, 5, 96), (2, 17, 64), (3, 517, 288), (5, 64, 1024), (8, 100, 3584),
+        (9, 33, 256), (15, 7, 512), (1, 4100, 8192), (1, 3, 131072 // 8)]
+
+
+@pytest.mark.parametrize("M,N,K", EDGE)
+def test_edge_shapes_both_ops(M, N, K):
+    say("edge", M, N, K)
+    W = wl.weights(100 + M, 1, N, K, outlier_rows=N >= 100)
+    if N > 2:
+        W[1] = 0.0  # zero row
+    X = wl.activations(100 + M, 2, M, K, outlier_channels=4 if K >= 64 else 0)
+    if M > 1:
+        X[M - 1] = 0.0  # zero activation vector
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert_w4a8_close(host(out["Y"]), ref["Y"])
+    X16 = X.astype(np.float16)
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    q8, s16_o = oracle.quant_w8(W)
+    assert np.array_equal(host(Wq8), q8)
+    assert np.array_equal(host(s16).view(np.uint16), s16_o)
+    y = host(qw.gemv_w8a16(dev(X16), Wq8, s16, workspace=qw.make_workspace("w8a16", M, N, K)))
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
+    if np.linalg.norm(y64) > 0:
+        assert rel_l2(y, y64) <= W8A16_RL2
+    if M > 1:
+        assert not np.any(y[M - 1]) and not np.any(host(out["Y"])[M - 1])
+
+
+TILINGS = [(1, 1, 4), (1, 2, 8), (1, 4, 16), (1, 8, 64), (2, 1, 4), (2, 4, 32), (2, 8, 32),
+           (4, 1, 8), (4, 2, 8), (4, 4, 16)]
+
+
+@pytest.mark.parametrize("M", [1, 2, 4])
+def test_every_tiling_gives_the_same_result(M):
+    K, N = 3584, 1000
+    say("tilings M", M)
+    W = wl.weights(55, 1, N, K, outlier_rows=True)
+    X = wl.activations(55, 2, M, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    X16 = X.astype(np.float16)
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    q8, s16_o = oracle.quant_w8(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
+    Xd, X16d = dev(X), dev(X16)
+    for (cpl, gb, rpw) in TILINGS:
+        mt = 1 if M == 1 else (2 if M == 2 else 4)
+        if mt * cpl > 8:
+            continue
+        ws = qw.tiled_workspace("w4a8", M, N, K, cpl, gb, rpw)
+        for rep in range(2):
+            Y = qw.gemv_w4a8_tiled(Xd, Wq, s, cpl, gb, rpw, workspace=ws)
+            assert_w4a8_close(host(Y), ref["Y"])
+        if ws is not None:
+            assert not host(ws).any()
+        ws8 = qw.tiled_workspace("w8a16", M, N, K, cpl, gb, rpw)
+        y = qw.gemv_w8a16_tiled(X16d, Wq8, s16, cpl, gb, rpw, workspace=ws8)
+        assert rel_l2(host(y), y64) <= W8A16_RL2, (cpl, gb, rpw)
+
+
+def test_repeated_calls_are_deterministic():
+    K, N, M = 4096, 2048, 1
+    W = wl.weights(66, 1, N, K)
+    X = wl.activations(66, 2, M, K)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    ws4 = qw.make_workspace("w4a8", M, N, K)
+    ws8 = qw.make_workspace("w8a16", M, N, K)
+    Xd, X16 = dev(X), dev(X.astype(np.float16))
+    a = [host(qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)) for _ in range(3)]
+    b = [host(qw.gemv_w8a16(X16, Wq8, s16, workspace=ws8)) for _ in range(3)]
+    for i in (1, 2):
+        assert np.array_equal(a[0].view(np.uint32), a[i].view(np.uint32))
+        assert np.array_equal(b[0].view(np.uint16), b[i].view(np.uint16))
+
+
+def test_packers_report_non_finite_weights():
+    W = np.zeros((4, 64), np.float32)
+    W[2, 5] = np.nan
+    with pytest.raises(qw.QWError) as e:
+        qw.quantize_pack_w4(dev(W))
+    assert e.value.status == qw.QW_ERR_NONFINITE
+    W[2, 5] = np.inf
+    with pytest.raises(qw.QWError) as e:
+        qw.quantize_pack_w8(dev(W))
+    assert e.value.status == qw.QW_ERR_NONFINITE
+    W[2, 5] = 1e7  # 1e7/127 overflows f16
+    with pytest.raises(qw.QWError) as e:
+        qw.quantize_pack_w8(dev(W))
+    assert e.value.status == qw.QW_ERR_NONFINITE
+
+
+def test_graph_capture_replays_match_eager():
+    K, N, M = 3584, 512, 1  # short N: split K, so the workspace protocol is exercised
+    W = wl.weights(77, 1, N, K)
+    X = wl.activations(77, 2, M, K)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    Xd, X16 = dev(X), dev(X.astype(np.float16))
+    ws4 = qw.make_workspace("w4a8", M, N, K)
+    ws8 = qw.make_workspace("w8a16", M, N, K)
+    e4 = host(qw.gemv_w4a8(Xd, Wq, s, workspace=ws4))
+    e8 = host(qw.gemv_w8a16(X16, Wq8, s16, workspace=ws8))
+    Y4 = torch.empty((M, N), device="cuda")
+    Y8 = torch.empty((M, N), device="cuda", dtype=torch.float16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qw.gemv_w4a8(Xd, Wq, s, workspace=ws4, out=Y4)
+        qw.gemv_w8a16(X16, Wq8, s16, workspace=ws8, out=Y8)
+    for rep in range(4):
+        Y4.fill_(float("nan"))
+        Y8.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y4).view(np.uint32), e4.view(np.uint32)), rep
+        assert np.array_equal(host(Y8).view(np.uint16), e8.view(np.uint16)), rep
+        qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)  # eager work between replays
+    if ws4 is not None:
+        assert not host(ws4).any()

@@ -46,9 +46,8 @@ SIGNATURES = {
     "qw_w4_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_w8_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_gemv_w4a8_debug": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
-    "qw_gemv_w4a8_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
-    "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
-    "qw_tiled_workspace_bytes": (_SZ, [_I, _I64, _I64, _I64, _I, _I, _I]),
+    "qw_gemv_w4a8_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
+    "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
 }
@@ -74,6 +73,11 @@ def lib():
             raise RuntimeError(
                 "libqwgemv.so is not built (%s); run __graft_entry__.build() or "
                 "python -m bit_weight_quantized_load_amd._build" % LIB_PATH)
+        # torch ships its own HIP runtime (same soname, libamdhip64.so.7).  Loading
+        # torch first makes the library bind to that one runtime instead of bringing
+        # a second copy of the runtime into the process.
+        import torch  # noqa: F401
+
         L = ctypes.CDLL(LIB_PATH)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(L, name)
@@ -133,23 +137,33 @@ def make_workspace(op: str, M: int, N: int, K: int, device="cuda", stream=None):
     return ws
 
 
+def w4_packed_bytes(N: int, K: int) -> int:
+    return int(lib().qw_w4_packed_bytes(N, K))
+
+
+def w8_packed_bytes(N: int, K: int) -> int:
+    return int(lib().qw_w8_packed_bytes(N, K))
+
+
 def quantize_pack_w4(W, stream=None):
-    """W fp32 [N][K] -> (Wq uint8 [N][K/2], w_scale fp32 [N]).  Load time; synchronises."""
+    """W fp32 [N][K] -> (Wq uint8 [w4_packed_bytes(N, K)] in the tile layout, w_scale fp32 [N]).
+    Load time; synchronises."""
     torch = _torch()
     N, K = W.shape
     _need(W, torch.float32, (N, K), "W")
-    Wq = torch.empty((N, K // 2), dtype=torch.uint8, device=W.device)
+    Wq = torch.empty((w4_packed_bytes(N, K),), dtype=torch.uint8, device=W.device)
     s = torch.empty((N,), dtype=torch.float32, device=W.device)
     _call("quantize_pack_w4", _ptr(W), N, K, _ptr(Wq), _ptr(s), _stream(stream))
     return Wq, s
 
 
 def quantize_pack_w8(W, stream=None):
-    """W fp32 [N][K] -> (Wq int8 [N][K], w_scale fp16 [N]).  Load time; synchronises."""
+    """W fp32 [N][K] -> (Wq uint8 [w8_packed_bytes(N, K)] in the tile layout, w_scale fp16 [N]).
+    Load time; synchronises."""
     torch = _torch()
     N, K = W.shape
     _need(W, torch.float32, (N, K), "W")
-    Wq = torch.empty((N, K), dtype=torch.int8, device=W.device)
+    Wq = torch.empty((w8_packed_bytes(N, K),), dtype=torch.uint8, device=W.device)
     s = torch.empty((N,), dtype=torch.float16, device=W.device)
     _call("quantize_pack_w8", _ptr(W), N, K, _ptr(Wq), _ptr(s), _stream(stream))
     return Wq, s
@@ -178,7 +192,7 @@ def gemv_w4a8(X, Wq, w_scale, workspace=None, out=None, stream=None):
     M, K = X.shape
     N = w_scale.shape[0]
     _need(X, torch.float32, (M, K), "X")
-    _need(Wq, torch.uint8, (N, K // 2), "Wq")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
     _need(w_scale, torch.float32, (N,), "w_scale")
     Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
     _need(Y, torch.float32, (M, N), "out")
@@ -193,7 +207,7 @@ def gemv_w4a8_debug(X, Wq, w_scale, workspace=None, stream=None):
     M, K = X.shape
     N = w_scale.shape[0]
     _need(X, torch.float32, (M, K), "X")
-    _need(Wq, torch.uint8, (N, K // 2), "Wq")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
     _need(w_scale, torch.float32, (N,), "w_scale")
     dev = X.device
     Y = torch.empty((M, N), dtype=torch.float32, device=dev)
@@ -212,7 +226,7 @@ def gemv_w8a16(X16, Wq, w_scale16, workspace=None, out=None, stream=None):
     M, K = X16.shape
     N = w_scale16.shape[0]
     _need(X16, torch.float16, (M, K), "X16")
-    _need(Wq, torch.int8, (N, K), "Wq")
+    _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
     _need(w_scale16, torch.float16, (N,), "w_scale16")
     Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
     _need(Y, torch.float16, (M, N), "out")
@@ -222,38 +236,29 @@ def gemv_w8a16(X16, Wq, w_scale16, workspace=None, out=None, stream=None):
     return Y
 
 
-def tiled_workspace(op: str, M, N, K, cpl, gb, rows_per_wave, device="cuda", stream=None):
-    nbytes = int(lib().qw_tiled_workspace_bytes(0 if op == "w4a8" else 1, M, N, K, cpl, gb,
-                                                rows_per_wave))
-    if nbytes == 0:
-        return None
-    torch = _torch()
-    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
-    _call("qw_workspace_clear", _ptr(ws), nbytes, _stream(stream))
-    return ws
-
-
-def gemv_w4a8_tiled(X, Wq, w_scale, cpl, gb, rows_per_wave, workspace=None, out=None,
-                    stream=None):
+def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, rg_per_wave, out=None, stream=None):
+    """gemv_w4a8 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X.shape
     N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
-    wp, wn = _ws_args(workspace)
-    _call("qw_gemv_w4a8_tiled", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn,
-          cpl, gb, rows_per_wave, _stream(stream))
+    _call("qw_gemv_w4a8_tiled", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
+          u, nw, rg_per_wave, _stream(stream))
     return Y
 
 
-def gemv_w8a16_tiled(X16, Wq, w_scale16, cpl, gb, rows_per_wave, workspace=None, out=None,
-                     stream=None):
+def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, rg_per_wave, out=None, stream=None):
+    """gemv_w8a16 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X16.shape
     N = w_scale16.shape[0]
+    _need(X16, torch.float16, (M, K), "X16")
+    _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
-    wp, wn = _ws_args(workspace)
-    _call("qw_gemv_w8a16_tiled", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y), wp, wn,
-          cpl, gb, rows_per_wave, _stream(stream))
+    _call("qw_gemv_w8a16_tiled", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
+          u, nw, rg_per_wave, _stream(stream))
     return Y
 
 

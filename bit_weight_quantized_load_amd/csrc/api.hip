@@ -19,7 +19,6 @@ thread_local int g_last_hip_error = 0;
 constexpr int64_t kMaxK = 131072;  // keeps 16 * 7 * 127 * K below 2^31
 constexpr int64_t kMaxM = 65535;
 constexpr int64_t kMaxN = (int64_t)1 << 28;
-constexpr size_t kAlign = 256;     // workspace sub-buffer alignment
 
 int hip_status(hipError_t e)
 {
@@ -31,8 +30,6 @@ int hip_status(hipError_t e)
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
-
 int check_shape(int64_t M, int64_t N, int64_t K)
 {
     if (M <= 0 || N <= 0 || K <= 0 || M > kMaxM || N > kMaxN || K > kMaxK || (K % 32) != 0)
@@ -40,90 +37,73 @@ int check_shape(int64_t M, int64_t N, int64_t K)
     return QW_OK;
 }
 
-int mt_for(int64_t M)
-{
-    if (M >= 8)
-        return 8;
-    if (M >= 3)
-        return M >= 5 ? 8 : 4;
-    return (int)M;
-}
+constexpr int kMaxLds = 60 * 1024;  // dynamic LDS budget per workgroup
 
-// Chunks (16 bytes of packed weights) per row: 32 INT4 or 16 INT8 weights each.
-int64_t chunks_per_row(int op, int64_t K) { return op == 0 ? K / 32 : K / 16; }
+// Bytes of LDS activation storage per tile per row of X: 16 chunks x 32 INT8 codes
+// (W4A8) or 32 chunks x 16 f16 values (W8A16).
+int act_tile_bytes(int bits) { return bits == 4 ? 512 : 1024; }
 
-bool tiling_ok(int mt, int cpl, int gb, int rows_per_wave)
+int scale_lds_bytes(int bits, int nw) { return bits == 4 ? 4 * 64 * nw * 4 : 2 * 64 * nw * 2; }
+
+bool tiling_ok(int u, int nw, int rg_per_wave, int cg)
 {
-    if (cpl != 1 && cpl != 2 && cpl != 4)
+    if (u != 4 && u != 8)
         return false;
-    if (gb != 1 && gb != 2 && gb != 4 && gb != 8)
+    if (nw != 4 && nw != 8)
         return false;
-    if (mt * cpl > 8 || gb * cpl > 16)
+    if (rg_per_wave < 1 || rg_per_wave > 64)  // output scales of a workgroup fit in LDS
         return false;
-    if (rows_per_wave <= 0 || rows_per_wave % (4 * gb) != 0 || rows_per_wave > 4096)
+    if ((int64_t)nw * rg_per_wave * cg * 1024 >= ((int64_t)1 << 31))
         return false;
     return true;
 }
 
-GemvTiling make_tiling(int op, int64_t M, int64_t N, int64_t K, int cpl, int gb,
-                       int rows_per_wave)
+// M == 1 with K <= 512 * kRegCG keeps activations in registers; otherwise rows of X
+// per workgroup are M rounded up to a power of two (at most 8), lowered until the
+// staged activations fit in LDS.
+GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw, int rg_per_wave)
 {
+    const qw::TileLayout L = qw::tile_layout(bits, N, K);
     GemvTiling t;
-    t.mt = mt_for(M);
-    t.cpl = cpl;
-    t.gb = gb;
-    t.rows_per_wave = rows_per_wave;
-    const int64_t slice = 16 * (int64_t)cpl;
-    t.slices = (int)((chunks_per_row(op, K) + slice - 1) / slice);
-    t.row_blocks = (int)((N + 4 * rows_per_wave - 1) / (4 * rows_per_wave));
+    t.u = u;
+    t.nw = nw;
+    t.rg_per_wave = rg_per_wave;
+    t.blocks = (L.nrg + nw * rg_per_wave - 1) / (nw * rg_per_wave);
+    const int scale_bytes = scale_lds_bytes(bits, nw);
+    if (M == 1 && L.cg <= qw::kRegCG) {
+        t.reg_cg = L.cg;
+        t.mt = 1;
+        t.lds_bytes = (bits == 4 ? L.cg * act_tile_bytes(4) : 0) + scale_bytes;
+    } else {
+        t.reg_cg = 0;
+        const int tiles = (L.cg + u - 1) / u * u;
+        int mt = M >= 5 ? 8 : (M >= 3 ? 4 : (int)M);
+        while (mt > 1 && mt * tiles * act_tile_bytes(bits) + scale_bytes > kMaxLds)
+            mt >>= 1;
+        t.mt = mt;
+        t.lds_bytes = mt * tiles * act_tile_bytes(bits) + scale_bytes;
+    }
     t.m_tiles = (int)((M + t.mt - 1) / t.mt);
     return t;
 }
 
-// Built-in tiling for the GEMV kernels.
-GemvTiling default_tiling(int op, int64_t M, int64_t N, int64_t K)
-{
-    const int mt = mt_for(M);
-    const int64_t cpr = chunks_per_row(op, K);
-    int cpl = cpr >= 256 ? 4 : (cpr >= 32 ? 2 : 1);
-    while (mt * cpl > 8)
-        cpl >>= 1;
-    const int64_t slices = (cpr + 16 * cpl - 1) / (16 * cpl);
-    const int64_t m_tiles = (M + mt - 1) / mt;
-    // Aim at about four workgroups per compute unit (256 CUs).
-    const int64_t target = 1024;
-    int64_t blocks = (target + slices * m_tiles - 1) / (slices * m_tiles);
-    if (blocks < 1)
-        blocks = 1;
-    int64_t rpw = (N + 4 * blocks - 1) / (4 * blocks);
-    int gb = 4;
-    while (gb * cpl > 16)
-        gb >>= 1;
-    if (rpw < 4 * gb) {
-        gb = rpw <= 4 ? 1 : (rpw <= 8 ? 2 : gb);
-    }
-    rpw = (rpw + 4 * gb - 1) / (4 * gb) * (4 * gb);
-    if (rpw > 4096)
-        rpw = 4096;
-    return make_tiling(op, M, N, K, cpl, gb, (int)rpw);
-}
+bool fits_lds(const GemvTiling& t) { return t.lds_bytes <= kMaxLds; }
 
-// Workspace layout: [per-op data, 256-aligned][counters].
-size_t workspace_for(int op, int64_t M, int64_t N, const GemvTiling& t)
+// Built-in launch shape: 4 waves per workgroup, 8 tiles per batch (LDS variant), and
+// as many row groups per wave as it takes to keep about 16 waves per compute unit
+// (256 CUs) in one round of work.
+GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
-    if (t.slices <= 1)
-        return 0;
-    size_t data = op == 0 ? (size_t)M * (size_t)N * 4u
-                          : (size_t)t.slices * (size_t)M * (size_t)N * 4u;
-    size_t counters = (size_t)t.row_blocks * (size_t)t.m_tiles * 4u;
-    return round_up(data, kAlign) + round_up(counters, kAlign);
-}
-
-size_t counters_offset(int op, int64_t M, int64_t N, const GemvTiling& t)
-{
-    size_t data = op == 0 ? (size_t)M * (size_t)N * 4u
-                          : (size_t)t.slices * (size_t)M * (size_t)N * 4u;
-    return round_up(data, kAlign);
+    const qw::TileLayout L = qw::tile_layout(bits, N, K);
+    const int nw = 4, u = 8;
+    int64_t g = (L.nrg + 4095) / 4096;
+    if (g < 1)
+        g = 1;
+    if (g > 64)
+        g = 64;
+    while (g > 1 && (int64_t)nw * g * L.cg * 1024 >= ((int64_t)1 << 31))
+        --g;
+    return make_tiling(bits, M, N, K, u, nw, (int)g);
 }
 
 // One device int per GPU for the packers' non-finite flag.
@@ -160,7 +140,7 @@ int read_flag(int* flag, hipStream_t st, int* host)
 
 int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
              int64_t K, float* Y, int32_t* acc, int8_t* xq, float* a_scale, void* workspace,
-             size_t ws_bytes, const GemvTiling& t, bool debug, void* stream)
+             const GemvTiling& t, bool debug, void* stream)
 {
     if (!X || !Wq || !w_scale || !Y)
         return QW_ERR_NULL;
@@ -170,9 +150,7 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
         !aligned16(workspace) || !aligned16(acc) || !aligned16(xq) || !aligned16(a_scale))
         return QW_ERR_ALIGN;
-    const size_t need = workspace_for(0, M, N, t);
-    if (need > 0 && (workspace == nullptr || ws_bytes < need))
-        return QW_ERR_WORKSPACE;
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
     qw::W4A8Args a;
     a.X = X;
     a.Wq = static_cast<const uint8_t*>(Wq);
@@ -181,11 +159,9 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.rows_per_wave = t.rows_per_wave;
-    a.acc_ws = need ? static_cast<int32_t*>(workspace) : nullptr;
-    a.counters = need ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                    counters_offset(0, M, N, t))
-                      : nullptr;
+    a.cg = L.cg;
+    a.nrg = L.nrg;
+    a.rg_per_wave = t.rg_per_wave;
     a.dbg_acc = acc;
     a.dbg_xq = xq;
     a.dbg_a = a_scale;
@@ -193,8 +169,7 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
 }
 
 int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_t M, int64_t N,
-              int64_t K, uint16_t* Y, void* workspace, size_t ws_bytes, const GemvTiling& t,
-              void* stream)
+              int64_t K, uint16_t* Y, void* workspace, const GemvTiling& t, void* stream)
 {
     if (!X || !Wq || !w_scale || !Y)
         return QW_ERR_NULL;
@@ -204,9 +179,7 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
         !aligned16(workspace))
         return QW_ERR_ALIGN;
-    const size_t need = workspace_for(1, M, N, t);
-    if (need > 0 && (workspace == nullptr || ws_bytes < need))
-        return QW_ERR_WORKSPACE;
+    const qw::TileLayout L = qw::tile_layout(8, N, K);
     qw::W8A16Args a;
     a.X = X;
     a.Wq = static_cast<const uint8_t*>(Wq);
@@ -215,11 +188,9 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     a.M = (int)M;
     a.N = (int)N;
     a.K = (int)K;
-    a.rows_per_wave = t.rows_per_wave;
-    a.part_ws = need ? static_cast<float*>(workspace) : nullptr;
-    a.counters = need ? reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) +
-                                                    counters_offset(1, M, N, t))
-                      : nullptr;
+    a.cg = L.cg;
+    a.nrg = L.nrg;
+    a.rg_per_wave = t.rg_per_wave;
     return hip_status(qw::launch_gemv_w8a16(a, t, static_cast<hipStream_t>(stream)));
 }
 
@@ -229,32 +200,25 @@ extern "C" {
 
 size_t qw_w4_packed_bytes(int64_t N, int64_t K)
 {
-    if (N <= 0 || K <= 0)
+    if (N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (K % 32) != 0)
         return 0;
-    return (size_t)N * (size_t)(K / 2);
+    return qw::packed_bytes(4, N, K);
 }
 
 size_t qw_w8_packed_bytes(int64_t N, int64_t K)
 {
-    if (N <= 0 || K <= 0)
+    if (N <= 0 || K <= 0 || N > kMaxN || K > kMaxK || (K % 32) != 0)
         return 0;
-    return (size_t)N * (size_t)K;
+    return qw::packed_bytes(8, N, K);
 }
 
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
 {
-    if ((op != 0 && op != 1) || check_shape(M, N, K) != QW_OK)
-        return 0;
-    return workspace_for(op, M, N, default_tiling(op, M, N, K));
-}
-
-size_t qw_tiled_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int cpl, int gb,
-                                int rows_per_wave)
-{
-    if ((op != 0 && op != 1) || check_shape(M, N, K) != QW_OK ||
-        !tiling_ok(mt_for(M), cpl, gb, rows_per_wave))
-        return 0;
-    return workspace_for(op, M, N, make_tiling(op, M, N, K, cpl, gb, rows_per_wave));
+    (void)op;
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;  // no kernel of this version keeps state between workgroups
 }
 
 int qw_workspace_clear(void* workspace, size_t ws_bytes, void* stream)
@@ -310,7 +274,7 @@ int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, s);
     if (e == hipSuccess)
-        e = qw::launch_pack_w8(W, (int)N, (int)K, static_cast<int8_t*>(Wq), w_scale_f16, flag, s);
+        e = qw::launch_pack_w8(W, (int)N, (int)K, static_cast<uint8_t*>(Wq), w_scale_f16, flag, s);
     if (e != hipSuccess)
         return hip_status(e);
     int host = 0;
@@ -335,54 +299,61 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream)
 {
+    (void)ws_bytes;
     if (check_shape(M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace, ws_bytes,
-                    default_tiling(0, M, N, K), false, stream);
+    return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
+                    default_tiling(4, M, N, K), false, stream);
 }
 
 int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int64_t M,
                        int64_t N, int64_t K, float* Y, int32_t* acc, int8_t* xq, float* a_scale,
                        void* workspace, size_t ws_bytes, void* stream)
 {
+    (void)ws_bytes;
     if (check_shape(M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    return run_w4a8(X, Wq, w_scale, M, N, K, Y, acc, xq, a_scale, workspace, ws_bytes,
-                    default_tiling(0, M, N, K), true, stream);
+    return run_w4a8(X, Wq, w_scale, M, N, K, Y, acc, xq, a_scale, workspace,
+                    default_tiling(4, M, N, K), true, stream);
 }
 
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes, int cpl,
-                       int gb, int rows_per_wave, void* stream)
+                       int64_t N, int64_t K, float* Y, int u, int nw, int rg_per_wave, void* stream)
 {
     if (check_shape(M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(mt_for(M), cpl, gb, rows_per_wave))
+    if (!tiling_ok(u, nw, rg_per_wave, qw::tile_layout(4, N, K).cg))
         return QW_ERR_TILING;
-    return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace, ws_bytes,
-                    make_tiling(0, M, N, K, cpl, gb, rows_per_wave), false, stream);
+    const GemvTiling t = make_tiling(4, M, N, K, u, nw, rg_per_wave);
+    if (!fits_lds(t))
+        return QW_ERR_TILING;
+    return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, nullptr, t, false,
+                    stream);
 }
 
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
                int64_t N, int64_t K, uint16_t* Y_f16, void* workspace, size_t ws_bytes,
                void* stream)
 {
+    (void)ws_bytes;
     if (check_shape(M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, ws_bytes,
-                     default_tiling(1, M, N, K), stream);
+    return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace,
+                     default_tiling(8, M, N, K), stream);
 }
 
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
-                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, void* workspace,
-                        size_t ws_bytes, int cpl, int gb, int rows_per_wave, void* stream)
+                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
+                        int rg_per_wave, void* stream)
 {
     if (check_shape(M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(mt_for(M), cpl, gb, rows_per_wave))
+    if (!tiling_ok(u, nw, rg_per_wave, qw::tile_layout(8, N, K).cg))
         return QW_ERR_TILING;
-    return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, ws_bytes,
-                     make_tiling(1, M, N, K, cpl, gb, rows_per_wave), stream);
+    const GemvTiling t = make_tiling(8, M, N, K, u, nw, rg_per_wave);
+    if (!fits_lds(t))
+        return QW_ERR_TILING;
+    return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, t, stream);
 }
 
 int qw_w4_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* stream)
@@ -407,7 +378,7 @@ int qw_w8_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* strea
         return st;
     if (!aligned16(Wq) || !aligned16(codes))
         return QW_ERR_ALIGN;
-    return hip_status(qw::launch_codes_w8(static_cast<const int8_t*>(Wq), (int)N, (int)K, codes,
+    return hip_status(qw::launch_codes_w8(static_cast<const uint8_t*>(Wq), (int)N, (int)K, codes,
                                           static_cast<hipStream_t>(stream)));
 }
 

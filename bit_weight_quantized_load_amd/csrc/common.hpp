@@ -40,6 +40,29 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// Maximum of non-negative values over the 64 lanes of a wave with DPP: rotations
+// within each 16-lane row, then row 0 -> 1 and row 2 -> 3 (row_bcast:15), then
+// row 1 -> rows 2, 3 (row_bcast:31); lane 63 ends with the maximum.  Rows outside a
+// broadcast's row mask keep the `old` operand, 0, which is harmless for a maximum
+// of non-negative values.
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x124, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x122, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x121, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xc, 0xf, false)));
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+}
+
+// Sum over the two 16-lane rows of each half wave (rows 0+1 and 2+3), after
+// row_sum16: the totals land in rows 1 and 3 (lanes 16..31 and 48..63).
+__device__ __forceinline__ float half_wave_sum_from_rows(float v)
+{
+    return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xa, 0xf, false));
+}
+
 // Maximum over a 256-thread workgroup.  `red` is 4 floats of LDS; every thread
 // must call this, and every thread gets the result.
 __device__ __forceinline__ float block_max(float v, float* red)
@@ -74,6 +97,91 @@ __device__ __forceinline__ int quant_code(float x, float scale, float qmax)
     float r = rintf(x / scale);
     r = fminf(fmaxf(r, -qmax), qmax);
     return (int)r;
+}
+
+// Buffer resource over [base, base + bytes): raw (unstrided) buffer loads through
+// it return zeros past the end instead of faulting, so the kernels load without
+// per-lane guards (a guarded load becomes a branch that serialises the loads).
+// The descriptor's last word is the gfx9 default data format.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+
+__device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t offset)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
+__device__ __forceinline__ float4 load16f(rsrc_t r, uint32_t offset)
+{
+    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
+}
+
+__device__ __forceinline__ uint32_t load4(rsrc_t r, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b32(r, offset, 0, 0);
+}
+
+__device__ __forceinline__ uint16_t load2(rsrc_t r, uint32_t offset)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, offset, 0, 0);
+}
+
+// Waits until this lane's outstanding vector memory operations (loads, stores and
+// atomics without return) have completed.  Used instead of a device-scope fence in
+// the split-K hand-off: the partial results travel through device-scope atomics,
+// which need only be complete, not flushed from a cache, before the hand-off
+// counter is bumped.  (A device-scope fence on a multi-die part writes back and
+// invalidates the whole L2.)
+__device__ __forceinline__ void wait_memory_ops()
+{
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// The same code computed with one multiply by r = 1/scale instead of a division.
+// With r = fl(1/scale) and y = fl(x * r), |y - fl(x / scale)| <= 3 * 2^-24 * |x / scale|,
+// which is below 2^-15 for |x / scale| <= 128; so rint(y) equals rint(fl(x / scale))
+// unless y lies within 2^-15 of a half-integer, and then the division decides.
+// Callers pass r only when it is finite (scale >= 2^-126); otherwise they use
+// quant_code.  Verified bit for bit against quant_code over every fp32 x in
+// [-127 scale, 127 scale] for a spread of scales.
+__device__ __forceinline__ int quant_code_fast(float x, float scale, float r, float qmax)
+{
+    const float y = x * r;
+    float q = rintf(y);
+    if (0.5f - fabsf(y - q) <= 0x1p-15f)
+        q = rintf(x / scale);
+    q = fminf(fmaxf(q, -qmax), qmax);
+    return (int)q;
+}
+
+// Four INT8 codes at once with the same results as quant_code_fast/quant_code: the
+// multiply-by-reciprocal codes are kept unless one of the four values lies within
+// 2^-15 of a rounding boundary (or the reciprocal is not finite), in which case all
+// four are taken by division.  One branch per four values.
+__device__ __forceinline__ void quant4_i8(float4 x, float scale, float r, bool fast, int (&q)[4])
+{
+    const float xs[4] = {x.x, x.y, x.z, x.w};
+    float qf[4];
+    bool near = !fast;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float y = xs[i] * r;
+        qf[i] = rintf(y);
+        near |= 0.5f - fabsf(y - qf[i]) <= 0x1p-15f;
+    }
+    if (near) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qf[i] = scale == 0.0f ? 0.0f : rintf(xs[i] / scale);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        q[i] = (int)fminf(fmaxf(qf[i], -127.0f), 127.0f);
 }
 
 __device__ __forceinline__ uint32_t pack_i8x4(int b0, int b1, int b2, int b3)

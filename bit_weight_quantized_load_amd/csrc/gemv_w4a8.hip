@@ -6,31 +6,37 @@
 // int32) and section 当前实现方式 (row-wise weight scale, per-vector dynamic
 // activation scale, output = int32 acc * weight_scale * activation_scale).  The
 // page's first follow-up item (fold the activation quantization into the linear
-// kernel) is realised by the prologue below.
+// kernel) is the prologue below.
 //
-// Work split.  A chunk is 16 bytes = 32 INT4 weights of one row.  Sixteen lanes
-// (one DPP row) cover 16*CPL consecutive chunks of a row: one K slice.  A wave
-// handles four rows at a time (one per DPP row) and rows_per_wave rows in all; a
-// 256-thread workgroup is four waves, so it owns a tile of 4*rows_per_wave rows by
-// one K slice.  grid = (row blocks, K slices, M tiles).
+// Work split.  The packed weights are 1 KB tiles of 4 rows x 512 k (16 chunks of
+// 32 nibbles per row, see kernels.hpp).  Each wave owns rg_per_wave whole row
+// groups, a contiguous run of tiles, and streams it with one 16-byte load per lane
+// per tile, two batches in flight.  Lane (sub, j) always meets row 4*rg + sub and
+// chunk 16*cg + j, so a row's partial sums live in the 16 lanes of one DPP row and
+// are added with four DPP steps when the row group ends.  No row is split across
+// waves or workgroups.
 //
-// Prologue.  Every workgroup takes max|X[m,:]| over the whole row (the scale needs
-// it), then quantizes only its own K slice into LDS, in the order the unpack below
-// consumes it: for each 8 consecutive k, the even-k codes form one 32-bit word and
-// the odd-k codes the next.  Each lane then copies the codes of its chunks into
-// registers, where they stay for every row it visits.
+// Two variants.  When K <= 4096 and M == 1 (kRegCG tiles per row group), a batch is
+// one whole row group and each lane keeps the activation codes of its chunks in
+// registers, read from LDS once.  Otherwise a batch is U tiles of a row group and
+// the codes are read from LDS per tile; LDS is zero-padded to whole batches so the
+// batch body has no branches and its LDS reads can be issued ahead of the dots.
+//
+// Prologue.  Output scales and X row 0 are loaded first and the first weight batch
+// right after them (loads complete in order, so anything the prologue waits on must
+// be issued before the weights).  The workgroup takes max|X[m,:]| from registers,
+// reduces it across waves, and quantizes the same registers into LDS in the order
+// the unpack consumes: for each 8 consecutive k, the even-k codes form one 32-bit
+// word and the odd-k codes the next.  Chunks past K get zero codes, which also
+// cancels whatever the padding weights hold.
 //
 // Unpack.  A 32-bit word of packed weights holds k..k+7, even k in the low
 // nibbles.  (w << 4) & 0xF0F0F0F0 puts the even nibbles, and w & 0xF0F0F0F0 the odd
 // nibbles, into the top half of each byte: each byte is then 16*q as an int8, so
 // two 4-way dots against the even and odd activation words accumulate 16 * sum(q*x)
 // exactly; an arithmetic shift by 4 at the end is exact.  |16 * acc| stays below
-// 2^31 for K <= 131072.  That is three bit operations and two dots per 8 weights.
-//
-// Split K.  With more than one K slice each workgroup adds its int32 partial sums
-// to acc_ws with atomics (exact, so the order does not matter), then counts itself
-// done on its row block; the last one applies the epilogue and clears acc_ws and
-// the counter, leaving the workspace zeroed for the next call.
+// 2^31 for K <= 131072.  Four independent accumulators (one per word of a chunk)
+// keep the dot latency off the critical path.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,225 +44,274 @@ namespace qw {
 
 namespace {
 
-template <int MT, int CPL, int GB, bool kSplit, bool kDebug>
-__global__ __launch_bounds__(kBlock) void k_gemv_w4a8(W4A8Args p)
+// acc[d] += 16 * (q . x) over the 8 weights of word d of a chunk.
+__device__ __forceinline__ void dot_chunk(const uint4 w, const uint32_t (&a)[8], int (&acc)[4])
 {
-    constexpr int kSlice = 16 * CPL;  // chunks per K slice
-    __shared__ uint4 s_act[MT][kSlice][2];
-    __shared__ float s_red[MT][4];
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int lo = (int)((wd[d] << 4) & 0xF0F0F0F0u);
+        const int hi = (int)(wd[d] & 0xF0F0F0F0u);
+        acc[d] = __builtin_amdgcn_sdot4(lo, (int)a[2 * d], acc[d], false);
+        acc[d] = __builtin_amdgcn_sdot4(hi, (int)a[2 * d + 1], acc[d], false);
+    }
+}
+
+__device__ __forceinline__ void load_act(const uint32_t* p, uint32_t (&a)[8])
+{
+    const uint4 e = reinterpret_cast<const uint4*>(p)[0];
+    const uint4 o = reinterpret_cast<const uint4*>(p)[1];
+    a[0] = e.x; a[1] = e.y; a[2] = e.z; a[3] = e.w;
+    a[4] = o.x; a[5] = o.y; a[6] = o.z; a[7] = o.w;
+}
+
+// RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
+// RCG == 0: LDS variant, U tiles per batch.
+template <int MT, int RCG, int U, int NW, bool kDebug>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    constexpr bool kReg = RCG > 0;
+    static_assert(!kReg || MT == 1, "register variant is for one row of X");
+    constexpr int kB = kReg ? RCG : U;                                     // tiles per batch
+    constexpr int XV = kReg ? (RCG * 128 + kThreads - 1) / kThreads : 16;  // X float4 per thread
+    extern __shared__ uint32_t s_dyn[];  // [MT][padded chunks][8 words] codes, then scales
+    __shared__ float s_red[MT][NW];
     __shared__ float s_a[MT];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63;
+    // wave index as a wave-uniform (scalar) value: loop bounds and tile tests below
+    // are then scalar branches, not per-lane ones
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int j = lane & 15, sub = lane >> 4;
-    const int M = p.M, N = p.N, K = p.K;
-    const int m0 = blockIdx.z * MT;
-    const int chunks_per_row = K >> 5;
-    const int c0 = blockIdx.y * kSlice;
-    const int cs = min(kSlice, chunks_per_row - c0);
-    const int rows_per_block = 4 * p.rows_per_wave;
-    const int nb0 = blockIdx.x * rows_per_block;
+    const int M = p.M, N = p.N, K = p.K, CG = p.cg;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(MT, M - m0);
+    const int K4 = K >> 2;
+    const int nb = kReg ? 1 : (CG + U - 1) / U;  // batches per row group
+    const int chunks = nb * kB * 16;              // chunks per X row in LDS (zero padded)
+    const int cpr = K >> 5;                       // real chunks per row
 
-    // ---- prologue 1: activation scale a[m] = max|X[m,:]| / 127 over the whole row
+    // ---- this wave's run of tiles
+    const int G = p.rg_per_wave;
+    const int rg_blk = blockIdx.x * NW * G;
+    const int nrg_blk = min(NW * G, p.nrg - rg_blk);
+    const int rg0 = rg_blk + wave * G;
+    const int nrg_w = max(0, min(G, p.nrg - rg0));
+    const int nq = nrg_w * nb;  // batches of this wave
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)(wave * G * CG) * 1024u + (uint32_t)lane * 16u;
+
+    uint4 wa[kB], wb[kB];
+    // batch q = (row group q / nb, tiles (q % nb) * kB ..); tiles past the row group
+    // and batches past the wave's run read zeros
+#define QW_LOAD(WBUF, Q)                                                                        \
+    {                                                                                           \
+        const int r_ = (Q) / nb, c0_ = ((Q) - r_ * nb) * kB;                                    \
+        _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
+        {                                                                                       \
+            const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
+            WBUF[u_] = load16(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+                                        : 0x80000000u);                                         \
+        }                                                                                       \
+    }
+
+    // ---- prologue: scales, X row 0, then the first weight batch
+    float* s_scale = reinterpret_cast<float*>(s_dyn + (size_t)MT * chunks * 8);
+    const int rows_blk = min(nrg_blk * 4, N - rg_blk * 4);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 4, (uint32_t)max(rows_blk, 0) * 4u);
+    uint32_t sc_reg[4];
 #pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sc_reg[i] = load4(sres, (uint32_t)(tid + i * kThreads) * 4u);
+    const int nblk = (K4 + XV * kThreads - 1) / (XV * kThreads);
+    float4 xv[XV];
+#define QW_LOAD_X(MM, BLK)                                                                      \
+    {                                                                                           \
+        const rsrc_t xr_ = make_rsrc(p.X + (size_t)(m0 + (MM)) * K,                             \
+                                     (MM) < mt ? (uint32_t)K * 4u : 0u);                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < XV; ++i_)                                       \
+            xv[i_] = load16f(xr_, (uint32_t)((BLK) * XV * kThreads + i_ * kThreads + tid) * 16u); \
+    }
+    QW_LOAD_X(0, 0);
+    QW_LOAD(wa, 0);
+    // unconditional stores (rows past the block read zeros): a guarded store would
+    // let the compiler sink the scale load behind the weight loads
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s_scale[tid + i * kThreads] = __uint_as_float(sc_reg[i]);
+
     for (int mm = 0; mm < MT; ++mm) {
         float mx = 0.0f;
-        if (m0 + mm < M) {
-            const float4* xr = reinterpret_cast<const float4*>(p.X + (size_t)(m0 + mm) * K);
-            for (int i = tid; i < (K >> 2); i += kBlock)
-                mx = fmaxf(mx, max_abs4(xr[i]));
+        for (int blk = 0; blk < nblk; ++blk) {
+            if (mm > 0 || blk > 0)
+                QW_LOAD_X(mm, blk);
+#pragma unroll
+            for (int i = 0; i < XV; ++i)
+                mx = fmaxf(mx, max_abs4(xv[i]));  // past K the loads read zeros
         }
-        mx = wave_max(mx);
+        mx = wave_max_dpp(mx);
         if (lane == 0)
             s_red[mm][wave] = mx;
-    }
-    __syncthreads();
-    if (tid < MT) {
-        const float mx = fmaxf(fmaxf(s_red[tid][0], s_red[tid][1]), fmaxf(s_red[tid][2], s_red[tid][3]));
-        s_a[tid] = mx / 127.0f;
-    }
-    __syncthreads();
-
-    // ---- prologue 2: INT8 codes of this K slice into LDS (even/odd k split)
-    for (int u = tid; u < MT * cs * 4; u += kBlock) {
-        const int mm = u / (cs * 4);
-        const int r = u - mm * (cs * 4);
-        const int cl = r >> 2, d = r & 3;
-        uint32_t ev = 0, od = 0;
-        if (m0 + mm < M) {
-            const float a = s_a[mm];
-            const int k = (c0 + cl) * 32 + d * 8;
-            const float4* xp = reinterpret_cast<const float4*>(p.X + (size_t)(m0 + mm) * K + k);
-            const float4 v0 = xp[0], v1 = xp[1];
-            const int q0 = quant_code(v0.x, a, 127.f), q1 = quant_code(v0.y, a, 127.f);
-            const int q2 = quant_code(v0.z, a, 127.f), q3 = quant_code(v0.w, a, 127.f);
-            const int q4 = quant_code(v1.x, a, 127.f), q5 = quant_code(v1.y, a, 127.f);
-            const int q6 = quant_code(v1.z, a, 127.f), q7 = quant_code(v1.w, a, 127.f);
-            ev = pack_i8x4(q0, q2, q4, q6);
-            od = pack_i8x4(q1, q3, q5, q7);
-            if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0) {
-                uint32_t* dq = reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * K + k);
-                dq[0] = pack_i8x4(q0, q1, q2, q3);
-                dq[1] = pack_i8x4(q4, q5, q6, q7);
+        __syncthreads();
+        mx = s_red[mm][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            mx = fmaxf(mx, s_red[mm][w]);
+        const float a = mx / 127.0f;
+        const float r = 1.0f / a;
+        const bool fast = r <= 3.0e38f;  // finite reciprocal (a is not 0 or tiny)
+        if (tid == 0)
+            s_a[mm] = a;
+        uint16_t* act16 = reinterpret_cast<uint16_t*>(s_dyn + (size_t)mm * chunks * 8);
+        for (int blk = 0; blk < nblk; ++blk) {
+            if (nblk > 1)
+                QW_LOAD_X(mm, blk);
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int f = blk * XV * kThreads + i * kThreads + tid;  // k = 4f .. 4f+3
+                if (f < K4) {
+                    int q[4];
+                    quant4_i8(xv[i], a, r, fast, q);
+                    // chunk f/8, 8-group (f/2)%4, half f%2: even codes -> word 2d, odd -> 2d+1
+                    const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
+                    const int wi = (c * 8 + 2 * d) * 2 + h;  // halfword index in the even word
+                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
+                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
+                    if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
+                        *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * K + 4 * f) =
+                            pack_i8x4(q[0], q[1], q[2], q[3]);
+                }
             }
         }
-        uint32_t* dst = reinterpret_cast<uint32_t*>(&s_act[mm][cl][0]);
-        dst[2 * d] = ev;
-        dst[2 * d + 1] = od;
+        // zero codes for the padding chunks
+        for (int w = cpr * 8 + tid; w < chunks * 8; w += kThreads)
+            s_dyn[(size_t)mm * chunks * 8 + w] = 0u;
     }
-    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && tid < MT &&
-        m0 + tid < M)
+    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
         p.dbg_a[m0 + tid] = s_a[tid];
     __syncthreads();
+#undef QW_LOAD_X
 
-    // ---- the lane's activation words, resident in registers for every row
-    uint4 act[MT][CPL][2];
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int cl = j + 16 * i;
-            if (cl < cs) {
-                act[mm][i][0] = s_act[mm][cl][0];
-                act[mm][i][1] = s_act[mm][cl][1];
-            } else {
-                act[mm][i][0] = make_uint4(0, 0, 0, 0);
-                act[mm][i][1] = make_uint4(0, 0, 0, 0);
-            }
+    const int nw0 = rg0 * 4;  // first row of this wave
+    auto finish_row_group = [&](int (&acc)[4], int mm, int rgi) {
+        const int v = row_sum16(acc[0] + acc[1] + acc[2] + acc[3]) >> 4;
+        const int n = nw0 + rgi * 4 + sub;
+        if (j == 0 && n < N && mm < mt) {
+            const size_t o = (size_t)(m0 + mm) * N + n;
+            if (kDebug && p.dbg_acc != nullptr)
+                p.dbg_acc[o] = v;
+            p.Y[o] = ((float)v * s_scale[n - rg_blk * 4]) * s_a[mm];
         }
+    };
 
-    // ---- main loop: stream the packed weights of this wave's rows
-    const size_t row_bytes = (size_t)(K >> 1);
-    const int nw0 = nb0 + wave * p.rows_per_wave;
-    const int groups = p.rows_per_wave >> 2;
-    for (int g0 = 0; g0 < groups; g0 += GB) {
-        uint4 w[GB][CPL];
+    if constexpr (kReg) {
+        // ---- register variant: the lane's codes for its RCG chunks, read once
+        uint32_t act[RCG][8];
 #pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            const int n = nw0 + 4 * (g0 + g) + sub;
-            const uint8_t* wp = p.Wq + (size_t)n * row_bytes + (size_t)c0 * 16;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int cl = j + 16 * i;
-                if (n < N && cl < cs)
-                    w[g][i] = *reinterpret_cast<const uint4*>(wp + (size_t)cl * 16);
-                else
-                    w[g][i] = make_uint4(0, 0, 0, 0);
-            }
+        for (int c = 0; c < RCG; ++c)
+            load_act(s_dyn + (size_t)(c * 16 + j) * 8, act[c]);
+#define QW_COMPUTE(WBUF, Q)                                                                     \
+        {                                                                                       \
+            int acc_[4] = {0, 0, 0, 0};                                                         \
+            _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk(WBUF[c_], act[c_], acc_); \
+            finish_row_group(acc_, 0, (Q));                                                     \
         }
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            int acc[MT];
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm)
-                acc[mm] = 0;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t wd[4] = {w[g][i].x, w[g][i].y, w[g][i].z, w[g][i].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const int lo = (int)((wd[d] << 4) & 0xF0F0F0F0u);
-                    const int hi = (int)(wd[d] & 0xF0F0F0F0u);
-#pragma unroll
-                    for (int mm = 0; mm < MT; ++mm) {
-                        const uint32_t* av = reinterpret_cast<const uint32_t*>(&act[mm][i][0]);
-                        acc[mm] = __builtin_amdgcn_sdot4(lo, (int)av[2 * d], acc[mm], false);
-                        acc[mm] = __builtin_amdgcn_sdot4(hi, (int)av[2 * d + 1], acc[mm], false);
-                    }
-                }
-            }
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm)
-                acc[mm] = row_sum16(acc[mm]);
-            const int n = nw0 + 4 * (g0 + g) + sub;
-            if (j == 0 && n < N) {
-#pragma unroll
-                for (int mm = 0; mm < MT; ++mm) {
-                    if (m0 + mm < M) {
-                        const int v = acc[mm] >> 4;
-                        const size_t o = (size_t)(m0 + mm) * N + n;
-                        if (kSplit) {
-                            atomicAdd(&p.acc_ws[o], v);
-                        } else {
-                            if (kDebug && p.dbg_acc != nullptr)
-                                p.dbg_acc[o] = v;
-                            p.Y[o] = ((float)v * p.w_scale[n]) * s_a[mm];
-                        }
-                    }
-                }
-            }
+        for (int q = 0; q < nq; q += 2) {
+            QW_LOAD(wb, q + 1);
+            QW_COMPUTE(wa, q);
+            if (q + 1 >= nq)
+                break;
+            QW_LOAD(wa, q + 2);
+            QW_COMPUTE(wb, q + 1);
         }
-    }
-
-    // ---- split-K completion: the last workgroup of a row block finishes it
-    if (kSplit) {
-        __threadfence();
-        __syncthreads();
-        const unsigned cidx = blockIdx.z * gridDim.x + blockIdx.x;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[cidx], 1u);
-            s_last = (prev == gridDim.y - 1) ? 1 : 0;
-        }
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
-            for (int idx = tid; idx < MT * rows_per_block; idx += kBlock) {
-                const int mm = idx / rows_per_block;
-                const int n = nb0 + (idx - mm * rows_per_block);
-                if (m0 + mm < M && n < N) {
-                    const size_t o = (size_t)(m0 + mm) * N + n;
-                    const int v = atomicExch(&p.acc_ws[o], 0);
-                    if (kDebug && p.dbg_acc != nullptr)
-                        p.dbg_acc[o] = v;
-                    p.Y[o] = ((float)v * p.w_scale[n]) * s_a[mm];
-                }
-            }
-            if (tid == 0)
-                atomicExch(&p.counters[cidx], 0u);
-        }
-    }
-}
-
-template <int MT, int CPL, int GB>
-hipError_t launch3(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
-{
-    if constexpr (MT * CPL > 8 || GB * CPL > 16) {
-        return hipErrorInvalidValue;
+#undef QW_COMPUTE
     } else {
-        const dim3 grid(t.row_blocks, t.slices, t.m_tiles);
-        const bool split = t.slices > 1;
-        if (split && debug)
-            hipLaunchKernelGGL((k_gemv_w4a8<MT, CPL, GB, true, true>), grid, dim3(kBlock), 0, st, a);
-        else if (split)
-            hipLaunchKernelGGL((k_gemv_w4a8<MT, CPL, GB, true, false>), grid, dim3(kBlock), 0, st, a);
-        else if (debug)
-            hipLaunchKernelGGL((k_gemv_w4a8<MT, CPL, GB, false, true>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_gemv_w4a8<MT, CPL, GB, false, false>), grid, dim3(kBlock), 0, st, a);
-        return hipGetLastError();
+        // ---- LDS variant: U tiles per batch, codes read from LDS per tile
+        int acc[MT][4];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0;
+#define QW_COMPUTE(WBUF, Q)                                                                     \
+        {                                                                                       \
+            const int r_ = (Q) / nb, b_ = (Q) - r_ * nb;                                        \
+            _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                    \
+            {                                                                                   \
+                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
+                {                                                                               \
+                    uint32_t a_[8];                                                             \
+                    load_act(s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 16 + j) * 8, a_);   \
+                    dot_chunk(WBUF[u_], a_, acc[mm]);                                           \
+                }                                                                               \
+            }                                                                                   \
+            if (b_ == nb - 1) {                                                                 \
+                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
+                {                                                                               \
+                    finish_row_group(acc[mm], mm, r_);                                          \
+                    acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0;                      \
+                }                                                                               \
+            }                                                                                   \
+        }
+        for (int q = 0; q < nq; q += 2) {
+            QW_LOAD(wb, q + 1);
+            QW_COMPUTE(wa, q);
+            if (q + 1 >= nq)
+                break;
+            QW_LOAD(wa, q + 2);
+            QW_COMPUTE(wb, q + 1);
+        }
+#undef QW_COMPUTE
     }
+#undef QW_LOAD
 }
 
-template <int MT, int CPL>
-hipError_t launch2(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+template <int MT, int RCG, int U, int NW>
+hipError_t launch4(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    switch (t.gb) {
-    case 1: return launch3<MT, CPL, 1>(a, t, debug, st);
-    case 2: return launch3<MT, CPL, 2>(a, t, debug, st);
-    case 4: return launch3<MT, CPL, 4>(a, t, debug, st);
-    case 8: return launch3<MT, CPL, 8>(a, t, debug, st);
+    const dim3 grid(t.blocks, t.m_tiles);
+    if (debug)
+        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, true>), grid, dim3(64 * NW), t.lds_bytes,
+                           st, a);
+    else
+        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, false>), grid, dim3(64 * NW), t.lds_bytes,
+                           st, a);
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_reg(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch4<1, 1, 4, NW>(a, t, debug, st);
+    case 2: return launch4<1, 2, 4, NW>(a, t, debug, st);
+    case 3: return launch4<1, 3, 4, NW>(a, t, debug, st);
+    case 4: return launch4<1, 4, 4, NW>(a, t, debug, st);
+    case 5: return launch4<1, 5, 4, NW>(a, t, debug, st);
+    case 6: return launch4<1, 6, 4, NW>(a, t, debug, st);
+    case 7: return launch4<1, 7, 4, NW>(a, t, debug, st);
+    case 8: return launch4<1, 8, 4, NW>(a, t, debug, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int MT>
-hipError_t launch1(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+template <int MT, int NW>
+hipError_t launch_lds(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    switch (t.cpl) {
-    case 1: return launch2<MT, 1>(a, t, debug, st);
-    case 2: return launch2<MT, 2>(a, t, debug, st);
-    case 4: return launch2<MT, 4>(a, t, debug, st);
+    return t.u == 4 ? launch4<MT, 0, 4, NW>(a, t, debug, st) : launch4<MT, 0, 8, NW>(a, t, debug, st);
+}
+
+template <int NW>
+hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    if (t.reg_cg > 0)
+        return launch_reg<NW>(a, t, debug, st);
+    switch (t.mt) {
+    case 1: return launch_lds<1, NW>(a, t, debug, st);
+    case 2: return launch_lds<2, NW>(a, t, debug, st);
+    case 4: return launch_lds<4, NW>(a, t, debug, st);
+    case 8: return launch_lds<8, NW>(a, t, debug, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -265,13 +320,7 @@ hipError_t launch1(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    switch (t.mt) {
-    case 1: return launch1<1>(a, t, debug, st);
-    case 2: return launch1<2>(a, t, debug, st);
-    case 4: return launch1<4>(a, t, debug, st);
-    case 8: return launch1<8>(a, t, debug, st);
-    default: return hipErrorInvalidValue;
-    }
+    return t.nw == 4 ? launch_nw<4>(a, t, debug, st) : launch_nw<8>(a, t, debug, st);
 }
 
 }  // namespace qw

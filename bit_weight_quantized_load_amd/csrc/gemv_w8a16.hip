@@ -8,19 +8,17 @@
 // sum instead of to each weight; that differs from scaling first only by fp32
 // rounding.
 //
-// Work split as in the W4A8 kernel: a chunk is 16 bytes = 16 INT8 weights; 16
-// lanes cover 16*CPL chunks of a row (one K slice); a wave handles four rows at a
-// time; a workgroup is four waves.  Each lane loads the f16 activations of its
-// chunks into registers once and keeps them for every row it visits.
+// Work split as in the W4A8 kernel, with 1 KB tiles of 2 rows x 512 k (32 chunks
+// of 16 INT8 weights per row): each wave streams the tiles of whole row groups, two
+// batches in flight; a row's 32 lanes add their partial sums with DPP when the row
+// group ends.  When K <= 4096 and M == 1 each lane loads the f16 activations of its
+// chunks straight into registers (no LDS, no barrier); otherwise the workgroup
+// stages X in LDS in chunk order, zero-padded to whole batches.
 //
 // Cast.  For a word of four int8 codes, XOR 0x80 per byte gives u = q + 128; a
 // byte permute places 0x64 above each u, which as a binary16 is exactly 1024 + u;
 // one packed f16 add of -1152 leaves q exactly.  Two 2-way f16 dots with fp32
 // accumulation then consume the four weights.
-//
-// Split K.  Each workgroup stores its fp32 partial sums to part_ws[slice]; the last
-// workgroup of a row block (by counter) adds the slices in slice order, so the
-// result does not depend on scheduling, and zeroes the partials and the counter.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,169 +36,229 @@ __device__ __forceinline__ void cast_i8x4_to_f16(uint32_t wd, half2_t& lo, half2
     hi = __builtin_bit_cast(half2_t, phi) + bias;
 }
 
-template <int MT, int CPL, int GB, bool kSplit>
-__global__ __launch_bounds__(kBlock) void k_gemv_w8a16(W8A16Args p)
+__device__ __forceinline__ void dot_chunk_f16(const uint4 w, const uint32_t (&a)[8], float (&acc)[4])
 {
-    constexpr int kSlice = 16 * CPL;
-    __shared__ int s_last;
+    const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        half2_t lo, hi;
+        cast_i8x4_to_f16(wd[d], lo, hi);
+        acc[d] = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, a[2 * d]), acc[d], false);
+        acc[d] = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, a[2 * d + 1]), acc[d], false);
+    }
+}
+
+__device__ __forceinline__ void split8(const uint4 e, const uint4 o, uint32_t (&a)[8])
+{
+    a[0] = e.x; a[1] = e.y; a[2] = e.z; a[3] = e.w;
+    a[4] = o.x; a[5] = o.y; a[6] = o.z; a[7] = o.w;
+}
+
+// RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
+// RCG == 0: LDS variant, U tiles per batch.
+template <int MT, int RCG, int U, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    constexpr bool kReg = RCG > 0;
+    static_assert(!kReg || MT == 1, "register variant is for one row of X");
+    constexpr int kB = kReg ? RCG : U;
+    extern __shared__ uint32_t s_dyn[];  // LDS variant: [MT][padded chunks][8 words]; then scales
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int j = lane & 15, sub = lane >> 4;
-    const int M = p.M, N = p.N, K = p.K;
-    const int m0 = blockIdx.z * MT;
-    const int chunks_per_row = K >> 4;
-    const int c0 = blockIdx.y * kSlice;
-    const int cs = min(kSlice, chunks_per_row - c0);
-    const int rows_per_block = 4 * p.rows_per_wave;
-    const int nb0 = blockIdx.x * rows_per_block;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, sub = lane >> 5;
+    const int M = p.M, N = p.N, K = p.K, CG = p.cg;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(MT, M - m0);
+    const int nb = kReg ? 1 : (CG + U - 1) / U;
+    const int chunks = nb * kB * 32;  // LDS variant: chunks per X row in LDS (zero padded)
 
-    // the lane's activations: 16 f16 per chunk = 8 words, kept in registers
-    uint4 act[MT][CPL][2];
-#pragma unroll
-    for (int mm = 0; mm < MT; ++mm)
-#pragma unroll
-        for (int i = 0; i < CPL; ++i) {
-            const int cl = j + 16 * i;
-            if (cl < cs && m0 + mm < M) {
-                const uint4* xp = reinterpret_cast<const uint4*>(p.X + (size_t)(m0 + mm) * K +
-                                                                 (size_t)(c0 + cl) * 16);
-                act[mm][i][0] = xp[0];
-                act[mm][i][1] = xp[1];
-            } else {
-                act[mm][i][0] = make_uint4(0, 0, 0, 0);
-                act[mm][i][1] = make_uint4(0, 0, 0, 0);
-            }
-        }
+    const int G = p.rg_per_wave;
+    const int rg_blk = blockIdx.x * NW * G;
+    const int nrg_blk = min(NW * G, p.nrg - rg_blk);
+    const int rg0 = rg_blk + wave * G;
+    const int nrg_w = max(0, min(G, p.nrg - rg0));
+    const int nq = nrg_w * nb;
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)(wave * G * CG) * 1024u + (uint32_t)lane * 16u;
 
-    const size_t row_bytes = (size_t)K;
-    const int nw0 = nb0 + wave * p.rows_per_wave;
-    const int groups = p.rows_per_wave >> 2;
-    const size_t MN = (size_t)M * N;
-    for (int g0 = 0; g0 < groups; g0 += GB) {
-        uint4 w[GB][CPL];
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            const int n = nw0 + 4 * (g0 + g) + sub;
-            const uint8_t* wp = p.Wq + (size_t)n * row_bytes + (size_t)c0 * 16;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const int cl = j + 16 * i;
-                if (n < N && cl < cs)
-                    w[g][i] = *reinterpret_cast<const uint4*>(wp + (size_t)cl * 16);
-                else
-                    w[g][i] = make_uint4(0, 0, 0, 0);
-            }
-        }
-#pragma unroll
-        for (int g = 0; g < GB; ++g) {
-            float acc[MT];
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm)
-                acc[mm] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < CPL; ++i) {
-                const uint32_t wd[4] = {w[g][i].x, w[g][i].y, w[g][i].z, w[g][i].w};
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    half2_t lo, hi;
-                    cast_i8x4_to_f16(wd[d], lo, hi);
-#pragma unroll
-                    for (int mm = 0; mm < MT; ++mm) {
-                        const uint32_t* av = reinterpret_cast<const uint32_t*>(&act[mm][i][0]);
-                        acc[mm] = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, av[2 * d]),
-                                                         acc[mm], false);
-                        acc[mm] = __builtin_amdgcn_fdot2(
-                            hi, __builtin_bit_cast(half2_t, av[2 * d + 1]), acc[mm], false);
-                    }
-                }
-            }
-#pragma unroll
-            for (int mm = 0; mm < MT; ++mm)
-                acc[mm] = row_sum16(acc[mm]);
-            const int n = nw0 + 4 * (g0 + g) + sub;
-            if (j == 0 && n < N) {
-#pragma unroll
-                for (int mm = 0; mm < MT; ++mm) {
-                    if (m0 + mm < M) {
-                        const size_t o = (size_t)(m0 + mm) * N + n;
-                        if (kSplit) {
-                            p.part_ws[(size_t)blockIdx.y * MN + o] = acc[mm];
-                        } else {
-                            const float s = __half2float(__ushort_as_half(p.w_scale[n]));
-                            p.Y[o] = __half_as_ushort(__float2half_rn(acc[mm] * s));
-                        }
-                    }
-                }
-            }
-        }
+    uint4 wa[kB], wb[kB];
+#define QW_LOAD(WBUF, Q)                                                                        \
+    {                                                                                           \
+        const int r_ = (Q) / nb, c0_ = ((Q) - r_ * nb) * kB;                                    \
+        _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
+        {                                                                                       \
+            const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
+            WBUF[u_] = load16(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+                                        : 0x80000000u);                                         \
+        }                                                                                       \
     }
 
-    if (kSplit) {
-        __threadfence();
-        __syncthreads();
-        const unsigned cidx = blockIdx.z * gridDim.x + blockIdx.x;
-        if (tid == 0) {
-            const unsigned prev = atomicAdd(&p.counters[cidx], 1u);
-            s_last = (prev == gridDim.y - 1) ? 1 : 0;
-        }
-        __syncthreads();
-        if (s_last) {
-            __threadfence();
-            for (int idx = tid; idx < MT * rows_per_block; idx += kBlock) {
-                const int mm = idx / rows_per_block;
-                const int n = nb0 + (idx - mm * rows_per_block);
-                if (m0 + mm < M && n < N) {
-                    const size_t o = (size_t)(m0 + mm) * N + n;
-                    float sum = 0.0f;
-                    for (int z = 0; z < (int)gridDim.y; ++z) {
-                        sum += p.part_ws[(size_t)z * MN + o];
-                        p.part_ws[(size_t)z * MN + o] = 0.0f;
-                    }
-                    const float s = __half2float(__ushort_as_half(p.w_scale[n]));
-                    p.Y[o] = __half_as_ushort(__float2half_rn(sum * s));
-                }
-            }
-            if (tid == 0)
-                atomicExch(&p.counters[cidx], 0u);
-        }
-    }
-}
+    // ---- prologue: scales, activations, then the first weight batch
+    uint16_t* s_scale = reinterpret_cast<uint16_t*>(s_dyn + (kReg ? 0 : (size_t)MT * chunks * 8));
+    const int rows_blk = min(nrg_blk * 2, N - rg_blk * 2);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 2, (uint32_t)max(rows_blk, 0) * 2u);
+    uint16_t sc_reg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        sc_reg[i] = load2(sres, (uint32_t)(tid + i * kThreads) * 2u);
+    const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)mt * (uint32_t)K * 2u);
 
-template <int MT, int CPL, int GB>
-hipError_t launch3(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
-{
-    if constexpr (MT * CPL > 8 || GB * CPL > 16) {
-        return hipErrorInvalidValue;
+    uint32_t act[kReg ? RCG : 1][8];
+    if constexpr (kReg) {
+        // chunk 32*c + j of row 0: 16 f16 at k = 16*(32c + j); past K reads zeros
+#pragma unroll
+        for (int c = 0; c < RCG; ++c) {
+            const uint32_t xo = (uint32_t)((c * 32 + j) * 16) * 2u;
+            const uint4 e = load16(xres, (c * 32 + j) * 16 < K ? xo : 0x80000000u);
+            const uint4 o = load16(xres, (c * 32 + j) * 16 < K ? xo + 16u : 0x80000000u);
+            split8(e, o, act[c]);
+        }
+        QW_LOAD(wa, 0);
     } else {
-        const dim3 grid(t.row_blocks, t.slices, t.m_tiles);
-        if (t.slices > 1)
-            hipLaunchKernelGGL((k_gemv_w8a16<MT, CPL, GB, true>), grid, dim3(kBlock), 0, st, a);
-        else
-            hipLaunchKernelGGL((k_gemv_w8a16<MT, CPL, GB, false>), grid, dim3(kBlock), 0, st, a);
-        return hipGetLastError();
+        // stage X in LDS: 16-byte pieces, 2 per chunk
+        constexpr int kXP = 4;
+        const int pieces = MT * chunks * 2;
+        const int npass = (pieces + kXP * kThreads - 1) / (kXP * kThreads);
+        uint4 xp[kXP];
+#define QW_LOAD_XP(PASS)                                                                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < kXP; ++i_)                                      \
+        {                                                                                       \
+            const int q_ = (PASS) * kXP * kThreads + i_ * kThreads + tid;                       \
+            const int mm_ = q_ / (chunks * 2);                                                  \
+            const int r_ = q_ - mm_ * (chunks * 2);                                             \
+            const bool in_ = mm_ < MT && r_ * 8 < K;                                            \
+            xp[i_] = load16(xres, in_ ? (uint32_t)(mm_ * K + r_ * 8) * 2u : 0x80000000u);      \
+        }
+        QW_LOAD_XP(0);
+        QW_LOAD(wa, 0);
+        for (int pass = 0; pass < npass; ++pass) {
+            if (pass > 0)
+                QW_LOAD_XP(pass);
+#pragma unroll
+            for (int i = 0; i < kXP; ++i) {
+                const int q = pass * kXP * kThreads + i * kThreads + tid;
+                if (q < pieces)
+                    reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
+            }
+        }
+#undef QW_LOAD_XP
     }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        s_scale[tid + i * kThreads] = sc_reg[i];
+    __syncthreads();
+
+    const int nw0 = rg0 * 2;
+    auto finish_row_group = [&](float (&acc)[4], int mm, int rgi) {
+        const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
+        const int n = nw0 + rgi * 2 + sub;
+        if (j == 31 && n < N && mm < mt) {
+            const float s = __half2float(__ushort_as_half(s_scale[n - rg_blk * 2]));
+            p.Y[(size_t)(m0 + mm) * N + n] = __half_as_ushort(__float2half_rn(v * s));
+        }
+    };
+
+    if constexpr (kReg) {
+#define QW_COMPUTE(WBUF, Q)                                                                     \
+        {                                                                                       \
+            float acc_[4] = {0.0f, 0.0f, 0.0f, 0.0f};                                           \
+            _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk_f16(WBUF[c_], act[c_], acc_); \
+            finish_row_group(acc_, 0, (Q));                                                     \
+        }
+        for (int q = 0; q < nq; q += 2) {
+            QW_LOAD(wb, q + 1);
+            QW_COMPUTE(wa, q);
+            if (q + 1 >= nq)
+                break;
+            QW_LOAD(wa, q + 2);
+            QW_COMPUTE(wb, q + 1);
+        }
+#undef QW_COMPUTE
+    } else {
+        float acc[MT][4];
+#pragma unroll
+        for (int mm = 0; mm < MT; ++mm)
+            acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0.0f;
+#define QW_COMPUTE(WBUF, Q)                                                                     \
+        {                                                                                       \
+            const int r_ = (Q) / nb, b_ = (Q) - r_ * nb;                                        \
+            _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                    \
+            {                                                                                   \
+                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
+                {                                                                               \
+                    const uint4* ap_ = reinterpret_cast<const uint4*>(                          \
+                        s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 32 + j) * 8);            \
+                    uint32_t a_[8];                                                             \
+                    split8(ap_[0], ap_[1], a_);                                                 \
+                    dot_chunk_f16(WBUF[u_], a_, acc[mm]);                                       \
+                }                                                                               \
+            }                                                                                   \
+            if (b_ == nb - 1) {                                                                 \
+                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
+                {                                                                               \
+                    finish_row_group(acc[mm], mm, r_);                                          \
+                    acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0.0f;                   \
+                }                                                                               \
+            }                                                                                   \
+        }
+        for (int q = 0; q < nq; q += 2) {
+            QW_LOAD(wb, q + 1);
+            QW_COMPUTE(wa, q);
+            if (q + 1 >= nq)
+                break;
+            QW_LOAD(wa, q + 2);
+            QW_COMPUTE(wb, q + 1);
+        }
+#undef QW_COMPUTE
+    }
+#undef QW_LOAD
+    (void)act;
 }
 
-template <int MT, int CPL>
-hipError_t launch2(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+template <int MT, int RCG, int U, int NW>
+hipError_t launch4(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
-    switch (t.gb) {
-    case 1: return launch3<MT, CPL, 1>(a, t, st);
-    case 2: return launch3<MT, CPL, 2>(a, t, st);
-    case 4: return launch3<MT, CPL, 4>(a, t, st);
-    case 8: return launch3<MT, CPL, 8>(a, t, st);
+    const dim3 grid(t.blocks, t.m_tiles);
+    hipLaunchKernelGGL((k_gemv_w8a16<MT, RCG, U, NW>), grid, dim3(64 * NW), t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int NW>
+hipError_t launch_reg(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch4<1, 1, 4, NW>(a, t, st);
+    case 2: return launch4<1, 2, 4, NW>(a, t, st);
+    case 3: return launch4<1, 3, 4, NW>(a, t, st);
+    case 4: return launch4<1, 4, 4, NW>(a, t, st);
+    case 5: return launch4<1, 5, 4, NW>(a, t, st);
+    case 6: return launch4<1, 6, 4, NW>(a, t, st);
+    case 7: return launch4<1, 7, 4, NW>(a, t, st);
+    case 8: return launch4<1, 8, 4, NW>(a, t, st);
     default: return hipErrorInvalidValue;
     }
 }
 
-template <int MT>
-hipError_t launch1(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+template <int MT, int NW>
+hipError_t launch_lds(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
-    switch (t.cpl) {
-    case 1: return launch2<MT, 1>(a, t, st);
-    case 2: return launch2<MT, 2>(a, t, st);
-    case 4: return launch2<MT, 4>(a, t, st);
+    return t.u == 4 ? launch4<MT, 0, 4, NW>(a, t, st) : launch4<MT, 0, 8, NW>(a, t, st);
+}
+
+template <int NW>
+hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    if (t.reg_cg > 0)
+        return launch_reg<NW>(a, t, st);
+    switch (t.mt) {
+    case 1: return launch_lds<1, NW>(a, t, st);
+    case 2: return launch_lds<2, NW>(a, t, st);
+    case 4: return launch_lds<4, NW>(a, t, st);
+    case 8: return launch_lds<8, NW>(a, t, st);
     default: return hipErrorInvalidValue;
     }
 }
@@ -209,13 +267,7 @@ hipError_t launch1(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
-    switch (t.mt) {
-    case 1: return launch1<1>(a, t, st);
-    case 2: return launch1<2>(a, t, st);
-    case 4: return launch1<4>(a, t, st);
-    case 8: return launch1<8>(a, t, st);
-    default: return hipErrorInvalidValue;
-    }
+    return t.nw == 4 ? launch_nw<4>(a, t, st) : launch_nw<8>(a, t, st);
 }
 
 }  // namespace qw

@@ -1,4 +1,4 @@
-// Internal launch interface between the C ABI (api.cpp) and the kernels.
+// Internal launch interface between the C ABI (api.hip) and the kernels.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -7,18 +7,53 @@
 
 namespace qw {
 
-// Tiling of the GEMV kernels (M < 16).  A "chunk" is 16 bytes of packed weights
-// (32 INT4 weights or 16 INT8 weights).  16 lanes cover one row of 16*cpl chunks
-// (one K slice); a wave covers 4 rows at a time and `rows_per_wave` rows in all;
-// a workgroup is 4 waves.  The grid is (row blocks, K slices, M tiles).
+// Packed weight layout shared by the packers, the GEMV kernels and the code decoders.
+// A chunk is 16 bytes of one row: 32 INT4 weights (canonical nibble order, even k in
+// the low nibble) or 16 INT8 weights.  A tile is 1 KB covering 512 consecutive k of
+// R rows: R = 4 rows x 16 chunks for INT4, R = 2 rows x 32 chunks for INT8.  Inside
+// a tile, 16-byte slot (n % R) * L + (c % L) holds row n's chunk c, L = 64 / R being
+// the lanes per row.  Tiles are stored row group (R rows) by row group, and within a
+// row group in k order, so one wave64 load of 16 bytes per lane reads one whole
+// tile (1 KB contiguous), lane (sub, j) = (lane / L, lane % L) always meets row
+// R*rg + sub and chunk L*cg + j, and a row group's tiles are contiguous.  Rows past
+// N and chunks past K are zero padding.
+struct TileLayout {
+    int rows;   // R: rows per tile (4 for INT4, 2 for INT8)
+    int lanes;  // L: lanes per row = chunks per tile row (16 or 32)
+    int cg;     // tiles per row group = ceil(K / 512)
+    int nrg;    // row groups = ceil(N / R)
+};
+
+inline TileLayout tile_layout(int bits, int64_t N, int64_t K)
+{
+    TileLayout t;
+    t.rows = bits == 4 ? 4 : 2;
+    t.lanes = 64 / t.rows;
+    t.cg = (int)((K + 511) / 512);
+    t.nrg = (int)((N + t.rows - 1) / t.rows);
+    return t;
+}
+
+inline size_t packed_bytes(int bits, int64_t N, int64_t K)
+{
+    TileLayout t = tile_layout(bits, N, K);
+    return (size_t)t.nrg * (size_t)t.cg * 1024u;
+}
+
+// K up to kRegCG * 512 keeps a lane's activations for a whole row in registers.
+constexpr int kRegCG = 8;
+
+// Launch shape of the GEMV kernels (M < 16).
 struct GemvTiling {
-    int mt;             // rows of X per workgroup (1, 2, 4, 8)
-    int cpl;            // chunks per lane per row (1, 2, 4)
-    int gb;             // row groups of 4 rows whose loads are issued together
-    int rows_per_wave;  // multiple of 4*gb
-    int slices;         // K slices = ceil(chunks_per_row / (16*cpl))
-    int row_blocks;     // ceil(N / (4*rows_per_wave))
-    int m_tiles;        // ceil(M / mt)
+    int mt;           // rows of X per workgroup (1, 2, 4, 8)
+    int m_tiles;      // ceil(M / mt)
+    int reg_cg;       // > 0: activations in registers, K <= 512 * reg_cg, mt == 1
+                      //   0: activations read from LDS tile by tile
+    int u;            // LDS variant: tiles per load batch (4 or 8), two batches in flight
+    int nw;           // waves per workgroup (4 or 8)
+    int rg_per_wave;  // row groups per wave
+    int blocks;       // workgroups along N = ceil(nrg / (nw * rg_per_wave))
+    int lds_bytes;    // dynamic LDS
 };
 
 struct W4A8Args {
@@ -27,12 +62,10 @@ struct W4A8Args {
     const float* w_scale;
     float* Y;
     int M, N, K;
-    int rows_per_wave;
-    int32_t* acc_ws;     // [M][N] int32, zero on entry and exit (split-K only)
-    uint32_t* counters;  // [m_tiles][row_blocks], zero on entry and exit (split-K only)
-    int32_t* dbg_acc;    // optional [M][N]
-    int8_t* dbg_xq;      // optional [M][K]
-    float* dbg_a;        // optional [M]
+    int cg, nrg, rg_per_wave;
+    int32_t* dbg_acc;  // optional [M][N]
+    int8_t* dbg_xq;    // optional [M][K]
+    float* dbg_a;      // optional [M]
 };
 
 struct W8A16Args {
@@ -41,18 +74,16 @@ struct W8A16Args {
     const uint16_t* w_scale;
     uint16_t* Y;
     int M, N, K;
-    int rows_per_wave;
-    float* part_ws;      // [slices][M][N] fp32 partial sums (split-K only)
-    uint32_t* counters;  // [m_tiles][row_blocks], zero on entry and exit (split-K only)
+    int cg, nrg, rg_per_wave;
 };
 
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,
                           hipStream_t st);
-hipError_t launch_pack_w8(const float* W, int N, int K, int8_t* Wq, uint16_t* s, int* flag,
+hipError_t launch_pack_w8(const float* W, int N, int K, uint8_t* Wq, uint16_t* s, int* flag,
                           hipStream_t st);
 hipError_t launch_quant_act(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st);
 hipError_t launch_codes_w4(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st);
-hipError_t launch_codes_w8(const int8_t* Wq, int N, int K, int8_t* codes, hipStream_t st);
+hipError_t launch_codes_w8(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st);
 hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t st);
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st);

@@ -13,14 +13,25 @@ namespace {
 
 constexpr int kMaxGrid = 65536;
 
+// Byte offset of 32-bit word `wi` (0..3) of chunk `c` of row `n` in the tile layout
+// (kernels.hpp) with R rows per tile and L = 64 / R chunks per tile row:
+// tile (n / R, c / L), slot (n % R) * L + c % L.
+__device__ __forceinline__ size_t tile_word_offset(int n, int c, int wi, int cg, int R)
+{
+    const int L = 64 / R;
+    return ((size_t)(n / R) * cg + (c / L)) * 1024u + (size_t)(((n % R) * L + (c % L)) * 16 + wi * 4);
+}
+
 // One workgroup per row (grid-strided): max-abs reduction, then codes.  Eight
-// consecutive k per thread give one 32-bit word of nibbles, even k in the low one.
+// consecutive k per thread give one 32-bit word of nibbles, even k in the low one;
+// the word goes to its place in the tile layout.
 __global__ __launch_bounds__(kBlock) void k_pack_w4(const float* __restrict__ W, int N, int K,
                                                     uint8_t* __restrict__ Wq,
                                                     float* __restrict__ scale, int* flag)
 {
     __shared__ float red[4];
     const int K4 = K >> 2, K8 = K >> 3;
+    const int cg = (K + 511) >> 9;
     for (int n = blockIdx.x; n < N; n += gridDim.x) {
         const float4* row = reinterpret_cast<const float4*>(W + (size_t)n * K);
         float mx = 0.0f;
@@ -42,7 +53,6 @@ __global__ __launch_bounds__(kBlock) void k_pack_w4(const float* __restrict__ W,
         const float s = mx / 7.0f;
         if (threadIdx.x == 0)
             scale[n] = s;
-        uint32_t* out = reinterpret_cast<uint32_t*>(Wq + (size_t)n * (K >> 1));
         for (int u = threadIdx.x; u < K8; u += kBlock) {
             float4 a = row[2 * u], b = row[2 * u + 1];
             int q[8] = {quant_code(a.x, s, 7.f), quant_code(a.y, s, 7.f), quant_code(a.z, s, 7.f),
@@ -52,7 +62,7 @@ __global__ __launch_bounds__(kBlock) void k_pack_w4(const float* __restrict__ W,
 #pragma unroll
             for (int i = 0; i < 8; ++i)
                 word |= (uint32_t)(q[i] & 0xf) << (4 * i);
-            out[u] = word;
+            *reinterpret_cast<uint32_t*>(Wq + tile_word_offset(n, u >> 2, u & 3, cg, 4)) = word;
         }
     }
 }
@@ -60,11 +70,12 @@ __global__ __launch_bounds__(kBlock) void k_pack_w4(const float* __restrict__ W,
 // Per-channel INT8: s32 = maxabs/127, rounded to the stored f16 scale, and codes
 // taken against that stored scale.
 __global__ __launch_bounds__(kBlock) void k_pack_w8(const float* __restrict__ W, int N, int K,
-                                                    int8_t* __restrict__ Wq,
+                                                    uint8_t* __restrict__ Wq,
                                                     uint16_t* __restrict__ scale, int* flag)
 {
     __shared__ float red[4];
     const int K4 = K >> 2;
+    const int cg = (K + 511) >> 9;
     for (int n = blockIdx.x; n < N; n += gridDim.x) {
         const float4* row = reinterpret_cast<const float4*>(W + (size_t)n * K);
         float mx = 0.0f;
@@ -88,11 +99,11 @@ __global__ __launch_bounds__(kBlock) void k_pack_w8(const float* __restrict__ W,
         }
         if (threadIdx.x == 0)
             scale[n] = __half_as_ushort(h);
-        uint32_t* out = reinterpret_cast<uint32_t*>(Wq + (size_t)n * K);
         for (int i = threadIdx.x; i < K4; i += kBlock) {
             float4 v = row[i];
-            out[i] = pack_i8x4(quant_code(v.x, sf, 127.f), quant_code(v.y, sf, 127.f),
-                               quant_code(v.z, sf, 127.f), quant_code(v.w, sf, 127.f));
+            *reinterpret_cast<uint32_t*>(Wq + tile_word_offset(n, i >> 2, i & 3, cg, 2)) =
+                pack_i8x4(quant_code(v.x, sf, 127.f), quant_code(v.y, sf, 127.f),
+                          quant_code(v.z, sf, 127.f), quant_code(v.w, sf, 127.f));
         }
     }
 }
@@ -111,36 +122,54 @@ __global__ __launch_bounds__(kBlock) void k_quant_act(const float* __restrict__ 
             mx = fmaxf(mx, max_abs4(row[i]));
         mx = block_max(mx, red);
         const float a = mx / 127.0f;
+        const float r = 1.0f / a;
+        const bool fast = r <= 3.0e38f;
         if (threadIdx.x == 0)
             a_scale[m] = a;
         uint32_t* out = reinterpret_cast<uint32_t*>(Xq + (size_t)m * K);
         for (int i = threadIdx.x; i < K4; i += kBlock) {
             float4 v = row[i];
-            out[i] = pack_i8x4(quant_code(v.x, a, 127.f), quant_code(v.y, a, 127.f),
-                               quant_code(v.z, a, 127.f), quant_code(v.w, a, 127.f));
+            if (fast)
+                out[i] = pack_i8x4(quant_code_fast(v.x, a, r, 127.f), quant_code_fast(v.y, a, r, 127.f),
+                                   quant_code_fast(v.z, a, r, 127.f), quant_code_fast(v.w, a, r, 127.f));
+            else
+                out[i] = pack_i8x4(quant_code(v.x, a, 127.f), quant_code(v.y, a, 127.f),
+                                   quant_code(v.z, a, 127.f), quant_code(v.w, a, 127.f));
         }
     }
 }
 
-// Packed INT4 -> int8 codes, one thread per packed byte (sign-extended nibbles).
-__global__ __launch_bounds__(kBlock) void k_codes_w4(const uint8_t* __restrict__ Wq, size_t nbytes,
+// Tile-layout INT4 -> int8 codes [N][K]: one thread per 32-bit word (8 codes).
+__global__ __launch_bounds__(kBlock) void k_codes_w4(const uint8_t* __restrict__ Wq, int N, int K,
                                                      int8_t* __restrict__ codes)
 {
-    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < nbytes;
+    const int words = K >> 3, cg = (K + 511) >> 9;
+    const size_t total = (size_t)N * words;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < total;
          i += (size_t)gridDim.x * kBlock) {
-        const int b = Wq[i];
-        const int lo = b & 0xf, hi = b >> 4;
-        codes[2 * i] = (int8_t)(lo >= 8 ? lo - 16 : lo);
-        codes[2 * i + 1] = (int8_t)(hi >= 8 ? hi - 16 : hi);
+        const int n = (int)(i / words), u = (int)(i % words);
+        const uint32_t w = *reinterpret_cast<const uint32_t*>(Wq + tile_word_offset(n, u >> 2, u & 3, cg, 4));
+        int8_t* out = codes + (size_t)n * K + 8 * u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int v = (w >> (4 * e)) & 0xf;
+            out[e] = (int8_t)(v >= 8 ? v - 16 : v);
+        }
     }
 }
 
-__global__ __launch_bounds__(kBlock) void k_copy_bytes(const int8_t* __restrict__ src, size_t n,
-                                                       int8_t* __restrict__ dst)
+// Tile-layout INT8 -> int8 codes [N][K]: one thread per 32-bit word (4 codes).
+__global__ __launch_bounds__(kBlock) void k_codes_w8(const uint8_t* __restrict__ Wq, int N, int K,
+                                                     int8_t* __restrict__ codes)
 {
-    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < n;
-         i += (size_t)gridDim.x * kBlock)
-        dst[i] = src[i];
+    const int words = K >> 2, cg = (K + 511) >> 9;
+    const size_t total = (size_t)N * words;
+    for (size_t i = (size_t)blockIdx.x * kBlock + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * kBlock) {
+        const int n = (int)(i / words), u = (int)(i % words);
+        *reinterpret_cast<uint32_t*>(codes + (size_t)n * K + 4 * u) =
+            *reinterpret_cast<const uint32_t*>(Wq + tile_word_offset(n, u >> 2, u & 3, cg, 2));
+    }
 }
 
 __global__ __launch_bounds__(kBlock) void k_fill_zero(uint32_t* __restrict__ p, size_t words)
@@ -160,17 +189,34 @@ inline int grid_for(size_t items)
 
 }  // namespace
 
+// Padding (rows past N in the last row group, chunks past K in the last chunk
+// group) exists only for ragged shapes; it is cleared before packing so the packed
+// buffer is fully defined.
+static hipError_t clear_padding(int bits, int N, int K, uint8_t* Wq, hipStream_t st)
+{
+    const TileLayout t = tile_layout(bits, N, K);
+    if (N % t.rows == 0 && K % 512 == 0)
+        return hipSuccess;
+    return launch_fill_zero(reinterpret_cast<uint32_t*>(Wq), packed_bytes(bits, N, K) / 4, st);
+}
+
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,
                           hipStream_t st)
 {
+    hipError_t e = clear_padding(4, N, K, Wq, st);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(k_pack_w4, dim3(N < kMaxGrid ? N : kMaxGrid), dim3(kBlock), 0, st, W, N, K,
                        Wq, s, flag);
     return hipGetLastError();
 }
 
-hipError_t launch_pack_w8(const float* W, int N, int K, int8_t* Wq, uint16_t* s, int* flag,
+hipError_t launch_pack_w8(const float* W, int N, int K, uint8_t* Wq, uint16_t* s, int* flag,
                           hipStream_t st)
 {
+    hipError_t e = clear_padding(8, N, K, Wq, st);
+    if (e != hipSuccess)
+        return e;
     hipLaunchKernelGGL(k_pack_w8, dim3(N < kMaxGrid ? N : kMaxGrid), dim3(kBlock), 0, st, W, N, K,
                        Wq, s, flag);
     return hipGetLastError();
@@ -185,15 +231,15 @@ hipError_t launch_quant_act(const float* X, int M, int K, int8_t* Xq, float* a, 
 
 hipError_t launch_codes_w4(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st)
 {
-    const size_t nbytes = (size_t)N * (size_t)(K / 2);
-    hipLaunchKernelGGL(k_codes_w4, dim3(grid_for(nbytes)), dim3(kBlock), 0, st, Wq, nbytes, codes);
+    const size_t words = (size_t)N * (size_t)(K / 8);
+    hipLaunchKernelGGL(k_codes_w4, dim3(grid_for(words)), dim3(kBlock), 0, st, Wq, N, K, codes);
     return hipGetLastError();
 }
 
-hipError_t launch_codes_w8(const int8_t* Wq, int N, int K, int8_t* codes, hipStream_t st)
+hipError_t launch_codes_w8(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st)
 {
-    const size_t n = (size_t)N * (size_t)K;
-    hipLaunchKernelGGL(k_copy_bytes, dim3(grid_for(n)), dim3(kBlock), 0, st, Wq, n, codes);
+    const size_t words = (size_t)N * (size_t)(K / 4);
+    hipLaunchKernelGGL(k_codes_w8, dim3(grid_for(words)), dim3(kBlock), 0, st, Wq, N, K, codes);
     return hipGetLastError();
 }
 

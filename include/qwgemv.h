@@ -51,23 +51,29 @@ enum {
     QW_ERR_WORKSPACE = 4,  /* ws_bytes below qw_workspace_bytes()               */
     QW_ERR_NONFINITE = 5,  /* a packer met a non-finite weight or f16 overflow  */
     QW_ERR_HIP = 6,        /* a HIP runtime call or launch failed               */
-    QW_ERR_TILING = 7      /* tiling arguments of a *_tiled call are invalid    */
+    QW_ERR_TILING = 7      /* launch-shape arguments of a *_tiled call invalid  */
 };
 
-/* Bytes of the packed weights: N*K/2 for INT4, N*K for INT8.  The packed buffer is
-   [N][K/2] bytes for INT4 (byte j of a row holds k=2j in its low nibble and k=2j+1
-   in its high nibble, 4-bit two's complement) and [N][K] int8 for INT8.  This
-   layout keeps each row contiguous, so the kernels read it with 128-bit loads that
-   cover 256 contiguous bytes per 16 lanes. */
+/* Bytes of the packed weights, and their layout.  The packed buffer is a sequence
+   of 1 KB tiles.  A chunk is 16 bytes of one row: 32 INT4 codes (byte j holds
+   k = 2j in its low nibble and k = 2j+1 in its high nibble, 4-bit two's complement)
+   or 16 INT8 codes.  Tile (rg, cg) holds rows 4rg..4rg+3 by chunks 16cg..16cg+15,
+   16-byte slot 16*(n % 4) + (chunk % 16) holding row n's chunk; tiles are stored
+   row group by row group, chunk groups in order within a row group, so a wave of
+   64 lanes loading 16 bytes each reads one tile as 1 KB of contiguous memory.
+   Rows past N and chunks past K are zero padding.  Size:
+   ceil(N/4) * ceil(K/512) KB for INT4 and ceil(N/4) * ceil(K/256) KB for INT8, which
+   is N*K/2 and N*K when N % 4 == 0 and K is a multiple of 512 (256).  Returns 0 for
+   an invalid shape.  qw_w4_codes / qw_w8_codes decode the layout back to codes. */
 size_t qw_w4_packed_bytes(int64_t N, int64_t K);
 size_t qw_w8_packed_bytes(int64_t N, int64_t K);
 
 /* Workspace that gemv_w4a8 (op 0) or gemv_w8a16 (op 1) needs for shape (M, N, K).
-   0 means the call needs none and accepts workspace == NULL.  A workspace must be
-   zero-filled before its first use (qw_workspace_clear does it); every call leaves
-   it zero-filled again, so one workspace serves any number of calls issued in
-   order on one stream, including inside a captured graph.  Calls that run
-   concurrently need separate workspaces. */
+   0 means the call needs none and accepts workspace == NULL; every kernel of this
+   version finishes its rows inside one workgroup, so this returns 0 for every
+   shape.  Callers that pass a workspace anyway must size it with this function and
+   zero-fill it before first use (qw_workspace_clear); the library leaves it
+   zero-filled. */
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zero-fills a workspace with a kernel (no memset node, safe to capture). */
@@ -75,7 +81,7 @@ int qw_workspace_clear(void* workspace, size_t ws_bytes, void* stream);
 
 /* Row-wise INT4 quantization and packing, done once at weight-load time
    ("Jetson Orin AGX 上的 INT4 量化推理实践", section 当前实现方式).
-   W fp32 [N][K] -> Wq (qw_w4_packed_bytes) and w_scale fp32 [N] with
+   W fp32 [N][K] -> Wq (qw_w4_packed_bytes, tile layout) and w_scale fp32 [N] with
    w_scale[n] = maxabs(W[n,:]) / 7 (fp32 division) and codes
    clamp(rint(W / w_scale), -7, 7) (round half to even); an all-zero row has scale 0.
    Synchronises `stream` once to read back a non-finite flag: not capturable. */
@@ -83,7 +89,7 @@ int quantize_pack_w4(const float* W, int64_t N, int64_t K, void* Wq, float* w_sc
                      void* stream);
 
 /* Per-output-channel INT8 quantization, done once at load time (ChatGLM2-6B W8A16
-   write-up, sections 2 and 3).  W fp32 [N][K] -> Wq int8 [N][K] and
+   write-up, sections 2 and 3).  W fp32 [N][K] -> Wq (qw_w8_packed_bytes, tile layout) and
    w_scale_f16 [N] = f16(maxabs(W[n,:]) / 127); codes clamp(rint(W / s16), -127, 127)
    are taken against the stored f16 scale.  A row whose f16 scale is 0 gets zero
    codes; a scale that overflows f16 is QW_ERR_NONFINITE.  Synchronises once. */
@@ -101,11 +107,11 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    X fp32 [M][K], Wq from quantize_pack_w4, w_scale fp32 [N] -> Y fp32 [M][N] with
    Y[m][n] = ((float)acc[m][n] * w_scale[n]) * a_scale[m] and
    acc[m][n] = sum_k q[n][k] * xq[m][k] in int32.  workspace/ws_bytes as described at
-   qw_workspace_bytes (op 0).  M >= 16 runs a skinny-GEMM kernel on the matrix cores. */
+   qw_workspace_bytes (op 0). */
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
 
-/* W8A16 linear.  X f16 [M][K], Wq int8 [N][K], w_scale_f16 [N] -> Y f16 [M][N] with
+/* W8A16 linear.  X f16 [M][K], Wq from quantize_pack_w8, w_scale_f16 [N] -> Y f16 [M][N] with
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
    rounding.  workspace as at qw_workspace_bytes (op 1). */
@@ -126,19 +132,17 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
                        int64_t N, int64_t K, float* Y, int32_t* acc, int8_t* xq,
                        float* a_scale, void* workspace, size_t ws_bytes, void* stream);
 
-/* The GEMV kernels (M < 16) with an explicit tiling instead of the built-in choice:
-   cpl = 16-byte chunks per lane per row in one K slice (1, 2 or 4), gb = row groups
-   of 4 rows loaded per batch (1, 2, 4 or 8), rows_per_wave = a multiple of 4*gb,
-   slices = K slices (>= 1; the slice length is 16*cpl chunks, so slices must equal
-   ceil(chunks_per_row / (16*cpl))).  Needs qw_tiled_workspace_bytes() of workspace. */
+/* The GEMV kernels (M < 16) with an explicit launch shape instead of the built-in
+   choice: u = tiles per load batch (4 or 8; two batches are in flight per wave),
+   nw = waves per workgroup (4, 8 or 16), rg_per_wave = row groups (4 rows each) per
+   wave (>= 1, with nw * rg_per_wave * ceil(K/512 or K/256) KB below 2 GB).  Results do
+   not depend on the launch shape.  QW_ERR_TILING for an invalid shape. */
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes,
-                       int cpl, int gb, int rows_per_wave, void* stream);
+                       int64_t N, int64_t K, float* Y, int u, int nw, int rg_per_wave,
+                       void* stream);
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
-                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, void* workspace,
-                        size_t ws_bytes, int cpl, int gb, int rows_per_wave, void* stream);
-size_t qw_tiled_workspace_bytes(int op, int64_t M, int64_t N, int64_t K, int cpl, int gb,
-                                int rows_per_wave);
+                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
+                        int rg_per_wave, void* stream);
 
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);

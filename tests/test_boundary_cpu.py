@@ -33,16 +33,24 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) >= 17
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
+    assert sorted(qw.SIGNATURES) == names
 
 
 def test_packed_sizes():
-    assert L.qw_w4_packed_bytes(18944, 3584) == 18944 * 1792
+    # tile layout: 1 KB tiles of 512 k by 4 rows (INT4) or 2 rows (INT8)
+    assert L.qw_w4_packed_bytes(18944, 3584) == 18944 * 3584 // 2
     assert L.qw_w8_packed_bytes(27392, 4096) == 27392 * 4096
+    assert L.qw_w8_packed_bytes(18944, 3584) == 18944 * 3584
+    assert L.qw_w4_packed_bytes(152064, 3584) == 152064 * 3584 // 2
+    assert L.qw_w4_packed_bytes(5, 96) == 2 * 1 * 1024
+    assert L.qw_w8_packed_bytes(517, 288) == 259 * 1 * 1024
+    assert L.qw_w4_packed_bytes(3584, 18944) == 896 * 37 * 1024
     assert L.qw_w4_packed_bytes(0, 64) == 0
+    assert L.qw_w4_packed_bytes(8, 48) == 0
 
 
 def test_status_strings():
@@ -51,16 +59,11 @@ def test_status_strings():
     assert L.qw_status_str(99) == b"unknown status"
 
 
-def test_workspace_sizes_are_aligned():
+def test_no_shape_needs_a_workspace():
     for op in (0, 1):
         for (M, N, K) in [(1, 512, 256), (1, 18944, 3584), (1, 3584, 18944), (4, 27392, 4096),
-                          (1, 512, 3584), (3, 5, 96)]:
-            b = L.qw_workspace_bytes(op, M, N, K)
-            assert b % 256 == 0
-            if b:
-                assert b >= M * N * 4
-    assert L.qw_workspace_bytes(0, 1, 512, 33) == 0   # bad shape -> 0
-    assert L.qw_workspace_bytes(7, 1, 512, 256) == 0  # bad op -> 0
+                          (1, 512, 3584), (3, 5, 96), (15, 7, 512)]:
+            assert L.qw_workspace_bytes(op, M, N, K) == 0
 
 
 @pytest.mark.parametrize("fn", ["gemv_w4a8", "gemv_w8a16"])
@@ -77,26 +80,15 @@ def test_gemv_rejects_bad_arguments(fn):
     assert f(A, A2, A3, 1, 64, 64, MIS, NULL, 0, NULL) == qw.QW_ERR_ALIGN
 
 
-@pytest.mark.parametrize("fn,op", [("gemv_w4a8", 0), ("gemv_w8a16", 1)])
-def test_gemv_rejects_missing_workspace(fn, op):
+@pytest.mark.parametrize("fn", ["qw_gemv_w4a8_tiled", "qw_gemv_w8a16_tiled"])
+def test_tiled_rejects_bad_launch_shapes(fn):
     f = getattr(L, fn)
-    # find a shape for which the built-in tiling splits K and so needs a workspace
-    for (M, N, K) in [(1, 512, 3584), (1, 64, 4096), (1, 3584, 18944), (1, 16, 8192)]:
-        need = L.qw_workspace_bytes(op, M, N, K)
-        if need:
-            break
-    assert need > 0
-    assert f(A, A2, A3, M, N, K, A4, NULL, 0, NULL) == qw.QW_ERR_WORKSPACE
-    assert f(A, A2, A3, M, N, K, A4, A, need - 256, NULL) == qw.QW_ERR_WORKSPACE
-
-
-def test_tiled_rejects_bad_tilings():
-    f = L.qw_gemv_w4a8_tiled
-    for (cpl, gb, rpw) in [(3, 4, 16), (2, 3, 24), (2, 4, 10), (2, 4, 0), (4, 8, 32)]:
-        assert f(A, A2, A3, 1, 64, 256, A4, NULL, 0, cpl, gb, rpw, NULL) == qw.QW_ERR_TILING
-    # MT*CPL > 8: M=8 (mt 8) with cpl 2
-    assert f(A, A2, A3, 8, 64, 256, A4, NULL, 0, 2, 1, 4, NULL) == qw.QW_ERR_TILING
-    assert L.qw_tiled_workspace_bytes(0, 1, 64, 256, 3, 4, 16) == 0
+    for (u, nw, rpw) in [(3, 8, 1), (8, 5, 1), (8, 8, 0), (8, 8, -1), (16, 8, 1),
+                         (8, 16, 1), (8, 8, 65)]:
+        assert f(A, A2, A3, 1, 64, 4096, A4, u, nw, rpw, NULL) == qw.QW_ERR_TILING, (u, nw, rpw)
+    assert f(A, A2, A3, 1, 64, 4016, A4, 8, 8, 1, NULL) == qw.QW_ERR_SHAPE
+    assert f(NULL, A2, A3, 1, 64, 40, A4, 8, 8, 1, NULL) == qw.QW_ERR_NULL
+    assert f(MIS, A2, A3, 1, 64, 4096, A4, 8, 8, 1, NULL) == qw.QW_ERR_ALIGN
 
 
 def test_packers_and_helpers_reject_bad_arguments():

@@ -56,16 +56,32 @@ def rel_l2(y, y64):
     return float(np.linalg.norm(y - y64) / max(np.linalg.norm(y64), 1e-300))
 
 
+def tile_layout(canon, N, R):
+    """Canonical packed rows [N][row_bytes] -> the library's tile layout: 1 KB tiles of
+    R rows x 512 k, i.e. R rows x (64 / R) chunks of 16 bytes, R = 4 for INT4 and 2 for
+    INT8; tiles row group by row group, k order inside; zero padding past N and K."""
+    L = 64 // R
+    row_bytes = canon.shape[1]
+    cg, nrg = -(-row_bytes // (16 * L)), -(-N // R)
+    pad = np.zeros((nrg * R, cg * L * 16), np.uint8)
+    pad[:N, :row_bytes] = canon
+    return pad.reshape(nrg, R, cg, L, 16).transpose(0, 2, 1, 3, 4).reshape(-1)
+
+
 def pack_w4_and_check(W, rows=None):
-    """GPU pack of W; compares packed bytes, codes and scales with the oracle (on
-    `rows` only when given).  Returns (Wq, s) on the device."""
+    """GPU pack of W; compares the packed bytes (whole matrix) or the decoded codes (on
+    `rows` only when given) and the scales with the oracle.  Returns (Wq, s, q, s)."""
+    N, K = W.shape
     Wq, s = qw.quantize_pack_w4(dev(W))
     Wsub = W if rows is None else W[rows]
     q_o, s_o = oracle.quant_w4(Wsub)
-    Wq_h = host(Wq if rows is None else Wq[torch.as_tensor(rows, device="cuda")])
-    s_h = host(s if rows is None else s[torch.as_tensor(rows, device="cuda")])
-    assert np.array_equal(s_h.view(np.uint32), s_o.view(np.uint32))
-    assert np.array_equal(Wq_h, oracle.pack_w4(q_o))
+    if rows is None:
+        assert np.array_equal(host(s).view(np.uint32), s_o.view(np.uint32))
+        assert np.array_equal(host(Wq), tile_layout(oracle.pack_w4(q_o), N, 4))
+    else:
+        ridx = torch.as_tensor(rows, device="cuda")
+        assert np.array_equal(host(s[ridx]).view(np.uint32), s_o.view(np.uint32))
+        assert np.array_equal(host(qw.w4_codes(Wq, N, K)[ridx]), q_o)
     return Wq, s, q_o, s_o
 
 
@@ -80,7 +96,7 @@ def test_tiny_w4a8_config_bit_exact():
     codes = host(qw.w4_codes(Wq, N, K))
     assert np.array_equal(codes, q_o)
     ref = oracle.gemv_w4a8(X, q_o, s_o)
-    ws = qw.make_workspace("w4a8", M, N, K)
+    ws = None  # no shape needs a workspace
     out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=ws)
     assert np.array_equal(host(out["xq"]), ref["xq"])
     assert np.array_equal(host(out["a"]).view(np.uint32), ref["a"].view(np.uint32))
@@ -135,19 +151,29 @@ def test_qwen7b_linear_w4a8(name, K, N):
 
 # ------------------------------------------------------------------ config 2 --
 
-def _w8a16_case(seed, tid_w, tid_x, M, N, K, rows=None):
-    W = wl.weights(seed, tid_w, N, K)
-    X16 = wl.activations(seed, tid_x, M, K, dtype=np.float16)
+def pack_w8_and_check(W, rows=None):
+    N, K = W.shape
     Wq, s16 = qw.quantize_pack_w8(dev(W))
     Wsub = W if rows is None else W[rows]
     q_o, s16_o = oracle.quant_w8(Wsub)
-    ridx = None if rows is None else torch.as_tensor(rows, device="cuda")
-    assert np.array_equal(host(Wq if ridx is None else Wq[ridx]), q_o)
-    assert np.array_equal(host(s16 if ridx is None else s16[ridx]).view(np.uint16), s16_o)
-    y = qw.gemv_w8a16(dev(X16), Wq, s16, workspace=qw.make_workspace("w8a16", M, N, K))
-    y = host(y if ridx is None else y[:, ridx]).astype(np.float64)
+    if rows is None:
+        assert np.array_equal(host(s16).view(np.uint16), s16_o)
+        assert np.array_equal(host(Wq), tile_layout(q_o.view(np.uint8), N, 2))
+    else:
+        ridx = torch.as_tensor(rows, device="cuda")
+        assert np.array_equal(host(s16[ridx]).view(np.uint16), s16_o)
+        assert np.array_equal(host(qw.w8_codes(Wq, N, K)[ridx]), q_o)
+    return Wq, s16, q_o, s16_o
+
+
+def _w8a16_case(seed, tid_w, tid_x, M, N, K, rows=None):
+    W = wl.weights(seed, tid_w, N, K)
+    X16 = wl.activations(seed, tid_x, M, K, dtype=np.float16)
+    Wq, s16, q_o, s16_o = pack_w8_and_check(W, rows)
+    y = qw.gemv_w8a16(dev(X16), Wq, s16)
+    y = host(y if rows is None else y[:, torch.as_tensor(rows, device="cuda")]).astype(np.float64)
     y64 = oracle.gemv_w8a16_ref64(X16, q_o, s16_o, nthreads=oracle.num_threads())
-    return W if rows is None else Wsub, X16, y, y64
+    return W if rows is None else W[rows], X16, y, y64
 
 
 def test_chatglm2_w8a16_config():
@@ -211,10 +237,8 @@ def test_skinny_sweep_sampled(M):
     assert_w4a8_close(host(Y[:, ridx]), ref["Y"])
     del Wq, s
     X16 = X.astype(np.float16)
-    Wq8, s16 = qw.quantize_pack_w8(dev(W))
-    q8, s16_o = oracle.quant_w8(W[rows])
-    assert np.array_equal(host(Wq8[ridx]), q8)
-    y = qw.gemv_w8a16(dev(X16), Wq8, s16, workspace=qw.make_workspace("w8a16", M, N, K))
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W, rows)
+    y = qw.gemv_w8a16(dev(X16), Wq8, s16)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     assert rel_l2(host(y[:, ridx]), y64) <= W8A16_RL2
 
@@ -235,16 +259,15 @@ def test_edge_shapes_both_ops(M, N, K):
     if M > 1:
         X[M - 1] = 0.0  # zero activation vector
     Wq, s, q_o, s_o = pack_w4_and_check(W)
+    assert np.array_equal(host(qw.w4_codes(Wq, N, K)), q_o)
     ref = oracle.gemv_w4a8(X, q_o, s_o)
-    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s)
     assert np.array_equal(host(out["acc"]), ref["acc"])
     assert_w4a8_close(host(out["Y"]), ref["Y"])
     X16 = X.astype(np.float16)
-    Wq8, s16 = qw.quantize_pack_w8(dev(W))
-    q8, s16_o = oracle.quant_w8(W)
-    assert np.array_equal(host(Wq8), q8)
-    assert np.array_equal(host(s16).view(np.uint16), s16_o)
-    y = host(qw.gemv_w8a16(dev(X16), Wq8, s16, workspace=qw.make_workspace("w8a16", M, N, K)))
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    assert np.array_equal(host(qw.w8_codes(Wq8, N, K)), q8)
+    y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
     if np.linalg.norm(y64) > 0:
         assert rel_l2(y, y64) <= W8A16_RL2
@@ -252,36 +275,31 @@ def test_edge_shapes_both_ops(M, N, K):
         assert not np.any(y[M - 1]) and not np.any(host(out["Y"])[M - 1])
 
 
-TILINGS = [(1, 1, 4), (1, 2, 8), (1, 4, 16), (1, 8, 64), (2, 1, 4), (2, 4, 32), (2, 8, 32),
-           (4, 1, 8), (4, 2, 8), (4, 4, 16)]
+SHAPES = [(u, nw, g) for u in (4, 8) for nw in (4, 8) for g in (1, 2, 3, 7, 64)]
 
 
-@pytest.mark.parametrize("M", [1, 2, 4])
-def test_every_tiling_gives_the_same_result(M):
+@pytest.mark.parametrize("M", [1, 2, 4, 8])
+def test_every_launch_shape_gives_the_same_result(M):
     K, N = 3584, 1000
-    say("tilings M", M)
+    say("launch shapes M", M)
     W = wl.weights(55, 1, N, K, outlier_rows=True)
     X = wl.activations(55, 2, M, K, outlier_channels=4)
     Wq, s, q_o, s_o = pack_w4_and_check(W)
     ref = oracle.gemv_w4a8(X, q_o, s_o)
     X16 = X.astype(np.float16)
-    Wq8, s16 = qw.quantize_pack_w8(dev(W))
-    q8, s16_o = oracle.quant_w8(W)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
     Xd, X16d = dev(X), dev(X16)
-    for (cpl, gb, rpw) in TILINGS:
-        mt = 1 if M == 1 else (2 if M == 2 else 4)
-        if mt * cpl > 8:
-            continue
-        ws = qw.tiled_workspace("w4a8", M, N, K, cpl, gb, rpw)
-        for rep in range(2):
-            Y = qw.gemv_w4a8_tiled(Xd, Wq, s, cpl, gb, rpw, workspace=ws)
-            assert_w4a8_close(host(Y), ref["Y"])
-        if ws is not None:
-            assert not host(ws).any()
-        ws8 = qw.tiled_workspace("w8a16", M, N, K, cpl, gb, rpw)
-        y = qw.gemv_w8a16_tiled(X16d, Wq8, s16, cpl, gb, rpw, workspace=ws8)
-        assert rel_l2(host(y), y64) <= W8A16_RL2, (cpl, gb, rpw)
+    y_first = None
+    for (u, nw, g) in SHAPES:
+        Y = qw.gemv_w4a8_tiled(Xd, Wq, s, u, nw, g)
+        assert_w4a8_close(host(Y), ref["Y"])
+        y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, u, nw, g))
+        assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, g)
+        # the f32 sum per row is taken in the same order for every launch shape
+        if y_first is None:
+            y_first = y
+        assert np.array_equal(y.view(np.uint16), y_first.view(np.uint16)), (u, nw, g)
 
 
 def test_repeated_calls_are_deterministic():
@@ -290,8 +308,7 @@ def test_repeated_calls_are_deterministic():
     X = wl.activations(66, 2, M, K)
     Wq, s = qw.quantize_pack_w4(dev(W))
     Wq8, s16 = qw.quantize_pack_w8(dev(W))
-    ws4 = qw.make_workspace("w4a8", M, N, K)
-    ws8 = qw.make_workspace("w8a16", M, N, K)
+    ws4 = ws8 = None
     Xd, X16 = dev(X), dev(X.astype(np.float16))
     a = [host(qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)) for _ in range(3)]
     b = [host(qw.gemv_w8a16(X16, Wq8, s16, workspace=ws8)) for _ in range(3)]
@@ -317,14 +334,13 @@ def test_packers_report_non_finite_weights():
 
 
 def test_graph_capture_replays_match_eager():
-    K, N, M = 3584, 512, 1  # short N: split K, so the workspace protocol is exercised
+    K, N, M = 3584, 512, 1
     W = wl.weights(77, 1, N, K)
     X = wl.activations(77, 2, M, K)
     Wq, s = qw.quantize_pack_w4(dev(W))
     Wq8, s16 = qw.quantize_pack_w8(dev(W))
     Xd, X16 = dev(X), dev(X.astype(np.float16))
-    ws4 = qw.make_workspace("w4a8", M, N, K)
-    ws8 = qw.make_workspace("w8a16", M, N, K)
+    ws4 = ws8 = None
     e4 = host(qw.gemv_w4a8(Xd, Wq, s, workspace=ws4))
     e8 = host(qw.gemv_w8a16(X16, Wq8, s16, workspace=ws8))
     Y4 = torch.empty((M, N), device="cuda")
@@ -342,5 +358,3 @@ def test_graph_capture_replays_match_eager():
         assert np.array_equal(host(Y4).view(np.uint32), e4.view(np.uint32)), rep
         assert np.array_equal(host(Y8).view(np.uint16), e8.view(np.uint16)), rep
         qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)  # eager work between replays
-    if ws4 is not None:
-        assert not host(ws4).any()

@@ -103,10 +103,13 @@ def cpu_baseline(W, X, X16, seconds, b_step):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run --steps device-to-device copies of BYTES bytes (a plain "
+                         "copy kernel of known size, to calibrate HBM byte counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -125,6 +128,15 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = [torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1) for _ in range(8)]
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for i in range(args.steps):
+            dst.copy_(src[i % 8])
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": args.steps}), flush=True)
+        return
     c = wl.HEADLINE
     M, K, N = c["M"], c["K"], c["N"]
     b4, b8 = bytes_w4a8(M, N, K), bytes_w8a16(M, N, K)
@@ -148,31 +160,54 @@ def main():
     ws4 = qw.make_workspace("w4a8", M, N, K)
     ws8 = qw.make_workspace("w8a16", M, N, K)
 
-    def step(i, ev=None):
-        w4, sc4, w8, sc8 = copies[i % R]
-        if ev is not None:
-            ev[0].record()
-        qw.gemv_w4a8(Xd, w4, sc4, workspace=ws4, out=Y4)
-        if ev is not None:
-            ev[1].record()
-        qw.gemv_w8a16(X16d, w8, sc8, workspace=ws8, out=Y8)
-        if ev is not None:
-            ev[2].record()
+    def w4(i):
+        w4q, sc4, _, _ = copies[i % R]
+        qw.gemv_w4a8(Xd, w4q, sc4, workspace=ws4, out=Y4)
+
+    def w8(i):
+        _, _, w8q, sc8 = copies[i % R]
+        qw.gemv_w8a16(X16d, w8q, sc8, workspace=ws8, out=Y8)
+
+    def step(i):
+        w4(i)
+        w8(i)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
+    # The K timed steps are launched as one HIP graph (a single host call), so the
+    # time is GPU time, not Python launch overhead.  Two more graphs of K launches of
+    # one kernel each give the per-kernel average launch duration from HIP events.
     K_steps = args.steps
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K_steps)]
+
+    def capture(fn):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(K_steps):
+                fn(i)
+        g.replay()  # first replay outside the timed region
+        torch.cuda.synchronize()
+        return g
+
+    g_step, g4, g8 = capture(step), capture(w4), capture(w8)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K_steps):
-        step(i, evs[i])
+    g_step.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    t4 = sum(e[0].elapsed_time(e[1]) for e in evs) / K_steps * 1e3  # us per launch
-    t8 = sum(e[1].elapsed_time(e[2]) for e in evs) / K_steps * 1e3
+
+    def event_time_us(g):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / K_steps
+
+    t4 = event_time_us(g4)
+    t8 = event_time_us(g8)
     ms_per_step = wall * 1e3 / K_steps
     value = b_step / (ms_per_step * 1e-3) / 1e9
 

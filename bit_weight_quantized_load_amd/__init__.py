@@ -236,7 +236,7 @@ def gemv_w8a16(X16, Wq, w_scale16, workspace=None, out=None, stream=None):
     return Y
 
 
-def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, rg_per_wave, out=None, stream=None):
+def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, nwaves, out=None, stream=None):
     """gemv_w4a8 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X.shape
@@ -245,11 +245,11 @@ def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, rg_per_wave, out=None, stream=None):
     _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
     _call("qw_gemv_w4a8_tiled", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
-          u, nw, rg_per_wave, _stream(stream))
+          u, nw, nwaves, _stream(stream))
     return Y
 
 
-def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, rg_per_wave, out=None, stream=None):
+def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, nwaves, out=None, stream=None):
     """gemv_w8a16 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X16.shape
@@ -258,7 +258,7 @@ def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, rg_per_wave, out=None, stream=No
     _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
     _call("qw_gemv_w8a16_tiled", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
-          u, nw, rg_per_wave, _stream(stream))
+          u, nw, nwaves, _stream(stream))
     return Y
 
 

@@ -39,71 +39,113 @@ int check_shape(int64_t M, int64_t N, int64_t K)
 
 constexpr int kMaxLds = 60 * 1024;  // dynamic LDS budget per workgroup
 
+// Largest K of the GEMVs: the streaming variant keeps one row of X (quantized codes
+// for W4A8, f16 for W8A16) in LDS, so K is bounded by the LDS budget.
+constexpr int64_t kMaxGemvK4 = 57344;
+constexpr int64_t kMaxGemvK8 = 28672;
+
+int check_gemv_shape(int bits, int64_t M, int64_t N, int64_t K)
+{
+    const int st = check_shape(M, N, K);
+    if (st != QW_OK)
+        return st;
+    return K <= (bits == 4 ? kMaxGemvK4 : kMaxGemvK8) ? QW_OK : QW_ERR_SHAPE;
+}
+
 // Bytes of LDS activation storage per tile per row of X: 16 chunks x 32 INT8 codes
 // (W4A8) or 32 chunks x 16 f16 values (W8A16).
 int act_tile_bytes(int bits) { return bits == 4 ? 512 : 1024; }
 
 int scale_lds_bytes(int bits, int nw) { return bits == 4 ? 4 * 64 * nw * 4 : 2 * 64 * nw * 2; }
 
-bool tiling_ok(int u, int nw, int rg_per_wave, int cg)
+// Launch-shape check.  u = 0: register variant (M == 1, K <= 4096); u = 1: eager
+// variant (at most 16 tiles per wave, at most 4 rows of X per workgroup); u = 4 or 8:
+// streaming LDS variant with u tiles per batch.  4, 8 or 16 waves per workgroup; at
+// most 64 row groups per wave (the workgroup's output scales are staged in LDS); a
+// workgroup's tiles addressable by one buffer resource.
+bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, const qw::TileLayout& L)
 {
-    if (u != 4 && u != 8)
+    if (u != 0 && u != 1 && u != 4 && u != 8)
         return false;
-    if (nw != 4 && nw != 8)
+    if (u == 0 && !(M == 1 && L.cg <= qw::kRegCG))
         return false;
-    if (rg_per_wave < 1 || rg_per_wave > 64)  // output scales of a workgroup fit in LDS
+    if (nw != 4 && nw != 8 && nw != 16)
         return false;
-    if ((int64_t)nw * rg_per_wave * cg * 1024 >= ((int64_t)1 << 31))
+    if (nwaves < 1)
         return false;
+    const int64_t per_wave = ((int64_t)L.nrg + nwaves - 1) / nwaves;
+    if (per_wave > 64)
+        return false;
+    if (u == 1 && per_wave * L.cg > 16)
+        return false;
+    if ((int64_t)nw * per_wave * L.cg * 1024 >= ((int64_t)1 << 31))
+        return false;
+    (void)bits;
     return true;
 }
 
-// M == 1 with K <= 512 * kRegCG keeps activations in registers; otherwise rows of X
-// per workgroup are M rounded up to a power of two (at most 8), lowered until the
-// staged activations fit in LDS.
-GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw, int rg_per_wave)
+GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw, int nwaves)
 {
     const qw::TileLayout L = qw::tile_layout(bits, N, K);
     GemvTiling t;
     t.u = u;
     t.nw = nw;
-    t.rg_per_wave = rg_per_wave;
-    t.blocks = (L.nrg + nw * rg_per_wave - 1) / (nw * rg_per_wave);
+    t.nwaves = nwaves;
+    t.blocks = (nwaves + nw - 1) / nw;
+    t.tmax = 0;
+    t.reg_cg = 0;
     const int scale_bytes = scale_lds_bytes(bits, nw);
-    if (M == 1 && L.cg <= qw::kRegCG) {
+    int tiles = 0, mt_cap = 8;
+    if (u == 0) {
         t.reg_cg = L.cg;
-        t.mt = 1;
-        t.lds_bytes = (bits == 4 ? L.cg * act_tile_bytes(4) : 0) + scale_bytes;
+        mt_cap = 1;
+        tiles = bits == 4 ? L.cg : 0;  // W8A16 keeps X in registers, W4A8 stages codes
+    } else if (u == 1) {
+        const int64_t per_wave = ((int64_t)L.nrg + nwaves - 1) / nwaves;
+        t.tmax = per_wave * L.cg <= 8 ? 8 : 16;
+        mt_cap = 4;
+        tiles = L.cg;
     } else {
-        t.reg_cg = 0;
-        const int tiles = (L.cg + u - 1) / u * u;
-        int mt = M >= 5 ? 8 : (M >= 3 ? 4 : (int)M);
-        while (mt > 1 && mt * tiles * act_tile_bytes(bits) + scale_bytes > kMaxLds)
-            mt >>= 1;
-        t.mt = mt;
-        t.lds_bytes = mt * tiles * act_tile_bytes(bits) + scale_bytes;
+        tiles = (L.cg + u - 1) / u * u;
     }
+    int mt = M >= 5 ? 8 : (M >= 3 ? 4 : (int)M);
+    if (mt > mt_cap)
+        mt = mt_cap;
+    while (mt > 1 && mt * tiles * act_tile_bytes(bits) + scale_bytes > kMaxLds)
+        mt >>= 1;
+    t.mt = mt;
+    t.lds_bytes = mt * tiles * act_tile_bytes(bits) + scale_bytes;
     t.m_tiles = (int)((M + t.mt - 1) / t.mt);
     return t;
 }
 
 bool fits_lds(const GemvTiling& t) { return t.lds_bytes <= kMaxLds; }
 
-// Built-in launch shape: 4 waves per workgroup, 8 tiles per batch (LDS variant), and
-// as many row groups per wave as it takes to keep about 16 waves per compute unit
-// (256 CUs) in one round of work.
+// with 8 tiles per batch; 4 waves per workgroup.
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
+    // Launch shapes picked by timing on MI355X at the decode shapes (K 3584..18944,
+    // N 3584..152064).  INT4 at M = 1 with K <= 4096: activations in registers, 2048
+    // waves (two 4-wave workgroups per CU, one pass over the chip), row groups split
+    // evenly.  Otherwise the LDS variant with 8-tile batches; INT8 gives each wave two
+    // row groups (one 2 KB batch pair in flight per row group), INT4 at most 4096 waves.
     const qw::TileLayout L = qw::tile_layout(bits, N, K);
-    const int nw = 4, u = 8;
-    int64_t g = (L.nrg + 4095) / 4096;
-    if (g < 1)
-        g = 1;
-    if (g > 64)
-        g = 64;
-    while (g > 1 && (int64_t)nw * g * L.cg * 1024 >= ((int64_t)1 << 31))
-        --g;
-    return make_tiling(bits, M, N, K, u, nw, (int)g);
+    const int nw = 4;
+    if (bits == 4 && M == 1 && L.cg <= qw::kRegCG) {
+        const int64_t nwaves = L.nrg < 2048 ? L.nrg : 2048;
+        if (((int64_t)L.nrg + nwaves - 1) / nwaves <= 64)
+            return make_tiling(bits, M, N, K, 0, nw, (int)nwaves);
+    }
+    int64_t nwaves;
+    if (bits == 8)
+        nwaves = ((int64_t)L.nrg + 1) / 2;
+    else
+        nwaves = L.nrg < 4096 ? L.nrg : 4096;
+    while (((int64_t)L.nrg + nwaves - 1) / nwaves > 64)
+        nwaves *= 2;
+    if (nwaves > L.nrg)
+        nwaves = L.nrg;
+    return make_tiling(bits, M, N, K, 8, nw, (int)nwaves);
 }
 
 // One device int per GPU for the packers' non-finite flag.
@@ -144,7 +186,7 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
 {
     if (!X || !Wq || !w_scale || !Y)
         return QW_ERR_NULL;
-    int st = check_shape(M, N, K);
+    int st = check_gemv_shape(4, M, N, K);
     if (st != QW_OK)
         return st;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
@@ -161,7 +203,7 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
     a.K = (int)K;
     a.cg = L.cg;
     a.nrg = L.nrg;
-    a.rg_per_wave = t.rg_per_wave;
+    a.nwaves = t.nwaves;
     a.dbg_acc = acc;
     a.dbg_xq = xq;
     a.dbg_a = a_scale;
@@ -173,7 +215,7 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
 {
     if (!X || !Wq || !w_scale || !Y)
         return QW_ERR_NULL;
-    int st = check_shape(M, N, K);
+    int st = check_gemv_shape(8, M, N, K);
     if (st != QW_OK)
         return st;
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
@@ -190,7 +232,7 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     a.K = (int)K;
     a.cg = L.cg;
     a.nrg = L.nrg;
-    a.rg_per_wave = t.rg_per_wave;
+    a.nwaves = t.nwaves;
     return hip_status(qw::launch_gemv_w8a16(a, t, static_cast<hipStream_t>(stream)));
 }
 
@@ -300,7 +342,7 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream)
 {
     (void)ws_bytes;
-    if (check_shape(M, N, K) != QW_OK)
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
                     default_tiling(4, M, N, K), false, stream);
@@ -311,20 +353,20 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
                        void* workspace, size_t ws_bytes, void* stream)
 {
     (void)ws_bytes;
-    if (check_shape(M, N, K) != QW_OK)
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, acc, xq, a_scale, workspace,
                     default_tiling(4, M, N, K), true, stream);
 }
 
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, int u, int nw, int rg_per_wave, void* stream)
+                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves, void* stream)
 {
-    if (check_shape(M, N, K) != QW_OK)
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(u, nw, rg_per_wave, qw::tile_layout(4, N, K).cg))
+    if (!tiling_ok(4, M, u, nw, nwaves, qw::tile_layout(4, N, K)))
         return QW_ERR_TILING;
-    const GemvTiling t = make_tiling(4, M, N, K, u, nw, rg_per_wave);
+    const GemvTiling t = make_tiling(4, M, N, K, u, nw, nwaves);
     if (!fits_lds(t))
         return QW_ERR_TILING;
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, nullptr, t, false,
@@ -336,7 +378,7 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
                void* stream)
 {
     (void)ws_bytes;
-    if (check_shape(M, N, K) != QW_OK)
+    if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
     return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace,
                      default_tiling(8, M, N, K), stream);
@@ -344,13 +386,13 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
 
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                         int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
-                        int rg_per_wave, void* stream)
+                        int nwaves, void* stream)
 {
-    if (check_shape(M, N, K) != QW_OK)
+    if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(u, nw, rg_per_wave, qw::tile_layout(8, N, K).cg))
+    if (!tiling_ok(8, M, u, nw, nwaves, qw::tile_layout(8, N, K)))
         return QW_ERR_TILING;
-    const GemvTiling t = make_tiling(8, M, N, K, u, nw, rg_per_wave);
+    const GemvTiling t = make_tiling(8, M, N, K, u, nw, nwaves);
     if (!fits_lds(t))
         return QW_ERR_TILING;
     return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, t, stream);

@@ -9,8 +9,8 @@
 // kernel) is the prologue below.
 //
 // Work split.  The packed weights are 1 KB tiles of 4 rows x 512 k (16 chunks of
-// 32 nibbles per row, see kernels.hpp).  Each wave owns rg_per_wave whole row
-// groups, a contiguous run of tiles, and streams it with one 16-byte load per lane
+// 32 nibbles per row, see kernels.hpp).  Each wave owns an even share of whole row
+// groups (nwaves waves split them), a contiguous run of tiles, and streams it with one 16-byte load per lane
 // per tile, two batches in flight.  Lane (sub, j) always meets row 4*rg + sub and
 // chunk 16*cg + j, so a row's partial sums live in the 16 lanes of one DPP row and
 // are added with four DPP steps when the row group ends.  No row is split across
@@ -19,8 +19,8 @@
 // Two variants.  When K <= 4096 and M == 1 (kRegCG tiles per row group), a batch is
 // one whole row group and each lane keeps the activation codes of its chunks in
 // registers, read from LDS once.  Otherwise a batch is U tiles of a row group and
-// the codes are read from LDS per tile; LDS is zero-padded to whole batches so the
-// batch body has no branches and its LDS reads can be issued ahead of the dots.
+// the codes are read from LDS per batch, all U tiles' words before the dots; LDS is
+// zero-padded to whole batches so the batch body has no branches.
 //
 // Prologue.  Output scales and X row 0 are loaded first and the first weight batch
 // right after them (loads complete in order, so anything the prologue waits on must
@@ -94,15 +94,20 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
     const int cpr = K >> 5;                       // real chunks per row
 
     // ---- this wave's run of tiles
-    const int G = p.rg_per_wave;
-    const int rg_blk = blockIdx.x * NW * G;
-    const int nrg_blk = min(NW * G, p.nrg - rg_blk);
-    const int rg0 = rg_blk + wave * G;
-    const int nrg_w = max(0, min(G, p.nrg - rg0));
+    // Waves along N split the row groups evenly: wave gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
+    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int nrg_w = rg1 - rg0;
     const int nq = nrg_w * nb;  // batches of this wave
     const rsrc_t wres =
         make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
-    const uint32_t wbase = (uint32_t)(wave * G * CG) * 1024u + (uint32_t)lane * 16u;
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
 
     uint4 wa[kB], wb[kB];
     // batch q = (row group q / nb, tiles (q % nb) * kB ..); tiles past the row group
@@ -237,14 +242,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 #define QW_COMPUTE(WBUF, Q)                                                                     \
         {                                                                                       \
             const int r_ = (Q) / nb, b_ = (Q) - r_ * nb;                                        \
-            _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                    \
+            _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                                   \
             {                                                                                   \
-                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
-                {                                                                               \
-                    uint32_t a_[8];                                                             \
-                    load_act(s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 16 + j) * 8, a_);   \
-                    dot_chunk(WBUF[u_], a_, acc[mm]);                                           \
-                }                                                                               \
+                uint32_t a_[U][8];                                                              \
+                _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
+                    load_act(s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 16 + j) * 8, a_[u_]); \
+                _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
+                    dot_chunk(WBUF[u_], a_[u_], acc[mm]);                                       \
             }                                                                                   \
             if (b_ == nb - 1) {                                                                 \
                 _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
@@ -267,6 +271,164 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 #undef QW_LOAD
 }
 
+// Eager variant: every tile of the wave (at most TMAX) is requested before the
+// prologue, so the whole matrix is in flight while the activations are quantized;
+// the codes are then read from LDS one tile ahead of the dots.
+template <int MT, int TMAX, int NW, bool kDebug>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    extern __shared__ uint32_t s_dyn[];  // [MT][cg*16 chunks][8 words] codes, then scales
+    __shared__ float s_red[MT][NW];
+    __shared__ float s_a[MT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, sub = lane >> 4;
+    const int M = p.M, N = p.N, K = p.K, CG = p.cg;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(MT, M - m0);
+    const int K4 = K >> 2;
+    const int chunks = CG * 16;
+    const int cpr = K >> 5;
+
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
+    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int T = (rg1 - rg0) * CG;  // tiles of this wave, at most TMAX
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
+
+    // ---- scales and X row 0 first, then every weight tile of the wave
+    float* s_scale = reinterpret_cast<float*>(s_dyn + (size_t)MT * chunks * 8);
+    const int rows_blk = min(nrg_blk * 4, N - rg_blk * 4);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 4, (uint32_t)max(rows_blk, 0) * 4u);
+    uint32_t sc_reg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sc_reg[i] = load4(sres, (uint32_t)(tid + i * kThreads) * 4u);
+    constexpr int XV = 4;
+    const int nblk = (K4 + XV * kThreads - 1) / (XV * kThreads);
+    float4 xv[XV];
+#define QW_LOAD_X(MM, BLK)                                                                      \
+    {                                                                                           \
+        const rsrc_t xr_ = make_rsrc(p.X + (size_t)(m0 + (MM)) * K,                             \
+                                     (MM) < mt ? (uint32_t)K * 4u : 0u);                        \
+        _Pragma("unroll") for (int i_ = 0; i_ < XV; ++i_)                                       \
+            xv[i_] = load16f(xr_, (uint32_t)((BLK) * XV * kThreads + i_ * kThreads + tid) * 16u); \
+    }
+    QW_LOAD_X(0, 0);
+    uint4 w[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+        w[t] = load16(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s_scale[tid + i * kThreads] = __uint_as_float(sc_reg[i]);
+
+    for (int mm = 0; mm < MT; ++mm) {
+        float mx = 0.0f;
+        for (int blk = 0; blk < nblk; ++blk) {
+            if (mm > 0 || blk > 0)
+                QW_LOAD_X(mm, blk);
+#pragma unroll
+            for (int i = 0; i < XV; ++i)
+                mx = fmaxf(mx, max_abs4(xv[i]));
+        }
+        mx = wave_max_dpp(mx);
+        if (lane == 0)
+            s_red[mm][wave] = mx;
+        __syncthreads();
+        mx = s_red[mm][0];
+#pragma unroll
+        for (int w_ = 1; w_ < NW; ++w_)
+            mx = fmaxf(mx, s_red[mm][w_]);
+        const float a = mx / 127.0f;
+        const float r = 1.0f / a;
+        const bool fast = r <= 3.0e38f;
+        if (tid == 0)
+            s_a[mm] = a;
+        uint16_t* act16 = reinterpret_cast<uint16_t*>(s_dyn + (size_t)mm * chunks * 8);
+        for (int blk = 0; blk < nblk; ++blk) {
+            if (nblk > 1)
+                QW_LOAD_X(mm, blk);
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int f = blk * XV * kThreads + i * kThreads + tid;
+                if (f < K4) {
+                    int q[4];
+                    quant4_i8(xv[i], a, r, fast, q);
+                    const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
+                    const int wi = (c * 8 + 2 * d) * 2 + h;
+                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
+                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
+                    if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
+                        *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * K + 4 * f) =
+                            pack_i8x4(q[0], q[1], q[2], q[3]);
+                }
+            }
+        }
+        for (int w_ = cpr * 8 + tid; w_ < chunks * 8; w_ += kThreads)
+            s_dyn[(size_t)mm * chunks * 8 + w_] = 0u;
+    }
+    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
+        p.dbg_a[m0 + tid] = s_a[tid];
+    __syncthreads();
+#undef QW_LOAD_X
+
+    // ---- tiles in order; the codes of the next tile are read while this one computes
+    int acc[MT][4];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+        acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0;
+    uint32_t a_cur[MT][8];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+        load_act(s_dyn + ((size_t)mm * chunks + j) * 8, a_cur[mm]);
+    int c = 0, rgi = 0;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+            const int cn = c + 1 == CG ? 0 : c + 1;
+            uint32_t a_nxt[MT][8];
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                load_act(s_dyn + ((size_t)mm * chunks + cn * 16 + j) * 8, a_nxt[mm]);
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                dot_chunk(w[t], a_cur[mm], acc[mm]);
+            if (cn == 0) {
+                const int n = (rg0 + rgi) * 4 + sub;
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) {
+                    const int v = row_sum16(acc[mm][0] + acc[mm][1] + acc[mm][2] + acc[mm][3]) >> 4;
+                    acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0;
+                    if (j == 0 && n < N && mm < mt) {
+                        const size_t o = (size_t)(m0 + mm) * N + n;
+                        if (kDebug && p.dbg_acc != nullptr)
+                            p.dbg_acc[o] = v;
+                        p.Y[o] = ((float)v * s_scale[n - rg_blk * 4]) * s_a[mm];
+                    }
+                }
+                ++rgi;
+            }
+            c = cn;
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a_cur[mm][e] = a_nxt[mm][e];
+        }
+    }
+}
+
 template <int MT, int RCG, int U, int NW>
 hipError_t launch4(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
@@ -278,6 +440,26 @@ hipError_t launch4(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream
         hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, false>), grid, dim3(64 * NW), t.lds_bytes,
                            st, a);
     return hipGetLastError();
+}
+
+template <int MT, int TMAX, int NW>
+hipError_t launch_eager(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    const dim3 grid(t.blocks, t.m_tiles);
+    if (debug)
+        hipLaunchKernelGGL((k_gemv_w4a8_eager<MT, TMAX, NW, true>), grid, dim3(64 * NW),
+                           t.lds_bytes, st, a);
+    else
+        hipLaunchKernelGGL((k_gemv_w4a8_eager<MT, TMAX, NW, false>), grid, dim3(64 * NW),
+                           t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int MT, int NW>
+hipError_t launch_eager_t(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    return t.tmax == 8 ? launch_eager<MT, 8, NW>(a, t, debug, st)
+                       : launch_eager<MT, 16, NW>(a, t, debug, st);
 }
 
 template <int NW>
@@ -305,6 +487,14 @@ hipError_t launch_lds(const W4A8Args& a, const GemvTiling& t, bool debug, hipStr
 template <int NW>
 hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
+    if (t.tmax > 0) {
+        switch (t.mt) {
+        case 1: return launch_eager_t<1, NW>(a, t, debug, st);
+        case 2: return launch_eager_t<2, NW>(a, t, debug, st);
+        case 4: return launch_eager_t<4, NW>(a, t, debug, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (t.reg_cg > 0)
         return launch_reg<NW>(a, t, debug, st);
     switch (t.mt) {
@@ -320,7 +510,12 @@ hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStre
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    return t.nw == 4 ? launch_nw<4>(a, t, debug, st) : launch_nw<8>(a, t, debug, st);
+    switch (t.nw) {
+    case 4: return launch_nw<4>(a, t, debug, st);
+    case 8: return launch_nw<8>(a, t, debug, st);
+    case 16: return launch_nw<16>(a, t, debug, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qw

@@ -75,15 +75,20 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
     const int nb = kReg ? 1 : (CG + U - 1) / U;
     const int chunks = nb * kB * 32;  // LDS variant: chunks per X row in LDS (zero padded)
 
-    const int G = p.rg_per_wave;
-    const int rg_blk = blockIdx.x * NW * G;
-    const int nrg_blk = min(NW * G, p.nrg - rg_blk);
-    const int rg0 = rg_blk + wave * G;
-    const int nrg_w = max(0, min(G, p.nrg - rg0));
-    const int nq = nrg_w * nb;
+    // Waves along N split the row groups evenly: wave gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
+    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int nrg_w = rg1 - rg0;
+    const int nq = nrg_w * nb;  // batches of this wave
     const rsrc_t wres =
         make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
-    const uint32_t wbase = (uint32_t)(wave * G * CG) * 1024u + (uint32_t)lane * 16u;
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
 
     uint4 wa[kB], wb[kB];
 #define QW_LOAD(WBUF, Q)                                                                        \
@@ -186,16 +191,17 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
 #define QW_COMPUTE(WBUF, Q)                                                                     \
         {                                                                                       \
             const int r_ = (Q) / nb, b_ = (Q) - r_ * nb;                                        \
-            _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                    \
+            _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                                   \
             {                                                                                   \
-                _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
+                uint32_t a_[U][8];                                                              \
+                _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
                 {                                                                               \
                     const uint4* ap_ = reinterpret_cast<const uint4*>(                          \
                         s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 32 + j) * 8);            \
-                    uint32_t a_[8];                                                             \
-                    split8(ap_[0], ap_[1], a_);                                                 \
-                    dot_chunk_f16(WBUF[u_], a_, acc[mm]);                                       \
+                    split8(ap_[0], ap_[1], a_[u_]);                                             \
                 }                                                                               \
+                _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
+                    dot_chunk_f16(WBUF[u_], a_[u_], acc[mm]);                                   \
             }                                                                                   \
             if (b_ == nb - 1) {                                                                 \
                 _Pragma("unroll") for (int mm = 0; mm < MT; ++mm)                               \
@@ -217,6 +223,141 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
     }
 #undef QW_LOAD
     (void)act;
+}
+
+// Eager variant (see the W4A8 kernel): every tile of the wave, at most TMAX, is
+// requested right after X; X is staged in LDS and read one tile ahead of the dots.
+template <int MT, int TMAX, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w8a16_eager(W8A16Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    extern __shared__ uint32_t s_dyn[];  // [MT][cg*32 chunks][8 words of f16 pairs]; then scales
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, sub = lane >> 5;
+    const int M = p.M, N = p.N, K = p.K, CG = p.cg;
+    const int m0 = blockIdx.y * MT;
+    const int mt = min(MT, M - m0);
+    const int chunks = CG * 32;
+
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
+    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int T = (rg1 - rg0) * CG;
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
+
+    uint16_t* s_scale = reinterpret_cast<uint16_t*>(s_dyn + (size_t)MT * chunks * 8);
+    const int rows_blk = min(nrg_blk * 2, N - rg_blk * 2);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 2, (uint32_t)max(rows_blk, 0) * 2u);
+    uint16_t sc_reg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        sc_reg[i] = load2(sres, (uint32_t)(tid + i * kThreads) * 2u);
+    const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)mt * (uint32_t)K * 2u);
+    constexpr int kXP = 4;
+    const int pieces = MT * chunks * 2;
+    const int npass = (pieces + kXP * kThreads - 1) / (kXP * kThreads);
+    uint4 xp[kXP];
+#define QW_LOAD_XP(PASS)                                                                        \
+    _Pragma("unroll") for (int i_ = 0; i_ < kXP; ++i_)                                          \
+    {                                                                                           \
+        const int q_ = (PASS) * kXP * kThreads + i_ * kThreads + tid;                           \
+        const int mm_ = q_ / (chunks * 2);                                                      \
+        const int r_ = q_ - mm_ * (chunks * 2);                                                 \
+        const bool in_ = mm_ < MT && r_ * 8 < K;                                                \
+        xp[i_] = load16(xres, in_ ? (uint32_t)(mm_ * K + r_ * 8) * 2u : 0x80000000u);          \
+    }
+    QW_LOAD_XP(0);
+    uint4 w[TMAX];
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t)
+        w[t] = load16(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
+    for (int pass = 0; pass < npass; ++pass) {
+        if (pass > 0)
+            QW_LOAD_XP(pass);
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int q = pass * kXP * kThreads + i * kThreads + tid;
+            if (q < pieces)
+                reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
+        }
+    }
+#undef QW_LOAD_XP
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        s_scale[tid + i * kThreads] = sc_reg[i];
+    __syncthreads();
+
+    float acc[MT][4];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm)
+        acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0.0f;
+    uint32_t a_cur[MT][8];
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+        const uint4* ap = reinterpret_cast<const uint4*>(s_dyn + ((size_t)mm * chunks + j) * 8);
+        split8(ap[0], ap[1], a_cur[mm]);
+    }
+    int c = 0, rgi = 0;
+#pragma unroll
+    for (int t = 0; t < TMAX; ++t) {
+        if (t < T) {
+            const int cn = c + 1 == CG ? 0 : c + 1;
+            uint32_t a_nxt[MT][8];
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm) {
+                const uint4* ap =
+                    reinterpret_cast<const uint4*>(s_dyn + ((size_t)mm * chunks + cn * 32 + j) * 8);
+                split8(ap[0], ap[1], a_nxt[mm]);
+            }
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+                dot_chunk_f16(w[t], a_cur[mm], acc[mm]);
+            if (cn == 0) {
+                const int n = (rg0 + rgi) * 2 + sub;
+#pragma unroll
+                for (int mm = 0; mm < MT; ++mm) {
+                    const float v = half_wave_sum_from_rows(
+                        row_sum16((acc[mm][0] + acc[mm][1]) + (acc[mm][2] + acc[mm][3])));
+                    acc[mm][0] = acc[mm][1] = acc[mm][2] = acc[mm][3] = 0.0f;
+                    if (j == 31 && n < N && mm < mt) {
+                        const float sc = __half2float(__ushort_as_half(s_scale[n - rg_blk * 2]));
+                        p.Y[(size_t)(m0 + mm) * N + n] = __half_as_ushort(__float2half_rn(v * sc));
+                    }
+                }
+                ++rgi;
+            }
+            c = cn;
+#pragma unroll
+            for (int mm = 0; mm < MT; ++mm)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    a_cur[mm][e] = a_nxt[mm][e];
+        }
+    }
+}
+
+template <int MT, int TMAX, int NW>
+hipError_t launch_eager(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    const dim3 grid(t.blocks, t.m_tiles);
+    hipLaunchKernelGGL((k_gemv_w8a16_eager<MT, TMAX, NW>), grid, dim3(64 * NW), t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int MT, int NW>
+hipError_t launch_eager_t(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    return t.tmax == 8 ? launch_eager<MT, 8, NW>(a, t, st) : launch_eager<MT, 16, NW>(a, t, st);
 }
 
 template <int MT, int RCG, int U, int NW>
@@ -252,6 +393,14 @@ hipError_t launch_lds(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 template <int NW>
 hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
+    if (t.tmax > 0) {
+        switch (t.mt) {
+        case 1: return launch_eager_t<1, NW>(a, t, st);
+        case 2: return launch_eager_t<2, NW>(a, t, st);
+        case 4: return launch_eager_t<4, NW>(a, t, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
     if (t.reg_cg > 0)
         return launch_reg<NW>(a, t, st);
     switch (t.mt) {
@@ -267,7 +416,12 @@ hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
-    return t.nw == 4 ? launch_nw<4>(a, t, st) : launch_nw<8>(a, t, st);
+    switch (t.nw) {
+    case 4: return launch_nw<4>(a, t, st);
+    case 8: return launch_nw<8>(a, t, st);
+    case 16: return launch_nw<16>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 }  // namespace qw

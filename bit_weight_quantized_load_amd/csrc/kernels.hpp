@@ -49,10 +49,11 @@ struct GemvTiling {
     int m_tiles;      // ceil(M / mt)
     int reg_cg;       // > 0: activations in registers, K <= 512 * reg_cg, mt == 1
                       //   0: activations read from LDS tile by tile
+    int tmax;         // > 0: eager variant, every tile of a wave (at most tmax) loaded up front
     int u;            // LDS variant: tiles per load batch (4 or 8), two batches in flight
-    int nw;           // waves per workgroup (4 or 8)
-    int rg_per_wave;  // row groups per wave
-    int blocks;       // workgroups along N = ceil(nrg / (nw * rg_per_wave))
+    int nw;           // waves per workgroup (4, 8 or 16)
+    int nwaves;       // waves along N; they split the row groups evenly
+    int blocks;       // workgroups along N = ceil(nwaves / nw)
     int lds_bytes;    // dynamic LDS
 };
 
@@ -62,7 +63,7 @@ struct W4A8Args {
     const float* w_scale;
     float* Y;
     int M, N, K;
-    int cg, nrg, rg_per_wave;
+    int cg, nrg, nwaves;
     int32_t* dbg_acc;  // optional [M][N]
     int8_t* dbg_xq;    // optional [M][K]
     float* dbg_a;      // optional [M]
@@ -74,7 +75,7 @@ struct W8A16Args {
     const uint16_t* w_scale;
     uint16_t* Y;
     int M, N, K;
-    int cg, nrg, rg_per_wave;
+    int cg, nrg, nwaves;
 };
 
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,

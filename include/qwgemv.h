@@ -22,7 +22,9 @@
  *  - Matrices are row-major and contiguous: W and the packed weights are [N][K]
  *    (output rows n, input columns k), X is [M][K], Y is [M][N].
  *  - Every pointer must be 16-byte aligned.  K must be a positive multiple of 32 and
- *    at most 131072; M and N must be positive (M at most 65535).
+ *    at most 131072 for the packers, at most 57344 for gemv_w4a8 and 28672 for
+ *    gemv_w8a16 (one row of X lives in on-chip LDS); M and N must be positive
+ *    (M at most 65535).  Larger K returns QW_ERR_SHAPE.
  *  - fp16 values travel as their IEEE binary16 bit patterns in uint16_t.
  *  - `stream` is a hipStream_t passed as void*; NULL is the null stream.  Work is
  *    enqueued asynchronously on it and the call returns without synchronising,
@@ -133,16 +135,19 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
                        float* a_scale, void* workspace, size_t ws_bytes, void* stream);
 
 /* The GEMV kernels (M < 16) with an explicit launch shape instead of the built-in
-   choice: u = tiles per load batch (4 or 8; two batches are in flight per wave),
-   nw = waves per workgroup (4, 8 or 16), rg_per_wave = row groups (4 rows each) per
-   wave (>= 1, with nw * rg_per_wave * ceil(K/512 or K/256) KB below 2 GB).  Results do
-   not depend on the launch shape.  QW_ERR_TILING for an invalid shape. */
+   choice.  u = 0 keeps each lane's activations in registers (only M == 1 with
+   K <= 4096); u = 1 issues every weight load of a wave before its first dot product
+   (at most 16 tiles of 512 k per wave, M <= 4 per workgroup); u = 4 or 8 reads the
+   activations from LDS in batches of u tiles, two batches in flight.  nw = waves per
+   workgroup (4, 8 or 16); nwaves = waves along N, which split the ceil(N/4) (INT4) or
+   ceil(N/2) (INT8) row groups evenly, at most 64 row groups each.  Results do not
+   depend on the launch shape.  QW_ERR_TILING for an invalid shape. */
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, int u, int nw, int rg_per_wave,
+                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves,
                        void* stream);
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                         int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
-                        int rg_per_wave, void* stream);
+                        int nwaves, void* stream);
 
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);

@@ -75,6 +75,9 @@ def test_gemv_rejects_bad_arguments(fn):
     for (M, N, K) in [(0, 64, 64), (1, 0, 64), (1, 64, 0), (1, 64, 48), (1, 64, 131072 + 32),
                       (70000, 64, 64), (-1, 64, 64)]:
         assert f(A, A2, A3, M, N, K, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE, (M, N, K)
+    # one row of X must fit on chip: K <= 57344 (INT4) or 28672 (INT8)
+    kmax = 57344 if fn == "gemv_w4a8" else 28672
+    assert f(A, A2, A3, 1, 64, kmax + 32, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE
     # alignment
     assert f(MIS, A2, A3, 1, 64, 64, A4, NULL, 0, NULL) == qw.QW_ERR_ALIGN
     assert f(A, A2, A3, 1, 64, 64, MIS, NULL, 0, NULL) == qw.QW_ERR_ALIGN
@@ -83,9 +86,13 @@ def test_gemv_rejects_bad_arguments(fn):
 @pytest.mark.parametrize("fn", ["qw_gemv_w4a8_tiled", "qw_gemv_w8a16_tiled"])
 def test_tiled_rejects_bad_launch_shapes(fn):
     f = getattr(L, fn)
-    for (u, nw, rpw) in [(3, 8, 1), (8, 5, 1), (8, 8, 0), (8, 8, -1), (16, 8, 1),
-                         (8, 16, 1), (8, 8, 65)]:
-        assert f(A, A2, A3, 1, 64, 4096, A4, u, nw, rpw, NULL) == qw.QW_ERR_TILING, (u, nw, rpw)
+    # (M, N, u, nw, nwaves): bad batch, bad wave count, no waves, register variant for
+    # M > 1 or K > 4096, more than 64 row groups per wave
+    for (M, N, K, u, nw, nwaves) in [(1, 64, 4096, 3, 8, 1), (1, 64, 4096, 8, 5, 1),
+                                     (1, 64, 4096, 8, 8, 0), (1, 64, 4096, 8, 8, -1),
+                                     (2, 64, 4096, 0, 4, 16), (1, 64, 8192, 0, 4, 16),
+                                     (1, 1000, 512, 8, 4, 1)]:
+        assert f(A, A2, A3, M, N, K, A4, u, nw, nwaves, NULL) == qw.QW_ERR_TILING, (M, N, u, nw, nwaves)
     assert f(A, A2, A3, 1, 64, 4016, A4, 8, 8, 1, NULL) == qw.QW_ERR_SHAPE
     assert f(NULL, A2, A3, 1, 64, 40, A4, 8, 8, 1, NULL) == qw.QW_ERR_NULL
     assert f(MIS, A2, A3, 1, 64, 4096, A4, 8, 8, 1, NULL) == qw.QW_ERR_ALIGN

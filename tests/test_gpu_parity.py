@@ -246,7 +246,19 @@ def test_skinny_sweep_sampled(M):
 # --------------------------------------------------------------- edge cases --
 
 EDGE = [(1, 1, 32), (1, 5, 96), (2, 17, 64), (3, 517, 288), (5, 64, 1024), (8, 100, 3584),
-        (9, 33, 256), (15, 7, 512), (1, 4100, 8192), (1, 3, 131072 // 8)]
+        (9, 33, 256), (15, 7, 512), (1, 4100, 8192), (1, 3, 131072 // 8), (2, 37, 28672)]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 37, 57344), (3, 5, 57344)])
+def test_w4a8_at_its_largest_k(M, N, K):
+    say("w4a8 max K", M, N, K)
+    W = wl.weights(200 + M, 1, N, K, outlier_rows=False)
+    X = wl.activations(200 + M, 2, M, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s)
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert_w4a8_close(host(out["Y"]), ref["Y"])
 
 
 @pytest.mark.parametrize("M,N,K", EDGE)
@@ -275,7 +287,21 @@ def test_edge_shapes_both_ops(M, N, K):
         assert not np.any(y[M - 1]) and not np.any(host(out["Y"])[M - 1])
 
 
-SHAPES = [(u, nw, g) for u in (4, 8) for nw in (4, 8) for g in (1, 2, 3, 7, 64)]
+def launch_shapes(M, nrg4, nrg8, cg):
+    """(u, nw, nwaves) combinations valid for both ops: u = 0 (register activations)
+    only for M == 1, u = 1 (eager) with at most 16 tiles per wave, at most 64 row
+    groups per wave."""
+    out = []
+    for u in ((0, 1, 4, 8) if M == 1 else (1, 4, 8)):
+        for nw in (4, 8, 16):
+            for nwaves in (8, 13, 64, 100, 250, 333, 500, 1000):
+                per4, per8 = -(-nrg4 // nwaves), -(-nrg8 // nwaves)
+                if per4 > 64 or per8 > 64:
+                    continue
+                if u == 1 and max(per4, per8) * cg > 16:
+                    continue
+                out.append((u, nw, nwaves))
+    return out
 
 
 @pytest.mark.parametrize("M", [1, 2, 4, 8])
@@ -291,15 +317,17 @@ def test_every_launch_shape_gives_the_same_result(M):
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
     Xd, X16d = dev(X), dev(X16)
     y_first = None
-    for (u, nw, g) in SHAPES:
-        Y = qw.gemv_w4a8_tiled(Xd, Wq, s, u, nw, g)
+    shapes = launch_shapes(M, -(-N // 4), -(-N // 2), -(-K // 512))
+    assert len(shapes) >= 12
+    for (u, nw, nwaves) in shapes:
+        Y = qw.gemv_w4a8_tiled(Xd, Wq, s, u, nw, nwaves)
         assert_w4a8_close(host(Y), ref["Y"])
-        y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, u, nw, g))
-        assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, g)
-        # the f32 sum per row is taken in the same order for every launch shape
+        y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, u, nw, nwaves))
+        assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, nwaves)
+        # every launch shape adds a row's products in the same order
         if y_first is None:
             y_first = y
-        assert np.array_equal(y.view(np.uint16), y_first.view(np.uint16)), (u, nw, g)
+        assert np.array_equal(y.view(np.uint16), y_first.view(np.uint16)), (u, nw, nwaves)
 
 
 def test_repeated_calls_are_deterministic():

@@ -124,27 +124,28 @@ bool fits_lds(const GemvTiling& t) { return t.lds_bytes <= kMaxLds; }
 // with 8 tiles per batch; 4 waves per workgroup.
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
-    // Launch shapes picked by timing on MI355X at the decode shapes (K 3584..18944,
-    // N 3584..152064).  INT4 at M = 1 with K <= 4096: activations in registers, 2048
-    // waves (two 4-wave workgroups per CU, one pass over the chip), row groups split
-    // evenly.  Otherwise the LDS variant with 8-tile batches; INT8 gives each wave two
-    // row groups (one 2 KB batch pair in flight per row group), INT4 at most 4096 waves.
+    // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 at M = 1
+    // with K <= 4096: activations in registers, about 1600 waves (six per CU), each
+    // with a whole number of row groups.  INT8: the LDS variant with 4-tile batches and
+    // about 4736 waves.  Otherwise (INT4 with M > 1 or K > 4096): the LDS variant with
+    // 8-tile batches and at most 4096 waves.  4-wave workgroups throughout.
     const qw::TileLayout L = qw::tile_layout(bits, N, K);
     const int nw = 4;
-    if (bits == 4 && M == 1 && L.cg <= qw::kRegCG) {
-        const int64_t nwaves = L.nrg < 2048 ? L.nrg : 2048;
-        if (((int64_t)L.nrg + nwaves - 1) / nwaves <= 64)
-            return make_tiling(bits, M, N, K, 0, nw, (int)nwaves);
-    }
-    int64_t nwaves;
+    const int64_t nrg = L.nrg;
+    auto waves_for = [&](int64_t target) {
+        int64_t per = (nrg + target / 2) / target;
+        per = per < 1 ? 1 : (per > 64 ? 64 : per);
+        return (nrg + per - 1) / per;
+    };
+    if (bits == 4 && M == 1 && L.cg <= qw::kRegCG)
+        return make_tiling(bits, M, N, K, 0, nw, (int)waves_for(1600));
     if (bits == 8)
-        nwaves = ((int64_t)L.nrg + 1) / 2;
-    else
-        nwaves = L.nrg < 4096 ? L.nrg : 4096;
-    while (((int64_t)L.nrg + nwaves - 1) / nwaves > 64)
+        return make_tiling(bits, M, N, K, 4, nw, (int)waves_for(4736));
+    int64_t nwaves = nrg < 4096 ? nrg : 4096;
+    while ((nrg + nwaves - 1) / nwaves > 64)
         nwaves *= 2;
-    if (nwaves > L.nrg)
-        nwaves = L.nrg;
+    if (nwaves > nrg)
+        nwaves = nrg;
     return make_tiling(bits, M, N, K, 8, nw, (int)nwaves);
 }
 

@@ -116,6 +116,14 @@ __device__ __forceinline__ uint4 load16(rsrc_t r, uint32_t offset)
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
 }
 
+// Weight stream: 16 bytes with the non-temporal hint.  Each weight byte is read once
+// per launch, so the hint keeps X and the scales, which every workgroup reads, from
+// being pushed out of L2 by the stream.
+__device__ __forceinline__ uint4 load16_stream(rsrc_t r, uint32_t offset)
+{
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 2));
+}
+
 __device__ __forceinline__ float4 load16f(rsrc_t r, uint32_t offset)
 {
     return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, offset, 0, 0));
@@ -137,6 +145,17 @@ __device__ __forceinline__ uint16_t load2(rsrc_t r, uint32_t offset)
 // which need only be complete, not flushed from a cache, before the hand-off
 // counter is bumped.  (A device-scope fence on a multi-die part writes back and
 // invalidates the whole L2.)
+// Issue-order barrier: every wave of the workgroup has issued its loads above this
+// point before any wave issues a load below it.  A CU serves vector loads in order,
+// so the small loads every wave waits on first (X) are not queued behind the weight
+// streams of the workgroup's other waves.  No memory ordering is implied.
+__device__ __forceinline__ void issue_barrier()
+{
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+}
+
 __device__ __forceinline__ void wait_memory_ops()
 {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");

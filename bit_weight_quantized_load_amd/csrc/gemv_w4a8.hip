@@ -65,6 +65,92 @@ __device__ __forceinline__ void load_act(const uint32_t* p, uint32_t (&a)[8])
     a[4] = o.x; a[5] = o.y; a[6] = o.z; a[7] = o.w;
 }
 
+// Block `blk` of X row m0 + mm (XV float4 per thread, kThreads threads) into xv.
+// Rows past the workgroup's mt rows and elements past K read zeros.
+template <int XV, int kThreads>
+__device__ __forceinline__ void load_x_block(const W4A8Args& p, int m0, int mt, int mm, int blk,
+                                             int tid, float4 (&xv)[XV])
+{
+    const rsrc_t xr = make_rsrc(p.X + (size_t)(m0 + mm) * p.K, mm < mt ? (uint32_t)p.K * 4u : 0u);
+#pragma unroll
+    for (int i = 0; i < XV; ++i)
+        xv[i] = load16f(xr, (uint32_t)(blk * XV * kThreads + i * kThreads + tid) * 16u);
+}
+
+// The activation prologue (the per-vector dynamic quantization of the Jetson Orin
+// INT4 write-up, section 当前实现方式), for the MT rows of X of this workgroup: per
+// row a = maxabs / 127 and codes clamp(rint(x / a), -127, 127), written to LDS at
+// act + mm * chunks * 8 words.  In chunk c (32 consecutive k), word 2d holds the
+// codes of k = 32c + 8d + {0, 2, 4, 6} and word 2d + 1 those of k = 32c + 8d + {1, 3,
+// 5, 7}, the order in which the INT4 unpack presents the weights; padding chunks are
+// zero.  Block 0 of row 0 must already be in xv.  kOne: K fits one block, so X is
+// never re-read; the only wait before the codes are written is then the one for X
+// itself, not for weight loads issued after it.
+template <int MT, int NW, int XV, bool kOne, bool kDebug>
+__device__ __forceinline__ void quantize_rows(const W4A8Args& p, float4 (&xv)[XV],
+                                              uint32_t* act, float (&s_red)[MT][NW],
+                                              float (&s_a)[MT], int chunks, int nblk, int m0,
+                                              int mt, int tid)
+{
+    constexpr int kThreads = 64 * NW;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int K4 = p.K >> 2;
+    const int cpr = p.K >> 5;  // real chunks per row
+    const int nb = kOne ? 1 : nblk;
+#pragma unroll
+    for (int mm = 0; mm < MT; ++mm) {
+        float mx = 0.0f;
+        for (int blk = 0; blk < nb; ++blk) {
+            if (mm > 0 || blk > 0)
+                load_x_block<XV, kThreads>(p, m0, mt, mm, blk, tid, xv);
+#pragma unroll
+            for (int i = 0; i < XV; ++i)
+                mx = fmaxf(mx, max_abs4(xv[i]));  // past K the loads read zeros
+        }
+        mx = wave_max_dpp(mx);
+        if (lane == 0)
+            s_red[mm][wave] = mx;
+        __syncthreads();
+        mx = s_red[mm][0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w)
+            mx = fmaxf(mx, s_red[mm][w]);
+        const float a = mx / 127.0f;
+        const float r = 1.0f / a;
+        const bool fast = r <= 3.0e38f;  // finite reciprocal (a is not 0 or tiny)
+        if (tid == 0)
+            s_a[mm] = a;
+        uint16_t* act16 = reinterpret_cast<uint16_t*>(act + (size_t)mm * chunks * 8);
+        for (int blk = 0; blk < nb; ++blk) {
+            if (!kOne)
+                load_x_block<XV, kThreads>(p, m0, mt, mm, blk, tid, xv);
+#pragma unroll
+            for (int i = 0; i < XV; ++i) {
+                const int f = blk * XV * kThreads + i * kThreads + tid;  // k = 4f .. 4f+3
+                if (f < K4) {
+                    int q[4];
+                    quant4_i8(xv[i], a, r, fast, q);
+                    // chunk f/8, 8-group (f/2)%4, half f%2: even codes -> word 2d, odd -> 2d+1
+                    const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
+                    const int wi = (c * 8 + 2 * d) * 2 + h;  // halfword index in the even word
+                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
+                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
+                    if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
+                        *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * p.K + 4 * f) =
+                            pack_i8x4(q[0], q[1], q[2], q[3]);
+                }
+            }
+        }
+        // zero codes for the padding chunks
+        for (int w = cpr * 8 + tid; w < chunks * 8; w += kThreads)
+            act[(size_t)mm * chunks * 8 + w] = 0u;
+    }
+    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
+        p.dbg_a[m0 + tid] = s_a[tid];
+    __syncthreads();
+}
+
 // RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
 // RCG == 0: LDS variant, U tiles per batch.
 template <int MT, int RCG, int U, int NW, bool kDebug>
@@ -91,7 +177,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
     const int K4 = K >> 2;
     const int nb = kReg ? 1 : (CG + U - 1) / U;  // batches per row group
     const int chunks = nb * kB * 16;              // chunks per X row in LDS (zero padded)
-    const int cpr = K >> 5;                       // real chunks per row
 
     // ---- this wave's run of tiles
     // Waves along N split the row groups evenly: wave gw owns [gw*nrg/W, (gw+1)*nrg/W).
@@ -118,9 +203,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
         _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
         {                                                                                       \
             const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
-            WBUF[u_] = load16(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
                                         : 0x80000000u);                                         \
         }                                                                                       \
+        /* keep the batch's loads ahead of the dots that follow: without this the    */       \
+        /* scheduler sinks them below the previous batch's dots, which then waits    */       \
+        /* for its whole batch first and only one batch is ever in flight            */       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
     }
 
     // ---- prologue: scales, X row 0, then the first weight batch
@@ -133,72 +222,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
         sc_reg[i] = load4(sres, (uint32_t)(tid + i * kThreads) * 4u);
     const int nblk = (K4 + XV * kThreads - 1) / (XV * kThreads);
     float4 xv[XV];
-#define QW_LOAD_X(MM, BLK)                                                                      \
-    {                                                                                           \
-        const rsrc_t xr_ = make_rsrc(p.X + (size_t)(m0 + (MM)) * K,                             \
-                                     (MM) < mt ? (uint32_t)K * 4u : 0u);                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < XV; ++i_)                                       \
-            xv[i_] = load16f(xr_, (uint32_t)((BLK) * XV * kThreads + i_ * kThreads + tid) * 16u); \
-    }
-    QW_LOAD_X(0, 0);
+    load_x_block<XV, kThreads>(p, m0, mt, 0, 0, tid, xv);
+    issue_barrier();
     QW_LOAD(wa, 0);
     // unconditional stores (rows past the block read zeros): a guarded store would
     // let the compiler sink the scale load behind the weight loads
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         s_scale[tid + i * kThreads] = __uint_as_float(sc_reg[i]);
-
-    for (int mm = 0; mm < MT; ++mm) {
-        float mx = 0.0f;
-        for (int blk = 0; blk < nblk; ++blk) {
-            if (mm > 0 || blk > 0)
-                QW_LOAD_X(mm, blk);
-#pragma unroll
-            for (int i = 0; i < XV; ++i)
-                mx = fmaxf(mx, max_abs4(xv[i]));  // past K the loads read zeros
-        }
-        mx = wave_max_dpp(mx);
-        if (lane == 0)
-            s_red[mm][wave] = mx;
-        __syncthreads();
-        mx = s_red[mm][0];
-#pragma unroll
-        for (int w = 1; w < NW; ++w)
-            mx = fmaxf(mx, s_red[mm][w]);
-        const float a = mx / 127.0f;
-        const float r = 1.0f / a;
-        const bool fast = r <= 3.0e38f;  // finite reciprocal (a is not 0 or tiny)
-        if (tid == 0)
-            s_a[mm] = a;
-        uint16_t* act16 = reinterpret_cast<uint16_t*>(s_dyn + (size_t)mm * chunks * 8);
-        for (int blk = 0; blk < nblk; ++blk) {
-            if (nblk > 1)
-                QW_LOAD_X(mm, blk);
-#pragma unroll
-            for (int i = 0; i < XV; ++i) {
-                const int f = blk * XV * kThreads + i * kThreads + tid;  // k = 4f .. 4f+3
-                if (f < K4) {
-                    int q[4];
-                    quant4_i8(xv[i], a, r, fast, q);
-                    // chunk f/8, 8-group (f/2)%4, half f%2: even codes -> word 2d, odd -> 2d+1
-                    const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
-                    const int wi = (c * 8 + 2 * d) * 2 + h;  // halfword index in the even word
-                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
-                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
-                    if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
-                        *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * K + 4 * f) =
-                            pack_i8x4(q[0], q[1], q[2], q[3]);
-                }
-            }
-        }
-        // zero codes for the padding chunks
-        for (int w = cpr * 8 + tid; w < chunks * 8; w += kThreads)
-            s_dyn[(size_t)mm * chunks * 8 + w] = 0u;
-    }
-    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
-        p.dbg_a[m0 + tid] = s_a[tid];
-    __syncthreads();
-#undef QW_LOAD_X
+    if (kReg || nblk == 1)
+        quantize_rows<MT, NW, XV, true, kDebug>(p, xv, s_dyn, s_red, s_a, chunks, nblk, m0, mt, tid);
+    else
+        quantize_rows<MT, NW, XV, false, kDebug>(p, xv, s_dyn, s_red, s_a, chunks, nblk, m0, mt, tid);
 
     const int nw0 = rg0 * 4;  // first row of this wave
     auto finish_row_group = [&](int (&acc)[4], int mm, int rgi) {
@@ -224,14 +259,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
             _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk(WBUF[c_], act[c_], acc_); \
             finish_row_group(acc_, 0, (Q));                                                     \
         }
-        for (int q = 0; q < nq; q += 2) {
+        // Pairs of batches with no branch in the loop body, the odd one after it: an
+        // exit from the middle of the body would let the compiler see the next batch
+        // as possibly pending at the loop head and wait for every load there.
+        int q = 0;
+        for (; q + 1 < nq; q += 2) {
             QW_LOAD(wb, q + 1);
             QW_COMPUTE(wa, q);
-            if (q + 1 >= nq)
-                break;
             QW_LOAD(wa, q + 2);
             QW_COMPUTE(wb, q + 1);
         }
+        if (q < nq)
+            QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
     } else {
         // ---- LDS variant: U tiles per batch, codes read from LDS per tile
@@ -258,14 +297,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
                 }                                                                               \
             }                                                                                   \
         }
-        for (int q = 0; q < nq; q += 2) {
+        // Pairs of batches with no branch in the loop body, the odd one after it: an
+        // exit from the middle of the body would let the compiler see the next batch
+        // as possibly pending at the loop head and wait for every load there.
+        int q = 0;
+        for (; q + 1 < nq; q += 2) {
             QW_LOAD(wb, q + 1);
             QW_COMPUTE(wa, q);
-            if (q + 1 >= nq)
-                break;
             QW_LOAD(wa, q + 2);
             QW_COMPUTE(wb, q + 1);
         }
+        if (q < nq)
+            QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
     }
 #undef QW_LOAD
@@ -291,7 +334,6 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
     const int mt = min(MT, M - m0);
     const int K4 = K >> 2;
     const int chunks = CG * 16;
-    const int cpr = K >> 5;
 
     const int W = p.nwaves;
     const int gw0 = blockIdx.x * NW;
@@ -317,71 +359,19 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
     constexpr int XV = 4;
     const int nblk = (K4 + XV * kThreads - 1) / (XV * kThreads);
     float4 xv[XV];
-#define QW_LOAD_X(MM, BLK)                                                                      \
-    {                                                                                           \
-        const rsrc_t xr_ = make_rsrc(p.X + (size_t)(m0 + (MM)) * K,                             \
-                                     (MM) < mt ? (uint32_t)K * 4u : 0u);                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < XV; ++i_)                                       \
-            xv[i_] = load16f(xr_, (uint32_t)((BLK) * XV * kThreads + i_ * kThreads + tid) * 16u); \
-    }
-    QW_LOAD_X(0, 0);
+    load_x_block<XV, kThreads>(p, m0, mt, 0, 0, tid, xv);
+    issue_barrier();
     uint4 w[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
-        w[t] = load16(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
+        w[t] = load16_stream(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
         s_scale[tid + i * kThreads] = __uint_as_float(sc_reg[i]);
-
-    for (int mm = 0; mm < MT; ++mm) {
-        float mx = 0.0f;
-        for (int blk = 0; blk < nblk; ++blk) {
-            if (mm > 0 || blk > 0)
-                QW_LOAD_X(mm, blk);
-#pragma unroll
-            for (int i = 0; i < XV; ++i)
-                mx = fmaxf(mx, max_abs4(xv[i]));
-        }
-        mx = wave_max_dpp(mx);
-        if (lane == 0)
-            s_red[mm][wave] = mx;
-        __syncthreads();
-        mx = s_red[mm][0];
-#pragma unroll
-        for (int w_ = 1; w_ < NW; ++w_)
-            mx = fmaxf(mx, s_red[mm][w_]);
-        const float a = mx / 127.0f;
-        const float r = 1.0f / a;
-        const bool fast = r <= 3.0e38f;
-        if (tid == 0)
-            s_a[mm] = a;
-        uint16_t* act16 = reinterpret_cast<uint16_t*>(s_dyn + (size_t)mm * chunks * 8);
-        for (int blk = 0; blk < nblk; ++blk) {
-            if (nblk > 1)
-                QW_LOAD_X(mm, blk);
-#pragma unroll
-            for (int i = 0; i < XV; ++i) {
-                const int f = blk * XV * kThreads + i * kThreads + tid;
-                if (f < K4) {
-                    int q[4];
-                    quant4_i8(xv[i], a, r, fast, q);
-                    const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
-                    const int wi = (c * 8 + 2 * d) * 2 + h;
-                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
-                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
-                    if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
-                        *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * K + 4 * f) =
-                            pack_i8x4(q[0], q[1], q[2], q[3]);
-                }
-            }
-        }
-        for (int w_ = cpr * 8 + tid; w_ < chunks * 8; w_ += kThreads)
-            s_dyn[(size_t)mm * chunks * 8 + w_] = 0u;
-    }
-    if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
-        p.dbg_a[m0 + tid] = s_a[tid];
-    __syncthreads();
-#undef QW_LOAD_X
+    if (nblk == 1)
+        quantize_rows<MT, NW, XV, true, kDebug>(p, xv, s_dyn, s_red, s_a, chunks, nblk, m0, mt, tid);
+    else
+        quantize_rows<MT, NW, XV, false, kDebug>(p, xv, s_dyn, s_red, s_a, chunks, nblk, m0, mt, tid);
 
     // ---- tiles in order; the codes of the next tile are read while this one computes
     int acc[MT][4];

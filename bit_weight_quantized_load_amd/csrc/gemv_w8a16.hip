@@ -54,6 +54,53 @@ __device__ __forceinline__ void split8(const uint4 e, const uint4 o, uint32_t (&
     a[4] = o.x; a[5] = o.y; a[6] = o.z; a[7] = o.w;
 }
 
+// X (f16) staged in LDS in chunk order: row mm's chunk c (16 f16) is 16-byte pieces
+// mm * 2 * chunks + 2c and + 2c + 1; pieces past K read zeros.  Pass `pass` of the
+// pieces, kXP per thread, into xp.
+template <int MT, int kXP, int kThreads>
+__device__ __forceinline__ void load_x_pass(rsrc_t xres, int chunks, int K, int pass, int tid,
+                                            uint4 (&xp)[kXP])
+{
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int q = pass * kXP * kThreads + i * kThreads + tid;
+        const int mm = q / (chunks * 2);
+        const int r = q - mm * (chunks * 2);
+        const bool in = mm < MT && r * 8 < K;
+        xp[i] = load16(xres, in ? (uint32_t)(mm * K + r * 8) * 2u : 0x80000000u);
+    }
+}
+
+// Writes the staged pieces to LDS; xp holds pass 0 on entry.  One pass (K <= 8192
+// at MT = 1 with 4 waves) is a straight line whose stores wait for X alone, not for
+// the weight loads issued after it.
+template <int MT, int kXP, int kThreads>
+__device__ __forceinline__ void store_x(rsrc_t xres, uint4 (&xp)[kXP], uint32_t* lds, int chunks,
+                                        int K, int tid)
+{
+    const int pieces = MT * chunks * 2;
+    const int npass = (pieces + kXP * kThreads - 1) / (kXP * kThreads);
+    if (npass == 1) {
+#pragma unroll
+        for (int i = 0; i < kXP; ++i) {
+            const int q = i * kThreads + tid;
+            if (q < pieces)
+                reinterpret_cast<uint4*>(lds)[q] = xp[i];
+        }
+    } else {
+        for (int pass = 0; pass < npass; ++pass) {
+            if (pass > 0)
+                load_x_pass<MT, kXP, kThreads>(xres, chunks, K, pass, tid, xp);
+#pragma unroll
+            for (int i = 0; i < kXP; ++i) {
+                const int q = pass * kXP * kThreads + i * kThreads + tid;
+                if (q < pieces)
+                    reinterpret_cast<uint4*>(lds)[q] = xp[i];
+            }
+        }
+    }
+}
+
 // RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
 // RCG == 0: LDS variant, U tiles per batch.
 template <int MT, int RCG, int U, int NW>
@@ -97,9 +144,13 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
         _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
         {                                                                                       \
             const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
-            WBUF[u_] = load16(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
                                         : 0x80000000u);                                         \
         }                                                                                       \
+        /* keep the batch's loads ahead of the dots that follow: without this the    */       \
+        /* scheduler sinks them below the previous batch's dots, which then waits    */       \
+        /* for its whole batch first and only one batch is ever in flight            */       \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
     }
 
     // ---- prologue: scales, activations, then the first weight batch
@@ -122,35 +173,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
             const uint4 o = load16(xres, (c * 32 + j) * 16 < K ? xo + 16u : 0x80000000u);
             split8(e, o, act[c]);
         }
+        issue_barrier();
         QW_LOAD(wa, 0);
     } else {
         // stage X in LDS: 16-byte pieces, 2 per chunk
         constexpr int kXP = 4;
-        const int pieces = MT * chunks * 2;
-        const int npass = (pieces + kXP * kThreads - 1) / (kXP * kThreads);
         uint4 xp[kXP];
-#define QW_LOAD_XP(PASS)                                                                        \
-        _Pragma("unroll") for (int i_ = 0; i_ < kXP; ++i_)                                      \
-        {                                                                                       \
-            const int q_ = (PASS) * kXP * kThreads + i_ * kThreads + tid;                       \
-            const int mm_ = q_ / (chunks * 2);                                                  \
-            const int r_ = q_ - mm_ * (chunks * 2);                                             \
-            const bool in_ = mm_ < MT && r_ * 8 < K;                                            \
-            xp[i_] = load16(xres, in_ ? (uint32_t)(mm_ * K + r_ * 8) * 2u : 0x80000000u);      \
-        }
-        QW_LOAD_XP(0);
+        load_x_pass<MT, kXP, kThreads>(xres, chunks, K, 0, tid, xp);
+        issue_barrier();
         QW_LOAD(wa, 0);
-        for (int pass = 0; pass < npass; ++pass) {
-            if (pass > 0)
-                QW_LOAD_XP(pass);
-#pragma unroll
-            for (int i = 0; i < kXP; ++i) {
-                const int q = pass * kXP * kThreads + i * kThreads + tid;
-                if (q < pieces)
-                    reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
-            }
-        }
-#undef QW_LOAD_XP
+        store_x<MT, kXP, kThreads>(xres, xp, s_dyn, chunks, K, tid);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -174,14 +206,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
             _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk_f16(WBUF[c_], act[c_], acc_); \
             finish_row_group(acc_, 0, (Q));                                                     \
         }
-        for (int q = 0; q < nq; q += 2) {
+        // Pairs of batches with no branch in the loop body, the odd one after it: an
+        // exit from the middle of the body would let the compiler see the next batch
+        // as possibly pending at the loop head and wait for every load there.
+        int q = 0;
+        for (; q + 1 < nq; q += 2) {
             QW_LOAD(wb, q + 1);
             QW_COMPUTE(wa, q);
-            if (q + 1 >= nq)
-                break;
             QW_LOAD(wa, q + 2);
             QW_COMPUTE(wb, q + 1);
         }
+        if (q < nq)
+            QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
     } else {
         float acc[MT][4];
@@ -211,14 +247,18 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
                 }                                                                               \
             }                                                                                   \
         }
-        for (int q = 0; q < nq; q += 2) {
+        // Pairs of batches with no branch in the loop body, the odd one after it: an
+        // exit from the middle of the body would let the compiler see the next batch
+        // as possibly pending at the loop head and wait for every load there.
+        int q = 0;
+        for (; q + 1 < nq; q += 2) {
             QW_LOAD(wb, q + 1);
             QW_COMPUTE(wa, q);
-            if (q + 1 >= nq)
-                break;
             QW_LOAD(wa, q + 2);
             QW_COMPUTE(wb, q + 1);
         }
+        if (q < nq)
+            QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
     }
 #undef QW_LOAD
@@ -264,34 +304,14 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16_eager(W8A16Args p)
         sc_reg[i] = load2(sres, (uint32_t)(tid + i * kThreads) * 2u);
     const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)mt * (uint32_t)K * 2u);
     constexpr int kXP = 4;
-    const int pieces = MT * chunks * 2;
-    const int npass = (pieces + kXP * kThreads - 1) / (kXP * kThreads);
     uint4 xp[kXP];
-#define QW_LOAD_XP(PASS)                                                                        \
-    _Pragma("unroll") for (int i_ = 0; i_ < kXP; ++i_)                                          \
-    {                                                                                           \
-        const int q_ = (PASS) * kXP * kThreads + i_ * kThreads + tid;                           \
-        const int mm_ = q_ / (chunks * 2);                                                      \
-        const int r_ = q_ - mm_ * (chunks * 2);                                                 \
-        const bool in_ = mm_ < MT && r_ * 8 < K;                                                \
-        xp[i_] = load16(xres, in_ ? (uint32_t)(mm_ * K + r_ * 8) * 2u : 0x80000000u);          \
-    }
-    QW_LOAD_XP(0);
+    load_x_pass<MT, kXP, kThreads>(xres, chunks, K, 0, tid, xp);
+    issue_barrier();
     uint4 w[TMAX];
 #pragma unroll
     for (int t = 0; t < TMAX; ++t)
-        w[t] = load16(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
-    for (int pass = 0; pass < npass; ++pass) {
-        if (pass > 0)
-            QW_LOAD_XP(pass);
-#pragma unroll
-        for (int i = 0; i < kXP; ++i) {
-            const int q = pass * kXP * kThreads + i * kThreads + tid;
-            if (q < pieces)
-                reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
-        }
-    }
-#undef QW_LOAD_XP
+        w[t] = load16_stream(wres, t < T ? wbase + (uint32_t)t * 1024u : 0x80000000u);
+    store_x<MT, kXP, kThreads>(xres, xp, s_dyn, chunks, K, tid);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         s_scale[tid + i * kThreads] = sc_reg[i];

@@ -257,11 +257,12 @@ size_t qw_w8_packed_bytes(int64_t N, int64_t K)
 
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
 {
-    (void)op;
-    (void)M;
     (void)N;
-    (void)K;
-    return 0;  // no kernel of this version keeps state between workgroups
+    // Only the W4A8 skinny GEMM (M >= 16) needs one: the activation codes and scales,
+    // quantized once per call in the matrix cores' operand order.
+    if (op == 0 && M >= qw::kMfmaMinM && M <= kMaxM && K > 0 && K <= kMaxK)
+        return qw::mfma_w4a8_workspace_bytes(M, K);
+    return 0;
 }
 
 int qw_workspace_clear(void* workspace, size_t ws_bytes, void* stream)
@@ -342,9 +343,20 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream)
 {
-    (void)ws_bytes;
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (M >= qw::kMfmaMinM) {
+        if (!X || !Wq || !w_scale || !Y)
+            return QW_ERR_NULL;
+        if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+            !aligned16(workspace))
+            return QW_ERR_ALIGN;
+        if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
+            return QW_ERR_WORKSPACE;
+        return hip_status(qw::launch_gemm_w4a8(X, (int)M, (int)N, (int)K,
+                                               static_cast<const uint8_t*>(Wq), w_scale, Y,
+                                               workspace, static_cast<hipStream_t>(stream)));
+    }
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
                     default_tiling(4, M, N, K), false, stream);
 }
@@ -381,6 +393,16 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
     (void)ws_bytes;
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (M >= qw::kMfmaMinM) {
+        if (!X_f16 || !Wq || !w_scale_f16 || !Y_f16)
+            return QW_ERR_NULL;
+        if (!aligned16(X_f16) || !aligned16(Wq) || !aligned16(w_scale_f16) || !aligned16(Y_f16) ||
+            !aligned16(workspace))
+            return QW_ERR_ALIGN;
+        return hip_status(qw::launch_gemm_w8a16(X_f16, (int)M, (int)N, (int)K,
+                                                static_cast<const uint8_t*>(Wq), w_scale_f16,
+                                                Y_f16, static_cast<hipStream_t>(stream)));
+    }
     return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace,
                      default_tiling(8, M, N, K), stream);
 }

@@ -78,6 +78,38 @@ struct W8A16Args {
     int cg, nrg, nwaves;
 };
 
+// Skinny GEMM (M >= kMfmaMinM) on the matrix cores.
+constexpr int kMfmaMinM = 16;
+
+struct MfmaW4A8Args {
+    const uint8_t* Xp;      // X codes in MFMA operand order (workspace)
+    const float* a_scale;   // [M] (workspace)
+    const uint8_t* Wq;
+    const float* w_scale;
+    float* Y;
+    int M, N, K;
+    int cg, nrg;
+    int ks;       // 64-k steps = ceil(K / 64)
+    int mbtot;    // 16-row blocks of X = ceil(M / 16)
+    int mgroups;  // workgroups along M
+};
+
+struct MfmaW8A16Args {
+    const uint16_t* X;
+    const uint8_t* Wq;
+    const uint16_t* w_scale;
+    uint16_t* Y;
+    int M, N, K;
+    int cg, nrg;
+    int mgroups;
+};
+
+size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K);
+hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
+                            const float* w_scale, float* Y, void* workspace, hipStream_t st);
+hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
+                             const uint16_t* w_scale, uint16_t* Y, hipStream_t st);
+
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,
                           hipStream_t st);
 hipError_t launch_pack_w8(const float* W, int N, int K, uint8_t* Wq, uint16_t* s, int* flag,

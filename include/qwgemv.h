@@ -59,23 +59,27 @@ enum {
 /* Bytes of the packed weights, and their layout.  The packed buffer is a sequence
    of 1 KB tiles.  A chunk is 16 bytes of one row: 32 INT4 codes (byte j holds
    k = 2j in its low nibble and k = 2j+1 in its high nibble, 4-bit two's complement)
-   or 16 INT8 codes.  Tile (rg, cg) holds rows 4rg..4rg+3 by chunks 16cg..16cg+15,
-   16-byte slot 16*(n % 4) + (chunk % 16) holding row n's chunk; tiles are stored
-   row group by row group, chunk groups in order within a row group, so a wave of
-   64 lanes loading 16 bytes each reads one tile as 1 KB of contiguous memory.
-   Rows past N and chunks past K are zero padding.  Size:
-   ceil(N/4) * ceil(K/512) KB for INT4 and ceil(N/4) * ceil(K/256) KB for INT8, which
-   is N*K/2 and N*K when N % 4 == 0 and K is a multiple of 512 (256).  Returns 0 for
-   an invalid shape.  qw_w4_codes / qw_w8_codes decode the layout back to codes. */
+   or 16 INT8 codes.  A tile covers 512 consecutive k of R rows: R = 4 rows of 16
+   chunks (INT4) or R = 2 rows of 32 chunks (INT8).  Tile (rg, t) holds rows
+   R*rg .. R*rg+R-1 and k 512t .. 512t+511; inside it, 16-byte slot
+   (n % R) * (64/R) + (chunk % (64/R)) holds row n's chunk.  Tiles are stored row group
+   by row group, in k order within a row group, so a wave of 64 lanes loading 16
+   bytes each reads one tile as 1 KB of contiguous memory.  Rows past N and chunks
+   past K are zero padding.  Size: ceil(N/4) * ceil(K/512) KB for INT4 and
+   ceil(N/2) * ceil(K/512) KB for INT8, which is N*K/2 and N*K when N % 4 == 0
+   (N % 2 == 0) and K is a multiple of 512.  Returns 0 for an invalid shape.
+   qw_w4_codes / qw_w8_codes decode the layout back to codes. */
 size_t qw_w4_packed_bytes(int64_t N, int64_t K);
 size_t qw_w8_packed_bytes(int64_t N, int64_t K);
 
 /* Workspace that gemv_w4a8 (op 0) or gemv_w8a16 (op 1) needs for shape (M, N, K).
-   0 means the call needs none and accepts workspace == NULL; every kernel of this
-   version finishes its rows inside one workgroup, so this returns 0 for every
-   shape.  Callers that pass a workspace anyway must size it with this function and
-   zero-fill it before first use (qw_workspace_clear); the library leaves it
-   zero-filled. */
+   0 means the call needs none and accepts workspace == NULL: every GEMV (M < 16)
+   finishes its rows inside one workgroup, and gemv_w8a16 needs none at any M.
+   gemv_w4a8 with M >= 16 runs on the matrix cores and needs
+   align256(ceil(M/16) * ceil(K/64) * 1024) + align256(4 * M) bytes: the activation
+   codes and scales, quantized once per call in operand order.  Its contents need
+   no initialisation and are overwritten by every call; calls that share one
+   workspace must not overlap in time. */
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
 
 /* Zero-fills a workspace with a kernel (no memset node, safe to capture). */
@@ -105,18 +109,24 @@ int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w
 int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scale,
                  void* stream);
 
-/* W4A8 linear, activation quantization fused into the prologue.
+/* W4A8 linear ("Jetson Orin AGX 上的 INT4 量化推理实践", sections 当前实现方式 and 正确方向).
    X fp32 [M][K], Wq from quantize_pack_w4, w_scale fp32 [N] -> Y fp32 [M][N] with
    Y[m][n] = ((float)acc[m][n] * w_scale[n]) * a_scale[m] and
-   acc[m][n] = sum_k q[n][k] * xq[m][k] in int32.  workspace/ws_bytes as described at
-   qw_workspace_bytes (op 0). */
+   acc[m][n] = sum_k q[n][k] * xq[m][k] in int32, where xq and a_scale are exactly
+   what quant_act_i8 computes.  M < 16: one GEMV kernel with the activation
+   quantization fused into its prologue; workspace may be NULL.  M >= 16: the
+   quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
+   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM; results are the same
+   bits as the GEMV's. */
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
 
-/* W8A16 linear.  X f16 [M][K], Wq from quantize_pack_w8, w_scale_f16 [N] -> Y f16 [M][N] with
+/* W8A16 linear (ChatGLM2-6B W8A16 write-up, section 4).  X f16 [M][K], Wq from
+   quantize_pack_w8, w_scale_f16 [N] -> Y f16 [M][N] with
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
-   rounding.  workspace as at qw_workspace_bytes (op 1). */
+   rounding.  M < 16: GEMV kernel; M >= 16: f16 matrix-core GEMM on the exactly cast
+   weights.  No workspace at any M (workspace may be NULL). */
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
                int64_t N, int64_t K, uint16_t* Y_f16, void* workspace, size_t ws_bytes,
                void* stream);

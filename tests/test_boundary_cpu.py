@@ -66,6 +66,20 @@ def test_no_shape_needs_a_workspace():
             assert L.qw_workspace_bytes(op, M, N, K) == 0
 
 
+def test_skinny_w4a8_workspace_size_and_checks():
+    def align(x):
+        return (x + 255) // 256 * 256
+    for (M, K) in [(16, 4096), (17, 544), (512, 4096), (65535, 3584)]:
+        want = align(-(-M // 16) * -(-K // 64) * 1024) + align(4 * M)
+        assert L.qw_workspace_bytes(0, M, 27392, K) == want, (M, K)
+        assert L.qw_workspace_bytes(1, M, 27392, K) == 0
+    # M >= 16 needs the workspace; validation fails before anything is launched
+    assert L.gemv_w4a8(A, A2, A3, 16, 64, 512, A4, NULL, 0, NULL) == qw.QW_ERR_WORKSPACE
+    need = L.qw_workspace_bytes(0, 16, 64, 512)
+    assert L.gemv_w4a8(A, A2, A3, 16, 64, 512, A4, A, need - 16, NULL) == qw.QW_ERR_WORKSPACE
+    assert L.gemv_w4a8(A, A2, A3, 16, 64, 512, A4, MIS, need, NULL) == qw.QW_ERR_ALIGN
+
+
 @pytest.mark.parametrize("fn", ["gemv_w4a8", "gemv_w8a16"])
 def test_gemv_rejects_bad_arguments(fn):
     f = getattr(L, fn)

@@ -243,6 +243,50 @@ def test_skinny_sweep_sampled(M):
     assert rel_l2(host(y[:, ridx]), y64) <= W8A16_RL2
 
 
+# ----------------------------------------------- skinny GEMM on the matrix cores --
+
+# M >= 16 runs the MFMA kernels: ragged M, N and K (K % 64 == 32 leaves half a step)
+MFMA_SHAPES = [(16, 64, 512), (17, 100, 544), (33, 257, 1056), (64, 128, 4096),
+               (65, 70, 1024), (100, 300, 2080), (130, 36, 3584)]
+
+
+@pytest.mark.parametrize("M,N,K", MFMA_SHAPES)
+def test_skinny_gemm_full_parity(M, N, K):
+    say("mfma", M, N, K)
+    W = wl.weights(300 + M, 1, N, K, outlier_rows=N >= 100)
+    W[0] = 0.0  # zero row
+    X = wl.activations(300 + M, 2, M, K, outlier_channels=4)
+    X[M // 2] = 0.0  # zero activation row
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    Xd = dev(X)
+    Y = qw.gemv_w4a8(Xd, Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+    assert_w4a8_close(host(Y), ref["Y"])
+    # the int32 sums are exact on both paths, so the GEMV kernels give the same bits
+    Yg = qw.gemv_w4a8_tiled(Xd, Wq, s, 8, 4, 7)
+    assert torch.equal(Y, Yg)
+    assert not torch.any(Y[M // 2]).item() and not torch.any(Y[:, 0]).item()
+    X16 = X.astype(np.float16)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
+    assert rel_l2(y, y64) <= W8A16_RL2
+    assert not np.any(y[M // 2]) and not np.any(y[:, 0])
+
+
+def test_skinny_gemm_workspace_reuse_and_sizes():
+    """One workspace sized for the larger call serves a smaller one after it."""
+    K, N = 1024, 96
+    W = wl.weights(400, 1, N, K)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ws = qw.make_workspace("w4a8", 80, N, K)
+    for M in (80, 16, 48):
+        X = wl.activations(400 + M, 2, M, K)
+        ref = oracle.gemv_w4a8(X, q_o, s_o)
+        Y = qw.gemv_w4a8(dev(X), Wq, s, workspace=ws)
+        assert_w4a8_close(host(Y), ref["Y"])
+
+
 # --------------------------------------------------------------- edge cases --
 
 EDGE = [(1, 1, 32), (1, 5, 96), (2, 17, 64), (3, 517, 288), (5, 64, 1024), (8, 100, 3584),

@@ -46,8 +46,10 @@ SIGNATURES = {
     "qw_w4_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_w8_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_gemv_w4a8_debug": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
-    "qw_gemv_w4a8_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
-    "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
+    "qw_gemv_w4a8_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
+    "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
+    "qw_gemm_w4a8_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
+    "qw_gemm_w8a16_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
 }
@@ -236,7 +238,7 @@ def gemv_w8a16(X16, Wq, w_scale16, workspace=None, out=None, stream=None):
     return Y
 
 
-def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, nwaves, out=None, stream=None):
+def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, nwaves, splitk=1, out=None, stream=None):
     """gemv_w4a8 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X.shape
@@ -245,11 +247,11 @@ def gemv_w4a8_tiled(X, Wq, w_scale, u, nw, nwaves, out=None, stream=None):
     _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
     _call("qw_gemv_w4a8_tiled", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y),
-          u, nw, nwaves, _stream(stream))
+          u, nw, nwaves, splitk, _stream(stream))
     return Y
 
 
-def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, nwaves, out=None, stream=None):
+def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, nwaves, splitk=1, out=None, stream=None):
     """gemv_w8a16 with an explicit launch shape (see include/qwgemv.h)."""
     torch = _torch()
     M, K = X16.shape
@@ -258,7 +260,43 @@ def gemv_w8a16_tiled(X16, Wq, w_scale16, u, nw, nwaves, out=None, stream=None):
     _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
     Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
     _call("qw_gemv_w8a16_tiled", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
-          u, nw, nwaves, _stream(stream))
+          u, nw, nwaves, splitk, _stream(stream))
+    return Y
+
+
+def gemm_w4a8_mfma(X, Wq, w_scale, nw=4, mb=1, nbw=1, workspace=None, out=None, stream=None):
+    """The W4A8 matrix-core kernel at any M with an explicit launch shape (nw waves per
+    workgroup, mb blocks of 16 rows of X per workgroup, nbw blocks of 16 output rows
+    per wave).  Needs a workspace of qw_workspace_bytes(2, M, N, K) bytes."""
+    torch = _torch()
+    M, K = X.shape
+    N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if workspace is None:
+        workspace = torch.empty((lib().qw_workspace_bytes(2, M, N, K),), dtype=torch.uint8,
+                                device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    wp, wn = _ws_args(workspace)
+    _call("qw_gemm_w4a8_mfma", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn,
+          nw, mb, nbw, _stream(stream))
+    return Y
+
+
+def gemm_w8a16_mfma(X16, Wq, w_scale16, nw=4, mb=1, nbw=1, out=None, stream=None):
+    """The W8A16 matrix-core kernel at any M with an explicit launch shape."""
+    torch = _torch()
+    M, K = X16.shape
+    N = w_scale16.shape[0]
+    _need(X16, torch.float16, (M, K), "X16")
+    _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
+    _need(w_scale16, torch.float16, (N,), "w_scale16")
+    Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
+    _need(Y, torch.float16, (M, N), "out")
+    _call("qw_gemm_w8a16_mfma", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
+          nw, mb, nbw, _stream(stream))
     return Y
 
 

@@ -1,9 +1,16 @@
-"""Build of the HIP library libqwgemv.so (gfx950) from csrc/, in the package folder."""
+"""Build of the HIP library libqwgemv.so (gfx950) from csrc/, in the package folder.
+
+Each csrc/*.hip is compiled to an object file in parallel (the GEMV sources hold many
+kernel instantiations), then the objects are linked into one shared library.
+"""
 from __future__ import annotations
 
+import concurrent.futures
 import glob
 import os
+import shutil
 import subprocess
+import tempfile
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
@@ -15,7 +22,6 @@ HIP_FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     "-fno-fast-math",
     "-ffp-contract=off",
     "-fno-gpu-flush-denormals-to-zero",
@@ -31,12 +37,28 @@ def sources():
 
 def build(verbose: bool = False) -> str:
     """Compile every csrc/*.hip into libqwgemv.so (always recompiles)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
-    subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
+    tmpdir = tempfile.mkdtemp(prefix="qwbuild")
+    try:
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
+            if verbose:
+                print(" ".join(cmd), flush=True)
+            subprocess.check_call(cmd)
+            return obj
+
+        srcs = sources()
+        workers = max(1, min(len(srcs), os.cpu_count() or 1, 16))
+        with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+            objs = list(ex.map(compile_one, srcs))
+        tmp = LIB + ".tmp%d" % os.getpid()
+        cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        subprocess.check_call(cmd)
+        os.replace(tmp, LIB)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     return LIB
 
 

@@ -61,9 +61,11 @@ int scale_lds_bytes(int bits, int nw) { return bits == 4 ? 4 * 64 * nw * 4 : 2 *
 // Launch-shape check.  u = 0: register variant (M == 1, K <= 4096); u = 1: eager
 // variant (at most 16 tiles per wave, at most 4 rows of X per workgroup); u = 4 or 8:
 // streaming LDS variant with u tiles per batch.  4, 8 or 16 waves per workgroup; at
-// most 64 row groups per wave (the workgroup's output scales are staged in LDS); a
-// workgroup's tiles addressable by one buffer resource.
-bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, const qw::TileLayout& L)
+// most 64 row groups per row run (the workgroup's output scales are staged in LDS); a
+// workgroup's tiles addressable by one buffer resource.  splitk 2 or 4: LDS variant
+// only, 4 or 8 waves, at most 16 row groups per row run.
+bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
+               const qw::TileLayout& L)
 {
     if (u != 0 && u != 1 && u != 4 && u != 8)
         return false;
@@ -71,10 +73,14 @@ bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, const qw::TileLay
         return false;
     if (nw != 4 && nw != 8 && nw != 16)
         return false;
+    if (splitk != 1 && splitk != 2 && splitk != 4)
+        return false;
+    if (splitk > 1 && (u < 4 || nw == 16))
+        return false;
     if (nwaves < 1)
         return false;
     const int64_t per_wave = ((int64_t)L.nrg + nwaves - 1) / nwaves;
-    if (per_wave > 64)
+    if (per_wave > (splitk > 1 ? 16 : 64))
         return false;
     if (u == 1 && per_wave * L.cg > 16)
         return false;
@@ -84,18 +90,21 @@ bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, const qw::TileLay
     return true;
 }
 
-GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw, int nwaves)
+GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw, int nwaves,
+                       int splitk = 1)
 {
     const qw::TileLayout L = qw::tile_layout(bits, N, K);
     GemvTiling t;
     t.u = u;
     t.nw = nw;
+    t.splitk = splitk;
     t.nwaves = nwaves;
-    t.blocks = (nwaves + nw - 1) / nw;
+    const int runs = nw / splitk;  // row runs per workgroup
+    t.blocks = (nwaves + runs - 1) / runs;
     t.tmax = 0;
     t.reg_cg = 0;
     const int scale_bytes = scale_lds_bytes(bits, nw);
-    int tiles = 0, mt_cap = 8;
+    int tiles = 0, mt_cap = splitk > 1 ? 2 : 8;
     if (u == 0) {
         t.reg_cg = L.cg;
         mt_cap = 1;
@@ -106,31 +115,38 @@ GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw,
         mt_cap = 4;
         tiles = L.cg;
     } else {
-        tiles = (L.cg + u - 1) / u * u;
+        const int slice = (L.cg + splitk - 1) / splitk;  // tiles per k-slice
+        tiles = splitk * ((slice + u - 1) / u) * u;
     }
+    // split-K partial sums: one int32 / fp32 per (run, row group, row of X, row, slice)
+    const int per_wave = (int)(((int64_t)L.nrg + nwaves - 1) / nwaves);
+    auto part_bytes = [&](int mt) {
+        return splitk > 1 ? nw * per_wave * mt * (bits == 4 ? 4 : 2) * 4 : 0;
+    };
     int mt = M >= 5 ? 8 : (M >= 3 ? 4 : (int)M);
     if (mt > mt_cap)
         mt = mt_cap;
-    while (mt > 1 && mt * tiles * act_tile_bytes(bits) + scale_bytes > kMaxLds)
+    while (mt > 1 && mt * tiles * act_tile_bytes(bits) + scale_bytes + part_bytes(mt) > kMaxLds)
         mt >>= 1;
     t.mt = mt;
-    t.lds_bytes = mt * tiles * act_tile_bytes(bits) + scale_bytes;
+    t.lds_bytes = mt * tiles * act_tile_bytes(bits) + scale_bytes + part_bytes(mt);
     t.m_tiles = (int)((M + t.mt - 1) / t.mt);
     return t;
 }
 
 bool fits_lds(const GemvTiling& t) { return t.lds_bytes <= kMaxLds; }
 
-// with 8 tiles per batch; 4 waves per workgroup.
+// Built-in launch shape of the GEMV kernels (M == 1 for W4A8, M <= 2 for W8A16).
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
-    // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 at M = 1
-    // with K <= 4096: activations in registers, about 1600 waves (six per CU), each
-    // with a whole number of row groups.  INT8: the LDS variant with 4-tile batches and
-    // about 4736 waves.  Otherwise (INT4 with M > 1 or K > 4096): the LDS variant with
-    // 8-tile batches and at most 4096 waves.  4-wave workgroups throughout.
+    // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 with
+    // K <= 4096: activations in registers, about 1600 waves (six per CU), each with a
+    // whole number of row groups.  INT8: the LDS variant with 4-tile batches and about
+    // 4736 waves.  INT4 with K > 4096: the LDS variant with 4-tile batches and 8-wave
+    // workgroups (one block of X per workgroup in the prologue); below 2048 row groups
+    // (the 18944 -> 3584 down projection) each row group is split over two waves along
+    // K, which measured 15.4 us against 19.5 us unsplit.
     const qw::TileLayout L = qw::tile_layout(bits, N, K);
-    const int nw = 4;
     const int64_t nrg = L.nrg;
     auto waves_for = [&](int64_t target) {
         int64_t per = (nrg + target / 2) / target;
@@ -138,15 +154,18 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         return (nrg + per - 1) / per;
     };
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG)
-        return make_tiling(bits, M, N, K, 0, nw, (int)waves_for(1600));
+        return make_tiling(bits, M, N, K, 0, 4, (int)waves_for(1600));
     if (bits == 8)
-        return make_tiling(bits, M, N, K, 4, nw, (int)waves_for(4736));
+        return make_tiling(bits, M, N, K, 4, 4, (int)waves_for(4736));
+    const GemvTiling t = nrg < 2048 ? make_tiling(bits, M, N, K, 4, 8, (int)nrg, 2)
+                                    : make_tiling(bits, M, N, K, 4, 8, (int)waves_for(4096));
+    if (t.lds_bytes <= kMaxLds)
+        return t;
+    // the longest rows of X: 4-wave workgroups, whose LDS holds one row of codes
     int64_t nwaves = nrg < 4096 ? nrg : 4096;
     while ((nrg + nwaves - 1) / nwaves > 64)
         nwaves *= 2;
-    if (nwaves > nrg)
-        nwaves = nrg;
-    return make_tiling(bits, M, N, K, 8, nw, (int)nwaves);
+    return make_tiling(bits, M, N, K, 8, 4, (int)(nwaves > nrg ? nrg : nwaves));
 }
 
 // One device int per GPU for the packers' non-finite flag.
@@ -193,6 +212,8 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
         !aligned16(workspace) || !aligned16(acc) || !aligned16(xq) || !aligned16(a_scale))
         return QW_ERR_ALIGN;
+    if (t.lds_bytes > kMaxLds)
+        return QW_ERR_TILING;
     const qw::TileLayout L = qw::tile_layout(4, N, K);
     qw::W4A8Args a;
     a.X = X;
@@ -222,6 +243,8 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
         !aligned16(workspace))
         return QW_ERR_ALIGN;
+    if (t.lds_bytes > kMaxLds)
+        return QW_ERR_TILING;
     const qw::TileLayout L = qw::tile_layout(8, N, K);
     qw::W8A16Args a;
     a.X = X;
@@ -235,6 +258,36 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     a.nrg = L.nrg;
     a.nwaves = t.nwaves;
     return hip_status(qw::launch_gemv_w8a16(a, t, static_cast<hipStream_t>(stream)));
+}
+
+int run_gemm_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, float* Y, void* workspace, size_t ws_bytes, int nw, int mb, int nbw,
+                  void* stream)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+        !aligned16(workspace))
+        return QW_ERR_ALIGN;
+    if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
+        return QW_ERR_WORKSPACE;
+    return hip_status(qw::launch_gemm_w4a8(X, (int)M, (int)N, (int)K,
+                                           static_cast<const uint8_t*>(Wq), w_scale, Y, workspace,
+                                           nw, mb, nbw, static_cast<hipStream_t>(stream)));
+}
+
+int run_gemm_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_t M,
+                   int64_t N, int64_t K, uint16_t* Y, void* workspace, int nw, int mb, int nbw,
+                   void* stream)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+        !aligned16(workspace))
+        return QW_ERR_ALIGN;
+    return hip_status(qw::launch_gemm_w8a16(X, (int)M, (int)N, (int)K,
+                                            static_cast<const uint8_t*>(Wq), w_scale, Y, nw, mb,
+                                            nbw, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -258,9 +311,12 @@ size_t qw_w8_packed_bytes(int64_t N, int64_t K)
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K)
 {
     (void)N;
-    // Only the W4A8 skinny GEMM (M >= 16) needs one: the activation codes and scales,
-    // quantized once per call in the matrix cores' operand order.
-    if (op == 0 && M >= qw::kMfmaMinM && M <= kMaxM && K > 0 && K <= kMaxK)
+    // Only the W4A8 matrix-core path needs one: the activation codes and scales,
+    // quantized once per call in the matrix cores' operand order.  op 2 is that path
+    // at any M (qw_gemm_w4a8_mfma).
+    if (M <= 0 || M > kMaxM || K <= 0 || K > kMaxK)
+        return 0;
+    if ((op == 0 && M >= qw::kMfmaMinM4) || op == 2)
         return qw::mfma_w4a8_workspace_bytes(M, K);
     return 0;
 }
@@ -345,17 +401,10 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
 {
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (M >= qw::kMfmaMinM) {
-        if (!X || !Wq || !w_scale || !Y)
-            return QW_ERR_NULL;
-        if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
-            !aligned16(workspace))
-            return QW_ERR_ALIGN;
-        if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
-            return QW_ERR_WORKSPACE;
-        return hip_status(qw::launch_gemm_w4a8(X, (int)M, (int)N, (int)K,
-                                               static_cast<const uint8_t*>(Wq), w_scale, Y,
-                                               workspace, static_cast<hipStream_t>(stream)));
+    if (M >= qw::kMfmaMinM4) {
+        int nw, mb, nbw;
+        qw::mfma_default_shape(4, M, &nw, &mb, &nbw);
+        return run_gemm_w4a8(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, nw, mb, nbw, stream);
     }
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
                     default_tiling(4, M, N, K), false, stream);
@@ -373,13 +422,14 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
 }
 
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves, void* stream)
+                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves, int splitk,
+                       void* stream)
 {
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(4, M, u, nw, nwaves, qw::tile_layout(4, N, K)))
+    if (!tiling_ok(4, M, u, nw, nwaves, splitk, qw::tile_layout(4, N, K)))
         return QW_ERR_TILING;
-    const GemvTiling t = make_tiling(4, M, N, K, u, nw, nwaves);
+    const GemvTiling t = make_tiling(4, M, N, K, u, nw, nwaves, splitk);
     if (!fits_lds(t))
         return QW_ERR_TILING;
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, nullptr, t, false,
@@ -393,15 +443,11 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
     (void)ws_bytes;
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (M >= qw::kMfmaMinM) {
-        if (!X_f16 || !Wq || !w_scale_f16 || !Y_f16)
-            return QW_ERR_NULL;
-        if (!aligned16(X_f16) || !aligned16(Wq) || !aligned16(w_scale_f16) || !aligned16(Y_f16) ||
-            !aligned16(workspace))
-            return QW_ERR_ALIGN;
-        return hip_status(qw::launch_gemm_w8a16(X_f16, (int)M, (int)N, (int)K,
-                                                static_cast<const uint8_t*>(Wq), w_scale_f16,
-                                                Y_f16, static_cast<hipStream_t>(stream)));
+    if (M >= qw::kMfmaMinM8) {
+        int nw, mb, nbw;
+        qw::mfma_default_shape(8, M, &nw, &mb, &nbw);
+        return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, nw, mb, nbw,
+                              stream);
     }
     return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace,
                      default_tiling(8, M, N, K), stream);
@@ -409,16 +455,38 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
 
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                         int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
-                        int nwaves, void* stream)
+                        int nwaves, int splitk, void* stream)
 {
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (!tiling_ok(8, M, u, nw, nwaves, qw::tile_layout(8, N, K)))
+    if (!tiling_ok(8, M, u, nw, nwaves, splitk, qw::tile_layout(8, N, K)))
         return QW_ERR_TILING;
-    const GemvTiling t = make_tiling(8, M, N, K, u, nw, nwaves);
+    const GemvTiling t = make_tiling(8, M, N, K, u, nw, nwaves, splitk);
     if (!fits_lds(t))
         return QW_ERR_TILING;
     return run_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, t, stream);
+}
+
+int qw_gemm_w4a8_mfma(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                      int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes, int nw,
+                      int mb, int nbw, void* stream)
+{
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
+        return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (!qw::mfma_shape_ok(4, nw, mb, nbw))
+        return QW_ERR_TILING;
+    return run_gemm_w4a8(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, nw, mb, nbw, stream);
+}
+
+int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
+                       int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int nw, int mb, int nbw,
+                       void* stream)
+{
+    if (check_gemv_shape(8, M, N, K) != QW_OK)
+        return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (!qw::mfma_shape_ok(8, nw, mb, nbw))
+        return QW_ERR_TILING;
+    return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, nw, mb, nbw, stream);
 }
 
 int qw_w4_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* stream)

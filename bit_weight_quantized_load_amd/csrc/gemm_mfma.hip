@@ -1,30 +1,36 @@
-// Skinny GEMM for M >= 16 on the matrix cores: the same linears as the GEMV kernels
-// (W4A8: "Jetson Orin AGX 上的 INT4 量化推理实践：从 9 tok/s 到 19.6 tok/s", sections
+// Skinny GEMM on the matrix cores: the same linears as the GEMV kernels (W4A8:
+// "Jetson Orin AGX 上的 INT4 量化推理实践：从 9 tok/s 到 19.6 tok/s", sections
 // 当前实现方式 and 正确方向; W8A16: ChatGLM2-6B W8A16 write-up (TPU-MLIR), section 4),
 // computed with v_mfma_i32_16x16x64_i8 (W4A8) and v_mfma_f32_16x16x32_f16 (W8A16).
 //
 // Operands.  For a 16x16xKL MFMA, lane l supplies row l % 16 of A and column l % 16 of
-// B, each at the KL consecutive k of block l / 16, and receives D[4 (l / 16) + i][l % 16]
+// B, each at the KL/4 consecutive k of block l / 16, and receives D[4 (l / 16) + i][l % 16]
 // for i = 0..3.  A is the weight (16 output rows n), B is X transposed (16 rows m), so
 // D holds Y transposed: D[n][m].
 //
-// Weights stay in the tile layout of the GEMV (kernels.hpp).  A workgroup owns 64
-// consecutive rows (four waves of 16 rows = 4 INT4 or 8 INT8 row groups) and a run of
-// row blocks of X; per 512-k tile each wave copies its tiles (one 1 KB wave load each)
-// into its own LDS region, padded so that the 16 lanes reading 16 different rows hit
-// different banks, and reads them back in operand order.
+// Work split.  A workgroup of NW waves owns NW * NBW * 16 consecutive output rows and
+// MB blocks of 16 rows of X; each wave owns NBW blocks of 16 output rows and walks K
+// in 512-k steps (one weight tile per row group).  Weights stay in the tile layout of
+// the GEMV (kernels.hpp): per step a wave issues one 1 KB wave load per row group it
+// owns, straight into registers, two steps ahead of the one it multiplies (three
+// register buffers), and passes them through its own LDS region to regroup them in
+// operand order (a wave's own LDS writes are seen by its later reads, so no barrier).
+// The X operands of a 512-k step are shared by the workgroup through a double-buffered
+// LDS slice: step c+1's slice is loaded while step c multiplies, one barrier per step.
+// Loads are issued X first, then weights, so waiting for X never waits for the weights
+// two steps ahead.  Workgroups that share a slice of weights (different blocks of X)
+// are placed on one XCD so that its L2 serves the repeats.
 //
 // W4A8: X is quantized once per call into the workspace by k_quant_act_mfma (the same
-// per-row scale and codes as quant_act_i8) in B-operand order, so the workgroup stages
-// it into LDS with plain 16-byte copies.  An INT4 operand of 16 k is 8 bytes of nibbles
-// presented as 16 * q (nibble moved to the high half of its byte; even k from the low
-// nibbles, odd k from the high ones), and the X codes are stored in the same k order;
-// the int32 result is exactly 16 * acc, so acc >> 4 is exact and the output equals the
-// GEMV's bit for bit.
+// per-row scale and codes as quant_act_i8) in B-operand order.  An INT4 operand of 16 k
+// is 8 bytes of nibbles presented as 16 * q (nibble moved to the high half of its
+// byte; even k from the low nibbles, odd k from the high ones), and the X codes are
+// stored in the same k order; the int32 result is exactly 16 * acc, so acc >> 4 is
+// exact and the output equals the GEMV's bit for bit.
 //
-// W8A16: X (f16) is staged in LDS in 128-k slices straight from the input; the INT8
-// weights are cast to f16 exactly in registers (the byte-permute cast of the GEMV) and
-// the per-channel scale multiplies the fp32 sum once.
+// W8A16: X (f16) is staged from its row-major input; the INT8 weights are cast to f16
+// exactly in registers (the byte-permute cast of the GEMV) and the per-channel scale
+// multiplies the fp32 sum once.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -36,8 +42,43 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-constexpr int kWaves = 4;
-constexpr int kThreadsG = 64 * kWaves;
+// Logical block of hardware block b out of G.  Workgroup b runs on XCD b % 8; this
+// numbers each XCD's blocks contiguously, so logical neighbours share an L2.
+__device__ __forceinline__ int xcd_block(int b, int G)
+{
+    const int per = (G + 7) / 8, r = G % 8;
+    const int x = b % 8, i = b / 8;
+    if (r == 0 || x < r)
+        return x * per + i;
+    return r * per + (x - r) * (per - 1) + i;
+}
+
+// The 512-k steps of a kernel: three weight register buffers (step c in w[c % 3]) and
+// two X register buffers (step c in x[c % 2]) rotate, so six steps make one loop trip
+// with no branch inside; the last zero to five steps follow the loop.  Expects QW_STEP,
+// the buffers w0, w1, w2, xa, xb and the step count CG.
+#define QW_STEPS_SIX()                                                                           \
+    {                                                                                            \
+        int c_ = 0;                                                                              \
+        for (; c_ + 6 <= CG; c_ += 6) {                                                          \
+            QW_STEP(w0, w2, xa, xb, c_);                                                         \
+            QW_STEP(w1, w0, xb, xa, c_ + 1);                                                     \
+            QW_STEP(w2, w1, xa, xb, c_ + 2);                                                     \
+            QW_STEP(w0, w2, xb, xa, c_ + 3);                                                     \
+            QW_STEP(w1, w0, xa, xb, c_ + 4);                                                     \
+            QW_STEP(w2, w1, xb, xa, c_ + 5);                                                     \
+        }                                                                                        \
+        if (c_ < CG)                                                                             \
+            QW_STEP(w0, w2, xa, xb, c_);                                                         \
+        if (c_ + 1 < CG)                                                                         \
+            QW_STEP(w1, w0, xb, xa, c_ + 1);                                                     \
+        if (c_ + 2 < CG)                                                                         \
+            QW_STEP(w2, w1, xa, xb, c_ + 2);                                                     \
+        if (c_ + 3 < CG)                                                                         \
+            QW_STEP(w0, w2, xb, xa, c_ + 3);                                                     \
+        if (c_ + 4 < CG)                                                                         \
+            QW_STEP(w1, w0, xa, xb, c_ + 4);                                                     \
+    }
 
 // ---------------------------------------------------------------- W4A8 --------
 
@@ -56,22 +97,32 @@ __device__ __forceinline__ uint4 pack_perm16(const int (&q)[16])
 // One workgroup per row of X (grid-strided over ceil(M / 16) * 16 rows; rows past M
 // are written as zeros).  a = maxabs / 127 and the codes exactly as k_quant_act, laid
 // out as B operands: row m, step st (64 k), lane block g -> 16 bytes at
-// ((m / 16) * KS + st) * 1024 + (16 g + m % 16) * 16.
+// ((m / 16) * KS + st) * 1024 + (16 g + m % 16) * 16.  A thread owns NS slots of 16
+// consecutive k (slot sl = tid + 256 t) and keeps their values in registers between
+// the maximum and the quantization, so X is read once.
+template <int NS>
 __global__ __launch_bounds__(kBlock) void k_quant_act_mfma(const float* __restrict__ X, int M,
                                                            int K, int Mp, int KS,
                                                            uint8_t* __restrict__ Xp,
                                                            float* __restrict__ a_scale)
 {
     __shared__ float red[4];
-    const int K4 = K >> 2;
     const int slots = KS * 4;  // 16-code slots per row
     for (int m = blockIdx.x; m < Mp; m += gridDim.x) {
         const bool live = m < M;
-        const float4* row = reinterpret_cast<const float4*>(X + (size_t)(live ? m : 0) * K);
+        // rows past M read zeros, and so do k past K
+        const rsrc_t xr = make_rsrc(X + (size_t)(live ? m : 0) * K, live ? (uint32_t)K * 4u : 0u);
+        float4 v[NS][4];
         float mx = 0.0f;
-        if (live)
-            for (int i = threadIdx.x; i < K4; i += kBlock)
-                mx = fmaxf(mx, max_abs4(row[i]));
+#pragma unroll
+        for (int t = 0; t < NS; ++t) {
+            const int sl = (int)threadIdx.x + kBlock * t;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                v[t][e] = load16f(xr, sl < slots ? (uint32_t)(16 * sl + 4 * e) * 4u : 0x80000000u);
+                mx = fmaxf(mx, max_abs4(v[t][e]));
+            }
+        }
         mx = block_max(mx, red);
         const float a = mx / 127.0f;
         const float r = 1.0f / a;
@@ -79,137 +130,173 @@ __global__ __launch_bounds__(kBlock) void k_quant_act_mfma(const float* __restri
         if (live && threadIdx.x == 0)
             a_scale[m] = a;
         uint8_t* base = Xp + (size_t)(m >> 4) * KS * 1024u + (size_t)(m & 15) * 16u;
-        for (int sl = threadIdx.x; sl < slots; sl += kBlock) {
-            int q[16];
-            const int k0 = 16 * sl;
-            if (live && k0 < K) {
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const float4 x = row[(k0 >> 2) + v];
-                    const float xs[4] = {x.x, x.y, x.z, x.w};
+        for (int t = 0; t < NS; ++t) {
+            const int sl = (int)threadIdx.x + kBlock * t;
+            if (sl < slots) {
+                int q[16];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        q[4 * v + e] = fast ? quant_code_fast(xs[e], a, r, 127.f)
-                                            : quant_code(xs[e], a, 127.f);
+                for (int e = 0; e < 4; ++e) {
+                    const float xs[4] = {v[t][e].x, v[t][e].y, v[t][e].z, v[t][e].w};
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        q[4 * e + i] = fast ? quant_code_fast(xs[i], a, r, 127.f)
+                                            : quant_code(xs[i], a, 127.f);
                 }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 16; ++e)
-                    q[e] = 0;
+                const int st = sl >> 2, g = sl & 3;
+                *reinterpret_cast<uint4*>(base + (size_t)st * 1024u + (size_t)g * 256u) =
+                    pack_perm16(q);
             }
-            const int st = sl >> 2, g = sl & 3;
-            *reinterpret_cast<uint4*>(base + (size_t)st * 1024u + (size_t)g * 256u) = pack_perm16(q);
         }
     }
 }
 
-// Padded LDS image of one wave's four INT4 tiles: tile i at i * 1088, tile row sub at
-// sub * 272, 16-byte chunk j at j * 16.
-constexpr int kW4TilePitch = 1088, kW4RowPitch = 272, kW4WaveBytes = 4 * kW4TilePitch;
+// Padded LDS image of one INT4 tile (4 rows x 16 chunks): row sub at sub * 272, chunk
+// j at j * 16, so the 16 lanes reading 16 different rows of a 16-row block hit
+// different banks.
+constexpr int kW4TilePitch = 1088, kW4RowPitch = 272;
 
-template <int MB>
-__global__ __launch_bounds__(kThreadsG) void k_gemm_w4a8(MfmaW4A8Args p)
+template <int NW, int MB, int NBW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_w4a8(MfmaW4A8Args p)
 {
-    extern __shared__ uint8_t s_mem[];  // [waves][4 tiles padded] then X [MB][8 steps][1 KB]
-    uint8_t* s_w = s_mem;
-    uint8_t* s_x = s_mem + kWaves * kW4WaveBytes;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kXStep = MB * 8 * 1024;                // X codes of one 512-k step
+    constexpr int kXLoads = kXStep / (kThreads * 16);    // 16-byte loads per thread
+    static_assert(kXLoads * kThreads * 16 == kXStep, "X slice must split evenly");
+    constexpr int kWT = 4 * NBW;                         // row groups (tiles per step) per wave
+    extern __shared__ uint8_t s_mem[];  // X [2][kXStep], then per wave kWT padded tiles
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int CG = p.cg, KS = p.ks, MG = p.mgroups;
-    const int mg = blockIdx.x % MG, nb = blockIdx.x / MG;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int mg = blk % MG, nb = blk / MG;
     const int mb0 = mg * MB;
-    const int rgw = nb * 16 + wave * 4;  // first row group of this wave
-    const int nrg_w = max(0, min(4, p.nrg - rgw));
-    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rgw * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
-    const rsrc_t xres = make_rsrc(p.Xp, (uint32_t)p.mbtot * (uint32_t)KS * 1024u);
+    const int rgw = (nb * NW + wave) * kWT;  // first row group (4 rows) of this wave
+    const int nrg_w = max(0, min(kWT, p.nrg - rgw));
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)min(rgw, p.nrg) * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
+    // this workgroup's blocks of X codes (at most MB * KS KB)
+    const int mbw = max(0, min(MB, p.mbtot - mb0));
+    const rsrc_t xres = make_rsrc(p.Xp + (size_t)min(mb0, p.mbtot) * KS * 1024u,
+                                  (uint32_t)mbw * (uint32_t)KS * 1024u);
+    uint8_t* s_x = s_mem;
+    uint8_t* s_w = s_mem + 2 * kXStep + wave * kWT * kW4TilePitch;
+#define QW_KT(C) (C)
 
-    uint4 wr[4], xr[2 * MB];
-    auto load_tiles = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            wr[i] = load16_stream(wres, (uint32_t)(i * CG + c) * 1024u + (uint32_t)lane * 16u);
-#pragma unroll
-        for (int v = 0; v < 2 * MB; ++v) {
-            const int piece = v * kThreadsG + tid;  // [mbl][s][lane slot]
-            const int mbl = piece >> 9, s = (piece >> 6) & 7, sl = piece & 63;
-            const bool ok = mb0 + mbl < p.mbtot && 8 * c + s < KS;
-            xr[v] = load16(xres, ok ? ((uint32_t)(mb0 + mbl) * (uint32_t)KS + (uint32_t)(8 * c + s)) * 1024u +
-                                          (uint32_t)sl * 16u
-                                    : 0x80000000u);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-    };
+    uint4 w0[kWT], w1[kWT], w2[kWT], xa[kXLoads], xb[kXLoads];
+    // weights of step c (zeros past K); X codes of step c (zeros past K and past M)
+#define QW_LOADW(WB, C)                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                           \
+        WB[i_] = load16_stream(wres, (C) < CG ? (uint32_t)(i_ * CG + QW_KT(C)) * 1024u + (uint32_t)lane * 16u \
+                                              : 0x80000000u);
+#define QW_LOADX(XB, C)                                                                          \
+    _Pragma("unroll") for (int v_ = 0; v_ < kXLoads; ++v_)                                       \
+    {                                                                                            \
+        const int pc_ = v_ * kThreads + tid; /* [mbl][s][lane] */                                \
+        const int mbl_ = pc_ >> 9, s_ = (pc_ >> 6) & 7, sl_ = pc_ & 63;                          \
+        const bool ok_ = (C) < CG && mbl_ < mbw && 8 * QW_KT(C) + s_ < KS;                       \
+        XB[v_] = load16(xres, ok_ ? ((uint32_t)mbl_ * (uint32_t)KS + (uint32_t)(8 * QW_KT(C) + s_)) * 1024u + \
+                                         (uint32_t)sl_ * 16u                                     \
+                                   : 0x80000000u);                                               \
+    }
+#define QW_STOREX(XB, BUF)                                                                       \
+    _Pragma("unroll") for (int v_ = 0; v_ < kXLoads; ++v_)                                       \
+        *reinterpret_cast<uint4*>(s_x + (BUF) * kXStep + (size_t)(v_ * kThreads + tid) * 16) = XB[v_];
 
-    v4i acc[MB];
+    v4i acc[NBW][MB];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-        acc[i] = v4i{0, 0, 0, 0};
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            acc[b][i] = v4i{0, 0, 0, 0};
 
-    uint8_t* my_w = s_w + wave * kW4WaveBytes;
     const int sub = lane >> 4, j = lane & 15;
-    // A operand of step s for lane (g, r): row r = tile r / 4, tile row r % 4; chunk
-    // 2 s + g / 2, half g % 2
+    // A operand of block b, step s for lane (g, r): row r of the block = tile 4 b + r / 4,
+    // tile row r % 4; 16 k = chunk 2 s + g / 2, half g % 2
     const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
 
-    load_tiles(0);
-    for (int c = 0; c < CG; ++c) {
-        __syncthreads();  // every wave is done with the previous tile's X
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            *reinterpret_cast<uint4*>(my_w + i * kW4TilePitch + sub * kW4RowPitch + j * 16) = wr[i];
-#pragma unroll
-        for (int v = 0; v < 2 * MB; ++v)
-            *reinterpret_cast<uint4*>(s_x + (size_t)(v * kThreadsG + tid) * 16) = xr[v];
-        __syncthreads();
-        if (c + 1 < CG)
-            load_tiles(c + 1);
-#pragma unroll
-        for (int s = 0; s < 8; ++s) {
-            const uint2 w = *reinterpret_cast<const uint2*>(my_w + a_off + s * 32);
-            v4i a;
-            a[0] = (int)((w.x << 4) & 0xF0F0F0F0u);
-            a[1] = (int)(w.x & 0xF0F0F0F0u);
-            a[2] = (int)((w.y << 4) & 0xF0F0F0F0u);
-            a[3] = (int)(w.y & 0xF0F0F0F0u);
-#pragma unroll
-            for (int mbl = 0; mbl < MB; ++mbl) {
-                const uint4 b4 = *reinterpret_cast<const uint4*>(s_x + ((mbl * 8 + s) * 64 + lane) * 16);
-                const v4i b = {(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
-                acc[mbl] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, acc[mbl], 0, 0, 0);
-            }
-        }
+    // One 512-k step C.  X of step C+2 (into XL, whose step C was stored last step) and
+    // the weights of step C+2 (into WN) are requested first; the weights of step C (WC)
+    // are regrouped through LDS and multiplied with the X slice in buffer C % 2; then X
+    // of step C+1 (XS) is stored and the workgroup syncs.  Waiting for XS waits only for
+    // loads issued before it, i.e. up to the weights of step C: the weights of steps C+1
+    // and C+2 stay in flight.
+#define QW_STEP(WC, WN, XL, XS, C)                                                               \
+    {                                                                                            \
+        QW_LOADX(XL, (C) + 2);                                                                   \
+        QW_LOADW(WN, (C) + 2);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                       \
+            *reinterpret_cast<uint4*>(s_w + i_ * kW4TilePitch + sub * kW4RowPitch + j * 16) = WC[i_]; \
+        const uint8_t* xb_ = s_x + ((C) & 1) * kXStep;                                           \
+        _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
+        {                                                                                        \
+            v4i bo_[MB];                                                                         \
+            _Pragma("unroll") for (int mbl_ = 0; mbl_ < MB; ++mbl_)                              \
+            {                                                                                    \
+                const uint4 b4_ = *reinterpret_cast<const uint4*>(xb_ + ((mbl_ * 8 + s_) * 64 + lane) * 16); \
+                bo_[mbl_] = v4i{(int)b4_.x, (int)b4_.y, (int)b4_.z, (int)b4_.w};                  \
+            }                                                                                    \
+            _Pragma("unroll") for (int b_ = 0; b_ < NBW; ++b_)                                   \
+            {                                                                                    \
+                const uint2 w_ = *reinterpret_cast<const uint2*>(s_w + b_ * 4 * kW4TilePitch + a_off + s_ * 32); \
+                const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),     \
+                                (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};    \
+                _Pragma("unroll") for (int mbl_ = 0; mbl_ < MB; ++mbl_)                          \
+                    acc[b_][mbl_] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, bo_[mbl_], acc[b_][mbl_], 0, 0, 0); \
+            }                                                                                    \
+        }                                                                                        \
+        QW_STOREX(XS, ((C) + 1) & 1);                                                            \
+        __syncthreads();                                                                         \
     }
 
+    QW_LOADX(xa, 0);
+    QW_LOADX(xb, 1);
+    QW_LOADW(w0, 0);
+    QW_LOADW(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    QW_STOREX(xa, 0);
+    __syncthreads();
+    QW_STEPS_SIX();
+#undef QW_STEP
+#undef QW_STOREX
+#undef QW_LOADX
+#undef QW_LOADW
+#undef QW_KT
+
     // lane (g, r) holds D[n = 4 g + i][m = r] of each 16 x 16 block
-    const int n0 = 4 * rgw + 4 * g;
     const rsrc_t sres = make_rsrc(p.w_scale, (uint32_t)p.N * 4u);
-    float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        sc[i] = __uint_as_float(load4(sres, (uint32_t)(n0 + i) * 4u));
+    for (int b = 0; b < NBW; ++b) {
+        const int n0 = 4 * rgw + 16 * b + 4 * g;
+        float sc[4];
 #pragma unroll
-    for (int mbl = 0; mbl < MB; ++mbl) {
-        const int m = (mb0 + mbl) * 16 + r;
-        if (m < p.M) {
-            const float am = p.a_scale[m];
+        for (int i = 0; i < 4; ++i)
+            sc[i] = __uint_as_float(load4(sres, (uint32_t)(n0 + i) * 4u));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (n0 + i < p.N)
-                    p.Y[(size_t)m * p.N + n0 + i] = ((float)(acc[mbl][i] >> 4) * sc[i]) * am;
+        for (int mbl = 0; mbl < MB; ++mbl) {
+            const int m = (mb0 + mbl) * 16 + r;
+            if (m < p.M) {
+                const float am = p.a_scale[m];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n0 + i < p.N)
+                        p.Y[(size_t)m * p.N + n0 + i] = ((float)(acc[b][mbl][i] >> 4) * sc[i]) * am;
+            }
         }
     }
 }
 
 // ---------------------------------------------------------------- W8A16 -------
 
-// Padded LDS image of one wave's eight INT8 tiles (2 rows x 32 chunks each): tile i at
-// i * 1056, tile row sub at sub * 528, chunk j at j * 16.
-constexpr int kW8TilePitch = 1056, kW8RowPitch = 528, kW8WaveBytes = 8 * kW8TilePitch;
-// X slice in LDS: 128 k (256 bytes) per row, rows padded to 272 bytes.
-constexpr int kXSliceK = 128, kXRowPitch = 272;
+// Padded LDS image of one INT8 tile (2 rows x 32 chunks): row sub at sub * 528, chunk
+// j at j * 16.
+constexpr int kW8TilePitch = 1056, kW8RowPitch = 528;
+// X slice of one 512-k step in LDS: 16 MB rows of 1 KB, rows padded to 1040 bytes.
+constexpr int kXRowPitch = 1040;
 
 // int8 x 4 -> f16 x 4, exact (see the GEMV kernel): bytes ^ 0x80 under a 0x64 byte
 // read as 1024 + q + 128, minus 1152.
@@ -223,121 +310,206 @@ __device__ __forceinline__ void cast4(uint32_t wd, half2_t& lo, half2_t& hi)
     hi = __builtin_bit_cast(half2_t, h) + off;
 }
 
-template <int MB>
-__global__ __launch_bounds__(kThreadsG) void k_gemm_w8a16(MfmaW8A16Args p)
+template <int NW, int MB, int NBW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_w8a16(MfmaW8A16Args p)
 {
-    extern __shared__ uint8_t s_mem[];  // [waves][8 tiles padded] then X [16 MB rows][272 B]
-    uint8_t* s_w = s_mem;
-    uint8_t* s_x = s_mem + kWaves * kW8WaveBytes;
+    constexpr int kThreads = 64 * NW;
+    constexpr int kXStep = MB * 16 * kXRowPitch;           // LDS bytes of one X slice
+    constexpr int kXPieces = MB * 16 * 64;                 // 16-byte pieces of one slice
+    constexpr int kXLoads = (kXPieces + kThreads - 1) / kThreads;
+    constexpr int kWT = 8 * NBW;                           // row groups (2 rows) per wave
+    extern __shared__ uint8_t s_mem[];  // X [2][kXStep], then per wave kWT padded tiles
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
     const int M = p.M, K = p.K, CG = p.cg, MG = p.mgroups;
-    const int mg = blockIdx.x % MG, nb = blockIdx.x / MG;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int mg = blk % MG, nb = blk / MG;
     const int m0 = mg * MB * 16;
-    const int rgw = nb * 32 + wave * 8;  // first row group (2 rows) of this wave
-    const int nrg_w = max(0, min(8, p.nrg - rgw));
-    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rgw * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
+    const int rgw = (nb * NW + wave) * kWT;  // first row group (2 rows) of this wave
+    const int nrg_w = max(0, min(kWT, p.nrg - rgw));
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)min(rgw, p.nrg) * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
     const int rows_x = max(0, min(MB * 16, M - m0));
-    const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)rows_x * (uint32_t)K * 2u);
+    const rsrc_t xres = make_rsrc(p.X + (size_t)min(m0, M) * K, (uint32_t)rows_x * (uint32_t)K * 2u);
+    uint8_t* s_x = s_mem;
+    uint8_t* s_w = s_mem + 2 * kXStep + wave * kWT * kW8TilePitch;
+#define QW_KT(C) (C)
 
-    // X slice: 16 MB rows x 128 k = MB * 256 pieces of 16 bytes, one per thread and pass
-    constexpr int kXPieces = MB * 16 * (kXSliceK / 8);
-    constexpr int kXPass = (kXPieces + kThreadsG - 1) / kThreadsG;
-
-    uint4 wr[8], xr[kXPass];
-    auto load_w = [&](int c) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            wr[i] = load16_stream(wres, (uint32_t)(i * CG + c) * 1024u + (uint32_t)lane * 16u);
-    };
-    auto load_x = [&](int kk) {  // slice starting at k = kk
-#pragma unroll
-        for (int v = 0; v < kXPass; ++v) {
-            const int piece = v * kThreadsG + tid;
-            const int row = piece >> 4, q = piece & 15;
-            const bool ok = piece < kXPieces && kk + 8 * q < K;
-            xr[v] = load16(xres, ok ? (uint32_t)(row * K + kk + 8 * q) * 2u : 0x80000000u);
-        }
-    };
-    auto store_x = [&]() {
-#pragma unroll
-        for (int v = 0; v < kXPass; ++v) {
-            const int piece = v * kThreadsG + tid;
-            if (piece < kXPieces)
-                *reinterpret_cast<uint4*>(s_x + (piece >> 4) * kXRowPitch + (piece & 15) * 16) = xr[v];
-        }
-    };
-
-    v4f acc[MB];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-        acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    uint8_t* my_w = s_w + wave * kW8WaveBytes;
-    const int sub = lane >> 5, j = lane & 31;
-    // A operand of step s (32 k) for lane (g, r): row r = tile r / 2, tile row r % 2;
-    // k = 32 s + 8 g .. + 7 = chunk 2 s + g / 2, half g % 2
-    const int a_off = (r >> 1) * kW8TilePitch + (r & 1) * kW8RowPitch + (g >> 1) * 16 + (g & 1) * 8;
-
-    load_w(0);
-    load_x(0);
-    __builtin_amdgcn_sched_barrier(0);
-    for (int c = 0; c < CG; ++c) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            *reinterpret_cast<uint4*>(my_w + i * kW8TilePitch + sub * kW8RowPitch + j * 16) = wr[i];
-        if (c + 1 < CG)
-            load_w(c + 1);
-        __builtin_amdgcn_sched_barrier(0);
-        for (int h = 0; h < 512 / kXSliceK; ++h) {
-            __syncthreads();  // every wave is done with the previous slice
-            store_x();
-            __syncthreads();
-            const int kn = 512 * c + kXSliceK * (h + 1);
-            if (kn < 512 * CG)
-                load_x(kn);
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int s = 0; s < kXSliceK / 32; ++s) {
-                const int st = h * (kXSliceK / 32) + s;  // 32-k step within the tile
-                const uint2 w = *reinterpret_cast<const uint2*>(my_w + a_off + st * 32);
-                half2_t h0, h1, h2, h3;
-                cast4(w.x, h0, h1);
-                cast4(w.y, h2, h3);
-                const v8h a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-#pragma unroll
-                for (int mbl = 0; mbl < MB; ++mbl) {
-                    const uint4 b4 = *reinterpret_cast<const uint4*>(
-                        s_x + (mbl * 16 + r) * kXRowPitch + (32 * s + 8 * g) * 2);
-                    const v8h b = __builtin_bit_cast(v8h, b4);
-                    acc[mbl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[mbl], 0, 0, 0);
-                }
-            }
-        }
+    uint4 w0[kWT], w1[kWT], w2[kWT], xa[kXLoads], xb[kXLoads];
+#define QW_LOADW(WB, C)                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                           \
+        WB[i_] = load16_stream(wres, (C) < CG ? (uint32_t)(i_ * CG + QW_KT(C)) * 1024u + (uint32_t)lane * 16u \
+                                              : 0x80000000u);
+    // piece pc of the slice of step C: row pc / 64, k = 512 QW_KT(C) + 8 (pc % 64)
+#define QW_LOADX(XB, C)                                                                          \
+    _Pragma("unroll") for (int v_ = 0; v_ < kXLoads; ++v_)                                       \
+    {                                                                                            \
+        const int pc_ = v_ * kThreads + tid;                                                     \
+        const int row_ = pc_ >> 6, k_ = 512 * QW_KT(C) + 8 * (pc_ & 63);                         \
+        const bool ok_ = (C) < CG && pc_ < kXPieces && k_ < K;                                   \
+        XB[v_] = load16(xres, ok_ ? (uint32_t)(row_ * K + k_) * 2u : 0x80000000u);               \
+    }
+#define QW_STOREX(XB, BUF)                                                                       \
+    _Pragma("unroll") for (int v_ = 0; v_ < kXLoads; ++v_)                                       \
+    {                                                                                            \
+        const int pc_ = v_ * kThreads + tid;                                                     \
+        if (pc_ < kXPieces)                                                                      \
+            *reinterpret_cast<uint4*>(s_x + (BUF) * kXStep + (pc_ >> 6) * kXRowPitch + (pc_ & 63) * 16) = XB[v_]; \
     }
 
-    const int n0 = 2 * rgw + 4 * g;
+    v4f acc[NBW][MB];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+#pragma unroll
+        for (int i = 0; i < MB; ++i)
+            acc[b][i] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const int sub = lane >> 5, j = lane & 31;
+    // A operand of block b, step s (32 k) for lane (g, r): row r of the block = tile
+    // 8 b + r / 2, tile row r % 2; k = 32 s + 8 g .. + 7 = chunk 2 s + g / 2, half g % 2
+    const int a_off = (r >> 1) * kW8TilePitch + (r & 1) * kW8RowPitch + (g >> 1) * 16 + (g & 1) * 8;
+
+    // One 512-k step, ordered as in the W4A8 kernel.  The 16 MFMA steps go in groups
+    // of four, so that the compiler does not hold every operand of the step at once.
+#define QW_STEP(WC, WN, XL, XS, C)                                                               \
+    {                                                                                            \
+        QW_LOADX(XL, (C) + 2);                                                                   \
+        QW_LOADW(WN, (C) + 2);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                       \
+            *reinterpret_cast<uint4*>(s_w + i_ * kW8TilePitch + sub * kW8RowPitch + j * 16) = WC[i_]; \
+        const uint8_t* xb_ = s_x + ((C) & 1) * kXStep;                                           \
+        _Pragma("unroll") for (int s_ = 0; s_ < 16; ++s_)                                        \
+        {                                                                                        \
+            v8h bo_[MB];                                                                         \
+            _Pragma("unroll") for (int mbl_ = 0; mbl_ < MB; ++mbl_)                              \
+                bo_[mbl_] = __builtin_bit_cast(v8h, *reinterpret_cast<const uint4*>(             \
+                    xb_ + (mbl_ * 16 + r) * kXRowPitch + s_ * 64 + g * 16));                     \
+            _Pragma("unroll") for (int b_ = 0; b_ < NBW; ++b_)                                   \
+            {                                                                                    \
+                const uint2 w_ = *reinterpret_cast<const uint2*>(s_w + b_ * 8 * kW8TilePitch + a_off + s_ * 32); \
+                half2_t h0_, h1_, h2_, h3_;                                                      \
+                cast4(w_.x, h0_, h1_);                                                           \
+                cast4(w_.y, h2_, h3_);                                                           \
+                const v8h a_ = {h0_[0], h0_[1], h1_[0], h1_[1], h2_[0], h2_[1], h3_[0], h3_[1]}; \
+                _Pragma("unroll") for (int mbl_ = 0; mbl_ < MB; ++mbl_)                          \
+                    acc[b_][mbl_] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_, bo_[mbl_], acc[b_][mbl_], 0, 0, 0); \
+            }                                                                                    \
+            if ((s_ & 3) == 3)                                                                   \
+                __builtin_amdgcn_sched_barrier(0);                                               \
+        }                                                                                        \
+        QW_STOREX(XS, ((C) + 1) & 1);                                                            \
+        __syncthreads();                                                                         \
+    }
+
+    QW_LOADX(xa, 0);
+    QW_LOADX(xb, 1);
+    QW_LOADW(w0, 0);
+    QW_LOADW(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    QW_STOREX(xa, 0);
+    __syncthreads();
+    QW_STEPS_SIX();
+#undef QW_STEP
+#undef QW_STOREX
+#undef QW_LOADX
+#undef QW_LOADW
+#undef QW_KT
+
     const rsrc_t sres = make_rsrc(p.w_scale, (uint32_t)p.N * 2u);
-    float sc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        sc[i] = __half2float(__ushort_as_half(load2(sres, (uint32_t)(n0 + i) * 2u)));
+    for (int b = 0; b < NBW; ++b) {
+        const int n0 = 2 * rgw + 16 * b + 4 * g;
+        float sc[4];
 #pragma unroll
-    for (int mbl = 0; mbl < MB; ++mbl) {
-        const int m = m0 + mbl * 16 + r;
-        if (m < M) {
+        for (int i = 0; i < 4; ++i)
+            sc[i] = __half2float(__ushort_as_half(load2(sres, (uint32_t)(n0 + i) * 2u)));
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                if (n0 + i < p.N)
-                    p.Y[(size_t)m * p.N + n0 + i] = __half_as_ushort(__float2half_rn(acc[mbl][i] * sc[i]));
+        for (int mbl = 0; mbl < MB; ++mbl) {
+            const int m = m0 + mbl * 16 + r;
+            if (m < M) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (n0 + i < p.N)
+                        p.Y[(size_t)m * p.N + n0 + i] =
+                            __half_as_ushort(__float2half_rn(acc[b][mbl][i] * sc[i]));
+            }
         }
     }
 }
 
+template <int NW, int MB, int NBW>
+size_t lds_w4() { return (size_t)2 * MB * 8 * 1024 + (size_t)NW * 4 * NBW * kW4TilePitch; }
+
+template <int NW, int MB, int NBW>
+size_t lds_w8() { return (size_t)2 * MB * 16 * kXRowPitch + (size_t)NW * 8 * NBW * kW8TilePitch; }
+
+// Dynamic LDS above 64 KB has to be allowed per kernel (gfx950 has 160 KB per CU).
+hipError_t allow_lds(const void* kernel, size_t bytes)
+{
+    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <int NW, int MB, int NBW>
+hipError_t go_w4(const MfmaW4A8Args& p, hipStream_t st)
+{
+    // once per kernel, before its first launch
+    static const hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8<NW, MB, NBW>), lds_w4<NW, MB, NBW>());
+    if (e != hipSuccess)
+        return e;
+    const int64_t nblocks = ((int64_t)p.nrg + NW * 4 * NBW - 1) / (NW * 4 * NBW);
+    if (nblocks * p.mgroups > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_gemm_w4a8<NW, MB, NBW>), dim3((unsigned)(nblocks * p.mgroups)),
+                       dim3(64 * NW), (lds_w4<NW, MB, NBW>()), st, p);
+    return hipGetLastError();
+}
+
+template <int NW, int MB, int NBW>
+hipError_t go_w8(const MfmaW8A16Args& p, hipStream_t st)
+{
+    static const hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(k_gemm_w8a16<NW, MB, NBW>), lds_w8<NW, MB, NBW>());
+    if (e != hipSuccess)
+        return e;
+    const int64_t nblocks = ((int64_t)p.nrg + NW * 8 * NBW - 1) / (NW * 8 * NBW);
+    if (nblocks * p.mgroups > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_gemm_w8a16<NW, MB, NBW>), dim3((unsigned)(nblocks * p.mgroups)),
+                       dim3(64 * NW), (lds_w8<NW, MB, NBW>()), st, p);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
+{
+    if (nw != 4 && nw != 8)
+        return false;
+    if (nbw != 1 && nbw != 2)
+        return false;
+    if (bits == 4)
+        return (mb == 1 || mb == 2 || mb == 4) && !(nw == 4 && mb == 4 && nbw == 2) &&
+               !(nw == 8 && mb == 1 && nbw == 2);
+    // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
+    // rows would not fit the registers
+    return (mb == 1 || mb == 2) && !(nw == 8 && nbw == 2);
+}
+
+void mfma_default_shape(int bits, int64_t M, int* nw, int* mb, int* nbw)
+{
+    const int64_t mbtot = (M + 15) / 16;
+    *nw = 4;
+    *nbw = 1;
+    if (bits == 4)
+        *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
+    else
+        *mb = mbtot >= 2 ? 2 : 1;
+}
 
 size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K)
 {
@@ -347,7 +519,8 @@ size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K)
 }
 
 hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
-                            const float* w_scale, float* Y, void* workspace, hipStream_t st)
+                            const float* w_scale, float* Y, void* workspace, int nw, int mb,
+                            int nbw, hipStream_t st)
 {
     const TileLayout L = tile_layout(4, N, K);
     const int mbtot = (M + 15) / 16, ks = (K + 63) / 64;
@@ -355,8 +528,19 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     const size_t xp_bytes = ((size_t)mbtot * ks * 1024u + 255u) & ~(size_t)255u;
     float* a = reinterpret_cast<float*>(xp + xp_bytes);
     const int qgrid = mbtot * 16 < 65536 ? mbtot * 16 : 65536;
-    hipLaunchKernelGGL(k_quant_act_mfma, dim3(qgrid), dim3(kBlock), 0, st, X, M, K, mbtot * 16, ks,
-                       xp, a);
+    const int ns = (ks * 4 + kBlock - 1) / kBlock;  // 16-code slots per thread
+    if (ns <= 1)
+        hipLaunchKernelGGL(k_quant_act_mfma<1>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
+    else if (ns <= 2)
+        hipLaunchKernelGGL(k_quant_act_mfma<2>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
+    else if (ns <= 4)
+        hipLaunchKernelGGL(k_quant_act_mfma<4>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
+    else
+        hipLaunchKernelGGL(k_quant_act_mfma<14>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -373,23 +557,19 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.nrg = L.nrg;
     p.ks = ks;
     p.mbtot = mbtot;
-    const int MB = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
-    p.mgroups = (mbtot + MB - 1) / MB;
-    const int64_t nblocks = (L.nrg + 15) / 16;
-    if (nblocks * p.mgroups > 0x7fffffff)
-        return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(nblocks * p.mgroups));
-    const size_t lds = (size_t)kWaves * kW4WaveBytes + (size_t)MB * 8 * 1024;
-    switch (MB) {
-    case 1: hipLaunchKernelGGL(k_gemm_w4a8<1>, grid, dim3(kThreadsG), lds, st, p); break;
-    case 2: hipLaunchKernelGGL(k_gemm_w4a8<2>, grid, dim3(kThreadsG), lds, st, p); break;
-    default: hipLaunchKernelGGL(k_gemm_w4a8<4>, grid, dim3(kThreadsG), lds, st, p); break;
-    }
-    return hipGetLastError();
+    p.mgroups = (mbtot + mb - 1) / mb;
+#define QW_GO(NW_, MB_, NBW_)                                                                    \
+    if (nw == NW_ && mb == MB_ && nbw == NBW_)                                                   \
+        return go_w4<NW_, MB_, NBW_>(p, st);
+    QW_GO(4, 1, 1) QW_GO(4, 2, 1) QW_GO(4, 4, 1) QW_GO(4, 1, 2) QW_GO(4, 2, 2)
+    QW_GO(8, 1, 1) QW_GO(8, 2, 1) QW_GO(8, 4, 1) QW_GO(8, 2, 2) QW_GO(8, 4, 2)
+#undef QW_GO
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
-                             const uint16_t* w_scale, uint16_t* Y, hipStream_t st)
+                             const uint16_t* w_scale, uint16_t* Y, int nw, int mb, int nbw,
+                             hipStream_t st)
 {
     const TileLayout L = tile_layout(8, N, K);
     const int mbtot = (M + 15) / 16;
@@ -403,19 +583,14 @@ hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8
     p.K = K;
     p.cg = L.cg;
     p.nrg = L.nrg;
-    const int MB = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
-    p.mgroups = (mbtot + MB - 1) / MB;
-    const int64_t nblocks = (L.nrg + 31) / 32;
-    if (nblocks * p.mgroups > 0x7fffffff)
-        return hipErrorInvalidConfiguration;
-    const dim3 grid((unsigned)(nblocks * p.mgroups));
-    const size_t lds = (size_t)kWaves * kW8WaveBytes + (size_t)MB * 16 * kXRowPitch;
-    switch (MB) {
-    case 1: hipLaunchKernelGGL(k_gemm_w8a16<1>, grid, dim3(kThreadsG), lds, st, p); break;
-    case 2: hipLaunchKernelGGL(k_gemm_w8a16<2>, grid, dim3(kThreadsG), lds, st, p); break;
-    default: hipLaunchKernelGGL(k_gemm_w8a16<4>, grid, dim3(kThreadsG), lds, st, p); break;
-    }
-    return hipGetLastError();
+    p.mgroups = (mbtot + mb - 1) / mb;
+#define QW_GO(NW_, MB_, NBW_)                                                                    \
+    if (nw == NW_ && mb == MB_ && nbw == NBW_)                                                   \
+        return go_w8<NW_, MB_, NBW_>(p, st);
+    QW_GO(4, 1, 1) QW_GO(4, 2, 1) QW_GO(4, 1, 2) QW_GO(4, 2, 2)
+    QW_GO(8, 1, 1) QW_GO(8, 2, 1)
+#undef QW_GO
+    return hipErrorInvalidValue;
 }
 
 }  // namespace qw

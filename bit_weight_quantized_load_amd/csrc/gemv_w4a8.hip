@@ -1,5 +1,6 @@
-// W4A8 GEMV for decode (M < 16): INT4 weights, INT8 activations quantized in the
-// prologue, int8 dot products into int32, output acc * w_scale * a_scale.
+// W4A8 GEMV for decode (the M == 1 path of gemv_w4a8; any M through the tiled entry):
+// INT4 weights, INT8 activations quantized in the prologue, int8 dot products into
+// int32, output acc * w_scale * a_scale.
 //
 // What is computed follows "Jetson Orin AGX 上的 INT4 量化推理实践：从 9 tok/s 到 19.6 tok/s":
 // section 正确方向 (INT4 widened to int8 lanes in registers, 4-way int8 dot into
@@ -152,13 +153,17 @@ __device__ __forceinline__ void quantize_rows(const W4A8Args& p, float4 (&xv)[XV
 }
 
 // RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
-// RCG == 0: LDS variant, U tiles per batch.
-template <int MT, int RCG, int U, int NW, bool kDebug>
+// RCG == 0: LDS variant, U tiles per batch; S > 1 splits K: the S waves that share a
+// row group each take one of S runs of its tiles, and their int32 partial sums are
+// added in LDS once every wave of the workgroup is done.
+template <int MT, int RCG, int U, int NW, int S, bool kDebug>
 __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 {
     constexpr int kThreads = 64 * NW;
     constexpr bool kReg = RCG > 0;
+    constexpr int NR = NW / S;  // row runs per workgroup
     static_assert(!kReg || MT == 1, "register variant is for one row of X");
+    static_assert(!kReg || S == 1, "split-K is in the LDS variant");
     constexpr int kB = kReg ? RCG : U;                                     // tiles per batch
     constexpr int XV = kReg ? (RCG * 128 + kThreads - 1) / kThreads : 16;  // X float4 per thread
     extern __shared__ uint32_t s_dyn[];  // [MT][padded chunks][8 words] codes, then scales
@@ -175,17 +180,23 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, M - m0);
     const int K4 = K >> 2;
-    const int nb = kReg ? 1 : (CG + U - 1) / U;  // batches per row group
-    const int chunks = nb * kB * 16;              // chunks per X row in LDS (zero padded)
+    // k-slice of this wave: tiles [c_lo, c_lo + Tw) of each of its row groups
+    const int ks = S > 1 ? wave % S : 0;
+    const int rw = S > 1 ? wave / S : wave;
+    const int T = (CG + S - 1) / S;
+    const int c_lo = ks * T;
+    const int Tw = max(0, min(CG, c_lo + T) - c_lo);
+    const int nb = kReg ? 1 : (T + U - 1) / U;  // batches per row group
+    const int chunks = S * nb * kB * 16;         // chunks per X row in LDS (zero padded)
 
     // ---- this wave's run of tiles
-    // Waves along N split the row groups evenly: wave gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    // Row runs along N split the row groups evenly: run gw owns [gw*nrg/W, (gw+1)*nrg/W).
     const int W = p.nwaves;
-    const int gw0 = blockIdx.x * NW;
+    const int gw0 = blockIdx.x * NR;
     const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NR, W) * p.nrg) / W);
     const int nrg_blk = rg_blk_end - rg_blk;
-    const int gw = gw0 + wave;
+    const int gw = gw0 + rw;
     const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
     const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
     const int nrg_w = rg1 - rg0;
@@ -202,8 +213,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
         const int r_ = (Q) / nb, c0_ = ((Q) - r_ * nb) * kB;                                    \
         _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
         {                                                                                       \
-            const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
-            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+            const bool ok_ = (Q) < nq && c0_ + u_ < Tw;                                         \
+            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c_lo + c0_ + u_) * 1024u \
                                         : 0x80000000u);                                         \
         }                                                                                       \
         /* keep the batch's loads ahead of the dots that follow: without this the    */       \
@@ -236,10 +247,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
         quantize_rows<MT, NW, XV, false, kDebug>(p, xv, s_dyn, s_red, s_a, chunks, nblk, m0, mt, tid);
 
     const int nw0 = rg0 * 4;  // first row of this wave
+    // split-K partial sums [run][row group][m][row][slice], after the scales
+    const int PW = (p.nrg + W - 1) / W;
+    int* s_part = reinterpret_cast<int*>(s_scale + 4 * kThreads);
     auto finish_row_group = [&](int (&acc)[4], int mm, int rgi) {
         const int v = row_sum16(acc[0] + acc[1] + acc[2] + acc[3]) >> 4;
         const int n = nw0 + rgi * 4 + sub;
-        if (j == 0 && n < N && mm < mt) {
+        if constexpr (S > 1) {
+            if (j == 0)
+                s_part[(((rw * PW + rgi) * MT + mm) * 4 + sub) * S + ks] = v;
+        } else if (j == 0 && n < N && mm < mt) {
             const size_t o = (size_t)(m0 + mm) * N + n;
             if (kDebug && p.dbg_acc != nullptr)
                 p.dbg_acc[o] = v;
@@ -285,7 +302,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
             {                                                                                   \
                 uint32_t a_[U][8];                                                              \
                 _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
-                    load_act(s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 16 + j) * 8, a_[u_]); \
+                    load_act(s_dyn + ((size_t)mm * chunks + (c_lo + b_ * U + u_) * 16 + j) * 8, a_[u_]); \
                 _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
                     dot_chunk(WBUF[u_], a_[u_], acc[mm]);                                       \
             }                                                                                   \
@@ -310,6 +327,30 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
         if (q < nq)
             QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
+        if constexpr (S > 1) {
+            // every wave of the workgroup reaches this barrier (a wave without row
+            // groups skips the loop); slice 0's wave of each run adds the partials
+            __syncthreads();
+            if (ks == 0 && lane < 4) {
+                for (int rgi = 0; rgi < nrg_w; ++rgi) {
+                    const int n = nw0 + rgi * 4 + lane;
+#pragma unroll
+                    for (int mm = 0; mm < MT; ++mm) {
+                        const int* pp = s_part + (((rw * PW + rgi) * MT + mm) * 4 + lane) * S;
+                        int v = 0;
+#pragma unroll
+                        for (int k = 0; k < S; ++k)
+                            v += pp[k];
+                        if (n < N && mm < mt) {
+                            const size_t o = (size_t)(m0 + mm) * N + n;
+                            if (kDebug && p.dbg_acc != nullptr)
+                                p.dbg_acc[o] = v;
+                            p.Y[o] = ((float)v * s_scale[n - rg_blk * 4]) * s_a[mm];
+                        }
+                    }
+                }
+            }
+        }
     }
 #undef QW_LOAD
 }
@@ -419,17 +460,28 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
     }
 }
 
-template <int MT, int RCG, int U, int NW>
+template <int MT, int RCG, int U, int NW, int S = 1>
 hipError_t launch4(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
     const dim3 grid(t.blocks, t.m_tiles);
     if (debug)
-        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, true>), grid, dim3(64 * NW), t.lds_bytes,
-                           st, a);
+        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, S, true>), grid, dim3(64 * NW),
+                           t.lds_bytes, st, a);
     else
-        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, false>), grid, dim3(64 * NW), t.lds_bytes,
-                           st, a);
+        hipLaunchKernelGGL((k_gemv_w4a8<MT, RCG, U, NW, S, false>), grid, dim3(64 * NW),
+                           t.lds_bytes, st, a);
     return hipGetLastError();
+}
+
+// split-K: at most 2 rows of X per workgroup, 4 or 8 waves
+template <int MT, int NW>
+hipError_t launch_split(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    if (t.u == 4)
+        return t.splitk == 2 ? launch4<MT, 0, 4, NW, 2>(a, t, debug, st)
+                             : launch4<MT, 0, 4, NW, 4>(a, t, debug, st);
+    return t.splitk == 2 ? launch4<MT, 0, 8, NW, 2>(a, t, debug, st)
+                         : launch4<MT, 0, 8, NW, 4>(a, t, debug, st);
 }
 
 template <int MT, int TMAX, int NW>
@@ -477,6 +529,17 @@ hipError_t launch_lds(const W4A8Args& a, const GemvTiling& t, bool debug, hipStr
 template <int NW>
 hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
+    if (t.splitk > 1) {
+        if constexpr (NW == 16) {
+            return hipErrorInvalidValue;
+        } else {
+            switch (t.mt) {
+            case 1: return launch_split<1, NW>(a, t, debug, st);
+            case 2: return launch_split<2, NW>(a, t, debug, st);
+            default: return hipErrorInvalidValue;
+            }
+        }
+    }
     if (t.tmax > 0) {
         switch (t.mt) {
         case 1: return launch_eager_t<1, NW>(a, t, debug, st);

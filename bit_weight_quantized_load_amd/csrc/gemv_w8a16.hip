@@ -1,4 +1,5 @@
-// W8A16 GEMV for decode (M < 16): per-channel INT8 weights dequantized in
+// W8A16 GEMV for decode (the M <= 2 path of gemv_w8a16; any M through the tiled
+// entry): per-channel INT8 weights dequantized in
 // registers against f16 activations, fp32 accumulation, f16 output.
 //
 // What is computed follows the ChatGLM2-6B W8A16 write-up (TPU-MLIR): section 2
@@ -102,13 +103,16 @@ __device__ __forceinline__ void store_x(rsrc_t xres, uint4 (&xp)[kXP], uint32_t*
 }
 
 // RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
-// RCG == 0: LDS variant, U tiles per batch.
-template <int MT, int RCG, int U, int NW>
+// RCG == 0: LDS variant, U tiles per batch; S > 1 splits K as in the W4A8 kernel, the
+// fp32 partial sums of the S slices being added in slice order.
+template <int MT, int RCG, int U, int NW, int S = 1>
 __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
 {
     constexpr int kThreads = 64 * NW;
     constexpr bool kReg = RCG > 0;
+    constexpr int NR = NW / S;  // row runs per workgroup
     static_assert(!kReg || MT == 1, "register variant is for one row of X");
+    static_assert(!kReg || S == 1, "split-K is in the LDS variant");
     constexpr int kB = kReg ? RCG : U;
     extern __shared__ uint32_t s_dyn[];  // LDS variant: [MT][padded chunks][8 words]; then scales
 
@@ -119,16 +123,22 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
     const int M = p.M, N = p.N, K = p.K, CG = p.cg;
     const int m0 = blockIdx.y * MT;
     const int mt = min(MT, M - m0);
-    const int nb = kReg ? 1 : (CG + U - 1) / U;
-    const int chunks = nb * kB * 32;  // LDS variant: chunks per X row in LDS (zero padded)
+    // k-slice of this wave: tiles [c_lo, c_lo + Tw) of each of its row groups
+    const int ks = S > 1 ? wave % S : 0;
+    const int rw = S > 1 ? wave / S : wave;
+    const int T = (CG + S - 1) / S;
+    const int c_lo = ks * T;
+    const int Tw = max(0, min(CG, c_lo + T) - c_lo);
+    const int nb = kReg ? 1 : (T + U - 1) / U;
+    const int chunks = S * nb * kB * 32;  // LDS variant: chunks per X row in LDS (zero padded)
 
-    // Waves along N split the row groups evenly: wave gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    // Row runs along N split the row groups evenly: run gw owns [gw*nrg/W, (gw+1)*nrg/W).
     const int W = p.nwaves;
-    const int gw0 = blockIdx.x * NW;
+    const int gw0 = blockIdx.x * NR;
     const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int rg_blk_end = (int)(((int64_t)min(gw0 + NR, W) * p.nrg) / W);
     const int nrg_blk = rg_blk_end - rg_blk;
-    const int gw = gw0 + wave;
+    const int gw = gw0 + rw;
     const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
     const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
     const int nrg_w = rg1 - rg0;
@@ -143,8 +153,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
         const int r_ = (Q) / nb, c0_ = ((Q) - r_ * nb) * kB;                                    \
         _Pragma("unroll") for (int u_ = 0; u_ < kB; ++u_)                                       \
         {                                                                                       \
-            const bool ok_ = (Q) < nq && c0_ + u_ < CG;                                         \
-            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c0_ + u_) * 1024u        \
+            const bool ok_ = (Q) < nq && c0_ + u_ < Tw;                                         \
+            WBUF[u_] = load16_stream(wres, ok_ ? wbase + (uint32_t)(r_ * CG + c_lo + c0_ + u_) * 1024u \
                                         : 0x80000000u);                                         \
         }                                                                                       \
         /* keep the batch's loads ahead of the dots that follow: without this the    */       \
@@ -190,10 +200,16 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
     __syncthreads();
 
     const int nw0 = rg0 * 2;
+    // split-K partial sums [run][row group][m][row][slice], after the scales
+    const int PW = (p.nrg + W - 1) / W;
+    float* s_part = reinterpret_cast<float*>(s_scale + 2 * kThreads);
     auto finish_row_group = [&](float (&acc)[4], int mm, int rgi) {
         const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
         const int n = nw0 + rgi * 2 + sub;
-        if (j == 31 && n < N && mm < mt) {
+        if constexpr (S > 1) {
+            if (j == 31)
+                s_part[(((rw * PW + rgi) * MT + mm) * 2 + sub) * S + ks] = v;
+        } else if (j == 31 && n < N && mm < mt) {
             const float s = __half2float(__ushort_as_half(s_scale[n - rg_blk * 2]));
             p.Y[(size_t)(m0 + mm) * N + n] = __half_as_ushort(__float2half_rn(v * s));
         }
@@ -233,7 +249,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
                 _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
                 {                                                                               \
                     const uint4* ap_ = reinterpret_cast<const uint4*>(                          \
-                        s_dyn + ((size_t)mm * chunks + (b_ * U + u_) * 32 + j) * 8);            \
+                        s_dyn + ((size_t)mm * chunks + (c_lo + b_ * U + u_) * 32 + j) * 8);     \
                     split8(ap_[0], ap_[1], a_[u_]);                                             \
                 }                                                                               \
                 _Pragma("unroll") for (int u_ = 0; u_ < U; ++u_)                                \
@@ -260,6 +276,28 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
         if (q < nq)
             QW_COMPUTE(wa, q);
 #undef QW_COMPUTE
+        if constexpr (S > 1) {
+            // every wave reaches this barrier; slice 0's wave of each run adds the
+            // partials in slice order and applies the scale
+            __syncthreads();
+            if (ks == 0 && lane < 2) {
+                for (int rgi = 0; rgi < nrg_w; ++rgi) {
+                    const int n = nw0 + rgi * 2 + lane;
+#pragma unroll
+                    for (int mm = 0; mm < MT; ++mm) {
+                        const float* pp = s_part + (((rw * PW + rgi) * MT + mm) * 2 + lane) * S;
+                        float v = pp[0];
+#pragma unroll
+                        for (int k = 1; k < S; ++k)
+                            v += pp[k];
+                        if (n < N && mm < mt) {
+                            const float sc = __half2float(__ushort_as_half(s_scale[n - rg_blk * 2]));
+                            p.Y[(size_t)(m0 + mm) * N + n] = __half_as_ushort(__float2half_rn(v * sc));
+                        }
+                    }
+                }
+            }
+        }
     }
 #undef QW_LOAD
     (void)act;
@@ -380,12 +418,21 @@ hipError_t launch_eager_t(const W8A16Args& a, const GemvTiling& t, hipStream_t s
     return t.tmax == 8 ? launch_eager<MT, 8, NW>(a, t, st) : launch_eager<MT, 16, NW>(a, t, st);
 }
 
-template <int MT, int RCG, int U, int NW>
+template <int MT, int RCG, int U, int NW, int S = 1>
 hipError_t launch4(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
     const dim3 grid(t.blocks, t.m_tiles);
-    hipLaunchKernelGGL((k_gemv_w8a16<MT, RCG, U, NW>), grid, dim3(64 * NW), t.lds_bytes, st, a);
+    hipLaunchKernelGGL((k_gemv_w8a16<MT, RCG, U, NW, S>), grid, dim3(64 * NW), t.lds_bytes, st, a);
     return hipGetLastError();
+}
+
+// split-K: at most 2 rows of X per workgroup, 4 or 8 waves
+template <int MT, int NW>
+hipError_t launch_split(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    if (t.u == 4)
+        return t.splitk == 2 ? launch4<MT, 0, 4, NW, 2>(a, t, st) : launch4<MT, 0, 4, NW, 4>(a, t, st);
+    return t.splitk == 2 ? launch4<MT, 0, 8, NW, 2>(a, t, st) : launch4<MT, 0, 8, NW, 4>(a, t, st);
 }
 
 template <int NW>
@@ -413,6 +460,17 @@ hipError_t launch_lds(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 template <int NW>
 hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
+    if (t.splitk > 1) {
+        if constexpr (NW == 16) {
+            return hipErrorInvalidValue;
+        } else {
+            switch (t.mt) {
+            case 1: return launch_split<1, NW>(a, t, st);
+            case 2: return launch_split<2, NW>(a, t, st);
+            default: return hipErrorInvalidValue;
+            }
+        }
+    }
     if (t.tmax > 0) {
         switch (t.mt) {
         case 1: return launch_eager_t<1, NW>(a, t, st);

@@ -43,7 +43,7 @@ inline size_t packed_bytes(int bits, int64_t N, int64_t K)
 // K up to kRegCG * 512 keeps a lane's activations for a whole row in registers.
 constexpr int kRegCG = 8;
 
-// Launch shape of the GEMV kernels (M < 16).
+// Launch shape of the GEMV kernels.
 struct GemvTiling {
     int mt;           // rows of X per workgroup (1, 2, 4, 8)
     int m_tiles;      // ceil(M / mt)
@@ -52,8 +52,10 @@ struct GemvTiling {
     int tmax;         // > 0: eager variant, every tile of a wave (at most tmax) loaded up front
     int u;            // LDS variant: tiles per load batch (4 or 8), two batches in flight
     int nw;           // waves per workgroup (4, 8 or 16)
-    int nwaves;       // waves along N; they split the row groups evenly
-    int blocks;       // workgroups along N = ceil(nwaves / nw)
+    int splitk;       // LDS variant: waves sharing each row group, each taking a k-slice
+                      //   (1, 2 or 4; above 1 only with 4 or 8 waves and mt <= 2)
+    int nwaves;       // row runs along N; they split the row groups evenly
+    int blocks;       // workgroups along N = ceil(nwaves / (nw / splitk))
     int lds_bytes;    // dynamic LDS
 };
 
@@ -78,8 +80,11 @@ struct W8A16Args {
     int cg, nrg, nwaves;
 };
 
-// Skinny GEMM (M >= kMfmaMinM) on the matrix cores.
-constexpr int kMfmaMinM = 16;
+// Rows of X from which gemv_w4a8 / gemv_w8a16 run on the matrix cores instead of the
+// GEMV kernels (measured on MI355X at K = 4096, N = 27392: the W4A8 GEMM is faster from
+// two rows, the W8A16 one from three).
+constexpr int kMfmaMinM4 = 2;
+constexpr int kMfmaMinM8 = 3;
 
 struct MfmaW4A8Args {
     const uint8_t* Xp;      // X codes in MFMA operand order (workspace)
@@ -105,10 +110,16 @@ struct MfmaW8A16Args {
 };
 
 size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K);
+// Launch shape of the matrix-core kernels: nw waves per workgroup (4 or 8), mb blocks
+// of 16 rows of X per workgroup, nbw blocks of 16 output rows per wave.
+bool mfma_shape_ok(int bits, int nw, int mb, int nbw);
+void mfma_default_shape(int bits, int64_t M, int* nw, int* mb, int* nbw);
 hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
-                            const float* w_scale, float* Y, void* workspace, hipStream_t st);
+                            const float* w_scale, float* Y, void* workspace, int nw, int mb,
+                            int nbw, hipStream_t st);
 hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
-                             const uint16_t* w_scale, uint16_t* Y, hipStream_t st);
+                             const uint16_t* w_scale, uint16_t* Y, int nw, int mb, int nbw,
+                             hipStream_t st);
 
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,
                           hipStream_t st);

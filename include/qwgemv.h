@@ -72,10 +72,10 @@ enum {
 size_t qw_w4_packed_bytes(int64_t N, int64_t K);
 size_t qw_w8_packed_bytes(int64_t N, int64_t K);
 
-/* Workspace that gemv_w4a8 (op 0) or gemv_w8a16 (op 1) needs for shape (M, N, K).
-   0 means the call needs none and accepts workspace == NULL: every GEMV (M < 16)
-   finishes its rows inside one workgroup, and gemv_w8a16 needs none at any M.
-   gemv_w4a8 with M >= 16 runs on the matrix cores and needs
+/* Workspace that gemv_w4a8 (op 0), gemv_w8a16 (op 1) or qw_gemm_w4a8_mfma (op 2) needs
+   for shape (M, N, K).  0 means the call needs none and accepts workspace == NULL:
+   gemv_w4a8 at M == 1 (the GEMV finishes its rows inside one workgroup) and gemv_w8a16
+   at any M.  gemv_w4a8 with M >= 2 runs on the matrix cores and needs
    align256(ceil(M/16) * ceil(K/64) * 1024) + align256(4 * M) bytes: the activation
    codes and scales, quantized once per call in operand order.  Its contents need
    no initialisation and are overwritten by every call; calls that share one
@@ -113,8 +113,8 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    X fp32 [M][K], Wq from quantize_pack_w4, w_scale fp32 [N] -> Y fp32 [M][N] with
    Y[m][n] = ((float)acc[m][n] * w_scale[n]) * a_scale[m] and
    acc[m][n] = sum_k q[n][k] * xq[m][k] in int32, where xq and a_scale are exactly
-   what quant_act_i8 computes.  M < 16: one GEMV kernel with the activation
-   quantization fused into its prologue; workspace may be NULL.  M >= 16: the
+   what quant_act_i8 computes.  M == 1: one GEMV kernel with the activation
+   quantization fused into its prologue; workspace may be NULL.  M >= 2: the
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
    bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM; results are the same
    bits as the GEMV's. */
@@ -125,7 +125,7 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
    quantize_pack_w8, w_scale_f16 [N] -> Y f16 [M][N] with
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
-   rounding.  M < 16: GEMV kernel; M >= 16: f16 matrix-core GEMM on the exactly cast
+   rounding.  M <= 2: GEMV kernel; M >= 3: f16 matrix-core GEMM on the exactly cast
    weights.  No workspace at any M (workspace may be NULL). */
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
                int64_t N, int64_t K, uint16_t* Y_f16, void* workspace, size_t ws_bytes,
@@ -144,20 +144,40 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
                        int64_t N, int64_t K, float* Y, int32_t* acc, int8_t* xq,
                        float* a_scale, void* workspace, size_t ws_bytes, void* stream);
 
-/* The GEMV kernels (M < 16) with an explicit launch shape instead of the built-in
+/* The GEMV kernels (any M up to 65535, rows of X in groups of up to 8 per workgroup)
+   with an explicit launch shape instead of the built-in
    choice.  u = 0 keeps each lane's activations in registers (only M == 1 with
    K <= 4096); u = 1 issues every weight load of a wave before its first dot product
    (at most 16 tiles of 512 k per wave, M <= 4 per workgroup); u = 4 or 8 reads the
    activations from LDS in batches of u tiles, two batches in flight.  nw = waves per
-   workgroup (4, 8 or 16); nwaves = waves along N, which split the ceil(N/4) (INT4) or
-   ceil(N/2) (INT8) row groups evenly, at most 64 row groups each.  Results do not
-   depend on the launch shape.  QW_ERR_TILING for an invalid shape. */
+   workgroup (4, 8 or 16); nwaves = row runs along N, which split the ceil(N/4) (INT4)
+   or ceil(N/2) (INT8) row groups evenly, at most 64 row groups each.  splitk = 1, or
+   2 or 4 to split K (u = 4 or 8, nw = 4 or 8, at most 16 row groups per run): that
+   many waves of a workgroup share each row run, each taking one k-slice of its tiles,
+   and their partial sums are added in on-chip memory.  Results do not depend on the
+   launch shape, except that W8A16 with splitk > 1 adds its fp32 partial sums in a
+   different order.  QW_ERR_TILING for an invalid shape. */
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
-                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves,
+                       int64_t N, int64_t K, float* Y, int u, int nw, int nwaves, int splitk,
                        void* stream);
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                         int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
-                        int nwaves, void* stream);
+                        int nwaves, int splitk, void* stream);
+
+/* The matrix-core kernels (the M >= 2 path of gemv_w4a8, M >= 3 of gemv_w8a16) at any
+   M with an explicit launch shape: nw waves per workgroup (4 or 8), mb blocks of 16
+   rows of X per workgroup (1, 2 or 4 for W4A8, not 4 with nw 4 and nbw 2; 1 or 2 for
+   W8A16), nbw blocks of 16 output rows per wave (1 or 2; not 2 with nw 8 and mb 1 for
+   W4A8, not 2 with nw 8 for W8A16).  Rows of X are padded to a multiple of 16 with
+   zeros.  The W4A8 one needs a workspace of qw_workspace_bytes(2, M, N, K) bytes (else
+   QW_ERR_WORKSPACE).  Results do not depend on the launch shape; the W4A8 outputs equal
+   gemv_w4a8's bit for bit.  QW_ERR_TILING for an invalid shape. */
+int qw_gemm_w4a8_mfma(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                      int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes, int nw,
+                      int mb, int nbw, void* stream);
+int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
+                       int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int nw, int mb,
+                       int nbw, void* stream);
 
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 18
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -59,11 +59,15 @@ def test_status_strings():
     assert L.qw_status_str(99) == b"unknown status"
 
 
-def test_no_shape_needs_a_workspace():
-    for op in (0, 1):
-        for (M, N, K) in [(1, 512, 256), (1, 18944, 3584), (1, 3584, 18944), (4, 27392, 4096),
-                          (1, 512, 3584), (3, 5, 96), (15, 7, 512)]:
-            assert L.qw_workspace_bytes(op, M, N, K) == 0
+def test_which_shapes_need_a_workspace():
+    # the GEMVs (W4A8 at M == 1, W8A16 at any M) need none
+    for (M, N, K) in [(1, 512, 256), (1, 18944, 3584), (1, 3584, 18944), (1, 512, 3584)]:
+        assert L.qw_workspace_bytes(0, M, N, K) == 0
+    for (M, N, K) in [(1, 512, 256), (4, 27392, 4096), (3, 5, 96), (15, 7, 512), (512, 64, 4096)]:
+        assert L.qw_workspace_bytes(1, M, N, K) == 0
+    # W4A8 from M == 2 runs on the matrix cores with a workspace
+    for (M, N, K) in [(4, 27392, 4096), (3, 5, 96), (15, 7, 512)]:
+        assert L.qw_workspace_bytes(0, M, N, K) > 0
 
 
 def test_skinny_w4a8_workspace_size_and_checks():
@@ -73,7 +77,11 @@ def test_skinny_w4a8_workspace_size_and_checks():
         want = align(-(-M // 16) * -(-K // 64) * 1024) + align(4 * M)
         assert L.qw_workspace_bytes(0, M, 27392, K) == want, (M, K)
         assert L.qw_workspace_bytes(1, M, 27392, K) == 0
-    # M >= 16 needs the workspace; validation fails before anything is launched
+    # M == 1 needs none; from M == 2 W4A8 needs one
+    assert L.qw_workspace_bytes(0, 1, 27392, 4096) == 0
+    assert L.qw_workspace_bytes(0, 2, 27392, 4096) == align(4096 // 64 * 1024) + align(8)
+    # M >= 2 needs the workspace; validation fails before anything is launched
+    assert L.gemv_w4a8(A, A2, A3, 2, 64, 512, A4, NULL, 0, NULL) == qw.QW_ERR_WORKSPACE
     assert L.gemv_w4a8(A, A2, A3, 16, 64, 512, A4, NULL, 0, NULL) == qw.QW_ERR_WORKSPACE
     need = L.qw_workspace_bytes(0, 16, 64, 512)
     assert L.gemv_w4a8(A, A2, A3, 16, 64, 512, A4, A, need - 16, NULL) == qw.QW_ERR_WORKSPACE
@@ -100,16 +108,46 @@ def test_gemv_rejects_bad_arguments(fn):
 @pytest.mark.parametrize("fn", ["qw_gemv_w4a8_tiled", "qw_gemv_w8a16_tiled"])
 def test_tiled_rejects_bad_launch_shapes(fn):
     f = getattr(L, fn)
-    # (M, N, u, nw, nwaves): bad batch, bad wave count, no waves, register variant for
-    # M > 1 or K > 4096, more than 64 row groups per wave
-    for (M, N, K, u, nw, nwaves) in [(1, 64, 4096, 3, 8, 1), (1, 64, 4096, 8, 5, 1),
-                                     (1, 64, 4096, 8, 8, 0), (1, 64, 4096, 8, 8, -1),
-                                     (2, 64, 4096, 0, 4, 16), (1, 64, 8192, 0, 4, 16),
-                                     (1, 1000, 512, 8, 4, 1)]:
-        assert f(A, A2, A3, M, N, K, A4, u, nw, nwaves, NULL) == qw.QW_ERR_TILING, (M, N, u, nw, nwaves)
-    assert f(A, A2, A3, 1, 64, 4016, A4, 8, 8, 1, NULL) == qw.QW_ERR_SHAPE
-    assert f(NULL, A2, A3, 1, 64, 40, A4, 8, 8, 1, NULL) == qw.QW_ERR_NULL
-    assert f(MIS, A2, A3, 1, 64, 4096, A4, 8, 8, 1, NULL) == qw.QW_ERR_ALIGN
+    # (M, N, K, u, nw, nwaves, splitk): bad batch, bad wave count, no waves, register
+    # variant for M > 1 or K > 4096, more than 64 row groups per wave; split-K with a
+    # bad factor, with the register or eager variant, with 16 waves, or with more than
+    # 16 row groups per row run
+    for (M, N, K, u, nw, nwaves, sk) in [(1, 64, 4096, 3, 8, 1, 1), (1, 64, 4096, 8, 5, 1, 1),
+                                         (1, 64, 4096, 8, 8, 0, 1), (1, 64, 4096, 8, 8, -1, 1),
+                                         (2, 64, 4096, 0, 4, 16, 1), (1, 64, 8192, 0, 4, 16, 1),
+                                         (1, 1000, 512, 8, 4, 1, 1), (1, 64, 4096, 8, 8, 1, 3),
+                                         (1, 64, 4096, 0, 4, 16, 2), (1, 64, 4096, 1, 4, 16, 2),
+                                         (1, 64, 4096, 8, 16, 16, 2), (1, 200, 4096, 8, 4, 1, 2),
+                                         (1, 64, 4096, 8, 4, 16, 0)]:
+        assert f(A, A2, A3, M, N, K, A4, u, nw, nwaves, sk, NULL) == qw.QW_ERR_TILING, \
+            (M, N, u, nw, nwaves, sk)
+    assert f(A, A2, A3, 1, 64, 4016, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_SHAPE
+    assert f(NULL, A2, A3, 1, 64, 40, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_NULL
+    assert f(MIS, A2, A3, 1, 64, 4096, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_ALIGN
+
+
+@pytest.mark.parametrize("fn", ["qw_gemm_w4a8_mfma", "qw_gemm_w8a16_mfma"])
+def test_matrix_core_helpers_reject_bad_launch_shapes(fn):
+    f = getattr(L, fn)
+    w4 = fn == "qw_gemm_w4a8_mfma"
+
+    def call(X, M, K, nw, mb, nbw, ws=A2, wsb=1 << 20):
+        if w4:
+            return f(X, A2, A3, M, 64, K, A4, ws, wsb, nw, mb, nbw, NULL)
+        return f(X, A2, A3, M, 64, K, A4, nw, mb, nbw, NULL)
+
+    for (nw, mb, nbw) in [(2, 1, 1), (16, 1, 1), (4, 3, 1), (4, 1, 3), (4, 1, 0), (8, 4, 8)]:
+        assert call(A, 16, 512, nw, mb, nbw) == qw.QW_ERR_TILING, (nw, mb, nbw)
+    if not w4:  # W8A16: at most 2 blocks of rows, and not 8 waves of 2 row blocks
+        assert call(A, 16, 512, 4, 4, 1) == qw.QW_ERR_TILING
+        assert call(A, 16, 512, 8, 1, 2) == qw.QW_ERR_TILING
+    else:  # the workspace is checked
+        assert call(A, 16, 512, 4, 1, 1, ws=NULL, wsb=0) == qw.QW_ERR_WORKSPACE
+        assert call(A, 16, 512, 4, 1, 1, wsb=100) == qw.QW_ERR_WORKSPACE
+        assert L.qw_workspace_bytes(2, 3, 64, 512) == L.qw_workspace_bytes(0, 16, 64, 512)
+    assert call(A, 16, 500, 4, 1, 1) == qw.QW_ERR_SHAPE
+    assert call(NULL, 16, 512, 4, 1, 1) == qw.QW_ERR_NULL
+    assert call(MIS, 16, 512, 4, 1, 1) == qw.QW_ERR_ALIGN
 
 
 def test_packers_and_helpers_reject_bad_arguments():

@@ -245,7 +245,8 @@ def test_skinny_sweep_sampled(M):
 
 # ----------------------------------------------- skinny GEMM on the matrix cores --
 
-# M >= 16 runs the MFMA kernels: ragged M, N and K (K % 64 == 32 leaves half a step)
+# M >= 2 (W4A8) / M >= 3 (W8A16) runs the MFMA kernels: ragged M, N and K (K % 64 == 32
+# leaves half a step)
 MFMA_SHAPES = [(16, 64, 512), (17, 100, 544), (33, 257, 1056), (64, 128, 4096),
                (65, 70, 1024), (100, 300, 2080), (130, 36, 3584)]
 
@@ -272,6 +273,35 @@ def test_skinny_gemm_full_parity(M, N, K):
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
     assert rel_l2(y, y64) <= W8A16_RL2
     assert not np.any(y[M // 2]) and not np.any(y[:, 0])
+
+
+MFMA_LAUNCH = [(4, 1, 1), (4, 2, 1), (4, 4, 1), (4, 1, 2), (8, 1, 1), (8, 2, 2), (8, 4, 2)]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 96, 512), (3, 70, 1056), (16, 257, 3584), (40, 300, 2080)])
+def test_matrix_core_kernels_every_launch_shape(M, N, K):
+    """The matrix-core kernels at small and ragged M (rows of X padded to 16), every
+    launch shape: W4A8 equals the GEMV bit for bit, W8A16 is within the bar (its fp32
+    sums start at a k that depends on the workgroup, so the last bits may differ
+    between launch shapes)."""
+    say("mfma shapes", M, N, K)
+    W = wl.weights(500 + M, 1, N, K, outlier_rows=N >= 100)
+    X = wl.activations(500 + M, 2, M, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    Xd = dev(X)
+    Yg = qw.gemv_w4a8_tiled(Xd, Wq, s, 8, 4, 7)
+    assert_w4a8_close(host(Yg), ref["Y"])
+    X16 = X.astype(np.float16)
+    X16d = dev(X16)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
+    for (nw, mb, nbw) in MFMA_LAUNCH:
+        Y = qw.gemm_w4a8_mfma(Xd, Wq, s, nw, mb, nbw)
+        assert torch.equal(Y, Yg), (nw, mb, nbw)
+        if not (mb == 4 or (nw == 8 and nbw == 2)):
+            y = host(qw.gemm_w8a16_mfma(X16d, Wq8, s16, nw, mb, nbw))
+            assert rel_l2(y, y64) <= W8A16_RL2, (nw, mb, nbw)
 
 
 def test_skinny_gemm_workspace_reuse_and_sizes():
@@ -372,6 +402,46 @@ def test_every_launch_shape_gives_the_same_result(M):
         if y_first is None:
             y_first = y
         assert np.array_equal(y.view(np.uint16), y_first.view(np.uint16)), (u, nw, nwaves)
+
+
+SPLITK_SHAPES = [(1, 512, 3584), (1, 100, 18944), (2, 37, 4640), (1, 4100, 1056), (2, 64, 32)]
+
+
+@pytest.mark.parametrize("M,N,K", SPLITK_SHAPES)
+def test_split_k_launch_shapes(M, N, K):
+    """Split-K inside the workgroup (2 or 4 waves per row run, each a k-slice) on ragged
+    shapes, including slices that hold no tile: W4A8 equals the oracle to its bar and
+    the unsplit launch bit for bit (int32 sums), W8A16 meets its bar."""
+    say("split-K", M, N, K)
+    W = wl.weights(600 + M, 1, N, K, outlier_rows=N >= 100)
+    X = wl.activations(600 + M, 2, M, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    X16 = X.astype(np.float16)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
+    Xd, X16d = dev(X), dev(X16)
+    Y1 = qw.gemv_w4a8_tiled(Xd, Wq, s, 4, 4, max(1, -(-N // 4) // 2))
+    assert_w4a8_close(host(Y1), ref["Y"])
+    nrg4, nrg8 = -(-N // 4), -(-N // 2)
+    n = n8 = 0
+    for splitk in (2, 4):
+        for u in (4, 8):
+            for nw in (4, 8):
+                for nwaves in (1, 3, 16, 100, 1000):
+                    if -(-nrg4 // nwaves) > 16 or -(-nrg8 // nwaves) > 16 or nw < splitk:
+                        continue
+                    Y = qw.gemv_w4a8_tiled(Xd, Wq, s, u, nw, nwaves, splitk)
+                    assert torch.equal(Y, Y1), (u, nw, nwaves, splitk)
+                    n += 1
+                    try:  # the f16 row of X, padded per k-slice, may not fit in LDS
+                        y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, u, nw, nwaves, splitk))
+                    except qw.QWError as e:
+                        assert e.status == qw.QW_ERR_TILING and K > 8192
+                        continue
+                    assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, nwaves, splitk)
+                    n8 += 1
+    assert n >= 4 and n8 >= 2
 
 
 def test_repeated_calls_are_deterministic():

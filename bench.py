@@ -10,8 +10,10 @@ not from the 256 MB last-level cache.
 
 Printed: ONE JSON line with `value` = algorithmic bytes of both GEMVs / time per
 step (GB/s), per-kernel microseconds and GB/s, the roofline of the dominant kernel
-(per-launch algorithmic bytes / average launch time from HIP events), and the CPU
-oracle timed on this host on the same inputs.
+(per-launch algorithmic bytes / average launch time from HIP events), the CPU
+oracle timed on this host on the same inputs, and the linear-layer time per token
+of the 28-layer decode-step chain in one HIP graph (unfused and with q|k|v and
+gate|up fused).
 """
 from __future__ import annotations
 
@@ -100,6 +102,52 @@ def cpu_baseline(W, X, X16, seconds, b_step):
                       "N=18944) in %.1f s on %d OpenMP threads" % (reps, dt, nt)}
 
 
+def chain_measurement(qw, wl, torch, replays):
+    """Linear-layer time per token of the decode step: 28 layers of the seven Qwen-7B
+    W4A8 linears plus the 3584 -> 152064 lm_head, captured in one HIP graph, unfused
+    (197 launches) and with q|k|v and gate|up fused (113 launches).  Each layer streams
+    its own copy of the packed weights."""
+    from bit_weight_quantized_load_amd import chain
+
+    seed = wl.QWEN7B_W4A8["seed"]
+    layer = {}
+    for name, K, N in wl.QWEN7B_LINEARS:
+        W = wl.weights(seed, wl.tensor_id(name, 0), N, K, outlier_rows=True)
+        layer[name] = qw.quantize_pack_w4(torch.from_numpy(W).cuda())
+        del W
+    c3 = wl.LMHEAD_W4A8
+    W = wl.weights(c3["seed"], wl.tensor_id("lm_head", 0), c3["N"], c3["K"])
+    lm = qw.quantize_pack_w4(torch.from_numpy(W).cuda())
+    del W
+    xh = torch.from_numpy(wl.activations(seed, wl.tensor_id("q_proj", 1), 1, wl.HIDDEN,
+                                         outlier_channels=4)).cuda()
+    xi = torch.from_numpy(wl.activations(seed, wl.tensor_id("down_proj", 1), 1, wl.INTERMEDIATE,
+                                         outlier_channels=4)).cuda()
+    out = {}
+    for key, fused in (("unfused", False), ("fused_qkv_gate_up", True)):
+        c = chain.DecodeChain(layer, lm, xh, xi, layers=wl.LAYERS, fused=fused)
+        g = c.capture()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / replays
+        b = c.bytes_per_token
+        out[key] = {"launches_per_token": c.launches_per_token, "us_per_token": round(us, 2),
+                    "tokens_per_s": round(1e6 / us, 1), "algo_bytes_per_token": b,
+                    "GB/s": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+        del c, g
+        torch.cuda.empty_cache()
+    out["layers"] = wl.LAYERS
+    out["replays"] = replays
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -107,6 +155,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chain", action="store_true",
+                    help="skip the 28-layer decode-step chain measurement")
+    ap.add_argument("--chain-replays", type=int, default=20)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run --steps device-to-device copies of BYTES bytes (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters) and exit")
@@ -223,6 +274,12 @@ def main():
     roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom}
 
+    del g_step, g4, g8, copies
+    torch.cuda.empty_cache()
+    chain_info = None
+    if not args.no_chain:
+        chain_info = chain_measurement(qw, wl, torch, args.chain_replays)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(W, X, X16, args.cpu_seconds, b_step)
@@ -235,6 +292,7 @@ def main():
         "config": {"workload": c["workload"], "M": M, "K": K, "N": N,
                    "step": "gemv_w4a8 + gemv_w8a16", "weight_copies_rotated": R},
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+        "decode_chain": chain_info,
     }
     print(json.dumps(line), flush=True)
 

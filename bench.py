@@ -102,6 +102,62 @@ def cpu_baseline(W, X, X16, seconds, b_step):
                       "N=18944) in %.1f s on %d OpenMP threads" % (reps, dt, nt)}
 
 
+def _pmc_per_dispatch(path, counter):
+    """{kernel name: [value per dispatch]} of one counter from a rocprofv3 --pmc CSV
+    (values reported per dimension are summed per dispatch)."""
+    import collections
+    import csv
+
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if (r.get("Counter_Name") or r.get("Counter-Name")) != counter:
+                continue
+            name = r.get("Kernel_Name") or r.get("Kernel-Name")
+            disp = r.get("Dispatch_Id") or r.get("Dispatch-Id")
+            per[name][disp] += float(r.get("Counter_Value") or r.get("Counter-Value"))
+    return {k: list(v.values()) for k, v in per.items()}
+
+
+def write_traffic(fetch_copy, write_copy, fetch_bench, write_bench, copy_bytes, commands):
+    """HBM bytes per launch of both GEMVs from four rocprofv3 --pmc runs (FETCH_SIZE and
+    WRITE_SIZE, KiB per dispatch, each on a plain device copy of copy_bytes and on this
+    benchmark), each counter scaled by copy_bytes / (its median reading on the copy);
+    written to profiles/traffic_<kernel>_<workload>.json with the hash of the kernel
+    sources they were taken on."""
+    import statistics
+
+    import workloads as wl
+
+    def median_of(path, counter, key):
+        vals = [v for k, vs in _pmc_per_dispatch(path, counter).items() if key in k for v in vs]
+        if not vals:
+            raise SystemExit("no %s dispatches of %s in %s" % (counter, key, path))
+        return statistics.median(vals)
+
+    fc = median_of(fetch_copy, "FETCH_SIZE", "copyBuffer")
+    wc = median_of(write_copy, "WRITE_SIZE", "copyBuffer")
+    f_scale, w_scale = copy_bytes / 1024.0 / fc, copy_bytes / 1024.0 / wc
+    c = wl.HEADLINE
+    M, K, N = c["M"], c["K"], c["N"]
+    for kernel, algo in (("gemv_w4a8", bytes_w4a8(M, N, K)), ("gemv_w8a16", bytes_w8a16(M, N, K))):
+        fk = median_of(fetch_bench, "FETCH_SIZE", kernel)
+        wk = median_of(write_bench, "WRITE_SIZE", kernel)
+        hbm = int(round((fk * f_scale + wk * w_scale) * 1024))
+        out = {"kernel": kernel, "workload": c["workload"],
+               "kernel_source_sha": kernel_source_hash(kernel),
+               "fetch_size_kib": fk, "write_size_kib": wk,
+               "fetch_scale": round(f_scale, 6), "write_scale": round(w_scale, 6),
+               "hbm_bytes_per_launch": hbm, "algorithmic_bytes_per_launch": algo,
+               "ratio": round(hbm / algo, 4),
+               "calibration": {"copy_bytes": copy_bytes, "fetch_size_kib": fc, "write_size_kib": wc},
+               "commands": commands}
+        path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, c["workload"]))
+        with open(path, "w") as fh:
+            json.dump(out, fh, indent=1)
+        print(json.dumps(out))
+
+
 def chain_measurement(qw, wl, torch, replays):
     """Linear-layer time per token of the decode step: 28 layers of the seven Qwen-7B
     W4A8 linears plus the 3584 -> 152064 lm_head, captured in one HIP graph, unfused
@@ -161,7 +217,19 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run --steps device-to-device copies of BYTES bytes (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters) and exit")
+    ap.add_argument("--write-traffic", nargs=4, metavar="CSV",
+                    help="(no GPU) write profiles/traffic_*.json from the counter CSVs of "
+                         "four rocprofv3 --pmc runs: FETCH_SIZE and WRITE_SIZE on the copy "
+                         "calibration, then FETCH_SIZE and WRITE_SIZE on this benchmark")
+    ap.add_argument("--pmc-commands", default="",
+                    help="with --write-traffic: the four commands, separated by ';;'")
     args = ap.parse_args()
+
+    if args.write_traffic:
+        cmds = [c.strip() for c in args.pmc_commands.split(";;") if c.strip()]
+        write_traffic(*args.write_traffic, copy_bytes=args.copy_calibration or 268435456,
+                      commands=cmds)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only (the GEMV needs no communication; "

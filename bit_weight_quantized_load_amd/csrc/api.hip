@@ -67,10 +67,18 @@ int scale_lds_bytes(int bits, int nw) { return bits == 4 ? 4 * 64 * nw * 4 : 2 *
 bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
                const qw::TileLayout& L)
 {
-    if (u != 0 && u != 1 && u != 4 && u != 8)
+    if (u != 0 && u != 1 && u != 2 && u != 4 && u != 8)
         return false;
-    if (u == 0 && !(M == 1 && L.cg <= qw::kRegCG))
+    if ((u == 0 || u == 2) && !(M == 1 && L.cg <= qw::kRegCG))
         return false;
+    // all in flight: 4 waves per workgroup with at most 4 (INT8) or 5 (INT4) row groups
+    // per wave, or for INT4 8 waves with at most 3
+    if (u == 2) {
+        const int64_t per = nwaves < 1 ? 0 : ((int64_t)L.nrg + nwaves - 1) / nwaves;
+        const int64_t cap = bits == 8 ? (nw == 4 ? 4 : 0) : (nw == 4 ? 5 : (nw == 8 ? 3 : 0));
+        if (splitk != 1 || nwaves < 1 || per > cap)
+            return false;
+    }
     if (nw != 4 && nw != 8 && nw != 16)
         return false;
     if (splitk != 1 && splitk != 2 && splitk != 4)
@@ -109,6 +117,12 @@ GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw,
         t.reg_cg = L.cg;
         mt_cap = 1;
         tiles = bits == 4 ? L.cg : 0;  // W8A16 keeps X in registers, W4A8 stages codes
+    } else if (u == 2) {
+        // all in flight: at most 4 row groups per wave, X (codes or f16) staged in LDS
+        t.reg_cg = L.cg;
+        t.tmax = (int)(((int64_t)L.nrg + nwaves - 1) / nwaves);
+        mt_cap = 1;
+        tiles = L.cg;
     } else if (u == 1) {
         const int64_t per_wave = ((int64_t)L.nrg + nwaves - 1) / nwaves;
         t.tmax = per_wave * L.cg <= 8 ? 8 : 16;
@@ -141,8 +155,9 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
     // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 with
     // K <= 4096: activations in registers, about 1600 waves (six per CU), each with a
-    // whole number of row groups.  INT8: the LDS variant with 4-tile batches and about
-    // 4736 waves.  INT4 with K > 4096: the LDS variant with 4-tile batches and 8-wave
+    // whole number of row groups.  INT8 at M == 1 with K <= 4096: all weight tiles of a
+    // wave in flight (12.0 us against 13.2 us at 3584 x 18944); otherwise the LDS
+    // variant with 4-tile batches and about 4736 waves.  INT4 with K > 4096: the LDS variant with 4-tile batches and 8-wave
     // workgroups (one block of X per workgroup in the prologue); below 2048 row groups
     // (the 18944 -> 3584 down projection) each row group is split over two waves along
     // K, which measured 15.4 us against 19.5 us unsplit.
@@ -155,6 +170,12 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     };
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG)
         return make_tiling(bits, M, N, K, 0, 4, (int)waves_for(1600));
+    if (bits == 8 && M == 1 && L.cg <= qw::kRegCG) {
+        // every weight tile of a wave requested up front: one row group per wave, two
+        // from 1024 to 2048 row groups (q/o-sized shapes), where that measured faster
+        const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
+        return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
+    }
     if (bits == 8)
         return make_tiling(bits, M, N, K, 4, 4, (int)waves_for(4736));
     const GemvTiling t = nrg < 2048 ? make_tiling(bits, M, N, K, 4, 8, (int)nrg, 2)
@@ -226,6 +247,8 @@ int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, in
     a.cg = L.cg;
     a.nrg = L.nrg;
     a.nwaves = t.nwaves;
+    a.per = L.nrg / t.nwaves;
+    a.rem = L.nrg % t.nwaves;
     a.dbg_acc = acc;
     a.dbg_xq = xq;
     a.dbg_a = a_scale;
@@ -257,6 +280,8 @@ int run_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_
     a.cg = L.cg;
     a.nrg = L.nrg;
     a.nwaves = t.nwaves;
+    a.per = L.nrg / t.nwaves;
+    a.rem = L.nrg % t.nwaves;
     return hip_status(qw::launch_gemv_w8a16(a, t, static_cast<hipStream_t>(stream)));
 }
 

@@ -149,7 +149,11 @@ __device__ __forceinline__ void quantize_rows(const W4A8Args& p, float4 (&xv)[XV
     }
     if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0 && tid < mt)
         p.dbg_a[m0 + tid] = s_a[tid];
+    // keep the weight unpacking of the caller below this barrier: hoisted above it, it
+    // makes every wave wait for its first weight tile before the barrier can complete
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
 }
 
 // RCG > 0: register variant for exactly RCG tiles per row group (MT == 1).
@@ -190,15 +194,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
     const int chunks = S * nb * kB * 16;         // chunks per X row in LDS (zero padded)
 
     // ---- this wave's run of tiles
-    // Row runs along N split the row groups evenly: run gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    // Row runs along N split the row groups evenly: run gw owns [rg_of(gw), rg_of(gw + 1)).
     const int W = p.nwaves;
     const int gw0 = blockIdx.x * NR;
-    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NR, W) * p.nrg) / W);
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NR, W), p.per, p.rem);
     const int nrg_blk = rg_blk_end - rg_blk;
     const int gw = gw0 + rw;
-    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
-    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
     const int nrg_w = rg1 - rg0;
     const int nq = nrg_w * nb;  // batches of this wave
     const rsrc_t wres =
@@ -248,7 +252,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 
     const int nw0 = rg0 * 4;  // first row of this wave
     // split-K partial sums [run][row group][m][row][slice], after the scales
-    const int PW = (p.nrg + W - 1) / W;
+    const int PW = p.per + (p.rem > 0 ? 1 : 0);
     int* s_part = reinterpret_cast<int*>(s_scale + 4 * kThreads);
     auto finish_row_group = [&](int (&acc)[4], int mm, int rgi) {
         const int v = row_sum16(acc[0] + acc[1] + acc[2] + acc[3]) >> 4;
@@ -378,12 +382,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
 
     const int W = p.nwaves;
     const int gw0 = blockIdx.x * NW;
-    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NW, W), p.per, p.rem);
     const int nrg_blk = rg_blk_end - rg_blk;
     const int gw = gw0 + wave;
-    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
-    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
     const int T = (rg1 - rg0) * CG;  // tiles of this wave, at most TMAX
     const rsrc_t wres =
         make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
@@ -457,6 +461,129 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_eager(W4A8Args p)
                 for (int e = 0; e < 8; ++e)
                     a_cur[mm][e] = a_nxt[mm][e];
         }
+    }
+}
+
+// All-in-flight variant (M == 1, RCG tiles per row group, at most RPW row groups per
+// wave): every weight tile of the wave is requested right after the scales and X,
+// before the prologue waits for anything, so the whole weight stream of the launch is
+// in flight while the activations are quantized, and each wave meets one memory
+// latency instead of one per batch.  Straight-line code: tiles of row groups the wave
+// does not own read zeros and only their stores are skipped.  The activation codes of
+// the lane's RCG chunks are then held in registers, as in the register variant.
+template <int RCG, int RPW, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_flight(W4A8Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    constexpr int XV = (RCG * 128 + kThreads - 1) / kThreads;  // X float4 per thread
+    extern __shared__ uint32_t s_dyn[];  // [RCG * 16 chunks][8 words] codes, then scales
+    __shared__ float s_red[1][NW];
+    __shared__ float s_a[1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, sub = lane >> 4;
+    const int N = p.N, CG = p.cg;
+    constexpr int chunks = RCG * 16;
+
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NW, W), p.per, p.rem);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
+    const int nrg_w = rg1 - rg0;
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
+
+    float* s_scale = reinterpret_cast<float*>(s_dyn + (size_t)chunks * 8);
+    const int rows_blk = min(nrg_blk * 4, N - rg_blk * 4);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 4, (uint32_t)max(rows_blk, 0) * 4u);
+    uint32_t sc_reg[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        sc_reg[i] = load4(sres, (uint32_t)(tid + i * kThreads) * 4u);
+    float4 xv[XV];
+    load_x_block<XV, kThreads>(p, 0, 1, 0, 0, tid, xv);
+    issue_barrier();
+    uint4 w[RPW][RCG];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            w[r][c] = load16_stream(wres, r < nrg_w ? wbase + (uint32_t)(r * CG + c) * 1024u
+                                                    : 0x80000000u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        s_scale[tid + i * kThreads] = __uint_as_float(sc_reg[i]);
+    quantize_rows<1, NW, XV, true, false>(p, xv, s_dyn, s_red, s_a, chunks, 1, 0, 1, tid);
+
+    uint32_t act[RCG][8];
+#pragma unroll
+    for (int c = 0; c < RCG; ++c)
+        load_act(s_dyn + (size_t)(c * 16 + j) * 8, act[c]);
+    const float a = s_a[0];
+    const int nw0 = rg0 * 4;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        int acc[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            dot_chunk(w[r][c], act[c], acc);
+        const int v = row_sum16(acc[0] + acc[1] + acc[2] + acc[3]) >> 4;
+        const int n = nw0 + r * 4 + sub;
+        if (j == 0 && r < nrg_w && n < N)
+            p.Y[n] = ((float)v * s_scale[n - rg_blk * 4]) * a;
+    }
+}
+
+template <int RCG, int RPW, int NW>
+hipError_t launch_flight(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_gemv_w4a8_flight<RCG, RPW, NW>), dim3(t.blocks), dim3(64 * NW),
+                       t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+// at most 5 row groups per wave with 4 waves per workgroup, 3 with 8
+template <int RCG>
+hipError_t launch_flight_r(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    if (t.nw == 8) {
+        switch (t.tmax) {
+        case 1: return launch_flight<RCG, 1, 8>(a, t, st);
+        case 2: return launch_flight<RCG, 2, 8>(a, t, st);
+        case 3: return launch_flight<RCG, 3, 8>(a, t, st);
+        default: return hipErrorInvalidValue;
+        }
+    }
+    switch (t.tmax) {
+    case 1: return launch_flight<RCG, 1, 4>(a, t, st);
+    case 2: return launch_flight<RCG, 2, 4>(a, t, st);
+    case 3: return launch_flight<RCG, 3, 4>(a, t, st);
+    case 4: return launch_flight<RCG, 4, 4>(a, t, st);
+    case 5: return launch_flight<RCG, 5, 4>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_flight_any(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch_flight_r<1>(a, t, st);
+    case 2: return launch_flight_r<2>(a, t, st);
+    case 3: return launch_flight_r<3>(a, t, st);
+    case 4: return launch_flight_r<4>(a, t, st);
+    case 5: return launch_flight_r<5>(a, t, st);
+    case 6: return launch_flight_r<6>(a, t, st);
+    case 7: return launch_flight_r<7>(a, t, st);
+    case 8: return launch_flight_r<8>(a, t, st);
+    default: return hipErrorInvalidValue;
     }
 }
 
@@ -563,6 +690,8 @@ hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStre
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
+    if (t.u == 2)
+        return debug ? hipErrorInvalidValue : launch_flight_any(a, t, st);
     switch (t.nw) {
     case 4: return launch_nw<4>(a, t, debug, st);
     case 8: return launch_nw<8>(a, t, debug, st);

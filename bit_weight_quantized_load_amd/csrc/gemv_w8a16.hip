@@ -132,15 +132,15 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
     const int nb = kReg ? 1 : (T + U - 1) / U;
     const int chunks = S * nb * kB * 32;  // LDS variant: chunks per X row in LDS (zero padded)
 
-    // Row runs along N split the row groups evenly: run gw owns [gw*nrg/W, (gw+1)*nrg/W).
+    // Row runs along N split the row groups evenly: run gw owns [rg_of(gw), rg_of(gw + 1)).
     const int W = p.nwaves;
     const int gw0 = blockIdx.x * NR;
-    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NR, W) * p.nrg) / W);
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NR, W), p.per, p.rem);
     const int nrg_blk = rg_blk_end - rg_blk;
     const int gw = gw0 + rw;
-    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
-    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
     const int nrg_w = rg1 - rg0;
     const int nq = nrg_w * nb;  // batches of this wave
     const rsrc_t wres =
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16(W8A16Args p)
 
     const int nw0 = rg0 * 2;
     // split-K partial sums [run][row group][m][row][slice], after the scales
-    const int PW = (p.nrg + W - 1) / W;
+    const int PW = p.per + (p.rem > 0 ? 1 : 0);
     float* s_part = reinterpret_cast<float*>(s_scale + 2 * kThreads);
     auto finish_row_group = [&](float (&acc)[4], int mm, int rgi) {
         const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
@@ -322,12 +322,12 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16_eager(W8A16Args p)
 
     const int W = p.nwaves;
     const int gw0 = blockIdx.x * NW;
-    const int rg_blk = (int)(((int64_t)gw0 * p.nrg) / W);
-    const int rg_blk_end = (int)(((int64_t)min(gw0 + NW, W) * p.nrg) / W);
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NW, W), p.per, p.rem);
     const int nrg_blk = rg_blk_end - rg_blk;
     const int gw = gw0 + wave;
-    const int rg0 = gw < W ? (int)(((int64_t)gw * p.nrg) / W) : rg_blk_end;
-    const int rg1 = gw < W ? (int)(((int64_t)(gw + 1) * p.nrg) / W) : rg_blk_end;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
     const int T = (rg1 - rg0) * CG;
     const rsrc_t wres =
         make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
@@ -418,6 +418,128 @@ hipError_t launch_eager_t(const W8A16Args& a, const GemvTiling& t, hipStream_t s
     return t.tmax == 8 ? launch_eager<MT, 8, NW>(a, t, st) : launch_eager<MT, 16, NW>(a, t, st);
 }
 
+// All-in-flight variant (M == 1, RCG tiles per row group, at most RPW row groups per
+// wave), as in the W4A8 kernel: every weight tile of the wave is requested right after
+// the scales and X, X is staged once per workgroup in LDS in chunk order, and each lane
+// then holds the f16 activations of its RCG chunks in registers.
+template <int RCG, int RPW, int NW>
+__global__ __launch_bounds__(64 * NW) void k_gemv_w8a16_flight(W8A16Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    constexpr int chunks = RCG * 32;
+    constexpr int kXP = (chunks * 2 + kThreads - 1) / kThreads;  // 16-byte X pieces per thread
+    extern __shared__ uint32_t s_dyn[];  // [RCG * 32 chunks][8 words] X, then scales
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, sub = lane >> 5;
+    const int N = p.N, K = p.K, CG = p.cg;
+
+    const int W = p.nwaves;
+    const int gw0 = blockIdx.x * NW;
+    const int rg_blk = rg_of(gw0, p.per, p.rem);
+    const int rg_blk_end = rg_of(min(gw0 + NW, W), p.per, p.rem);
+    const int nrg_blk = rg_blk_end - rg_blk;
+    const int gw = gw0 + wave;
+    const int rg0 = gw < W ? rg_of(gw, p.per, p.rem) : rg_blk_end;
+    const int rg1 = gw < W ? rg_of(gw + 1, p.per, p.rem) : rg_blk_end;
+    const int nrg_w = rg1 - rg0;
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
+
+    uint16_t* s_scale = reinterpret_cast<uint16_t*>(s_dyn + (size_t)chunks * 8);
+    const int rows_blk = min(nrg_blk * 2, N - rg_blk * 2);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg_blk * 2, (uint32_t)max(rows_blk, 0) * 2u);
+    uint16_t sc_reg[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        sc_reg[i] = load2(sres, (uint32_t)(tid + i * kThreads) * 2u);
+    const rsrc_t xres = make_rsrc(p.X, (uint32_t)K * 2u);
+    uint4 xp[kXP];
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int q = i * kThreads + tid;  // piece q: f16 elements 8q .. 8q+7
+        xp[i] = load16(xres, q * 8 < K ? (uint32_t)q * 16u : 0x80000000u);
+    }
+    issue_barrier();
+    uint4 w[RPW][RCG];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            w[r][c] = load16_stream(wres, r < nrg_w ? wbase + (uint32_t)(r * CG + c) * 1024u
+                                                    : 0x80000000u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int q = i * kThreads + tid;
+        if (q < chunks * 2)
+            reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        s_scale[tid + i * kThreads] = sc_reg[i];
+    __syncthreads();
+
+    uint32_t act[RCG][8];
+#pragma unroll
+    for (int c = 0; c < RCG; ++c) {
+        const uint4* ap = reinterpret_cast<const uint4*>(s_dyn + (size_t)(c * 32 + j) * 8);
+        split8(ap[0], ap[1], act[c]);
+    }
+    const int nw0 = rg0 * 2;
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            dot_chunk_f16(w[r][c], act[c], acc);
+        const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
+        const int n = nw0 + r * 2 + sub;
+        if (j == 31 && r < nrg_w && n < N) {
+            const float sc = __half2float(__ushort_as_half(s_scale[n - rg_blk * 2]));
+            p.Y[n] = __half_as_ushort(__float2half_rn(v * sc));
+        }
+    }
+}
+
+template <int RCG, int RPW>
+hipError_t launch_flight(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_gemv_w8a16_flight<RCG, RPW, 4>), dim3(t.blocks), dim3(256),
+                       t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int RCG>
+hipError_t launch_flight_r(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.tmax) {
+    case 1: return launch_flight<RCG, 1>(a, t, st);
+    case 2: return launch_flight<RCG, 2>(a, t, st);
+    case 3: return launch_flight<RCG, 3>(a, t, st);
+    case 4: return launch_flight<RCG, 4>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_flight_any(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch_flight_r<1>(a, t, st);
+    case 2: return launch_flight_r<2>(a, t, st);
+    case 3: return launch_flight_r<3>(a, t, st);
+    case 4: return launch_flight_r<4>(a, t, st);
+    case 5: return launch_flight_r<5>(a, t, st);
+    case 6: return launch_flight_r<6>(a, t, st);
+    case 7: return launch_flight_r<7>(a, t, st);
+    case 8: return launch_flight_r<8>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int MT, int RCG, int U, int NW, int S = 1>
 hipError_t launch4(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
@@ -494,6 +616,8 @@ hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
+    if (t.u == 2)
+        return launch_flight_any(a, t, st);
     switch (t.nw) {
     case 4: return launch_nw<4>(a, t, st);
     case 8: return launch_nw<8>(a, t, st);

@@ -40,6 +40,14 @@ inline size_t packed_bytes(int bits, int64_t N, int64_t K)
     return (size_t)t.nrg * (size_t)t.cg * 1024u;
 }
 
+// First row group of row run g out of W when nrg = per * W + rem row groups are split
+// evenly (the first rem runs take one more); g = W gives nrg.  Multiply-add only: the
+// quotient and remainder come from the host, so no division runs on the device.
+__host__ __device__ __forceinline__ int rg_of(int g, int per, int rem)
+{
+    return g * per + (g < rem ? g : rem);
+}
+
 // K up to kRegCG * 512 keeps a lane's activations for a whole row in registers.
 constexpr int kRegCG = 8;
 
@@ -66,6 +74,7 @@ struct W4A8Args {
     float* Y;
     int M, N, K;
     int cg, nrg, nwaves;
+    int per, rem;      // row groups per row run: nrg = per * nwaves + rem (see rg_of)
     int32_t* dbg_acc;  // optional [M][N]
     int8_t* dbg_xq;    // optional [M][K]
     float* dbg_a;      // optional [M]
@@ -78,6 +87,7 @@ struct W8A16Args {
     uint16_t* Y;
     int M, N, K;
     int cg, nrg, nwaves;
+    int per, rem;      // row groups per row run: nrg = per * nwaves + rem (see rg_of)
 };
 
 // Rows of X from which gemv_w4a8 / gemv_w8a16 run on the matrix cores instead of the

@@ -154,8 +154,9 @@ bool fits_lds(const GemvTiling& t) { return t.lds_bytes <= kMaxLds; }
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
     // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 with
-    // K <= 4096: activations in registers, about 1600 waves (six per CU), each with a
-    // whole number of row groups.  INT8 at M == 1 with K <= 4096: all weight tiles of a
+    // K <= 4096: activations in registers; 2048 waves (two 4-wave workgroups per CU) from
+    // 2048 row groups up (7.95 us against 8.5 us at 3584 x 18944), below that about
+    // 1600 waves, each with a whole number of row groups.  INT8 at M == 1 with K <= 4096: all weight tiles of a
     // wave in flight (12.0 us against 13.2 us at 3584 x 18944); otherwise the LDS
     // variant with 4-tile batches and about 4736 waves.  INT4 with K > 4096: the LDS variant with 4-tile batches and 8-wave
     // workgroups (one block of X per workgroup in the prologue); below 2048 row groups
@@ -169,12 +170,18 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         return (nrg + per - 1) / per;
     };
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG)
-        return make_tiling(bits, M, N, K, 0, 4, (int)waves_for(1600));
+        return make_tiling(bits, M, N, K, 0, 4, (int)(nrg >= 2048 ? 2048 : waves_for(1600)));
     if (bits == 8 && M == 1 && L.cg <= qw::kRegCG) {
         // every weight tile of a wave requested up front: one row group per wave, two
         // from 1024 to 2048 row groups (q/o-sized shapes), where that measured faster
         const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
         return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
+    }
+    if (bits == 8 && M == 1 && nrg < 2048) {
+        // long K, short N (the 18944 -> 3584 down projection): split K over two waves
+        const GemvTiling t = make_tiling(bits, M, N, K, 4, 8, (int)nrg, 2);
+        if (t.lds_bytes <= kMaxLds)
+            return t;
     }
     if (bits == 8)
         return make_tiling(bits, M, N, K, 4, 4, (int)waves_for(4736));

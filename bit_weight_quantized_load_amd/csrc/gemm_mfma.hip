@@ -290,6 +290,121 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8(MfmaW4A8Args p)
     }
 }
 
+// The same linear with all of the workgroup's X codes resident in LDS (one block of 16
+// rows, K up to 4096: at most 64 KB): X is copied in once, behind the first two steps'
+// weight loads, and the steps then stream weights only, with no barrier and no X loads.
+constexpr int kXAllMaxBytes = 64 * 1024;
+
+template <int NW, int NBW>
+__global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_xall(MfmaW4A8Args p)
+{
+    constexpr int kThreads = 64 * NW;
+    constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
+    constexpr int kWT = 4 * NBW;
+    extern __shared__ uint8_t s_mem[];  // X [KS steps][1 KB], then per wave kWT padded tiles
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r = lane & 15;
+    const int CG = p.cg, KS = p.ks, MG = p.mgroups;
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int mg = blk % MG, nb = blk / MG;  // mg: the block of 16 rows of X
+    const int rgw = (nb * NW + wave) * kWT;
+    const int nrg_w = max(0, min(kWT, p.nrg - rgw));
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)min(rgw, p.nrg) * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
+    const rsrc_t xres = make_rsrc(p.Xp + (size_t)mg * KS * 1024u, (uint32_t)KS * 1024u);
+    const int xbytes = CG * 8 * 1024;  // whole 512-k steps; past K the loads read zeros
+    uint8_t* s_x = s_mem;
+    uint8_t* s_w = s_mem + xbytes + wave * kWT * kW4TilePitch;
+
+    uint4 w0[kWT], w1[kWT], w2[kWT];
+#define QW_LOADW(WB, C)                                                                          \
+    _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                           \
+        WB[i_] = load16_stream(wres, (C) < CG ? (uint32_t)(i_ * CG + (C)) * 1024u + (uint32_t)lane * 16u \
+                                              : 0x80000000u);
+    // X first (every piece of the workgroup's block; pieces past the block read zeros),
+    // then the weights of steps 0 and 1; storing X waits for X alone
+    uint4 xr[kXP];
+#pragma unroll
+    for (int v = 0; v < kXP; ++v) {
+        const int pc = v * kThreads + tid;
+        xr[v] = load16(xres, pc * 16 < xbytes ? (uint32_t)pc * 16u : 0x80000000u);
+    }
+    QW_LOADW(w0, 0);
+    QW_LOADW(w1, 1);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int v = 0; v < kXP; ++v) {
+        const int pc = v * kThreads + tid;
+        if (pc * 16 < xbytes)
+            *reinterpret_cast<uint4*>(s_x + (size_t)pc * 16) = xr[v];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    v4i acc[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b)
+        acc[b] = v4i{0, 0, 0, 0};
+    const int sub = lane >> 4, j = lane & 15;
+    const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
+
+#define QW_STEP(WC, WN, C)                                                                       \
+    {                                                                                            \
+        QW_LOADW(WN, (C) + 2);                                                                   \
+        __builtin_amdgcn_sched_barrier(0);                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                       \
+            *reinterpret_cast<uint4*>(s_w + i_ * kW4TilePitch + sub * kW4RowPitch + j * 16) = WC[i_]; \
+        const uint8_t* xb_ = s_x + (size_t)(C) * 8 * 1024;                                       \
+        _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
+        {                                                                                        \
+            const uint4 b4_ = *reinterpret_cast<const uint4*>(xb_ + (s_ * 64 + lane) * 16);      \
+            const v4i bo_ = {(int)b4_.x, (int)b4_.y, (int)b4_.z, (int)b4_.w};                     \
+            _Pragma("unroll") for (int b_ = 0; b_ < NBW; ++b_)                                   \
+            {                                                                                    \
+                const uint2 w_ = *reinterpret_cast<const uint2*>(s_w + b_ * 4 * kW4TilePitch + a_off + s_ * 32); \
+                const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),     \
+                                (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};    \
+                acc[b_] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, bo_, acc[b_], 0, 0, 0);      \
+            }                                                                                    \
+        }                                                                                        \
+    }
+
+    int c = 0;
+    for (; c + 3 <= CG; c += 3) {
+        QW_STEP(w0, w2, c);
+        QW_STEP(w1, w0, c + 1);
+        QW_STEP(w2, w1, c + 2);
+    }
+    if (c < CG)
+        QW_STEP(w0, w2, c);
+    if (c + 1 < CG)
+        QW_STEP(w1, w0, c + 1);
+#undef QW_STEP
+#undef QW_LOADW
+
+    const rsrc_t sres = make_rsrc(p.w_scale, (uint32_t)p.N * 4u);
+    const int m = mg * 16 + r;
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+        const int n0 = 4 * rgw + 16 * b + 4 * g;
+        float sc[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            sc[i] = __uint_as_float(load4(sres, (uint32_t)(n0 + i) * 4u));
+        if (m < p.M) {
+            const float am = p.a_scale[m];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (n0 + i < p.N)
+                    p.Y[(size_t)m * p.N + n0 + i] = ((float)(acc[b][i] >> 4) * sc[i]) * am;
+        }
+    }
+}
+
 // ---------------------------------------------------------------- W8A16 -------
 
 // Padded LDS image of one INT8 tile (2 rows x 32 chunks): row sub at sub * 528, chunk
@@ -469,6 +584,22 @@ hipError_t go_w4(const MfmaW4A8Args& p, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int NW, int NBW>
+hipError_t go_w4_xall(const MfmaW4A8Args& p, hipStream_t st)
+{
+    const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)NW * 4 * NBW * kW4TilePitch;
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_xall<NW, NBW>),
+                                          (size_t)kXAllMaxBytes + (size_t)NW * 4 * NBW * kW4TilePitch);
+    if (e != hipSuccess)
+        return e;
+    const int64_t nblocks = ((int64_t)p.nrg + NW * 4 * NBW - 1) / (NW * 4 * NBW);
+    if (nblocks * p.mgroups > 0x7fffffff)
+        return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((k_gemm_w4a8_xall<NW, NBW>), dim3((unsigned)(nblocks * p.mgroups)),
+                       dim3(64 * NW), lds, st, p);
+    return hipGetLastError();
+}
+
 template <int NW, int MB, int NBW>
 hipError_t go_w8(const MfmaW8A16Args& p, hipStream_t st)
 {
@@ -493,22 +624,30 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
     if (nbw != 1 && nbw != 2)
         return false;
     if (bits == 4)
-        return (mb == 1 || mb == 2 || mb == 4) && !(nw == 4 && mb == 4 && nbw == 2) &&
-               !(nw == 8 && mb == 1 && nbw == 2);
+        return ((mb == 1 || mb == 2 || mb == 4) && !(nw == 4 && mb == 4 && nbw == 2) &&
+                !(nw == 8 && mb == 1 && nbw == 2)) ||
+               (mb == 0 && !(nw == 4 && nbw == 2));
     // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
     // rows would not fit the registers
     return (mb == 1 || mb == 2) && !(nw == 8 && nbw == 2);
 }
 
-void mfma_default_shape(int bits, int64_t M, int* nw, int* mb, int* nbw)
+void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
 {
+    // measured at K = 4096, N = 27392: W4A8 up to 16 rows with X resident in LDS and
+    // 8-wave workgroups (16.3 us against 17.1 us), then 8 waves and 2 or 4 blocks of X;
+    // W8A16 8 waves with 1 or 2 blocks
     const int64_t mbtot = (M + 15) / 16;
-    *nw = 4;
+    *nw = 8;
     *nbw = 1;
-    if (bits == 4)
-        *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
-    else
+    if (bits == 4) {
+        if (mbtot == 1 && (K + 511) / 512 * 8192 <= 65536)
+            *mb = 0;
+        else
+            *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
+    } else {
         *mb = mbtot >= 2 ? 2 : 1;
+    }
 }
 
 size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K)
@@ -557,6 +696,18 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.nrg = L.nrg;
     p.ks = ks;
     p.mbtot = mbtot;
+    if (mb == 0) {  // X resident in LDS: one block of 16 rows per workgroup
+        if ((size_t)L.cg * 8 * 1024 > (size_t)kXAllMaxBytes)
+            return hipErrorInvalidValue;
+        p.mgroups = mbtot;
+        if (nw == 4 && nbw == 1)
+            return go_w4_xall<4, 1>(p, st);
+        if (nw == 8 && nbw == 1)
+            return go_w4_xall<8, 1>(p, st);
+        if (nw == 8 && nbw == 2)
+            return go_w4_xall<8, 2>(p, st);
+        return hipErrorInvalidValue;
+    }
     p.mgroups = (mbtot + mb - 1) / mb;
 #define QW_GO(NW_, MB_, NBW_)                                                                    \
     if (nw == NW_ && mb == MB_ && nbw == NBW_)                                                   \

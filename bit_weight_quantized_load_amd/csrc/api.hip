@@ -67,8 +67,15 @@ int scale_lds_bytes(int bits, int nw) { return bits == 4 ? 4 * 64 * nw * 4 : 2 *
 bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
                const qw::TileLayout& L)
 {
-    if (u != 0 && u != 1 && u != 2 && u != 4 && u != 8)
+    if (u < 0 || u > 8 || u == 5 || u == 6 || u == 7)
         return false;
+    // all in flight with K split over 2..8 (INT4) or 2..7 (INT8) waves of 8-tile slices:
+    // one row run of at most 4 row groups per workgroup, M == 1, K <= 4096 * splitk
+    if (u == 3) {
+        const int64_t per = nwaves < 1 ? 0 : ((int64_t)L.nrg + nwaves - 1) / nwaves;
+        return M == 1 && splitk >= 2 && splitk <= (bits == 4 ? 8 : 7) && L.cg <= 8 * splitk &&
+               per >= 1 && per <= 4;
+    }
     if ((u == 0 || u == 2) && !(M == 1 && L.cg <= qw::kRegCG))
         return false;
     // all in flight: 4 waves per workgroup with at most 4 (INT8) or 5 (INT4) row groups
@@ -107,12 +114,25 @@ GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw,
     t.nw = nw;
     t.splitk = splitk;
     t.nwaves = nwaves;
-    const int runs = nw / splitk;  // row runs per workgroup
+    const int runs = nw / splitk > 0 ? nw / splitk : 1;  // row runs per workgroup
     t.blocks = (nwaves + runs - 1) / runs;
     t.tmax = 0;
     t.reg_cg = 0;
     const int scale_bytes = scale_lds_bytes(bits, nw);
     int tiles = 0, mt_cap = splitk > 1 ? 2 : 8;
+    if (u == 3) {
+        // one row run per workgroup of splitk waves; LDS: X (codes or f16) for 8 * splitk
+        // tiles, then RPW rows' scales and partial sums
+        const int per = (int)(((int64_t)L.nrg + nwaves - 1) / nwaves);
+        t.tmax = per == 3 ? 4 : per;
+        t.nw = splitk;
+        t.blocks = nwaves;
+        t.mt = 1;
+        t.m_tiles = (int)M;
+        const int R = bits == 4 ? 4 : 2;
+        t.lds_bytes = 8 * splitk * act_tile_bytes(bits) + t.tmax * R * 4 + t.tmax * R * splitk * 4;
+        return t;
+    }
     if (u == 0) {
         t.reg_cg = L.cg;
         mt_cap = 1;
@@ -176,6 +196,18 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         // from 1024 to 2048 row groups (q/o-sized shapes), where that measured faster
         const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
         return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
+    }
+    // M == 1 with K > 4096: all in flight with K split into 8-tile slices, one wave per
+    // slice, where that measured faster: INT4 always (18944 -> 3584: 13.6 us against
+    // 14.7 us; 18944 -> 512: 7.5 against 13.7), INT8 below 1024 row groups (18944 -> 512:
+    // 4.3 us against 7.0)
+    const int64_t slices = (L.cg + 7) / 8;
+    if (M == 1 && slices >= 2 && slices <= (bits == 4 ? 8 : 7) && (bits == 4 || nrg < 1024)) {
+        const int64_t rpw = bits == 4 && nrg >= 512 ? 4 : 1;
+        const GemvTiling t = make_tiling(bits, M, N, K, 3, 4, (int)((nrg + rpw - 1) / rpw),
+                                         (int)slices);
+        if (t.lds_bytes <= kMaxLds)
+            return t;
     }
     if (bits == 8 && M == 1 && nrg < 2048) {
         // long K, short N (the 18944 -> 3584 down projection): split K over two waves
@@ -449,8 +481,15 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
     (void)ws_bytes;
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    return run_w4a8(X, Wq, w_scale, M, N, K, Y, acc, xq, a_scale, workspace,
-                    default_tiling(4, M, N, K), true, stream);
+    // the debug outputs come from the register and LDS variants (every variant gives
+    // the same bits)
+    GemvTiling t = default_tiling(4, M, N, K);
+    if (t.u == 2 || t.u == 3) {
+        const qw::TileLayout L = qw::tile_layout(4, N, K);
+        t = L.cg <= qw::kRegCG && M == 1 ? make_tiling(4, M, N, K, 0, 4, L.nrg < 1600 ? L.nrg : 1600)
+                                         : make_tiling(4, M, N, K, 8, 4, L.nrg < 4096 ? L.nrg : 4096);
+    }
+    return run_w4a8(X, Wq, w_scale, M, N, K, Y, acc, xq, a_scale, workspace, t, true, stream);
 }
 
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,

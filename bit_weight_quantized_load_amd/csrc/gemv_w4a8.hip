@@ -542,6 +542,115 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8_flight(W4A8Args p)
     }
 }
 
+// Long-K form of the all-in-flight variant (M == 1): one row run of up to RPW row groups
+// per workgroup, its S waves each taking one k-slice of 8 tiles (the last one shorter).
+// Each wave requests all of its tiles right after X, holds its slice's activation codes
+// in registers, and leaves one int32 partial per row in LDS; after one barrier wave 0
+// adds the S partials and applies the epilogue.  K up to 4096 * S.
+template <int RPW, int S>
+__global__ __launch_bounds__(64 * S) void k_gemv_w4a8_flight_split(W4A8Args p)
+{
+    constexpr int NW = S, kThreads = 64 * S, RCG = 8;
+    constexpr int XV = 16;  // X float4 per thread: K / 4 <= 16 * kThreads
+    extern __shared__ uint32_t s_dyn[];  // [S * 8 * 16 chunks][8 words] codes; scales; partials
+    __shared__ float s_red[1][NW];
+    __shared__ float s_a[1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // this wave's k-slice
+    const int j = lane & 15, sub = lane >> 4;
+    const int N = p.N, CG = p.cg;
+    constexpr int chunks = S * RCG * 16;
+    const int c_lo = ks * RCG;
+    const int Tw = max(0, min(CG, c_lo + RCG) - c_lo);
+
+    const int W = p.nwaves;  // row runs, one per workgroup
+    const int gw = blockIdx.x;
+    const int rg0 = rg_of(gw, p.per, p.rem);
+    const int rg1 = rg_of(gw + 1, p.per, p.rem);
+    const int nrg_w = gw < W ? rg1 - rg0 : 0;
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)c_lo * 1024u + (uint32_t)lane * 16u;
+
+    float* s_scale = reinterpret_cast<float*>(s_dyn + (size_t)chunks * 8);
+    int* s_part = reinterpret_cast<int*>(s_scale + RPW * 4);  // [RPW][4 rows][S]
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 4, (uint32_t)max(0, min(nrg_w * 4, N - rg0 * 4)) * 4u);
+    const uint32_t sc_reg = load4(sres, (uint32_t)(tid < RPW * 4 ? tid : 0x20000000) * 4u);
+    float4 xv[XV];
+    load_x_block<XV, kThreads>(p, 0, 1, 0, 0, tid, xv);
+    issue_barrier();
+    uint4 w[RPW][RCG];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            w[r][c] = load16_stream(wres, r < nrg_w && c < Tw ? wbase + (uint32_t)(r * CG + c) * 1024u
+                                                             : 0x80000000u);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < RPW * 4)
+        s_scale[tid] = __uint_as_float(sc_reg);
+    quantize_rows<1, NW, XV, true, false>(p, xv, s_dyn, s_red, s_a, chunks, 1, 0, 1, tid);
+
+    uint32_t act[RCG][8];
+#pragma unroll
+    for (int c = 0; c < RCG; ++c)
+        load_act(s_dyn + (size_t)((c_lo + c) * 16 + j) * 8, act[c]);
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        int acc[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            dot_chunk(w[r][c], act[c], acc);
+        const int v = row_sum16(acc[0] + acc[1] + acc[2] + acc[3]) >> 4;
+        if (j == 0)
+            s_part[(r * 4 + sub) * S + ks] = v;
+    }
+    __syncthreads();
+    if (tid < RPW * 4) {
+        const int r = tid >> 2, n = rg0 * 4 + tid;
+        int v = 0;
+#pragma unroll
+        for (int k = 0; k < S; ++k)
+            v += s_part[tid * S + k];
+        if (r < nrg_w && n < N)
+            p.Y[n] = ((float)v * s_scale[tid]) * s_a[0];
+    }
+}
+
+template <int RPW, int S>
+hipError_t launch_flight_split(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_gemv_w4a8_flight_split<RPW, S>), dim3(t.blocks), dim3(64 * S),
+                       t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int RPW>
+hipError_t launch_flight_split_s(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.splitk) {
+    case 2: return launch_flight_split<RPW, 2>(a, t, st);
+    case 3: return launch_flight_split<RPW, 3>(a, t, st);
+    case 4: return launch_flight_split<RPW, 4>(a, t, st);
+    case 5: return launch_flight_split<RPW, 5>(a, t, st);
+    case 6: return launch_flight_split<RPW, 6>(a, t, st);
+    case 7: return launch_flight_split<RPW, 7>(a, t, st);
+    case 8: return launch_flight_split<RPW, 8>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_flight_split_any(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.tmax) {
+    case 1: return launch_flight_split_s<1>(a, t, st);
+    case 2: return launch_flight_split_s<2>(a, t, st);
+    case 4: return launch_flight_split_s<4>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int RCG, int RPW, int NW>
 hipError_t launch_flight(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
 {
@@ -692,6 +801,8 @@ hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, 
 {
     if (t.u == 2)
         return debug ? hipErrorInvalidValue : launch_flight_any(a, t, st);
+    if (t.u == 3)
+        return debug ? hipErrorInvalidValue : launch_flight_split_any(a, t, st);
     switch (t.nw) {
     case 4: return launch_nw<4>(a, t, debug, st);
     case 8: return launch_nw<8>(a, t, debug, st);

@@ -505,6 +505,127 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w8a16_flight(W8A16Args p)
     }
 }
 
+// Long-K form of the all-in-flight variant (M == 1), as in the W4A8 kernel: one row run
+// of up to RPW row groups per workgroup, its S waves each taking a k-slice of 8 tiles;
+// fp32 partial sums added in slice order by wave 0.  K up to 4096 * S.
+template <int RPW, int S>
+__global__ __launch_bounds__(64 * S) void k_gemv_w8a16_flight_split(W8A16Args p)
+{
+    constexpr int kThreads = 64 * S, RCG = 8;
+    constexpr int chunks = S * RCG * 32;
+    constexpr int kXP = (chunks * 2 + kThreads - 1) / kThreads;  // 16-byte X pieces per thread
+    extern __shared__ uint32_t s_dyn[];  // [S * 8 * 32 chunks][8 words] X; scales; partials
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 31, sub = lane >> 5;
+    const int N = p.N, K = p.K, CG = p.cg;
+    const int c_lo = ks * RCG;
+    const int Tw = max(0, min(CG, c_lo + RCG) - c_lo);
+
+    const int W = p.nwaves;
+    const int gw = blockIdx.x;
+    const int rg0 = rg_of(gw, p.per, p.rem);
+    const int rg1 = rg_of(gw + 1, p.per, p.rem);
+    const int nrg_w = gw < W ? rg1 - rg0 : 0;
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)c_lo * 1024u + (uint32_t)lane * 16u;
+
+    uint16_t* s_scale = reinterpret_cast<uint16_t*>(s_dyn + (size_t)chunks * 8);
+    float* s_part = reinterpret_cast<float*>(s_dyn + (size_t)chunks * 8 + RPW);  // [RPW][2][S]
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 2, (uint32_t)max(0, min(nrg_w * 2, N - rg0 * 2)) * 2u);
+    const uint16_t sc_reg = load2(sres, (uint32_t)(tid < RPW * 2 ? tid : 0x20000000) * 2u);
+    const rsrc_t xres = make_rsrc(p.X, (uint32_t)K * 2u);
+    uint4 xp[kXP];
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int q = i * kThreads + tid;
+        xp[i] = load16(xres, q * 8 < K ? (uint32_t)q * 16u : 0x80000000u);
+    }
+    issue_barrier();
+    uint4 w[RPW][RCG];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r)
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            w[r][c] = load16_stream(wres, r < nrg_w && c < Tw ? wbase + (uint32_t)(r * CG + c) * 1024u
+                                                             : 0x80000000u);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < kXP; ++i) {
+        const int q = i * kThreads + tid;
+        if (q < chunks * 2)
+            reinterpret_cast<uint4*>(s_dyn)[q] = xp[i];
+    }
+    if (tid < RPW * 2)
+        s_scale[tid] = sc_reg;
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    uint32_t act[RCG][8];
+#pragma unroll
+    for (int c = 0; c < RCG; ++c) {
+        const uint4* ap = reinterpret_cast<const uint4*>(s_dyn + (size_t)((c_lo + c) * 32 + j) * 8);
+        split8(ap[0], ap[1], act[c]);
+    }
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+        float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int c = 0; c < RCG; ++c)
+            dot_chunk_f16(w[r][c], act[c], acc);
+        const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
+        if (j == 31)
+            s_part[(r * 2 + sub) * S + ks] = v;
+    }
+    __syncthreads();
+    if (tid < RPW * 2) {
+        const int r = tid >> 1, n = rg0 * 2 + tid;
+        float v = s_part[tid * S];
+#pragma unroll
+        for (int k = 1; k < S; ++k)
+            v += s_part[tid * S + k];
+        if (r < nrg_w && n < N) {
+            const float sc = __half2float(__ushort_as_half(s_scale[tid]));
+            p.Y[n] = __half_as_ushort(__float2half_rn(v * sc));
+        }
+    }
+}
+
+template <int RPW, int S>
+hipError_t launch_flight_split(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    hipLaunchKernelGGL((k_gemv_w8a16_flight_split<RPW, S>), dim3(t.blocks), dim3(64 * S),
+                       t.lds_bytes, st, a);
+    return hipGetLastError();
+}
+
+template <int RPW>
+hipError_t launch_flight_split_s(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.splitk) {
+    case 2: return launch_flight_split<RPW, 2>(a, t, st);
+    case 3: return launch_flight_split<RPW, 3>(a, t, st);
+    case 4: return launch_flight_split<RPW, 4>(a, t, st);
+    case 5: return launch_flight_split<RPW, 5>(a, t, st);
+    case 6: return launch_flight_split<RPW, 6>(a, t, st);
+    case 7: return launch_flight_split<RPW, 7>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_flight_split_any(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.tmax) {
+    case 1: return launch_flight_split_s<1>(a, t, st);
+    case 2: return launch_flight_split_s<2>(a, t, st);
+    case 4: return launch_flight_split_s<4>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int RCG, int RPW>
 hipError_t launch_flight(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
@@ -618,6 +739,8 @@ hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_
 {
     if (t.u == 2)
         return launch_flight_any(a, t, st);
+    if (t.u == 3)
+        return launch_flight_split_any(a, t, st);
     switch (t.nw) {
     case 4: return launch_nw<4>(a, t, st);
     case 8: return launch_nw<8>(a, t, st);

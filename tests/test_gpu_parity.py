@@ -367,7 +367,7 @@ def launch_shapes(M, nrg4, nrg8, cg):
     only for M == 1, u = 1 (eager) with at most 16 tiles per wave, at most 64 row
     groups per wave."""
     out = []
-    for u in ((0, 1, 4, 8) if M == 1 else (1, 4, 8)):
+    for u in ((0, 1, 2, 4, 8) if M == 1 else (1, 4, 8)):
         for nw in (4, 8, 16):
             for nwaves in (8, 13, 64, 100, 250, 333, 500, 1000):
                 per4, per8 = -(-nrg4 // nwaves), -(-nrg8 // nwaves)
@@ -375,6 +375,8 @@ def launch_shapes(M, nrg4, nrg8, cg):
                     continue
                 if u == 1 and max(per4, per8) * cg > 16:
                     continue
+                if u == 2 and (nw != 4 or max(per4, per8) > 4):
+                    continue  # all in flight: 4-wave workgroups, at most 4 row groups a wave
                 out.append((u, nw, nwaves))
     return out
 
@@ -443,6 +445,16 @@ def test_split_k_launch_shapes(M, N, K):
                     assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, nwaves, splitk)
                     n8 += 1
     assert n >= 4 and n8 >= 2
+    # all in flight with K in 8-tile slices (M == 1): 2..8 slices, 1..4 row groups a run
+    if M == 1:
+        cg = -(-K // 512)
+        for S in sorted({max(2, -(-cg // 8)), max(2, -(-cg // 8)) + 1}):
+            for per in (1, 2, 3, 4):
+                y4 = qw.gemv_w4a8_tiled(Xd, Wq, s, 3, 4, -(-nrg4 // per), S)
+                assert torch.equal(y4, Y1), ("flight split", S, per)
+                if S <= 7:
+                    y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 3, 4, -(-nrg8 // per), S))
+                    assert rel_l2(y, y64) <= W8A16_RL2, ("flight split", S, per)
 
 
 def test_repeated_calls_are_deterministic():

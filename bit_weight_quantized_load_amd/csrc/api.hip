@@ -175,8 +175,9 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
     // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 with
     // K <= 4096: activations in registers; 2048 waves (two 4-wave workgroups per CU) from
-    // 2048 row groups up (7.95 us against 8.5 us at 3584 x 18944), below that about
-    // 1600 waves, each with a whole number of row groups.  INT8 at M == 1 with K <= 4096: all weight tiles of a
+    // 2048 row groups up (7.95 us against 8.5 us at 3584 x 18944), 1024 waves (one
+    // workgroup per CU) from 1024 (3584 -> 4608: 5.5 us against 6.8 us with one row
+    // group per wave), else one row group per wave.  INT8 at M == 1 with K <= 4096: all weight tiles of a
     // wave in flight (12.0 us against 13.2 us at 3584 x 18944); otherwise the LDS
     // variant with 4-tile batches and about 4736 waves.  INT4 with K > 4096: the LDS variant with 4-tile batches and 8-wave
     // workgroups (one block of X per workgroup in the prologue); below 2048 row groups
@@ -190,7 +191,8 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         return (nrg + per - 1) / per;
     };
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG)
-        return make_tiling(bits, M, N, K, 0, 4, (int)(nrg >= 2048 ? 2048 : waves_for(1600)));
+        return make_tiling(bits, M, N, K, 0, 4,
+                           (int)(nrg >= 2048 ? 2048 : (nrg > 1024 ? 1024 : nrg)));
     if (bits == 8 && M == 1 && L.cg <= qw::kRegCG) {
         // every weight tile of a wave requested up front: one row group per wave, two
         // from 1024 to 2048 row groups (q/o-sized shapes), where that measured faster

@@ -776,7 +776,7 @@ hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStre
             }
         }
     }
-    if (t.tmax > 0) {
+    if (t.u == 1) {
         switch (t.mt) {
         case 1: return launch_eager_t<1, NW>(a, t, debug, st);
         case 2: return launch_eager_t<2, NW>(a, t, debug, st);

@@ -714,7 +714,7 @@ hipError_t launch_nw(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
             }
         }
     }
-    if (t.tmax > 0) {
+    if (t.u == 1) {
         switch (t.mt) {
         case 1: return launch_eager_t<1, NW>(a, t, st);
         case 2: return launch_eager_t<2, NW>(a, t, st);

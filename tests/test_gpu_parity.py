@@ -248,7 +248,7 @@ def test_skinny_sweep_sampled(M):
 # M >= 2 (W4A8) / M >= 3 (W8A16) runs the MFMA kernels: ragged M, N and K (K % 64 == 32
 # leaves half a step)
 MFMA_SHAPES = [(16, 64, 512), (17, 100, 544), (33, 257, 1056), (64, 128, 4096),
-               (65, 70, 1024), (100, 300, 2080), (130, 36, 3584)]
+               (65, 70, 1024), (100, 300, 2080), (130, 36, 3584), (300, 200, 1568)]
 
 
 @pytest.mark.parametrize("M,N,K", MFMA_SHAPES)

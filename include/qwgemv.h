@@ -145,18 +145,26 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
                        float* a_scale, void* workspace, size_t ws_bytes, void* stream);
 
 /* The GEMV kernels (any M up to 65535, rows of X in groups of up to 8 per workgroup)
-   with an explicit launch shape instead of the built-in
-   choice.  u = 0 keeps each lane's activations in registers (only M == 1 with
-   K <= 4096); u = 1 issues every weight load of a wave before its first dot product
-   (at most 16 tiles of 512 k per wave, M <= 4 per workgroup); u = 4 or 8 reads the
-   activations from LDS in batches of u tiles, two batches in flight.  nw = waves per
+   with an explicit launch shape instead of the built-in choice.  nw = waves per
    workgroup (4, 8 or 16); nwaves = row runs along N, which split the ceil(N/4) (INT4)
-   or ceil(N/2) (INT8) row groups evenly, at most 64 row groups each.  splitk = 1, or
-   2 or 4 to split K (u = 4 or 8, nw = 4 or 8, at most 16 row groups per run): that
-   many waves of a workgroup share each row run, each taking one k-slice of its tiles,
-   and their partial sums are added in on-chip memory.  Results do not depend on the
-   launch shape, except that W8A16 with splitk > 1 adds its fp32 partial sums in a
-   different order.  QW_ERR_TILING for an invalid shape. */
+   or ceil(N/2) (INT8) row groups evenly.
+     u = 0  activations in registers, two batches of whole row groups in flight (M == 1,
+            K <= 4096, at most 64 row groups per run);
+     u = 1  every weight load of a wave issued before its first dot product (at most 16
+            tiles of 512 k per wave, M <= 4 per workgroup);
+     u = 2  every weight tile of a wave requested right after X, activations in
+            registers (M == 1, K <= 4096; nw 4 with at most 4 (INT8) or 5 (INT4) row
+            groups per run, or for INT4 nw 8 with at most 3);
+     u = 3  as u = 2 with K split into 8-tile slices, one wave per slice: splitk = 2..8
+            (INT4) or 2..7 (INT8) waves per workgroup with K <= 4096 * splitk, one row
+            run of at most 4 row groups per workgroup (nw is ignored, M == 1);
+     u = 4, 8  activations read from LDS in batches of u tiles, two batches in flight;
+            splitk = 2 or 4 splits each row run's tiles over that many waves of the
+            workgroup (nw 4 or 8, at most 16 row groups per run), whose partial sums
+            are added in on-chip memory.
+   splitk must be 1 unless stated.  Results do not depend on the launch shape, except
+   that W8A16 with splitk > 1 adds its fp32 partial sums in a different order.
+   QW_ERR_TILING for an invalid shape. */
 int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
                        int64_t N, int64_t K, float* Y, int u, int nw, int nwaves, int splitk,
                        void* stream);

@@ -359,6 +359,159 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 #undef QW_LOAD
 }
 
+// Producer-wave variant (M == 1, RCG tiles per row group, one workgroup per CU): P
+// producer waves quantize X while NW consumer waves stream weights.
+//
+// Why: a CU accepts new vector loads only as fast as data comes back, so a wave that
+// has just requested weight tiles stalls on its next load instruction, and any barrier
+// after those loads waits for that stall.  When every wave both requests weights and
+// takes part in the activation reduction (the register variant), the prologue ends
+// only once the first weight batch has been accepted; measured per wave, the codes
+// were ready after 1.3-1.9 us and a second workgroup on the same CU waited 4 us, its X
+// queued behind the first one's weights.  Here the producers request X (before any
+// weight, by the first barrier), reduce the maximum among themselves through an LDS
+// atomic and a counter (no barrier, so no wait on the consumers' load stalls), and
+// write the codes; the consumers request their first row group and meet the producers
+// at the second barrier, then stream the rest with two row groups in flight.
+//
+// Work split: row groups split evenly over the workgroups (p.per / p.rem count row
+// groups per workgroup, not per wave), then evenly over the consumer waves of each.
+// Codes, accumulators and outputs are those of the other variants bit for bit.
+template <int RCG, int NW, int P, bool kDebug>
+__global__ __launch_bounds__(64 * (NW + P)) void k_gemv_w4a8_prod(W4A8Args p)
+{
+    constexpr int XP = (RCG * 128 + 64 * P - 1) / (64 * P);  // X float4 per producer lane
+    constexpr int CH = RCG * 16;                             // chunks of one row of codes
+    __shared__ uint32_t s_act[CH * 8];
+    __shared__ float s_a;
+    __shared__ unsigned s_max, s_cnt;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = lane & 15, sub = lane >> 4;
+    const int N = p.N, K = p.K, CG = p.cg;
+    const int rg_blk = rg_of(blockIdx.x, p.per, p.rem);
+    const int nrg_blk = rg_of(blockIdx.x + 1, p.per, p.rem) - rg_blk;
+    if (tid == 0) {
+        s_max = 0u;
+        s_cnt = 0u;
+    }
+    if (wave >= NW) {
+        // ---- producer pr: float4 blocks [pr * XP, (pr + 1) * XP) of X
+        const int pr = wave - NW;
+        const int K4 = K >> 2;
+        const rsrc_t xr = make_rsrc(p.X, (uint32_t)K * 4u);
+        float4 xv[XP];
+#pragma unroll
+        for (int i = 0; i < XP; ++i)
+            xv[i] = load16f(xr, (uint32_t)((pr * XP + i) * 64 + lane) * 16u);
+        __syncthreads();  // (1) X is requested before any weight tile; counters are zero
+        float mx = 0.0f;
+#pragma unroll
+        for (int i = 0; i < XP; ++i)
+            mx = fmaxf(mx, max_abs4(xv[i]));  // past K the loads read zeros
+        mx = wave_max_dpp(mx);
+        // non-negative floats order like their bit patterns: an unsigned maximum
+        if (lane == 0) {
+            __hip_atomic_fetch_max(&s_max, __float_as_uint(mx), __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+            __hip_atomic_fetch_add(&s_cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+        // Every producer adds 1 once, unconditionally, after its own X only, so the
+        // count reaches P; the bound is a guard, not a path taken.
+        for (int spin = 0; spin < (1 << 20) &&
+                           __hip_atomic_load(&s_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
+                               (unsigned)P;
+             ++spin)
+            __builtin_amdgcn_s_sleep(1);
+        mx = __uint_as_float(__hip_atomic_load(&s_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
+        const float a = mx / 127.0f;
+        const float r = 1.0f / a;
+        const bool fast = r <= 3.0e38f;  // finite reciprocal (a is not 0 or tiny)
+        // codes in the unpack order: in chunk c, word 2d holds the even-k codes of
+        // k = 32c + 8d .. + 7 and word 2d + 1 the odd-k ones
+        uint16_t* act16 = reinterpret_cast<uint16_t*>(s_act);
+#pragma unroll
+        for (int i = 0; i < XP; ++i) {
+            const int f = (pr * XP + i) * 64 + lane;  // k = 4f .. 4f + 3
+            if (f < K4) {
+                int q[4];
+                quant4_i8(xv[i], a, r, fast, q);
+                const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
+                const int wi = (c * 8 + 2 * d) * 2 + h;
+                act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
+                act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
+                if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0)
+                    *reinterpret_cast<uint32_t*>(p.dbg_xq + 4 * f) = pack_i8x4(q[0], q[1], q[2], q[3]);
+            }
+        }
+        // zero codes for the chunks past K (they also cancel the zero weight padding)
+        for (int w = (K >> 5) * 8 + pr * 64 + lane; w < CH * 8; w += 64 * P)
+            s_act[w] = 0u;
+        if (pr == 0 && lane == 0) {
+            s_a = a;
+            if (kDebug && p.dbg_a != nullptr && blockIdx.x == 0)
+                p.dbg_a[0] = a;
+        }
+        __syncthreads();  // (2) codes in LDS
+        return;
+    }
+
+    // ---- consumer: nq row groups from rg0
+    const int pw = nrg_blk / NW, pr_ = nrg_blk - pw * NW;
+    const int rg0 = rg_blk + rg_of(wave, pw, pr_);
+    const int nq = rg_of(wave + 1, pw, pr_) - rg_of(wave, pw, pr_);
+    const rsrc_t wres =
+        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
+    const rsrc_t sres =
+        make_rsrc(p.w_scale + (size_t)rg0 * 4, (uint32_t)max(0, min(nq * 4, N - rg0 * 4)) * 4u);
+    uint4 wa[RCG], wb[RCG];
+    float sa, sb;
+    // row group Q of the wave with its output scales; past the wave's run the loads read
+    // zeros (straight-line code: see the register variant)
+#define QW_PLOAD(WBUF, SC, Q)                                                                   \
+    {                                                                                           \
+        _Pragma("unroll") for (int u_ = 0; u_ < RCG; ++u_)                                     \
+            WBUF[u_] = load16_stream(wres, (Q) < nq ? wbase + (uint32_t)((Q) * CG + u_) * 1024u \
+                                                    : 0x80000000u);                             \
+        SC = __uint_as_float(load4(sres, (uint32_t)((Q) * 4 + sub) * 4u));                      \
+        __builtin_amdgcn_sched_barrier(0);                                                      \
+    }
+    __syncthreads();  // (1)
+    QW_PLOAD(wa, sa, 0);
+    __syncthreads();  // (2)
+    uint32_t act[RCG][8];
+#pragma unroll
+    for (int c = 0; c < RCG; ++c)
+        load_act(s_act + (size_t)(c * 16 + j) * 8, act[c]);
+    const float a = s_a;
+#define QW_PCOMPUTE(WBUF, SC, Q)                                                                \
+    {                                                                                           \
+        int acc_[4] = {0, 0, 0, 0};                                                             \
+        _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk(WBUF[c_], act[c_], acc_); \
+        const int v_ = row_sum16(acc_[0] + acc_[1] + acc_[2] + acc_[3]) >> 4;                   \
+        const int n_ = (rg0 + (Q)) * 4 + sub;                                                   \
+        if (j == 0 && n_ < N) {                                                                 \
+            if (kDebug && p.dbg_acc != nullptr)                                                 \
+                p.dbg_acc[n_] = v_;                                                             \
+            p.Y[n_] = ((float)v_ * SC) * a;                                                     \
+        }                                                                                       \
+    }
+    int q = 0;
+    for (; q + 1 < nq; q += 2) {
+        QW_PLOAD(wb, sb, q + 1);
+        QW_PCOMPUTE(wa, sa, q);
+        QW_PLOAD(wa, sa, q + 2);
+        QW_PCOMPUTE(wb, sb, q + 1);
+    }
+    if (q < nq)
+        QW_PCOMPUTE(wa, sa, q);
+#undef QW_PLOAD
+#undef QW_PCOMPUTE
+}
+
 // Eager variant: every tile of the wave (at most TMAX) is requested before the
 // prologue, so the whole matrix is in flight while the activations are quantized;
 // the codes are then read from LDS one tile ahead of the dots.
@@ -795,10 +948,53 @@ hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStre
     }
 }
 
+template <int RCG, int NW, int P>
+hipError_t launch_prod(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    if (debug) {
+        if constexpr (NW == 8 && P == 2)
+            hipLaunchKernelGGL((k_gemv_w4a8_prod<RCG, NW, P, true>), dim3(t.blocks),
+                               dim3(64 * (NW + P)), 0, st, a);
+        else
+            return hipErrorInvalidValue;
+    } else {
+        hipLaunchKernelGGL((k_gemv_w4a8_prod<RCG, NW, P, false>), dim3(t.blocks),
+                           dim3(64 * (NW + P)), 0, st, a);
+    }
+    return hipGetLastError();
+}
+
+template <int RCG>
+hipError_t launch_prod_w(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    if (t.nw == 8 && t.prod == 2) return launch_prod<RCG, 8, 2>(a, t, debug, st);
+    if (t.nw == 6 && t.prod == 2) return launch_prod<RCG, 6, 2>(a, t, debug, st);
+    if (t.nw == 5 && t.prod == 3) return launch_prod<RCG, 5, 3>(a, t, debug, st);
+    if (t.nw == 4 && t.prod == 4) return launch_prod<RCG, 4, 4>(a, t, debug, st);
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_prod_any(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch_prod_w<1>(a, t, debug, st);
+    case 2: return launch_prod_w<2>(a, t, debug, st);
+    case 3: return launch_prod_w<3>(a, t, debug, st);
+    case 4: return launch_prod_w<4>(a, t, debug, st);
+    case 5: return launch_prod_w<5>(a, t, debug, st);
+    case 6: return launch_prod_w<6>(a, t, debug, st);
+    case 7: return launch_prod_w<7>(a, t, debug, st);
+    case 8: return launch_prod_w<8>(a, t, debug, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
+    if (t.u == 5)
+        return launch_prod_any(a, t, debug, st);
     if (t.u == 2)
         return debug ? hipErrorInvalidValue : launch_flight_any(a, t, st);
     if (t.u == 3)

@@ -63,8 +63,12 @@ struct GemvTiling {
     int splitk;       // LDS variant: waves sharing each row group, each taking a k-slice
                       //   (1, 2 or 4; above 1 only with 4 or 8 waves and mt <= 2)
     int nwaves;       // row runs along N; they split the row groups evenly
+                      //   (producer variant: consumer waves of all workgroups)
     int blocks;       // workgroups along N = ceil(nwaves / (nw / splitk))
     int lds_bytes;    // dynamic LDS
+    int prod;         // > 0: producer variant (u == 5, M == 1) with `prod` producer
+                      //   waves and nw consumer waves per workgroup; the row groups
+                      //   are split over the workgroups (W4A8Args per / rem)
 };
 
 struct W4A8Args {
@@ -74,7 +78,8 @@ struct W4A8Args {
     float* Y;
     int M, N, K;
     int cg, nrg, nwaves;
-    int per, rem;      // row groups per row run: nrg = per * nwaves + rem (see rg_of)
+    int per, rem;      // row groups per row run: nrg = per * nwaves + rem (see rg_of);
+                       //   per workgroup in the producer variant: nrg = per * blocks + rem
     int32_t* dbg_acc;  // optional [M][N]
     int8_t* dbg_xq;    // optional [M][K]
     float* dbg_a;      // optional [M]

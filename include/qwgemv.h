@@ -161,7 +161,12 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
      u = 4, 8  activations read from LDS in batches of u tiles, two batches in flight;
             splitk = 2 or 4 splits each row run's tiles over that many waves of the
             workgroup (nw 4 or 8, at most 16 row groups per run), whose partial sums
-            are added in on-chip memory.
+            are added in on-chip memory;
+     u = 5  (INT4, M == 1, K <= 4096) producer waves: each workgroup has nw consumer
+            waves streaming weights and splitk producer waves quantizing X, with
+            (nw, splitk) = (8, 2), (6, 2), (5, 3) or (4, 4); nwaves = workgroups * nw,
+            and the row groups are split evenly over the workgroups, then over the
+            consumer waves.
    splitk must be 1 unless stated.  Results do not depend on the launch shape, except
    that W8A16 with splitk > 1 adds its fp32 partial sums in a different order.
    QW_ERR_TILING for an invalid shape. */

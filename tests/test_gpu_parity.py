@@ -407,6 +407,41 @@ def test_every_launch_shape_gives_the_same_result(M):
         assert np.array_equal(y.view(np.uint16), y_first.view(np.uint16)), (u, nw, nwaves)
 
 
+# (N, K): at least 2048 row groups (the default path runs the producer variant), ragged
+# N and K, one tile, one chunk, more workgroups than row groups
+PRODUCER_SHAPES = [(8200, 3584), (9000, 4096), (4100, 1056), (2500, 2080), (333, 512), (37, 32)]
+
+
+@pytest.mark.parametrize("N,K", PRODUCER_SHAPES)
+def test_producer_wave_variant(N, K):
+    """The producer-wave GEMV (u = 5) at every split of a workgroup into consumer and
+    producer waves and at 1..301 workgroups gives the oracle's outputs; where the default
+    path runs it (>= 2048 row groups), its debug outputs (int32 accumulators, activation
+    codes and scale) equal the oracle's bit for bit."""
+    say("producer variant N", N, "K", K)
+    W = wl.weights(61, 1, N, K, outlier_rows=True)
+    X = wl.activations(61, 2, 1, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    for (nw, P) in ((8, 2), (6, 2), (5, 3), (4, 4)):
+        for blocks in (1, 3, 64, 256, 301):
+            Y = qw.gemv_w4a8_tiled(Xd, Wq, s, 5, nw, blocks * nw, P)
+            y = host(Y)
+            assert_w4a8_close(y, ref["Y"])
+            assert np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32)), (nw, P, blocks)
+    if -(-N // 4) >= 2048:
+        out = qw.gemv_w4a8_debug(Xd, Wq, s)
+        assert np.array_equal(host(out["acc"]), ref["acc"])
+        assert np.array_equal(host(out["xq"]), ref["xq"])
+        assert np.array_equal(host(out["a"]).view(np.uint32), ref["a"].view(np.uint32))
+        assert np.array_equal(host(out["Y"]).view(np.uint32), ref["Y"].view(np.uint32))
+    with pytest.raises(qw.QWError):
+        qw.gemv_w4a8_tiled(Xd, Wq, s, 5, 8, 8, 3)  # not a supported split
+    with pytest.raises(qw.QWError):
+        qw.gemv_w4a8_tiled(Xd, Wq, s, 5, 8, 12, 2)  # not whole workgroups
+
+
 SPLITK_SHAPES = [(1, 512, 3584), (1, 100, 18944), (2, 37, 4640), (1, 4100, 1056), (2, 64, 32)]
 
 

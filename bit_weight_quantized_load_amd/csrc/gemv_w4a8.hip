@@ -359,8 +359,8 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 #undef QW_LOAD
 }
 
-// Producer-wave variant (M == 1, RCG tiles per row group, one workgroup per CU): P
-// producer waves quantize X while NW consumer waves stream weights.
+// Producer-wave variant (M == 1, one workgroup per CU): P producer waves quantize X
+// while NW consumer waves stream weights.
 //
 // Why: a CU accepts new vector loads only as fast as data comes back, so a wave that
 // has just requested weight tiles stalls on its next load instruction, and any barrier
@@ -375,16 +375,29 @@ __global__ __launch_bounds__(64 * NW) void k_gemv_w4a8(W4A8Args p)
 // at the second barrier, then stream the rest with two row groups in flight.
 //
 // Work split: row groups split evenly over the workgroups (p.per / p.rem count row
-// groups per workgroup, not per wave), then evenly over the consumer waves of each.
-// Codes, accumulators and outputs are those of the other variants bit for bit.
-template <int RCG, int NW, int P, bool kDebug>
+// groups per workgroup, not per wave).  The NW consumers form NW / S row runs of S
+// waves; each run takes an even share of the workgroup's row groups and each of its S
+// waves one k-slice of at most T tiles of them (ceil(cg / S) tiles, T >= that), whose
+// activation codes it holds in registers.  With S > 1 (long K) the int32 partial sums
+// of the slices are added in LDS after a last barrier.  Codes, accumulators and outputs
+// are those of the other variants bit for bit.
+constexpr int kProdMaxRgS = 16;  // row groups per workgroup when K is split (S > 1)
+
+template <int T, int NW, int P, int S, bool kDebug>
 __global__ __launch_bounds__(64 * (NW + P)) void k_gemv_w4a8_prod(W4A8Args p)
 {
-    constexpr int XP = (RCG * 128 + 64 * P - 1) / (64 * P);  // X float4 per producer lane
-    constexpr int CH = RCG * 16;                             // chunks of one row of codes
+    constexpr int XP = (S * T * 128 + 64 * P - 1) / (64 * P);  // X float4 per producer lane
+    constexpr int CH = S * T * 16;                             // chunks of codes in LDS
+    constexpr int NR = NW / S;                                 // row runs
+    // row groups a consumer requests before the codes barrier: two when K is split (its
+    // batches are short and the quantization of a long X takes longer)
+    constexpr int PRE = S > 1 ? 2 : 1;
+    static_assert(NR * S == NW, "consumer waves must form whole row runs");
     __shared__ uint32_t s_act[CH * 8];
     __shared__ float s_a;
     __shared__ unsigned s_max, s_cnt;
+    __shared__ int s_part[S > 1 ? kProdMaxRgS * 4 * S : 1];
+    __shared__ float s_sc[S > 1 ? kProdMaxRgS * 4 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -455,61 +468,97 @@ __global__ __launch_bounds__(64 * (NW + P)) void k_gemv_w4a8_prod(W4A8Args p)
                 p.dbg_a[0] = a;
         }
         __syncthreads();  // (2) codes in LDS
-        return;
-    }
-
-    // ---- consumer: nq row groups from rg0
-    const int pw = nrg_blk / NW, pr_ = nrg_blk - pw * NW;
-    const int rg0 = rg_blk + rg_of(wave, pw, pr_);
-    const int nq = rg_of(wave + 1, pw, pr_) - rg_of(wave, pw, pr_);
-    const rsrc_t wres =
-        make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
-    const uint32_t wbase = (uint32_t)((rg0 - rg_blk) * CG) * 1024u + (uint32_t)lane * 16u;
-    const rsrc_t sres =
-        make_rsrc(p.w_scale + (size_t)rg0 * 4, (uint32_t)max(0, min(nq * 4, N - rg0 * 4)) * 4u);
-    uint4 wa[RCG], wb[RCG];
-    float sa, sb;
-    // row group Q of the wave with its output scales; past the wave's run the loads read
-    // zeros (straight-line code: see the register variant)
+    } else {
+        // ---- consumer: run rw, k-slice ks (tiles [c_lo, c_lo + Tw)), nq row groups from rg0
+        const int rw = S > 1 ? wave / S : wave;
+        const int ks = S > 1 ? wave - rw * S : 0;
+        const int Ts = (CG + S - 1) / S;
+        const int c_lo = ks * Ts;
+        const int Tw = max(0, min(CG, c_lo + Ts) - c_lo);
+        const int pw = nrg_blk / NR, pr_ = nrg_blk - pw * NR;
+        const int rgi0 = rg_of(rw, pw, pr_);  // first row group of the run in the workgroup
+        const int rg0 = rg_blk + rgi0;
+        const int nq = rg_of(rw + 1, pw, pr_) - rgi0;
+        const rsrc_t wres =
+            make_rsrc(p.Wq + (size_t)rg_blk * CG * 1024u, (uint32_t)(nrg_blk * CG) * 1024u);
+        const uint32_t wbase = (uint32_t)(rgi0 * CG + c_lo) * 1024u + (uint32_t)lane * 16u;
+        const rsrc_t sres =
+            make_rsrc(p.w_scale + (size_t)rg0 * 4, (uint32_t)max(0, min(nq * 4, N - rg0 * 4)) * 4u);
+        uint4 wa[T], wb[T];
+        float sa, sb;
+        // row group Q of the run, this wave's slice, with its output scales; tiles past the
+        // slice or the run read zeros (straight-line code: see the register variant)
 #define QW_PLOAD(WBUF, SC, Q)                                                                   \
-    {                                                                                           \
-        _Pragma("unroll") for (int u_ = 0; u_ < RCG; ++u_)                                     \
-            WBUF[u_] = load16_stream(wres, (Q) < nq ? wbase + (uint32_t)((Q) * CG + u_) * 1024u \
-                                                    : 0x80000000u);                             \
-        SC = __uint_as_float(load4(sres, (uint32_t)((Q) * 4 + sub) * 4u));                      \
-        __builtin_amdgcn_sched_barrier(0);                                                      \
-    }
-    __syncthreads();  // (1)
-    QW_PLOAD(wa, sa, 0);
-    __syncthreads();  // (2)
-    uint32_t act[RCG][8];
+        {                                                                                       \
+            _Pragma("unroll") for (int u_ = 0; u_ < T; ++u_)                                   \
+                WBUF[u_] = load16_stream(wres, (Q) < nq && u_ < Tw                              \
+                                                   ? wbase + (uint32_t)((Q) * CG + u_) * 1024u \
+                                                   : 0x80000000u);                              \
+            SC = __uint_as_float(load4(sres, (uint32_t)((Q) * 4 + sub) * 4u));                  \
+            __builtin_amdgcn_sched_barrier(0);                                                  \
+        }
+        __syncthreads();  // (1)
+        QW_PLOAD(wa, sa, 0);
+        if constexpr (PRE == 2)
+            QW_PLOAD(wb, sb, 1);
+        __syncthreads();  // (2)
+        uint32_t act[T][8];
 #pragma unroll
-    for (int c = 0; c < RCG; ++c)
-        load_act(s_act + (size_t)(c * 16 + j) * 8, act[c]);
-    const float a = s_a;
+        for (int c = 0; c < T; ++c)
+            load_act(s_act + (size_t)((c_lo + c) * 16 + j) * 8, act[c]);
+        const float a = s_a;
+        // S == 1: the row is complete, write it; S > 1: leave the slice's partial sum
 #define QW_PCOMPUTE(WBUF, SC, Q)                                                                \
-    {                                                                                           \
-        int acc_[4] = {0, 0, 0, 0};                                                             \
-        _Pragma("unroll") for (int c_ = 0; c_ < RCG; ++c_) dot_chunk(WBUF[c_], act[c_], acc_); \
-        const int v_ = row_sum16(acc_[0] + acc_[1] + acc_[2] + acc_[3]) >> 4;                   \
-        const int n_ = (rg0 + (Q)) * 4 + sub;                                                   \
-        if (j == 0 && n_ < N) {                                                                 \
-            if (kDebug && p.dbg_acc != nullptr)                                                 \
-                p.dbg_acc[n_] = v_;                                                             \
-            p.Y[n_] = ((float)v_ * SC) * a;                                                     \
-        }                                                                                       \
-    }
-    int q = 0;
-    for (; q + 1 < nq; q += 2) {
-        QW_PLOAD(wb, sb, q + 1);
-        QW_PCOMPUTE(wa, sa, q);
-        QW_PLOAD(wa, sa, q + 2);
-        QW_PCOMPUTE(wb, sb, q + 1);
-    }
-    if (q < nq)
-        QW_PCOMPUTE(wa, sa, q);
+        {                                                                                       \
+            int acc_[4] = {0, 0, 0, 0};                                                         \
+            _Pragma("unroll") for (int c_ = 0; c_ < T; ++c_) dot_chunk(WBUF[c_], act[c_], acc_); \
+            const int v_ = row_sum16(acc_[0] + acc_[1] + acc_[2] + acc_[3]) >> 4;               \
+            if constexpr (S > 1) {                                                              \
+                if (j == 0) {                                                                   \
+                    s_part[((rgi0 + (Q)) * 4 + sub) * S + ks] = v_;                             \
+                    if (ks == 0)                                                                \
+                        s_sc[(rgi0 + (Q)) * 4 + sub] = SC;                                      \
+                }                                                                               \
+            } else {                                                                            \
+                const int n_ = (rg0 + (Q)) * 4 + sub;                                           \
+                if (j == 0 && n_ < N) {                                                         \
+                    if (kDebug && p.dbg_acc != nullptr)                                         \
+                        p.dbg_acc[n_] = v_;                                                     \
+                    p.Y[n_] = ((float)v_ * SC) * a;                                             \
+                }                                                                               \
+            }                                                                                   \
+        }
+        int q = 0;
+        for (; q + 1 < nq; q += 2) {
+            if constexpr (PRE == 1)
+                QW_PLOAD(wb, sb, q + 1);
+            QW_PCOMPUTE(wa, sa, q);
+            QW_PLOAD(wa, sa, q + 2);
+            QW_PCOMPUTE(wb, sb, q + 1);
+            if constexpr (PRE == 2)
+                QW_PLOAD(wb, sb, q + 3);
+        }
+        if (q < nq)
+            QW_PCOMPUTE(wa, sa, q);
 #undef QW_PLOAD
 #undef QW_PCOMPUTE
+    }
+    if constexpr (S > 1) {
+        // every wave of the workgroup, producers included, reaches this barrier once
+        __syncthreads();
+        const int rows = min(nrg_blk * 4, N - rg_blk * 4);
+        const float a = s_a;
+        for (int i = tid; i < rows; i += 64 * (NW + P)) {
+            int v = 0;
+#pragma unroll
+            for (int k = 0; k < S; ++k)
+                v += s_part[i * S + k];
+            const int n = rg_blk * 4 + i;
+            if (kDebug && p.dbg_acc != nullptr)
+                p.dbg_acc[n] = v;
+            p.Y[n] = ((float)v * s_sc[i]) * a;
+        }
+    }
 }
 
 // Eager variant: every tile of the wave (at most TMAX) is requested before the
@@ -948,34 +997,56 @@ hipError_t launch_nw(const W4A8Args& a, const GemvTiling& t, bool debug, hipStre
     }
 }
 
-template <int RCG, int NW, int P>
+template <int T, int NW, int P, int S>
 hipError_t launch_prod(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
     if (debug) {
-        if constexpr (NW == 8 && P == 2)
-            hipLaunchKernelGGL((k_gemv_w4a8_prod<RCG, NW, P, true>), dim3(t.blocks),
+        if constexpr ((NW == 8 && P == 2 && S == 1) || (NW == 8 && P == 8 && S > 1))
+            hipLaunchKernelGGL((k_gemv_w4a8_prod<T, NW, P, S, true>), dim3(t.blocks),
                                dim3(64 * (NW + P)), 0, st, a);
         else
             return hipErrorInvalidValue;
     } else {
-        hipLaunchKernelGGL((k_gemv_w4a8_prod<RCG, NW, P, false>), dim3(t.blocks),
+        hipLaunchKernelGGL((k_gemv_w4a8_prod<T, NW, P, S, false>), dim3(t.blocks),
                            dim3(64 * (NW + P)), 0, st, a);
     }
     return hipGetLastError();
 }
 
-template <int RCG>
+// K <= 4096: every row of codes in registers (T = tiles per row group)
+template <int T>
 hipError_t launch_prod_w(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    if (t.nw == 8 && t.prod == 2) return launch_prod<RCG, 8, 2>(a, t, debug, st);
-    if (t.nw == 6 && t.prod == 2) return launch_prod<RCG, 6, 2>(a, t, debug, st);
-    if (t.nw == 5 && t.prod == 3) return launch_prod<RCG, 5, 3>(a, t, debug, st);
-    if (t.nw == 4 && t.prod == 4) return launch_prod<RCG, 4, 4>(a, t, debug, st);
+    if (t.nw == 8 && t.prod == 2) return launch_prod<T, 8, 2, 1>(a, t, debug, st);
+    if (t.nw == 6 && t.prod == 2) return launch_prod<T, 6, 2, 1>(a, t, debug, st);
+    if (t.nw == 5 && t.prod == 3) return launch_prod<T, 5, 3, 1>(a, t, debug, st);
+    if (t.nw == 4 && t.prod == 4) return launch_prod<T, 4, 4, 1>(a, t, debug, st);
     return hipErrorInvalidValue;
+}
+
+// K split over S waves of 5..7 tiles each: 8 consumer and 8 producer waves (with 16 waves
+// per CU a wave has 128 registers; 8 tiles per slice would spill)
+template <int S>
+hipError_t launch_prod_s(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
+{
+    if (t.nw != 8 || t.prod != 8)
+        return hipErrorInvalidValue;
+    switch (t.reg_cg) {
+    case 5: return launch_prod<5, 8, 8, S>(a, t, debug, st);
+    case 6: return launch_prod<6, 8, 8, S>(a, t, debug, st);
+    case 7: return launch_prod<7, 8, 8, S>(a, t, debug, st);
+    default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_prod_any(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
+    switch (t.splitk) {
+    case 2: return launch_prod_s<2>(a, t, debug, st);
+    case 4: return launch_prod_s<4>(a, t, debug, st);
+    case 8: return launch_prod_s<8>(a, t, debug, st);
+    default: break;
+    }
     switch (t.reg_cg) {
     case 1: return launch_prod_w<1>(a, t, debug, st);
     case 2: return launch_prod_w<2>(a, t, debug, st);
@@ -993,7 +1064,7 @@ hipError_t launch_prod_any(const W4A8Args& a, const GemvTiling& t, bool debug, h
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
-    if (t.u == 5)
+    if (t.u == 5 || t.u == 6)
         return launch_prod_any(a, t, debug, st);
     if (t.u == 2)
         return debug ? hipErrorInvalidValue : launch_flight_any(a, t, st);

@@ -66,9 +66,11 @@ struct GemvTiling {
                       //   (producer variant: consumer waves of all workgroups)
     int blocks;       // workgroups along N = ceil(nwaves / (nw / splitk))
     int lds_bytes;    // dynamic LDS
-    int prod;         // > 0: producer variant (u == 5, M == 1) with `prod` producer
+    int prod;         // > 0: producer variant (u == 5 or 6, M == 1) with `prod` producer
                       //   waves and nw consumer waves per workgroup; the row groups
-                      //   are split over the workgroups (W4A8Args per / rem)
+                      //   are split over the workgroups (W4A8Args per / rem); splitk
+                      //   consumer waves share each row group's tiles, at most reg_cg
+                      //   tiles each
 };
 
 struct W4A8Args {

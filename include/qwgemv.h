@@ -166,7 +166,12 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
             waves streaming weights and splitk producer waves quantizing X, with
             (nw, splitk) = (8, 2), (6, 2), (5, 3) or (4, 4); nwaves = workgroups * nw,
             and the row groups are split evenly over the workgroups, then over the
-            consumer waves.
+            consumer waves;
+     u = 6  (INT4, M == 1) the producer-wave variant with K split: nw = 8 consumer and
+            8 producer waves per workgroup, each row group's tiles split over splitk =
+            2, 4 or 8 consumer waves (at most 7 tiles each, so K <= 3584 * splitk),
+            whose int32 partial sums are added in on-chip memory; at most 16 row groups
+            per workgroup (nwaves = workgroups * 8).
    splitk must be 1 unless stated.  Results do not depend on the launch shape, except
    that W8A16 with splitk > 1 adds its fp32 partial sums in a different order.
    QW_ERR_TILING for an invalid shape. */

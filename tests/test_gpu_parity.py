@@ -442,6 +442,45 @@ def test_producer_wave_variant(N, K):
         qw.gemv_w4a8_tiled(Xd, Wq, s, 5, 8, 12, 2)  # not whole workgroups
 
 
+# (N, K) with K > 4096: the down projection, a short-N one, ragged K with 10, 16, 33 and
+# 56 tiles per row (the largest K the split reaches, 7 tiles on each of 8 waves)
+PRODUCER_SPLIT_SHAPES = [(3584, 18944), (512, 18944), (1000, 4640), (333, 8192), (4100, 16416),
+                         (37, 28672)]
+
+
+@pytest.mark.parametrize("N,K", PRODUCER_SPLIT_SHAPES)
+def test_producer_wave_variant_split_k(N, K):
+    """The producer-wave GEMV with K split over 2, 4 or 8 consumer waves (u = 6), at every
+    valid split and several workgroup counts, gives the oracle's outputs bit for bit; the
+    default path at M = 1 with K > 4096 runs it, debug outputs included."""
+    say("producer variant split-K N", N, "K", K)
+    W = wl.weights(62, 1, N, K, outlier_rows=True)
+    X = wl.activations(62, 2, 1, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    nrg, cg = -(-N // 4), -(-K // 512)
+    tried = 0
+    for S in (2, 4, 8):
+        if -(-cg // S) > 7:
+            continue
+        for blocks in sorted({-(-nrg // 16), 64, 256, 301}):
+            if -(-nrg // blocks) > 16:
+                continue
+            y = host(qw.gemv_w4a8_tiled(Xd, Wq, s, 6, 8, blocks * 8, S))
+            assert np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32)), (S, blocks)
+            tried += 1
+    assert tried >= 2
+    out = qw.gemv_w4a8_debug(Xd, Wq, s)
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert np.array_equal(host(out["xq"]), ref["xq"])
+    assert np.array_equal(host(out["a"]).view(np.uint32), ref["a"].view(np.uint32))
+    y = host(qw.gemv_w4a8(Xd, Wq, s))
+    assert np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32))
+    with pytest.raises(qw.QWError):
+        qw.gemv_w4a8_tiled(Xd, Wq, s, 6, 8, 8 * 256, 3)  # not a supported split
+
+
 SPLITK_SHAPES = [(1, 512, 3584), (1, 100, 18944), (2, 37, 4640), (1, 4100, 1056), (2, 64, 32)]
 
 

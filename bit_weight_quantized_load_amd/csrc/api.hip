@@ -248,13 +248,22 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         per = per < 1 ? 1 : (per > 64 ? 64 : per);
         return (nrg + per - 1) / per;
     };
-    // INT4 with K <= 4096 from 2048 row groups: the producer variant, one workgroup of 8
+    // INT4 with K <= 4096: the producer variant.  From 2048 row groups one workgroup of 8
     // consumer and 2 producer waves per CU (3584 x 18944: 6.97 us against 8.11 us for the
-    // register variant in the same session; 3584 x 152064: 41.9 against 42.5 us)
-    if (bits == 4 && M == 1 && L.cg <= qw::kRegCG && nrg >= 2048) {
+    // register variant in the same session; 3584 x 152064: 41.9 against 42.5 us); below,
+    // 4 consumer and 4 producer waves on at most one workgroup per two row groups
+    // (3584 -> 3584: 3.28 against 4.32 us; 3584 -> 512: 3.02 against 4.16 us; 3584 -> 4608:
+    // 3.87 against 4.72 us)
+    if (bits == 4 && M == 1 && L.cg <= qw::kRegCG) {
         const int cus = device_cus();
-        if (tiling_ok(bits, M, 5, 8, cus * 8, 2, L))
-            return make_tiling(bits, M, N, K, 5, 8, cus * 8, 2);
+        if (nrg >= 2048) {
+            if (tiling_ok(bits, M, 5, 8, cus * 8, 2, L))
+                return make_tiling(bits, M, N, K, 5, 8, cus * 8, 2);
+        } else {
+            const int blocks = (int)std::min<int64_t>(cus, std::max<int64_t>(1, nrg / 2));
+            if (tiling_ok(bits, M, 5, 4, blocks * 4, 4, L))
+                return make_tiling(bits, M, N, K, 5, 4, blocks * 4, 4);
+        }
     }
     // INT4 with K > 4096: the producer variant with K split over 2, 4 or 8 consumer waves
     // where at most 16 row groups fall on a workgroup (18944 -> 3584: 7.9 us against 13.2 us
@@ -560,8 +569,9 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
     (void)ws_bytes;
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    // the debug outputs come from the register and LDS variants (every variant gives
-    // the same bits)
+    // the debug outputs come from the built-in variant where it has a debug build (the
+    // producer, register and LDS variants), else from the register or LDS variant (every
+    // variant gives the same bits)
     GemvTiling t = default_tiling(4, M, N, K);
     if (t.u == 2 || t.u == 3) {
         const qw::TileLayout L = qw::tile_layout(4, N, K);

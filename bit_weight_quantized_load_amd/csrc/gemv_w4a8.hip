@@ -1001,7 +1001,8 @@ template <int T, int NW, int P, int S>
 hipError_t launch_prod(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
     if (debug) {
-        if constexpr ((NW == 8 && P == 2 && S == 1) || (NW == 8 && P == 8 && S > 1))
+        if constexpr ((NW == 8 && P == 2 && S == 1) || (NW == 4 && P == 4 && S == 1) ||
+                      (NW == 8 && P == 8 && S > 1))
             hipLaunchKernelGGL((k_gemv_w4a8_prod<T, NW, P, S, true>), dim3(t.blocks),
                                dim3(64 * (NW + P)), 0, st, a);
         else

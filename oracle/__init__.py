@@ -13,6 +13,9 @@ and which passage of the pages it follows, is stated in ``qw_oracle.c``:
 * ``quant_act_i8`` -- dynamic per-vector INT8 activation quantization (same section).
 * ``gemv_w4a8`` -- int32 dot of the codes, output acc * w_scale * a_scale (sections
   正确方向 and 当前实现方式).
+* ``quant_w4g`` / ``gemv_w4a8g`` -- group-wise INT4 scales (one per output row and
+  group of g consecutive k), per-group int32 dots summed in fp32 (the same page,
+  section 后续优化方向, which lists group-wise scales as future work).
 * ``quant_w8`` / ``gemv_w8a16_ref64`` -- per-channel INT8 weights with an f16
   scale, dequantize-then-matmul in fp64 (ChatGLM2-6B W8A16 write-up, sections 2-4).
 * ``f16_from_f32`` / ``f32_from_f16`` -- IEEE binary16 conversions written from the
@@ -61,6 +64,8 @@ def _load():
             "qwo_unpack_w4": [P, I64, I64, P],
             "qwo_quant_act_i8": [P, I64, I64, P, P],
             "qwo_gemv_w4a8": [P, P, P, I64, I64, I64, P, P, P, P, ctypes.c_int],
+            "qwo_quant_w4g": [P, I64, I64, I64, P, P],
+            "qwo_gemv_w4a8g": [P, P, P, I64, I64, I64, I64, P, P, P, P, ctypes.c_int],
             "qwo_quant_w8": [P, I64, I64, P, P],
             "qwo_gemv_w8a16_ref64": [P, P, P, I64, I64, I64, P, ctypes.c_int],
             "qwo_f16_from_f32_n": [P, I64, P],
@@ -160,6 +165,49 @@ def gemv_w4a8(X, q, s, nthreads: int = 1):
     _check(_load().qwo_gemv_w4a8(_p(X), _p(q), _p(s), M, N, K, _p(Y), _p(acc), _p(xq), _p(a),
                                  int(nthreads)))
     return {"Y": Y, "acc": acc, "xq": xq, "a": a}
+
+
+def quant_w4g(W, g):
+    """W fp32 [N][K] -> (codes int8 [N][K] in -7..7, scales fp32 [N][K/g]), one scale per
+    output row and group of g consecutive k."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    q = np.empty((N, K), np.int8)
+    s = np.empty((N, K // g if g > 0 else 0), np.float32)
+    _check(_load().qwo_quant_w4g(_p(W), N, K, int(g), _p(q), _p(s)))
+    return q, s
+
+
+def gemv_w4a8g(X, q, s, g, nthreads=1):
+    """Group-wise W4A8 linear; returns dict Y fp32 [M][N], accg int32 [M][N][K/g] (the
+    per-group dots), xq int8 [M][K], a fp32 [M]."""
+    X = _c(X, np.float32)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    M, K = X.shape
+    N = q.shape[0]
+    G = K // g
+    assert q.shape == (N, K) and s.shape == (N, G)
+    Y = np.empty((M, N), np.float32)
+    accg = np.empty((M, N, G), np.int32)
+    xq = np.empty((M, K), np.int8)
+    a = np.empty((M,), np.float32)
+    _check(_load().qwo_gemv_w4a8g(_p(X), _p(q), _p(s), M, N, K, int(g), _p(Y), _p(accg), _p(xq),
+                                  _p(a), int(nthreads)))
+    return {"Y": Y, "accg": accg, "xq": xq, "a": a}
+
+
+def w4a8g_ref64(accg, s, a):
+    """fp64 value of the group-wise output from exact per-group dots: sum over groups of
+    acc * s, times a (each product is exact in fp64), and the fp32 error bound
+    (G + 2) * 2^-24 * sum |acc * s| * |a| that any summation order of the fp32 terms
+    meets.  Returns (y64 [M][N], bound [M][N])."""
+    t = accg.astype(np.float64) * s.astype(np.float64)[None, :, :]
+    a64 = a.astype(np.float64)[:, None]
+    G = accg.shape[2]
+    y64 = t.sum(axis=2) * a64
+    bound = (G + 2) * 2.0 ** -24 * np.abs(t).sum(axis=2) * np.abs(a64)
+    return y64, bound
 
 
 def quant_w8(W):

@@ -32,6 +32,10 @@
  *  - Canonical INT4 packing: byte j of a row = low nibble k=2j, high nibble k=2j+1.
  *  - The activation scale is per row m of X (per vector).
  *  - Epilogue order: ((float)acc * w_scale[n]) * a_scale[m].
+ *  - Group-wise INT4 (listed by [P1] 后续优化方向 as future work, with no formula):
+ *    one fp32 scale per output row and group of g consecutive k, the row-wise
+ *    rule inside each group; per-group int32 dots scaled and summed in fp32 in
+ *    group order, then multiplied by the activation scale.
  *  - W8A16: the fp32 scale is rounded to an f16 scale, and the codes are computed
  *    against that stored f16 scale.
  *
@@ -248,6 +252,75 @@ int qwo_gemv_w4a8(const float* X, const int8_t* q, const float* s, int64_t M, in
         if (acc)
             acc[m * N + n] = sum;
         Y[m * N + n] = ((float)sum * s[n]) * a[m];
+    }
+    return QWO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P1] 后续优化方向 (follow-up work) lists trying a group-wise scale.  Reading  */
+/* (the page gives no formula): one fp32 scale per output row n and per group */
+/* t of g consecutive k (K a multiple of g), the row-wise rule applied inside */
+/* each group:                                                                */
+/*   s[n][t] = maxabs(W[n][t*g .. t*g+g-1]) / 7                               */
+/*   q[n][k] = clamp(rint(W[n][k] / s[n][k / g]), -7, 7)                      */
+/* s is [N][K/g].  With g == K this is qwo_quant_w4.                          */
+/* ------------------------------------------------------------------------ */
+int qwo_quant_w4g(const float* W, int64_t N, int64_t K, int64_t g, int8_t* q, float* s)
+{
+    if (N < 0 || K < 0 || g <= 0 || K % g != 0)
+        return QWO_ERR_ARG;
+    const int64_t G = K / g;
+    for (int64_t n = 0; n < N; ++n) {
+        const float* row = W + n * K;
+        if (!all_finite(row, K))
+            return QWO_ERR_NONFINITE;
+        for (int64_t t = 0; t < G; ++t) {
+            float sc = maxabs_f32(row + t * g, g) / 7.0f;
+            s[n * G + t] = sc;
+            for (int64_t k = t * g; k < (t + 1) * g; ++k)
+                q[n * K + k] = quant_one(row[k], sc, 7);
+        }
+    }
+    return QWO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Group-wise W4A8 linear (the same reading): the activation quantization of  */
+/* [P1] 当前实现方式, an exact int32 dot per group,                            */
+/*   acc[m][n][t] = sum_{k in group t} q[n][k] * xq[m][k],                     */
+/* each scaled by its group scale and added in fp32, group by group:          */
+/*   y = 0;  for t = 0 .. G-1:  y = y + (float)acc[m][n][t] * s[n][t]         */
+/*   Y[m][n] = y * a[m]                                                        */
+/* With one group (g == K), 0 + x == x makes this qwo_gemv_w4a8 bit for bit.  */
+/* accg ([M][N][K/g]) may be NULL.  Each output element is summed in order on */
+/* one thread, so the result does not depend on the thread count.             */
+/* ------------------------------------------------------------------------ */
+int qwo_gemv_w4a8g(const float* X, const int8_t* q, const float* s, int64_t M, int64_t N,
+                   int64_t K, int64_t g, float* Y, int32_t* accg, int8_t* xq, float* a,
+                   int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || g <= 0 || K % g != 0)
+        return QWO_ERR_ARG;
+    int st = qwo_quant_act_i8(X, M, K, xq, a);
+    if (st != QWO_OK)
+        return st;
+    if (nthreads < 1)
+        nthreads = 1;
+    const int64_t G = K / g;
+    int64_t total = M * N;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        float y = 0.0f;
+        for (int64_t t = 0; t < G; ++t) {
+            int32_t sum = 0;
+            for (int64_t k = t * g; k < (t + 1) * g; ++k)
+                sum += (int32_t)q[n * K + k] * (int32_t)xq[m * K + k];
+            if (accg)
+                accg[(m * N + n) * G + t] = sum;
+            y = y + (float)sum * s[n * G + t];
+        }
+        Y[m * N + n] = y * a[m];
     }
     return QWO_OK;
 }

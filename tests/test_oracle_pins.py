@@ -234,6 +234,115 @@ def test_gemv_w4a8_symmetries_and_threads():
     assert np.array_equal(rt["Y"], r["Y"]) and np.array_equal(rt["acc"], r["acc"])
 
 
+# --------------------------------------------------- group-wise INT4 scales --
+
+def test_quant_w4g_closed_form_groups():
+    """Each group c * 2^-e_t with a +-7 present: its scale is exactly 2^-e_t and its codes
+    are c, whatever the other groups of the row hold."""
+    rng = np.random.default_rng(41)
+    N, g, G = 7, 64, 5
+    es = [0, 3, 9, 1, 12]
+    W = np.empty((N, g * G), np.float32)
+    C = np.empty((N, g * G), np.int8)
+    for t, e in enumerate(es):
+        Wt, ct = _pow2_rows(rng, N, g, 7, e)
+        W[:, t * g:(t + 1) * g] = Wt
+        C[:, t * g:(t + 1) * g] = ct
+    q, sc = oracle.quant_w4g(W, g)
+    assert sc.shape == (N, G)
+    assert np.all(sc == np.array([np.float32(2.0 ** -e) for e in es], np.float32)[None, :])
+    assert np.array_equal(q, C)
+
+
+def test_quant_w4g_one_group_is_row_wise_and_groups_are_rows():
+    """g = K is the row-wise quantization; and every group quantizes as a row of its own
+    (the matrix [N][K] seen as [N*K/g][g]): a misplaced group index fails one of them."""
+    W = workloads.weights(42, 1, 48, 512, outlier_rows=True)
+    q1, s1 = oracle.quant_w4g(W, 512)
+    qr, sr = oracle.quant_w4(W)
+    assert np.array_equal(q1, qr) and np.array_equal(s1[:, 0].view(np.uint32), sr.view(np.uint32))
+    for g in (32, 64, 128, 256):
+        qg, sg = oracle.quant_w4g(W, g)
+        qrows, srows = oracle.quant_w4(W.reshape(-1, g))
+        assert np.array_equal(qg.reshape(-1, g), qrows)
+        assert np.array_equal(sg.reshape(-1).view(np.uint32), srows.view(np.uint32))
+
+
+def test_quant_w4g_invariants_and_rejections():
+    W = workloads.weights(43, 1, 32, 384, outlier_rows=True)
+    W[3, 128:256] = 0.0  # one all-zero group
+    q, s = oracle.quant_w4g(W, 128)
+    assert s[3, 1] == 0 and not q[3, 128:256].any()
+    assert np.abs(q).max() <= 7
+    groups = np.abs(q.reshape(32, 3, 128)).max(axis=2)
+    assert np.all(groups[s > 0] == 7)
+    err = np.abs(W.astype(np.float64) - q * np.repeat(s, 128, axis=1).astype(np.float64))
+    assert np.all(err <= np.repeat(s, 128, axis=1) * (0.5 + 2.0 ** -20))
+    with pytest.raises(oracle.OracleError):
+        oracle.quant_w4g(W, 100)  # K not a multiple of g
+
+
+def test_gemv_w4a8g_brute_force_exact_identity_and_bound():
+    """Per-group dots by brute force; the group decomposition equals the dequantized dot
+    sum_k (q s_t(k))(xq a) exactly in rationals; Y lies within the fp32 summation bound
+    of that exact value."""
+    g, G, N, M = 8, 4, 5, 3
+    K = g * G
+    W = workloads.weights(44, 1, N, K)
+    X = workloads.activations(44, 2, M, K)
+    q, s = oracle.quant_w4g(W, g)
+    r = oracle.gemv_w4a8g(X, q, s, g)
+    xq, a = r["xq"], r["a"]
+    u = Fraction(1, 2 ** 24)
+    for m in range(M):
+        for n in range(N):
+            terms = []
+            for t in range(G):
+                acc = sum(int(q[n, k]) * int(xq[m, k]) for k in range(t * g, (t + 1) * g))
+                assert r["accg"][m, n, t] == acc
+                terms.append(Fraction(acc) * Fraction(float(s[n, t])))
+            exact = sum(terms) * Fraction(float(a[m]))
+            deq = sum(Fraction(int(q[n, k])) * Fraction(float(s[n, k // g])) * Fraction(int(xq[m, k]))
+                      for k in range(K)) * Fraction(float(a[m]))
+            assert exact == deq
+            bound = (G + 2) * u * sum(abs(x) for x in terms) * abs(Fraction(float(a[m])))
+            assert abs(Fraction(float(r["Y"][m, n])) - exact) <= bound
+
+
+def test_gemv_w4a8g_one_group_equals_row_wise_bit_for_bit():
+    W = workloads.weights(45, 1, 200, 256, outlier_rows=True)
+    X = workloads.activations(45, 2, 2, 256, outlier_channels=4)
+    q, s = oracle.quant_w4g(W, 256)
+    rg = oracle.gemv_w4a8g(X, q, s, 256)
+    rr = oracle.gemv_w4a8(X, q, s[:, 0])
+    assert np.array_equal(rg["Y"].view(np.uint32), rr["Y"].view(np.uint32))
+    assert np.array_equal(rg["accg"][:, :, 0], rr["acc"])
+
+
+def test_gemv_w4a8g_against_fp64_and_int64_matmuls():
+    """At a decode shape: the per-group dots equal an int64 matmul of the codes group by
+    group, and Y is within the summation bound of the fp64 value."""
+    W = workloads.weights(46, 1, 96, 3584, outlier_rows=True)
+    X = workloads.activations(46, 2, 1, 3584, outlier_channels=4)
+    q, s = oracle.quant_w4g(W, 128)
+    r = oracle.gemv_w4a8g(X, q, s, 128, nthreads=4)
+    acc64 = np.einsum("mtk,ntk->mnt", r["xq"].astype(np.int64).reshape(1, 28, 128),
+                      q.astype(np.int64).reshape(96, 28, 128))
+    assert np.array_equal(r["accg"], acc64)
+    y64, bound = oracle.w4a8g_ref64(r["accg"], s, r["a"])
+    deq = (r["xq"].astype(np.float64) * r["a"].astype(np.float64)[:, None]) @ \
+        (q.astype(np.float64) * np.repeat(s, 128, axis=1).astype(np.float64)).T
+    assert np.allclose(y64, deq, rtol=1e-12, atol=0)
+    assert np.all(np.abs(r["Y"] - y64) <= bound)
+    # finer groups track the unquantized product at least as well as row-wise scales
+    qr, sr = oracle.quant_w4(W)
+    yr = oracle.gemv_w4a8(X, qr, sr)["Y"]
+    ref = X.astype(np.float64) @ W.astype(np.float64).T
+    assert np.linalg.norm(r["Y"] - ref) <= np.linalg.norm(yr - ref)
+    rt = oracle.gemv_w4a8g(X, q, s, 128, nthreads=1)
+    assert np.array_equal(rt["Y"], r["Y"])
+
+
 # ------------------------------------------------------------ W8 weights --
 
 def test_quant_w8_closed_form_rows():

@@ -8,7 +8,8 @@ kernels; there is no fallback, and importing the compute functions without the
 built library raises.
 
 W4A8 follows "Jetson Orin AGX 上的 INT4 量化推理实践：从 9 tok/s 到 19.6 tok/s"
-(sections 正确方向 and 当前实现方式); W8A16 follows the ChatGLM2-6B W8A16 write-up
+(sections 正确方向 and 当前实现方式; the group-wise variant is the scale granularity its
+section 后续优化方向 lists as future work); W8A16 follows the ChatGLM2-6B W8A16 write-up
 (TPU-MLIR, sections 2-4).
 """
 from __future__ import annotations
@@ -50,6 +51,11 @@ SIGNATURES = {
     "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
     "qw_gemm_w4a8_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
     "qw_gemm_w8a16_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
+    "qw_w4g_scale_bytes": (_SZ, [_I64, _I64, _I64]),
+    "quantize_pack_w4g": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "qw_w4g_scales": (_I, [_P, _I64, _I64, _I64, _P, _P]),
+    "gemv_w4a8g": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "qw_gemv_w4a8g_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
 }
@@ -235,6 +241,60 @@ def gemv_w8a16(X16, Wq, w_scale16, workspace=None, out=None, stream=None):
     wp, wn = _ws_args(workspace)
     _call("gemv_w8a16", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y), wp, wn,
           _stream(stream))
+    return Y
+
+
+def w4g_scale_bytes(N: int, K: int, group: int) -> int:
+    return int(lib().qw_w4g_scale_bytes(N, K, group))
+
+
+def quantize_pack_w4g(W, group, stream=None):
+    """W fp32 [N][K] -> (Wq uint8 [w4_packed_bytes(N, K)], group scales fp32 in the device
+    layout [w4g_scale_bytes(N, K, group) / 4]), one scale per output row and group of
+    `group` consecutive k.  Load time; synchronises."""
+    torch = _torch()
+    N, K = W.shape
+    _need(W, torch.float32, (N, K), "W")
+    nb = w4g_scale_bytes(N, K, group)
+    if nb == 0:
+        raise QWError("quantize_pack_w4g", QW_ERR_SHAPE, lib())
+    Wq = torch.empty((w4_packed_bytes(N, K),), dtype=torch.uint8, device=W.device)
+    s = torch.empty((nb // 4,), dtype=torch.float32, device=W.device)
+    _call("quantize_pack_w4g", _ptr(W), N, K, group, _ptr(Wq), _ptr(s), _stream(stream))
+    return Wq, s
+
+
+def w4g_scales(w_scale, N, K, group, stream=None):
+    """Group scales in the device layout -> fp32 [N][K / group]."""
+    torch = _torch()
+    out = torch.empty((N, K // group), dtype=torch.float32, device=w_scale.device)
+    _call("qw_w4g_scales", _ptr(w_scale), N, K, group, _ptr(out), _stream(stream))
+    return out
+
+
+def gemv_w4a8g(X, Wq, w_scale, N, group, out=None, stream=None):
+    """Y fp32 [1][N] = group-wise W4A8 linear of X fp32 [1][K] (M == 1)."""
+    torch = _torch()
+    M, K = X.shape
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (w4g_scale_bytes(N, K, group) // 4,), "w_scale")
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    _call("gemv_w4a8g", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, group, _ptr(Y), None, 0,
+          _stream(stream))
+    return Y
+
+
+def gemv_w4a8g_tiled(X, Wq, w_scale, N, group, u, nw, nwaves, splitk, out=None, stream=None):
+    """gemv_w4a8g with an explicit launch shape (see include/qwgemv.h)."""
+    torch = _torch()
+    M, K = X.shape
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _call("qw_gemv_w4a8g_tiled", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, group, _ptr(Y),
+          u, nw, nwaves, splitk, _stream(stream))
     return Y
 
 

@@ -442,6 +442,88 @@ int run_gemm_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, i
                                             nbw, static_cast<hipStream_t>(stream)));
 }
 
+// ---- group-wise INT4 scales
+
+bool group_ok(int64_t K, int64_t group)
+{
+    return (group == 32 || group == 64 || group == 128 || group == 256 || group == 512) &&
+           K % group == 0;
+}
+
+// Launch shapes the group-wise kernels exist for: the producer variant with 8 + 2 or 4 + 4
+// waves (K <= 4096), or with the K split over 2, 4 or 8 waves of at most 6 tiles.
+bool tiling_ok_g(int64_t M, int u, int nw, int nwaves, int splitk, const qw::TileLayout& L)
+{
+    if (u == 5)
+        return ((nw == 8 && splitk == 2) || (nw == 4 && splitk == 4)) &&
+               tiling_ok(4, M, u, nw, nwaves, splitk, L);
+    if (u == 6)
+        return (L.cg + splitk - 1) / splitk <= 6 && tiling_ok(4, M, u, nw, nwaves, splitk, L);
+    return false;
+}
+
+// Built-in launch shape of the group-wise GEMV: the row-wise choice of the producer
+// variant; false when none fits.
+bool default_tiling_g(int64_t N, int64_t K, GemvTiling* t)
+{
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
+    const int cus = device_cus();
+    if (L.cg <= qw::kRegCG) {
+        const int64_t nrg = L.nrg;
+        const int nw = nrg >= 2048 ? 8 : 4, P = nrg >= 2048 ? 2 : 4;
+        const int blocks =
+            nrg >= 2048 ? cus : (int)std::min<int64_t>(cus, std::max<int64_t>(1, nrg / 2));
+        if (!tiling_ok_g(1, 5, nw, blocks * nw, P, L))
+            return false;
+        *t = make_tiling(4, 1, N, K, 5, nw, blocks * nw, P);
+        return true;
+    }
+    for (int S = 2; S <= 8; S *= 2)
+        if (tiling_ok_g(1, 6, 8, cus * 8, S, L)) {
+            *t = make_tiling(4, 1, N, K, 6, 8, cus * 8, S);
+            return true;
+        }
+    return false;
+}
+
+int run_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+              int64_t K, int64_t group, float* Y, const GemvTiling& t, void* stream)
+{
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
+    qw::W4A8Args a;
+    a.X = X;
+    a.Wq = static_cast<const uint8_t*>(Wq);
+    a.w_scale = w_scale;
+    a.Y = Y;
+    a.M = (int)M;
+    a.N = (int)N;
+    a.K = (int)K;
+    a.cg = L.cg;
+    a.nrg = L.nrg;
+    a.nwaves = t.nwaves;
+    a.per = L.nrg / t.blocks;  // row groups per workgroup
+    a.rem = L.nrg % t.blocks;
+    a.dbg_acc = nullptr;
+    a.dbg_xq = nullptr;
+    a.dbg_a = nullptr;
+    return hip_status(qw::launch_gemv_w4a8g(a, t, (int)group, static_cast<hipStream_t>(stream)));
+}
+
+int check_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                int64_t K, int64_t group, const float* Y)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    int st = check_gemv_shape(4, M, N, K);
+    if (st != QW_OK)
+        return st;
+    if (M != 1 || !group_ok(K, group))
+        return QW_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y))
+        return QW_ERR_ALIGN;
+    return QW_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -533,6 +615,82 @@ int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w
     if ((st = read_flag(flag, s, &host)) != QW_OK)
         return st;
     return host ? QW_ERR_NONFINITE : QW_OK;
+}
+
+size_t qw_w4g_scale_bytes(int64_t N, int64_t K, int64_t group)
+{
+    if (check_shape(1, N, K) != QW_OK || !group_ok(K, group))
+        return 0;
+    return qw::w4g_scale_floats(N, K, group) * sizeof(float);
+}
+
+int quantize_pack_w4g(const float* W, int64_t N, int64_t K, int64_t group, void* Wq,
+                      float* w_scale, void* stream)
+{
+    if (!W || !Wq || !w_scale)
+        return QW_ERR_NULL;
+    int st = check_shape(1, N, K);
+    if (st != QW_OK)
+        return st;
+    if (!group_ok(K, group))
+        return QW_ERR_SHAPE;
+    if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_scale))
+        return QW_ERR_ALIGN;
+    int* flag = nullptr;
+    if ((st = get_flag(&flag)) != QW_OK)
+        return st;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, s);
+    if (e == hipSuccess)
+        e = qw::launch_pack_w4g(W, (int)N, (int)K, (int)group, static_cast<uint8_t*>(Wq), w_scale,
+                                flag, s);
+    if (e != hipSuccess)
+        return hip_status(e);
+    int host = 0;
+    if ((st = read_flag(flag, s, &host)) != QW_OK)
+        return st;
+    return host ? QW_ERR_NONFINITE : QW_OK;
+}
+
+int qw_w4g_scales(const float* w_scale, int64_t N, int64_t K, int64_t group, float* out,
+                  void* stream)
+{
+    if (!w_scale || !out)
+        return QW_ERR_NULL;
+    int st = check_shape(1, N, K);
+    if (st != QW_OK)
+        return st;
+    if (!group_ok(K, group))
+        return QW_ERR_SHAPE;
+    return hip_status(qw::launch_w4g_scales(w_scale, (int)N, (int)K, (int)group, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+               int64_t K, int64_t group, float* Y, void* workspace, size_t ws_bytes, void* stream)
+{
+    (void)workspace;
+    (void)ws_bytes;
+    int st = check_w4a8g(X, Wq, w_scale, M, N, K, group, Y);
+    if (st != QW_OK)
+        return st;
+    GemvTiling t;
+    if (!default_tiling_g(N, K, &t))
+        return QW_ERR_SHAPE;
+    return run_w4a8g(X, Wq, w_scale, M, N, K, group, Y, t, stream);
+}
+
+int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, int64_t group, float* Y, int u, int nw, int nwaves,
+                        int splitk, void* stream)
+{
+    int st = check_w4a8g(X, Wq, w_scale, M, N, K, group, Y);
+    if (st != QW_OK)
+        return st;
+    if (!tiling_ok_g(M, u, nw, nwaves, splitk, qw::tile_layout(4, N, K)))
+        return QW_ERR_TILING;
+    return run_w4a8g(X, Wq, w_scale, M, N, K, group, Y, make_tiling(4, M, N, K, u, nw, nwaves, splitk),
+                     stream);
 }
 
 int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scale, void* stream)

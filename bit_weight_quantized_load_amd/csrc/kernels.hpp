@@ -40,6 +40,26 @@ inline size_t packed_bytes(int bits, int64_t N, int64_t K)
     return (size_t)t.nrg * (size_t)t.cg * 1024u;
 }
 
+// Group-wise INT4 scales (one fp32 scale per output row and group of g consecutive k,
+// g = 32, 64, 128, 256 or 512, K a multiple of g).  Device layout: for each row group, each
+// of its 4 rows, each of the 512 / g groups of a tile, the scales of that group in tile
+// order, padded to a multiple of 4 tiles (cgp = ceil(cg / 4) * 4): index
+//   ((((n / 4) * 4 + n % 4) * (512 / g) + (k % 512) / g) * cgp + k / 512
+// for the group holding k.  A GEMV lane (row n % 4, chunk group j) then reads the scales
+// of all its tiles as consecutive floats.  Padding entries are zero.
+__host__ __device__ __forceinline__ size_t w4g_scale_index(int n, int k, int g, int cg)
+{
+    const int cgp = (cg + 3) & ~3;
+    return ((((size_t)(n >> 2) * 4 + (n & 3)) * (size_t)(512 / g) + (size_t)((k & 511) / g)) *
+            (size_t)cgp) + (size_t)(k >> 9);
+}
+
+inline size_t w4g_scale_floats(int64_t N, int64_t K, int64_t g)
+{
+    const int64_t cg = (K + 511) / 512, cgp = (cg + 3) / 4 * 4, nrg = (N + 3) / 4;
+    return (size_t)(nrg * 4 * (512 / g) * cgp);
+}
+
 // First row group of row run g out of W when nrg = per * W + rem row groups are split
 // evenly (the first rem runs take one more); g = W gives nrg.  Multiply-add only: the
 // quotient and remainder come from the host, so no division runs on the device.
@@ -144,10 +164,16 @@ hipError_t launch_pack_w8(const float* W, int N, int K, uint8_t* Wq, uint16_t* s
                           hipStream_t st);
 hipError_t launch_quant_act(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st);
 hipError_t launch_codes_w4(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st);
+hipError_t launch_pack_w4g(const float* W, int N, int K, int g, uint8_t* Wq, float* s,
+                           int* flag, hipStream_t st);
+hipError_t launch_w4g_scales(const float* s, int N, int K, int g, float* out, hipStream_t st);
 hipError_t launch_codes_w8(const uint8_t* Wq, int N, int K, int8_t* codes, hipStream_t st);
 hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t st);
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st);
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st);
+// Group-wise W4A8 GEMV (M == 1, producer-wave tilings u == 5 or 6): w_scale holds the
+// group scales in the layout of w4g_scale_index; group = 32 .. 512.
+hipError_t launch_gemv_w4a8g(const W4A8Args& a, const GemvTiling& t, int group, hipStream_t st);
 
 }  // namespace qw

@@ -67,6 +67,64 @@ __global__ __launch_bounds__(kBlock) void k_pack_w4(const float* __restrict__ W,
     }
 }
 
+// Group-wise INT4 (the INT4 write-up, section 后续优化方向, lists group-wise scales as
+// future work): the row-wise rule applied to each group of g consecutive k (g = 32 ..
+// 512, K a multiple of g), one fp32 scale per output row and group.  One workgroup per
+// row; the g / 8 threads of a group (each holding 8 consecutive k, one word of nibbles)
+// take the group's maximum with cross-lane exchanges (a group never straddles a wave).
+// Scales go to the device layout of w4g_scale_index (kernels.hpp).  A row with a
+// non-finite weight raises the flag and keeps the zero scales the buffer was cleared to.
+__global__ __launch_bounds__(kBlock) void k_pack_w4g(const float* __restrict__ W, int N, int K,
+                                                     int g, uint8_t* __restrict__ Wq,
+                                                     float* __restrict__ scale, int* flag)
+{
+    const int K4 = K >> 2, K8 = K >> 3;
+    const int cg = (K + 511) >> 9;
+    const int tpg = g >> 3;  // threads per group
+    for (int n = blockIdx.x; n < N; n += gridDim.x) {
+        const float4* row = reinterpret_cast<const float4*>(W + (size_t)n * K);
+        int bad = 0;
+        for (int i = threadIdx.x; i < K4; i += kBlock)
+            bad |= !finite4(row[i]);
+        bad = __syncthreads_or(bad);
+        if (bad) {
+            if (threadIdx.x == 0)
+                atomicOr(flag, 1);
+            continue;
+        }
+        for (int u = threadIdx.x; u < K8; u += kBlock) {
+            const float4 a = row[2 * u], b = row[2 * u + 1];
+            float mx = fmaxf(max_abs4(a), max_abs4(b));
+            for (int off = 1; off < tpg; off <<= 1)
+                mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+            const float s = mx / 7.0f;
+            if ((u & (tpg - 1)) == 0)
+                scale[w4g_scale_index(n, 8 * u, g, cg)] = s;
+            const int q[8] = {quant_code(a.x, s, 7.f), quant_code(a.y, s, 7.f), quant_code(a.z, s, 7.f),
+                              quant_code(a.w, s, 7.f), quant_code(b.x, s, 7.f), quant_code(b.y, s, 7.f),
+                              quant_code(b.z, s, 7.f), quant_code(b.w, s, 7.f)};
+            uint32_t word = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                word |= (uint32_t)(q[i] & 0xf) << (4 * i);
+            *reinterpret_cast<uint32_t*>(Wq + tile_word_offset(n, u >> 2, u & 3, cg, 4)) = word;
+        }
+    }
+}
+
+// Device layout of group scales -> canonical [N][K / g].
+__global__ __launch_bounds__(kBlock) void k_w4g_scales(const float* __restrict__ scale, int N,
+                                                       int K, int g, float* __restrict__ out)
+{
+    const int G = K / g, cg = (K + 511) >> 9;
+    const size_t total = (size_t)N * G;
+    for (size_t i = blockIdx.x * (size_t)kBlock + threadIdx.x; i < total;
+         i += (size_t)gridDim.x * kBlock) {
+        const int n = (int)(i / G), t = (int)(i % G);
+        out[i] = scale[w4g_scale_index(n, t * g, g, cg)];
+    }
+}
+
 // Per-channel INT8: s32 = maxabs/127, rounded to the stored f16 scale, and codes
 // taken against that stored scale.
 __global__ __launch_bounds__(kBlock) void k_pack_w8(const float* __restrict__ W, int N, int K,
@@ -208,6 +266,26 @@ hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, i
         return e;
     hipLaunchKernelGGL(k_pack_w4, dim3(N < kMaxGrid ? N : kMaxGrid), dim3(kBlock), 0, st, W, N, K,
                        Wq, s, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w4g(const float* W, int N, int K, int g, uint8_t* Wq, float* s,
+                           int* flag, hipStream_t st)
+{
+    hipError_t e = clear_padding(4, N, K, Wq, st);
+    if (e == hipSuccess)
+        e = launch_fill_zero(reinterpret_cast<uint32_t*>(s), w4g_scale_floats(N, K, g), st);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_pack_w4g, dim3(N < kMaxGrid ? N : kMaxGrid), dim3(kBlock), 0, st, W, N, K,
+                       g, Wq, s, flag);
+    return hipGetLastError();
+}
+
+hipError_t launch_w4g_scales(const float* s, int N, int K, int g, float* out, hipStream_t st)
+{
+    const size_t total = (size_t)N * (size_t)(K / g);
+    hipLaunchKernelGGL(k_w4g_scales, dim3(grid_for(total)), dim3(kBlock), 0, st, s, N, K, g, out);
     return hipGetLastError();
 }
 

@@ -121,6 +121,37 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
 
+/* Group-wise INT4 scales ("Jetson Orin AGX 上的 INT4 量化推理实践", section 后续优化方向,
+   which lists a group-wise scale as future work; the formula is this library's reading:
+   the row-wise rule applied to each group).  One fp32 scale per output row n and group t
+   of `group` consecutive k, group = 32, 64, 128, 256 or 512 with K a multiple of it:
+     s[n][t] = maxabs(W[n][t*group .. t*group + group - 1]) / 7,
+     q[n][k] = clamp(rint(W[n][k] / s[n][k / group]), -7, 7).
+   Wq has the layout of quantize_pack_w4; w_scale has a device layout of
+   qw_w4g_scale_bytes(N, K, group) bytes (0 for an invalid shape or group): for each
+   group of 4 rows, each row, each group of a 512-k tile, the scales of that group in
+   tile order, zero padded to a multiple of 4 tiles.  qw_w4g_scales decodes it to
+   [N][K / group].  Non-finite weights: QW_ERR_NONFINITE (those rows keep zero scales).
+   Synchronises once on `stream`, like the other packers. */
+size_t qw_w4g_scale_bytes(int64_t N, int64_t K, int64_t group);
+int quantize_pack_w4g(const float* W, int64_t N, int64_t K, int64_t group, void* Wq,
+                      float* w_scale, void* stream);
+int qw_w4g_scales(const float* w_scale, int64_t N, int64_t K, int64_t group, float* out,
+                  void* stream);
+
+/* Group-wise W4A8 linear, M == 1 (decode; QW_ERR_SHAPE otherwise).  X fp32 [1][K], Wq
+   and w_scale from quantize_pack_w4g -> Y fp32 [1][N] with, for each output row,
+     acc_t = sum over k in group t of q[n][k] * xq[k]   (int32, exact),
+     Y[n]  = (sum over t of (float)acc_t * s[n][t]) * a_scale,
+   the activation codes xq and scale a_scale being exactly those of quant_act_i8, and
+   the sum over groups taken in fp32 (in an order of the kernel's choosing: the result
+   lies within (K/group + 2) * 2^-24 * sum_t |acc_t * s[n][t]| * |a_scale| of the exact
+   value).  K <= 4096, or K <= 24576 when the rows fit 16 groups of 4 rows per compute
+   unit; else QW_ERR_SHAPE.  No workspace (may be NULL). */
+int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+               int64_t K, int64_t group, float* Y, void* workspace, size_t ws_bytes,
+               void* stream);
+
 /* W8A16 linear (ChatGLM2-6B W8A16 write-up, section 4).  X f16 [M][K], Wq from
    quantize_pack_w8, w_scale_f16 [N] -> Y f16 [M][N] with
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
@@ -180,6 +211,14 @@ int qw_gemv_w4a8_tiled(const float* X, const void* Wq, const float* w_scale, int
                        void* stream);
 int qw_gemv_w8a16_tiled(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                         int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int u, int nw,
+                        int nwaves, int splitk, void* stream);
+
+/* gemv_w4a8g with an explicit launch shape of the producer-wave kernel: u = 5 with
+   (nw, splitk) = (8, 2) or (4, 4) consumer and producer waves (K <= 4096), or u = 6 with
+   K split over splitk = 2, 4 or 8 waves of at most 6 tiles (see qw_gemv_w4a8_tiled).
+   QW_ERR_TILING for an invalid shape. */
+int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, int64_t group, float* Y, int u, int nw,
                         int nwaves, int splitk, void* stream);
 
 /* The matrix-core kernels (the M >= 2 path of gemv_w4a8, M >= 3 of gemv_w8a16) at any

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 23
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -165,6 +165,44 @@ def test_packers_and_helpers_reject_bad_arguments():
     assert L.qw_workspace_clear(MIS, 256, NULL) == qw.QW_ERR_ALIGN
     assert L.qw_gemv_w4a8_debug(A, A2, A3, 1, 64, 64, A4, MIS, NULL, NULL, NULL, 0, NULL) \
         == qw.QW_ERR_ALIGN
+
+
+def test_group_wise_sizes_and_argument_checks():
+    # scale layout: per row group, 4 rows x (512 / g) groups x tiles padded to 4
+    assert L.qw_w4g_scale_bytes(18944, 3584, 128) == 4736 * 4 * 4 * 8 * 4
+    assert L.qw_w4g_scale_bytes(3584, 18944, 128) == 896 * 4 * 4 * 40 * 4
+    assert L.qw_w4g_scale_bytes(5, 1056, 32) == 2 * 4 * 16 * 4 * 4
+    assert L.qw_w4g_scale_bytes(64, 512, 512) == 16 * 4 * 1 * 4 * 4
+    for g in (0, 16, 48, 100, 1024):
+        assert L.qw_w4g_scale_bytes(64, 3072, g) == 0, g
+    assert L.qw_w4g_scale_bytes(64, 3200, 256) == 0      # K not a multiple of g
+    # packer
+    assert L.quantize_pack_w4g(NULL, 4, 256, 64, A, A2, NULL) == qw.QW_ERR_NULL
+    assert L.quantize_pack_w4g(A, 4, 256, 96, A2, A3, NULL) == qw.QW_ERR_SHAPE
+    assert L.quantize_pack_w4g(A, 4, 3200, 512, A2, A3, NULL) == qw.QW_ERR_SHAPE
+    assert L.quantize_pack_w4g(A, 4, 256, 64, A2, MIS, NULL) == qw.QW_ERR_ALIGN
+    assert L.qw_w4g_scales(A, 4, 256, 33, A2, NULL) == qw.QW_ERR_SHAPE
+    # GEMV: M == 1 only, a supported group dividing K, K within the producer-wave shapes
+    f = L.gemv_w4a8g
+    assert f(NULL, A2, A3, 1, 64, 512, 128, A4, NULL, 0, NULL) == qw.QW_ERR_NULL
+    assert f(A, A2, A3, 2, 64, 512, 128, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE
+    assert f(A, A2, A3, 1, 64, 512, 48, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE
+    assert f(A, A2, A3, 1, 64, 3200, 256, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE
+    assert f(A, A2, A3, 1, 64, 32768, 128, A4, NULL, 0, NULL) == qw.QW_ERR_SHAPE  # > 24576
+    assert f(A, A2, MIS, 1, 64, 512, 128, A4, NULL, 0, NULL) == qw.QW_ERR_ALIGN
+    t = L.qw_gemv_w4a8g_tiled
+    # only the producer-wave shapes: u 5 with (8, 2) or (4, 4), u 6 with <= 6 tiles a wave
+    for (K, u, nw, nwaves, sk) in [(512, 0, 4, 16, 1), (512, 5, 6, 12, 2), (512, 5, 8, 12, 2),
+                                   (3584, 6, 8, 256, 3), (18944, 6, 8, 2048, 4),
+                                   (28672, 6, 8, 2048, 8)]:
+        assert t(A, A2, A3, 1, 64, K, 128, A4, u, nw, nwaves, sk, NULL) == qw.QW_ERR_TILING, \
+            (K, u, nw, nwaves, sk)
+    # the row-wise tiled entry rejects producer-wave shapes that do not exist
+    w4 = L.qw_gemv_w4a8_tiled
+    assert w4(A, A2, A3, 1, 64, 512, A4, 5, 8, 8, 3, NULL) == qw.QW_ERR_TILING
+    assert w4(A, A2, A3, 2, 64, 512, A4, 5, 8, 8, 2, NULL) == qw.QW_ERR_TILING
+    assert w4(A, A2, A3, 1, 64, 32768, A4, 6, 8, 2048, 8, NULL) == qw.QW_ERR_TILING
+    assert L.qw_gemv_w8a16_tiled(A, A2, A3, 1, 64, 512, A4, 5, 8, 8, 2, NULL) == qw.QW_ERR_TILING
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

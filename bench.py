@@ -9,7 +9,8 @@ enough distinct copies (rotated step by step) that every step reads them from HB
 not from the 256 MB last-level cache.
 
 Printed: ONE JSON line with `value` = algorithmic bytes of both GEMVs / time per
-step (GB/s), per-kernel microseconds and GB/s, the roofline of the dominant kernel
+step (GB/s), per-kernel microseconds and GB/s (also of the group-wise INT4 variant on
+the same shape, outside the step), the roofline of the dominant kernel
 (per-launch algorithmic bytes / average launch time from HIP events), the CPU
 oracle timed on this host on the same inputs, and the linear-layer time per token
 of the 28-layer decode-step chain in one HIP graph (unfused and with q|k|v and
@@ -39,6 +40,12 @@ ROTATE_BYTES = 1.5e9  # > 256 MB last-level cache, several times over
 def bytes_w4a8(M, N, K):
     """Algorithmic bytes: 0.5 B per INT4 weight, 4 B per scale, X element and Y element."""
     return N * K // 2 + 4 * N + 4 * M * K + 4 * M * N
+
+
+def bytes_w4a8g(M, N, K, g):
+    """Algorithmic bytes of the group-wise variant: 0.5 B per INT4 weight, 4 B per group
+    scale (N * K / g of them), 4 B per X and Y element."""
+    return N * K // 2 + 4 * N * (K // g) + 4 * M * K + 4 * M * N
 
 
 def bytes_w8a16(M, N, K):
@@ -268,6 +275,8 @@ def main():
     Wd = torch.from_numpy(W).cuda()
     Wq4, s4 = qw.quantize_pack_w4(Wd)
     Wq8, s8 = qw.quantize_pack_w8(Wd)
+    GROUP = 128
+    Wq4g, s4g = qw.quantize_pack_w4g(Wd, GROUP)
     del Wd
     R = max(2, math.ceil(ROTATE_BYTES / (Wq4.numel() + Wq8.numel())))
     copies = [(Wq4, s4, Wq8, s8)] + [(Wq4.clone(), s4.clone(), Wq8.clone(), s8.clone())
@@ -279,9 +288,16 @@ def main():
     ws4 = qw.make_workspace("w4a8", M, N, K)
     ws8 = qw.make_workspace("w8a16", M, N, K)
 
+    Rg = max(2, math.ceil(ROTATE_BYTES / (Wq4g.numel() + 4 * s4g.numel())))
+    copies_g = [(Wq4g, s4g)] + [(Wq4g.clone(), s4g.clone()) for _ in range(Rg - 1)]
+
     def w4(i):
         w4q, sc4, _, _ = copies[i % R]
         qw.gemv_w4a8(Xd, w4q, sc4, workspace=ws4, out=Y4)
+
+    def w4g(i):
+        wq, sc = copies_g[i % Rg]
+        qw.gemv_w4a8g(Xd, wq, sc, N, GROUP, out=Y4)
 
     def w8(i):
         _, _, w8q, sc8 = copies[i % R]
@@ -309,7 +325,7 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    g_step, g4, g8 = capture(step), capture(w4), capture(w8)
+    g_step, g4, g8, g4g = capture(step), capture(w4), capture(w8), capture(w4g)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g_step.replay()
@@ -327,6 +343,8 @@ def main():
 
     t4 = event_time_us(g4)
     t8 = event_time_us(g8)
+    t4g = event_time_us(g4g)
+    b4g = bytes_w4a8g(M, N, K, GROUP)
     ms_per_step = wall * 1e3 / K_steps
     value = b_step / (ms_per_step * 1e-3) / 1e9
 
@@ -335,6 +353,11 @@ def main():
                       "frac_of_peak": round(b4 / t4 / 1e3 / PEAK_HBM_GBS, 4)},
         "gemv_w8a16": {"us": round(t8, 3), "algo_bytes": b8, "GB/s": round(b8 / t8 / 1e3, 1),
                        "frac_of_peak": round(b8 / t8 / 1e3 / PEAK_HBM_GBS, 4)},
+        # the group-wise INT4 variant (one scale per row and 128 k) on the same shape:
+        # context, not part of the step
+        "gemv_w4a8g_g128": {"us": round(t4g, 3), "algo_bytes": b4g,
+                            "GB/s": round(b4g / t4g / 1e3, 1),
+                            "frac_of_peak": round(b4g / t4g / 1e3 / PEAK_HBM_GBS, 4)},
     }
     dom = "gemv_w8a16" if t8 >= t4 else "gemv_w4a8"
     ach = kernels[dom]["GB/s"]
@@ -342,7 +365,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom}
 
-    del g_step, g4, g8, copies
+    del g_step, g4, g8, g4g, copies, copies_g
     torch.cuda.empty_cache()
     chain_info = None
     if not args.no_chain:

@@ -18,6 +18,10 @@ and which passage of the pages it follows, is stated in ``qw_oracle.c``:
   section 后续优化方向, which lists group-wise scales as future work).
 * ``quant_w8`` / ``gemv_w8a16_ref64`` -- per-channel INT8 weights with an f16
   scale, dequantize-then-matmul in fp64 (ChatGLM2-6B W8A16 write-up, sections 2-4).
+* ``gemv_f16_ref64`` / ``gemv_w4f32`` -- the two ablations the INT4 page times beside
+  W4A8 (section 速度结果): an FP16 GEMV (fp64 reference) and weight-only INT4 with
+  float activations, unpacked to float and multiplied-added in fp32 (sections 最初的问题
+  and 问题原因).
 * ``f16_from_f32`` / ``f32_from_f16`` -- IEEE binary16 conversions written from the
   format's definition.
 
@@ -66,6 +70,8 @@ def _load():
             "qwo_gemv_w4a8": [P, P, P, I64, I64, I64, P, P, P, P, ctypes.c_int],
             "qwo_quant_w4g": [P, I64, I64, I64, P, P],
             "qwo_gemv_w4a8g": [P, P, P, I64, I64, I64, I64, P, P, P, P, ctypes.c_int],
+            "qwo_gemv_f16_ref64": [P, P, I64, I64, I64, P, ctypes.c_int],
+            "qwo_gemv_w4f32": [P, P, P, I64, I64, I64, P, P, ctypes.c_int],
             "qwo_quant_w8": [P, I64, I64, P, P],
             "qwo_gemv_w8a16_ref64": [P, P, P, I64, I64, I64, P, ctypes.c_int],
             "qwo_f16_from_f32_n": [P, I64, P],
@@ -208,6 +214,38 @@ def w4a8g_ref64(accg, s, a):
     y64 = t.sum(axis=2) * a64
     bound = (G + 2) * 2.0 ** -24 * np.abs(t).sum(axis=2) * np.abs(a64)
     return y64, bound
+
+
+def gemv_f16_ref64(X16, W16, nthreads=1):
+    """fp64 value of the FP16 GEMV: X16 f16 [M][K], W16 f16 [N][K] -> float64 [M][N]."""
+    X16 = _c(X16, np.float16).view(np.uint16)
+    W16 = _c(W16, np.float16).view(np.uint16)
+    M, K = X16.shape
+    N = W16.shape[0]
+    Y64 = np.empty((M, N), np.float64)
+    _check(_load().qwo_gemv_f16_ref64(_p(X16), _p(W16), M, N, K, _p(Y64), int(nthreads)))
+    return Y64
+
+
+def gemv_w4f32(X, q, s, nthreads=1):
+    """Weight-only INT4, float activations: (Y fp32 [M][N], Y64 float64 [M][N])."""
+    X = _c(X, np.float32)
+    q = _c(q, np.int8)
+    s = _c(s, np.float32)
+    M, K = X.shape
+    N = q.shape[0]
+    Y = np.empty((M, N), np.float32)
+    Y64 = np.empty((M, N), np.float64)
+    _check(_load().qwo_gemv_w4f32(_p(X), _p(q), _p(s), M, N, K, _p(Y), _p(Y64), int(nthreads)))
+    return Y, Y64
+
+
+def w4f32_bound(X, q, s):
+    """Per-element bound (K + 2) * 2^-24 * s[n] * sum_k |q x| on |Y - Y64| for any order of
+    the K fp32 multiply-adds (and the final scale multiply)."""
+    K = X.shape[1]
+    t = np.abs(X.astype(np.float64)) @ np.abs(q.astype(np.float64)).T
+    return (K + 2) * 2.0 ** -24 * t * s.astype(np.float64)[None, :]
 
 
 def quant_w8(W):

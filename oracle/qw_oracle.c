@@ -381,6 +381,63 @@ int qwo_gemv_w8a16_ref64(const uint16_t* X16, const int8_t* q, const uint16_t* s
     return QWO_OK;
 }
 
+/* ------------------------------------------------------------------------ */
+/* [P1] 速度结果 (speed results) times an FP16 baseline and a weight-only INT4  */
+/* path beside W4A8.  The two ablations, as this library reads them:           */
+/*                                                                            */
+/* FP16 GEMV: weights and activations in f16, no quantization, as an fp64      */
+/*   value: Y64[m][n] = sum_k (double)w16[n][k] * (double)x16[m][k].            */
+/* ------------------------------------------------------------------------ */
+int qwo_gemv_f16_ref64(const uint16_t* X16, const uint16_t* W16, int64_t M, int64_t N,
+                       int64_t K, double* Y64, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return QWO_ERR_ARG;
+    if (nthreads < 1)
+        nthreads = 1;
+    int64_t total = M * N;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        double sum = 0.0;
+        for (int64_t k = 0; k < K; ++k)
+            sum += (double)qwo_f32_from_f16(W16[n * K + k]) * (double)qwo_f32_from_f16(X16[m * K + k]);
+        Y64[m * N + n] = sum;
+    }
+    return QWO_OK;
+}
+
+/* Weight-only INT4 with float activations ([P1] 最初的问题 and 问题原因: the INT4   */
+/* weight is unpacked in the kernel, sign-extended, converted to float and used  */
+/* in a float FMA; the activation stays float).  Row-wise INT4 codes and scales  */
+/* as qwo_quant_w4; the row scale multiplies the finished sum (it factors out):  */
+/*   y = 0;  for k: y = fmaf((float)q[n][k], x[m][k], y);   Y[m][n] = y * s[n]  */
+/* and Y64[m][n] = sum_k ((double)q[n][k] * s[n]) * x[m][k] in fp64.  Y64 may be  */
+/* NULL.                                                                         */
+int qwo_gemv_w4f32(const float* X, const int8_t* q, const float* s, int64_t M, int64_t N,
+                   int64_t K, float* Y, double* Y64, int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0)
+        return QWO_ERR_ARG;
+    if (nthreads < 1)
+        nthreads = 1;
+    int64_t total = M * N;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t i = 0; i < total; ++i) {
+        int64_t m = i / N, n = i % N;
+        float y = 0.0f;
+        double y64 = 0.0;
+        for (int64_t k = 0; k < K; ++k) {
+            y = fmaf((float)q[n * K + k], X[m * K + k], y);
+            y64 += ((double)q[n * K + k] * (double)s[n]) * (double)X[m * K + k];
+        }
+        Y[m * N + n] = y * s[n];
+        if (Y64)
+            Y64[m * N + n] = y64;
+    }
+    return QWO_OK;
+}
+
 int qwo_num_threads(void)
 {
 #ifdef _OPENMP

@@ -343,6 +343,51 @@ def test_gemv_w4a8g_against_fp64_and_int64_matmuls():
     assert np.array_equal(rt["Y"], r["Y"])
 
 
+# ------------------------------------------------- the page's two ablations --
+
+def test_gemv_f16_ref64_brute_force_and_one_hot():
+    rng = np.random.default_rng(51)
+    X16 = rng.standard_normal((2, 24)).astype(np.float16)
+    W16 = (rng.standard_normal((5, 24)) * 0.02).astype(np.float16)
+    y = oracle.gemv_f16_ref64(X16, W16)
+    for m in range(2):
+        for n in range(5):
+            exact = sum(Fraction(float(W16[n, k])) * Fraction(float(X16[m, k])) for k in range(24))
+            assert abs(Fraction(y[m, n]) - exact) <= abs(exact) * Fraction(1, 2 ** 48) + Fraction(1, 2 ** 80)
+    e = np.zeros((1, 24), np.float16)
+    e[0, 7] = 1.0
+    assert np.array_equal(oracle.gemv_f16_ref64(e, W16)[0], W16[:, 7].astype(np.float64))
+
+
+def test_gemv_w4f32_brute_force_and_bound():
+    W = workloads.weights(52, 1, 6, 40)
+    X = workloads.activations(52, 2, 3, 40)
+    q, s = oracle.quant_w4(W)
+    Y, Y64 = oracle.gemv_w4f32(X, q, s)
+    bound = oracle.w4f32_bound(X, q, s)
+    for m in range(3):
+        for n in range(6):
+            exact = sum(Fraction(int(q[n, k])) * Fraction(float(s[n])) * Fraction(float(X[m, k]))
+                        for k in range(40))
+            assert abs(Fraction(float(Y64[m, n])) - exact) <= abs(exact) * Fraction(1, 2 ** 45) + Fraction(1, 2 ** 100)
+            assert abs(Fraction(float(Y[m, n])) - exact) <= Fraction(float(bound[m, n]))
+
+
+def test_gemv_w4f32_equals_w4a8_on_integer_activations():
+    """Activations that are integers in [-127, 127] with a 127 present quantize to
+    themselves with scale 1; every partial sum is then an exact fp32 integer, so the
+    float-unpack path and the integer path give the same bits."""
+    W = workloads.weights(53, 1, 64, 512, outlier_rows=True)
+    q, s = oracle.quant_w4(W)
+    rng = np.random.default_rng(53)
+    X = rng.integers(-127, 128, size=(2, 512)).astype(np.float32)
+    X[:, 3] = 127.0
+    Yf, _ = oracle.gemv_w4f32(X, q, s)
+    r = oracle.gemv_w4a8(X, q, s)
+    assert np.all(r["a"] == 1.0) and np.array_equal(r["xq"], X.astype(np.int8))
+    assert np.array_equal(Yf.view(np.uint32), r["Y"].view(np.uint32))
+
+
 # ------------------------------------------------------------ W8 weights --
 
 def test_quant_w8_closed_form_rows():

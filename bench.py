@@ -9,8 +9,9 @@ enough distinct copies (rotated step by step) that every step reads them from HB
 not from the 256 MB last-level cache.
 
 Printed: ONE JSON line with `value` = algorithmic bytes of both GEMVs / time per
-step (GB/s), per-kernel microseconds and GB/s (also of the group-wise INT4 variant on
-the same shape, outside the step), the roofline of the dominant kernel
+step (GB/s), per-kernel microseconds and GB/s (also, outside the step, of the group-wise
+INT4 variant and of the INT4 page's two ablations -- an FP16 GEMV and weight-only INT4
+unpacked to float -- on the same shape), the roofline of the dominant kernel
 (per-launch algorithmic bytes / average launch time from HIP events), the CPU
 oracle timed on this host on the same inputs, and the linear-layer time per token
 of the 28-layer decode-step chain in one HIP graph (unfused and with q|k|v and
@@ -290,6 +291,11 @@ def main():
 
     Rg = max(2, math.ceil(ROTATE_BYTES / (Wq4g.numel() + 4 * s4g.numel())))
     copies_g = [(Wq4g, s4g)] + [(Wq4g.clone(), s4g.clone()) for _ in range(Rg - 1)]
+    # the INT4 page's ablations on the same shape: FP16 weights, and INT4 weights unpacked
+    # to float against fp32 activations (the W4A8 packed copies)
+    W16 = torch.from_numpy(W.astype(np.float16)).cuda()
+    R16 = max(2, math.ceil(ROTATE_BYTES / (2 * W16.numel())))
+    copies16 = [W16] + [W16.clone() for _ in range(R16 - 1)]
 
     def w4(i):
         w4q, sc4, _, _ = copies[i % R]
@@ -298,6 +304,13 @@ def main():
     def w4g(i):
         wq, sc = copies_g[i % Rg]
         qw.gemv_w4a8g(Xd, wq, sc, N, GROUP, out=Y4)
+
+    def f16(i):
+        qw.gemv_f16(X16d, copies16[i % R16], out=Y8)
+
+    def w4f(i):
+        w4q, sc4, _, _ = copies[i % R]
+        qw.gemv_w4f32(Xd, w4q, sc4, out=Y4)
 
     def w8(i):
         _, _, w8q, sc8 = copies[i % R]
@@ -326,6 +339,7 @@ def main():
         return g
 
     g_step, g4, g8, g4g = capture(step), capture(w4), capture(w8), capture(w4g)
+    g16, g4f = capture(f16), capture(w4f)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g_step.replay()
@@ -345,6 +359,9 @@ def main():
     t8 = event_time_us(g8)
     t4g = event_time_us(g4g)
     b4g = bytes_w4a8g(M, N, K, GROUP)
+    t16 = event_time_us(g16)
+    t4f = event_time_us(g4f)
+    b16 = 2 * N * K + 2 * M * K + 2 * M * N
     ms_per_step = wall * 1e3 / K_steps
     value = b_step / (ms_per_step * 1e-3) / 1e9
 
@@ -358,6 +375,13 @@ def main():
         "gemv_w4a8g_g128": {"us": round(t4g, 3), "algo_bytes": b4g,
                             "GB/s": round(b4g / t4g / 1e3, 1),
                             "frac_of_peak": round(b4g / t4g / 1e3 / PEAK_HBM_GBS, 4)},
+        # the page's ablations (context): FP16 GEMV, and weight-only INT4 unpacked to float
+        "ablation_fp16_gemv": {"us": round(t16, 3), "algo_bytes": b16,
+                               "GB/s": round(b16 / t16 / 1e3, 1),
+                               "frac_of_peak": round(b16 / t16 / 1e3 / PEAK_HBM_GBS, 4)},
+        "ablation_w4_float_unpack": {"us": round(t4f, 3), "algo_bytes": b4,
+                                     "GB/s": round(b4 / t4f / 1e3, 1),
+                                     "frac_of_peak": round(b4 / t4f / 1e3 / PEAK_HBM_GBS, 4)},
     }
     dom = "gemv_w8a16" if t8 >= t4 else "gemv_w4a8"
     ach = kernels[dom]["GB/s"]
@@ -365,7 +389,7 @@ def main():
     roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom}
 
-    del g_step, g4, g8, g4g, copies, copies_g
+    del g_step, g4, g8, g4g, g16, g4f, copies, copies_g, copies16, W16
     torch.cuda.empty_cache()
     chain_info = None
     if not args.no_chain:

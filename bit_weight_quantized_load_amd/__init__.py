@@ -56,6 +56,8 @@ SIGNATURES = {
     "qw_w4g_scales": (_I, [_P, _I64, _I64, _I64, _P, _P]),
     "gemv_w4a8g": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "qw_gemv_w4a8g_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
+    "qw_gemv_f16": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
+    "qw_gemv_w4f32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
 }
@@ -357,6 +359,35 @@ def gemm_w8a16_mfma(X16, Wq, w_scale16, nw=4, mb=1, nbw=1, out=None, stream=None
     _need(Y, torch.float16, (M, N), "out")
     _call("qw_gemm_w8a16_mfma", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
           nw, mb, nbw, _stream(stream))
+    return Y
+
+
+def gemv_f16(X16, W16, rows_per_wave=0, out=None, stream=None):
+    """The FP16 baseline GEMV (an ablation): Y f16 [1][N] of X16 f16 [1][K] and row-major
+    W16 f16 [N][K]."""
+    torch = _torch()
+    M, K = X16.shape
+    N = W16.shape[0]
+    _need(X16, torch.float16, (M, K), "X16")
+    _need(W16, torch.float16, (N, K), "W16")
+    Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
+    _need(Y, torch.float16, (M, N), "out")
+    _call("qw_gemv_f16", _ptr(X16), _ptr(W16), M, N, K, _ptr(Y), rows_per_wave, _stream(stream))
+    return Y
+
+
+def gemv_w4f32(X, Wq, w_scale, rows_per_wave=0, out=None, stream=None):
+    """Weight-only INT4 with float activations (an ablation): Y fp32 [1][N]."""
+    torch = _torch()
+    M, K = X.shape
+    N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    _call("qw_gemv_w4f32", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), rows_per_wave,
+          _stream(stream))
     return Y
 
 

@@ -693,6 +693,51 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
                      stream);
 }
 
+int check_ablation(const void* X, const void* W, int64_t M, int64_t N, int64_t K, const void* Y,
+                   int rows_per_wave)
+{
+    if (!X || !W || !Y)
+        return QW_ERR_NULL;
+    int st = check_shape(M, N, K);
+    if (st != QW_OK)
+        return st;
+    if (M != 1 || K > 4096 || N > ((int64_t)1 << 26))
+        return QW_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(W) || !aligned16(Y))
+        return QW_ERR_ALIGN;
+    if (rows_per_wave != 0 && rows_per_wave != 1 && rows_per_wave != 2 && rows_per_wave != 4)
+        return QW_ERR_TILING;
+    return QW_OK;
+}
+
+int qw_gemv_f16(const uint16_t* X16, const uint16_t* W16, int64_t M, int64_t N, int64_t K,
+                uint16_t* Y16, int rows_per_wave, void* stream)
+{
+    int st = check_ablation(X16, W16, M, N, K, Y16, rows_per_wave);
+    if (st != QW_OK)
+        return st;
+    return hip_status(qw::launch_gemv_f16(X16, W16, Y16, (int)N, (int)K,
+                                          rows_per_wave ? rows_per_wave : 2,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, float* Y, int rows_per_wave, void* stream)
+{
+    int st = check_ablation(X, Wq, M, N, K, Y, rows_per_wave);
+    if (st != QW_OK)
+        return st;
+    if (!w_scale)
+        return QW_ERR_NULL;
+    if (!aligned16(w_scale))
+        return QW_ERR_ALIGN;
+    // one row group per wave by default: with more, the compiler keeps several row
+    // groups' converted weights live and the kernel runs at one wave per SIMD
+    return hip_status(qw::launch_gemv_w4f32(X, static_cast<const uint8_t*>(Wq), w_scale, Y,
+                                            (int)N, (int)K, rows_per_wave ? rows_per_wave : 1,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scale, void* stream)
 {
     if (!X || !Xq || !a_scale)

@@ -172,6 +172,13 @@ hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t st);
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st);
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st);
+// The INT4 page's ablations (M == 1, K <= 4096): FP16 GEMV on row-major f16 weights, and
+// weight-only INT4 (quantize_pack_w4 layout) with fp32 activations unpacked to float;
+// rpw rows (FP16) or row groups (INT4) per wave, 1, 2 or 4.
+hipError_t launch_gemv_f16(const uint16_t* X, const uint16_t* W, uint16_t* Y, int N, int K,
+                           int rpw, hipStream_t st);
+hipError_t launch_gemv_w4f32(const float* X, const uint8_t* Wq, const float* s, float* Y, int N,
+                             int K, int rpw, hipStream_t st);
 // Group-wise W4A8 GEMV (M == 1, producer-wave tilings u == 5 or 6): w_scale holds the
 // group scales in the layout of w4g_scale_index; group = 32 .. 512.
 hipError_t launch_gemv_w4a8g(const W4A8Args& a, const GemvTiling& t, int group, hipStream_t st);

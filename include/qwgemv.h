@@ -238,6 +238,22 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int nw, int mb,
                        int nbw, void* stream);
 
+/* The two ablations the INT4 write-up times beside its INT4-weight / INT8-activation
+   path ("Jetson Orin AGX 上的 INT4 量化推理实践", section 速度结果), as M == 1 GEMVs with
+   K <= 4096 (QW_ERR_SHAPE otherwise); not part of the quantized linear itself.
+   qw_gemv_f16: the FP16 baseline.  X16 f16 [1][K], W16 f16 [N][K] row-major (no
+     packing) -> Y16 f16 [1][N] = f16(sum_k w * x), the sum in fp32.
+   qw_gemv_w4f32: weight-only INT4 with float activations (sections 最初的问题 and
+     问题原因): Wq and w_scale from quantize_pack_w4, X fp32 [1][K] -> Y fp32 [1][N] =
+     w_scale[n] * sum_k (float)q[n][k] * x[k], each nibble sign-extended, converted to
+     float and multiplied-added in fp32 (summation order of the kernel's choosing).
+   rows_per_wave: rows (FP16) or groups of 4 rows (INT4) per wave, 1, 2 or 4, or 0 for
+   the default (2 for FP16, 1 for INT4); QW_ERR_TILING otherwise. */
+int qw_gemv_f16(const uint16_t* X16, const uint16_t* W16, int64_t M, int64_t N, int64_t K,
+                uint16_t* Y16, int rows_per_wave, void* stream);
+int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, float* Y, int rows_per_wave, void* stream);
+
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);
 /* The hipError_t of the last QW_ERR_HIP returned on this thread (0 if none). */

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 23
+    assert len(names) == 25
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -203,6 +203,21 @@ def test_group_wise_sizes_and_argument_checks():
     assert w4(A, A2, A3, 2, 64, 512, A4, 5, 8, 8, 2, NULL) == qw.QW_ERR_TILING
     assert w4(A, A2, A3, 1, 64, 32768, A4, 6, 8, 2048, 8, NULL) == qw.QW_ERR_TILING
     assert L.qw_gemv_w8a16_tiled(A, A2, A3, 1, 64, 512, A4, 5, 8, 8, 2, NULL) == qw.QW_ERR_TILING
+
+
+def test_ablation_entry_points_check_arguments():
+    for f in (L.qw_gemv_f16,):
+        assert f(NULL, A2, 1, 64, 512, A3, 0, NULL) == qw.QW_ERR_NULL
+        assert f(A, A2, 2, 64, 512, A3, 0, NULL) == qw.QW_ERR_SHAPE     # M == 1 only
+        assert f(A, A2, 1, 64, 4608, A3, 0, NULL) == qw.QW_ERR_SHAPE    # K <= 4096
+        assert f(A, A2, 1, 64, 500, A3, 0, NULL) == qw.QW_ERR_SHAPE
+        assert f(A, MIS, 1, 64, 512, A3, 0, NULL) == qw.QW_ERR_ALIGN
+        assert f(A, A2, 1, 64, 512, A3, 3, NULL) == qw.QW_ERR_TILING
+    g = L.qw_gemv_w4f32
+    assert g(A, A2, NULL, 1, 64, 512, A3, 0, NULL) == qw.QW_ERR_NULL
+    assert g(A, A2, A4, 3, 64, 512, A3, 0, NULL) == qw.QW_ERR_SHAPE
+    assert g(A, A2, MIS, 1, 64, 512, A3, 0, NULL) == qw.QW_ERR_ALIGN
+    assert g(A, A2, A4, 1, 64, 512, A3, 8, NULL) == qw.QW_ERR_TILING
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

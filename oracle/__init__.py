@@ -22,6 +22,8 @@ and which passage of the pages it follows, is stated in ``qw_oracle.c``:
   W4A8 (section 速度结果): an FP16 GEMV (fp64 reference) and weight-only INT4 with
   float activations, unpacked to float and multiplied-added in fp32 (sections 最初的问题
   and 问题原因).
+* ``index_lut`` / ``index_cint`` / ``index_softmax`` / ``int_attention`` -- IndexSoftmax, the
+  integer softmax of the IntAttention summary (sections 基准/方法设计 and 方法细节).
 * ``f16_from_f32`` / ``f32_from_f16`` -- IEEE binary16 conversions written from the
   format's definition.
 
@@ -72,6 +74,9 @@ def _load():
             "qwo_gemv_w4a8g": [P, P, P, I64, I64, I64, I64, P, P, P, P, ctypes.c_int],
             "qwo_gemv_f16_ref64": [P, P, I64, I64, I64, P, ctypes.c_int],
             "qwo_gemv_w4f32": [P, P, P, I64, I64, I64, P, P, ctypes.c_int],
+            "qwo_index_lut": [ctypes.c_int, ctypes.c_double, P],
+            "qwo_index_softmax": [P, I64, I64, ctypes.c_int32, ctypes.c_int, P, P, P, ctypes.c_int],
+            "qwo_int_attention": [P, P, P, I64, I64, I64, ctypes.c_int, ctypes.c_double, P, P, P, P],
             "qwo_quant_w8": [P, I64, I64, P, P],
             "qwo_gemv_w8a16_ref64": [P, P, P, I64, I64, I64, P, ctypes.c_int],
             "qwo_f16_from_f32_n": [P, I64, P],
@@ -82,6 +87,8 @@ def _load():
             fn.argtypes = args
             fn.restype = ctypes.c_int if not name.endswith("_n") else None
         lib.qwo_num_threads.restype = ctypes.c_int
+        lib.qwo_index_cint.restype = ctypes.c_int32
+        lib.qwo_index_cint.argtypes = [ctypes.c_double, ctypes.c_int, ctypes.c_double, ctypes.c_double]
         _lib = lib
     return _lib
 
@@ -246,6 +253,46 @@ def w4f32_bound(X, q, s):
     K = X.shape[1]
     t = np.abs(X.astype(np.float64)) @ np.abs(q.astype(np.float64)).T
     return (K + 2) * 2.0 ** -24 * t * s.astype(np.float64)[None, :]
+
+
+def index_lut(b=5, c=6.6):
+    """The 2^b-entry UINT8 exponent table of IndexSoftmax."""
+    lut = np.empty((1 << b,), np.uint8)
+    _check(_load().qwo_index_lut(int(b), float(c), _p(lut)))
+    return lut
+
+
+def index_cint(c, d, s_q, s_k):
+    """Integer clipping threshold round(c * sqrt(d) / (s_Q * s_K))."""
+    return int(_load().qwo_index_cint(float(c), int(d), float(s_q), float(s_k)))
+
+
+def index_softmax(A, c_int, b=5, c=6.6, nthreads=1):
+    """IndexSoftmax of int32 logits A [rows][L] -> (P uint8 [rows][L], rowSum int32 [rows])."""
+    A = _c(A, np.int32)
+    rows, L = A.shape
+    lut = index_lut(b, c)
+    P = np.empty((rows, L), np.uint8)
+    rs = np.empty((rows,), np.int32)
+    _check(_load().qwo_index_softmax(_p(A), rows, L, int(c_int), int(b), _p(lut), _p(P), _p(rs),
+                                     int(nthreads)))
+    return P, rs
+
+
+def int_attention(Q, K, V, b=5, c=6.6):
+    """One head of the all-integer attention: dict A int32, P uint8, O fp32, c_int."""
+    Q = _c(Q, np.float32)
+    K = _c(K, np.float32)
+    V = _c(V, np.float32)
+    Lq, d = Q.shape
+    Lk = K.shape[0]
+    A = np.empty((Lq, Lk), np.int32)
+    P = np.empty((Lq, Lk), np.uint8)
+    O = np.empty((Lq, d), np.float32)
+    ci = np.zeros((1,), np.int32)
+    _check(_load().qwo_int_attention(_p(Q), _p(K), _p(V), Lq, Lk, d, int(b), float(c), _p(A), _p(P),
+                                     _p(O), _p(ci)))
+    return {"A": A, "P": P, "O": O, "c_int": int(ci[0])}
 
 
 def quant_w8(W):

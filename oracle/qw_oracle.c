@@ -17,6 +17,9 @@
  *         in int32 (the DP4A dot); INT4 values widened to int8 lanes.
  *       - section 问题原因 (cause of the problem): the unpack step sign-extends the
  *         nibble, so nibbles hold two's-complement values.
+ *  [P3] IntAttention (CSDN summary of the MLSys 2026 paper): IndexSoftmax, section
+ *       基准/方法设计 (clipping, LUT exponent, integer normalisation) and section
+ *       方法细节 (the all-integer attention data flow).
  *  [P2] ChatGLM2-6B W8A16 deployment on BM1684X (TPU-MLIR write-up)
  *       - section 2 量化方案 (quantization scheme): linear weights stored per-channel
  *         as INT8 and dequantized back to F16 at compute time.
@@ -45,6 +48,7 @@
  */
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #ifdef _OPENMP
@@ -436,6 +440,127 @@ int qwo_gemv_w4f32(const float* X, const int8_t* q, const float* s, int64_t M, i
             Y64[m * N + n] = y64;
     }
     return QWO_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* [P3] IntAttention (CSDN summary of the MLSys 2026 paper), 基准/方法设计:      */
+/* IndexSoftmax, an integer replacement of softmax over int32 logits, in three */
+/* steps per row of the logit matrix A (int32, from an INT8 QK^T):             */
+/*  1. clipping (机制一):  D = rowMax(A) - A;  D' = min(D, c_int), with          */
+/*     c_int = round(c * sqrt(d) / (s_Q * s_K)) fixed per tensor pair;          */
+/*  2. LUT exponent (机制二):  idx = round(D' * (2^b - 1) / c_int);             */
+/*     E = LUT[idx], LUT[i] = round(255 * exp(-c * i / (2^b - 1))), the last     */
+/*     entry forced to 0 (a 2^b-entry UINT8 table; (b, c) = (5, 6.6));          */
+/*  3. integer normalisation (机制三):  rowSum = sum E (32-bit);                 */
+/*     P = round(255 * E / rowSum), UINT8.                                       */
+/* Readings (the page writes the rounding as a bracket only): every rounding of */
+/* a non-negative ratio is half up, done in integers: round(x / y) =            */
+/* (2x + y) / (2y); the table rounds to nearest (round()).  c_int must be >= 1. */
+/* ------------------------------------------------------------------------ */
+int qwo_index_lut(int b, double c, uint8_t* lut)
+{
+    if (b < 1 || b > 8 || !(c > 0.0))
+        return QWO_ERR_ARG;
+    const int n = (1 << b) - 1;
+    for (int i = 0; i < n; ++i)
+        lut[i] = (uint8_t)round(255.0 * exp(-c * (double)i / (double)n));
+    lut[n] = 0;
+    return QWO_OK;
+}
+
+int32_t qwo_index_cint(double c, int d, double s_q, double s_k)
+{
+    return (int32_t)llround(c * sqrt((double)d) / (s_q * s_k));
+}
+
+int qwo_index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b,
+                      const uint8_t* lut, uint8_t* P, int32_t* rowsum, int nthreads)
+{
+    if (rows < 0 || L < 1 || c_int < 1 || b < 1 || b > 8)
+        return QWO_ERR_ARG;
+    if (nthreads < 1)
+        nthreads = 1;
+    const int64_t n = (1 << b) - 1;
+#pragma omp parallel for num_threads(nthreads) schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const int32_t* a = A + r * L;
+        int32_t mx = a[0];
+        for (int64_t j = 1; j < L; ++j)
+            if (a[j] > mx)
+                mx = a[j];
+        int64_t sum = 0;
+        for (int64_t j = 0; j < L; ++j) {
+            int64_t dl = (int64_t)mx - (int64_t)a[j];
+            if (dl > c_int)
+                dl = c_int;
+            const int64_t idx = (2 * dl * n + c_int) / (2 * (int64_t)c_int);
+            sum += lut[idx];
+        }
+        if (rowsum)
+            rowsum[r] = (int32_t)sum;
+        for (int64_t j = 0; j < L; ++j) {
+            int64_t dl = (int64_t)mx - (int64_t)a[j];
+            if (dl > c_int)
+                dl = c_int;
+            const int64_t idx = (2 * dl * n + c_int) / (2 * (int64_t)c_int);
+            P[r * L + j] = (uint8_t)((2 * 255 * (int64_t)lut[idx] + sum) / (2 * sum));
+        }
+    }
+    return QWO_OK;
+}
+
+/* [P3] 方法细节 (the full data flow): per-tensor symmetric INT8 Q, K, V            */
+/* (scale = maxabs/127, the activation rule of qwo_quant_act_i8 over the whole   */
+/* tensor), A = Qq Kq^T in int32, IndexSoftmax with c_int from the scales and d,  */
+/* UINT8 P, O_acc = P Vq in int32, O = O_acc * s_V / 255.  One head: Q [Lq][d],   */
+/* K and V [Lk][d].  Outputs A [Lq][Lk], P [Lq][Lk], O [Lq][d]; *c_int_out.        */
+int qwo_int_attention(const float* Q, const float* K, const float* V, int64_t Lq, int64_t Lk,
+                      int64_t d, int b, double c, int32_t* A, uint8_t* P, float* O,
+                      int32_t* c_int_out)
+{
+    if (Lq < 1 || Lk < 1 || d < 1)
+        return QWO_ERR_ARG;
+    int8_t* q = (int8_t*)malloc((size_t)(Lq * d));
+    int8_t* k = (int8_t*)malloc((size_t)(Lk * d));
+    int8_t* v = (int8_t*)malloc((size_t)(Lk * d));
+    int st = QWO_ERR_ARG;
+    float sq, sk, sv;
+    uint8_t lut[256];
+    if (!q || !k || !v)
+        goto done;
+    if ((st = qwo_quant_act_i8(Q, 1, Lq * d, q, &sq)) != QWO_OK ||
+        (st = qwo_quant_act_i8(K, 1, Lk * d, k, &sk)) != QWO_OK ||
+        (st = qwo_quant_act_i8(V, 1, Lk * d, v, &sv)) != QWO_OK)
+        goto done;
+    st = QWO_ERR_ARG;
+    if (!(sq > 0.0f) || !(sk > 0.0f))
+        goto done;
+    for (int64_t i = 0; i < Lq; ++i)
+        for (int64_t j = 0; j < Lk; ++j) {
+            int32_t acc = 0;
+            for (int64_t t = 0; t < d; ++t)
+                acc += (int32_t)q[i * d + t] * (int32_t)k[j * d + t];
+            A[i * Lk + j] = acc;
+        }
+    const int32_t ci = qwo_index_cint(c, (int)d, sq, sk);
+    *c_int_out = ci;
+    if (ci < 1 || qwo_index_lut(b, c, lut) != QWO_OK)
+        goto done;
+    if ((st = qwo_index_softmax(A, Lq, Lk, ci, b, lut, P, NULL, 1)) != QWO_OK)
+        goto done;
+    for (int64_t i = 0; i < Lq; ++i)
+        for (int64_t t = 0; t < d; ++t) {
+            int32_t acc = 0;
+            for (int64_t j = 0; j < Lk; ++j)
+                acc += (int32_t)P[i * Lk + j] * (int32_t)v[j * d + t];
+            O[i * d + t] = (float)((double)acc * (double)sv / 255.0);
+        }
+    st = QWO_OK;
+done:
+    free(q);
+    free(k);
+    free(v);
+    return st;
 }
 
 int qwo_num_threads(void)

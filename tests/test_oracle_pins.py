@@ -388,6 +388,88 @@ def test_gemv_w4f32_equals_w4a8_on_integer_activations():
     assert np.array_equal(Yf.view(np.uint32), r["Y"].view(np.uint32))
 
 
+# ------------------------------------------------------------ IndexSoftmax --
+
+def test_index_lut_values():
+    """(b, c) = (5, 6.6): 32 UINT8 entries; entry 0 is exp(0) * 255, entry 1 is
+    255 * e^(-6.6/31) = 206.1, the last is forced to 0; within half a unit of the
+    formula evaluated with numpy's exp; non-increasing."""
+    lut = oracle.index_lut(5, 6.6)
+    assert lut.shape == (32,) and lut[0] == 255 and lut[1] == 206 and lut[31] == 0
+    ref = 255.0 * np.exp(-6.6 * np.arange(31) / 31.0)
+    assert np.all(np.abs(lut[:31] - ref) <= 0.5)
+    assert np.all(np.diff(lut.astype(int)) <= 0)
+    assert oracle.index_lut(4, 6.6)[15] == 0 and oracle.index_lut(4, 6.6).shape == (16,)
+
+
+def test_index_softmax_closed_forms():
+    # equal logits: every E is 255, P = round(255 / L), ties up (L = 2: 127.5 -> 128)
+    for L, want in ((1, 255), (2, 128), (3, 85), (4, 64), (255, 1), (256, 1), (600, 0)):
+        P, rs = oracle.index_softmax(np.full((1, L), -37, np.int32), 100)
+        assert np.all(P == want) and rs[0] == 255 * L, L
+    # one logit ahead of the rest by at least c_int: the rest clip to the last entry (0)
+    A = np.array([[5, 5 + 1000, 5, -2**30]], np.int32)
+    P, rs = oracle.index_softmax(A, 1000)
+    assert P.tolist() == [[0, 255, 0, 0]] and rs[0] == 255
+    # index rounding half up: with c_int = 62, D = 1 maps to 31/62 = 0.5 -> entry 1 and
+    # D = 3 to 1.5 -> entry 2
+    P, rs = oracle.index_softmax(np.array([[10, 9, 7]], np.int32), 62)
+    lut = oracle.index_lut()
+    assert rs[0] == 255 + int(lut[1]) + int(lut[2])
+
+
+def test_index_softmax_invariants_and_float_softmax():
+    rng = np.random.default_rng(61)
+    d, sq, sk = 128, 0.02, 0.03
+    A = rng.integers(-30000, 30000, size=(64, 777)).astype(np.int32)
+    ci = oracle.index_cint(6.6, d, sq, sk)
+    assert ci == 124_451  # 6.6 * sqrt(128) / 0.0006 = 124450.79...
+    assert ci == round(6.6 * np.sqrt(128) / (0.02 * 0.03))
+    P, rs = oracle.index_softmax(A, ci)
+    P2, rs2 = oracle.index_softmax(A + np.int32(12345), ci)   # shift invariance
+    assert np.array_equal(P, P2) and np.array_equal(rs, rs2)
+    Pt, _ = oracle.index_softmax(A, ci, nthreads=4)
+    assert np.array_equal(P, Pt)
+    # each P rounds 255 E / rowSum: the row totals stay within L/2 of 255
+    assert np.all(np.abs(P.astype(np.int64).sum(axis=1) - 255) <= 777 / 2)
+    # the row maximum gets the largest probability
+    assert np.all(P[np.arange(64), A.argmax(axis=1)] == P.max(axis=1))
+    # close to the float softmax of the dequantized logits (the page reports cosine
+    # 0.9991 for UINT8 probabilities) on rows as peaked as attention rows (logits of
+    # standard deviation 3); on flat rows over many keys every probability is below
+    # 1/510 and rounds to 0 or 1 (the 8-bit ceiling the page lists as a limitation)
+    z = rng.standard_normal((64, 256)) * 3.0
+    A = np.round(z * np.sqrt(d) / (sq * sk)).astype(np.int32)
+    P, _ = oracle.index_softmax(A, ci)
+    z = A.astype(np.float64) * sq * sk / np.sqrt(d)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    q = P / 255.0
+    cos = (p * q).sum(axis=1) / np.linalg.norm(p, axis=1) / np.linalg.norm(q, axis=1)
+    assert cos.mean() > 0.998 and cos.min() > 0.99
+
+
+def test_int_attention_pipeline():
+    rng = np.random.default_rng(62)
+    Lq, Lk, d = 16, 200, 64
+    Q = rng.standard_normal((Lq, d)).astype(np.float32)
+    K = rng.standard_normal((Lk, d)).astype(np.float32)
+    V = rng.standard_normal((Lk, d)).astype(np.float32)
+    r = oracle.int_attention(Q, K, V)
+    q, sq = oracle.quant_act_i8(Q.reshape(1, -1))
+    k, sk = oracle.quant_act_i8(K.reshape(1, -1))
+    A = q.reshape(Lq, d).astype(np.int64) @ k.reshape(Lk, d).astype(np.int64).T
+    assert np.array_equal(r["A"], A)
+    assert r["c_int"] == oracle.index_cint(6.6, d, sq[0], sk[0])
+    assert np.array_equal(r["P"], oracle.index_softmax(r["A"], r["c_int"])[0])
+    z = (Q.astype(np.float64) @ K.astype(np.float64).T) / np.sqrt(d)
+    p = np.exp(z - z.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    O = p @ V.astype(np.float64)
+    cos = (O * r["O"]).sum() / np.linalg.norm(O) / np.linalg.norm(r["O"])
+    assert cos > 0.98
+
+
 # ------------------------------------------------------------ W8 weights --
 
 def test_quant_w8_closed_form_rows():

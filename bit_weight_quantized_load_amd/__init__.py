@@ -58,6 +58,8 @@ SIGNATURES = {
     "qw_gemv_w4a8g_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
     "qw_gemv_f16": (_I, [_P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "qw_gemv_w4f32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
+    "index_softmax": (_I, [_P, _I64, _I64, ctypes.c_int32, _I, ctypes.c_double, _P, _P]),
+    "qw_index_cint": (ctypes.c_int32, [ctypes.c_double, _I64, ctypes.c_double, ctypes.c_double]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
 }
@@ -389,6 +391,22 @@ def gemv_w4f32(X, Wq, w_scale, rows_per_wave=0, out=None, stream=None):
     _call("qw_gemv_w4f32", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), rows_per_wave,
           _stream(stream))
     return Y
+
+
+def index_cint(c, d, s_q, s_k) -> int:
+    """IndexSoftmax clipping threshold round(c * sqrt(d) / (s_Q * s_K)) (-1 if invalid)."""
+    return int(lib().qw_index_cint(float(c), int(d), float(s_q), float(s_k)))
+
+
+def index_softmax(A, c_int, b=5, c=6.6, out=None, stream=None):
+    """IndexSoftmax of int32 logits A [rows][L] -> UINT8 probabilities [rows][L]."""
+    torch = _torch()
+    rows, L = A.shape
+    _need(A, torch.int32, (rows, L), "A")
+    P = torch.empty((rows, L), dtype=torch.uint8, device=A.device) if out is None else out
+    _need(P, torch.uint8, (rows, L), "out")
+    _call("index_softmax", _ptr(A), rows, L, int(c_int), int(b), float(c), _ptr(P), _stream(stream))
+    return P
 
 
 def w4_codes(Wq, N, K, stream=None):

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <atomic>
 #include <mutex>
 #include <stddef.h>
@@ -736,6 +737,43 @@ int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t 
     return hip_status(qw::launch_gemv_w4f32(X, static_cast<const uint8_t*>(Wq), w_scale, Y,
                                             (int)N, (int)K, rows_per_wave ? rows_per_wave : 1,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k)
+{
+    if (!(c > 0.0) || d < 1 || !(s_q > 0.0) || !(s_k > 0.0))
+        return -1;
+    const double v = c * std::sqrt((double)d) / (s_q * s_k);
+    if (!(v < 2147483647.0))
+        return -1;
+    return (int32_t)std::llround(v);
+}
+
+int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b, double c,
+                  uint8_t* P, void* stream)
+{
+    if (!A || !P)
+        return QW_ERR_NULL;
+    if (rows < 1 || rows > 2147483647 || L < 1 || L > 16384 || c_int < 1 || b < 4 || b > 6 ||
+        !(c > 0.0) || !(c < 1e6))
+        return QW_ERR_SHAPE;
+    if (!aligned16(A) || !aligned16(P))
+        return QW_ERR_ALIGN;
+    // the exponent table of the IntAttention summary (section 基准/方法设计):
+    // LUT[i] = round(255 exp(-c i / n)), the last entry 0; and the index thresholds
+    qw::IndexSoftmaxArgs t;
+    t.c_int = c_int;
+    t.b = b;
+    const int n = (1 << b) - 1;
+    for (int i = 0; i < 64; ++i) {
+        t.lut[i] = 0;
+        t.thr[i] = 0;
+    }
+    for (int i = 0; i < n; ++i)
+        t.lut[i] = (uint32_t)std::lround(255.0 * std::exp(-c * (double)i / (double)n));
+    for (int k = 1; k <= n; ++k)
+        t.thr[k] = (uint32_t)(((int64_t)c_int * (2 * k - 1) + 2 * n - 1) / (2 * n));
+    return hip_status(qw::launch_index_softmax(A, rows, L, t, P, static_cast<hipStream_t>(stream)));
 }
 
 int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scale, void* stream)

@@ -175,6 +175,18 @@ hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_
 // The INT4 page's ablations (M == 1, K <= 4096): FP16 GEMV on row-major f16 weights, and
 // weight-only INT4 (quantize_pack_w4 layout) with fp32 activations unpacked to float;
 // rpw rows (FP16) or row groups (INT4) per wave, 1, 2 or 4.
+// IndexSoftmax (integer softmax over int32 logits): b-bit table (n = 2^b - 1 entries past
+// 0), thr[k] = ceil(c_int * (2k - 1) / (2n)) for k = 1..n (thr[0] unused), lut[k] the
+// UINT8 exponent table (lut[n] = 0).  1 <= L <= 16384.
+struct IndexSoftmaxArgs {
+    int32_t c_int;
+    int b;
+    uint32_t thr[64];
+    uint32_t lut[64];
+};
+hipError_t launch_index_softmax(const int32_t* A, int64_t rows, int64_t L,
+                                const IndexSoftmaxArgs& t, uint8_t* P, hipStream_t st);
+
 hipError_t launch_gemv_f16(const uint16_t* X, const uint16_t* W, uint16_t* Y, int N, int K,
                            int rpw, hipStream_t st);
 hipError_t launch_gemv_w4f32(const float* X, const uint8_t* Wq, const float* s, float* Y, int N,

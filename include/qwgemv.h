@@ -254,6 +254,21 @@ int qw_gemv_f16(const uint16_t* X16, const uint16_t* W16, int64_t M, int64_t N, 
 int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
                   int64_t K, float* Y, int rows_per_wave, void* stream);
 
+/* IndexSoftmax, the integer softmax of the IntAttention summary (CSDN, MLSys 2026 paper),
+   section 基准/方法设计: int32 attention logits A [rows][L] (row-major, from an INT8
+   QK^T) -> UINT8 probabilities P [rows][L].  Per row, with n = 2^b - 1:
+     D = rowMax(A) - A,  D' = min(D, c_int),  idx = round(D' * n / c_int),
+     E = LUT[idx],  LUT[i] = round(255 * exp(-c * i / n)) (LUT[n] = 0),
+     P = round(255 * E / sum_row E)   (32-bit row sum),
+   every rounding of a non-negative ratio half up.  The page recommends (b, c) = (5, 6.6);
+   b = 4, 5 or 6, 1 <= L <= 16384 (the page's longest sequence), c_int >= 1 (QW_ERR_SHAPE otherwise); A and P 16-byte
+   aligned.  One pass over memory: 4 bytes read and 1 written per logit.
+   qw_index_cint gives c_int = round(c * sqrt(d) / (s_Q * s_K)) for head dimension d and
+   the per-tensor scales of Q and K, or -1 when that is not a positive int32. */
+int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b, double c,
+                  uint8_t* P, void* stream);
+int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k);
+
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);
 /* The hipError_t of the last QW_ERR_HIP returned on this thread (0 if none). */

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 25
+    assert len(names) == 27
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -218,6 +218,20 @@ def test_ablation_entry_points_check_arguments():
     assert g(A, A2, A4, 3, 64, 512, A3, 0, NULL) == qw.QW_ERR_SHAPE
     assert g(A, A2, MIS, 1, 64, 512, A3, 0, NULL) == qw.QW_ERR_ALIGN
     assert g(A, A2, A4, 1, 64, 512, A3, 8, NULL) == qw.QW_ERR_TILING
+
+
+def test_index_softmax_checks_and_threshold():
+    f = L.index_softmax
+    assert f(NULL, 4, 64, 100, 5, 6.6, A2, NULL) == qw.QW_ERR_NULL
+    for (rows, Ln, ci, b, c) in [(0, 64, 100, 5, 6.6), (4, 0, 100, 5, 6.6), (4, 16385, 100, 5, 6.6),
+                                 (4, 64, 0, 5, 6.6), (4, 64, 100, 3, 6.6), (4, 64, 100, 7, 6.6),
+                                 (4, 64, 100, 5, 0.0), (4, 64, 100, 5, -1.0)]:
+        assert f(A, rows, Ln, ci, b, c, A2, NULL) == qw.QW_ERR_SHAPE, (rows, Ln, ci, b, c)
+    assert f(MIS, 4, 64, 100, 5, 6.6, A2, NULL) == qw.QW_ERR_ALIGN
+    assert f(A, 4, 64, 100, 5, 6.6, MIS, NULL) == qw.QW_ERR_ALIGN
+    assert L.qw_index_cint(6.6, 128, 0.02, 0.03) == 124451      # 124450.79...
+    assert L.qw_index_cint(6.6, 128, 0.0, 0.03) == -1
+    assert L.qw_index_cint(6.6, 128, 1e-9, 1e-9) == -1          # beyond int32
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

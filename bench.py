@@ -11,7 +11,8 @@ not from the 256 MB last-level cache.
 Printed: ONE JSON line with `value` = algorithmic bytes of both GEMVs / time per
 step (GB/s), per-kernel microseconds and GB/s (also, outside the step, of the group-wise
 INT4 variant and of the INT4 page's two ablations -- an FP16 GEMV and weight-only INT4
-unpacked to float -- on the same shape), the roofline of the dominant kernel
+unpacked to float -- on the same shape, and of IndexSoftmax on 8192 x 4096 int32
+attention logits), the roofline of the dominant kernel
 (per-launch algorithmic bytes / average launch time from HIP events), the CPU
 oracle timed on this host on the same inputs, and the linear-layer time per token
 of the 28-layer decode-step chain in one HIP graph (unfused and with q|k|v and
@@ -212,6 +213,44 @@ def chain_measurement(qw, wl, torch, replays):
     return out
 
 
+def index_softmax_measurement(qw, torch, launches):
+    """IndexSoftmax (the integer softmax of the IntAttention summary) on attention-like
+    int32 logits: 8192 rows (2 heads x 4096 queries) of 4096 keys, d = 128, (b, c) =
+    (5, 6.6); 4 B read and 1 B written per logit; input copies rotated past the cache."""
+    rows, L, d = 8192, 4096, 128
+    s_q, s_k = 0.02, 0.03
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    z = torch.randn((rows, L), generator=g, device="cuda") * 3.0
+    A = torch.round(z * (d ** 0.5) / (s_q * s_k)).to(torch.int32)
+    del z
+    ci = qw.index_cint(6.6, d, s_q, s_k)
+    R = max(2, math.ceil(ROTATE_BYTES / (A.numel() * 4)))
+    copies = [A] + [A.clone() for _ in range(R - 1)]
+    P = torch.empty((rows, L), dtype=torch.uint8, device="cuda")
+    n = max(20, launches // 20)
+    qw.index_softmax(A, ci, out=P)
+    torch.cuda.synchronize()
+    gr = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gr):
+        for i in range(n):
+            qw.index_softmax(copies[i % R], ci, out=P)
+    gr.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    gr.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / n
+    b = rows * L * 5
+    del gr, copies, A, P
+    torch.cuda.empty_cache()
+    return {"rows": rows, "L": L, "c_int": ci, "us": round(us, 2), "algo_bytes": b,
+            "GB/s": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -222,6 +261,8 @@ def main():
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the 28-layer decode-step chain measurement")
     ap.add_argument("--chain-replays", type=int, default=20)
+    ap.add_argument("--no-index-softmax", action="store_true",
+                    help="skip the IndexSoftmax measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run --steps device-to-device copies of BYTES bytes (a plain "
                          "copy kernel of known size, to calibrate HBM byte counters) and exit")
@@ -391,6 +432,7 @@ def main():
 
     del g_step, g4, g8, g4g, g16, g4f, copies, copies_g, copies16, W16
     torch.cuda.empty_cache()
+    isoft = None if args.no_index_softmax else index_softmax_measurement(qw, torch, K_steps)
     chain_info = None
     if not args.no_chain:
         chain_info = chain_measurement(qw, wl, torch, args.chain_replays)
@@ -408,6 +450,7 @@ def main():
                    "step": "gemv_w4a8 + gemv_w8a16", "weight_copies_rotated": R},
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
         "decode_chain": chain_info,
+        "index_softmax": isoft,
     }
     print(json.dumps(line), flush=True)
 

@@ -765,6 +765,7 @@ int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int 
     t.c_int = c_int;
     t.b = b;
     const int n = (1 << b) - 1;
+    t.scale = (float)((double)n / (double)c_int);
     for (int i = 0; i < 64; ++i) {
         t.lut[i] = 0;
         t.thr[i] = 0;

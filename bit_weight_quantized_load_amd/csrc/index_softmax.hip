@@ -9,10 +9,11 @@
 //
 // One workgroup per row, one pass over memory: the row is read once into registers (4 B
 // per logit) and P written once (1 B).  No division per element: idx >= k exactly when
-// D' >= T_k = ceil(c_int * (2k - 1) / (2n)), so a b-step binary search over the b
-// thresholds (host-computed, in LDS) gives idx; and P depends on idx only, so after the
-// row sum the 2^b probabilities round(255 * LUT[k] / sum) are computed once (one integer
-// division per table entry) and gathered.
+// D' >= T_k = ceil(c_int * (2k - 1) / (2n)) (host-computed thresholds, in LDS).  A float
+// estimate round(D' * (n / c_int)) is within one of idx (its error is below 1e-5 of a
+// step), and one comparison with the thresholds on each side makes it exact.  P depends
+// on idx only, so after the row sum the 2^b probabilities round(255 * LUT[k] / sum) are
+// computed once (one integer division per table entry) and gathered.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -100,9 +101,12 @@ __global__ __launch_bounds__(64 * NW) void k_index_softmax(const int32_t* __rest
             // mx >= v: the difference is exact as an unsigned 32-bit number
             uint32_t d = (uint32_t)mx - (uint32_t)v4[u];
             d = d < cint ? d : cint;
-            uint32_t k = 0;
-            for (int step = (n + 1) >> 1; step > 0; step >>= 1)
-                k = d >= s_thr[k + step] ? k + step : k;
+            uint32_t k = (uint32_t)((float)d * t.scale + 0.5f);
+            k = k < (uint32_t)n ? k : (uint32_t)n;
+            if (k > 0 && d < s_thr[k])
+                --k;
+            else if (k < (uint32_t)n && d >= s_thr[k + 1])
+                ++k;
             if (e + u < L)
                 sum += s_lut[k];
             packed |= k << (8 * u);

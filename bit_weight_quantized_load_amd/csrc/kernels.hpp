@@ -181,6 +181,7 @@ hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_
 struct IndexSoftmaxArgs {
     int32_t c_int;
     int b;
+    float scale;  // n / c_int, for the index estimate
     uint32_t thr[64];
     uint32_t lut[64];
 };

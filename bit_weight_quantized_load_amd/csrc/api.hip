@@ -426,7 +426,7 @@ int run_gemm_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t 
         return QW_ERR_WORKSPACE;
     return hip_status(qw::launch_gemm_w4a8(X, (int)M, (int)N, (int)K,
                                            static_cast<const uint8_t*>(Wq), w_scale, Y, workspace,
-                                           nw, mb, nbw, static_cast<hipStream_t>(stream)));
+                                           nw, mb, nbw, device_cus(), static_cast<hipStream_t>(stream)));
 }
 
 int run_gemm_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, int64_t M,

@@ -21,6 +21,10 @@
 // two steps ahead.  Workgroups that share a slice of weights (different blocks of X)
 // are placed on one XCD so that its L2 serves the repeats.
 //
+// The balanced W4A8 kernel (K up to 4096, the default up to 16 rows of X) splits the
+// work differently: one workgroup per CU, each with an even share of the row groups cut
+// into (step, block) units that its waves take in contiguous runs (see its comment).
+//
 // W4A8: X is quantized once per call into the workspace by k_quant_act_mfma (the same
 // per-row scale and codes as quant_act_i8) in B-operand order.  An INT4 operand of 16 k
 // is 8 bytes of nibbles presented as 16 * q (nibble moved to the high half of its
@@ -31,6 +35,8 @@
 // W8A16: X (f16) is staged from its row-major input; the INT8 weights are cast to f16
 // exactly in registers (the byte-permute cast of the GEMV) and the per-channel scale
 // multiplies the fp32 sum once.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -290,50 +296,92 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8(MfmaW4A8Args p)
     }
 }
 
-// The same linear with all of the workgroup's X codes resident in LDS (one block of 16
-// rows, K up to 4096: at most 64 KB): X is copied in once, behind the first two steps'
-// weight loads, and the steps then stream weights only, with no barrier and no X loads.
+// Largest X code slice a balanced workgroup keeps in LDS: K up to 4096.
 constexpr int kXAllMaxBytes = 64 * 1024;
 
-template <int NW, int NBW>
-__global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_xall(MfmaW4A8Args p)
+// The same linear with the work balanced over the CUs, for K up to 4096.  Workgroup
+// (b, mb) takes block mb of 16 rows of X (blockIdx.y) and a contiguous run of row groups
+// (per or per + 1 of them; one workgroup per CU and block of X), i.e. nb output blocks
+// of 16 rows (the last one partial: rows past the run read zeros) and T = nb * CG
+// (512-k step, block) units in step-major order, so that consecutive units share
+// their X operands.  Wave w takes units [w T / NW, (w + 1) T / NW), at most U of them,
+// in a fully unrolled software pipeline: the weights of unit u + 1 are requested just
+// before unit u is multiplied.  (Requesting many units ahead was measured slower: a
+// wave stalls in its requests while the CU's queue is full, and the units left when
+// the stream ends are multiplied one after another.)  Every wave first requests its
+// share of the block's X codes and of the scales, and only after an issue barrier its
+// first unit of weights, so that no X load queues behind another wave's weights.  The
+// X codes go to LDS; each unit's four tiles are regrouped through the wave's LDS tile
+// area into A operands and multiplied against them, and the unit's int32 sums are
+// added into the workgroup's LDS totals (integer adds: exact in any order).  After one
+// more barrier the workgroup writes its outputs, consecutive threads on consecutive n.
+constexpr int kBalMaxBlocks = 40;      // output blocks per workgroup (LDS totals)
+constexpr int kBalSumPitch = 17;       // int32 per row of m in the LDS totals
+
+template <int NW, int U>
+__global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
 {
     constexpr int kThreads = 64 * NW;
     constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
-    constexpr int kWT = 4 * NBW;
-    extern __shared__ uint8_t s_mem[];  // X [KS steps][1 KB], then per wave kWT padded tiles
+    constexpr int kScales = 4 * 4 * kBalMaxBlocks;       // row scales of the workgroup
+    constexpr int kSP = (kScales + kThreads - 1) / kThreads;
+    // LDS: X [CG steps][8 KB], per wave 4 padded tiles, the int32 totals
+    // [nbmax][16 m][17], the row scales and the 16 activation scales
+    extern __shared__ uint8_t s_mem[];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 4, r = lane & 15;
-    const int CG = p.cg, KS = p.ks, MG = p.mgroups;
-    const int blk = xcd_block(blockIdx.x, gridDim.x);
-    const int mg = blk % MG, nb = blk / MG;  // mg: the block of 16 rows of X
-    const int rgw = (nb * NW + wave) * kWT;
-    const int nrg_w = max(0, min(kWT, p.nrg - rgw));
-    const rsrc_t wres =
-        make_rsrc(p.Wq + (size_t)min(rgw, p.nrg) * CG * 1024u, (uint32_t)(nrg_w * CG) * 1024u);
-    const rsrc_t xres = make_rsrc(p.Xp + (size_t)mg * KS * 1024u, (uint32_t)KS * 1024u);
+    const int CG = p.cg, KS = p.ks;
+    const int b = blockIdx.x, mb = blockIdx.y;
+    const int rg0 = min(b * p.per + min(b, p.rem), p.nrg);
+    const int nrg_b = max(0, min(p.per + (b < p.rem ? 1 : 0), p.nrg - rg0));
+    const int nb = max(1, (nrg_b + 3) >> 2);
+    const int T = nb * CG;
+    const int u0 = (wave * T) / NW, u1 = ((wave + 1) * T) / NW;
+    const int n0 = 4 * rg0;
+    const int nrows = max(0, min(4 * nrg_b, p.N - n0));
+    const int mv = min(p.M - 16 * mb, 16);  // live rows of this block of X
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_b * CG) * 1024u);
+    const rsrc_t xres = make_rsrc(p.Xp + (size_t)mb * KS * 1024u, (uint32_t)KS * 1024u);
+    const rsrc_t sres = make_rsrc(p.w_scale + n0, (uint32_t)nrows * 4u);
+    const rsrc_t ares = make_rsrc(p.a_scale + 16 * mb, (uint32_t)mv * 4u);
     const int xbytes = CG * 8 * 1024;  // whole 512-k steps; past K the loads read zeros
     uint8_t* s_x = s_mem;
-    uint8_t* s_w = s_mem + xbytes + wave * kWT * kW4TilePitch;
+    uint8_t* s_w = s_mem + xbytes + wave * 4 * kW4TilePitch;
+    int* s_sum = reinterpret_cast<int*>(s_mem + xbytes + NW * 4 * kW4TilePitch);
+    float* s_sc = reinterpret_cast<float*>(s_sum + p.nbmax * 16 * kBalSumPitch);
+    float* s_a = s_sc + 4 * 4 * p.nbmax;
 
-    uint4 w0[kWT], w1[kWT], w2[kWT];
-#define QW_LOADW(WB, C)                                                                          \
-    _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                           \
-        WB[i_] = load16_stream(wres, (C) < CG ? (uint32_t)(i_ * CG + (C)) * 1024u + (uint32_t)lane * 16u \
-                                              : 0x80000000u);
-    // X first (every piece of the workgroup's block; pieces past the block read zeros),
-    // then the weights of steps 0 and 1; storing X waits for X alone
+    // (step, block) of the wave's unit u, step-major: c = (u0 + u) / nb
+    const int c0 = u0 / nb, blk0 = u0 - c0 * nb;
+    uint4 wb[U][4];
+    // the four tiles of unit u (zeros past the wave's run and past the workgroup's rows)
+#define QW_LOADU(U_)                                                                             \
+    {                                                                                            \
+        const int q_ = blk0 + (U_);                                                              \
+        const int c_ = c0 + q_ / nb, blk_ = q_ % nb;                                             \
+        const bool live_ = u0 + (U_) < u1;                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                         \
+            wb[U_][i_] = load16_stream(wres, live_ ? (uint32_t)((4 * blk_ + i_) * CG + c_) * 1024u + \
+                                                         (uint32_t)lane * 16u                    \
+                                                   : 0x80000000u);                               \
+    }
+
     uint4 xr[kXP];
 #pragma unroll
     for (int v = 0; v < kXP; ++v) {
         const int pc = v * kThreads + tid;
         xr[v] = load16(xres, pc * 16 < xbytes ? (uint32_t)pc * 16u : 0x80000000u);
     }
-    QW_LOADW(w0, 0);
-    QW_LOADW(w1, 1);
+    uint32_t sr[kSP];
+#pragma unroll
+    for (int v = 0; v < kSP; ++v)
+        sr[v] = load4(sres, (uint32_t)(v * kThreads + tid) * 4u);
+    const uint32_t ar = load4(ares, (uint32_t)(tid & 15) * 4u);
+    issue_barrier();
+    QW_LOADU(0);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int v = 0; v < kXP; ++v) {
@@ -341,66 +389,67 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_xall(MfmaW4A8Args p)
         if (pc * 16 < xbytes)
             *reinterpret_cast<uint4*>(s_x + (size_t)pc * 16) = xr[v];
     }
+#pragma unroll
+    for (int v = 0; v < kSP; ++v)
+        if (v * kThreads + tid < 4 * 4 * p.nbmax)
+            s_sc[v * kThreads + tid] = __uint_as_float(sr[v]);
+    if (tid < 16)
+        s_a[tid] = __uint_as_float(ar);
+    for (int e = tid; e < nb * 16 * kBalSumPitch; e += kThreads)
+        s_sum[e] = 0;
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
-    v4i acc[NBW];
-#pragma unroll
-    for (int b = 0; b < NBW; ++b)
-        acc[b] = v4i{0, 0, 0, 0};
     const int sub = lane >> 4, j = lane & 15;
+    // A operand of step s for lane (g, r): row r of the block = tile r / 4, tile row
+    // r % 4; 16 k = chunk 2 s + g / 2, half g % 2
     const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
-
-#define QW_STEP(WC, WN, C)                                                                       \
-    {                                                                                            \
-        QW_LOADW(WN, (C) + 2);                                                                   \
-        __builtin_amdgcn_sched_barrier(0);                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < kWT; ++i_)                                       \
-            *reinterpret_cast<uint4*>(s_w + i_ * kW4TilePitch + sub * kW4RowPitch + j * 16) = WC[i_]; \
-        const uint8_t* xb_ = s_x + (size_t)(C) * 8 * 1024;                                       \
-        _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
-        {                                                                                        \
-            const uint4 b4_ = *reinterpret_cast<const uint4*>(xb_ + (s_ * 64 + lane) * 16);      \
-            const v4i bo_ = {(int)b4_.x, (int)b4_.y, (int)b4_.z, (int)b4_.w};                     \
-            _Pragma("unroll") for (int b_ = 0; b_ < NBW; ++b_)                                   \
-            {                                                                                    \
-                const uint2 w_ = *reinterpret_cast<const uint2*>(s_w + b_ * 4 * kW4TilePitch + a_off + s_ * 32); \
-                const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),     \
-                                (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};    \
-                acc[b_] = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, bo_, acc[b_], 0, 0, 0);      \
-            }                                                                                    \
-        }                                                                                        \
-    }
-
-    int c = 0;
-    for (; c + 3 <= CG; c += 3) {
-        QW_STEP(w0, w2, c);
-        QW_STEP(w1, w0, c + 1);
-        QW_STEP(w2, w1, c + 2);
-    }
-    if (c < CG)
-        QW_STEP(w0, w2, c);
-    if (c + 1 < CG)
-        QW_STEP(w1, w0, c + 1);
-#undef QW_STEP
-#undef QW_LOADW
-
-    const rsrc_t sres = make_rsrc(p.w_scale, (uint32_t)p.N * 4u);
-    const int m = mg * 16 + r;
+    v4i bo[8];
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) {
-        const int n0 = 4 * rgw + 16 * b + 4 * g;
-        float sc[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            sc[i] = __uint_as_float(load4(sres, (uint32_t)(n0 + i) * 4u));
-        if (m < p.M) {
-            const float am = p.a_scale[m];
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U)
+            QW_LOADU(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int q = blk0 + u;
+        const int c = c0 + q / nb, blk = q % nb;
+        if (u0 + u < u1) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (n0 + i < p.N)
-                    p.Y[(size_t)m * p.N + n0 + i] = ((float)(acc[b][i] >> 4) * sc[i]) * am;
+                *reinterpret_cast<uint4*>(s_w + i * kW4TilePitch + sub * kW4RowPitch + j * 16) = wb[u][i];
+            if (u == 0 || blk == 0) {
+                // B operands of step c (the first unit, or a new step)
+                const uint8_t* xb = s_x + (size_t)c * 8 * 1024;
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const uint4 b4 = *reinterpret_cast<const uint4*>(xb + (s * 64 + lane) * 16);
+                    bo[s] = v4i{(int)b4.x, (int)b4.y, (int)b4.z, (int)b4.w};
+                }
+            }
+            v4i acc = v4i{0, 0, 0, 0};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const uint2 w = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
+                const v4i a = {(int)((w.x << 4) & 0xF0F0F0F0u), (int)(w.x & 0xF0F0F0F0u),
+                               (int)((w.y << 4) & 0xF0F0F0F0u), (int)(w.y & 0xF0F0F0F0u)};
+                acc = __builtin_amdgcn_mfma_i32_16x16x64_i8(a, bo[s], acc, 0, 0, 0);
+            }
+            // lane (g, r) holds D[n = 4 g + i][m = r] of block blk
+            int* dst = s_sum + (blk * 16 + r) * kBalSumPitch + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                __hip_atomic_fetch_add(dst + i, acc[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+#undef QW_LOADU
+    __syncthreads();
+
+    for (int m = 0; m < mv; ++m) {
+        const float am = s_a[m];
+        float* yrow = p.Y + (size_t)(16 * mb + m) * p.N + n0;
+        for (int nn = tid; nn < nrows; nn += kThreads) {
+            const int v = s_sum[((nn >> 4) * 16 + m) * kBalSumPitch + (nn & 15)];
+            yrow[nn] = ((float)(v >> 4) * s_sc[nn]) * am;
         }
     }
 }
@@ -584,20 +633,46 @@ hipError_t go_w4(const MfmaW4A8Args& p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int NW, int NBW>
-hipError_t go_w4_xall(const MfmaW4A8Args& p, hipStream_t st)
+template <int NW, int U>
+hipError_t go_w4_bal_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
 {
-    const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)NW * 4 * NBW * kW4TilePitch;
-    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_xall<NW, NBW>),
-                                          (size_t)kXAllMaxBytes + (size_t)NW * 4 * NBW * kW4TilePitch);
+    // once per kernel, before its first launch
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bal<NW, U>),
+                                          (size_t)kXAllMaxBytes + (size_t)NW * 4 * kW4TilePitch +
+                                              (size_t)kBalMaxBlocks * (16 * kBalSumPitch + 16) * 4 + 64);
     if (e != hipSuccess)
         return e;
-    const int64_t nblocks = ((int64_t)p.nrg + NW * 4 * NBW - 1) / (NW * 4 * NBW);
-    if (nblocks * p.mgroups > 0x7fffffff)
-        return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL((k_gemm_w4a8_xall<NW, NBW>), dim3((unsigned)(nblocks * p.mgroups)),
+    hipLaunchKernelGGL((k_gemm_w4a8_bal<NW, U>), dim3((unsigned)nwg, (unsigned)p.mbtot),
                        dim3(64 * NW), lds, st, p);
     return hipGetLastError();
+}
+
+// Units per wave the balanced kernel is built for.
+constexpr int kBalMaxUnits = 16;
+
+template <int NW>
+hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
+{
+    if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot > 65535)
+        return hipErrorInvalidValue;
+    // one workgroup per CU with at least four row groups each; more workgroups when a
+    // wave would take more than kBalMaxUnits units or the totals more than
+    // kBalMaxBlocks blocks
+    const int bmax = std::min(kBalMaxBlocks, kBalMaxUnits * NW / p.cg);
+    int nwg = std::max(1, std::min(cus, p.nrg / 4));
+    nwg = std::max(nwg, (p.nrg + 4 * bmax - 1) / (4 * bmax));
+    p.per = p.nrg / nwg;
+    p.rem = p.nrg % nwg;
+    p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 3) / 4;
+    p.mgroups = p.mbtot;
+    const int umax = (p.nbmax * p.cg + NW - 1) / NW;
+    const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)NW * 4 * kW4TilePitch +
+                       (size_t)p.nbmax * (16 * kBalSumPitch + 16) * 4 + 64;
+    if (umax <= 4)
+        return go_w4_bal_u<NW, 4>(p, nwg, lds, st);
+    if (umax <= 8)
+        return go_w4_bal_u<NW, 8>(p, nwg, lds, st);
+    return go_w4_bal_u<NW, 16>(p, nwg, lds, st);
 }
 
 template <int NW, int MB, int NBW>
@@ -626,7 +701,7 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
     if (bits == 4)
         return ((mb == 1 || mb == 2 || mb == 4) && !(nw == 4 && mb == 4 && nbw == 2) &&
                 !(nw == 8 && mb == 1 && nbw == 2)) ||
-               (mb == 0 && !(nw == 4 && nbw == 2));
+               (mb == 0 && nbw == 1);
     // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
     // rows would not fit the registers
     return (mb == 1 || mb == 2) && !(nw == 8 && nbw == 2);
@@ -634,14 +709,15 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
 
 void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
 {
-    // measured at K = 4096, N = 27392: W4A8 up to 16 rows with X resident in LDS and
-    // 8-wave workgroups (16.3 us against 17.1 us), then 8 waves and 2 or 4 blocks of X;
-    // W8A16 8 waves with 1 or 2 blocks
+    // measured at K = 4096, N = 27392: W4A8 up to 16 rows with the balanced kernel and
+    // 8-wave workgroups (14.3 us at 2 rows against 15.4 us for the streaming kernel,
+    // 7.9 against 11.7 us at N = 3584), then 8 waves and 2 or 4 blocks of X; W8A16 8
+    // waves with 1 or 2 blocks
     const int64_t mbtot = (M + 15) / 16;
     *nw = 8;
     *nbw = 1;
     if (bits == 4) {
-        if (mbtot == 1 && (K + 511) / 512 * 8192 <= 65536)
+        if (mbtot == 1 && (K + 511) / 512 * 8192 <= kXAllMaxBytes)
             *mb = 0;
         else
             *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
@@ -659,7 +735,7 @@ size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K)
 
 hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
                             const float* w_scale, float* Y, void* workspace, int nw, int mb,
-                            int nbw, hipStream_t st)
+                            int nbw, int cus, hipStream_t st)
 {
     const TileLayout L = tile_layout(4, N, K);
     const int mbtot = (M + 15) / 16, ks = (K + 63) / 64;
@@ -696,16 +772,11 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.nrg = L.nrg;
     p.ks = ks;
     p.mbtot = mbtot;
-    if (mb == 0) {  // X resident in LDS: one block of 16 rows per workgroup
-        if ((size_t)L.cg * 8 * 1024 > (size_t)kXAllMaxBytes)
-            return hipErrorInvalidValue;
-        p.mgroups = mbtot;
-        if (nw == 4 && nbw == 1)
-            return go_w4_xall<4, 1>(p, st);
-        if (nw == 8 && nbw == 1)
-            return go_w4_xall<8, 1>(p, st);
-        if (nw == 8 && nbw == 2)
-            return go_w4_xall<8, 2>(p, st);
+    if (mb == 0) {  // balanced: one block of 16 rows of X per workgroup, resident in LDS
+        if (nw == 8)
+            return go_w4_bal<8>(p, cus, st);
+        if (nw == 4)
+            return go_w4_bal<4>(p, cus, st);
         return hipErrorInvalidValue;
     }
     p.mgroups = (mbtot + mb - 1) / mb;

@@ -134,6 +134,9 @@ struct MfmaW4A8Args {
     int ks;       // 64-k steps = ceil(K / 64)
     int mbtot;    // 16-row blocks of X = ceil(M / 16)
     int mgroups;  // workgroups along M
+    // balanced variant: row groups per workgroup (the first rem get one more) and the
+    // most 16-row output blocks a workgroup holds
+    int per, rem, nbmax;
 };
 
 struct MfmaW8A16Args {
@@ -153,7 +156,7 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw);
 void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw);
 hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
                             const float* w_scale, float* Y, void* workspace, int nw, int mb,
-                            int nbw, hipStream_t st);
+                            int nbw, int cus, hipStream_t st);
 hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
                              const uint16_t* w_scale, uint16_t* Y, int nw, int mb, int nbw,
                              hipStream_t st);

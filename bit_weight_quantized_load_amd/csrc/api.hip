@@ -440,7 +440,7 @@ int run_gemm_w8a16(const uint16_t* X, const void* Wq, const uint16_t* w_scale, i
         return QW_ERR_ALIGN;
     return hip_status(qw::launch_gemm_w8a16(X, (int)M, (int)N, (int)K,
                                             static_cast<const uint8_t*>(Wq), w_scale, Y, nw, mb,
-                                            nbw, static_cast<hipStream_t>(stream)));
+                                            nbw, device_cus(), static_cast<hipStream_t>(stream)));
 }
 
 // ---- group-wise INT4 scales
@@ -889,6 +889,8 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
     if (!qw::mfma_shape_ok(8, nw, mb, nbw))
+        return QW_ERR_TILING;
+    if (mb == 0 && (M > 16 || (K + 511) / 512 > 8))  // balanced: 16 rows, K up to 4096
         return QW_ERR_TILING;
     return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, nw, mb, nbw, stream);
 }

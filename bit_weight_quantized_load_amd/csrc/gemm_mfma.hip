@@ -444,13 +444,11 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
 #undef QW_LOADU
     __syncthreads();
 
-    for (int m = 0; m < mv; ++m) {
-        const float am = s_a[m];
-        float* yrow = p.Y + (size_t)(16 * mb + m) * p.N + n0;
-        for (int nn = tid; nn < nrows; nn += kThreads) {
-            const int v = s_sum[((nn >> 4) * 16 + m) * kBalSumPitch + (nn & 15)];
-            yrow[nn] = ((float)(v >> 4) * s_sc[nn]) * am;
-        }
+    // outputs (m, nn), independent across threads
+    for (int e = tid; e < mv * nrows; e += kThreads) {
+        const int m = e / nrows, nn = e - m * nrows;
+        const int v = s_sum[((nn >> 4) * 16 + m) * kBalSumPitch + (nn & 15)];
+        p.Y[(size_t)(16 * mb + m) * p.N + n0 + nn] = ((float)(v >> 4) * s_sc[nn]) * s_a[m];
     }
 }
 
@@ -605,6 +603,125 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w8a16(MfmaW8A16Args p)
     }
 }
 
+// The W8A16 linear for one block of 16 rows of X (M <= 16, K up to 4096), balanced
+// over the CUs like the W4A8 kernel above, but with one wave per 512-k step: wave w of
+// a workgroup of CG waves takes step w of every output block of the workgroup's run of
+// row groups, so that its X operands (16 rows x 512 k of f16, 16 KB) stay in its
+// registers for all its units; a unit is one block of 16 rows (eight INT8 tiles, 8 KB).
+// The same one-unit-ahead pipeline and issue order as there; the tiles are regrouped
+// through the wave's LDS tile area and cast exactly to f16.  Each wave stores its fp32
+// partial sums per block in LDS, and the epilogue adds the CG partials of an output in
+// step order (deterministic), scales once and rounds to f16.
+constexpr int kW8BalMaxBlocks = 8;   // output blocks per workgroup
+constexpr int kW8BalMaxSteps = 8;    // waves per workgroup (K <= 4096)
+
+template <int U>
+__global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A16Args p)
+{
+    // LDS: per wave 8 padded tiles, then the fp32 partials [CG][nbmax][16 m][17] and
+    // the row scales
+    extern __shared__ uint8_t s_mem[];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = the 512-k step
+    const int nthreads = (int)blockDim.x;
+    const int g = lane >> 4, r = lane & 15;
+    const int CG = p.cg, M = p.M, K = p.K;
+    const int b = blockIdx.x;
+    const int rg0 = min(b * p.per + min(b, p.rem), p.nrg);
+    const int nrg_b = max(0, min(p.per + (b < p.rem ? 1 : 0), p.nrg - rg0));
+    const int nb = min(U, (nrg_b + 7) >> 3);
+    const int n0 = 2 * rg0;
+    const int nrows = max(0, min(2 * nrg_b, p.N - n0));
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_b * CG) * 1024u);
+    const rsrc_t xres = make_rsrc(p.X, (uint32_t)M * (uint32_t)K * 2u);
+    const rsrc_t sres = make_rsrc(p.w_scale + n0, (uint32_t)nrows * 2u);
+    uint8_t* s_w = s_mem + wave * 8 * kW8TilePitch;
+    float* s_part = reinterpret_cast<float*>(s_mem + kW8BalMaxSteps * 8 * kW8TilePitch);
+    float* s_sc = s_part + CG * p.nbmax * 16 * 17;
+
+    // X operands of step w: substep s (32 k), lane (g, r) -> X[r][512 w + 32 s + 8 g ..+7]
+    uint4 xb[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) {
+        const int k = 512 * wave + 32 * s + 8 * g;
+        xb[s] = load16(xres, r < M && k < K ? (uint32_t)(r * K + k) * 2u : 0x80000000u);
+    }
+    // the workgroup's row scales (at most 16 nbmax <= 128 rows, two per thread)
+    const uint32_t sr0 = load2(sres, (uint32_t)tid * 2u);
+    const uint32_t sr1 = load2(sres, (uint32_t)(tid + nthreads) * 2u);
+    uint4 wb[U][8];
+    // the eight tiles of unit u: block u of the run at step w (zeros past the run)
+#define QW_LOADU8(U_)                                                                            \
+    _Pragma("unroll") for (int i_ = 0; i_ < 8; ++i_)                                             \
+        wb[U_][i_] = load16_stream(wres, (U_) < nb ? (uint32_t)((8 * (U_) + i_) * CG + wave) * 1024u + \
+                                                         (uint32_t)lane * 16u                    \
+                                                   : 0x80000000u);
+    issue_barrier();
+    QW_LOADU8(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < 16 * p.nbmax)
+        s_sc[tid] = __half2float(__ushort_as_half((uint16_t)sr0));
+    if (tid + nthreads < 16 * p.nbmax)
+        s_sc[tid + nthreads] = __half2float(__ushort_as_half((uint16_t)sr1));
+    v8h bo[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s)
+        bo[s] = __builtin_bit_cast(v8h, xb[s]);
+
+    const int sub = lane >> 5, j = lane & 31;
+    // A operand of substep s for lane (g, r): row r of the block = tile r / 2, tile row
+    // r % 2; k = 32 s + 8 g .. + 7 = chunk 2 s + g / 2, half g % 2
+    const int a_off = (r >> 1) * kW8TilePitch + (r & 1) * kW8RowPitch + (g >> 1) * 16 + (g & 1) * 8;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) {
+            QW_LOADU8(u + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < nb) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                *reinterpret_cast<uint4*>(s_w + i * kW8TilePitch + sub * kW8RowPitch + j * 16) = wb[u][i];
+            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 16; ++s) {
+                const uint2 w = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
+                half2_t h0, h1, h2, h3;
+                cast4(w.x, h0, h1);
+                cast4(w.y, h2, h3);
+                const v8h a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bo[s], acc, 0, 0, 0);
+            }
+            // lane (g, r) holds D[n = 4 g + i][m = r] of block u
+            float* dst = s_part + ((wave * p.nbmax + u) * 16 + r) * 17 + 4 * g;
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dst[i] = acc[i];
+        }
+    }
+#undef QW_LOADU8
+    __syncthreads();
+
+    // outputs (m, nn), independent across threads: the CG partials in step order,
+    // times the row scale, rounded to f16
+    const int nout = min(M, 16) * nrows;
+    for (int e = tid; e < nout; e += nthreads) {
+        const int m = e / nrows, nn = e - m * nrows;
+        const float* src = s_part + ((nn >> 4) * 16 + m) * 17 + (nn & 15);
+        float pv[kW8BalMaxSteps];
+#pragma unroll
+        for (int c = 0; c < kW8BalMaxSteps; ++c)
+            pv[c] = c < CG ? src[c * p.nbmax * 16 * 17] : 0.0f;
+        float v = pv[0];
+#pragma unroll
+        for (int c = 1; c < kW8BalMaxSteps; ++c)
+            if (c < CG)
+                v += pv[c];
+        p.Y[(size_t)m * p.N + n0 + nn] = __half_as_ushort(__float2half_rn(v * s_sc[nn]));
+    }
+}
+
 template <int NW, int MB, int NBW>
 size_t lds_w4() { return (size_t)2 * MB * 8 * 1024 + (size_t)NW * 4 * NBW * kW4TilePitch; }
 
@@ -690,6 +807,38 @@ hipError_t go_w8(const MfmaW8A16Args& p, hipStream_t st)
     return hipGetLastError();
 }
 
+template <int U>
+hipError_t go_w8_bal_u(const MfmaW8A16Args& p, int nwg, size_t lds, hipStream_t st)
+{
+    static const hipError_t e =
+        allow_lds(reinterpret_cast<const void*>(k_gemm_w8a16_bal<U>),
+                  (size_t)kW8BalMaxSteps * 8 * kW8TilePitch +
+                      (size_t)kW8BalMaxSteps * kW8BalMaxBlocks * 16 * 17 * 4 + 16 * kW8BalMaxBlocks * 4);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((k_gemm_w8a16_bal<U>), dim3((unsigned)nwg), dim3(64 * p.cg), lds, st, p);
+    return hipGetLastError();
+}
+
+hipError_t go_w8_bal(MfmaW8A16Args p, int cus, hipStream_t st)
+{
+    if (p.M > 16 || p.cg > kW8BalMaxSteps)
+        return hipErrorInvalidValue;
+    // one workgroup per CU with at least one block (8 row groups of 2 rows) each, at
+    // most kW8BalMaxBlocks blocks
+    int nwg = std::max(1, std::min(cus, p.nrg / 8));
+    nwg = std::max(nwg, (p.nrg + 8 * kW8BalMaxBlocks - 1) / (8 * kW8BalMaxBlocks));
+    p.per = p.nrg / nwg;
+    p.rem = p.nrg % nwg;
+    p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 7) / 8;
+    p.mgroups = 1;
+    const size_t lds = (size_t)kW8BalMaxSteps * 8 * kW8TilePitch +
+                       (size_t)p.cg * p.nbmax * 16 * 17 * 4 + (size_t)16 * p.nbmax * 4;
+    if (p.nbmax <= 4)
+        return go_w8_bal_u<4>(p, nwg, lds, st);
+    return go_w8_bal_u<8>(p, nwg, lds, st);
+}
+
 }  // namespace
 
 bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
@@ -703,8 +852,9 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
                 !(nw == 8 && mb == 1 && nbw == 2)) ||
                (mb == 0 && nbw == 1);
     // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
-    // rows would not fit the registers
-    return (mb == 1 || mb == 2) && !(nw == 8 && nbw == 2);
+    // rows would not fit the registers.  mb 0: the balanced kernel (one wave per 512-k
+    // step), nw 8 and nbw 1 only
+    return ((mb == 1 || mb == 2) && !(nw == 8 && nbw == 2)) || (mb == 0 && nw == 8 && nbw == 1);
 }
 
 void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
@@ -721,6 +871,8 @@ void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* n
             *mb = 0;
         else
             *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
+    } else if (mbtot == 1 && (K + 511) / 512 <= 8) {
+        *mb = 0;
     } else {
         *mb = mbtot >= 2 ? 2 : 1;
     }
@@ -791,7 +943,7 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
 
 hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
                              const uint16_t* w_scale, uint16_t* Y, int nw, int mb, int nbw,
-                             hipStream_t st)
+                             int cus, hipStream_t st)
 {
     const TileLayout L = tile_layout(8, N, K);
     const int mbtot = (M + 15) / 16;
@@ -805,6 +957,8 @@ hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8
     p.K = K;
     p.cg = L.cg;
     p.nrg = L.nrg;
+    if (mb == 0)
+        return nw == 8 && nbw == 1 ? go_w8_bal(p, cus, st) : hipErrorInvalidValue;
     p.mgroups = (mbtot + mb - 1) / mb;
 #define QW_GO(NW_, MB_, NBW_)                                                                    \
     if (nw == NW_ && mb == MB_ && nbw == NBW_)                                                   \

@@ -147,6 +147,7 @@ struct MfmaW8A16Args {
     int M, N, K;
     int cg, nrg;
     int mgroups;
+    int per, rem, nbmax;  // balanced variant (as in MfmaW4A8Args)
 };
 
 size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K);
@@ -159,7 +160,7 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
                             int nbw, int cus, hipStream_t st);
 hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
                              const uint16_t* w_scale, uint16_t* Y, int nw, int mb, int nbw,
-                             hipStream_t st);
+                             int cus, hipStream_t st);
 
 hipError_t launch_pack_w4(const float* W, int N, int K, uint8_t* Wq, float* s, int* flag,
                           hipStream_t st);

@@ -227,7 +227,9 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
    W8A16), nbw blocks of 16 output rows per wave (1 or 2; not 2 with nw 8 and mb 1 for
    W4A8, not 2 with nw 8 for W8A16).  W4A8 also takes mb = 0 (nbw 1, K <= 4096): the
    balanced kernel, one workgroup per CU and block of 16 rows of X, with that block's
-   activation codes resident in on-chip memory.  Rows of X are padded to a multiple of 16 with
+   activation codes resident in on-chip memory.  W8A16 takes mb = 0 too (nw 8, nbw 1,
+   M <= 16, K <= 4096): the balanced kernel with one wave per 512-k step, whose f16 X
+   operands stay in registers.  Rows of X are padded to a multiple of 16 with
    zeros.  The W4A8 one needs a workspace of qw_workspace_bytes(2, M, N, K) bytes (else
    QW_ERR_WORKSPACE).  Results do not depend on the launch shape; the W4A8 outputs equal
    gemv_w4a8's bit for bit.  QW_ERR_TILING for an invalid shape. */

@@ -309,8 +309,9 @@ def test_matrix_core_kernels_every_launch_shape(M, N, K):
 # 2 and 16 rows (its default range), ragged N (a partial row group and a partial block
 # of 16 output rows), tiny N (fewer row groups than waves), 16 units per wave (N = 40000)
 # and more workgroups than CUs (N = 70000, K = 4096), K not a multiple of 512
-BALANCED_SHAPES = [(2, 27392, 4096), (16, 27392, 4096), (5, 4101, 3584), (16, 37, 96),
-                   (3, 40000, 4096), (2, 70000, 4096), (7, 1000, 1056)]
+BALANCED_SHAPES = [(2, 27392, 4096), (4, 27392, 4096), (16, 27392, 4096), (5, 4101, 3584),
+                   (16, 37, 96), (8, 37, 96), (3, 40000, 4096), (2, 70000, 4096),
+                   (7, 1000, 1056), (1, 512, 4064), (6, 300, 544)]
 
 
 @pytest.mark.parametrize("M,N,K", BALANCED_SHAPES)
@@ -323,12 +324,38 @@ def test_balanced_matrix_core_kernel_matches_oracle(M, N, K):
     ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
     Xd = dev(X)
     ws = qw.make_workspace("w4a8", M, N, K)
+    # the int32 sums are exact in any order: the streaming kernel gives the same bits
+    Yg = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 1, 1, workspace=ws))
+    assert_w4a8_close(Yg, ref["Y"])
     for nw in (8, 4):
         Y = host(qw.gemm_w4a8_mfma(Xd, Wq, s, nw, 0, 1, workspace=ws))
-        assert_w4a8_close(Y, ref["Y"])
-        # the int32 sums are exact in any order: the streaming kernel gives the same bits
-        Yg = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 1, 1, workspace=ws))
         assert np.array_equal(Y.view(np.uint32), Yg.view(np.uint32)), nw
+
+
+# The balanced W8A16 matrix-core kernel (mb = 0, one wave per 512-k step): the 4096 ->
+# 27392 linear at 3 and 16 rows, ragged N, tiny N, one step (K = 512, more workgroups
+# than CUs), K not a multiple of 512
+W8_BALANCED_SHAPES = [(3, 27392, 4096), (16, 27392, 4096), (5, 4100, 3584), (16, 38, 96),
+                      (7, 1000, 1056), (4, 40000, 512), (8, 600, 544)]
+
+
+@pytest.mark.parametrize("M,N,K", W8_BALANCED_SHAPES)
+def test_balanced_w8a16_matrix_core_kernel_matches_oracle(M, N, K):
+    say("balanced w8a16 mfma", M, N, K)
+    W = wl.weights(700 + M, 1, N, K, outlier_rows=True)
+    X16 = wl.activations(700 + M, 2, M, K, outlier_channels=4).astype(np.float16)
+    X16[M // 2, : K // 3] = 0
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    Xd = dev(X16)
+    y = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 1))
+    assert rel_l2(y, y64) <= W8A16_RL2
+    assert np.all(np.isfinite(y.astype(np.float32)))
+    ys = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 1, 1))
+    assert rel_l2(ys, y64) <= W8A16_RL2
+    # the default path at these rows is the balanced kernel
+    yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
+    assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 
 
 def test_skinny_gemm_workspace_reuse_and_sizes():

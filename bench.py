@@ -251,6 +251,68 @@ def index_softmax_measurement(qw, torch, launches):
             "GB/s": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
 
 
+PEAK_MFMA_I8_TOPS = 5000.0   # dense int8 matrix cores
+PEAK_MFMA_F16_TFLOPS = 2500.0  # dense f16 matrix cores
+
+
+def skinny_sweep_measurement(qw, wl, torch, launches):
+    """The skinny-GEMM sweep: gemv_w4a8 and gemv_w8a16 (default paths: the GEMV kernels
+    at M = 1, the matrix-core kernels above) on ChatGLM2's 4096 -> 27392 linear for each
+    M of the sweep, weight copies rotated past the cache.  Reports time, HBM bandwidth
+    of the algorithmic bytes, and for M > 1 the matrix-core rate against the dense peak
+    (int8 for W4A8, f16 for W8A16)."""
+    c = wl.SKINNY
+    K, N = c["K"], c["N"]
+    W = torch.from_numpy(wl.weights(c["seed"], 1, N, K, outlier_rows=True)).cuda()
+    Wq4, s4 = qw.quantize_pack_w4(W)
+    Wq8, s8 = qw.quantize_pack_w8(W)
+    del W
+    R = max(2, math.ceil(ROTATE_BYTES / (Wq4.numel() + Wq8.numel())))
+    copies = [(Wq4, s4, Wq8, s8)] + [(Wq4.clone(), s4.clone(), Wq8.clone(), s8.clone())
+                                     for _ in range(R - 1)]
+    n = max(10, min(40, launches // 25))
+    out = {"workload": c["workload"], "K": K, "N": N, "launches": n, "weight_copies_rotated": R}
+
+    def timed(fn):
+        fn(0)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        del g
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    for M in c["Ms"]:
+        X = torch.from_numpy(wl.activations(c["seed"], 2, M, K, outlier_channels=4)).cuda()
+        X16 = X.half()
+        Y4 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+        Y8 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+        ws4 = qw.make_workspace("w4a8", M, N, K)
+        t4 = timed(lambda i: qw.gemv_w4a8(X, copies[i % R][0], copies[i % R][1], workspace=ws4, out=Y4))
+        t8 = timed(lambda i: qw.gemv_w8a16(X16, copies[i % R][2], copies[i % R][3], out=Y8))
+        row = {}
+        for key, t, b, peak in (("w4a8", t4, bytes_w4a8(M, N, K), PEAK_MFMA_I8_TOPS),
+                                ("w8a16", t8, bytes_w8a16(M, N, K), PEAK_MFMA_F16_TFLOPS)):
+            tf = 2.0 * M * N * K / t / 1e6
+            row[key] = {"us": round(t, 3), "algo_bytes": b, "GB/s": round(b / t / 1e3, 1),
+                        "frac_of_hbm": round(b / t / 1e3 / PEAK_HBM_GBS, 4),
+                        "T(FL)OP/s": round(tf, 2), "frac_of_mfma": round(tf / peak, 4)}
+        out["M=%d" % M] = row
+        del X, X16, Y4, Y8, ws4
+    del copies, Wq4, s4, Wq8, s8
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -261,6 +323,8 @@ def main():
     ap.add_argument("--no-chain", action="store_true",
                     help="skip the 28-layer decode-step chain measurement")
     ap.add_argument("--chain-replays", type=int, default=20)
+    ap.add_argument("--no-skinny", action="store_true",
+                    help="skip the skinny-GEMM sweep (K = 4096, N = 27392, M = 1 .. 512)")
     ap.add_argument("--no-index-softmax", action="store_true",
                     help="skip the IndexSoftmax measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -433,6 +497,7 @@ def main():
     del g_step, g4, g8, g4g, g16, g4f, copies, copies_g, copies16, W16
     torch.cuda.empty_cache()
     isoft = None if args.no_index_softmax else index_softmax_measurement(qw, torch, K_steps)
+    skinny = None if args.no_skinny else skinny_sweep_measurement(qw, wl, torch, K_steps)
     chain_info = None
     if not args.no_chain:
         chain_info = chain_measurement(qw, wl, torch, args.chain_replays)
@@ -451,6 +516,7 @@ def main():
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
         "decode_chain": chain_info,
         "index_softmax": isoft,
+        "skinny_sweep": skinny,
     }
     print(json.dumps(line), flush=True)
 

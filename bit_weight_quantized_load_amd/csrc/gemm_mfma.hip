@@ -21,9 +21,10 @@
 // two steps ahead.  Workgroups that share a slice of weights (different blocks of X)
 // are placed on one XCD so that its L2 serves the repeats.
 //
-// The balanced W4A8 kernel (K up to 4096, the default up to 16 rows of X) splits the
-// work differently: one workgroup per CU, each with an even share of the row groups cut
-// into (step, block) units that its waves take in contiguous runs (see its comment).
+// The balanced kernels (K up to 4096; the defaults up to 16 rows of X, and for W4A8 up
+// to 64 rows where measured faster) split the work differently: one workgroup per CU,
+// each with an even share of the row groups cut into units that its waves take in
+// contiguous runs (see their comments).
 //
 // W4A8: X is quantized once per call into the workspace by k_quant_act_mfma (the same
 // per-row scale and codes as quant_act_i8) in B-operand order.  An INT4 operand of 16 k
@@ -452,6 +453,187 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
     }
 }
 
+// The balanced W4A8 kernel for 17 to 64 rows of X (2 to 4 blocks of 16), K up to 4096.
+// The same workgroup split, units and pipeline as k_gemm_w4a8_bal for block 0 of X;
+// each wave also keeps the regrouped A operands of its units in registers (16 VGPRs a
+// unit), so that blocks 1 .. MBT-1 of X are multiplied against them afterwards without
+// reading the weights again: block by block, the workgroup stores that block's codes
+// in LDS (the next block's are requested before the multiplies), and the int32 sums go
+// to the LDS totals of that block.
+constexpr int kBalmMaxBlocks = 8;  // output blocks per workgroup
+
+template <int U>
+__global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
+{
+    constexpr int NW = 8, kThreads = 512;
+    constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
+    // LDS: X [CG steps][8 KB] of one block, per wave 4 padded tiles, the int32 totals
+    // [MBT][nbmax][16 m][17], the row scales and the 64 activation scales
+    extern __shared__ uint8_t s_mem[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = lane >> 4, r = lane & 15;
+    const int CG = p.cg, KS = p.ks, MBT = p.mbtot;
+    const int b = blockIdx.x;
+    const int rg0 = min(b * p.per + min(b, p.rem), p.nrg);
+    const int nrg_b = max(0, min(p.per + (b < p.rem ? 1 : 0), p.nrg - rg0));
+    const int nb = max(1, (nrg_b + 3) >> 2);
+    const int T = nb * CG;
+    const int u0 = (wave * T) / NW, u1 = ((wave + 1) * T) / NW;
+    const int n0 = 4 * rg0;
+    const int nrows = max(0, min(4 * nrg_b, p.N - n0));
+    const int bsum = p.nbmax * 16 * kBalSumPitch;  // int32 totals of one block of X
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_b * CG) * 1024u);
+    const rsrc_t sres = make_rsrc(p.w_scale + n0, (uint32_t)nrows * 4u);
+    const rsrc_t ares = make_rsrc(p.a_scale, (uint32_t)p.M * 4u);
+    const int xbytes = CG * 8 * 1024;  // whole 512-k steps; past K the loads read zeros
+    uint8_t* s_x = s_mem;
+    uint8_t* s_w = s_mem + xbytes + wave * 4 * kW4TilePitch;
+    int* s_sum = reinterpret_cast<int*>(s_mem + xbytes + NW * 4 * kW4TilePitch);
+    float* s_sc = reinterpret_cast<float*>(s_sum + MBT * bsum);
+    float* s_a = s_sc + 4 * 4 * p.nbmax;
+
+    const int c0 = u0 / nb, blk0 = u0 - c0 * nb;
+    uint4 wb[U][4];
+#define QW_LOADU(U_)                                                                             \
+    {                                                                                            \
+        const int q_ = blk0 + (U_);                                                              \
+        const int c_ = c0 + q_ / nb, blk_ = q_ % nb;                                             \
+        const bool live_ = u0 + (U_) < u1;                                                       \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                         \
+            wb[U_][i_] = load16_stream(wres, live_ ? (uint32_t)((4 * blk_ + i_) * CG + c_) * 1024u + \
+                                                         (uint32_t)lane * 16u                    \
+                                                   : 0x80000000u);                               \
+    }
+    // X codes of block MB_ (zeros past K and past M)
+#define QW_LOADXB(XR, MB_)                                                                       \
+    {                                                                                            \
+        const rsrc_t xres_ = make_rsrc(p.Xp + (size_t)(MB_) * KS * 1024u, (uint32_t)KS * 1024u); \
+        _Pragma("unroll") for (int v_ = 0; v_ < kXP; ++v_)                                       \
+        {                                                                                        \
+            const int pc_ = v_ * kThreads + tid;                                                 \
+            XR[v_] = load16(xres_, pc_ * 16 < xbytes ? (uint32_t)pc_ * 16u : 0x80000000u);       \
+        }                                                                                        \
+    }
+#define QW_STOREXB(XR)                                                                           \
+    _Pragma("unroll") for (int v_ = 0; v_ < kXP; ++v_)                                           \
+    {                                                                                            \
+        const int pc_ = v_ * kThreads + tid;                                                     \
+        if (pc_ * 16 < xbytes)                                                                   \
+            *reinterpret_cast<uint4*>(s_x + (size_t)pc_ * 16) = XR[v_];                          \
+    }
+    // B operands of step C_ from LDS (the first unit of a wave, or a new step)
+#define QW_LOAD_BO(C_)                                                                           \
+    {                                                                                            \
+        const uint8_t* xb_ = s_x + (size_t)(C_) * 8 * 1024;                                      \
+        _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
+        {                                                                                        \
+            const uint4 b4_ = *reinterpret_cast<const uint4*>(xb_ + (s_ * 64 + lane) * 16);      \
+            bo[s_] = v4i{(int)b4_.x, (int)b4_.y, (int)b4_.z, (int)b4_.w};                         \
+        }                                                                                        \
+    }
+    // one unit's eight multiplies against bo; sums into SUM
+#define QW_UNIT_MFMA(U_, SUM)                                                                    \
+    {                                                                                            \
+        v4i acc_ = v4i{0, 0, 0, 0};                                                              \
+        _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
+        {                                                                                        \
+            const v4i bo_ = bo[s_];                                                              \
+            uint2 w_ = ua[U_][s_];                                                               \
+            /* opaque copy: keeps the unpack inside the loop over blocks of X (hoisted, the */  \
+            /* unpacked operands of every unit would not fit the registers) */                  \
+            asm volatile("" : "+v"(w_.x), "+v"(w_.y));                                           \
+            const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),         \
+                            (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};        \
+            acc_ = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, bo_, acc_, 0, 0, 0);                \
+        }                                                                                        \
+        int* dst_ = (SUM) + (blk * 16 + r) * kBalSumPitch + 4 * g;                               \
+        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                         \
+            __hip_atomic_fetch_add(dst_ + i_, acc_[i_], __ATOMIC_RELAXED,                        \
+                                   __HIP_MEMORY_SCOPE_WORKGROUP);                                \
+    }
+
+    uint4 xr[kXP];
+    QW_LOADXB(xr, 0);
+    const uint32_t sr = load4(sres, (uint32_t)tid * 4u);
+    const uint32_t ar = load4(ares, (uint32_t)(tid & 63) * 4u);
+    issue_barrier();
+    QW_LOADU(0);
+    __builtin_amdgcn_sched_barrier(0);
+    QW_STOREXB(xr);
+    if (tid < 4 * 4 * p.nbmax)
+        s_sc[tid] = __uint_as_float(sr);
+    if (tid < 64)
+        s_a[tid] = __uint_as_float(ar);
+    for (int e = tid; e < MBT * bsum; e += kThreads)
+        s_sum[e] = 0;
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+
+    const int sub = lane >> 4, j = lane & 15;
+    // A operand of step s for lane (g, r): row r of the block = tile r / 4, tile row
+    // r % 4; 16 k = chunk 2 s + g / 2, half g % 2
+    const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
+    v4i bo[8];
+    uint2 ua[U][8];  // regrouped A operands of every unit of the wave
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U)
+            QW_LOADU(u + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        const int q = blk0 + u;
+        const int c = c0 + q / nb, blk = q % nb;
+        if (u0 + u < u1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                *reinterpret_cast<uint4*>(s_w + i * kW4TilePitch + sub * kW4RowPitch + j * 16) = wb[u][i];
+            if (u == 0 || blk == 0)
+                QW_LOAD_BO(c);
+#pragma unroll
+            for (int s = 0; s < 8; ++s)
+                ua[u][s] = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
+            QW_UNIT_MFMA(u, s_sum);
+        }
+    }
+#undef QW_LOADU
+
+    // blocks 1 .. MBT-1 of X against the A operands held in registers
+    QW_LOADXB(xr, 1);
+    for (int mb = 1; mb < MBT; ++mb) {
+        __syncthreads();  // every wave is done with the previous block's codes
+        QW_STOREXB(xr);
+        __syncthreads();
+        if (mb + 1 < MBT)
+            QW_LOADXB(xr, mb + 1);
+        int* sum_mb = s_sum + mb * bsum;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int q = blk0 + u;
+            const int c = c0 + q / nb, blk = q % nb;
+            if (u0 + u < u1) {
+                if (u == 0 || blk == 0)
+                    QW_LOAD_BO(c);
+                QW_UNIT_MFMA(u, sum_mb);
+            }
+        }
+    }
+#undef QW_LOADXB
+#undef QW_STOREXB
+#undef QW_UNIT_MFMA
+#undef QW_LOAD_BO
+    __syncthreads();
+
+    // outputs (m, nn), independent across threads
+    for (int e = tid; e < p.M * nrows; e += kThreads) {
+        const int m = e / nrows, nn = e - m * nrows;
+        const int v = s_sum[(m >> 4) * bsum + ((nn >> 4) * 16 + (m & 15)) * kBalSumPitch + (nn & 15)];
+        p.Y[(size_t)m * p.N + n0 + nn] = ((float)(v >> 4) * s_sc[nn]) * s_a[m];
+    }
+}
+
 // ---------------------------------------------------------------- W8A16 -------
 
 // Padded LDS image of one INT8 tile (2 rows x 32 chunks): row sub at sub * 528, chunk
@@ -792,6 +974,43 @@ hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
     return go_w4_bal_u<NW, 16>(p, nwg, lds, st);
 }
 
+template <int U>
+hipError_t go_w4_balm_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
+{
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_balm<U>),
+                                          (size_t)kXAllMaxBytes + (size_t)8 * 4 * kW4TilePitch +
+                                              (size_t)4 * kBalmMaxBlocks * 16 * kBalSumPitch * 4 +
+                                              (size_t)16 * kBalmMaxBlocks * 4 + 256);
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL((k_gemm_w4a8_balm<U>), dim3((unsigned)nwg), dim3(512), lds, st, p);
+    return hipGetLastError();
+}
+
+hipError_t go_w4_balm(MfmaW4A8Args p, int cus, hipStream_t st)
+{
+    if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot < 2 || p.mbtot > 4)
+        return hipErrorInvalidValue;
+    // at most 8 units per wave and kBalmMaxBlocks blocks per workgroup
+    const int bmax = std::min(kBalmMaxBlocks, 8 * 8 / p.cg);
+    int nwg = std::max(1, std::min(cus, p.nrg / 4));
+    nwg = std::max(nwg, (p.nrg + 4 * bmax - 1) / (4 * bmax));
+    p.per = p.nrg / nwg;
+    p.rem = p.nrg % nwg;
+    p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 3) / 4;
+    p.mgroups = 1;
+    const int umax = (p.nbmax * p.cg + 7) / 8;
+    const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)8 * 4 * kW4TilePitch +
+                       (size_t)p.mbtot * p.nbmax * 16 * kBalSumPitch * 4 + (size_t)16 * p.nbmax * 4 + 256;
+    if (umax <= 4)
+        return go_w4_balm_u<4>(p, nwg, lds, st);
+    if (umax <= 6)
+        return go_w4_balm_u<6>(p, nwg, lds, st);
+    if (umax <= 7)
+        return go_w4_balm_u<7>(p, nwg, lds, st);
+    return go_w4_balm_u<8>(p, nwg, lds, st);
+}
+
 template <int NW, int MB, int NBW>
 hipError_t go_w8(const MfmaW8A16Args& p, hipStream_t st)
 {
@@ -850,27 +1069,37 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
     if (bits == 4)
         return ((mb == 1 || mb == 2 || mb == 4) && !(nw == 4 && mb == 4 && nbw == 2) &&
                 !(nw == 8 && mb == 1 && nbw == 2)) ||
-               (mb == 0 && nbw == 1);
+               (mb == 0 && (nbw == 1 || nw == 8));
     // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
     // rows would not fit the registers.  mb 0: the balanced kernel (one wave per 512-k
     // step), nw 8 and nbw 1 only
     return ((mb == 1 || mb == 2) && !(nw == 8 && nbw == 2)) || (mb == 0 && nw == 8 && nbw == 1);
 }
 
-void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
+void mfma_default_shape(int bits, int64_t M, int64_t N, int64_t K, int cus, int* nw, int* mb,
+                        int* nbw)
 {
-    // measured at K = 4096, N = 27392: W4A8 up to 16 rows with the balanced kernel and
-    // 8-wave workgroups (14.3 us at 2 rows against 15.4 us for the streaming kernel,
-    // 7.9 against 11.7 us at N = 3584), then 8 waves and 2 or 4 blocks of X; W8A16 8
-    // waves with 1 or 2 blocks
+    // measured on MI355X: W4A8 up to 16 rows with the balanced kernel; 17 to 48 rows with
+    // the balanced kernel over 2 or 3 blocks of X (weights held in registers; 22.9
+    // against 24.3 us at 48 rows on 4096 -> 27392), 49 to 64 rows too when a workgroup
+    // holds at most 5 output blocks (20.5 against 23.3 us at 64 rows on 3584 -> 18944,
+    // but 26.8 against 25.6 us on 4096 -> 27392, where the streaming kernel's multiplies
+    // of the four blocks hide under its stream); else 8 waves and 2 or 4 blocks of X.
+    // W8A16: the balanced kernel up to 16 rows, else 8 waves with 1 or 2 blocks.
     const int64_t mbtot = (M + 15) / 16;
+    const bool k_fits = (K + 511) / 512 * 8192 <= kXAllMaxBytes;
     *nw = 8;
     *nbw = 1;
     if (bits == 4) {
-        if (mbtot == 1 && (K + 511) / 512 * 8192 <= kXAllMaxBytes)
+        const int64_t nrg = (N + 3) / 4;
+        if (mbtot == 1 && k_fits) {
             *mb = 0;
-        else
+        } else if (k_fits && (mbtot == 2 || mbtot == 3 || (mbtot == 4 && nrg <= 20 * (int64_t)cus))) {
+            *mb = 0;
+            *nbw = 2;
+        } else {
             *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
+        }
     } else if (mbtot == 1 && (K + 511) / 512 <= 8) {
         *mb = 0;
     } else {
@@ -924,7 +1153,12 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.nrg = L.nrg;
     p.ks = ks;
     p.mbtot = mbtot;
-    if (mb == 0) {  // balanced: one block of 16 rows of X per workgroup, resident in LDS
+    if (mb == 0) {  // balanced: one workgroup per CU, X codes of one block resident in LDS
+        if (nbw == 2 && mbtot >= 2) {
+            if (mbtot > 4 || nw != 8)
+                return hipErrorInvalidValue;
+            return go_w4_balm(p, cus, st);  // weights held in registers across the blocks
+        }
         if (nw == 8)
             return go_w4_bal<8>(p, cus, st);
         if (nw == 4)

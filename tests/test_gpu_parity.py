@@ -332,6 +332,33 @@ def test_balanced_matrix_core_kernel_matches_oracle(M, N, K):
         assert np.array_equal(Y.view(np.uint32), Yg.view(np.uint32)), nw
 
 
+# The balanced W4A8 kernel over 2 to 4 blocks of X (mb = 0, nbw = 2: weights held in
+# registers across the blocks): 17 and 64 rows on 4096 -> 27392, ragged N and M, tiny N,
+# K not a multiple of 512, more workgroups than CUs
+BALANCED_MULTI_SHAPES = [(17, 27392, 4096), (64, 27392, 4096), (40, 4101, 3584), (33, 37, 96),
+                         (50, 1000, 1056), (20, 70000, 4096), (63, 300, 544)]
+
+
+@pytest.mark.parametrize("M,N,K", BALANCED_MULTI_SHAPES)
+def test_balanced_multi_block_kernel_matches_oracle(M, N, K):
+    say("balanced multi-block mfma", M, N, K)
+    W = wl.weights(800 + M, 1, N, K, outlier_rows=True)
+    X = wl.activations(800 + M, 2, M, K, outlier_channels=4)
+    X[M // 2] = 0.0  # a zero row
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    ws = qw.make_workspace("w4a8", M, N, K)
+    Y = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 0, 2, workspace=ws))
+    assert_w4a8_close(Y, ref["Y"])
+    assert not np.any(Y[M // 2])
+    # the int32 sums are exact in any order: the streaming kernel gives the same bits
+    Yg = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 2, 1, workspace=ws))
+    assert np.array_equal(Y.view(np.uint32), Yg.view(np.uint32))
+    with pytest.raises(qw.QWError):
+        qw.gemm_w4a8_mfma(Xd, Wq, s, 4, 0, 2, workspace=ws)
+
+
 # The balanced W8A16 matrix-core kernel (mb = 0, one wave per 512-k step): the 4096 ->
 # 27392 linear at 3 and 16 rows, ragged N, tiny N, one step (K = 512, more workgroups
 # than CUs), K not a multiple of 512

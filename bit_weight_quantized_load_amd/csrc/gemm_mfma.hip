@@ -453,22 +453,24 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
     }
 }
 
-// The balanced W4A8 kernel for 17 to 64 rows of X (2 to 4 blocks of 16), K up to 4096.
-// The same workgroup split, units and pipeline as k_gemm_w4a8_bal for block 0 of X;
-// each wave also keeps the regrouped A operands of its units in registers (16 VGPRs a
-// unit), so that blocks 1 .. MBT-1 of X are multiplied against them afterwards without
-// reading the weights again: block by block, the workgroup stores that block's codes
-// in LDS (the next block's are requested before the multiplies), and the int32 sums go
-// to the LDS totals of that block.
-constexpr int kBalmMaxBlocks = 8;  // output blocks per workgroup
+// The balanced W4A8 kernel for 17 to 1024 rows of X (2 to 64 blocks of 16), K up to
+// 4096.  The same workgroup split, units and pipeline as k_gemm_w4a8_bal for block 0 of
+// X; each wave also keeps the regrouped A operands of its units in registers (16 VGPRs
+// a unit), so that blocks 1 .. MBT-1 of X are multiplied against them afterwards without
+// reading the weights again.  Block by block, the workgroup stores that block's codes in
+// LDS (the next block's are requested before the multiplies), writes the outputs of the
+// previous block, and adds the block's int32 sums into one of two LDS total buffers
+// (each entry is zeroed as the outputs read it); two barriers per block.
+constexpr int kBalmMaxBlocks = 8;    // output blocks per workgroup
+constexpr int kBalmMaxRows = 1024;   // rows of X
 
 template <int U>
 __global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
 {
     constexpr int NW = 8, kThreads = 512;
     constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
-    // LDS: X [CG steps][8 KB] of one block, per wave 4 padded tiles, the int32 totals
-    // [MBT][nbmax][16 m][17], the row scales and the 64 activation scales
+    // LDS: X [CG steps][8 KB] of one block, per wave 4 padded tiles, two int32 total
+    // buffers [nbmax][16 m][17], the row scales and the M activation scales
     extern __shared__ uint8_t s_mem[];
 
     const int tid = threadIdx.x;
@@ -492,7 +494,7 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
     uint8_t* s_x = s_mem;
     uint8_t* s_w = s_mem + xbytes + wave * 4 * kW4TilePitch;
     int* s_sum = reinterpret_cast<int*>(s_mem + xbytes + NW * 4 * kW4TilePitch);
-    float* s_sc = reinterpret_cast<float*>(s_sum + MBT * bsum);
+    float* s_sc = reinterpret_cast<float*>(s_sum + 2 * bsum);
     float* s_a = s_sc + 4 * 4 * p.nbmax;
 
     const int c0 = u0 / nb, blk0 = u0 - c0 * nb;
@@ -558,16 +560,19 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
     uint4 xr[kXP];
     QW_LOADXB(xr, 0);
     const uint32_t sr = load4(sres, (uint32_t)tid * 4u);
-    const uint32_t ar = load4(ares, (uint32_t)(tid & 63) * 4u);
+    const uint32_t ar0 = load4(ares, (uint32_t)tid * 4u);
+    const uint32_t ar1 = load4(ares, (uint32_t)(tid + kThreads) * 4u);
     issue_barrier();
     QW_LOADU(0);
     __builtin_amdgcn_sched_barrier(0);
     QW_STOREXB(xr);
     if (tid < 4 * 4 * p.nbmax)
         s_sc[tid] = __uint_as_float(sr);
-    if (tid < 64)
-        s_a[tid] = __uint_as_float(ar);
-    for (int e = tid; e < MBT * bsum; e += kThreads)
+    if (tid < p.M)
+        s_a[tid] = __uint_as_float(ar0);
+    if (tid + kThreads < p.M)
+        s_a[tid + kThreads] = __uint_as_float(ar1);
+    for (int e = tid; e < 2 * bsum; e += kThreads)
         s_sum[e] = 0;
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -600,15 +605,31 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
     }
 #undef QW_LOADU
 
+    // outputs of block MB_ from total buffer (MB_) % 2, each entry zeroed once read
+#define QW_OUT_BLOCK(MB_)                                                                        \
+    {                                                                                            \
+        int* sb_ = s_sum + ((MB_) & 1) * bsum;                                                   \
+        const int mv_ = min(p.M - 16 * (MB_), 16);                                               \
+        for (int e_ = tid; e_ < mv_ * nrows; e_ += kThreads) {                                   \
+            const int m_ = e_ / nrows, nn_ = e_ - m_ * nrows;                                    \
+            int* cell_ = sb_ + ((nn_ >> 4) * 16 + m_) * kBalSumPitch + (nn_ & 15);               \
+            const int v_ = *cell_;                                                               \
+            *cell_ = 0;                                                                          \
+            p.Y[(size_t)(16 * (MB_) + m_) * p.N + n0 + nn_] =                                    \
+                ((float)(v_ >> 4) * s_sc[nn_]) * s_a[16 * (MB_) + m_];                           \
+        }                                                                                        \
+    }
+
     // blocks 1 .. MBT-1 of X against the A operands held in registers
     QW_LOADXB(xr, 1);
     for (int mb = 1; mb < MBT; ++mb) {
-        __syncthreads();  // every wave is done with the previous block's codes
+        __syncthreads();  // block mb-1's multiplies and sums are done
         QW_STOREXB(xr);
-        __syncthreads();
+        QW_OUT_BLOCK(mb - 1);
         if (mb + 1 < MBT)
             QW_LOADXB(xr, mb + 1);
-        int* sum_mb = s_sum + mb * bsum;
+        __syncthreads();  // block mb's codes are in LDS
+        int* sum_mb = s_sum + (mb & 1) * bsum;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int q = blk0 + u;
@@ -620,18 +641,13 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
             }
         }
     }
+    __syncthreads();
+    QW_OUT_BLOCK(MBT - 1);
 #undef QW_LOADXB
 #undef QW_STOREXB
 #undef QW_UNIT_MFMA
 #undef QW_LOAD_BO
-    __syncthreads();
-
-    // outputs (m, nn), independent across threads
-    for (int e = tid; e < p.M * nrows; e += kThreads) {
-        const int m = e / nrows, nn = e - m * nrows;
-        const int v = s_sum[(m >> 4) * bsum + ((nn >> 4) * 16 + (m & 15)) * kBalSumPitch + (nn & 15)];
-        p.Y[(size_t)m * p.N + n0 + nn] = ((float)(v >> 4) * s_sc[nn]) * s_a[m];
-    }
+#undef QW_OUT_BLOCK
 }
 
 // ---------------------------------------------------------------- W8A16 -------
@@ -979,8 +995,8 @@ hipError_t go_w4_balm_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t 
 {
     static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_balm<U>),
                                           (size_t)kXAllMaxBytes + (size_t)8 * 4 * kW4TilePitch +
-                                              (size_t)4 * kBalmMaxBlocks * 16 * kBalSumPitch * 4 +
-                                              (size_t)16 * kBalmMaxBlocks * 4 + 256);
+                                              (size_t)2 * kBalmMaxBlocks * 16 * kBalSumPitch * 4 +
+                                              (size_t)16 * kBalmMaxBlocks * 4 + (size_t)kBalmMaxRows * 4);
     if (e != hipSuccess)
         return e;
     hipLaunchKernelGGL((k_gemm_w4a8_balm<U>), dim3((unsigned)nwg), dim3(512), lds, st, p);
@@ -989,7 +1005,7 @@ hipError_t go_w4_balm_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t 
 
 hipError_t go_w4_balm(MfmaW4A8Args p, int cus, hipStream_t st)
 {
-    if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot < 2 || p.mbtot > 4)
+    if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot < 2 || p.M > kBalmMaxRows)
         return hipErrorInvalidValue;
     // at most 8 units per wave and kBalmMaxBlocks blocks per workgroup
     const int bmax = std::min(kBalmMaxBlocks, 8 * 8 / p.cg);
@@ -1001,7 +1017,8 @@ hipError_t go_w4_balm(MfmaW4A8Args p, int cus, hipStream_t st)
     p.mgroups = 1;
     const int umax = (p.nbmax * p.cg + 7) / 8;
     const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)8 * 4 * kW4TilePitch +
-                       (size_t)p.mbtot * p.nbmax * 16 * kBalSumPitch * 4 + (size_t)16 * p.nbmax * 4 + 256;
+                       (size_t)2 * p.nbmax * 16 * kBalSumPitch * 4 + (size_t)16 * p.nbmax * 4 +
+                       (size_t)p.M * 4;
     if (umax <= 4)
         return go_w4_balm_u<4>(p, nwg, lds, st);
     if (umax <= 6)
@@ -1079,12 +1096,13 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
 void mfma_default_shape(int bits, int64_t M, int64_t N, int64_t K, int cus, int* nw, int* mb,
                         int* nbw)
 {
-    // measured on MI355X: W4A8 up to 16 rows with the balanced kernel; 17 to 48 rows with
-    // the balanced kernel over 2 or 3 blocks of X (weights held in registers; 22.9
-    // against 24.3 us at 48 rows on 4096 -> 27392), 49 to 64 rows too when a workgroup
-    // holds at most 5 output blocks (20.5 against 23.3 us at 64 rows on 3584 -> 18944,
-    // but 26.8 against 25.6 us on 4096 -> 27392, where the streaming kernel's multiplies
-    // of the four blocks hide under its stream); else 8 waves and 2 or 4 blocks of X.
+    // measured on MI355X: W4A8 up to 16 rows with the balanced kernel; from 17 rows with
+    // the balanced kernel over all blocks of X (weights held in registers; 22.9 against
+    // 24.3 us at 48 rows on 4096 -> 27392, 40.7 against 44.2 at 128, 123.7 against 138.0
+    // at 512), except 49 to 64 rows when a workgroup would hold more than 5 output
+    // blocks (26.8 against 25.6 us at 64 rows on 4096 -> 27392, where the streaming
+    // kernel's multiplies of the four blocks hide under its stream; 20.5 against 23.3 us
+    // on 3584 -> 18944): there, and for K > 4096, 8 waves and 2 or 4 blocks of X.
     // W8A16: the balanced kernel up to 16 rows, else 8 waves with 1 or 2 blocks.
     const int64_t mbtot = (M + 15) / 16;
     const bool k_fits = (K + 511) / 512 * 8192 <= kXAllMaxBytes;
@@ -1094,7 +1112,7 @@ void mfma_default_shape(int bits, int64_t M, int64_t N, int64_t K, int cus, int*
         const int64_t nrg = (N + 3) / 4;
         if (mbtot == 1 && k_fits) {
             *mb = 0;
-        } else if (k_fits && (mbtot == 2 || mbtot == 3 || (mbtot == 4 && nrg <= 20 * (int64_t)cus))) {
+        } else if (k_fits && M <= kBalmMaxRows && (mbtot != 4 || nrg <= 20 * (int64_t)cus)) {
             *mb = 0;
             *nbw = 2;
         } else {
@@ -1155,7 +1173,7 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.mbtot = mbtot;
     if (mb == 0) {  // balanced: one workgroup per CU, X codes of one block resident in LDS
         if (nbw == 2 && mbtot >= 2) {
-            if (mbtot > 4 || nw != 8)
+            if (M > kBalmMaxRows || nw != 8)
                 return hipErrorInvalidValue;
             return go_w4_balm(p, cus, st);  // weights held in registers across the blocks
         }

@@ -227,7 +227,7 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
    W8A16), nbw blocks of 16 output rows per wave (1 or 2; not 2 with nw 8 and mb 1 for
    W4A8, not 2 with nw 8 for W8A16).  W4A8 also takes mb = 0 (nbw 1, K <= 4096): the
    balanced kernel, one workgroup per CU and block of 16 rows of X, with that block's
-   activation codes resident in on-chip memory; with nw 8 and nbw 2 and 17 to 64 rows,
+   activation codes resident in on-chip memory; with nw 8 and nbw 2 and 17 to 1024 rows,
    one workgroup per CU over all blocks of X, the weights held in registers after one
    pass.  W8A16 takes mb = 0 too (nw 8, nbw 1,
    M <= 16, K <= 4096): the balanced kernel with one wave per 512-k step, whose f16 X

@@ -336,7 +336,8 @@ def test_balanced_matrix_core_kernel_matches_oracle(M, N, K):
 # registers across the blocks): 17 and 64 rows on 4096 -> 27392, ragged N and M, tiny N,
 # K not a multiple of 512, more workgroups than CUs
 BALANCED_MULTI_SHAPES = [(17, 27392, 4096), (64, 27392, 4096), (40, 4101, 3584), (33, 37, 96),
-                         (50, 1000, 1056), (20, 70000, 4096), (63, 300, 544)]
+                         (50, 1000, 1056), (20, 70000, 4096), (63, 300, 544), (300, 4101, 3584),
+                         (129, 2000, 1056), (1024, 260, 512)]
 
 
 @pytest.mark.parametrize("M,N,K", BALANCED_MULTI_SHAPES)
@@ -357,6 +358,26 @@ def test_balanced_multi_block_kernel_matches_oracle(M, N, K):
     assert np.array_equal(Y.view(np.uint32), Yg.view(np.uint32))
     with pytest.raises(qw.QWError):
         qw.gemm_w4a8_mfma(Xd, Wq, s, 4, 0, 2, workspace=ws)
+
+
+def test_balanced_multi_block_full_size_equals_streaming_kernel():
+    """512 rows on 4096 -> 27392 (the sweep's largest M; the oracle would take minutes):
+    the balanced kernel gives the streaming kernel's bits, and that kernel is held to the
+    oracle at the other shapes."""
+    M, N, K = 512, 27392, 4096
+    say("balanced multi-block full size", M, N, K)
+    W = wl.weights(900, 1, N, K, outlier_rows=True)
+    X = wl.activations(900, 2, M, K, outlier_channels=4)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    Xd = dev(X)
+    ws = qw.make_workspace("w4a8", M, N, K)
+    Y = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 0, 2, workspace=ws))
+    Yg = host(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 4, 1, workspace=ws))
+    assert np.array_equal(Y.view(np.uint32), Yg.view(np.uint32))
+    assert np.all(np.isfinite(Y)) and np.any(Y)
+    with pytest.raises(qw.QWError):  # more than 1024 rows
+        qw.gemm_w4a8_mfma(dev(wl.activations(901, 2, 1040, K)), Wq, s, 8, 0, 2,
+                          workspace=qw.make_workspace("w4a8", 1040, N, K))
 
 
 # The balanced W8A16 matrix-core kernel (mb = 0, one wave per 512-k step): the 4096 ->

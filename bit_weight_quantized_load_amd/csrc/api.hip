@@ -797,7 +797,7 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
     if (M >= qw::kMfmaMinM4) {
         int nw, mb, nbw;
-        qw::mfma_default_shape(4, M, N, K, device_cus(), &nw, &mb, &nbw);
+        qw::mfma_default_shape(4, M, K, &nw, &mb, &nbw);
         return run_gemm_w4a8(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, nw, mb, nbw, stream);
     }
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
@@ -847,7 +847,7 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
     if (M >= qw::kMfmaMinM8) {
         int nw, mb, nbw;
-        qw::mfma_default_shape(8, M, N, K, device_cus(), &nw, &mb, &nbw);
+        qw::mfma_default_shape(8, M, K, &nw, &mb, &nbw);
         return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, nw, mb, nbw,
                               stream);
     }

@@ -453,200 +453,167 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
     }
 }
 
-// The balanced W4A8 kernel for 17 to 1024 rows of X (2 to 64 blocks of 16), K up to
-// 4096.  The same workgroup split, units and pipeline as k_gemm_w4a8_bal for block 0 of
-// X; each wave also keeps the regrouped A operands of its units in registers (16 VGPRs
-// a unit), so that blocks 1 .. MBT-1 of X are multiplied against them afterwards without
-// reading the weights again.  Block by block, the workgroup stores that block's codes in
-// LDS (the next block's are requested before the multiplies), writes the outputs of the
-// previous block, and adds the block's int32 sums into one of two LDS total buffers
-// (each entry is zeroed as the outputs read it); two barriers per block.
-constexpr int kBalmMaxBlocks = 8;    // output blocks per workgroup
-constexpr int kBalmMaxRows = 1024;   // rows of X
+constexpr int kBalmMaxRows = 1024;   // rows of X of the kernel over many blocks
 
+// The balanced W4A8 kernel over many blocks of X with one wave per 512-k step (K up
+// to 4096, 1 to 1024 rows of X).  Workgroup b owns an even run of row groups, nb <= U
+// output blocks of 16 rows; wave w takes step w of every one of them (unit u = block u
+// at step w), so that the X operands it needs for one block of 16 rows of X are the
+// 8 KB of step w, loaded straight into registers.  Block 0 of X goes through the
+// one-unit-ahead pipeline as the weights stream in, and each unit's regrouped A
+// operands stay in registers (16 VGPRs a unit); blocks 1 .. MBT-1 are then multiplied
+// against them, the next block's operands requested one block ahead.  The CG partial
+// sums of an output meet in one of two LDS total buffers (integer adds, exact in any
+// order); after one barrier per block the workgroup writes that block's outputs and
+// zeroes each entry it reads.
 template <int U>
-__global__ __launch_bounds__(512) void k_gemm_w4a8_balm(MfmaW4A8Args p)
+__global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
 {
-    constexpr int NW = 8, kThreads = 512;
-    constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
-    // LDS: X [CG steps][8 KB] of one block, per wave 4 padded tiles, two int32 total
-    // buffers [nbmax][16 m][17], the row scales and the M activation scales
+    // LDS: per wave 4 padded tiles, two int32 total buffers [nbmax][16 m][17], the row
+    // scales and two sets of 16 activation scales
     extern __shared__ uint8_t s_mem[];
-
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = the 512-k step
+    const int nthreads = (int)blockDim.x;
     const int g = lane >> 4, r = lane & 15;
     const int CG = p.cg, KS = p.ks, MBT = p.mbtot;
     const int b = blockIdx.x;
     const int rg0 = min(b * p.per + min(b, p.rem), p.nrg);
     const int nrg_b = max(0, min(p.per + (b < p.rem ? 1 : 0), p.nrg - rg0));
-    const int nb = max(1, (nrg_b + 3) >> 2);
-    const int T = nb * CG;
-    const int u0 = (wave * T) / NW, u1 = ((wave + 1) * T) / NW;
+    const int nb = min(U, (nrg_b + 3) >> 2);
     const int n0 = 4 * rg0;
     const int nrows = max(0, min(4 * nrg_b, p.N - n0));
-    const int bsum = p.nbmax * 16 * kBalSumPitch;  // int32 totals of one block of X
+    const int bsum = p.nbmax * 16 * kBalSumPitch;
     const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_b * CG) * 1024u);
     const rsrc_t sres = make_rsrc(p.w_scale + n0, (uint32_t)nrows * 4u);
     const rsrc_t ares = make_rsrc(p.a_scale, (uint32_t)p.M * 4u);
-    const int xbytes = CG * 8 * 1024;  // whole 512-k steps; past K the loads read zeros
-    uint8_t* s_x = s_mem;
-    uint8_t* s_w = s_mem + xbytes + wave * 4 * kW4TilePitch;
-    int* s_sum = reinterpret_cast<int*>(s_mem + xbytes + NW * 4 * kW4TilePitch);
+    uint8_t* s_w = s_mem + wave * 4 * kW4TilePitch;
+    int* s_sum = reinterpret_cast<int*>(s_mem + 8 * 4 * kW4TilePitch);
     float* s_sc = reinterpret_cast<float*>(s_sum + 2 * bsum);
-    float* s_a = s_sc + 4 * 4 * p.nbmax;
+    float* s_a = s_sc + 4 * 4 * p.nbmax;  // [2][16]
 
-    const int c0 = u0 / nb, blk0 = u0 - c0 * nb;
-    uint4 wb[U][4];
-#define QW_LOADU(U_)                                                                             \
-    {                                                                                            \
-        const int q_ = blk0 + (U_);                                                              \
-        const int c_ = c0 + q_ / nb, blk_ = q_ % nb;                                             \
-        const bool live_ = u0 + (U_) < u1;                                                       \
-        _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                         \
-            wb[U_][i_] = load16_stream(wres, live_ ? (uint32_t)((4 * blk_ + i_) * CG + c_) * 1024u + \
-                                                         (uint32_t)lane * 16u                    \
-                                                   : 0x80000000u);                               \
-    }
-    // X codes of block MB_ (zeros past K and past M)
-#define QW_LOADXB(XR, MB_)                                                                       \
+    // X operands of block MB_ at step w: substep s -> 16 bytes at (MB_ KS + 8 w + s) KB
+    // + 16 lane (zeros past K)
+#define QW_LOADB(BO, MB_)                                                                        \
     {                                                                                            \
         const rsrc_t xres_ = make_rsrc(p.Xp + (size_t)(MB_) * KS * 1024u, (uint32_t)KS * 1024u); \
-        _Pragma("unroll") for (int v_ = 0; v_ < kXP; ++v_)                                       \
-        {                                                                                        \
-            const int pc_ = v_ * kThreads + tid;                                                 \
-            XR[v_] = load16(xres_, pc_ * 16 < xbytes ? (uint32_t)pc_ * 16u : 0x80000000u);       \
-        }                                                                                        \
-    }
-#define QW_STOREXB(XR)                                                                           \
-    _Pragma("unroll") for (int v_ = 0; v_ < kXP; ++v_)                                           \
-    {                                                                                            \
-        const int pc_ = v_ * kThreads + tid;                                                     \
-        if (pc_ * 16 < xbytes)                                                                   \
-            *reinterpret_cast<uint4*>(s_x + (size_t)pc_ * 16) = XR[v_];                          \
-    }
-    // B operands of step C_ from LDS (the first unit of a wave, or a new step)
-#define QW_LOAD_BO(C_)                                                                           \
-    {                                                                                            \
-        const uint8_t* xb_ = s_x + (size_t)(C_) * 8 * 1024;                                      \
         _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
-        {                                                                                        \
-            const uint4 b4_ = *reinterpret_cast<const uint4*>(xb_ + (s_ * 64 + lane) * 16);      \
-            bo[s_] = v4i{(int)b4_.x, (int)b4_.y, (int)b4_.z, (int)b4_.w};                         \
-        }                                                                                        \
+            BO[s_] = load16(xres_, (uint32_t)(8 * wave + s_) * 1024u + (uint32_t)lane * 16u);    \
     }
-    // one unit's eight multiplies against bo; sums into SUM
-#define QW_UNIT_MFMA(U_, SUM)                                                                    \
+    // the four tiles of unit U_: block U_ at step w (zeros past the run)
+#define QW_LOADU(U_)                                                                             \
+    _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                             \
+        wb[U_][i_] = load16_stream(wres, (U_) < nb ? (uint32_t)((4 * (U_) + i_) * CG + wave) * 1024u + \
+                                                         (uint32_t)lane * 16u                    \
+                                                   : 0x80000000u);
+    // one unit's eight multiplies against bo, its sums into total buffer SB
+#define QW_UNIT_MFMA(U_, SB)                                                                     \
     {                                                                                            \
         v4i acc_ = v4i{0, 0, 0, 0};                                                              \
         _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
         {                                                                                        \
-            const v4i bo_ = bo[s_];                                                              \
             uint2 w_ = ua[U_][s_];                                                               \
             /* opaque copy: keeps the unpack inside the loop over blocks of X (hoisted, the */  \
             /* unpacked operands of every unit would not fit the registers) */                  \
             asm volatile("" : "+v"(w_.x), "+v"(w_.y));                                           \
             const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),         \
                             (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};        \
-            acc_ = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, bo_, acc_, 0, 0, 0);                \
+            const v4i b_ = {(int)bo[s_].x, (int)bo[s_].y, (int)bo[s_].z, (int)bo[s_].w};         \
+            acc_ = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, b_, acc_, 0, 0, 0);                 \
         }                                                                                        \
-        int* dst_ = (SUM) + (blk * 16 + r) * kBalSumPitch + 4 * g;                               \
+        int* dst_ = (SB) + ((U_) * 16 + r) * kBalSumPitch + 4 * g;                               \
         _Pragma("unroll") for (int i_ = 0; i_ < 4; ++i_)                                         \
             __hip_atomic_fetch_add(dst_ + i_, acc_[i_], __ATOMIC_RELAXED,                        \
                                    __HIP_MEMORY_SCOPE_WORKGROUP);                                \
     }
+    // outputs of block MB_ (total buffer and scales (MB_) % 2), each entry zeroed once read
+#define QW_OUT_BLOCK(MB_)                                                                        \
+    {                                                                                            \
+        int* sb_ = s_sum + ((MB_) & 1) * bsum;                                                   \
+        const float* sa_ = s_a + ((MB_) & 1) * 16;                                               \
+        const int mv_ = min(p.M - 16 * (MB_), 16);                                               \
+        for (int e_ = tid; e_ < mv_ * nrows; e_ += nthreads) {                                   \
+            const int m_ = e_ / nrows, nn_ = e_ - m_ * nrows;                                    \
+            int* cell_ = sb_ + ((nn_ >> 4) * 16 + m_) * kBalSumPitch + (nn_ & 15);               \
+            const int v_ = *cell_;                                                               \
+            *cell_ = 0;                                                                          \
+            p.Y[(size_t)(16 * (MB_) + m_) * p.N + n0 + nn_] = ((float)(v_ >> 4) * s_sc[nn_]) * sa_[m_]; \
+        }                                                                                        \
+    }
 
-    uint4 xr[kXP];
-    QW_LOADXB(xr, 0);
-    const uint32_t sr = load4(sres, (uint32_t)tid * 4u);
-    const uint32_t ar0 = load4(ares, (uint32_t)tid * 4u);
-    const uint32_t ar1 = load4(ares, (uint32_t)(tid + kThreads) * 4u);
+    uint4 bo[8], bn[8];
+    QW_LOADB(bo, 0);
+    const uint32_t sr0 = load4(sres, (uint32_t)tid * 4u);
+    const uint32_t sr1 = load4(sres, (uint32_t)(tid + nthreads) * 4u);
+    const uint32_t ar = load4(ares, (uint32_t)(tid & 15) * 4u);
+    uint4 wb[U][4];
     issue_barrier();
     QW_LOADU(0);
     __builtin_amdgcn_sched_barrier(0);
-    QW_STOREXB(xr);
     if (tid < 4 * 4 * p.nbmax)
-        s_sc[tid] = __uint_as_float(sr);
-    if (tid < p.M)
-        s_a[tid] = __uint_as_float(ar0);
-    if (tid + kThreads < p.M)
-        s_a[tid + kThreads] = __uint_as_float(ar1);
-    for (int e = tid; e < 2 * bsum; e += kThreads)
+        s_sc[tid] = __uint_as_float(sr0);
+    if (tid + nthreads < 4 * 4 * p.nbmax)
+        s_sc[tid + nthreads] = __uint_as_float(sr1);
+    if (tid < 16)
+        s_a[tid] = __uint_as_float(ar);
+    for (int e = tid; e < 2 * bsum; e += nthreads)
         s_sum[e] = 0;
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
 
     const int sub = lane >> 4, j = lane & 15;
-    // A operand of step s for lane (g, r): row r of the block = tile r / 4, tile row
+    // A operand of substep s for lane (g, r): row r of the block = tile r / 4, tile row
     // r % 4; 16 k = chunk 2 s + g / 2, half g % 2
     const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
-    v4i bo[8];
     uint2 ua[U][8];  // regrouped A operands of every unit of the wave
+    // block 0 of X as the weights stream in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-        if (u + 1 < U)
+        if (u + 1 < U) {
             QW_LOADU(u + 1);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        const int q = blk0 + u;
-        const int c = c0 + q / nb, blk = q % nb;
-        if (u0 + u < u1) {
+        if (u < nb) {
 #pragma unroll
             for (int i = 0; i < 4; ++i)
                 *reinterpret_cast<uint4*>(s_w + i * kW4TilePitch + sub * kW4RowPitch + j * 16) = wb[u][i];
-            if (u == 0 || blk == 0)
-                QW_LOAD_BO(c);
 #pragma unroll
             for (int s = 0; s < 8; ++s)
                 ua[u][s] = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
             QW_UNIT_MFMA(u, s_sum);
         }
     }
-#undef QW_LOADU
-
-    // outputs of block MB_ from total buffer (MB_) % 2, each entry zeroed once read
-#define QW_OUT_BLOCK(MB_)                                                                        \
-    {                                                                                            \
-        int* sb_ = s_sum + ((MB_) & 1) * bsum;                                                   \
-        const int mv_ = min(p.M - 16 * (MB_), 16);                                               \
-        for (int e_ = tid; e_ < mv_ * nrows; e_ += kThreads) {                                   \
-            const int m_ = e_ / nrows, nn_ = e_ - m_ * nrows;                                    \
-            int* cell_ = sb_ + ((nn_ >> 4) * 16 + m_) * kBalSumPitch + (nn_ & 15);               \
-            const int v_ = *cell_;                                                               \
-            *cell_ = 0;                                                                          \
-            p.Y[(size_t)(16 * (MB_) + m_) * p.N + n0 + nn_] =                                    \
-                ((float)(v_ >> 4) * s_sc[nn_]) * s_a[16 * (MB_) + m_];                           \
-        }                                                                                        \
-    }
-
-    // blocks 1 .. MBT-1 of X against the A operands held in registers
-    QW_LOADXB(xr, 1);
-    for (int mb = 1; mb < MBT; ++mb) {
-        __syncthreads();  // block mb-1's multiplies and sums are done
-        QW_STOREXB(xr);
-        QW_OUT_BLOCK(mb - 1);
-        if (mb + 1 < MBT)
-            QW_LOADXB(xr, mb + 1);
-        __syncthreads();  // block mb's codes are in LDS
-        int* sum_mb = s_sum + (mb & 1) * bsum;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int q = blk0 + u;
-            const int c = c0 + q / nb, blk = q % nb;
-            if (u0 + u < u1) {
-                if (u == 0 || blk == 0)
-                    QW_LOAD_BO(c);
-                QW_UNIT_MFMA(u, sum_mb);
-            }
-        }
-    }
+    if (MBT > 1)
+        QW_LOADB(bn, 1);
+    float an = 0.0f;
+    if (MBT > 1)
+        an = __uint_as_float(load4(ares, (uint32_t)(16 + (tid & 15)) * 4u));
     __syncthreads();
-    QW_OUT_BLOCK(MBT - 1);
-#undef QW_LOADXB
-#undef QW_STOREXB
+    QW_OUT_BLOCK(0);
+    // blocks 1 .. MBT-1 against the A operands held in registers
+    for (int mb = 1; mb < MBT; ++mb) {
+#pragma unroll
+        for (int s = 0; s < 8; ++s)
+            bo[s] = bn[s];
+        if (tid < 16)
+            s_a[(mb & 1) * 16 + tid] = an;
+        if (mb + 1 < MBT) {
+            QW_LOADB(bn, mb + 1);
+            an = __uint_as_float(load4(ares, (uint32_t)(16 * (mb + 1) + (tid & 15)) * 4u));
+        }
+        int* sb = s_sum + (mb & 1) * bsum;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (u < nb)
+                QW_UNIT_MFMA(u, sb);
+        __syncthreads();
+        QW_OUT_BLOCK(mb);
+    }
+#undef QW_LOADB
+#undef QW_LOADU
 #undef QW_UNIT_MFMA
-#undef QW_LOAD_BO
 #undef QW_OUT_BLOCK
 }
 
@@ -991,41 +958,34 @@ hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
 }
 
 template <int U>
-hipError_t go_w4_balm_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
+hipError_t go_w4_bals_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
 {
-    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_balm<U>),
-                                          (size_t)kXAllMaxBytes + (size_t)8 * 4 * kW4TilePitch +
-                                              (size_t)2 * kBalmMaxBlocks * 16 * kBalSumPitch * 4 +
-                                              (size_t)16 * kBalmMaxBlocks * 4 + (size_t)kBalmMaxRows * 4);
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bals<U>),
+                                          (size_t)96 * 1024);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_gemm_w4a8_balm<U>), dim3((unsigned)nwg), dim3(512), lds, st, p);
+    hipLaunchKernelGGL((k_gemm_w4a8_bals<U>), dim3((unsigned)nwg), dim3(64 * p.cg), lds, st, p);
     return hipGetLastError();
 }
 
-hipError_t go_w4_balm(MfmaW4A8Args p, int cus, hipStream_t st)
+hipError_t go_w4_bals(MfmaW4A8Args p, int cus, hipStream_t st)
 {
-    if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot < 2 || p.M > kBalmMaxRows)
+    if (p.cg > 8 || p.M > kBalmMaxRows)
         return hipErrorInvalidValue;
-    // at most 8 units per wave and kBalmMaxBlocks blocks per workgroup
-    const int bmax = std::min(kBalmMaxBlocks, 8 * 8 / p.cg);
+    // one workgroup per CU, at least four row groups and at most 8 output blocks each
     int nwg = std::max(1, std::min(cus, p.nrg / 4));
-    nwg = std::max(nwg, (p.nrg + 4 * bmax - 1) / (4 * bmax));
+    nwg = std::max(nwg, (p.nrg + 31) / 32);
     p.per = p.nrg / nwg;
     p.rem = p.nrg % nwg;
     p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 3) / 4;
     p.mgroups = 1;
-    const int umax = (p.nbmax * p.cg + 7) / 8;
-    const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)8 * 4 * kW4TilePitch +
-                       (size_t)2 * p.nbmax * 16 * kBalSumPitch * 4 + (size_t)16 * p.nbmax * 4 +
-                       (size_t)p.M * 4;
-    if (umax <= 4)
-        return go_w4_balm_u<4>(p, nwg, lds, st);
-    if (umax <= 6)
-        return go_w4_balm_u<6>(p, nwg, lds, st);
-    if (umax <= 7)
-        return go_w4_balm_u<7>(p, nwg, lds, st);
-    return go_w4_balm_u<8>(p, nwg, lds, st);
+    // the LDS it needs, padded so that one workgroup fills a CU
+    const size_t need = (size_t)8 * 4 * kW4TilePitch + (size_t)2 * p.nbmax * 16 * kBalSumPitch * 4 +
+                        (size_t)(16 * p.nbmax + 32) * 4;
+    const size_t lds = std::max(need, (size_t)82 * 1024);
+    if (p.nbmax <= 4)
+        return go_w4_bals_u<4>(p, nwg, lds, st);
+    return go_w4_bals_u<8>(p, nwg, lds, st);
 }
 
 template <int NW, int MB, int NBW>
@@ -1093,26 +1053,22 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
     return ((mb == 1 || mb == 2) && !(nw == 8 && nbw == 2)) || (mb == 0 && nw == 8 && nbw == 1);
 }
 
-void mfma_default_shape(int bits, int64_t M, int64_t N, int64_t K, int cus, int* nw, int* mb,
-                        int* nbw)
+void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
 {
-    // measured on MI355X: W4A8 up to 16 rows with the balanced kernel; from 17 rows with
-    // the balanced kernel over all blocks of X (weights held in registers; 22.9 against
-    // 24.3 us at 48 rows on 4096 -> 27392, 40.7 against 44.2 at 128, 123.7 against 138.0
-    // at 512), except 49 to 64 rows when a workgroup would hold more than 5 output
-    // blocks (26.8 against 25.6 us at 64 rows on 4096 -> 27392, where the streaming
-    // kernel's multiplies of the four blocks hide under its stream; 20.5 against 23.3 us
-    // on 3584 -> 18944): there, and for K > 4096, 8 waves and 2 or 4 blocks of X.
-    // W8A16: the balanced kernel up to 16 rows, else 8 waves with 1 or 2 blocks.
+    // measured on MI355X: W4A8 with K <= 4096 and up to 16 rows on the balanced kernel,
+    // 17 to 1024 rows on the one with one wave per step and the weights held in
+    // registers (on 4096 -> 27392: 25.4 against 25.8 us for the streaming kernel at 64
+    // rows, 39.0 against 44.2 at 128, 114.5 against 138.0 at 512); else the streaming
+    // kernel with 8 waves and 2 or 4 blocks of X.  W8A16: the balanced kernel up to 16
+    // rows, else 8 waves with 1 or 2 blocks.
     const int64_t mbtot = (M + 15) / 16;
     const bool k_fits = (K + 511) / 512 * 8192 <= kXAllMaxBytes;
     *nw = 8;
     *nbw = 1;
     if (bits == 4) {
-        const int64_t nrg = (N + 3) / 4;
         if (mbtot == 1 && k_fits) {
             *mb = 0;
-        } else if (k_fits && M <= kBalmMaxRows && (mbtot != 4 || nrg <= 20 * (int64_t)cus)) {
+        } else if (k_fits && M <= kBalmMaxRows) {
             *mb = 0;
             *nbw = 2;
         } else {
@@ -1172,11 +1128,8 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     p.ks = ks;
     p.mbtot = mbtot;
     if (mb == 0) {  // balanced: one workgroup per CU, X codes of one block resident in LDS
-        if (nbw == 2 && mbtot >= 2) {
-            if (M > kBalmMaxRows || nw != 8)
-                return hipErrorInvalidValue;
-            return go_w4_balm(p, cus, st);  // weights held in registers across the blocks
-        }
+        if (nbw == 2)  // one wave per 512-k step, weights held in registers across the blocks
+            return nw == 8 ? go_w4_bals(p, cus, st) : hipErrorInvalidValue;
         if (nw == 8)
             return go_w4_bal<8>(p, cus, st);
         if (nw == 4)

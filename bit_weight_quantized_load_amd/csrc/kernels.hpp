@@ -154,8 +154,7 @@ size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K);
 // Launch shape of the matrix-core kernels: nw waves per workgroup (4 or 8), mb blocks
 // of 16 rows of X per workgroup, nbw blocks of 16 output rows per wave.
 bool mfma_shape_ok(int bits, int nw, int mb, int nbw);
-void mfma_default_shape(int bits, int64_t M, int64_t N, int64_t K, int cus, int* nw, int* mb,
-                        int* nbw);
+void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw);
 hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* Wq,
                             const float* w_scale, float* Y, void* workspace, int nw, int mb,
                             int nbw, int cus, hipStream_t st);

@@ -507,18 +507,18 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
         wb[U_][i_] = load16_stream(wres, (U_) < nb ? (uint32_t)((4 * (U_) + i_) * CG + wave) * 1024u + \
                                                          (uint32_t)lane * 16u                    \
                                                    : 0x80000000u);
-    // one unit's eight multiplies against bo, its sums into total buffer SB
+    // one unit's eight multiplies against bo, its sums into total buffer SB.  The shift
+    // and mask of the nibble unpack are scalars the compiler cannot see through (an
+    // opaque zero added per block of X): hoisted out of the loop over blocks, the
+    // unpacked operands of every unit would not fit the registers
 #define QW_UNIT_MFMA(U_, SB)                                                                     \
     {                                                                                            \
         v4i acc_ = v4i{0, 0, 0, 0};                                                              \
         _Pragma("unroll") for (int s_ = 0; s_ < 8; ++s_)                                         \
         {                                                                                        \
-            uint2 w_ = ua[U_][s_];                                                               \
-            /* opaque copy: keeps the unpack inside the loop over blocks of X (hoisted, the */  \
-            /* unpacked operands of every unit would not fit the registers) */                  \
-            asm volatile("" : "+v"(w_.x), "+v"(w_.y));                                           \
-            const v4i a_ = {(int)((w_.x << 4) & 0xF0F0F0F0u), (int)(w_.x & 0xF0F0F0F0u),         \
-                            (int)((w_.y << 4) & 0xF0F0F0F0u), (int)(w_.y & 0xF0F0F0F0u)};        \
+            const uint2 w_ = ua[U_][s_];                                                         \
+            const v4i a_ = {(int)((w_.x << ush) & umask), (int)(w_.x & umask),                   \
+                            (int)((w_.y << ush) & umask), (int)(w_.y & umask)};                  \
             const v4i b_ = {(int)bo[s_].x, (int)bo[s_].y, (int)bo[s_].z, (int)bo[s_].w};         \
             acc_ = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, b_, acc_, 0, 0, 0);                 \
         }                                                                                        \
@@ -527,18 +527,27 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
             __hip_atomic_fetch_add(dst_ + i_, acc_[i_], __ATOMIC_RELAXED,                        \
                                    __HIP_MEMORY_SCOPE_WORKGROUP);                                \
     }
-    // outputs of block MB_ (total buffer and scales (MB_) % 2), each entry zeroed once read
+    // outputs of block MB_ (total buffer and scales (MB_) % 2), each entry zeroed once
+    // read; thread t takes output row n0 + t % 64 (+ 64) and rows of X t / 64, t / 64 +
+    // nthreads / 64, ... (a workgroup's run is at most 16 U <= 128 rows)
 #define QW_OUT_BLOCK(MB_)                                                                        \
     {                                                                                            \
         int* sb_ = s_sum + ((MB_) & 1) * bsum;                                                   \
         const float* sa_ = s_a + ((MB_) & 1) * 16;                                               \
         const int mv_ = min(p.M - 16 * (MB_), 16);                                               \
-        for (int e_ = tid; e_ < mv_ * nrows; e_ += nthreads) {                                   \
-            const int m_ = e_ / nrows, nn_ = e_ - m_ * nrows;                                    \
-            int* cell_ = sb_ + ((nn_ >> 4) * 16 + m_) * kBalSumPitch + (nn_ & 15);               \
-            const int v_ = *cell_;                                                               \
-            *cell_ = 0;                                                                          \
-            p.Y[(size_t)(16 * (MB_) + m_) * p.N + n0 + nn_] = ((float)(v_ >> 4) * s_sc[nn_]) * sa_[m_]; \
+        float* y_ = p.Y + (size_t)(16 * (MB_)) * p.N + n0;                                       \
+        _Pragma("unroll") for (int h_ = 0; h_ < (U > 4 ? 2 : 1); ++h_)                           \
+        {                                                                                        \
+            const int nn_ = lane + 64 * h_;                                                      \
+            if (nn_ < nrows) {                                                                   \
+                const float sc_ = s_sc[nn_];                                                     \
+                for (int m_ = wave; m_ < mv_; m_ += nthreads >> 6) {                             \
+                    int* cell_ = sb_ + ((nn_ >> 4) * 16 + m_) * kBalSumPitch + (nn_ & 15);       \
+                    const int v_ = *cell_;                                                       \
+                    *cell_ = 0;                                                                  \
+                    y_[(size_t)m_ * p.N + nn_] = ((float)(v_ >> 4) * sc_) * sa_[m_];             \
+                }                                                                                \
+            }                                                                                    \
         }                                                                                        \
     }
 
@@ -568,6 +577,7 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
     // r % 4; 16 k = chunk 2 s + g / 2, half g % 2
     const int a_off = (r >> 2) * kW4TilePitch + (r & 3) * kW4RowPitch + (g >> 1) * 16 + (g & 1) * 8;
     uint2 ua[U][8];  // regrouped A operands of every unit of the wave
+    uint32_t ush = 4u, umask = 0xF0F0F0F0u;
     // block 0 of X as the weights stream in
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -594,6 +604,10 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
     QW_OUT_BLOCK(0);
     // blocks 1 .. MBT-1 against the A operands held in registers
     for (int mb = 1; mb < MBT; ++mb) {
+        uint32_t z;
+        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+        ush = 4u + z;
+        umask = 0xF0F0F0F0u + z;
 #pragma unroll
         for (int s = 0; s < 8; ++s)
             bo[s] = bn[s];

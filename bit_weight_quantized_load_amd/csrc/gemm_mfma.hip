@@ -462,11 +462,14 @@ constexpr int kBalmMaxRows = 1024;   // rows of X of the kernel over many blocks
 // 8 KB of step w, loaded straight into registers.  Block 0 of X goes through the
 // one-unit-ahead pipeline as the weights stream in, and each unit's regrouped A
 // operands stay in registers (16 VGPRs a unit); blocks 1 .. MBT-1 are then multiplied
-// against them, the next block's operands requested one block ahead.  The CG partial
-// sums of an output meet in one of two LDS total buffers (integer adds, exact in any
-// order); after one barrier per block the workgroup writes that block's outputs and
-// zeroes each entry it reads.
-template <int U>
+// against them, the next block's operands requested one block ahead; with PAIR, two
+// blocks at a time, each unpacked A operand feeding both (the block loop is bound by the
+// nibble unpack on the vector ALU, 6 instructions per multiply), their operands
+// requested at the start of the pair.  The CG partial sums of an output meet in one of
+// two (PAIR: four) LDS total buffers (integer adds, exact in any order); after one
+// barrier per block (pair) the workgroup writes the outputs and zeroes each entry it
+// reads.
+template <int U, bool PAIR>
 __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
 {
     // LDS: per wave 4 padded tiles, two int32 total buffers [nbmax][16 m][17], the row
@@ -490,8 +493,9 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
     const rsrc_t ares = make_rsrc(p.a_scale, (uint32_t)p.M * 4u);
     uint8_t* s_w = s_mem + wave * 4 * kW4TilePitch;
     int* s_sum = reinterpret_cast<int*>(s_mem + 8 * 4 * kW4TilePitch);
-    float* s_sc = reinterpret_cast<float*>(s_sum + 2 * bsum);
-    float* s_a = s_sc + 4 * 4 * p.nbmax;  // [2][16]
+    constexpr int kBufs = PAIR ? 4 : 2;  // int32 total buffers (and sets of a-scales)
+    float* s_sc = reinterpret_cast<float*>(s_sum + kBufs * bsum);
+    float* s_a = s_sc + 4 * 4 * p.nbmax;  // [kBufs][16]
 
     // X operands of block MB_ at step w: substep s -> 16 bytes at (MB_ KS + 8 w + s) KB
     // + 16 lane (zeros past K)
@@ -532,8 +536,8 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
     // nthreads / 64, ... (a workgroup's run is at most 16 U <= 128 rows)
 #define QW_OUT_BLOCK(MB_)                                                                        \
     {                                                                                            \
-        int* sb_ = s_sum + ((MB_) & 1) * bsum;                                                   \
-        const float* sa_ = s_a + ((MB_) & 1) * 16;                                               \
+        int* sb_ = s_sum + ((MB_) & (kBufs - 1)) * bsum;                                         \
+        const float* sa_ = s_a + ((MB_) & (kBufs - 1)) * 16;                                     \
         const int mv_ = min(p.M - 16 * (MB_), 16);                                               \
         float* y_ = p.Y + (size_t)(16 * (MB_)) * p.N + n0;                                       \
         _Pragma("unroll") for (int h_ = 0; h_ < (U > 4 ? 2 : 1); ++h_)                           \
@@ -566,7 +570,7 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
         s_sc[tid + nthreads] = __uint_as_float(sr1);
     if (tid < 16)
         s_a[tid] = __uint_as_float(ar);
-    for (int e = tid; e < 2 * bsum; e += nthreads)
+    for (int e = tid; e < kBufs * bsum; e += nthreads)
         s_sum[e] = 0;
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
@@ -595,35 +599,90 @@ __global__ __launch_bounds__(512) void k_gemm_w4a8_bals(MfmaW4A8Args p)
             QW_UNIT_MFMA(u, s_sum);
         }
     }
-    if (MBT > 1)
+    if (!PAIR && MBT > 1)
         QW_LOADB(bn, 1);
     float an = 0.0f;
-    if (MBT > 1)
+    if (!PAIR && MBT > 1)
         an = __uint_as_float(load4(ares, (uint32_t)(16 + (tid & 15)) * 4u));
     __syncthreads();
     QW_OUT_BLOCK(0);
-    // blocks 1 .. MBT-1 against the A operands held in registers
-    for (int mb = 1; mb < MBT; ++mb) {
-        uint32_t z;
-        asm volatile("s_mov_b32 %0, 0" : "=s"(z));
-        ush = 4u + z;
-        umask = 0xF0F0F0F0u + z;
+    if (PAIR) {
+        // blocks 1 .. MBT-1 two at a time: each unpacked A operand feeds two multiplies
+        for (int mb = 1; mb < MBT; mb += 2) {
+            uint32_t z;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+            ush = 4u + z;
+            umask = 0xF0F0F0F0u + z;
+            const bool two = mb + 1 < MBT;
+            QW_LOADB(bo, mb);
+            if (two) {
+                QW_LOADB(bn, mb + 1);
+            } else {
 #pragma unroll
-        for (int s = 0; s < 8; ++s)
-            bo[s] = bn[s];
-        if (tid < 16)
-            s_a[(mb & 1) * 16 + tid] = an;
-        if (mb + 1 < MBT) {
-            QW_LOADB(bn, mb + 1);
-            an = __uint_as_float(load4(ares, (uint32_t)(16 * (mb + 1) + (tid & 15)) * 4u));
+                for (int s = 0; s < 8; ++s)
+                    bn[s] = uint4{0u, 0u, 0u, 0u};
+            }
+            if (tid < 16) {
+                s_a[(mb & 3) * 16 + tid] = __uint_as_float(load4(ares, (uint32_t)(16 * mb + tid) * 4u));
+                s_a[((mb + 1) & 3) * 16 + tid] =
+                    __uint_as_float(load4(ares, (uint32_t)(16 * (mb + 1) + tid) * 4u));
+            }
+            int* sb0 = s_sum + (mb & 3) * bsum;
+            int* sb1 = s_sum + ((mb + 1) & 3) * bsum;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                if (u < nb) {
+                    v4i acc0 = v4i{0, 0, 0, 0}, acc1 = v4i{0, 0, 0, 0};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const uint2 w_ = ua[u][s];
+                        const v4i a_ = {(int)((w_.x << ush) & umask), (int)(w_.x & umask),
+                                        (int)((w_.y << ush) & umask), (int)(w_.y & umask)};
+                        const v4i b0 = {(int)bo[s].x, (int)bo[s].y, (int)bo[s].z, (int)bo[s].w};
+                        const v4i b1 = {(int)bn[s].x, (int)bn[s].y, (int)bn[s].z, (int)bn[s].w};
+                        acc0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, b0, acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_, b1, acc1, 0, 0, 0);
+                    }
+                    int* d0 = sb0 + (u * 16 + r) * kBalSumPitch + 4 * g;
+                    int* d1 = sb1 + (u * 16 + r) * kBalSumPitch + 4 * g;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        __hip_atomic_fetch_add(d0 + i, acc0[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                        if (two)
+                            __hip_atomic_fetch_add(d1 + i, acc1[i], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_WORKGROUP);
+                    }
+                }
+            }
+            __syncthreads();
+            QW_OUT_BLOCK(mb);
+            if (two)
+                QW_OUT_BLOCK(mb + 1);
         }
-        int* sb = s_sum + (mb & 1) * bsum;
+    } else {
+        // blocks 1 .. MBT-1 against the A operands held in registers
+        for (int mb = 1; mb < MBT; ++mb) {
+            uint32_t z;
+            asm volatile("s_mov_b32 %0, 0" : "=s"(z));
+            ush = 4u + z;
+            umask = 0xF0F0F0F0u + z;
 #pragma unroll
-        for (int u = 0; u < U; ++u)
-            if (u < nb)
-                QW_UNIT_MFMA(u, sb);
-        __syncthreads();
-        QW_OUT_BLOCK(mb);
+            for (int s = 0; s < 8; ++s)
+                bo[s] = bn[s];
+            if (tid < 16)
+                s_a[(mb & 1) * 16 + tid] = an;
+            if (mb + 1 < MBT) {
+                QW_LOADB(bn, mb + 1);
+                an = __uint_as_float(load4(ares, (uint32_t)(16 * (mb + 1) + (tid & 15)) * 4u));
+            }
+            int* sb = s_sum + (mb & 1) * bsum;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                if (u < nb)
+                    QW_UNIT_MFMA(u, sb);
+            __syncthreads();
+            QW_OUT_BLOCK(mb);
+        }
     }
 #undef QW_LOADB
 #undef QW_LOADU
@@ -971,19 +1030,23 @@ hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
     return go_w4_bal_u<NW, 16>(p, nwg, lds, st);
 }
 
-template <int U>
+template <int U, bool PAIR>
 hipError_t go_w4_bals_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
 {
-    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bals<U>),
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bals<U, PAIR>),
                                           (size_t)96 * 1024);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_gemm_w4a8_bals<U>), dim3((unsigned)nwg), dim3(64 * p.cg), lds, st, p);
+    hipLaunchKernelGGL((k_gemm_w4a8_bals<U, PAIR>), dim3((unsigned)nwg), dim3(64 * p.cg), lds, st, p);
     return hipGetLastError();
 }
 
 hipError_t go_w4_bals(MfmaW4A8Args p, int cus, hipStream_t st)
 {
+    // blocks after the first two at a time from three blocks of X on (measured on
+    // 4096 -> 27392: 88.8 against 104.6 us at 512 rows, 33.9 against 37.6 at 128;
+    // with two blocks the pair would be half empty: 18.9 against 18.0 us at 17 rows)
+    const bool pair = p.mbtot >= 3;
     if (p.cg > 8 || p.M > kBalmMaxRows)
         return hipErrorInvalidValue;
     // one workgroup per CU, at least four row groups and at most 8 output blocks each
@@ -994,12 +1057,12 @@ hipError_t go_w4_bals(MfmaW4A8Args p, int cus, hipStream_t st)
     p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 3) / 4;
     p.mgroups = 1;
     // the LDS it needs, padded so that one workgroup fills a CU
-    const size_t need = (size_t)8 * 4 * kW4TilePitch + (size_t)2 * p.nbmax * 16 * kBalSumPitch * 4 +
-                        (size_t)(16 * p.nbmax + 32) * 4;
+    const size_t need = (size_t)8 * 4 * kW4TilePitch + (size_t)4 * p.nbmax * 16 * kBalSumPitch * 4 +
+                        (size_t)(16 * p.nbmax + 64) * 4;
     const size_t lds = std::max(need, (size_t)82 * 1024);
-    if (p.nbmax <= 4)
-        return go_w4_bals_u<4>(p, nwg, lds, st);
-    return go_w4_bals_u<8>(p, nwg, lds, st);
+    if (pair)
+        return p.nbmax <= 4 ? go_w4_bals_u<4, true>(p, nwg, lds, st) : go_w4_bals_u<8, true>(p, nwg, lds, st);
+    return p.nbmax <= 4 ? go_w4_bals_u<4, false>(p, nwg, lds, st) : go_w4_bals_u<8, false>(p, nwg, lds, st);
 }
 
 template <int NW, int MB, int NBW>

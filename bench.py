@@ -57,8 +57,8 @@ def bytes_w8a16(M, N, K):
 
 def kernel_source_hash(kernel: str) -> str:
     csrc = os.path.join(ROOT, "bit_weight_quantized_load_amd", "csrc")
-    files = ["common.hpp", "kernels.hpp", "api.hip",
-             "gemv_w4a8.hip" if kernel == "gemv_w4a8" else "gemv_w8a16.hip"]
+    files = ["common.hpp", "kernels.hpp", "api.hip"]
+    files += ["gemv_w4a8.hip", "w4a8_prod.hpp"] if kernel == "gemv_w4a8" else ["gemv_w8a16.hip"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(csrc, f), "rb") as fh:

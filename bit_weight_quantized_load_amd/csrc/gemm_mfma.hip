@@ -453,7 +453,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
     }
 }
 
-constexpr int kBalmMaxRows = 1024;   // rows of X of the kernel over many blocks
+constexpr int kBalsMaxRows = 1024;   // rows of X of the kernel over many blocks
 
 // The balanced W4A8 kernel over many blocks of X with one wave per 512-k step (K up
 // to 4096, 1 to 1024 rows of X).  Workgroup b owns an even run of row groups, nb <= U
@@ -1047,7 +1047,7 @@ hipError_t go_w4_bals(MfmaW4A8Args p, int cus, hipStream_t st)
     // 4096 -> 27392: 88.8 against 104.6 us at 512 rows, 33.9 against 37.6 at 128;
     // with two blocks the pair would be half empty: 18.9 against 18.0 us at 17 rows)
     const bool pair = p.mbtot >= 3;
-    if (p.cg > 8 || p.M > kBalmMaxRows)
+    if (p.cg > 8 || p.M > kBalsMaxRows)
         return hipErrorInvalidValue;
     // one workgroup per CU, at least four row groups and at most 8 output blocks each
     int nwg = std::max(1, std::min(cus, p.nrg / 4));
@@ -1145,7 +1145,7 @@ void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* n
     if (bits == 4) {
         if (mbtot == 1 && k_fits) {
             *mb = 0;
-        } else if (k_fits && M <= kBalmMaxRows) {
+        } else if (k_fits && M <= kBalsMaxRows) {
             *mb = 0;
             *nbw = 2;
         } else {

@@ -890,7 +890,8 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
     if (!qw::mfma_shape_ok(8, nw, mb, nbw))
         return QW_ERR_TILING;
-    if (mb == 0 && (M > 16 || (K + 511) / 512 > 8))  // balanced: 16 rows, K up to 4096
+    // balanced: K up to 4096; nbw 1 up to 16 rows of X, nbw 2 up to 1024
+    if (mb == 0 && ((K + 511) / 512 > 8 || M > (nbw == 1 ? 16 : 1024)))
         return QW_ERR_TILING;
     return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, nw, mb, nbw, stream);
 }

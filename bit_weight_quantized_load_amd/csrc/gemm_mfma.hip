@@ -851,40 +851,48 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w8a16(MfmaW8A16Args p)
 // partial sums per block in LDS, and the epilogue adds the CG partials of an output in
 // step order (deterministic), scales once and rounds to f16.
 constexpr int kW8BalMaxBlocks = 8;   // output blocks per workgroup
+constexpr size_t kLdsBytes = 160 * 1024;  // LDS of one CU
 constexpr int kW8BalMaxSteps = 8;    // waves per workgroup (K <= 4096)
 
-template <int U>
+template <int U, int MB2>
 __global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A16Args p)
 {
-    // LDS: per wave 8 padded tiles, then the fp32 partials [CG][nbmax][16 m][17] and
-    // the row scales
+    // LDS: per wave 8 padded tiles (4 with MB2 == 2: a unit is regrouped in two halves),
+    // then the fp32 partials [MB2][CG][nbmax][16 m][17] and the row scales
     extern __shared__ uint8_t s_mem[];
+    constexpr int kStageTiles = MB2 == 2 ? 4 : 8;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // = the 512-k step
     const int nthreads = (int)blockDim.x;
     const int g = lane >> 4, r = lane & 15;
-    const int CG = p.cg, M = p.M, K = p.K;
+    const int CG = p.cg, K = p.K;
+    const int m0 = 16 * MB2 * (int)blockIdx.y;  // first row of X of this workgroup
+    const int M = min(p.M - m0, 16 * MB2);
     const int b = blockIdx.x;
     const int rg0 = min(b * p.per + min(b, p.rem), p.nrg);
     const int nrg_b = max(0, min(p.per + (b < p.rem ? 1 : 0), p.nrg - rg0));
     const int nb = min(U, (nrg_b + 7) >> 3);
     const int n0 = 2 * rg0;
     const int nrows = max(0, min(2 * nrg_b, p.N - n0));
+    const int bpart = CG * p.nbmax * 16 * 17;  // floats of the partials of one block of X
     const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nrg_b * CG) * 1024u);
-    const rsrc_t xres = make_rsrc(p.X, (uint32_t)M * (uint32_t)K * 2u);
+    const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)M * (uint32_t)K * 2u);
     const rsrc_t sres = make_rsrc(p.w_scale + n0, (uint32_t)nrows * 2u);
-    uint8_t* s_w = s_mem + wave * 8 * kW8TilePitch;
-    float* s_part = reinterpret_cast<float*>(s_mem + kW8BalMaxSteps * 8 * kW8TilePitch);
-    float* s_sc = s_part + CG * p.nbmax * 16 * 17;
+    uint8_t* s_w = s_mem + wave * kStageTiles * kW8TilePitch;
+    float* s_part = reinterpret_cast<float*>(s_mem + kW8BalMaxSteps * kStageTiles * kW8TilePitch);
+    float* s_sc = s_part + MB2 * bpart;
 
-    // X operands of step w: substep s (32 k), lane (g, r) -> X[r][512 w + 32 s + 8 g ..+7]
-    uint4 xb[16];
+    // X operands of step w for block bl of X: substep s (32 k), lane (g, r) ->
+    // X[m0 + 16 bl + r][512 w + 32 s + 8 g .. + 7]
+    uint4 xb[MB2][16];
 #pragma unroll
-    for (int s = 0; s < 16; ++s) {
-        const int k = 512 * wave + 32 * s + 8 * g;
-        xb[s] = load16(xres, r < M && k < K ? (uint32_t)(r * K + k) * 2u : 0x80000000u);
-    }
+    for (int bl = 0; bl < MB2; ++bl)
+#pragma unroll
+        for (int s = 0; s < 16; ++s) {
+            const int k = 512 * wave + 32 * s + 8 * g, m = 16 * bl + r;
+            xb[bl][s] = load16(xres, m < M && k < K ? (uint32_t)(m * K + k) * 2u : 0x80000000u);
+        }
     // the workgroup's row scales (at most 16 nbmax <= 128 rows, two per thread)
     const uint32_t sr0 = load2(sres, (uint32_t)tid * 2u);
     const uint32_t sr1 = load2(sres, (uint32_t)(tid + nthreads) * 2u);
@@ -902,15 +910,13 @@ __global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A1
         s_sc[tid] = __half2float(__ushort_as_half((uint16_t)sr0));
     if (tid + nthreads < 16 * p.nbmax)
         s_sc[tid + nthreads] = __half2float(__ushort_as_half((uint16_t)sr1));
-    v8h bo[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s)
-        bo[s] = __builtin_bit_cast(v8h, xb[s]);
 
     const int sub = lane >> 5, j = lane & 31;
     // A operand of substep s for lane (g, r): row r of the block = tile r / 2, tile row
-    // r % 2; k = 32 s + 8 g .. + 7 = chunk 2 s + g / 2, half g % 2
-    const int a_off = (r >> 1) * kW8TilePitch + (r & 1) * kW8RowPitch + (g >> 1) * 16 + (g & 1) * 8;
+    // r % 2; k = 32 s + 8 g .. + 7 = chunk 2 s + g / 2, half g % 2 (with a half-unit
+    // staging area, tile (r % 8) / 2 of half r / 8)
+    const int a_off = ((MB2 == 2 ? (r & 7) : r) >> 1) * kW8TilePitch + (r & 1) * kW8RowPitch +
+                      (g >> 1) * 16 + (g & 1) * 8;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u + 1 < U) {
@@ -918,24 +924,61 @@ __global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A1
         }
         __builtin_amdgcn_sched_barrier(0);
         if (u < nb) {
+            v4f acc[MB2];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                *reinterpret_cast<uint4*>(s_w + i * kW8TilePitch + sub * kW8RowPitch + j * 16) = wb[u][i];
-            v4f acc = v4f{0.f, 0.f, 0.f, 0.f};
+            for (int bl = 0; bl < MB2; ++bl)
+                acc[bl] = v4f{0.f, 0.f, 0.f, 0.f};
+            if constexpr (MB2 == 1) {
 #pragma unroll
-            for (int s = 0; s < 16; ++s) {
-                const uint2 w = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
-                half2_t h0, h1, h2, h3;
-                cast4(w.x, h0, h1);
-                cast4(w.y, h2, h3);
-                const v8h a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bo[s], acc, 0, 0, 0);
+                for (int i = 0; i < 8; ++i)
+                    *reinterpret_cast<uint4*>(s_w + i * kW8TilePitch + sub * kW8RowPitch + j * 16) = wb[u][i];
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    const uint2 w = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
+                    half2_t h0, h1, h2, h3;
+                    cast4(w.x, h0, h1);
+                    cast4(w.y, h2, h3);
+                    const v8h a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+                    acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(v8h, xb[0][s]),
+                                                                    acc[0], 0, 0, 0);
+                }
+            } else {
+                // regroup in two halves (tiles 0-3: rows 0-7, tiles 4-7: rows 8-15); a
+                // lane reads its row's operands in its half, the wave's own LDS writes
+                // and reads in program order
+                uint2 wa[16];
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        *reinterpret_cast<uint4*>(s_w + i * kW8TilePitch + sub * kW8RowPitch + j * 16) =
+                            wb[u][4 * h + i];
+                    if ((r >> 3) == h) {
+#pragma unroll
+                        for (int s = 0; s < 16; ++s)
+                            wa[s] = *reinterpret_cast<const uint2*>(s_w + a_off + s * 32);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < 16; ++s) {
+                    half2_t h0, h1, h2, h3;
+                    cast4(wa[s].x, h0, h1);
+                    cast4(wa[s].y, h2, h3);
+                    const v8h a = {h0[0], h0[1], h1[0], h1[1], h2[0], h2[1], h3[0], h3[1]};
+#pragma unroll
+                    for (int bl = 0; bl < MB2; ++bl)
+                        acc[bl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, __builtin_bit_cast(v8h, xb[bl][s]),
+                                                                         acc[bl], 0, 0, 0);
+                }
             }
             // lane (g, r) holds D[n = 4 g + i][m = r] of block u
-            float* dst = s_part + ((wave * p.nbmax + u) * 16 + r) * 17 + 4 * g;
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                dst[i] = acc[i];
+            for (int bl = 0; bl < MB2; ++bl) {
+                float* dst = s_part + bl * bpart + ((wave * p.nbmax + u) * 16 + r) * 17 + 4 * g;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    dst[i] = acc[bl][i];
+            }
         }
     }
 #undef QW_LOADU8
@@ -943,10 +986,10 @@ __global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A1
 
     // outputs (m, nn), independent across threads: the CG partials in step order,
     // times the row scale, rounded to f16
-    const int nout = min(M, 16) * nrows;
+    const int nout = M * nrows;
     for (int e = tid; e < nout; e += nthreads) {
         const int m = e / nrows, nn = e - m * nrows;
-        const float* src = s_part + ((nn >> 4) * 16 + m) * 17 + (nn & 15);
+        const float* src = s_part + (m >> 4) * bpart + ((nn >> 4) * 16 + (m & 15)) * 17 + (nn & 15);
         float pv[kW8BalMaxSteps];
 #pragma unroll
         for (int c = 0; c < kW8BalMaxSteps; ++c)
@@ -956,7 +999,7 @@ __global__ __launch_bounds__(64 * kW8BalMaxSteps) void k_gemm_w8a16_bal(MfmaW8A1
         for (int c = 1; c < kW8BalMaxSteps; ++c)
             if (c < CG)
                 v += pv[c];
-        p.Y[(size_t)m * p.N + n0 + nn] = __half_as_ushort(__float2half_rn(v * s_sc[nn]));
+        p.Y[(size_t)(m0 + m) * p.N + n0 + nn] = __half_as_ushort(__float2half_rn(v * s_sc[nn]));
     }
 }
 
@@ -1080,36 +1123,42 @@ hipError_t go_w8(const MfmaW8A16Args& p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int U>
+template <int U, int MB2>
 hipError_t go_w8_bal_u(const MfmaW8A16Args& p, int nwg, size_t lds, hipStream_t st)
 {
-    static const hipError_t e =
-        allow_lds(reinterpret_cast<const void*>(k_gemm_w8a16_bal<U>),
-                  (size_t)kW8BalMaxSteps * 8 * kW8TilePitch +
-                      (size_t)kW8BalMaxSteps * kW8BalMaxBlocks * 16 * 17 * 4 + 16 * kW8BalMaxBlocks * 4);
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w8a16_bal<U, MB2>), kLdsBytes);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_gemm_w8a16_bal<U>), dim3((unsigned)nwg), dim3(64 * p.cg), lds, st, p);
+    const int mrows = ((p.M + 15) / 16 + MB2 - 1) / MB2;  // workgroup rows along M
+    hipLaunchKernelGGL((k_gemm_w8a16_bal<U, MB2>), dim3((unsigned)nwg, (unsigned)mrows), dim3(64 * p.cg),
+                       lds, st, p);
     return hipGetLastError();
 }
 
-hipError_t go_w8_bal(MfmaW8A16Args p, int cus, hipStream_t st)
+// mb2: blocks of 16 rows of X per workgroup (1: M <= 16; 2: any M, workgroup rows of 32)
+hipError_t go_w8_bal(MfmaW8A16Args p, int cus, int mb2, hipStream_t st)
 {
-    if (p.M > 16 || p.cg > kW8BalMaxSteps)
+    if (p.cg > kW8BalMaxSteps || (mb2 == 1 && p.M > 16) || p.M > 1024)
         return hipErrorInvalidValue;
-    // one workgroup per CU with at least one block (8 row groups of 2 rows) each, at
-    // most kW8BalMaxBlocks blocks
+    // one workgroup per CU and row of X blocks with at least one block (8 row groups of
+    // 2 rows) each, at most kW8BalMaxBlocks blocks
+    // 2 rows of X blocks: blocks per workgroup as many as the partials leave room for
+    // in LDS (7 at 8 steps)
+    const size_t fixed = (size_t)kW8BalMaxSteps * (mb2 == 2 ? 4 : 8) * kW8TilePitch;
+    const int bmax = std::min<int>(kW8BalMaxBlocks,
+                                   (int)((kLdsBytes - fixed) / ((size_t)mb2 * p.cg * 16 * 17 * 4 + 16 * 4)));
     int nwg = std::max(1, std::min(cus, p.nrg / 8));
-    nwg = std::max(nwg, (p.nrg + 8 * kW8BalMaxBlocks - 1) / (8 * kW8BalMaxBlocks));
+    nwg = std::max(nwg, (p.nrg + 8 * bmax - 1) / (8 * bmax));
     p.per = p.nrg / nwg;
     p.rem = p.nrg % nwg;
     p.nbmax = (p.per + (p.rem > 0 ? 1 : 0) + 7) / 8;
     p.mgroups = 1;
-    const size_t lds = (size_t)kW8BalMaxSteps * 8 * kW8TilePitch +
-                       (size_t)p.cg * p.nbmax * 16 * 17 * 4 + (size_t)16 * p.nbmax * 4;
+    const size_t lds = fixed + (size_t)mb2 * p.cg * p.nbmax * 16 * 17 * 4 + (size_t)16 * p.nbmax * 4;
+    if (mb2 == 2)
+        return p.nbmax <= 4 ? go_w8_bal_u<4, 2>(p, nwg, lds, st) : go_w8_bal_u<8, 2>(p, nwg, lds, st);
     if (p.nbmax <= 4)
-        return go_w8_bal_u<4>(p, nwg, lds, st);
-    return go_w8_bal_u<8>(p, nwg, lds, st);
+        return go_w8_bal_u<4, 1>(p, nwg, lds, st);
+    return go_w8_bal_u<8, 1>(p, nwg, lds, st);
 }
 
 }  // namespace
@@ -1126,8 +1175,8 @@ bool mfma_shape_ok(int bits, int nw, int mb, int nbw)
                (mb == 0 && (nbw == 1 || nw == 8));
     // W8A16 X slices are 16 KB per block of 16 rows; eight waves of two blocks of
     // rows would not fit the registers.  mb 0: the balanced kernel (one wave per 512-k
-    // step), nw 8 and nbw 1 only
-    return ((mb == 1 || mb == 2) && !(nw == 8 && nbw == 2)) || (mb == 0 && nw == 8 && nbw == 1);
+    // step), nw 8, with nbw 1 (up to 16 rows) or 2 (two blocks of X per workgroup)
+    return ((mb == 1 || mb == 2) && !(nw == 8 && nbw == 2)) || (mb == 0 && nw == 8);
 }
 
 void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* nbw)
@@ -1136,8 +1185,10 @@ void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* n
     // 17 to 1024 rows on the one with one wave per step and the weights held in
     // registers (on 4096 -> 27392: 25.4 against 25.8 us for the streaming kernel at 64
     // rows, 39.0 against 44.2 at 128, 114.5 against 138.0 at 512); else the streaming
-    // kernel with 8 waves and 2 or 4 blocks of X.  W8A16: the balanced kernel up to 16
-    // rows, else 8 waves with 1 or 2 blocks.
+    // kernel with 8 waves and 2 or 4 blocks of X.  W8A16 with K <= 4096: the balanced
+    // kernel up to 16 rows, its two-block form for 17 to 64 (25.3 against 31.0 us for
+    // the streaming kernel at 17 rows, 28.6 against 32.3 at 32, 41.9 against 49.6 at 64
+    // on 3584 -> 18944); else 8 waves with 1 or 2 blocks.
     const int64_t mbtot = (M + 15) / 16;
     const bool k_fits = (K + 511) / 512 * 8192 <= kXAllMaxBytes;
     *nw = 8;
@@ -1151,8 +1202,9 @@ void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* n
         } else {
             *mb = mbtot >= 4 ? 4 : (mbtot >= 2 ? 2 : 1);
         }
-    } else if (mbtot == 1 && (K + 511) / 512 <= 8) {
+    } else if (mbtot <= 4 && (K + 511) / 512 <= 8) {
         *mb = 0;
+        *nbw = mbtot == 1 ? 1 : 2;
     } else {
         *mb = mbtot >= 2 ? 2 : 1;
     }
@@ -1239,8 +1291,8 @@ hipError_t launch_gemm_w8a16(const uint16_t* X, int M, int N, int K, const uint8
     p.K = K;
     p.cg = L.cg;
     p.nrg = L.nrg;
-    if (mb == 0)
-        return nw == 8 && nbw == 1 ? go_w8_bal(p, cus, st) : hipErrorInvalidValue;
+    if (mb == 0)  // balanced: nbw 1 one block of X per workgroup, nbw 2 two
+        return nw == 8 ? go_w8_bal(p, cus, nbw, st) : hipErrorInvalidValue;
     p.mgroups = (mbtot + mb - 1) / mb;
 #define QW_GO(NW_, MB_, NBW_)                                                                    \
     if (nw == NW_ && mb == MB_ && nbw == NBW_)                                                   \

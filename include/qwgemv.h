@@ -229,9 +229,10 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
    balanced kernel, one workgroup per CU and block of 16 rows of X, with that block's
    activation codes resident in on-chip memory; with nw 8 and nbw 2 and 17 to 1024 rows,
    one workgroup per CU over all blocks of X, the weights held in registers after one
-   pass.  W8A16 takes mb = 0 too (nw 8, nbw 1,
-   M <= 16, K <= 4096): the balanced kernel with one wave per 512-k step, whose f16 X
-   operands stay in registers.  Rows of X are padded to a multiple of 16 with
+   pass.  W8A16 takes mb = 0 too (nw 8, K <= 4096): the balanced kernel with one wave
+   per 512-k step, whose f16 X operands stay in registers, with one block of 16 rows of X
+   per workgroup (nbw 1, M <= 16) or two (nbw 2, M <= 1024; each INT8 weight converted
+   once for both).  Rows of X are padded to a multiple of 16 with
    zeros.  The W4A8 one needs a workspace of qw_workspace_bytes(2, M, N, K) bytes (else
    QW_ERR_WORKSPACE).  Results do not depend on the launch shape; the W4A8 outputs equal
    gemv_w4a8's bit for bit.  QW_ERR_TILING for an invalid shape. */

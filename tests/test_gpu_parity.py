@@ -406,6 +406,45 @@ def test_balanced_w8a16_matrix_core_kernel_matches_oracle(M, N, K):
     assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 
 
+W8_BALANCED_MULTI_SHAPES = [(17, 1000, 1056), (32, 27392, 4096), (40, 600, 544), (64, 4100, 3584),
+                            (100, 38, 96), (300, 2050, 512), (33, 40000, 512)]
+
+
+@pytest.mark.parametrize("M,N,K", W8_BALANCED_MULTI_SHAPES)
+def test_balanced_w8a16_two_block_kernel_matches_oracle(M, N, K):
+    """The balanced W8A16 kernel with two 16-row blocks of X per workgroup (nbw 2)."""
+    say("balanced w8a16 mfma two blocks", M, N, K)
+    W = wl.weights(720 + M, 1, N, K, outlier_rows=True)
+    X16 = wl.activations(720 + M, 2, M, K, outlier_channels=4).astype(np.float16)
+    X16[M // 2, : K // 3] = 0
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    Xd = dev(X16)
+    y = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 2))
+    assert rel_l2(y, y64) <= W8A16_RL2
+    assert np.all(np.isfinite(y.astype(np.float32)))
+    # each row of X is summed in the same order as by the one-block kernel
+    if M <= 16:
+        y1 = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 1))
+        assert np.array_equal(y.view(np.uint16), y1.view(np.uint16))
+    yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
+    assert rel_l2(yd, y64) <= W8A16_RL2
+    if M <= 64:  # the default path at 17 to 64 rows is this kernel
+        assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
+
+
+def test_balanced_w8a16_kernel_limits():
+    K, N = 512, 64
+    W = wl.weights(730, 1, N, K)
+    Wq8, s16, _, _ = pack_w8_and_check(W)
+    X17 = dev(wl.activations(731, 2, 17, K).astype(np.float16))
+    with pytest.raises(qw.QWError):
+        qw.gemm_w8a16_mfma(X17, Wq8, s16, 8, 0, 1)  # one block: at most 16 rows
+    X = dev(wl.activations(732, 2, 1025, K).astype(np.float16))
+    with pytest.raises(qw.QWError):
+        qw.gemm_w8a16_mfma(X, Wq8, s16, 8, 0, 2)  # two blocks: at most 1024 rows
+
+
 def test_skinny_gemm_workspace_reuse_and_sizes():
     """One workspace sized for the larger call serves a smaller one after it."""
     K, N = 1024, 96

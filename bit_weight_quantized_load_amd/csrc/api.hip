@@ -93,7 +93,19 @@ bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
         const int64_t per_blk = ((int64_t)L.nrg + blocks - 1) / blocks;
         return per_blk <= 16 && per_blk * L.cg * 1024 < ((int64_t)1 << 31);
     }
-    if (u < 0 || u > 8 || u == 5 || u == 6 || u == 7)
+    // balanced long-K variant (INT8, M == 1): nwaves workgroups (one per CU, more only
+    // past 16 row groups each) of nw == splitk waves, each taking a k-slice of every row
+    // group of the workgroup: up to 16 waves with slices of at most 4 tiles, up to 8
+    // with slices of at most 8
+    if (u == 7) {
+        const int T = (L.cg + splitk - 1) / splitk;
+        if (bits != 8 || M != 1 || nw != splitk || splitk < 1 || T > 8 || splitk > (T <= 4 ? 16 : 8) ||
+            nwaves < 1)
+            return false;
+        const int64_t per = ((int64_t)L.nrg + nwaves - 1) / nwaves;
+        return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31);
+    }
+    if (u < 0 || u > 8 || u == 5 || u == 6)
         return false;
     // all in flight with K split over 2..8 (INT4) or 2..7 (INT8) waves of 8-tile slices:
     // one row run of at most 4 row groups per workgroup, M == 1, K <= 4096 * splitk
@@ -153,6 +165,14 @@ GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw,
         t.splitk = u == 5 ? 1 : splitk;
         t.blocks = nwaves / nw;
         t.reg_cg = u == 5 ? L.cg : std::max(5, (L.cg + splitk - 1) / splitk);
+        t.mt = 1;
+        t.m_tiles = 1;
+        t.lds_bytes = 0;
+        return t;
+    }
+    if (u == 7) {
+        t.blocks = nwaves;
+        t.reg_cg = (L.cg + splitk - 1) / splitk;  // tiles per k-slice
         t.mt = 1;
         t.m_tiles = 1;
         t.lds_bytes = 0;
@@ -284,6 +304,18 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
         return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
     }
+    // INT8, M == 1, K > 4096 from 1024 row groups: the balanced long-K variant, one
+    // workgroup per CU of min(8, ceil(CG / 4)) waves, one k-slice each (18944 -> 3584:
+    // 12.9 us against 13.9 us for the LDS variant split over two waves; 18944 -> 4608:
+    // 16.7 against 19.3; 28672 -> 3584: 17.8 against 19.2; 8192 -> 2048: 5.1 against 5.9;
+    // at 512 row groups, 18944 -> 1024, the all-in-flight split below stays faster:
+    // 6.0 against 6.9)
+    if (bits == 8 && M == 1 && L.cg > qw::kRegCG && nrg >= 1024) {
+        const int S = (int)std::min<int64_t>(8, (L.cg + 3) / 4);
+        const int64_t nwg = std::max<int64_t>(std::min<int64_t>(device_cus(), nrg), (nrg + 15) / 16);
+        if (tiling_ok(bits, M, 7, S, (int)nwg, S, L))
+            return make_tiling(bits, M, N, K, 7, S, (int)nwg, S);
+    }
     // M == 1 with K > 4096: all in flight with K split into 8-tile slices, one wave per
     // slice, where that measured faster: INT4 always (18944 -> 3584: 13.6 us against
     // 14.7 us; 18944 -> 512: 7.5 against 13.7), INT8 below 1024 row groups (18944 -> 512:
@@ -297,7 +329,7 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
             return t;
     }
     if (bits == 8 && M == 1 && nrg < 2048) {
-        // long K, short N (the 18944 -> 3584 down projection): split K over two waves
+        // long K, short N where neither form above applies: split K over two waves
         const GemvTiling t = make_tiling(bits, M, N, K, 4, 8, (int)nrg, 2);
         if (t.lds_bytes <= kMaxLds)
             return t;

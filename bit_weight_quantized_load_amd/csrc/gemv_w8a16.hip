@@ -594,6 +594,118 @@ __global__ __launch_bounds__(64 * S) void k_gemv_w8a16_flight_split(W8A16Args p)
     }
 }
 
+// Balanced long-K form (M == 1): one workgroup per CU (more only past U row groups per
+// CU) owns an even run of row groups; its S waves each take a k-slice of T tiles of every
+// row group of the run, so each lane's f16 activations of the slice (T chunks of 16)
+// stay in registers for the whole run.  A unit is one row group's T tiles of the wave's
+// slice; the run goes through an unrolled pipeline with one unit requested ahead, X and
+// the scales requested before any weight.  Up to 16 waves with slices of at most 4
+// tiles, 8 with longer ones (their registers).  The per-slice fp32 row sums meet in LDS and
+// are added in slice order (deterministic) before the scale and the f16 rounding.
+constexpr int kBsMaxWaves = 16;
+
+template <int T, int U>
+__global__ __launch_bounds__(T <= 4 ? 64 * kBsMaxWaves : 512) void k_gemv_w8a16_bsplit(W8A16Args p)
+{
+    __shared__ float s_part[2 * U * kBsMaxWaves];  // [row of the run][slice]
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // the k-slice of this wave
+    const int S = (int)(blockDim.x >> 6);
+    const int j = lane & 31, sub = lane >> 5;
+    const int N = p.N, K = p.K, CG = p.cg;
+    const int c_lo = ks * T;
+    const int b = blockIdx.x;
+    const int rg0 = rg_of(b, p.per, p.rem);
+    const int nb = min(U, rg_of(b + 1, p.per, p.rem) - rg0);
+    const int nrows = max(0, min(2 * nb, N - 2 * rg0));
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nb * CG) * 1024u);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 2, (uint32_t)nrows * 2u);
+    const rsrc_t xres = make_rsrc(p.X, (uint32_t)K * 2u);
+
+    // lane (j, sub): chunk j (16 k) of tile c of the slice -> X[512 (c_lo + c) + 16 j ..]
+    uint4 xp[T][2];
+#pragma unroll
+    for (int c = 0; c < T; ++c) {
+        const int k = 512 * (c_lo + c) + 16 * j;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xp[c][h] = load16(xres, k < K ? (uint32_t)(k + 8 * h) * 2u : 0x80000000u);
+    }
+    const uint16_t sc_reg = load2(sres, (uint32_t)tid * 2u);
+    uint4 w[U][T];
+    // the T tiles of unit U_ (row group U_ of the run; zeros past the run and past CG)
+#define QW_LOADW(U_)                                                                             \
+    _Pragma("unroll") for (int c_ = 0; c_ < T; ++c_)                                             \
+        w[U_][c_] = load16_stream(wres, (U_) < nb && c_lo + c_ < CG                              \
+                                            ? (uint32_t)((U_) * CG + c_lo + c_) * 1024u +        \
+                                                  (uint32_t)lane * 16u                           \
+                                            : 0x80000000u);
+    issue_barrier();
+    QW_LOADW(0);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t act[T][8];
+#pragma unroll
+    for (int c = 0; c < T; ++c)
+        split8(xp[c][0], xp[c][1], act[c]);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) {
+            QW_LOADW(u + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < nb) {
+            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int c = 0; c < T; ++c)
+                dot_chunk_f16(w[u][c], act[c], acc);
+            const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
+            if (j == 31)
+                s_part[(2 * u + sub) * kBsMaxWaves + ks] = v;
+        }
+    }
+#undef QW_LOADW
+    __syncthreads();
+    if (tid < nrows) {
+        float v = s_part[tid * kBsMaxWaves];
+        for (int k = 1; k < S; ++k)
+            v += s_part[tid * kBsMaxWaves + k];
+        const float sc = __half2float(__ushort_as_half(sc_reg));
+        p.Y[2 * rg0 + tid] = __half_as_ushort(__float2half_rn(v * sc));
+    }
+}
+
+template <int T, int U>
+hipError_t launch_bsplit_u(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    if (t.splitk > (T <= 4 ? kBsMaxWaves : 8))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemv_w8a16_bsplit<T, U>), dim3(t.blocks), dim3(64 * t.splitk), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int T>
+hipError_t launch_bsplit_t(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    const int per = a.per + (a.rem > 0 ? 1 : 0);
+    return per <= 8 ? launch_bsplit_u<T, 8>(a, t, st) : launch_bsplit_u<T, 16>(a, t, st);
+}
+
+hipError_t launch_bsplit(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    switch (t.reg_cg) {
+    case 1: return launch_bsplit_t<1>(a, t, st);
+    case 2: return launch_bsplit_t<2>(a, t, st);
+    case 3: return launch_bsplit_t<3>(a, t, st);
+    case 4: return launch_bsplit_t<4>(a, t, st);
+    case 5: return launch_bsplit_t<5>(a, t, st);
+    case 6: return launch_bsplit_t<6>(a, t, st);
+    case 7: return launch_bsplit_t<7>(a, t, st);
+    case 8: return launch_bsplit_t<8>(a, t, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <int RPW, int S>
 hipError_t launch_flight_split(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
@@ -741,6 +853,8 @@ hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_
         return launch_flight_any(a, t, st);
     if (t.u == 3)
         return launch_flight_split_any(a, t, st);
+    if (t.u == 7)
+        return launch_bsplit(a, t, st);
     switch (t.nw) {
     case 4: return launch_nw<4>(a, t, st);
     case 8: return launch_nw<8>(a, t, st);

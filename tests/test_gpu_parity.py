@@ -671,6 +671,70 @@ def test_split_k_launch_shapes(M, N, K):
                     assert rel_l2(y, y64) <= W8A16_RL2, ("flight split", S, per)
 
 
+# The balanced long-K W8A16 variant (u = 7, M = 1): the 18944 -> 3584 down projection,
+# K = 28672 (the longest W8A16 row), ragged N (a partial row group), tiny N (fewer row
+# groups than workgroups), short K (one slice) and more than 8 row groups per workgroup
+W8_BSPLIT_SHAPES = [(3584, 18944), (512, 18944), (301, 28672), (5, 8192), (4100, 3584),
+                    (640, 4608), (2000, 96)]
+
+
+@pytest.mark.parametrize("N,K", W8_BSPLIT_SHAPES)
+def test_balanced_long_k_w8a16_matches_oracle(N, K):
+    say("w8a16 balanced long k", N, K)
+    W = wl.weights(760 + N % 97, 1, N, K, outlier_rows=N >= 100)
+    X16 = wl.activations(761 + N % 97, 2, 1, K, outlier_channels=4).astype(np.float16)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    X16d = dev(X16)
+    cg, nrg = -(-K // 512), -(-N // 2)
+    ref = None
+    n = 0
+    s8 = max(1, -(-cg // 8))
+    for S in sorted({s8, min(8, s8 + 1), 8, max(1, -(-cg // 4)), 16}):
+        T = -(-cg // S)
+        if T > 8 or S > (16 if T <= 4 else 8):
+            continue
+        for nwaves in sorted({1, 7, 256, -(-nrg // 16), nrg}):
+            if nwaves > nrg or -(-nrg // nwaves) > 16:
+                continue
+            y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 7, S, nwaves, S))
+            assert rel_l2(y, y64) <= W8A16_RL2, (S, nwaves)
+            assert np.all(np.isfinite(y.astype(np.float32)))
+            # the slices' sums are added in slice order: the number of workgroups does
+            # not change the bits
+            if ref is None or ref[0] != S:
+                ref = (S, y)
+            else:
+                assert np.array_equal(y.view(np.uint16), ref[1].view(np.uint16)), (S, nwaves)
+            n += 1
+    assert n >= 4
+    yd = host(qw.gemv_w8a16(X16d, Wq8, s16))
+    assert rel_l2(yd, y64) <= W8A16_RL2
+
+
+def test_balanced_long_k_w8a16_limits():
+    N, K = 64, 8192
+    W = wl.weights(770, 1, N, K)
+    Wq8, s16, _, _ = pack_w8_and_check(W)
+    X16d = dev(wl.activations(771, 2, 1, K).astype(np.float16))
+    for bad in [(7, 1, 2, 1),    # 16 tiles in one slice (at most 8)
+                (7, 17, 2, 17),  # more than 16 waves
+                (7, 4, 2, 2),    # nw must equal splitk (one wave per slice)
+                (7, 2, 1, 2)]:   # 32 row groups on one workgroup (at most 16)
+        with pytest.raises(qw.QWError):
+            qw.gemv_w8a16_tiled(X16d, Wq8, s16, *bad)
+    X2 = dev(wl.activations(772, 2, 2, K).astype(np.float16))
+    with pytest.raises(qw.QWError):
+        qw.gemv_w8a16_tiled(X2, Wq8, s16, 7, 2, 4, 2)  # M == 1 only
+    N2, K2 = 64, 28672  # 56 tiles: 9 or 10 waves would take 7 or 6 tiles each (at most 8 waves)
+    W2 = wl.weights(773, 1, N2, K2)
+    Wq2, s2, _, _ = pack_w8_and_check(W2)
+    X3 = dev(wl.activations(774, 2, 1, K2).astype(np.float16))
+    for S in (9, 10):
+        with pytest.raises(qw.QWError):
+            qw.gemv_w8a16_tiled(X3, Wq2, s2, 7, S, 4, S)
+
+
 def test_repeated_calls_are_deterministic():
     K, N, M = 4096, 2048, 1
     W = wl.weights(66, 1, N, K)

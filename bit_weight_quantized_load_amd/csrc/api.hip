@@ -93,13 +93,14 @@ bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
         const int64_t per_blk = ((int64_t)L.nrg + blocks - 1) / blocks;
         return per_blk <= 16 && per_blk * L.cg * 1024 < ((int64_t)1 << 31);
     }
-    // balanced long-K variant (INT8, M == 1): nwaves workgroups (one per CU, more only
-    // past 16 row groups each) of nw == splitk waves, each taking a k-slice of every row
-    // group of the workgroup: up to 16 waves with slices of at most 4 tiles, up to 8
-    // with slices of at most 8
+    // balanced long-K variant (INT8): nwaves workgroups (one per CU, more only past 16
+    // row groups each) of nw == splitk waves, each taking a k-slice of every row group
+    // of the workgroup, for 1, 2 or 4 rows of X (a grid row per such group of rows):
+    // at M == 1 up to 16 waves with slices of at most 4 tiles, else up to 8 waves with
+    // slices of at most 8 tiles (at most 5 when M >= 3)
     if (u == 7) {
         const int T = (L.cg + splitk - 1) / splitk;
-        if (bits != 8 || M != 1 || nw != splitk || splitk < 1 || T > 8 || splitk > (T <= 4 ? 16 : 8) ||
+        if (bits != 8 || nw != splitk || splitk < 1 || T > 8 || splitk > (T <= 4 && M == 1 ? 16 : 8) ||
             nwaves < 1)
             return false;
         const int64_t per = ((int64_t)L.nrg + nwaves - 1) / nwaves;
@@ -173,8 +174,8 @@ GemvTiling make_tiling(int bits, int64_t M, int64_t N, int64_t K, int u, int nw,
     if (u == 7) {
         t.blocks = nwaves;
         t.reg_cg = (L.cg + splitk - 1) / splitk;  // tiles per k-slice
-        t.mt = 1;
-        t.m_tiles = 1;
+        t.mt = M == 1 ? 1 : (M >= 3 && t.reg_cg <= 5 ? 4 : 2);  // rows of X per workgroup
+        t.m_tiles = (int)((M + t.mt - 1) / t.mt);
         t.lds_bytes = 0;
         return t;
     }
@@ -250,6 +251,10 @@ int device_cus()
 }
 
 // Built-in launch shape of the GEMV kernels (M == 1 for W4A8, M <= 2 for W8A16).
+// Rows of X up to which W8A16 with K > 4096 runs the balanced long-K GEMV variant
+// instead of the matrix-core kernels.
+constexpr int64_t kBsplitMaxM8 = 16;
+
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
     // Launch shapes picked by timing on MI355X at the decode shapes.  INT4 with
@@ -304,13 +309,16 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
         return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
     }
-    // INT8, M == 1, K > 4096 from 1024 row groups: the balanced long-K variant, one
-    // workgroup per CU of min(8, ceil(CG / 4)) waves, one k-slice each (18944 -> 3584:
-    // 12.9 us against 13.9 us for the LDS variant split over two waves; 18944 -> 4608:
-    // 16.7 against 19.3; 28672 -> 3584: 17.8 against 19.2; 8192 -> 2048: 5.1 against 5.9;
-    // at 512 row groups, 18944 -> 1024, the all-in-flight split below stays faster:
-    // 6.0 against 6.9)
-    if (bits == 8 && M == 1 && L.cg > qw::kRegCG && nrg >= 1024) {
+    // INT8 with K > 4096, M == 1 from 1024 row groups and 2 to 16 rows always: the
+    // balanced long-K variant, one workgroup per CU of min(8, ceil(CG / 4)) waves, one
+    // k-slice each, 1, 2 or 4 rows of X per workgroup (at M == 1, 18944 -> 3584: 12.9 us
+    // against 13.9 us for the LDS variant split over two waves; 18944 -> 4608: 16.7
+    // against 19.3; 28672 -> 3584: 17.8 against 19.2; 8192 -> 2048: 5.1 against 5.9; at
+    // 512 row groups, 18944 -> 1024, the all-in-flight split below stays faster: 6.0
+    // against 6.9.  From 2 rows it replaces the LDS variant and the matrix-core kernels,
+    // whose 128-row workgroups leave most CUs idle at these N: 18944 -> 3584 at 2, 4, 8
+    // and 16 rows 14.3, 18.0, 32.7 and 62.0 us against 26.2, 82.0, 82.3 and 83.5)
+    if (bits == 8 && L.cg > qw::kRegCG && M <= kBsplitMaxM8 && (M >= 2 || nrg >= 1024)) {
         const int S = (int)std::min<int64_t>(8, (L.cg + 3) / 4);
         const int64_t nwg = std::max<int64_t>(std::min<int64_t>(device_cus(), nrg), (nrg + 15) / 16);
         if (tiling_ok(bits, M, 7, S, (int)nwg, S, L))
@@ -877,7 +885,7 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
     (void)ws_bytes;
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (M >= qw::kMfmaMinM8) {
+    if (M >= qw::kMfmaMinM8 && !(K > 512 * qw::kRegCG && M <= kBsplitMaxM8)) {
         int nw, mb, nbw;
         qw::mfma_default_shape(8, M, K, &nw, &mb, &nbw);
         return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, nw, mb, nbw,

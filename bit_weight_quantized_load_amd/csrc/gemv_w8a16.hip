@@ -594,44 +594,52 @@ __global__ __launch_bounds__(64 * S) void k_gemv_w8a16_flight_split(W8A16Args p)
     }
 }
 
-// Balanced long-K form (M == 1): one workgroup per CU (more only past U row groups per
-// CU) owns an even run of row groups; its S waves each take a k-slice of T tiles of every
-// row group of the run, so each lane's f16 activations of the slice (T chunks of 16)
-// stay in registers for the whole run.  A unit is one row group's T tiles of the wave's
-// slice; the run goes through an unrolled pipeline with one unit requested ahead, X and
-// the scales requested before any weight.  Up to 16 waves with slices of at most 4
-// tiles, 8 with longer ones (their registers).  The per-slice fp32 row sums meet in LDS and
-// are added in slice order (deterministic) before the scale and the f16 rounding.
+// Balanced long-K form: one workgroup per CU (more only past U row groups per CU) owns
+// an even run of row groups; its S waves each take a k-slice of T tiles of every row
+// group of the run, so each lane's f16 activations of the slice (T chunks of 16, for
+// each of the workgroup's MT rows of X) stay in registers for the whole run.  A unit
+// is one row group's T tiles of the wave's slice; the run goes through an unrolled
+// pipeline with one unit requested ahead, X and the scales requested before any
+// weight.  Each weight word is cast once for the MT rows of X.  The per-slice fp32 row
+// sums meet in LDS and are added in slice order (deterministic) before the scale and
+// the f16 rounding.  Grid: (workgroups, ceil(M / MT)).  Up to 16 waves with MT == 1
+// and slices of at most 4 tiles, else up to 8 (their registers).
 constexpr int kBsMaxWaves = 16;
 
-template <int T, int U>
-__global__ __launch_bounds__(T <= 4 ? 64 * kBsMaxWaves : 512) void k_gemv_w8a16_bsplit(W8A16Args p)
+template <int T, int U, int MT>
+__global__ __launch_bounds__(T <= 4 && MT == 1 ? 64 * kBsMaxWaves : 512) void k_gemv_w8a16_bsplit(W8A16Args p)
 {
-    __shared__ float s_part[2 * U * kBsMaxWaves];  // [row of the run][slice]
+    __shared__ float s_part[MT * 2 * U * kBsMaxWaves];  // [row of X][row of the run][slice]
+    __shared__ float s_sc[2 * U];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // the k-slice of this wave
-    const int S = (int)(blockDim.x >> 6);
+    const int nthreads = (int)blockDim.x;
+    const int S = nthreads >> 6;
     const int j = lane & 31, sub = lane >> 5;
     const int N = p.N, K = p.K, CG = p.cg;
     const int c_lo = ks * T;
     const int b = blockIdx.x;
+    const int m0 = MT * (int)blockIdx.y;
+    const int mv = min(MT, p.M - m0);
     const int rg0 = rg_of(b, p.per, p.rem);
     const int nb = min(U, rg_of(b + 1, p.per, p.rem) - rg0);
     const int nrows = max(0, min(2 * nb, N - 2 * rg0));
     const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nb * CG) * 1024u);
     const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 2, (uint32_t)nrows * 2u);
-    const rsrc_t xres = make_rsrc(p.X, (uint32_t)K * 2u);
+    const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)mv * (uint32_t)K * 2u);
 
-    // lane (j, sub): chunk j (16 k) of tile c of the slice -> X[512 (c_lo + c) + 16 j ..]
-    uint4 xp[T][2];
+    // lane (j, sub): chunk j (16 k) of tile c of the slice -> X[m0 + m][512 (c_lo + c) + 16 j ..]
+    uint4 xp[MT][T][2];
 #pragma unroll
-    for (int c = 0; c < T; ++c) {
-        const int k = 512 * (c_lo + c) + 16 * j;
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-            xp[c][h] = load16(xres, k < K ? (uint32_t)(k + 8 * h) * 2u : 0x80000000u);
-    }
+        for (int c = 0; c < T; ++c) {
+            const int k = 512 * (c_lo + c) + 16 * j;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                xp[m][c][h] = load16(xres, m < mv && k < K ? (uint32_t)(m * K + k + 8 * h) * 2u : 0x80000000u);
+        }
     const uint16_t sc_reg = load2(sres, (uint32_t)tid * 2u);
     uint4 w[U][T];
     // the T tiles of unit U_ (row group U_ of the run; zeros past the run and past CG)
@@ -644,10 +652,14 @@ __global__ __launch_bounds__(T <= 4 ? 64 * kBsMaxWaves : 512) void k_gemv_w8a16_
     issue_barrier();
     QW_LOADW(0);
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t act[T][8];
+    if (tid < 2 * U)
+        s_sc[tid] = __half2float(__ushort_as_half(sc_reg));
+    uint32_t act[MT][T][8];
 #pragma unroll
-    for (int c = 0; c < T; ++c)
-        split8(xp[c][0], xp[c][1], act[c]);
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < T; ++c)
+            split8(xp[m][c][0], xp[m][c][1], act[m][c]);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u + 1 < U) {
@@ -655,33 +667,71 @@ __global__ __launch_bounds__(T <= 4 ? 64 * kBsMaxWaves : 512) void k_gemv_w8a16_
         }
         __builtin_amdgcn_sched_barrier(0);
         if (u < nb) {
-            float acc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            float acc[MT][4];
 #pragma unroll
-            for (int c = 0; c < T; ++c)
-                dot_chunk_f16(w[u][c], act[c], acc);
-            const float v = half_wave_sum_from_rows(row_sum16((acc[0] + acc[1]) + (acc[2] + acc[3])));
-            if (j == 31)
-                s_part[(2 * u + sub) * kBsMaxWaves + ks] = v;
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    acc[m][d] = 0.0f;
+#pragma unroll
+            for (int c = 0; c < T; ++c) {
+                const uint32_t wd[4] = {w[u][c].x, w[u][c].y, w[u][c].z, w[u][c].w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    half2_t lo, hi;
+                    cast_i8x4_to_f16(wd[d], lo, hi);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        acc[m][d] = __builtin_amdgcn_fdot2(lo, __builtin_bit_cast(half2_t, act[m][c][2 * d]),
+                                                           acc[m][d], false);
+                        acc[m][d] = __builtin_amdgcn_fdot2(hi, __builtin_bit_cast(half2_t, act[m][c][2 * d + 1]),
+                                                           acc[m][d], false);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float v = half_wave_sum_from_rows(row_sum16((acc[m][0] + acc[m][1]) + (acc[m][2] + acc[m][3])));
+                if (j == 31)
+                    s_part[((m * U + u) * 2 + sub) * kBsMaxWaves + ks] = v;
+            }
         }
     }
 #undef QW_LOADW
     __syncthreads();
-    if (tid < nrows) {
-        float v = s_part[tid * kBsMaxWaves];
+    for (int e = tid; e < mv * nrows; e += nthreads) {
+        const int m = e / nrows, rr = e - m * nrows;
+        const float* src = s_part + (m * 2 * U + rr) * kBsMaxWaves;
+        float v = src[0];
         for (int k = 1; k < S; ++k)
-            v += s_part[tid * kBsMaxWaves + k];
-        const float sc = __half2float(__ushort_as_half(sc_reg));
-        p.Y[2 * rg0 + tid] = __half_as_ushort(__float2half_rn(v * sc));
+            v += src[k];
+        p.Y[(size_t)(m0 + m) * N + 2 * rg0 + rr] = __half_as_ushort(__float2half_rn(v * s_sc[rr]));
     }
+}
+
+template <int T, int U, int MT>
+hipError_t launch_bsplit_m(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
+{
+    if (t.splitk > (T <= 4 && MT == 1 ? kBsMaxWaves : 8))
+        return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_gemv_w8a16_bsplit<T, U, MT>), dim3(t.blocks, t.m_tiles), dim3(64 * t.splitk), 0,
+                       st, a);
+    return hipGetLastError();
 }
 
 template <int T, int U>
 hipError_t launch_bsplit_u(const W8A16Args& a, const GemvTiling& t, hipStream_t st)
 {
-    if (t.splitk > (T <= 4 ? kBsMaxWaves : 8))
-        return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemv_w8a16_bsplit<T, U>), dim3(t.blocks), dim3(64 * t.splitk), 0, st, a);
-    return hipGetLastError();
+    switch (t.mt) {
+    case 1: return launch_bsplit_m<T, U, 1>(a, t, st);
+    case 2: return launch_bsplit_m<T, U, 2>(a, t, st);
+    case 4:
+        if constexpr (T <= 5)
+            return launch_bsplit_m<T, U, 4>(a, t, st);
+        else
+            return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
 }
 
 template <int T>

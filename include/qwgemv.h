@@ -203,12 +203,13 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
             2, 4 or 8 consumer waves (at most 7 tiles each, so K <= 3584 * splitk),
             whose int32 partial sums are added in on-chip memory; at most 16 row groups
             per workgroup (nwaves = workgroups * 8);
-     u = 7  (INT8, M == 1) balanced long-K variant: nwaves workgroups, which split the
-            row groups evenly (at most 16 each), of nw == splitk waves; wave s takes
-            k-slice s (ceil(CG / splitk) <= 8 tiles, CG = ceil(K / 512)) of every row
-            group of its workgroup with that slice of X held in registers; up to 16
-            waves with slices of at most 4 tiles, else up to 8.  The slices' fp32 sums
-            are added in slice order.
+     u = 7  (INT8) balanced long-K variant: nwaves workgroups, which split the row
+            groups evenly (at most 16 each), of nw == splitk waves; wave s takes k-slice
+            s (ceil(CG / splitk) <= 8 tiles, CG = ceil(K / 512)) of every row group of
+            its workgroup with that slice of X held in registers, for 1 (M == 1), 4
+            (M >= 3 with slices of at most 5 tiles) or 2 rows of X per workgroup; at
+            M == 1 up to 16 waves with slices of at most 4 tiles, else up to 8.  The
+            slices' fp32 sums are added in slice order.
    splitk must be 1 unless stated.  Results do not depend on the launch shape, except
    that W8A16 with splitk > 1 adds its fp32 partial sums in a different order.
    QW_ERR_TILING for an invalid shape. */

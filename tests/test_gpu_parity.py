@@ -671,18 +671,22 @@ def test_split_k_launch_shapes(M, N, K):
                     assert rel_l2(y, y64) <= W8A16_RL2, ("flight split", S, per)
 
 
-# The balanced long-K W8A16 variant (u = 7, M = 1): the 18944 -> 3584 down projection,
+# The balanced long-K W8A16 variant (u = 7): the 18944 -> 3584 down projection,
 # K = 28672 (the longest W8A16 row), ragged N (a partial row group), tiny N (fewer row
-# groups than workgroups), short K (one slice) and more than 8 row groups per workgroup
-W8_BSPLIT_SHAPES = [(3584, 18944), (512, 18944), (301, 28672), (5, 8192), (4100, 3584),
-                    (640, 4608), (2000, 96)]
+# groups than workgroups), short K (one slice) and more than 8 row groups per workgroup;
+# 2 to 9 rows of X (workgroups of 2 or 4 rows, a ragged last one)
+W8_BSPLIT_SHAPES = [(1, 3584, 18944), (1, 512, 18944), (1, 301, 28672), (1, 5, 8192),
+                    (1, 4100, 3584), (1, 640, 4608), (1, 2000, 96), (2, 3584, 18944),
+                    (3, 512, 18944), (4, 301, 28672), (5, 2050, 8192), (9, 640, 4608),
+                    (7, 38, 96)]
 
 
-@pytest.mark.parametrize("N,K", W8_BSPLIT_SHAPES)
-def test_balanced_long_k_w8a16_matches_oracle(N, K):
-    say("w8a16 balanced long k", N, K)
+@pytest.mark.parametrize("M,N,K", W8_BSPLIT_SHAPES)
+def test_balanced_long_k_w8a16_matches_oracle(M, N, K):
+    say("w8a16 balanced long k", M, N, K)
     W = wl.weights(760 + N % 97, 1, N, K, outlier_rows=N >= 100)
-    X16 = wl.activations(761 + N % 97, 2, 1, K, outlier_channels=4).astype(np.float16)
+    X16 = wl.activations(761 + N % 97, 2, M, K, outlier_channels=4).astype(np.float16)
+    X16[M // 2, : K // 3] = 0
     Wq8, s16, q8, s16_o = pack_w8_and_check(W)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     X16d = dev(X16)
@@ -692,7 +696,7 @@ def test_balanced_long_k_w8a16_matches_oracle(N, K):
     s8 = max(1, -(-cg // 8))
     for S in sorted({s8, min(8, s8 + 1), 8, max(1, -(-cg // 4)), 16}):
         T = -(-cg // S)
-        if T > 8 or S > (16 if T <= 4 else 8):
+        if T > 8 or S > (16 if T <= 4 and M == 1 else 8):
             continue
         for nwaves in sorted({1, 7, 256, -(-nrg // 16), nrg}):
             if nwaves > nrg or -(-nrg // nwaves) > 16:
@@ -710,6 +714,10 @@ def test_balanced_long_k_w8a16_matches_oracle(N, K):
     assert n >= 4
     yd = host(qw.gemv_w8a16(X16d, Wq8, s16))
     assert rel_l2(yd, y64) <= W8A16_RL2
+    if cg > 8 and M <= 16 and (M >= 2 or nrg >= 1024):  # the default path is this variant
+        S = min(8, -(-cg // 4))
+        yv = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 7, S, -(-nrg // 16), S))
+        assert np.array_equal(yd.view(np.uint16), yv.view(np.uint16))
 
 
 def test_balanced_long_k_w8a16_limits():
@@ -724,8 +732,9 @@ def test_balanced_long_k_w8a16_limits():
         with pytest.raises(qw.QWError):
             qw.gemv_w8a16_tiled(X16d, Wq8, s16, *bad)
     X2 = dev(wl.activations(772, 2, 2, K).astype(np.float16))
+    qw.gemv_w8a16_tiled(X16d, Wq8, s16, 7, 16, 2, 16)  # 16 waves of one tile at M == 1 ...
     with pytest.raises(qw.QWError):
-        qw.gemv_w8a16_tiled(X2, Wq8, s16, 7, 2, 4, 2)  # M == 1 only
+        qw.gemv_w8a16_tiled(X2, Wq8, s16, 7, 16, 2, 16)  # ... 8 at most from 2 rows
     N2, K2 = 64, 28672  # 56 tiles: 9 or 10 waves would take 7 or 6 tiles each (at most 8 waves)
     W2 = wl.weights(773, 1, N2, K2)
     Wq2, s2, _, _ = pack_w8_and_check(W2)

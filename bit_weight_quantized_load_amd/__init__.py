@@ -50,6 +50,7 @@ SIGNATURES = {
     "qw_gemv_w4a8_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
     "qw_gemv_w8a16_tiled": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _I, _P]),
     "qw_gemm_w4a8_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
+    "qw_gemv_w4a8_long_k": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _P]),
     "qw_gemm_w8a16_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
     "qw_w4g_scale_bytes": (_SZ, [_I64, _I64, _I64]),
     "quantize_pack_w4g": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
@@ -346,6 +347,27 @@ def gemm_w4a8_mfma(X, Wq, w_scale, nw=4, mb=1, nbw=1, workspace=None, out=None, 
     wp, wn = _ws_args(workspace)
     _call("qw_gemm_w4a8_mfma", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn,
           nw, mb, nbw, _stream(stream))
+    return Y
+
+
+def gemv_w4a8_long_k(X, Wq, w_scale, waves, workgroups, workspace=None, out=None, stream=None):
+    """The balanced long-K W4A8 kernel at any M with an explicit launch shape (`waves`
+    k-slices per workgroup, `workgroups` workgroups).  Needs a workspace of
+    qw_workspace_bytes(2, M, N, K) bytes."""
+    torch = _torch()
+    M, K = X.shape
+    N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if workspace is None:
+        workspace = torch.empty((lib().qw_workspace_bytes(2, M, N, K),), dtype=torch.uint8,
+                                device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    wp, wn = _ws_args(workspace)
+    _call("qw_gemv_w4a8_long_k", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn,
+          waves, workgroups, _stream(stream))
     return Y
 
 

@@ -567,6 +567,64 @@ int check_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M,
 
 }  // namespace
 
+// Balanced long-K W4A8 path: the activations quantized into the workspace (row-major
+// codes, then one scale per row; one workgroup per row), then the balanced kernel
+// with `waves` k-slices per workgroup and `blocks` workgroups.
+bool w4_bsplit_ok(int64_t M, int64_t N, int64_t K, int waves, int blocks)
+{
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
+    if (waves < 1 || waves > 8 || (L.cg + waves - 1) / waves > 8 || blocks < 1 || blocks > L.nrg)
+        return false;
+    const int64_t per = ((int64_t)L.nrg + blocks - 1) / blocks;
+    return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 31);
+}
+
+int run_w4_bsplit(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                  int64_t K, float* Y, void* workspace, size_t ws_bytes, int waves, int blocks,
+                  void* stream)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+        !aligned16(workspace))
+        return QW_ERR_ALIGN;
+    if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
+        return QW_ERR_WORKSPACE;
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
+    const size_t codes = ((size_t)M * (size_t)K + 255u) & ~(size_t)255u;
+    int8_t* xq = static_cast<int8_t*>(workspace);
+    float* a = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + codes);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = qw::launch_quant_act_rows(X, (int)M, (int)K, xq, a, st);
+    if (e != hipSuccess)
+        return hip_status(e);
+    qw::W4A8BsplitArgs p;
+    p.Xq = xq;
+    p.a_scale = a;
+    p.Wq = static_cast<const uint8_t*>(Wq);
+    p.w_scale = w_scale;
+    p.Y = Y;
+    p.M = (int)M;
+    p.N = (int)N;
+    p.K = (int)K;
+    p.cg = L.cg;
+    p.nrg = L.nrg;
+    p.per = L.nrg / blocks;
+    p.rem = L.nrg % blocks;
+    return hip_status(qw::launch_gemv_w4a8_bsplit(p, blocks, waves, st));
+}
+
+// Rows of X from 2 up to which W4A8 with K > 4096 runs the balanced long-K kernel
+// instead of the matrix-core kernels.
+constexpr int64_t kBsplitMaxM4 = 16;
+
+void w4_bsplit_default(int64_t N, int64_t K, int* waves, int* blocks)
+{
+    const qw::TileLayout L = qw::tile_layout(4, N, K);
+    *waves = (int)std::min<int64_t>(8, (L.cg + 3) / 4);
+    *blocks = (int)std::max<int64_t>(std::min<int64_t>(device_cus(), L.nrg), (L.nrg + 15) / 16);
+}
+
 extern "C" {
 
 size_t qw_w4_packed_bytes(int64_t N, int64_t K)
@@ -835,6 +893,14 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
 {
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (M >= qw::kMfmaMinM4 && K > 512 * qw::kRegCG && M <= kBsplitMaxM4) {
+        // long K, 2 to 16 rows: the matrix-core kernels walk all of K in each workgroup
+        // (about 46 us at 18944 -> 3584 whatever M), the balanced long-K kernel splits it
+        int waves, blocks;
+        w4_bsplit_default(N, K, &waves, &blocks);
+        if (w4_bsplit_ok(M, N, K, waves, blocks))
+            return run_w4_bsplit(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, waves, blocks, stream);
+    }
     if (M >= qw::kMfmaMinM4) {
         int nw, mb, nbw;
         qw::mfma_default_shape(4, M, K, &nw, &mb, &nbw);
@@ -920,6 +986,17 @@ int qw_gemm_w4a8_mfma(const float* X, const void* Wq, const float* w_scale, int6
     if (mb == 0 && (K + 511) / 512 * 8192 > 65536)  // X resident in LDS: K up to 4096
         return QW_ERR_TILING;
     return run_gemm_w4a8(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, nw, mb, nbw, stream);
+}
+
+int qw_gemv_w4a8_long_k(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes,
+                        int waves, int workgroups, void* stream)
+{
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
+        return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
+    if (!w4_bsplit_ok(M, N, K, waves, workgroups))
+        return QW_ERR_TILING;
+    return run_w4_bsplit(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, waves, workgroups, stream);
 }
 
 int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,

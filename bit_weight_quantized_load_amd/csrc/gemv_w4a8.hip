@@ -857,4 +857,255 @@ hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, 
     }
 }
 
+namespace {
+
+// Activation quantization for the long-K kernel: one workgroup of 1024 threads per row
+// of X, which loads the whole row into registers at once (NV float4 per thread, so a
+// single memory round trip), takes max|x| across the workgroup and writes the row-major
+// codes from the same registers.  The scale and the codes are computed exactly as by
+// the standalone quantization kernel.
+constexpr int kQrThreads = 1024;
+
+template <int NV>
+__global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __restrict__ X, int K,
+                                                               int8_t* __restrict__ Xq,
+                                                               float* __restrict__ a_scale)
+{
+    __shared__ float red[kQrThreads / 64];
+    const int tid = threadIdx.x;
+    const int m = blockIdx.x;
+    const int K4 = K >> 2;
+    const rsrc_t xr = make_rsrc(X + (size_t)m * K, (uint32_t)K * 4u);
+    float4 v[NV];
+    float mx = 0.0f;
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+        const int i = tid + kQrThreads * t;
+        v[t] = load16f(xr, i < K4 ? (uint32_t)i * 16u : 0x80000000u);
+        mx = fmaxf(mx, max_abs4(v[t]));
+    }
+    mx = wave_max(mx);
+    if ((tid & 63) == 0)
+        red[tid >> 6] = mx;
+    __syncthreads();
+    mx = red[0];
+#pragma unroll
+    for (int w = 1; w < kQrThreads / 64; ++w)
+        mx = fmaxf(mx, red[w]);
+    const float a = mx / 127.0f;
+    const float r = 1.0f / a;
+    const bool fast = r <= 3.0e38f;
+    if (tid == 0)
+        a_scale[m] = a;
+    uint32_t* out = reinterpret_cast<uint32_t*>(Xq + (size_t)m * K);
+#pragma unroll
+    for (int t = 0; t < NV; ++t) {
+        const int i = tid + kQrThreads * t;
+        if (i < K4) {
+            const float4 x = v[t];
+            out[i] = fast ? pack_i8x4(quant_code_fast(x.x, a, r, 127.f), quant_code_fast(x.y, a, r, 127.f),
+                                      quant_code_fast(x.z, a, r, 127.f), quant_code_fast(x.w, a, r, 127.f))
+                          : pack_i8x4(quant_code(x.x, a, 127.f), quant_code(x.y, a, 127.f),
+                                      quant_code(x.z, a, 127.f), quant_code(x.w, a, 127.f));
+        }
+    }
+}
+
+// Balanced long-K W4A8 kernel for 1 to 16 rows of X (grid rows of MT rows): the same
+// split as the W8A16 long-K form.  One workgroup per CU (more only past U row groups
+// per CU) owns an even run of row groups; its S waves each take a k-slice of T tiles of
+// every row group of the run.  The activation codes come from the workspace (row-major
+// int8, written by the standalone quantization kernel, with one scale per row); each
+// lane loads the 32 codes of its chunk of each tile of its slice for its MT rows once
+// and regroups every 8 of them into the even-k and odd-k words the unpack meets.  A
+// unit is one row group's T tiles of the wave's slice, one unit requested ahead.  The
+// per-slice int32 row sums (16 times the dot, exact) meet in LDS; the epilogue adds
+// them (exact in any order) and writes ((sum >> 4) * w_scale) * a_scale.
+constexpr int kW4BsMaxWaves = 8;
+
+template <int T, int U, int MT>
+__global__ __launch_bounds__(64 * kW4BsMaxWaves) void k_gemv_w4a8_bsplit(W4A8BsplitArgs p)
+{
+    __shared__ int s_part[MT * 4 * U * kW4BsMaxWaves];  // [row of X][row of the run][slice]
+    __shared__ float s_sc[4 * U];
+    __shared__ float s_a[MT];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int ks = __builtin_amdgcn_readfirstlane(tid >> 6);  // the k-slice of this wave
+    const int nthreads = (int)blockDim.x;
+    const int S = nthreads >> 6;
+    const int j = lane & 15, sub = lane >> 4;
+    const int N = p.N, K = p.K, CG = p.cg;
+    const int c_lo = ks * T;
+    const int b = blockIdx.x;
+    const int m0 = MT * (int)blockIdx.y;
+    const int mv = min(MT, p.M - m0);
+    const int rg0 = rg_of(b, p.per, p.rem);
+    const int nb = min(U, rg_of(b + 1, p.per, p.rem) - rg0);
+    const int nrows = max(0, min(4 * nb, N - 4 * rg0));
+    const rsrc_t wres = make_rsrc(p.Wq + (size_t)rg0 * CG * 1024u, (uint32_t)(nb * CG) * 1024u);
+    const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 4, (uint32_t)nrows * 4u);
+    const rsrc_t xres = make_rsrc(p.Xq + (size_t)m0 * K, (uint32_t)mv * (uint32_t)K);
+    const rsrc_t ares = make_rsrc(p.a_scale + m0, (uint32_t)mv * 4u);
+
+    // lane (j, sub): chunk j (32 k) of tile c of the slice -> codes X[m0 + m][512 (c_lo + c) + 32 j ..]
+    uint4 xp[MT][T][2];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < T; ++c) {
+            const int k = 512 * (c_lo + c) + 32 * j;
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                xp[m][c][h] = load16(xres, m < mv && k < K ? (uint32_t)(m * K + k + 16 * h) : 0x80000000u);
+        }
+    const uint32_t sc_reg = load4(sres, (uint32_t)tid * 4u);
+    const uint32_t a_reg = load4(ares, (uint32_t)(tid < MT ? tid : 0x10000000) * 4u);
+    uint4 w[U][T];
+    // the T tiles of unit U_ (row group U_ of the run; zeros past the run and past CG)
+#define QW_LOADW(U_)                                                                             \
+    _Pragma("unroll") for (int c_ = 0; c_ < T; ++c_)                                             \
+        w[U_][c_] = load16_stream(wres, (U_) < nb && c_lo + c_ < CG                              \
+                                            ? (uint32_t)((U_) * CG + c_lo + c_) * 1024u +        \
+                                                  (uint32_t)lane * 16u                           \
+                                            : 0x80000000u);
+    issue_barrier();
+    QW_LOADW(0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < 4 * U)
+        s_sc[tid] = __uint_as_float(sc_reg);
+    if (tid < MT)
+        s_a[tid] = __uint_as_float(a_reg);
+    // codes k .. k + 7 of word d: the even-k codes in one word, the odd-k codes in the next
+    uint32_t act[MT][T][8];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int c = 0; c < T; ++c) {
+            const uint32_t nat[8] = {xp[m][c][0].x, xp[m][c][0].y, xp[m][c][0].z, xp[m][c][0].w,
+                                     xp[m][c][1].x, xp[m][c][1].y, xp[m][c][1].z, xp[m][c][1].w};
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+                act[m][c][2 * d] = __builtin_amdgcn_perm(nat[2 * d + 1], nat[2 * d], 0x06040200u);
+                act[m][c][2 * d + 1] = __builtin_amdgcn_perm(nat[2 * d + 1], nat[2 * d], 0x07050301u);
+            }
+        }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        if (u + 1 < U) {
+            QW_LOADW(u + 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        if (u < nb) {
+            int acc[MT][4];
+#pragma unroll
+            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                for (int d = 0; d < 4; ++d)
+                    acc[m][d] = 0;
+#pragma unroll
+            for (int c = 0; c < T; ++c) {
+                const uint32_t wd[4] = {w[u][c].x, w[u][c].y, w[u][c].z, w[u][c].w};
+#pragma unroll
+                for (int d = 0; d < 4; ++d) {
+                    const int lo = (int)((wd[d] << 4) & 0xF0F0F0F0u);
+                    const int hi = (int)(wd[d] & 0xF0F0F0F0u);
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        acc[m][d] = __builtin_amdgcn_sdot4(lo, (int)act[m][c][2 * d], acc[m][d], false);
+                        acc[m][d] = __builtin_amdgcn_sdot4(hi, (int)act[m][c][2 * d + 1], acc[m][d], false);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int v = row_sum16((acc[m][0] + acc[m][1]) + (acc[m][2] + acc[m][3]));
+                if (j == 0)
+                    s_part[((m * U + u) * 4 + sub) * kW4BsMaxWaves + ks] = v;
+            }
+        }
+    }
+#undef QW_LOADW
+    __syncthreads();
+    for (int e = tid; e < mv * nrows; e += nthreads) {
+        const int m = e / nrows, rr = e - m * nrows;
+        const int* src = s_part + (m * 4 * U + rr) * kW4BsMaxWaves;
+        int v = 0;
+        for (int k = 0; k < S; ++k)
+            v += src[k];
+        p.Y[(size_t)(m0 + m) * N + 4 * rg0 + rr] = ((float)(v >> 4) * s_sc[rr]) * s_a[m];
+    }
+}
+
+template <int T, int U, int MT>
+hipError_t launch_w4_bsplit_m(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st)
+{
+    const int mtiles = (a.M + MT - 1) / MT;
+    hipLaunchKernelGGL((k_gemv_w4a8_bsplit<T, U, MT>), dim3(blocks, mtiles), dim3(64 * waves), 0, st, a);
+    return hipGetLastError();
+}
+
+template <int T, int U>
+hipError_t launch_w4_bsplit_u(const W4A8BsplitArgs& a, int blocks, int waves, int mt, hipStream_t st)
+{
+    switch (mt) {
+    case 1: return launch_w4_bsplit_m<T, U, 1>(a, blocks, waves, st);
+    case 2: return launch_w4_bsplit_m<T, U, 2>(a, blocks, waves, st);
+    case 4:
+        if constexpr (T <= 5)
+            return launch_w4_bsplit_m<T, U, 4>(a, blocks, waves, st);
+        else
+            return hipErrorInvalidValue;
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <int T>
+hipError_t launch_w4_bsplit_t(const W4A8BsplitArgs& a, int blocks, int waves, int mt, hipStream_t st)
+{
+    const int per = a.per + (a.rem > 0 ? 1 : 0);
+    return per <= 8 ? launch_w4_bsplit_u<T, 8>(a, blocks, waves, mt, st)
+                    : launch_w4_bsplit_u<T, 16>(a, blocks, waves, mt, st);
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
+{
+    const int nv = (K / 4 + kQrThreads - 1) / kQrThreads;  // float4 per thread
+    const dim3 grid((unsigned)M), block(kQrThreads);
+    if (nv <= 1)
+        hipLaunchKernelGGL(k_quant_act_rows<1>, grid, block, 0, st, X, K, Xq, a);
+    else if (nv <= 2)
+        hipLaunchKernelGGL(k_quant_act_rows<2>, grid, block, 0, st, X, K, Xq, a);
+    else if (nv <= 4)
+        hipLaunchKernelGGL(k_quant_act_rows<4>, grid, block, 0, st, X, K, Xq, a);
+    else if (nv <= 8)
+        hipLaunchKernelGGL(k_quant_act_rows<8>, grid, block, 0, st, X, K, Xq, a);
+    else if (nv <= 14)
+        hipLaunchKernelGGL(k_quant_act_rows<14>, grid, block, 0, st, X, K, Xq, a);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_w4a8_bsplit(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st)
+{
+    if (waves < 1 || waves > kW4BsMaxWaves || blocks < 1)
+        return hipErrorInvalidValue;
+    const int T = (a.cg + waves - 1) / waves;
+    const int mt = a.M == 1 ? 1 : (a.M >= 3 && T <= 5 ? 4 : 2);
+    switch (T) {
+    case 1: return launch_w4_bsplit_t<1>(a, blocks, waves, mt, st);
+    case 2: return launch_w4_bsplit_t<2>(a, blocks, waves, mt, st);
+    case 3: return launch_w4_bsplit_t<3>(a, blocks, waves, mt, st);
+    case 4: return launch_w4_bsplit_t<4>(a, blocks, waves, mt, st);
+    case 5: return launch_w4_bsplit_t<5>(a, blocks, waves, mt, st);
+    case 6: return launch_w4_bsplit_t<6>(a, blocks, waves, mt, st);
+    case 7: return launch_w4_bsplit_t<7>(a, blocks, waves, mt, st);
+    case 8: return launch_w4_bsplit_t<8>(a, blocks, waves, mt, st);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace qw

@@ -107,6 +107,18 @@ struct W4A8Args {
     float* dbg_a;      // optional [M]
 };
 
+// Balanced long-K W4A8 kernel: activation codes and scales precomputed (workspace).
+struct W4A8BsplitArgs {
+    const int8_t* Xq;       // [M][K] row-major int8 codes
+    const float* a_scale;   // [M]
+    const uint8_t* Wq;
+    const float* w_scale;
+    float* Y;
+    int M, N, K;
+    int cg, nrg;
+    int per, rem;           // row groups per workgroup: nrg = per * blocks + rem (see rg_of)
+};
+
 struct W8A16Args {
     const uint16_t* X;
     const uint8_t* Wq;
@@ -176,6 +188,12 @@ hipError_t launch_fill_zero(uint32_t* p, size_t words, hipStream_t st);
 
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st);
 hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_t st);
+// blocks workgroups of `waves` (1..8) waves, one k-slice of ceil(cg / waves) <= 8 tiles
+// each; 1, 2 or 4 rows of X per workgroup (chosen from M and the slice length)
+hipError_t launch_gemv_w4a8_bsplit(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st);
+// row-major int8 codes and one scale per row of X, as launch_quant_act; one 1024-thread
+// workgroup per row holding the row in registers (K <= 57344)
+hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st);
 // The INT4 page's ablations (M == 1, K <= 4096): FP16 GEMV on row-major f16 weights, and
 // weight-only INT4 (quantize_pack_w4 layout) with fp32 activations unpacked to float;
 // rpw rows (FP16) or row groups (INT4) per wave, 1, 2 or 4.

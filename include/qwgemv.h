@@ -72,12 +72,14 @@ enum {
 size_t qw_w4_packed_bytes(int64_t N, int64_t K);
 size_t qw_w8_packed_bytes(int64_t N, int64_t K);
 
-/* Workspace that gemv_w4a8 (op 0), gemv_w8a16 (op 1) or qw_gemm_w4a8_mfma (op 2) needs
-   for shape (M, N, K).  0 means the call needs none and accepts workspace == NULL:
-   gemv_w4a8 at M == 1 (the GEMV finishes its rows inside one workgroup) and gemv_w8a16
-   at any M.  gemv_w4a8 with M >= 2 runs on the matrix cores and needs
-   align256(ceil(M/16) * ceil(K/64) * 1024) + align256(4 * M) bytes: the activation
-   codes and scales, quantized once per call in operand order.  Its contents need
+/* Workspace that gemv_w4a8 (op 0), gemv_w8a16 (op 1) or qw_gemm_w4a8_mfma and
+   qw_gemv_w4a8_long_k (op 2) need for shape (M, N, K).  0 means the call needs none
+   and accepts workspace == NULL: gemv_w4a8 at M == 1 (the GEMV finishes its rows
+   inside one workgroup) and gemv_w8a16 at any M.  gemv_w4a8 with M >= 2 runs on the
+   matrix cores (or, with K > 4096 and up to 16 rows, on the balanced long-K kernel)
+   and needs align256(ceil(M/16) * ceil(K/64) * 1024) + align256(4 * M) bytes: the
+   activation codes and scales, quantized once per call (in operand order for the
+   matrix cores, row-major for the long-K kernel).  Its contents need
    no initialisation and are overwritten by every call; calls that share one
    workspace must not overlap in time. */
 size_t qw_workspace_bytes(int op, int64_t M, int64_t N, int64_t K);
@@ -246,6 +248,20 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
 int qw_gemm_w4a8_mfma(const float* X, const void* Wq, const float* w_scale, int64_t M,
                       int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes, int nw,
                       int mb, int nbw, void* stream);
+
+/* The balanced long-K W4A8 GEMV (Jetson Orin INT4 page, sections on the correct
+   direction and the current implementation: INT4 weights widened to int8, 4-way int8
+   dots into int32, output acc * weight scale * activation scale) at any M with an
+   explicit launch shape: X is first quantized per row (as by quant_act_i8) into the
+   workspace (qw_workspace_bytes(2, M, N, K) bytes, else QW_ERR_WORKSPACE); then
+   `workgroups` workgroups (at most the row-group count, at most 16 row groups each)
+   of `waves` waves (1..8) each take k-slices of ceil(ceil(K / 512) / waves) <= 8 tiles
+   of every row group of their share, for 1, 2 or 4 rows of X per workgroup.  The int32
+   sums are exact, so the outputs equal gemv_w4a8's bit for bit; gemv_w4a8 runs this
+   kernel for 2 to 16 rows with K > 4096.  QW_ERR_TILING for an invalid shape. */
+int qw_gemv_w4a8_long_k(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                        int64_t N, int64_t K, float* Y, void* workspace, size_t ws_bytes,
+                        int waves, int workgroups, void* stream);
 int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int nw, int mb,
                        int nbw, void* stream);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 27
+    assert len(names) == 28
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -124,6 +124,24 @@ def test_tiled_rejects_bad_launch_shapes(fn):
     assert f(A, A2, A3, 1, 64, 4016, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_SHAPE
     assert f(NULL, A2, A3, 1, 64, 40, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_NULL
     assert f(MIS, A2, A3, 1, 64, 4096, A4, 8, 8, 1, 1, NULL) == qw.QW_ERR_ALIGN
+
+
+def test_long_k_w4a8_rejects_bad_arguments_on_the_host():
+    """Every check of qw_gemv_w4a8_long_k runs before any launch (no GPU here)."""
+    f = L.qw_gemv_w4a8_long_k
+    ws = 1 << 20
+    M, N, K = 2, 64, 8192  # 16 tiles a row, 16 row groups
+    assert f(A, A2, A3, M, N, K, A4, A, ws, 9, 1, NULL) == qw.QW_ERR_TILING   # > 8 waves
+    assert f(A, A2, A3, M, N, K, A4, A, ws, 1, 1, NULL) == qw.QW_ERR_TILING   # 16-tile slice
+    assert f(A, A2, A3, M, N, K, A4, A, ws, 2, 0, NULL) == qw.QW_ERR_TILING   # no workgroup
+    assert f(A, A2, A3, M, N, K, A4, A, ws, 2, 17, NULL) == qw.QW_ERR_TILING  # > row groups
+    assert f(A, A2, A3, M, 256, K, A4, A, ws, 2, 1, NULL) == qw.QW_ERR_TILING  # 64 row groups on one
+    assert f(NULL, A2, A3, M, N, K, A4, A, ws, 2, 4, NULL) == qw.QW_ERR_NULL
+    assert f(MIS, A2, A3, M, N, K, A4, A, ws, 2, 4, NULL) == qw.QW_ERR_ALIGN
+    need = L.qw_workspace_bytes(2, M, N, K)
+    assert f(A, A2, A3, M, N, K, A4, A, need - 1, 2, 4, NULL) == qw.QW_ERR_WORKSPACE
+    assert f(A, A2, A3, M, N, K, A4, NULL, need, 2, 4, NULL) == qw.QW_ERR_WORKSPACE
+    assert f(A, A2, A3, M, N, 40, A4, A, ws, 2, 4, NULL) == qw.QW_ERR_SHAPE  # K % 32
 
 
 @pytest.mark.parametrize("fn", ["qw_gemm_w4a8_mfma", "qw_gemm_w8a16_mfma"])

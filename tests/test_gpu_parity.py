@@ -744,6 +744,48 @@ def test_balanced_long_k_w8a16_limits():
             qw.gemv_w8a16_tiled(X3, Wq2, s2, 7, S, 4, S)
 
 
+# The balanced long-K W4A8 kernel: the 18944 -> 3584 down projection, short and ragged
+# N, K = 32768 (the longest slice split, 8 tiles on each of 8 waves), short K; 1 to 16
+# rows of X (workgroups of 1, 2 or 4 rows, a ragged last one)
+W4_BSPLIT_SHAPES = [(1, 3584, 18944), (2, 3584, 18944), (3, 512, 18944), (4, 301, 32768),
+                    (5, 2050, 8192), (9, 640, 4608), (16, 38, 96), (16, 1000, 18944),
+                    (7, 6, 8192)]
+
+
+@pytest.mark.parametrize("M,N,K", W4_BSPLIT_SHAPES)
+def test_balanced_long_k_w4a8_matches_oracle(M, N, K):
+    say("w4a8 balanced long k", M, N, K)
+    W = wl.weights(780 + N % 97, 1, N, K, outlier_rows=N >= 100)
+    X = wl.activations(781 + N % 97, 2, M, K, outlier_channels=4)
+    X[M // 2, : K // 3] = 0
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    ws = torch.empty((qw.lib().qw_workspace_bytes(2, M, N, K),), dtype=torch.uint8, device="cuda")
+    cg, nrg = -(-K // 512), -(-N // 4)
+    s8 = max(1, -(-cg // 8))
+    first = None
+    n = 0
+    for waves in sorted({s8, min(8, s8 + 1), 8, min(8, max(1, -(-cg // 4)))}):
+        if -(-cg // waves) > 8:
+            continue
+        for wg in sorted({1, 7, 256, -(-nrg // 16), nrg}):
+            if wg > nrg or -(-nrg // wg) > 16:
+                continue
+            Y = qw.gemv_w4a8_long_k(Xd, Wq, s, waves, wg, workspace=ws)
+            if first is None:
+                first = Y.clone()
+                assert_w4a8_close(host(Y), ref["Y"])
+            else:  # exact int32 sums: the same bits at every launch shape
+                assert torch.equal(Y, first), (waves, wg)
+            n += 1
+    assert n >= 3
+    Yd = qw.gemv_w4a8(Xd, Wq, s, workspace=ws)
+    assert torch.equal(Yd, first)
+    if M >= 2:
+        assert torch.equal(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 1, 1, workspace=ws), first)
+
+
 def test_repeated_calls_are_deterministic():
     K, N, M = 4096, 2048, 1
     W = wl.weights(66, 1, N, K)

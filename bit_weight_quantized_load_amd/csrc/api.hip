@@ -251,9 +251,17 @@ int device_cus()
 }
 
 // Built-in launch shape of the GEMV kernels (M == 1 for W4A8, M <= 2 for W8A16).
-// Rows of X up to which W8A16 with K > 4096 runs the balanced long-K GEMV variant
-// instead of the matrix-core kernels.
-constexpr int64_t kBsplitMaxM8 = 16;
+// Whether M rows of X with K > 4096 run the balanced long-K GEMV kernels (W4A8 from 2
+// rows, W8A16 from 1) rather than the matrix-core ones: up to 8 rows (a grid row of
+// workgroups per 4 rows, each reading all the weights), up to 16 when the weights are
+// below 24 MB.  Measured at 16 rows: W4A8 18944 -> 3584 (34 MB) 41.3 us against 38.0
+// for the 4-wave matrix-core kernel, 18944 -> 512 17.7 against 38.0; W8A16
+// 8192 -> 2048 (17 MB) 17.2 against about 28.
+bool long_k_rows(int bits, int64_t M, int64_t N, int64_t K)
+{
+    const int64_t wbytes = bits == 4 ? N * K / 2 : N * K;
+    return K > 512 * qw::kRegCG && M <= 16 && (M <= 8 || wbytes < ((int64_t)24 << 20));
+}
 
 GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
 {
@@ -309,7 +317,7 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
         const int per = nrg >= 1024 && nrg <= 2048 ? 2 : 1;
         return make_tiling(bits, M, N, K, 2, 4, (int)((nrg + per - 1) / per));
     }
-    // INT8 with K > 4096, M == 1 from 1024 row groups and 2 to 16 rows always: the
+    // INT8 with K > 4096, M == 1 from 1024 row groups and 2 to 8 (16) rows always: the
     // balanced long-K variant, one workgroup per CU of min(8, ceil(CG / 4)) waves, one
     // k-slice each, 1, 2 or 4 rows of X per workgroup (at M == 1, 18944 -> 3584: 12.9 us
     // against 13.9 us for the LDS variant split over two waves; 18944 -> 4608: 16.7
@@ -318,7 +326,7 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     // against 6.9.  From 2 rows it replaces the LDS variant and the matrix-core kernels,
     // whose 128-row workgroups leave most CUs idle at these N: 18944 -> 3584 at 2, 4, 8
     // and 16 rows 14.3, 18.0, 32.7 and 62.0 us against 26.2, 82.0, 82.3 and 83.5)
-    if (bits == 8 && L.cg > qw::kRegCG && M <= kBsplitMaxM8 && (M >= 2 || nrg >= 1024)) {
+    if (bits == 8 && long_k_rows(8, M, N, K) && (M >= 2 || nrg >= 1024)) {
         const int S = (int)std::min<int64_t>(8, (L.cg + 3) / 4);
         const int64_t nwg = std::max<int64_t>(std::min<int64_t>(device_cus(), nrg), (nrg + 15) / 16);
         if (tiling_ok(bits, M, 7, S, (int)nwg, S, L))
@@ -614,10 +622,6 @@ int run_w4_bsplit(const float* X, const void* Wq, const float* w_scale, int64_t 
     return hip_status(qw::launch_gemv_w4a8_bsplit(p, blocks, waves, st));
 }
 
-// Rows of X from 2 up to which W4A8 with K > 4096 runs the balanced long-K kernel
-// instead of the matrix-core kernels.
-constexpr int64_t kBsplitMaxM4 = 16;
-
 void w4_bsplit_default(int64_t N, int64_t K, int* waves, int* blocks)
 {
     const qw::TileLayout L = qw::tile_layout(4, N, K);
@@ -893,9 +897,9 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
 {
     if (check_gemv_shape(4, M, N, K) != QW_OK)
         return (!X || !Wq || !w_scale || !Y) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (M >= qw::kMfmaMinM4 && K > 512 * qw::kRegCG && M <= kBsplitMaxM4) {
-        // long K, 2 to 16 rows: the matrix-core kernels walk all of K in each workgroup
-        // (about 46 us at 18944 -> 3584 whatever M), the balanced long-K kernel splits it
+    if (M >= qw::kMfmaMinM4 && long_k_rows(4, M, N, K)) {
+        // long K, 2 to 8 (16) rows: the matrix-core kernels walk all of K in each
+        // workgroup (37 to 46 us at 18944 -> 3584 whatever M), the long-K kernel splits it
         int waves, blocks;
         w4_bsplit_default(N, K, &waves, &blocks);
         if (w4_bsplit_ok(M, N, K, waves, blocks))
@@ -951,7 +955,7 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
     (void)ws_bytes;
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
-    if (M >= qw::kMfmaMinM8 && !(K > 512 * qw::kRegCG && M <= kBsplitMaxM8)) {
+    if (M >= qw::kMfmaMinM8 && !long_k_rows(8, M, N, K)) {
         int nw, mb, nbw;
         qw::mfma_default_shape(8, M, K, &nw, &mb, &nbw);
         return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, nw, mb, nbw,

@@ -1188,8 +1188,20 @@ void mfma_default_shape(int bits, int64_t M, int64_t K, int* nw, int* mb, int* n
     // kernel with 8 waves and 2 or 4 blocks of X.  W8A16 with K <= 4096: the balanced
     // kernel up to 16 rows, its two-block form for 17 to 64 (25.3 against 31.0 us for
     // the streaming kernel at 17 rows, 28.6 against 32.3 at 32, 41.9 against 49.6 at 64
-    // on 3584 -> 18944); else 8 waves with 1 or 2 blocks.
+    // on 3584 -> 18944); else 8 waves with 1 or 2 blocks.  K > 4096 (the long-K GEMV
+    // kernels take up to 16 rows): each workgroup walks all of K, so more, smaller
+    // workgroups win up to 128 rows: 4 waves with one block of X (18944 -> 3584 at 32
+    // rows: W4A8 39.0 against 54.6 us with 8 waves and 2 blocks, W8A16 59.9 against
+    // 106.0; at 128 rows W4A8 50.4 against 78.3), W8A16 from 65 to 128 rows with 2 blocks
+    // (77.3 against 105.8); beyond, the 8-wave shapes (512 rows: W4A8 90.8 us with 4
+    // blocks against 147.2 with 4 waves of one).
     const int64_t mbtot = (M + 15) / 16;
+    if (K > 4096 && M <= 128) {
+        *nw = 4;
+        *nbw = 1;
+        *mb = bits == 8 && M > 64 ? 2 : 1;
+        return;
+    }
     const bool k_fits = (K + 511) / 512 * 8192 <= kXAllMaxBytes;
     *nw = 8;
     *nbw = 1;

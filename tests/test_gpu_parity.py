@@ -714,7 +714,8 @@ def test_balanced_long_k_w8a16_matches_oracle(M, N, K):
     assert n >= 4
     yd = host(qw.gemv_w8a16(X16d, Wq8, s16))
     assert rel_l2(yd, y64) <= W8A16_RL2
-    if cg > 8 and M <= 16 and (M >= 2 or nrg >= 1024):  # the default path is this variant
+    # the default path is this variant up to 8 rows (16 with weights below 24 MB)
+    if cg > 8 and (M <= 8 or (M <= 16 and N * K < 24 << 20)) and (M >= 2 or nrg >= 1024):
         S = min(8, -(-cg // 4))
         yv = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 7, S, -(-nrg // 16), S))
         assert np.array_equal(yd.view(np.uint16), yv.view(np.uint16))
@@ -784,6 +785,28 @@ def test_balanced_long_k_w4a8_matches_oracle(M, N, K):
     assert torch.equal(Yd, first)
     if M >= 2:
         assert torch.equal(qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 1, 1, workspace=ws), first)
+
+
+@pytest.mark.parametrize("M,N,K", [(17, 600, 8192), (70, 300, 18944), (130, 520, 4608)])
+def test_long_k_matrix_core_defaults_beyond_sixteen_rows(M, N, K):
+    """K > 4096 from 17 rows: the default matrix-core shapes (4 waves up to 128 rows)
+    give the oracle's W4A8 outputs and the same bits as another launch shape; W8A16
+    within the bar."""
+    say("long k mfma defaults", M, N, K)
+    W = wl.weights(790 + M, 1, N, K, outlier_rows=True)
+    X = wl.activations(791 + M, 2, M, K, outlier_channels=4)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    ws = torch.empty((qw.lib().qw_workspace_bytes(2, M, N, K),), dtype=torch.uint8, device="cuda")
+    Yd = qw.gemv_w4a8(Xd, Wq, s, workspace=ws)
+    assert_w4a8_close(host(Yd), ref["Y"])
+    assert torch.equal(Yd, qw.gemm_w4a8_mfma(Xd, Wq, s, 8, 2, 1, workspace=ws))
+    X16 = X.astype(np.float16)
+    Wq8, s16, q8, s16_o = pack_w8_and_check(W)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
+    assert rel_l2(y, y64) <= W8A16_RL2
 
 
 def test_repeated_calls_are_deterministic():

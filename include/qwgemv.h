@@ -118,8 +118,9 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    what quant_act_i8 computes.  M == 1: one GEMV kernel with the activation
    quantization fused into its prologue; workspace may be NULL.  M >= 2: the
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
-   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM; results are the same
-   bits as the GEMV's. */
+   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM, or with K > 4096 and
+   up to 8 rows (16 with packed weights below 24 MB) the balanced long-K GEMV kernel
+   (qw_gemv_w4a8_long_k); results are the same bits as the GEMV's. */
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
 
@@ -159,7 +160,9 @@ int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, 
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
    rounding.  M <= 2: GEMV kernel; M >= 3: f16 matrix-core GEMM on the exactly cast
-   weights.  No workspace at any M (workspace may be NULL). */
+   weights, except with K > 4096 and up to 8 rows (16 with weights below 24 MB), where
+   the balanced long-K GEMV variant runs (u = 7 of qw_gemv_w8a16_tiled).  No workspace
+   at any M (workspace may be NULL). */
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
                int64_t N, int64_t K, uint16_t* Y_f16, void* workspace, size_t ws_bytes,
                void* stream);
@@ -230,7 +233,8 @@ int qw_gemv_w4a8g_tiled(const float* X, const void* Wq, const float* w_scale, in
                         int64_t N, int64_t K, int64_t group, float* Y, int u, int nw,
                         int nwaves, int splitk, void* stream);
 
-/* The matrix-core kernels (the M >= 2 path of gemv_w4a8, M >= 3 of gemv_w8a16) at any
+/* The matrix-core kernels (the M >= 2 path of gemv_w4a8, M >= 3 of gemv_w8a16, outside
+   the long-K rows above) at any
    M with an explicit launch shape: nw waves per workgroup (4 or 8), mb blocks of 16
    rows of X per workgroup (1, 2 or 4 for W4A8, not 4 with nw 4 and nbw 2; 1 or 2 for
    W8A16), nbw blocks of 16 output rows per wave (1 or 2; not 2 with nw 8 and mb 1 for

@@ -867,6 +867,40 @@ def test_graph_capture_replays_match_eager():
         qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)  # eager work between replays
 
 
+@pytest.mark.parametrize("M", [1, 2, 5, 12])
+def test_long_k_graph_replays_match_eager(M):
+    """The long-K defaults (the producer-wave W4A8 GEMV and the balanced long-K W8A16
+    variant at one row; the balanced long-K kernels, with the W4A8 row quantization
+    into the workspace, from two) captured in one graph: every replay, with eager work
+    between replays, gives the eager bits."""
+    K, N = 8192, 1000
+    say("long-k graph replays M", M)
+    W = wl.weights(1300 + M, 1, N, K)
+    X = wl.activations(1300 + M, 2, M, K)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    Wq8, s16 = qw.quantize_pack_w8(dev(W))
+    Xd, X16 = dev(X), dev(X.astype(np.float16))
+    ws4 = qw.make_workspace("w4a8", M, N, K)
+    e4 = host(qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)).copy()
+    e8 = host(qw.gemv_w8a16(X16, Wq8, s16)).copy()
+    Y4 = torch.empty((M, N), device="cuda")
+    Y8 = torch.empty((M, N), device="cuda", dtype=torch.float16)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qw.gemv_w4a8(Xd, Wq, s, workspace=ws4, out=Y4)
+        qw.gemv_w8a16(X16, Wq8, s16, out=Y8)
+    for rep in range(4):
+        Y4.fill_(float("nan"))
+        Y8.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(Y4).view(np.uint32), e4.view(np.uint32)), rep
+        assert np.array_equal(host(Y8).view(np.uint16), e8.view(np.uint16)), rep
+        qw.gemv_w4a8(Xd, Wq, s, workspace=ws4)  # eager work between replays
+        qw.gemv_w8a16(X16, Wq8, s16)
+
+
 @pytest.mark.parametrize("M", [4, 20, 40, 64])
 def test_matrix_core_graph_replays_match_eager(M):
     """The matrix-core defaults (balanced kernels up to 16 rows; the W4A8 kernel over many

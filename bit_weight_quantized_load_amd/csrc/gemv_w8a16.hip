@@ -629,16 +629,16 @@ __global__ __launch_bounds__(T <= 4 && MT == 1 ? 64 * kBsMaxWaves : 512) void k_
     const rsrc_t sres = make_rsrc(p.w_scale + (size_t)rg0 * 2, (uint32_t)nrows * 2u);
     const rsrc_t xres = make_rsrc(p.X + (size_t)m0 * K, (uint32_t)mv * (uint32_t)K * 2u);
 
-    // lane (j, sub): chunk j (16 k) of tile c of the slice -> X[m0 + m][512 (c_lo + c) + 16 j ..]
-    uint4 xp[MT][T][2];
+    // lane (j, sub): chunk j (16 k) of tile c of the slice -> X[m0 + m][512 (c_lo + c) + 16 j ..];
+    // lanes j and j + 32 need the same chunk: each loads half of it (sub) and the
+    // halves are swapped across the two half-waves
+    uint4 xh[MT][T];
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
         for (int c = 0; c < T; ++c) {
             const int k = 512 * (c_lo + c) + 16 * j;
-#pragma unroll
-            for (int h = 0; h < 2; ++h)
-                xp[m][c][h] = load16(xres, m < mv && k < K ? (uint32_t)(m * K + k + 8 * h) * 2u : 0x80000000u);
+            xh[m][c] = load16(xres, m < mv && k < K ? (uint32_t)(m * K + k + 8 * sub) * 2u : 0x80000000u);
         }
     const uint16_t sc_reg = load2(sres, (uint32_t)tid * 2u);
     uint4 w[U][T];
@@ -658,8 +658,18 @@ __global__ __launch_bounds__(T <= 4 && MT == 1 ? 64 * kBsMaxWaves : 512) void k_
 #pragma unroll
     for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int c = 0; c < T; ++c)
-            split8(xp[m][c][0], xp[m][c][1], act[m][c]);
+        for (int c = 0; c < T; ++c) {
+            const uint4 mine = xh[m][c];
+            uint4 other;
+            other.x = (uint32_t)__shfl_xor((int)mine.x, 32, 64);
+            other.y = (uint32_t)__shfl_xor((int)mine.y, 32, 64);
+            other.z = (uint32_t)__shfl_xor((int)mine.z, 32, 64);
+            other.w = (uint32_t)__shfl_xor((int)mine.w, 32, 64);
+            if (sub == 0)
+                split8(mine, other, act[m][c]);
+            else
+                split8(other, mine, act[m][c]);
+        }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
         if (u + 1 < U) {

@@ -255,13 +255,14 @@ PEAK_MFMA_I8_TOPS = 5000.0   # dense int8 matrix cores
 PEAK_MFMA_F16_TFLOPS = 2500.0  # dense f16 matrix cores
 
 
-def skinny_sweep_measurement(qw, wl, torch, launches):
-    """The skinny-GEMM sweep: gemv_w4a8 and gemv_w8a16 (default paths: the GEMV kernels
-    at M = 1, the matrix-core kernels above) on ChatGLM2's 4096 -> 27392 linear for each
-    M of the sweep, weight copies rotated past the cache.  Reports time, HBM bandwidth
-    of the algorithmic bytes, and for M > 1 the matrix-core rate against the dense peak
-    (int8 for W4A8, f16 for W8A16)."""
-    c = wl.SKINNY
+def skinny_sweep_measurement(qw, wl, torch, launches, c=None):
+    """The skinny-GEMM sweep: gemv_w4a8 and gemv_w8a16 on their default paths for each M
+    of the sweep, weight copies rotated past the cache; by default ChatGLM2's 4096 ->
+    27392 linear (the GEMV kernels at M = 1, the matrix-core kernels above), or the
+    given config (the long-K down projection: the long-K kernels up to 16 rows).
+    Reports time, HBM bandwidth of the algorithmic bytes, and the rate against the dense
+    matrix-core peak (int8 for W4A8, f16 for W8A16)."""
+    c = wl.SKINNY if c is None else c
     K, N = c["K"], c["N"]
     W = torch.from_numpy(wl.weights(c["seed"], 1, N, K, outlier_rows=True)).cuda()
     Wq4, s4 = qw.quantize_pack_w4(W)
@@ -324,7 +325,8 @@ def main():
                     help="skip the 28-layer decode-step chain measurement")
     ap.add_argument("--chain-replays", type=int, default=20)
     ap.add_argument("--no-skinny", action="store_true",
-                    help="skip the skinny-GEMM sweep (K = 4096, N = 27392, M = 1 .. 512)")
+                    help="skip the skinny-GEMM sweeps (K = 4096, N = 27392, M = 1 .. 512; "
+                         "K = 18944, N = 3584, M = 1 .. 16)")
     ap.add_argument("--no-index-softmax", action="store_true",
                     help="skip the IndexSoftmax measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -498,6 +500,7 @@ def main():
     torch.cuda.empty_cache()
     isoft = None if args.no_index_softmax else index_softmax_measurement(qw, torch, K_steps)
     skinny = None if args.no_skinny else skinny_sweep_measurement(qw, wl, torch, K_steps)
+    long_k = None if args.no_skinny else skinny_sweep_measurement(qw, wl, torch, K_steps, wl.LONG_K)
     chain_info = None
     if not args.no_chain:
         chain_info = chain_measurement(qw, wl, torch, args.chain_replays)
@@ -517,6 +520,7 @@ def main():
         "decode_chain": chain_info,
         "index_softmax": isoft,
         "skinny_sweep": skinny,
+        "long_k_sweep": long_k,
     }
     print(json.dumps(line), flush=True)
 

@@ -105,15 +105,17 @@ __device__ __forceinline__ uint4 pack_perm16(const int (&q)[16])
 // are written as zeros).  a = maxabs / 127 and the codes exactly as k_quant_act, laid
 // out as B operands: row m, step st (64 k), lane block g -> 16 bytes at
 // ((m / 16) * KS + st) * 1024 + (16 g + m % 16) * 16.  A thread owns NS slots of 16
-// consecutive k (slot sl = tid + 256 t) and keeps their values in registers between
-// the maximum and the quantization, so X is read once.
-template <int NS>
-__global__ __launch_bounds__(kBlock) void k_quant_act_mfma(const float* __restrict__ X, int M,
-                                                           int K, int Mp, int KS,
-                                                           uint8_t* __restrict__ Xp,
-                                                           float* __restrict__ a_scale)
+// consecutive k (slot sl = tid + NT t) and keeps their values in registers between
+// the maximum and the quantization, so X is read once.  NT = 256 threads, or 1024 for
+// rows of more than 1024 slots (K > 16384), which keeps NS <= 4.
+template <int NS, int NT>
+__global__ __launch_bounds__(NT) void k_quant_act_mfma(const float* __restrict__ X, int M,
+                                                       int K, int Mp, int KS,
+                                                       uint8_t* __restrict__ Xp,
+                                                       float* __restrict__ a_scale)
 {
-    __shared__ float red[4];
+    constexpr int kBlock = NT;
+    __shared__ float red[NT / 64];
     const int slots = KS * 4;  // 16-code slots per row
     for (int m = blockIdx.x; m < Mp; m += gridDim.x) {
         const bool live = m < M;
@@ -130,7 +132,19 @@ __global__ __launch_bounds__(kBlock) void k_quant_act_mfma(const float* __restri
                 mx = fmaxf(mx, max_abs4(v[t][e]));
             }
         }
-        mx = block_max(mx, red);
+        if constexpr (NT == 256) {
+            mx = block_max(mx, red);
+        } else {
+            mx = wave_max(mx);
+            if ((threadIdx.x & 63) == 0)
+                red[threadIdx.x >> 6] = mx;
+            __syncthreads();
+            mx = red[0];
+#pragma unroll
+            for (int w = 1; w < NT / 64; ++w)
+                mx = fmaxf(mx, red[w]);
+            __syncthreads();  // red is reused by the next row of the grid-stride loop
+        }
         const float a = mx / 127.0f;
         const float r = 1.0f / a;
         const bool fast = r <= 3.0e38f;
@@ -1239,19 +1253,25 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     const size_t xp_bytes = ((size_t)mbtot * ks * 1024u + 255u) & ~(size_t)255u;
     float* a = reinterpret_cast<float*>(xp + xp_bytes);
     const int qgrid = mbtot * 16 < 65536 ? mbtot * 16 : 65536;
-    const int ns = (ks * 4 + kBlock - 1) / kBlock;  // 16-code slots per thread
+    const int ns = (ks * 4 + kBlock - 1) / kBlock;  // 16-code slots per thread of 256
+    const int ns_wide = (ks * 4 + 1023) / 1024;      // ... of 1024 (at most 4: K <= 65536)
     if (ns <= 1)
-        hipLaunchKernelGGL(k_quant_act_mfma<1>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+        hipLaunchKernelGGL((k_quant_act_mfma<1, kBlock>), dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
                            mbtot * 16, ks, xp, a);
     else if (ns <= 2)
-        hipLaunchKernelGGL(k_quant_act_mfma<2>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+        hipLaunchKernelGGL((k_quant_act_mfma<2, kBlock>), dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
                            mbtot * 16, ks, xp, a);
     else if (ns <= 4)
-        hipLaunchKernelGGL(k_quant_act_mfma<4>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+        hipLaunchKernelGGL((k_quant_act_mfma<4, kBlock>), dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
+    else if (ns_wide <= 2)
+        hipLaunchKernelGGL((k_quant_act_mfma<2, 1024>), dim3(qgrid), dim3(1024), 0, st, X, M, K,
+                           mbtot * 16, ks, xp, a);
+    else if (ns_wide <= 4)
+        hipLaunchKernelGGL((k_quant_act_mfma<4, 1024>), dim3(qgrid), dim3(1024), 0, st, X, M, K,
                            mbtot * 16, ks, xp, a);
     else
-        hipLaunchKernelGGL(k_quant_act_mfma<14>, dim3(qgrid), dim3(kBlock), 0, st, X, M, K,
-                           mbtot * 16, ks, xp, a);
+        return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -59,6 +59,9 @@ QWEN7B_W4A8 = {"workload": "qwen7b_linears_w4a8", "M": 1, "seed": 1,
 CHATGLM2_W8A16 = {"workload": "chatglm2_w8a16", "M": 1, "K": 4096, "N": 27392, "seed": 2}
 LMHEAD_W4A8 = {"workload": "lm_head_w4a8", "M": 1, "K": HIDDEN, "N": VOCAB, "seed": 3}
 SKINNY = {"workload": "skinny_sweep", "K": 4096, "N": 27392, "Ms": (1, 4, 16, 64, 512), "seed": 4}
+# The down projection of the Qwen-7B-class layer (long K) at a few rows of X.
+LONG_K = {"workload": "long_k_sweep_18944x3584", "K": INTERMEDIATE, "N": HIDDEN,
+          "Ms": (1, 2, 4, 16), "seed": 5}
 # The headline decode linear: the gate/up projection of the Qwen-7B-class layer.
 HEADLINE = {"workload": "qwen7b_gate_up_3584x18944", "M": 1, "K": HIDDEN, "N": INTERMEDIATE}
 

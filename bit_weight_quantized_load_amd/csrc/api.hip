@@ -104,7 +104,9 @@ bool tiling_ok(int bits, int64_t M, int u, int nw, int nwaves, int splitk,
             nwaves < 1)
             return false;
         const int64_t per = ((int64_t)L.nrg + nwaves - 1) / nwaves;
-        return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31);
+        const int64_t mtiles = M == 1 ? 1 : (M + 1) / 2;  // at least 2 rows of X per workgroup
+        return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31) &&
+               (int64_t)nwaves * mtiles * 64 * splitk < ((int64_t)1 << 31);
     }
     if (u < 0 || u > 8 || u == 5 || u == 6)
         return false;
@@ -584,7 +586,9 @@ bool w4_bsplit_ok(int64_t M, int64_t N, int64_t K, int waves, int blocks)
     if (waves < 1 || waves > 8 || (L.cg + waves - 1) / waves > 8 || blocks < 1 || blocks > L.nrg)
         return false;
     const int64_t per = ((int64_t)L.nrg + blocks - 1) / blocks;
-    return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 31);
+    const int64_t mtiles = M == 1 ? 1 : (M + 1) / 2;  // at least 2 rows of X per workgroup
+    return per <= 16 && per * L.cg * 1024 < ((int64_t)1 << 31) && M * K < ((int64_t)1 << 31) &&
+           (int64_t)blocks * mtiles * 64 * waves < ((int64_t)1 << 31);
 }
 
 int run_w4_bsplit(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,

@@ -22,6 +22,18 @@ __device__ __forceinline__ int row_sum16(int v)
     return v;
 }
 
+// Logical block of hardware block b out of G.  Workgroup b runs on XCD b % 8; this
+// numbers each XCD's blocks contiguously, so logical neighbours share an L2 (and, being
+// dispatched in order, run at about the same time).
+__device__ __forceinline__ int xcd_block(int b, int G)
+{
+    const int per = (G + 7) / 8, r = G % 8;
+    const int x = b % 8, i = b / 8;
+    if (r == 0 || x < r)
+        return x * per + i;
+    return r * per + (x - r) * (per - 1) + i;
+}
+
 __device__ __forceinline__ float row_sum16(float v)
 {
     v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x128, 0xf, 0xf, false));

@@ -49,17 +49,6 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-// Logical block of hardware block b out of G.  Workgroup b runs on XCD b % 8; this
-// numbers each XCD's blocks contiguously, so logical neighbours share an L2.
-__device__ __forceinline__ int xcd_block(int b, int G)
-{
-    const int per = (G + 7) / 8, r = G % 8;
-    const int x = b % 8, i = b / 8;
-    if (r == 0 || x < r)
-        return x * per + i;
-    return r * per + (x - r) * (per - 1) + i;
-}
-
 // The 512-k steps of a kernel: three weight register buffers (step c in w[c % 3]) and
 // two X register buffers (step c in x[c % 2]) rotate, so six steps make one loop trip
 // with no branch inside; the last zero to five steps follow the loop.  Expects QW_STEP,

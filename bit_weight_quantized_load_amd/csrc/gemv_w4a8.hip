@@ -937,8 +937,12 @@ __global__ __launch_bounds__(64 * kW4BsMaxWaves) void k_gemv_w4a8_bsplit(W4A8Bsp
     const int j = lane & 15, sub = lane >> 4;
     const int N = p.N, K = p.K, CG = p.cg;
     const int c_lo = ks * T;
-    const int b = blockIdx.x;
-    const int m0 = MT * (int)blockIdx.y;
+    // workgroup (run b, rows m0 ..): with several groups of rows, the groups of one run
+    // are logical neighbours on one XCD, so the repeated reads of its weights meet in L2
+    const int mtiles = (p.M + MT - 1) / MT;
+    const int L = mtiles > 1 ? xcd_block((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int b = L / mtiles;
+    const int m0 = MT * (L - b * mtiles);
     const int mv = min(MT, p.M - m0);
     const int rg0 = rg_of(b, p.per, p.rem);
     const int nb = min(U, rg_of(b + 1, p.per, p.rem) - rg0);
@@ -1041,7 +1045,7 @@ template <int T, int U, int MT>
 hipError_t launch_w4_bsplit_m(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st)
 {
     const int mtiles = (a.M + MT - 1) / MT;
-    hipLaunchKernelGGL((k_gemv_w4a8_bsplit<T, U, MT>), dim3(blocks, mtiles), dim3(64 * waves), 0, st, a);
+    hipLaunchKernelGGL((k_gemv_w4a8_bsplit<T, U, MT>), dim3(blocks * mtiles), dim3(64 * waves), 0, st, a);
     return hipGetLastError();
 }
 

@@ -602,7 +602,8 @@ __global__ __launch_bounds__(64 * S) void k_gemv_w8a16_flight_split(W8A16Args p)
 // pipeline with one unit requested ahead, X and the scales requested before any
 // weight.  Each weight word is cast once for the MT rows of X.  The per-slice fp32 row
 // sums meet in LDS and are added in slice order (deterministic) before the scale and
-// the f16 rounding.  Grid: (workgroups, ceil(M / MT)).  Up to 16 waves with MT == 1
+// the f16 rounding.  Grid: workgroups x ceil(M / MT) in one dimension, the groups of rows
+// of one run numbered onto one XCD.  Up to 16 waves with MT == 1
 // and slices of at most 4 tiles, else up to 8 (their registers).
 constexpr int kBsMaxWaves = 16;
 
@@ -619,8 +620,12 @@ __global__ __launch_bounds__(T <= 4 && MT == 1 ? 64 * kBsMaxWaves : 512) void k_
     const int j = lane & 31, sub = lane >> 5;
     const int N = p.N, K = p.K, CG = p.cg;
     const int c_lo = ks * T;
-    const int b = blockIdx.x;
-    const int m0 = MT * (int)blockIdx.y;
+    // workgroup (run b, rows m0 ..): with several groups of rows, the groups of one run
+    // are logical neighbours on one XCD, so the repeated reads of its weights meet in L2
+    const int mtiles = (p.M + MT - 1) / MT;
+    const int L = mtiles > 1 ? xcd_block((int)blockIdx.x, (int)gridDim.x) : (int)blockIdx.x;
+    const int b = L / mtiles;
+    const int m0 = MT * (L - b * mtiles);
     const int mv = min(MT, p.M - m0);
     const int rg0 = rg_of(b, p.per, p.rem);
     const int nb = min(U, rg_of(b + 1, p.per, p.rem) - rg0);
@@ -724,7 +729,7 @@ hipError_t launch_bsplit_m(const W8A16Args& a, const GemvTiling& t, hipStream_t 
 {
     if (t.splitk > (T <= 4 && MT == 1 ? kBsMaxWaves : 8))
         return hipErrorInvalidValue;
-    hipLaunchKernelGGL((k_gemv_w8a16_bsplit<T, U, MT>), dim3(t.blocks, t.m_tiles), dim3(64 * t.splitk), 0,
+    hipLaunchKernelGGL((k_gemv_w8a16_bsplit<T, U, MT>), dim3(t.blocks * t.m_tiles), dim3(64 * t.splitk), 0,
                        st, a);
     return hipGetLastError();
 }

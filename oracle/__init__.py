@@ -286,6 +286,8 @@ def int_attention(Q, K, V, b=5, c=6.6):
     V = _c(V, np.float32)
     Lq, d = Q.shape
     Lk = K.shape[0]
+    if K.shape != (Lk, d) or V.shape != (Lk, d):
+        raise ValueError("K and V must be [Lk][d] with the d of Q [Lq][d]")
     A = np.empty((Lq, Lk), np.int32)
     P = np.empty((Lq, Lk), np.uint8)
     O = np.empty((Lq, d), np.float32)

@@ -470,6 +470,54 @@ def test_int_attention_pipeline():
     assert cos > 0.98
 
 
+def test_int_attention_pv_and_output_scale_hand_case():
+    """A hand-sized case of the all-integer data flow of the IntAttention summary
+    (section 方法细节: per-tensor INT8 V, UINT8 P times INT8 V in integers, then one
+    dequantization; the UINT8 probabilities carry a factor 255, mechanism 3).  Two keys
+    with identical rows give equal logits, so IndexSoftmax gives P = round(255 / 2) =
+    128 (half up) for both.  V = [[1.0, -0.25], [0.5, 0.75]] has maxabs 1, so
+    s_V = fl32(1 / 127) and its codes are 127, -32 (-31.75), 64 (63.5 rounds half to
+    even) and 95 (95.25).  The integer P.V is then [128 * (127 + 64), 128 * (-32 + 95)]
+    = [24448, 8064] and O = P.V * s_V / 255, within one fp32 rounding."""
+    Q = np.array([[1.0, -2.0]], np.float32)
+    K = np.array([[0.5, 0.25], [0.5, 0.25]], np.float32)
+    V = np.array([[1.0, -0.25], [0.5, 0.75]], np.float32)
+    r = oracle.int_attention(Q, K, V)
+    assert r["P"].tolist() == [[128, 128]]
+    s_v = np.float32(1.0) / np.float32(127.0)
+    expect = np.array([24448.0, 8064.0]) * np.float64(s_v) / 255.0
+    expect = expect.astype(np.float32)
+    assert np.array_equal(r["O"][0], expect)
+    # the float attention over two equal logits averages the rows of V: [0.75, 0.25]
+    assert np.abs(r["O"][0] - np.array([0.75, 0.25])).max() < 0.01
+    # O scales with V exactly (a dropped or misplaced s_V fails), and flips with its sign
+    r2 = oracle.int_attention(Q, K, V * np.float32(2.0))
+    assert np.array_equal(r2["O"][0], np.float32(2.0) * expect)
+    r3 = oracle.int_attention(Q, K, -V)
+    assert np.array_equal(r3["O"][0], -expect)
+    with pytest.raises(ValueError):  # V of another head width
+        oracle.int_attention(Q, K, V[:, :1])
+
+
+def test_int_attention_pv_equals_an_int64_matmul():
+    """On a random head the oracle's output equals the int64 product of its UINT8
+    probabilities and the per-tensor INT8 codes of V (taken by the pinned activation
+    quantizer), dequantized once by s_V / 255: the integer P.V is checked whole."""
+    rng = np.random.default_rng(63)
+    Lq, Lk, d = 12, 150, 32
+    Q = rng.standard_normal((Lq, d)).astype(np.float32)
+    K = rng.standard_normal((Lk, d)).astype(np.float32)
+    V = rng.standard_normal((Lk, d)).astype(np.float32)
+    r = oracle.int_attention(Q, K, V)
+    v, sv = oracle.quant_act_i8(V.reshape(1, -1))
+    acc = r["P"].astype(np.int64) @ v.reshape(Lk, d).astype(np.int64)
+    assert np.abs(acc).max() < 2 ** 31
+    O = (acc.astype(np.float64) * np.float64(sv[0]) / 255.0).astype(np.float32)
+    assert np.array_equal(r["O"].view(np.uint32), O.view(np.uint32))
+    # the probabilities of each row sum to 255 within half a unit per key
+    assert np.all(np.abs(r["P"].astype(np.int64).sum(axis=1) - 255) <= Lk // 2)
+
+
 # ------------------------------------------------------------ W8 weights --
 
 def test_quant_w8_closed_form_rows():

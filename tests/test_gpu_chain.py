@@ -109,3 +109,35 @@ def test_fused_projections_equal_the_separate_ones(layer):
     assert np.array_equal(f["gate_up_proj"].view(np.uint32), gate_up.view(np.uint32))
     assert np.array_equal(f["o_proj"].view(np.uint32), o["o_proj"].view(np.uint32))
     assert np.array_equal(f["down_proj"].view(np.uint32), o["down_proj"].view(np.uint32))
+
+
+@pytest.mark.parametrize("group", ["qkv_proj", "gate_up_proj"])
+def test_fused_projection_matches_the_oracle(layer, group):
+    """The fused q|k|v (3584 -> 4608) and gate|up (3584 -> 37888) launches, one
+    activation quantization each, against the oracle on the concatenated weights: the
+    activation codes and scale, every int32 sum and every output (the page's next step
+    of removing the repeated quantization of the QKV and MLP projections, "Jetson Orin
+    AGX 上的 INT4 量化推理实践", section 后续优化方向)."""
+    packed, lm, xh, xi, sample = layer
+    parts = dict(chain.FUSED_GROUPS)[group]
+    W = np.concatenate([wl.weights(SEED, wl.tensor_id(p, 0), dict((n, N) for n, _, N in
+                                                                  wl.QWEN7B_LINEARS)[p],
+                                   wl.HIDDEN, outlier_rows=True) for p in parts])
+    N = W.shape[0]
+    say("fused vs oracle", group, N)
+    q, s = oracle.quant_w4(W)
+    del W
+    ref = oracle.gemv_w4a8(xh, q, s, nthreads=oracle.num_threads())
+    wq, sc = chain.fuse_along_n([packed[p] for p in parts])
+    assert np.array_equal(host(sc).view(np.uint32), s.view(np.uint32))
+    assert np.array_equal(host(qw.w4_codes(wq, N, wl.HIDDEN)), q)
+    xd = torch.from_numpy(xh).cuda()
+    out = qw.gemv_w4a8_debug(xd, wq, sc)
+    assert np.array_equal(host(out["xq"]), ref["xq"])
+    assert np.array_equal(host(out["a"]).view(np.uint32), ref["a"].view(np.uint32))
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert np.array_equal(host(out["Y"]).view(np.uint32), ref["Y"].view(np.uint32))
+    # the fused chain's launch of this group gives the same bits
+    fus = chain.DecodeChain(packed, None, xd, torch.from_numpy(xi).cuda(), layers=1, fused=True)
+    fus.run()
+    assert np.array_equal(host(fus.out[group]).view(np.uint32), ref["Y"].view(np.uint32))

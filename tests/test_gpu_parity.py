@@ -56,6 +56,37 @@ def rel_l2(y, y64):
     return float(np.linalg.norm(y - y64) / max(np.linalg.norm(y64), 1e-300))
 
 
+def half_ulp16(v):
+    """Half a binary16 ulp at magnitude |v| (2^-25 in the subnormal range)."""
+    v = np.abs(np.asarray(v, np.float64))
+    _, e = np.frexp(np.maximum(v, 2.0 ** -14))
+    return np.ldexp(1.0, e - 12)
+
+
+def w8a16_bound(X16, q, s16):
+    """Per-element bound of a W8A16 output around the exact value: the kernel sums the
+    K exact products q*x in fp32 in an order of its choosing (each addition rounds by at
+    most 2^-24 relative, so the sum is within (K - 1) * 2^-24 * sum|q*x|), multiplies by
+    the f16 scale (one more rounding) and rounds to f16 (half an ulp).  sum|q*x| is
+    taken in fp32 from exactly representable |q| and |x| and padded by 0.1%."""
+    K = X16.shape[1]
+    s = oracle.f32_from_f16(np.asarray(s16)).astype(np.float64)
+    absdot = np.abs(X16.astype(np.float32)) @ np.abs(q.astype(np.float32)).T
+    return (K + 2) * 2.0 ** -24 * absdot.astype(np.float64) * s[None, :] * 1.001
+
+
+def check_w8a16(y, X16, q, s16, y64):
+    """The W8A16 bars: relative L2 error <= 1e-3 over the whole output, and per element
+    |y - y64| <= half an f16 ulp + the fp32 summation bound (any valid order of the
+    fp32 sums meets it; a mis-indexed chunk or row does not)."""
+    y = np.asarray(y, np.float32).astype(np.float64)
+    assert rel_l2(y, y64) <= W8A16_RL2
+    bound = half_ulp16(np.maximum(np.abs(y), np.abs(y64))) + w8a16_bound(X16, q, s16)
+    err = np.abs(y - y64)
+    bad = err > bound
+    assert not bad.any(), (int(bad.sum()), float((err - bound).max()), np.argwhere(bad)[:4])
+
+
 def tile_layout(canon, N, R):
     """Canonical packed rows [N][row_bytes] -> the library's tile layout: 1 KB tiles of
     R rows x 512 k, i.e. R rows x (64 / R) chunks of 16 bytes, R = 4 for INT4 and 2 for
@@ -173,15 +204,15 @@ def _w8a16_case(seed, tid_w, tid_x, M, N, K, rows=None):
     y = qw.gemv_w8a16(dev(X16), Wq, s16)
     y = host(y if rows is None else y[:, torch.as_tensor(rows, device="cuda")]).astype(np.float64)
     y64 = oracle.gemv_w8a16_ref64(X16, q_o, s16_o, nthreads=oracle.num_threads())
-    return W if rows is None else W[rows], X16, y, y64
+    return W if rows is None else W[rows], X16, y, y64, q_o, s16_o
 
 
 def test_chatglm2_w8a16_config():
     c = wl.CHATGLM2_W8A16
     say("chatglm2 W8A16", c["K"], c["N"])
-    W, X16, y, y64 = _w8a16_case(c["seed"], wl.tensor_id("chatglm2", 0),
-                                 wl.tensor_id("chatglm2", 1), 1, c["N"], c["K"])
-    assert rel_l2(y, y64) <= W8A16_RL2
+    W, X16, y, y64, q8, s16 = _w8a16_case(c["seed"], wl.tensor_id("chatglm2", 0),
+                                          wl.tensor_id("chatglm2", 1), 1, c["N"], c["K"])
+    check_w8a16(y, X16, q8, s16, y64)
     yf = X16.astype(np.float64) @ W.astype(np.float64).T
     cos = float((y * yf).sum() / np.linalg.norm(y) / np.linalg.norm(yf))
     assert cos > 0.99
@@ -190,9 +221,9 @@ def test_chatglm2_w8a16_config():
 def test_headline_w8a16_shape():
     c = wl.HEADLINE
     say("headline W8A16", c["K"], c["N"])
-    _, _, y, y64 = _w8a16_case(7, wl.tensor_id("headline_w8", 0), wl.tensor_id("headline_w8", 1),
-                               1, c["N"], c["K"])
-    assert rel_l2(y, y64) <= W8A16_RL2
+    _, X16, y, y64, q8, s16 = _w8a16_case(7, wl.tensor_id("headline_w8", 0),
+                                          wl.tensor_id("headline_w8", 1), 1, c["N"], c["K"])
+    check_w8a16(y, X16, q8, s16, y64)
 
 
 # ------------------------------------------------------------------ config 3 --
@@ -203,21 +234,21 @@ def _sample_rows(N, n=2048, seed=0):
     return np.unique(rows)
 
 
-def test_lm_head_w4a8_sampled():
+def test_lm_head_w4a8_full():
+    """Every one of the 152064 rows: packed bytes, scales, int32 sums and outputs."""
     c = wl.LMHEAD_W4A8
     K, N = c["K"], c["N"]
     say("lm_head W4A8", K, N)
     W = wl.weights(c["seed"], wl.tensor_id("lm_head", 0), N, K)
     X = wl.activations(c["seed"], wl.tensor_id("lm_head", 1), 1, K)
-    rows = _sample_rows(N)
-    Wq, s, q_o, s_o = pack_w4_and_check(W, rows)
+    Wq, s, q_o, s_o = pack_w4_and_check(W)
     del W
-    out = qw.gemv_w4a8_debug(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", 1, N, K))
-    ref = oracle.gemv_w4a8(X, q_o, s_o)
-    ridx = torch.as_tensor(rows, device="cuda")
-    assert np.array_equal(host(out["acc"][:, ridx]), ref["acc"])
-    assert_w4a8_close(host(out["Y"][:, ridx]), ref["Y"])
-    assert torch.isfinite(out["Y"]).all().item()
+    out = qw.gemv_w4a8_debug(dev(X), Wq, s)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    assert np.array_equal(host(out["acc"]), ref["acc"])
+    assert np.array_equal(host(out["Y"]).view(np.uint32), ref["Y"].view(np.uint32))
+    Y = qw.gemv_w4a8(dev(X), Wq, s)
+    assert np.array_equal(host(Y).view(np.uint32), ref["Y"].view(np.uint32))
 
 
 # ------------------------------------------------------------------ config 4 --
@@ -240,7 +271,7 @@ def test_skinny_sweep_sampled(M):
     Wq8, s16, q8, s16_o = pack_w8_and_check(W, rows)
     y = qw.gemv_w8a16(dev(X16), Wq8, s16)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
-    assert rel_l2(host(y[:, ridx]), y64) <= W8A16_RL2
+    check_w8a16(host(y[:, ridx]), X16, q8, s16_o, y64)
 
 
 # ----------------------------------------------- skinny GEMM on the matrix cores --
@@ -271,7 +302,7 @@ def test_skinny_gemm_full_parity(M, N, K):
     Wq8, s16, q8, s16_o = pack_w8_and_check(W)
     y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
-    assert rel_l2(y, y64) <= W8A16_RL2
+    check_w8a16(y, X16, q8, s16_o, y64)
     assert not np.any(y[M // 2]) and not np.any(y[:, 0])
 
 
@@ -302,7 +333,7 @@ def test_matrix_core_kernels_every_launch_shape(M, N, K):
         assert torch.equal(Y, Yg), (nw, mb, nbw)
         if mb in (1, 2) and not (nw == 8 and nbw == 2):
             y = host(qw.gemm_w8a16_mfma(X16d, Wq8, s16, nw, mb, nbw))
-            assert rel_l2(y, y64) <= W8A16_RL2, (nw, mb, nbw)
+            check_w8a16(y, X16, q8, s16_o, y64)
 
 
 # The balanced matrix-core kernel (mb = 0): the ChatGLM2-shaped linear 4096 -> 27392 at
@@ -397,10 +428,10 @@ def test_balanced_w8a16_matrix_core_kernel_matches_oracle(M, N, K):
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     Xd = dev(X16)
     y = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 1))
-    assert rel_l2(y, y64) <= W8A16_RL2
+    check_w8a16(y, X16, q8, s16_o, y64)
     assert np.all(np.isfinite(y.astype(np.float32)))
     ys = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 1, 1))
-    assert rel_l2(ys, y64) <= W8A16_RL2
+    check_w8a16(ys, X16, q8, s16_o, y64)
     # the default path at these rows is the balanced kernel
     yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
     assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
@@ -421,14 +452,14 @@ def test_balanced_w8a16_two_block_kernel_matches_oracle(M, N, K):
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     Xd = dev(X16)
     y = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 2))
-    assert rel_l2(y, y64) <= W8A16_RL2
+    check_w8a16(y, X16, q8, s16_o, y64)
     assert np.all(np.isfinite(y.astype(np.float32)))
     # each row of X is summed in the same order as by the one-block kernel
     if M <= 16:
         y1 = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 0, 1))
         assert np.array_equal(y.view(np.uint16), y1.view(np.uint16))
     yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
-    assert rel_l2(yd, y64) <= W8A16_RL2
+    check_w8a16(yd, X16, q8, s16_o, y64)
     if M <= 64:  # the default path at 17 to 64 rows is this kernel
         assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 
@@ -497,7 +528,7 @@ def test_edge_shapes_both_ops(M, N, K):
     y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o)
     if np.linalg.norm(y64) > 0:
-        assert rel_l2(y, y64) <= W8A16_RL2
+        check_w8a16(y, X16, q8, s16_o, y64)
     if M > 1:
         assert not np.any(y[M - 1]) and not np.any(host(out["Y"])[M - 1])
 
@@ -540,7 +571,7 @@ def test_every_launch_shape_gives_the_same_result(M):
         Y = qw.gemv_w4a8_tiled(Xd, Wq, s, u, nw, nwaves)
         assert_w4a8_close(host(Y), ref["Y"])
         y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, u, nw, nwaves))
-        assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, nwaves)
+        check_w8a16(y, X16, q8, s16_o, y64)
         # every launch shape adds a row's products in the same order
         if y_first is None:
             y_first = y
@@ -656,7 +687,7 @@ def test_split_k_launch_shapes(M, N, K):
                     except qw.QWError as e:
                         assert e.status == qw.QW_ERR_TILING and K > 8192
                         continue
-                    assert rel_l2(y, y64) <= W8A16_RL2, (u, nw, nwaves, splitk)
+                    check_w8a16(y, X16, q8, s16_o, y64)
                     n8 += 1
     assert n >= 4 and n8 >= 2
     # all in flight with K in 8-tile slices (M == 1): 2..8 slices, 1..4 row groups a run
@@ -668,7 +699,7 @@ def test_split_k_launch_shapes(M, N, K):
                 assert torch.equal(y4, Y1), ("flight split", S, per)
                 if S <= 7:
                     y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 3, 4, -(-nrg8 // per), S))
-                    assert rel_l2(y, y64) <= W8A16_RL2, ("flight split", S, per)
+                    check_w8a16(y, X16, q8, s16_o, y64)
 
 
 # The balanced long-K W8A16 variant (u = 7): the 18944 -> 3584 down projection,
@@ -702,7 +733,7 @@ def test_balanced_long_k_w8a16_matches_oracle(M, N, K):
             if nwaves > nrg or -(-nrg // nwaves) > 16:
                 continue
             y = host(qw.gemv_w8a16_tiled(X16d, Wq8, s16, 7, S, nwaves, S))
-            assert rel_l2(y, y64) <= W8A16_RL2, (S, nwaves)
+            check_w8a16(y, X16, q8, s16_o, y64)
             assert np.all(np.isfinite(y.astype(np.float32)))
             # the slices' sums are added in slice order: the number of workgroups does
             # not change the bits
@@ -713,7 +744,7 @@ def test_balanced_long_k_w8a16_matches_oracle(M, N, K):
             n += 1
     assert n >= 4
     yd = host(qw.gemv_w8a16(X16d, Wq8, s16))
-    assert rel_l2(yd, y64) <= W8A16_RL2
+    check_w8a16(yd, X16, q8, s16_o, y64)
     # the default path is this variant up to 8 rows (16 with weights below 24 MB)
     if cg > 8 and (M <= 8 or (M <= 16 and N * K < 24 << 20)) and (M >= 2 or nrg >= 1024):
         S = min(8, -(-cg // 4))
@@ -806,7 +837,7 @@ def test_long_k_matrix_core_defaults_beyond_sixteen_rows(M, N, K):
     Wq8, s16, q8, s16_o = pack_w8_and_check(W)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     y = host(qw.gemv_w8a16(dev(X16), Wq8, s16))
-    assert rel_l2(y, y64) <= W8A16_RL2
+    check_w8a16(y, X16, q8, s16_o, y64)
 
 
 def test_repeated_calls_are_deterministic():

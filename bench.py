@@ -87,28 +87,53 @@ def host_threads() -> int:
     return max(1, n)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(W, X, X16, seconds, b_step):
-    """The oracle, as it stands, on this host: W4A8 (activation quantization, integer
-    GEMV, epilogue) plus the fp64 W8A16 reference, repeated for about `seconds`.
-    Weight quantization is load-time work on both sides and is not timed."""
+    """The oracle, as it stands, on this host: one step is W4A8 (activation quantization,
+    integer GEMV, epilogue) plus the fp64 W8A16 reference on the headline inputs.  At all
+    of the host's threads: the median of 5 runs of `reps` steps each, `reps` chosen so
+    the 5 runs take about `seconds`; at one thread: the median of 5 single steps.  Weight
+    quantization is load-time work on both sides and is not timed."""
+    import statistics
+
     import oracle
 
     q4, s4 = oracle.quant_w4(W)
     q8, s8 = oracle.quant_w8(W)
     nt = host_threads()
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.gemv_w4a8(X, q4, s4, nthreads=nt)
-        oracle.gemv_w8a16_ref64(X16, q8, s8, nthreads=nt)
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= seconds:
-            break
-    return {"value": round(reps * b_step / dt / 1e9, 4), "unit": "GB/s", "cores": nt,
+
+    def step(n):
+        oracle.gemv_w4a8(X, q4, s4, nthreads=n)
+        oracle.gemv_w8a16_ref64(X16, q8, s8, nthreads=n)
+
+    def run(n, reps):
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            step(n)
+        return (time.perf_counter() - t0) / reps
+
+    step(nt)
+    reps = max(1, int(seconds / 5 / max(run(nt, 1), 1e-4)))
+    t_all = statistics.median(run(nt, reps) for _ in range(5))
+    t_one = statistics.median(run(1, 1) for _ in range(5))
+    return {"value": round(b_step / t_all / 1e9, 4), "unit": "GB/s", "cores": nt,
             "kind": "oracle",
-            "sample": "%d repetitions of the full step (W4A8 + fp64 W8A16 reference, M=1 K=3584 "
-                      "N=18944) in %.1f s on %d OpenMP threads" % (reps, dt, nt)}
+            "sample": "the full step (W4A8 + fp64 W8A16 reference, M=1 K=3584 N=18944): median "
+                      "of 5 runs of %d steps on %d OpenMP threads; 1 thread: median of 5 steps"
+                      % (reps, nt),
+            "value_1_thread": round(b_step / t_one / 1e9, 4),
+            "ms_per_step": {"1_thread": round(t_one * 1e3, 3), "%d_threads" % nt: round(t_all * 1e3, 3)},
+            "cpu_model": cpu_model(), "host_cpus": len(os.sched_getaffinity(0))}
 
 
 def _pmc_per_dispatch(path, counter):
@@ -165,6 +190,174 @@ def write_traffic(fetch_copy, write_copy, fetch_bench, write_bench, copy_bytes, 
         with open(path, "w") as fh:
             json.dump(out, fh, indent=1)
         print(json.dumps(out))
+
+
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print("bench: " + msg, file=sys.stderr, flush=True)
+
+
+def graph_us(torch, fn, n, reps=3):
+    """Per-launch microseconds of fn(0), ..., fn(n - 1) captured in one HIP graph: one
+    untimed replay, then the median of `reps` replays timed with HIP events on the
+    stream the graph runs on.  Callers pass n >= the number of rotated copies, so every
+    copy is read in each replay."""
+    import statistics
+
+    fn(0)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / n)
+    del g
+    return statistics.median(ts)
+
+
+class ReadPool:
+    """One large device buffer whose disjoint slices serve as rotated sources of the bare
+    streaming read: slices of B bytes at 4 KB-aligned offsets, as many as fit."""
+
+    def __init__(self, torch, nbytes=int(2 * ROTATE_BYTES)):
+        self.torch = torch
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.buf.fill_(0x5A)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        self.sink = torch.empty(max(cus, 1024), dtype=torch.int32, device="cuda")
+
+    def time_us(self, qw, B, launches):
+        """Bare read of B bytes (rounded up to 16), rotated over the pool's slices."""
+        B = -(-B // 16) * 16
+        step = -(-B // 4096) * 4096
+        R = max(1, self.buf.numel() // step)
+        srcs = [self.buf[i * step:i * step + B] for i in range(R)]
+        n = max(launches, R)
+        return graph_us(self.torch, lambda i: qw.stream_read(srcs[i % R], self.sink), n), R
+
+
+def w4_config_times(qw, torch, W, X, pool, launches):
+    """W4A8 at M = 1 on the given weights (fp32 host arrays): (us, weight copies, bare-read
+    us of the same algorithmic bytes)."""
+    N, K = W.shape
+    Wq, s = qw.quantize_pack_w4(torch.from_numpy(W).cuda())
+    R = max(2, math.ceil(ROTATE_BYTES / Wq.numel()))
+    copies = [(Wq, s)] + [(Wq.clone(), s.clone()) for _ in range(R - 1)]
+    Xd = torch.from_numpy(X).cuda()
+    Y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+    t = graph_us(torch, lambda i: qw.gemv_w4a8(Xd, copies[i % R][0], copies[i % R][1], out=Y),
+                 max(launches, R))
+    tb, _ = pool.time_us(qw, bytes_w4a8(1, N, K), launches)
+    del copies, Wq, s
+    return t, R, tb
+
+
+def w8_config_times(qw, torch, W, X16, pool, launches):
+    N, K = W.shape
+    Wq, s = qw.quantize_pack_w8(torch.from_numpy(W).cuda())
+    R = max(2, math.ceil(ROTATE_BYTES / Wq.numel()))
+    copies = [(Wq, s)] + [(Wq.clone(), s.clone()) for _ in range(R - 1)]
+    Xd = torch.from_numpy(X16).cuda()
+    Y = torch.empty((1, N), dtype=torch.float16, device="cuda")
+    t = graph_us(torch, lambda i: qw.gemv_w8a16(Xd, copies[i % R][0], copies[i % R][1], out=Y),
+                 max(launches, R))
+    tb, _ = pool.time_us(qw, bytes_w8a16(1, N, K), launches)
+    del copies, Wq, s
+    return t, R, tb
+
+
+def oracle_ms(fn, runs):
+    """Median wall time of `runs` calls of fn(), in ms."""
+    import statistics
+
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        fn()
+        ts.append((time.perf_counter() - t0) * 1e3)
+    return statistics.median(ts)
+
+
+def configs_measurement(qw, wl, torch, pool, launches, with_oracle):
+    """Each decode linear of the workloads at M = 1 on its own: the tiny config, the seven
+    Qwen-7B projections (one line per distinct shape), the fused q|k|v and gate|up
+    launches, the lm_head and ChatGLM2's W8A16 linear.  Per line: GPU us (HIP events,
+    weight copies rotated past the cache), algorithmic bytes, GB/s and fraction of
+    8 TB/s, the bare streaming read of the same number of bytes (the ceiling a
+    weight-streaming kernel of that size meets on this GPU), and the oracle's wall time
+    on this host at 1 thread and at all threads (median of 3, of 1 for the lm_head at
+    1 thread)."""
+    import oracle
+
+    nt = host_threads()
+    seed = wl.QWEN7B_W4A8["seed"]
+    lines = {}
+
+    def qwen(name, rows=None):
+        K, N = [(k, n) for nm, k, n in wl.QWEN7B_LINEARS if nm == name][0]
+        return wl.weights(seed, wl.tensor_id(name, 0), N, K, outlier_rows=True)
+
+    xh = wl.activations(seed, wl.tensor_id("q_proj", 1), 1, wl.HIDDEN, outlier_channels=4)
+    xi = wl.activations(seed, wl.tensor_id("down_proj", 1), 1, wl.INTERMEDIATE, outlier_channels=4)
+    c0 = wl.TINY_W4A8
+    c3 = wl.LMHEAD_W4A8
+    c2 = wl.CHATGLM2_W8A16
+    cases = [
+        ("tiny_256x512", lambda: wl.weights(0, wl.tensor_id("tiny", 0), c0["N"], c0["K"]),
+         lambda: wl.activations(0, wl.tensor_id("tiny", 1), 1, c0["K"]), 4),
+        ("qwen7b_q_o_3584x3584", lambda: qwen("q_proj"), lambda: xh, 4),
+        ("qwen7b_k_v_3584x512", lambda: qwen("k_proj"), lambda: xh, 4),
+        ("qwen7b_gate_up_3584x18944", lambda: qwen("gate_proj"), lambda: xh, 4),
+        ("qwen7b_down_18944x3584", lambda: qwen("down_proj"), lambda: xi, 4),
+        ("qwen7b_qkv_fused_3584x4608",
+         lambda: np.concatenate([qwen("q_proj"), qwen("k_proj"), qwen("v_proj")]), lambda: xh, 4),
+        ("qwen7b_gate_up_fused_3584x37888",
+         lambda: np.concatenate([qwen("gate_proj"), qwen("up_proj")]), lambda: xh, 4),
+        ("lm_head_3584x152064", lambda: wl.weights(c3["seed"], wl.tensor_id("lm_head", 0), c3["N"], c3["K"]),
+         lambda: wl.activations(c3["seed"], wl.tensor_id("lm_head", 1), 1, c3["K"]), 4),
+        ("chatglm2_4096x27392", lambda: wl.weights(c2["seed"], wl.tensor_id("chatglm2", 0), c2["N"], c2["K"]),
+         lambda: wl.activations(c2["seed"], wl.tensor_id("chatglm2", 1), 1, c2["K"], dtype=np.float16), 8),
+    ]
+    for name, mkW, mkX, bits in cases:
+        progress("config " + name)
+        W, X = mkW(), mkX()
+        N, K = W.shape
+        if bits == 4:
+            t, R, tb = w4_config_times(qw, torch, W, X, pool, launches)
+            b = bytes_w4a8(1, N, K)
+        else:
+            t, R, tb = w8_config_times(qw, torch, W, X, pool, launches)
+            b = bytes_w8a16(1, N, K)
+        line = {"op": "gemv_w4a8" if bits == 4 else "gemv_w8a16", "M": 1, "K": K, "N": N,
+                "us": round(t, 3), "algo_bytes": b, "GB/s": round(b / t / 1e3, 1),
+                "frac_of_peak": round(b / t / 1e3 / PEAK_HBM_GBS, 4),
+                "bare_read_us": round(tb, 3), "frac_of_bare_read": round(tb / t, 4),
+                "weight_copies_rotated": R}
+        if with_oracle:
+            if bits == 4:
+                q, sc = oracle.quant_w4(W)
+                run = {n: (lambda n=n: oracle.gemv_w4a8(X, q, sc, nthreads=n)) for n in (1, nt)}
+            else:
+                q, sc = oracle.quant_w8(W)
+                run = {n: (lambda n=n: oracle.gemv_w8a16_ref64(X, q, sc, nthreads=n)) for n in (1, nt)}
+            big = N * K > 200_000_000
+            line["oracle_ms"] = {"1_thread": round(oracle_ms(run[1], 1 if big else 3), 3),
+                                 "%d_threads" % nt: round(oracle_ms(run[nt], 3), 3)}
+            del q, sc, run
+        lines[name] = line
+        del W
+        torch.cuda.empty_cache()
+    return lines
 
 
 def chain_measurement(qw, wl, torch, replays):
@@ -271,28 +464,15 @@ def skinny_sweep_measurement(qw, wl, torch, launches, c=None):
     R = max(2, math.ceil(ROTATE_BYTES / (Wq4.numel() + Wq8.numel())))
     copies = [(Wq4, s4, Wq8, s8)] + [(Wq4.clone(), s4.clone(), Wq8.clone(), s8.clone())
                                      for _ in range(R - 1)]
-    n = max(10, min(40, launches // 25))
-    out = {"workload": c["workload"], "K": K, "N": N, "launches": n, "weight_copies_rotated": R}
+    n = max(R, 20)  # every rotated copy is read in each timed replay
+    out = {"workload": c["workload"], "K": K, "N": N, "launches": n, "weight_copies_rotated": R,
+           "timing": "median of 3 graph replays of %d launches after an untimed one" % n}
 
     def timed(fn):
-        fn(0)
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n):
-                fn(i)
-        g.replay()
-        torch.cuda.synchronize()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        del g
-        return e0.elapsed_time(e1) * 1e3 / n
+        return graph_us(torch, fn, n)
 
     for M in c["Ms"]:
+        progress("%s M=%d" % (c["workload"], M))
         X = torch.from_numpy(wl.activations(c["seed"], 2, M, K, outlier_channels=4)).cuda()
         X16 = X.half()
         Y4 = torch.empty((M, N), dtype=torch.float32, device="cuda")
@@ -327,6 +507,9 @@ def main():
     ap.add_argument("--no-skinny", action="store_true",
                     help="skip the skinny-GEMM sweeps (K = 4096, N = 27392, M = 1 .. 512; "
                          "K = 18944, N = 3584, M = 1 .. 16)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-config M = 1 lines (each linear alone, beside a bare "
+                         "read of its bytes and the oracle's time)")
     ap.add_argument("--no-index-softmax", action="store_true",
                     help="skip the IndexSoftmax measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -445,50 +628,51 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    g_step, g4, g8, g4g = capture(step), capture(w4), capture(w8), capture(w4g)
-    g16, g4f = capture(f16), capture(w4f)
+    progress("headline step")
+    g_step = capture(step)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g_step.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    del g_step
 
-    def event_time_us(g):
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record()
-        g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / K_steps
-
-    t4 = event_time_us(g4)
-    t8 = event_time_us(g8)
-    t4g = event_time_us(g4g)
+    # per-kernel average launch time: a graph of max(K, copies) launches of one kernel,
+    # median of 3 replays timed with HIP events after an untimed one
+    n_k = max(K_steps, R, Rg, R16)
+    t4 = graph_us(torch, w4, n_k)
+    t8 = graph_us(torch, w8, n_k)
+    t4g = graph_us(torch, w4g, n_k)
     b4g = bytes_w4a8g(M, N, K, GROUP)
-    t16 = event_time_us(g16)
-    t4f = event_time_us(g4f)
+    t16 = graph_us(torch, f16, n_k)
+    t4f = graph_us(torch, w4f, n_k)
     b16 = 2 * N * K + 2 * M * K + 2 * M * N
     ms_per_step = wall * 1e3 / K_steps
     value = b_step / (ms_per_step * 1e-3) / 1e9
+    # the bare streaming read of the same bytes, rotated the same way: the ceiling a
+    # weight-streaming kernel of this size meets on this GPU
+    pool = ReadPool(torch)
+    tr4, rr4 = pool.time_us(qw, b4, n_k)
+    tr8, rr8 = pool.time_us(qw, b8, n_k)
+
+    def kline(t, b, **extra):
+        d = {"us": round(t, 3), "algo_bytes": b, "GB/s": round(b / t / 1e3, 1),
+             "frac_of_peak": round(b / t / 1e3 / PEAK_HBM_GBS, 4)}
+        d.update(extra)
+        return d
 
     kernels = {
-        "gemv_w4a8": {"us": round(t4, 3), "algo_bytes": b4, "GB/s": round(b4 / t4 / 1e3, 1),
-                      "frac_of_peak": round(b4 / t4 / 1e3 / PEAK_HBM_GBS, 4)},
-        "gemv_w8a16": {"us": round(t8, 3), "algo_bytes": b8, "GB/s": round(b8 / t8 / 1e3, 1),
-                       "frac_of_peak": round(b8 / t8 / 1e3 / PEAK_HBM_GBS, 4)},
+        "gemv_w4a8": kline(t4, b4, frac_of_bare_read=round(tr4 / t4, 4)),
+        "gemv_w8a16": kline(t8, b8, frac_of_bare_read=round(tr8 / t8, 4)),
+        # plain streaming reads of the two GEMVs' algorithmic bytes (qw_stream_read)
+        "bare_read_34MB": kline(tr4, b4, copies_rotated=rr4),
+        "bare_read_68MB": kline(tr8, b8, copies_rotated=rr8),
         # the group-wise INT4 variant (one scale per row and 128 k) on the same shape:
         # context, not part of the step
-        "gemv_w4a8g_g128": {"us": round(t4g, 3), "algo_bytes": b4g,
-                            "GB/s": round(b4g / t4g / 1e3, 1),
-                            "frac_of_peak": round(b4g / t4g / 1e3 / PEAK_HBM_GBS, 4)},
+        "gemv_w4a8g_g128": kline(t4g, b4g),
         # the page's ablations (context): FP16 GEMV, and weight-only INT4 unpacked to float
-        "ablation_fp16_gemv": {"us": round(t16, 3), "algo_bytes": b16,
-                               "GB/s": round(b16 / t16 / 1e3, 1),
-                               "frac_of_peak": round(b16 / t16 / 1e3 / PEAK_HBM_GBS, 4)},
-        "ablation_w4_float_unpack": {"us": round(t4f, 3), "algo_bytes": b4,
-                                     "GB/s": round(b4 / t4f / 1e3, 1),
-                                     "frac_of_peak": round(b4 / t4f / 1e3 / PEAK_HBM_GBS, 4)},
+        "ablation_fp16_gemv": kline(t16, b16),
+        "ablation_w4_float_unpack": kline(t4f, b4),
     }
     dom = "gemv_w8a16" if t8 >= t4 else "gemv_w4a8"
     ach = kernels[dom]["GB/s"]
@@ -496,17 +680,25 @@ def main():
     roofline = {"bound": "hbm", "achieved": ach, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "kernel": dom}
 
-    del g_step, g4, g8, g4g, g16, g4f, copies, copies_g, copies16, W16
+    del copies, copies_g, copies16, W16
     torch.cuda.empty_cache()
+    configs = None if args.no_configs else configs_measurement(
+        qw, wl, torch, pool, K_steps, with_oracle=not args.no_cpu_baseline)
+    del pool
+    torch.cuda.empty_cache()
+    progress("index softmax")
     isoft = None if args.no_index_softmax else index_softmax_measurement(qw, torch, K_steps)
+    progress("skinny sweep")
     skinny = None if args.no_skinny else skinny_sweep_measurement(qw, wl, torch, K_steps)
     long_k = None if args.no_skinny else skinny_sweep_measurement(qw, wl, torch, K_steps, wl.LONG_K)
     chain_info = None
     if not args.no_chain:
+        progress("decode chain")
         chain_info = chain_measurement(qw, wl, torch, args.chain_replays)
 
     cpu = None
     if not args.no_cpu_baseline:
+        progress("oracle on the host")
         cpu = cpu_baseline(W, X, X16, args.cpu_seconds, b_step)
 
     line = {
@@ -517,6 +709,7 @@ def main():
         "config": {"workload": c["workload"], "M": M, "K": K, "N": N,
                    "step": "gemv_w4a8 + gemv_w8a16", "weight_copies_rotated": R},
         "kernels": kernels, "roofline": roofline, "cpu_baseline": cpu,
+        "configs": configs,
         "decode_chain": chain_info,
         "index_softmax": isoft,
         "skinny_sweep": skinny,

@@ -63,6 +63,8 @@ SIGNATURES = {
     "qw_index_cint": (ctypes.c_int32, [ctypes.c_double, _I64, ctypes.c_double, ctypes.c_double]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
+    "qw_device_status": (_I, [_P, _I]),
+    "qw_stream_read": (_I, [_P, _SZ, _P, _I, _I, _I, _P]),
 }
 
 
@@ -443,3 +445,31 @@ def w8_codes(Wq, N, K, stream=None):
     codes = torch.empty((N, K), dtype=torch.int8, device=Wq.device)
     _call("qw_w8_codes", _ptr(Wq), N, K, _ptr(codes), _stream(stream))
     return codes
+
+
+def device_status(clear: bool = True) -> int:
+    """The library's device status word on the current device (QW_STATUS_* bits; 0 when
+    every fused activation quantization since the last clear ran as designed)."""
+    out = ctypes.c_uint32(0)
+    _call("qw_device_status", ctypes.byref(out), 1 if clear else 0)
+    return int(out.value)
+
+
+QW_STATUS_PRODUCER_WAIT = 1
+
+
+def stream_read(src, sink, waves=0, blocks=0, loads_in_flight=0, stream=None):
+    """Bandwidth reference: the kernel reads every byte of the contiguous device tensor
+    ``src`` once and writes one XOR word per workgroup into ``sink`` (uint32 or int32,
+    at least ``blocks`` words; ``blocks`` 0 = one workgroup per compute unit)."""
+    torch = _torch()
+    if not src.is_contiguous() or src.device.type != "cuda":
+        raise ValueError("src must be a contiguous device tensor")
+    if sink.device.type != "cuda" or sink.dtype not in (torch.int32, torch.uint32):
+        raise ValueError("sink must be a 32-bit device tensor")
+    need = blocks if blocks else torch.cuda.get_device_properties(src.device).multi_processor_count
+    if sink.numel() < need or not sink.is_contiguous():
+        raise ValueError("sink needs %d contiguous words" % need)
+    _call("qw_stream_read", _ptr(src), src.numel() * src.element_size(), _ptr(sink), int(waves),
+          int(blocks), int(loads_in_flight), _stream(stream))
+    return sink

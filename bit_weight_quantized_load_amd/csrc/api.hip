@@ -42,6 +42,11 @@ int check_shape(int64_t M, int64_t N, int64_t K)
 
 constexpr int kMaxLds = 60 * 1024;  // dynamic LDS budget per workgroup
 
+// Default launch shape of qw_stream_read: one workgroup per CU of kStreamReadWaves waves,
+// kStreamReadLoads 16-byte loads in flight per lane.
+constexpr int kStreamReadWaves = 8;
+constexpr int kStreamReadLoads = 4;
+
 // Largest K of the GEMVs: the streaming variant keeps one row of X (quantized codes
 // for W4A8, f16 for W8A16) in LDS, so K is bounded by the LDS budget.
 constexpr int64_t kMaxGemvK4 = 57344;
@@ -365,11 +370,15 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     return make_tiling(bits, M, N, K, 8, 4, (int)(nwaves > nrg ? nrg : nwaves));
 }
 
-// One device int per GPU for the packers' non-finite flag.
+// One device int per GPU for the packers' non-finite flag.  A packer call holds the
+// lock from clearing the flag to reading it back, so packers called at the same time
+// from several host threads run one after another and each reads its own result.
 std::mutex g_flag_mu;
 int* g_flag[64] = {nullptr};
 
-int get_flag(int** out)
+// Runs pack(flag) between clearing and reading back the device flag, under the lock.
+template <class F>
+int run_packer(hipStream_t st, F pack)
 {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -385,16 +394,18 @@ int get_flag(int** out)
             return hip_status(e);
         g_flag[dev] = static_cast<int*>(p);
     }
-    *out = g_flag[dev];
-    return QW_OK;
-}
-
-int read_flag(int* flag, hipStream_t st, int* host)
-{
-    hipError_t e = hipMemcpyAsync(host, flag, sizeof(int), hipMemcpyDeviceToHost, st);
+    int* flag = g_flag[dev];
+    e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, st);
+    if (e == hipSuccess)
+        e = pack(flag);
+    int host = 0;
+    if (e == hipSuccess)
+        e = hipMemcpyAsync(&host, flag, sizeof(int), hipMemcpyDeviceToHost, st);
     if (e == hipSuccess)
         e = hipStreamSynchronize(st);
-    return hip_status(e);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return host ? QW_ERR_NONFINITE : QW_OK;
 }
 
 int run_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
@@ -684,19 +695,10 @@ int quantize_pack_w4(const float* W, int64_t N, int64_t K, void* Wq, float* w_sc
         return st;
     if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_scale))
         return QW_ERR_ALIGN;
-    int* flag = nullptr;
-    if ((st = get_flag(&flag)) != QW_OK)
-        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, s);
-    if (e == hipSuccess)
-        e = qw::launch_pack_w4(W, (int)N, (int)K, static_cast<uint8_t*>(Wq), w_scale, flag, s);
-    if (e != hipSuccess)
-        return hip_status(e);
-    int host = 0;
-    if ((st = read_flag(flag, s, &host)) != QW_OK)
-        return st;
-    return host ? QW_ERR_NONFINITE : QW_OK;
+    return run_packer(s, [&](int* flag) {
+        return qw::launch_pack_w4(W, (int)N, (int)K, static_cast<uint8_t*>(Wq), w_scale, flag, s);
+    });
 }
 
 int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w_scale_f16,
@@ -709,19 +711,11 @@ int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w
         return st;
     if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_scale_f16))
         return QW_ERR_ALIGN;
-    int* flag = nullptr;
-    if ((st = get_flag(&flag)) != QW_OK)
-        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, s);
-    if (e == hipSuccess)
-        e = qw::launch_pack_w8(W, (int)N, (int)K, static_cast<uint8_t*>(Wq), w_scale_f16, flag, s);
-    if (e != hipSuccess)
-        return hip_status(e);
-    int host = 0;
-    if ((st = read_flag(flag, s, &host)) != QW_OK)
-        return st;
-    return host ? QW_ERR_NONFINITE : QW_OK;
+    return run_packer(s, [&](int* flag) {
+        return qw::launch_pack_w8(W, (int)N, (int)K, static_cast<uint8_t*>(Wq), w_scale_f16, flag,
+                                  s);
+    });
 }
 
 size_t qw_w4g_scale_bytes(int64_t N, int64_t K, int64_t group)
@@ -743,20 +737,11 @@ int quantize_pack_w4g(const float* W, int64_t N, int64_t K, int64_t group, void*
         return QW_ERR_SHAPE;
     if (!aligned16(W) || !aligned16(Wq) || !aligned16(w_scale))
         return QW_ERR_ALIGN;
-    int* flag = nullptr;
-    if ((st = get_flag(&flag)) != QW_OK)
-        return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t e = qw::launch_fill_zero(reinterpret_cast<uint32_t*>(flag), 1, s);
-    if (e == hipSuccess)
-        e = qw::launch_pack_w4g(W, (int)N, (int)K, (int)group, static_cast<uint8_t*>(Wq), w_scale,
-                                flag, s);
-    if (e != hipSuccess)
-        return hip_status(e);
-    int host = 0;
-    if ((st = read_flag(flag, s, &host)) != QW_OK)
-        return st;
-    return host ? QW_ERR_NONFINITE : QW_OK;
+    return run_packer(s, [&](int* flag) {
+        return qw::launch_pack_w4g(W, (int)N, (int)K, (int)group, static_cast<uint8_t*>(Wq),
+                                   w_scale, flag, s);
+    });
 }
 
 int qw_w4g_scales(const float* w_scale, int64_t N, int64_t K, int64_t group, float* out,
@@ -1063,5 +1048,46 @@ const char* qw_status_str(int status)
 }
 
 int qw_last_hip_error(void) { return g_last_hip_error; }
+
+int qw_stream_read(const void* src, size_t bytes, uint32_t* sink, int waves, int blocks,
+                   int loads_in_flight, void* stream)
+{
+    if (!src || !sink)
+        return QW_ERR_NULL;
+    if (bytes == 0 || (bytes % 16) != 0)
+        return QW_ERR_SHAPE;
+    if (!aligned16(src) || ((uintptr_t)sink & 3u) != 0)
+        return QW_ERR_ALIGN;
+    if (waves == 0)
+        waves = kStreamReadWaves;
+    if (blocks == 0)
+        blocks = device_cus();
+    if (loads_in_flight == 0)
+        loads_in_flight = kStreamReadLoads;
+    const size_t words = bytes / 16;
+    const int u = loads_in_flight;
+    if (!(waves == 1 || waves == 2 || waves == 4 || waves == 8 || waves == 16) || blocks < 1 ||
+        blocks > 65535 || !(u == 1 || u == 2 || u == 4 || u == 8 || u == 16))
+        return QW_ERR_TILING;
+    // each workgroup's share addressed by one buffer resource, below 2^31 bytes
+    if ((words + (size_t)blocks - 1) / (size_t)blocks * 16u >= ((size_t)1 << 31))
+        return QW_ERR_SHAPE;
+    return hip_status(qw::launch_stream_read(static_cast<const uint8_t*>(src), words, waves, blocks,
+                                             u, sink, static_cast<hipStream_t>(stream)));
+}
+
+int qw_device_status(uint32_t* status, int clear)
+{
+    if (!status)
+        return QW_ERR_NULL;
+    unsigned a = 0, b = 0;
+    hipError_t e = qw::prod_guard_status_rowwise(&a, clear != 0);
+    if (e == hipSuccess)
+        e = qw::prod_guard_status_groupwise(&b, clear != 0);
+    if (e != hipSuccess)
+        return hip_status(e);
+    *status = (a || b) ? QW_STATUS_PRODUCER_WAIT : 0u;
+    return QW_OK;
+}
 
 }  // extern "C"

@@ -151,12 +151,6 @@ __device__ __forceinline__ uint16_t load2(rsrc_t r, uint32_t offset)
     return __builtin_amdgcn_raw_buffer_load_b16(r, offset, 0, 0);
 }
 
-// Waits until this lane's outstanding vector memory operations (loads, stores and
-// atomics without return) have completed.  Used instead of a device-scope fence in
-// the split-K hand-off: the partial results travel through device-scope atomics,
-// which need only be complete, not flushed from a cache, before the hand-off
-// counter is bumped.  (A device-scope fence on a multi-die part writes back and
-// invalidates the whole L2.)
 // Issue-order barrier: every wave of the workgroup has issued its loads above this
 // point before any wave issues a load below it.  A CU serves vector loads in order,
 // so the small loads every wave waits on first (X) are not queued behind the weight
@@ -166,11 +160,6 @@ __device__ __forceinline__ void issue_barrier()
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-}
-
-__device__ __forceinline__ void wait_memory_ops()
-{
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
 // The same code computed with one multiply by r = 1/scale instead of a division.

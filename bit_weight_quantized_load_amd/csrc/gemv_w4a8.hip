@@ -841,6 +841,11 @@ hipError_t launch_prod_any(const W4A8Args& a, const GemvTiling& t, bool debug, h
 
 }  // namespace
 
+hipError_t prod_guard_status_rowwise(unsigned* trips, bool clear)
+{
+    return read_prod_guard(trips, clear);
+}
+
 hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, hipStream_t st)
 {
     if (t.u == 5 || t.u == 6)

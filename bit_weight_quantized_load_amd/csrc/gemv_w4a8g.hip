@@ -67,6 +67,11 @@ hipError_t launch_g_any(const W4A8Args& a, const GemvTiling& t, hipStream_t st)
 
 }  // namespace
 
+hipError_t prod_guard_status_groupwise(unsigned* trips, bool clear)
+{
+    return read_prod_guard(trips, clear);
+}
+
 hipError_t launch_gemv_w4a8g(const W4A8Args& a, const GemvTiling& t, int group, hipStream_t st)
 {
     if (t.u != 5 && t.u != 6)

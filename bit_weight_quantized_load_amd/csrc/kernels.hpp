@@ -217,5 +217,13 @@ hipError_t launch_gemv_w4f32(const float* X, const uint8_t* Wq, const float* s, 
 // Group-wise W4A8 GEMV (M == 1, producer-wave tilings u == 5 or 6): w_scale holds the
 // group scales in the layout of w4g_scale_index; group = 32 .. 512.
 hipError_t launch_gemv_w4a8g(const W4A8Args& a, const GemvTiling& t, int group, hipStream_t st);
+// Plain streaming read of `words` 16-byte words (bandwidth reference): `blocks`
+// workgroups of `waves` waves, u loads in flight per lane; one XOR word per workgroup.
+hipError_t launch_stream_read(const uint8_t* src, size_t words, int waves, int blocks, int u,
+                              uint32_t* sink, hipStream_t st);
+// Status words of the producer-wave kernels (row-wise and group-wise builds): nonzero when
+// a producer's bounded wait ran out since the last clear; synchronous.
+hipError_t prod_guard_status_rowwise(unsigned* trips, bool clear);
+hipError_t prod_guard_status_groupwise(unsigned* trips, bool clear);
 
 }  // namespace qw

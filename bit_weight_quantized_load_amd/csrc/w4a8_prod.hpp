@@ -15,6 +15,24 @@ namespace qw {
 
 namespace {
 
+// Set to 1 by a producer wave whose bounded wait for the other producers' maxima ran out
+// (never expected: every producer adds its maximum after its own loads only).  One word
+// per source file that includes this header, read and cleared from the host through
+// read_prod_guard; the kernel still finishes normally when it trips.
+__device__ unsigned int g_prod_guard_trips;
+
+inline hipError_t read_prod_guard(unsigned* out, bool clear)
+{
+    hipError_t e = hipMemcpyFromSymbol(out, HIP_SYMBOL(g_prod_guard_trips), sizeof(unsigned), 0,
+                                       hipMemcpyDeviceToHost);
+    if (e == hipSuccess && clear) {
+        const unsigned zero = 0;
+        e = hipMemcpyToSymbol(HIP_SYMBOL(g_prod_guard_trips), &zero, sizeof(unsigned), 0,
+                              hipMemcpyHostToDevice);
+    }
+    return e;
+}
+
 // acc[d] += 16 * (q . x) over the 8 weights of word d of a chunk.
 __device__ __forceinline__ void dot_chunk(const uint4 w, const uint32_t (&a)[8], int (&acc)[4])
 {
@@ -141,12 +159,16 @@ __global__ __launch_bounds__(64 * (NW + P)) void k_gemv_w4a8_prod(W4A8Args p)
             __hip_atomic_fetch_add(&s_cnt, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
         // Every producer adds 1 once, unconditionally, after its own X only, so the
-        // count reaches P; the bound is a guard, not a path taken.
+        // count reaches P; the bound is a guard, not a path taken.  If it ever runs out,
+        // the codes would come from a partial maximum: the status word records it.
         for (int spin = 0; spin < (1 << 20) &&
                            __hip_atomic_load(&s_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) <
                                (unsigned)P;
              ++spin)
             __builtin_amdgcn_s_sleep(1);
+        if (lane == 0 &&
+            __hip_atomic_load(&s_cnt, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < (unsigned)P)
+            atomicOr(&g_prod_guard_trips, 1u);
         mx = __uint_as_float(__hip_atomic_load(&s_max, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP));
         const float a = mx / 127.0f;
         const float r = 1.0f / a;

@@ -100,7 +100,10 @@ int quantize_pack_w4(const float* W, int64_t N, int64_t K, void* Wq, float* w_sc
    write-up, sections 2 and 3).  W fp32 [N][K] -> Wq (qw_w8_packed_bytes, tile layout) and
    w_scale_f16 [N] = f16(maxabs(W[n,:]) / 127); codes clamp(rint(W / s16), -127, 127)
    are taken against the stored f16 scale.  A row whose f16 scale is 0 gets zero
-   codes; a scale that overflows f16 is QW_ERR_NONFINITE.  Synchronises once. */
+   codes; a scale that overflows f16 is QW_ERR_NONFINITE.  Synchronises once.
+   The three packers share one device flag per GPU: calls from several host threads
+   are serialised inside the library (each call holds a lock from clearing the flag to
+   reading it back), so each reports its own non-finite status. */
 int quantize_pack_w8(const float* W, int64_t N, int64_t K, void* Wq, uint16_t* w_scale_f16,
                      void* stream);
 
@@ -300,6 +303,29 @@ int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t 
 int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b, double c,
                   uint8_t* P, void* stream);
 int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k);
+
+/* Bandwidth reference (not part of the linear): a kernel that only streams `bytes`
+   bytes (a multiple of 16) from src with 16-byte loads, each byte once, and writes one
+   32-bit XOR of what it read per workgroup to sink (4-byte aligned, at least `blocks`
+   words, or one per compute unit when `blocks` is 0).  A weight-streaming GEMV cannot be faster than this read of its weight
+   bytes: decode is memory-bound and GEMV-dominated ("Jetson Orin AGX 上的 INT4
+   量化推理实践", section 为什么这个结果有意义).  Launch shape: `blocks` workgroups
+   (0: one per compute unit) of `waves` waves (1, 2, 4, 8 or 16; 0: 8), each lane with
+   `loads_in_flight` loads requested before use (1, 2, 4, 8 or 16; 0: 4); the bytes are
+   split evenly over the workgroups.  QW_ERR_SHAPE for 0 or a non-multiple of 16 bytes or
+   a workgroup share of 2 GiB or more, QW_ERR_TILING for another launch shape. */
+int qw_stream_read(const void* src, size_t bytes, uint32_t* sink, int waves, int blocks,
+                   int loads_in_flight, void* stream);
+
+/* Device status of the library on the current device, read synchronously into the HOST
+   word *status, then cleared when `clear` is nonzero.  Bit QW_STATUS_PRODUCER_WAIT is set
+   when, in some earlier gemv_w4a8 / gemv_w4a8g call at M == 1, a wave of the fused
+   activation quantization stopped waiting for the other waves' partial maxima after its
+   bounded wait ran out (it cannot happen in a correct run: every wave publishes its own
+   maximum before waiting).  The call then finished normally but its activation codes may
+   have come from a partial maximum.  Not a hot-path call: it synchronises the device. */
+#define QW_STATUS_PRODUCER_WAIT 1u
+int qw_device_status(uint32_t* status, int clear);
 
 /* Text for a status code (static storage). */
 const char* qw_status_str(int status);

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 28
+    assert len(names) == 30
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -257,3 +257,17 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(qw, "_lib", None)
     with pytest.raises(RuntimeError, match="not built"):
         qw.lib()
+
+
+def test_stream_read_and_device_status_check_arguments_on_the_host():
+    sink = A2
+    assert L.qw_stream_read(NULL, 1024, sink, 0, 0, 0, NULL) == qw.QW_ERR_NULL
+    assert L.qw_stream_read(A, 1024, NULL, 0, 0, 0, NULL) == qw.QW_ERR_NULL
+    assert L.qw_stream_read(A, 0, sink, 0, 0, 0, NULL) == qw.QW_ERR_SHAPE
+    assert L.qw_stream_read(A, 1000, sink, 0, 0, 0, NULL) == qw.QW_ERR_SHAPE
+    assert L.qw_stream_read(MIS, 1024, sink, 0, 0, 0, NULL) == qw.QW_ERR_ALIGN
+    for bad in [(3, 1, 4), (8, -1, 4), (8, 1, 3), (32, 1, 4), (8, 70000, 4)]:
+        assert L.qw_stream_read(A, 1024, sink, *bad, NULL) == qw.QW_ERR_TILING, bad
+    # one workgroup's share would need a buffer resource of 2 GiB or more
+    assert L.qw_stream_read(A, 1 << 31, sink, 8, 1, 4, NULL) == qw.QW_ERR_SHAPE
+    assert L.qw_device_status(NULL, 0) == qw.QW_ERR_NULL

@@ -44,6 +44,7 @@ SIGNATURES = {
     "quant_act_i8": (_I, [_P, _I64, _I64, _P, _P, _P]),
     "gemv_w4a8": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
     "gemv_w8a16": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _P]),
+    "gemv_w4a8_noalloc": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "qw_w4_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_w8_codes": (_I, [_P, _I64, _I64, _P, _P]),
     "qw_gemv_w4a8_debug": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -213,6 +214,22 @@ def gemv_w4a8(X, Wq, w_scale, workspace=None, out=None, stream=None):
     _need(Y, torch.float32, (M, N), "out")
     wp, wn = _ws_args(workspace)
     _call("gemv_w4a8", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn, _stream(stream))
+    return Y
+
+
+def gemv_w4a8_noalloc(X, Wq, w_scale, out=None, stream=None):
+    """gemv_w4a8 without a workspace: from two rows of X the library's fixed per-GPU
+    scratch array (8 MiB) holds the activation codes; larger shapes raise QWError
+    (QW_ERR_WORKSPACE).  Calls overlapping on one GPU race."""
+    torch = _torch()
+    M, K = X.shape
+    N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    _call("gemv_w4a8_noalloc", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), _stream(stream))
     return Y
 
 

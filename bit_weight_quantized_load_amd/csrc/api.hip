@@ -370,6 +370,41 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     return make_tiling(bits, M, N, K, 8, 4, (int)(nwaves > nrg ? nrg : nwaves));
 }
 
+// Scratch of gemv_w4a8_noalloc: the activation codes and scales that gemv_w4a8 keeps in a
+// caller's workspace from two rows of X, here in a fixed device array instead, for
+// callers that cannot allocate.  Each GPU holds its own copy until the process ends.
+// Host code uses the address hipGetSymbolAddress gives on each device, never the
+// array's name (which on the host is only a stand-in).
+constexpr size_t kScratchBytes = (size_t)8 << 20;
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch[64] = {nullptr};
+
+// The device address of `scratch` on the current device, looked up on the first call
+// per device (with that device current) and kept.
+int scratch_address(void** out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return hip_status(e);
+    if (dev < 0 || dev >= 64)
+        return hip_status(hipErrorInvalidDevice);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return hip_status(e);
+        if (p == nullptr)
+            return hip_status(hipErrorInvalidSymbol);
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return QW_OK;
+}
+
 // One device int per GPU for the packers' non-finite flag.  A packer call holds the
 // lock from clearing the flag to reading it back, so packers called at the same time
 // from several host threads run one after another and each reads its own result.
@@ -901,6 +936,27 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
     }
     return run_w4a8(X, Wq, w_scale, M, N, K, Y, nullptr, nullptr, nullptr, workspace,
                     default_tiling(4, M, N, K), false, stream);
+}
+
+int gemv_w4a8_noalloc(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                      int64_t N, int64_t K, float* Y, void* stream)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
+        return QW_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y))
+        return QW_ERR_ALIGN;
+    const size_t need = qw_workspace_bytes(0, M, N, K);
+    if (need > kScratchBytes)
+        return QW_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        const int st = scratch_address(&ws);
+        if (st != QW_OK)
+            return st;
+    }
+    return gemv_w4a8(X, Wq, w_scale, M, N, K, Y, ws, need, stream);
 }
 
 int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int64_t M,

@@ -127,6 +127,21 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
               int64_t K, float* Y, void* workspace, size_t ws_bytes, void* stream);
 
+/* gemv_w4a8 for callers that cannot allocate (code under HIP graph capture, tight
+   serving loops, harnesses that forbid hipMalloc): the same computation and the same
+   output bits as gemv_w4a8, but from two rows of X the activation codes and scales go
+   to a fixed array of 8 MiB in device memory that the library holds on each GPU it runs
+   on until the process ends, instead of a caller's workspace.  The call allocates
+   nothing (no hipMalloc, hipFree or allocating library routine); the array's address is
+   looked up once per device on the first call, with that device current.  Shapes whose
+   workspace (qw_workspace_bytes(0, M, N, K)) exceeds 8 MiB return QW_ERR_WORKSPACE
+   (e.g. M = 512 fits up to K = 16320, M = 64 up to K = 57344).  Every call on one GPU
+   shares that GPU's array: calls that overlap in time on one GPU (several streams or
+   host threads) race and must be serialised by the caller.  The array needs no
+   initialisation: each call overwrites what it reads. */
+int gemv_w4a8_noalloc(const float* X, const void* Wq, const float* w_scale, int64_t M,
+                      int64_t N, int64_t K, float* Y, void* stream);
+
 /* Group-wise INT4 scales ("Jetson Orin AGX 上的 INT4 量化推理实践", section 后续优化方向,
    which lists a group-wise scale as future work; the formula is this library's reading:
    the row-wise rule applied to each group).  One fp32 scale per output row n and group t

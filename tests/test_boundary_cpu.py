@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 30
+    assert len(names) == 31
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -271,3 +271,14 @@ def test_stream_read_and_device_status_check_arguments_on_the_host():
     # one workgroup's share would need a buffer resource of 2 GiB or more
     assert L.qw_stream_read(A, 1 << 31, sink, 8, 1, 4, NULL) == qw.QW_ERR_SHAPE
     assert L.qw_device_status(NULL, 0) == qw.QW_ERR_NULL
+
+
+def test_noalloc_w4a8_checks_arguments_and_its_limit_on_the_host():
+    f = L.gemv_w4a8_noalloc
+    assert f(NULL, A2, A3, 2, 64, 512, A4, NULL) == qw.QW_ERR_NULL
+    assert f(A, A2, A3, 2, 64, 500, A4, NULL) == qw.QW_ERR_SHAPE
+    assert f(A, A2, A3, 0, 64, 512, A4, NULL) == qw.QW_ERR_SHAPE
+    # 512 rows fit the 8 MiB array up to K = 16320; 16384 does not
+    assert L.qw_workspace_bytes(0, 512, 64, 16320) <= 8 << 20 < L.qw_workspace_bytes(0, 512, 64, 16384)
+    assert f(A, A2, A3, 512, 64, 16384, A4, NULL) == qw.QW_ERR_WORKSPACE
+    assert f(A, A2, A3, 4096, 64, 4096, A4, NULL) == qw.QW_ERR_WORKSPACE

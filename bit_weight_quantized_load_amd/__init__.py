@@ -53,6 +53,8 @@ SIGNATURES = {
     "qw_gemm_w4a8_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _I, _P]),
     "qw_gemv_w4a8_long_k": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _I, _P]),
     "qw_gemm_w8a16_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
+    "qw_gemm_w8a16_tile": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
+    "qw_gemm_w4a8_tile": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _P]),
     "qw_w4g_scale_bytes": (_SZ, [_I64, _I64, _I64]),
     "quantize_pack_w4g": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "qw_w4g_scales": (_I, [_P, _I64, _I64, _I64, _P, _P]),
@@ -402,6 +404,42 @@ def gemm_w8a16_mfma(X16, Wq, w_scale16, nw=4, mb=1, nbw=1, out=None, stream=None
     _need(Y, torch.float16, (M, N), "out")
     _call("qw_gemm_w8a16_mfma", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y),
           nw, mb, nbw, _stream(stream))
+    return Y
+
+
+def gemm_w8a16_tile(X16, Wq, w_scale16, variant=0, out=None, stream=None):
+    """The tiled f16 matrix-core W8A16 GEMM at launch variant 0, 1 or 2 (128 rows of W by
+    128, 256 or 64 rows of X per workgroup)."""
+    torch = _torch()
+    M, K = X16.shape
+    N = w_scale16.shape[0]
+    _need(X16, torch.float16, (M, K), "X16")
+    _need(Wq, torch.uint8, (w8_packed_bytes(N, K),), "Wq")
+    _need(w_scale16, torch.float16, (N,), "w_scale16")
+    Y = torch.empty((M, N), dtype=torch.float16, device=X16.device) if out is None else out
+    _need(Y, torch.float16, (M, N), "out")
+    _call("qw_gemm_w8a16_tile", _ptr(X16), _ptr(Wq), _ptr(w_scale16), M, N, K, _ptr(Y), int(variant),
+          _stream(stream))
+    return Y
+
+
+def gemm_w4a8_tile(X, Wq, w_scale, variant=0, workspace=None, out=None, stream=None):
+    """The tiled int8 matrix-core W4A8 GEMM at a launch variant (see gemm_w8a16_tile);
+    the workspace (op 2 size) is allocated when not given."""
+    torch = _torch()
+    M, K = X.shape
+    N = w_scale.shape[0]
+    _need(X, torch.float32, (M, K), "X")
+    _need(Wq, torch.uint8, (w4_packed_bytes(N, K),), "Wq")
+    _need(w_scale, torch.float32, (N,), "w_scale")
+    if workspace is None:
+        workspace = torch.empty(int(lib().qw_workspace_bytes(2, M, N, K)), dtype=torch.uint8,
+                                device=X.device)
+    Y = torch.empty((M, N), dtype=torch.float32, device=X.device) if out is None else out
+    _need(Y, torch.float32, (M, N), "out")
+    wp, wn = _ws_args(workspace)
+    _call("qw_gemm_w4a8_tile", _ptr(X), _ptr(Wq), _ptr(w_scale), M, N, K, _ptr(Y), wp, wn, int(variant),
+          _stream(stream))
     return Y
 
 

@@ -7,6 +7,7 @@ from __future__ import annotations
 
 import concurrent.futures
 import glob
+import hashlib
 import os
 import shutil
 import subprocess
@@ -35,16 +36,37 @@ def sources():
     return sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every csrc/*.hip into libqwgemv.so (always recompiles)."""
+def _inputs_hash(src: str) -> str:
+    """Hash of a source, every header it may include and the flags."""
+    h = hashlib.sha256(" ".join(HIP_FLAGS).encode())
+    deps = [src] + sorted(glob.glob(os.path.join(HERE, "csrc", "*.hpp"))) + \
+        sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+    for f in deps:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:20]
+
+
+def build(verbose: bool = False, incremental: bool = False) -> str:
+    """Compile every csrc/*.hip into libqwgemv.so.  By default every source is compiled
+    again; with incremental=True an object whose source, headers and flags are unchanged
+    is taken from the _build/ cache at the repository root."""
     tmpdir = tempfile.mkdtemp(prefix="qwbuild")
+    cache = os.path.join(ROOT, "_build", "obj")
+    if incremental:
+        os.makedirs(cache, exist_ok=True)
     try:
         def compile_one(src):
             obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            cached = os.path.join(cache, "%s.%s.o" % (os.path.basename(src), _inputs_hash(src)))
+            if incremental and os.path.exists(cached):
+                return cached
             cmd = [HIPCC, *HIP_FLAGS, "-I", os.path.join(ROOT, "include"), "-c", src, "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             subprocess.check_call(cmd)
+            if incremental:
+                shutil.copyfile(obj, cached)
             return obj
 
         srcs = sources()
@@ -63,4 +85,6 @@ def build(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+
+    print(build(verbose=True, incremental="--incremental" in sys.argv))

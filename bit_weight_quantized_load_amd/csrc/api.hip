@@ -405,6 +405,34 @@ int scratch_address(void** out)
     return QW_OK;
 }
 
+// Launch variant of the tiled matrix-core GEMM for M rows of X, or -1 where the other
+// kernels stay faster.  Measured on MI355X at K = 4096, N = 27392 (us, tile against the
+// kernel it replaces): W8A16 at 48 rows 38.6 / 54.2, 64 rows 38.5 / 58.7 (128 x 64
+// tile), 96 rows 52.1 / 84.8 and 128 rows 53.7 / 112.9 (128 x 128), 256 rows 78.7 / 192.8
+// (256 x 128), 512 rows 144.9 / 369.9 (256 x 256); from 32 rows down the balanced kernels
+// stay (30.5 against 37.7 at 32).  W4A8 at 256 rows 47.4 / 54.1, 512 rows 84.1 / 89.1;
+// below 193 rows the many-block kernel stays (24.9 against 25.6 at 64, 35.6 / 34.9 at
+// 128).  A tile grid needs at least 128 tiles (half the compute units) to be used: the
+// largest tile of the row range that reaches it is taken, else the other kernels.
+int tile_variant(int bits, int64_t M, int64_t N)
+{
+    static const int v_lo[] = {2, -1}, v_mid[] = {0, 2, -1}, v_hi[] = {4, 0, 2, -1},
+                     v_top[] = {6, 4, 0, 2, -1};
+    const int* cand;
+    if (bits == 8)
+        cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 81 ? v_mid : M >= 33 ? v_lo : nullptr;
+    else
+        cand = M >= 385 ? v_top : M >= 193 ? v_hi : nullptr;
+    if (cand == nullptr)
+        return -1;
+    for (; *cand >= 0; ++cand) {
+        const int bm = qw::tile_rows_m(*cand), bn = *cand >= 4 ? 256 : 128;
+        if ((N + bn - 1) / bn * ((M + bm - 1) / bm) >= 128)
+            return *cand;
+    }
+    return -1;
+}
+
 // One device int per GPU for the packers' non-finite flag.  A packer call holds the
 // lock from clearing the flag to reading it back, so packers called at the same time
 // from several host threads run one after another and each reads its own result.
@@ -672,6 +700,23 @@ int run_w4_bsplit(const float* X, const void* Wq, const float* w_scale, int64_t 
     return hip_status(qw::launch_gemv_w4a8_bsplit(p, blocks, waves, st));
 }
 
+// Tiled matrix-core W4A8 path: the activations quantized into the workspace (row-major
+// codes, then one scale per row at the next multiple of 256 bytes; one workgroup per
+// row), then the tile kernel at the given launch variant.
+int run_w4_tile(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                int64_t K, float* Y, void* workspace, int variant, void* stream)
+{
+    const size_t codes = ((size_t)M * (size_t)K + 255u) & ~(size_t)255u;
+    int8_t* xq = static_cast<int8_t*>(workspace);
+    float* a = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + codes);
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = qw::launch_quant_act_rows(X, (int)M, (int)K, xq, a, st);
+    if (e != hipSuccess)
+        return hip_status(e);
+    return hip_status(qw::launch_gemm_w4a8_tile(xq, a, (int)M, (int)N, (int)K,
+                                                static_cast<const uint8_t*>(Wq), w_scale, Y, variant, st));
+}
+
 void w4_bsplit_default(int64_t N, int64_t K, int* waves, int* blocks)
 {
     const qw::TileLayout L = qw::tile_layout(4, N, K);
@@ -930,6 +975,17 @@ int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, i
             return run_w4_bsplit(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, waves, blocks, stream);
     }
     if (M >= qw::kMfmaMinM4) {
+        const int v = tile_variant(4, M, N);
+        if (v >= 0) {
+            if (!X || !Wq || !w_scale || !Y)
+                return QW_ERR_NULL;
+            if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+                !aligned16(workspace))
+                return QW_ERR_ALIGN;
+            if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
+                return QW_ERR_WORKSPACE;
+            return run_w4_tile(X, Wq, w_scale, M, N, K, Y, workspace, v, stream);
+        }
         int nw, mb, nbw;
         qw::mfma_default_shape(4, M, K, &nw, &mb, &nbw);
         return run_gemm_w4a8(X, Wq, w_scale, M, N, K, Y, workspace, ws_bytes, nw, mb, nbw, stream);
@@ -1001,6 +1057,9 @@ int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f1
     if (check_gemv_shape(8, M, N, K) != QW_OK)
         return (!X_f16 || !Wq || !w_scale_f16 || !Y_f16) ? QW_ERR_NULL : QW_ERR_SHAPE;
     if (M >= qw::kMfmaMinM8 && !long_k_rows(8, M, N, K)) {
+        const int v = tile_variant(8, M, N);
+        if (v >= 0)
+            return qw_gemm_w8a16_tile(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, v, stream);
         int nw, mb, nbw;
         qw::mfma_default_shape(8, M, K, &nw, &mb, &nbw);
         return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, workspace, nw, mb, nbw,
@@ -1060,6 +1119,40 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
     if (mb == 0 && ((K + 511) / 512 > 8 || M > (nbw == 1 ? 16 : 1024)))
         return QW_ERR_TILING;
     return run_gemm_w8a16(X_f16, Wq, w_scale_f16, M, N, K, Y_f16, nullptr, nw, mb, nbw, stream);
+}
+
+int qw_gemm_w8a16_tile(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
+                       int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int variant, void* stream)
+{
+    if (!X_f16 || !Wq || !w_scale_f16 || !Y_f16)
+        return QW_ERR_NULL;
+    if (check_gemv_shape(8, M, N, K) != QW_OK)
+        return QW_ERR_SHAPE;
+    if (!aligned16(X_f16) || !aligned16(Wq) || !aligned16(w_scale_f16) || !aligned16(Y_f16))
+        return QW_ERR_ALIGN;
+    if (qw::tile_rows_m(variant) == 0)
+        return QW_ERR_TILING;
+    return hip_status(qw::launch_gemm_w8a16_tile(X_f16, (int)M, (int)N, (int)K,
+                                                 static_cast<const uint8_t*>(Wq), w_scale_f16, Y_f16,
+                                                 variant, static_cast<hipStream_t>(stream)));
+}
+
+int qw_gemm_w4a8_tile(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
+                      int64_t K, float* Y, void* workspace, size_t ws_bytes, int variant,
+                      void* stream)
+{
+    if (!X || !Wq || !w_scale || !Y)
+        return QW_ERR_NULL;
+    if (check_gemv_shape(4, M, N, K) != QW_OK)
+        return QW_ERR_SHAPE;
+    if (!aligned16(X) || !aligned16(Wq) || !aligned16(w_scale) || !aligned16(Y) ||
+        !aligned16(workspace))
+        return QW_ERR_ALIGN;
+    if (!workspace || ws_bytes < qw::mfma_w4a8_workspace_bytes(M, K))
+        return QW_ERR_WORKSPACE;
+    if (qw::tile_rows_m(variant) == 0)
+        return QW_ERR_TILING;
+    return run_w4_tile(X, Wq, w_scale, M, N, K, Y, workspace, variant, stream);
 }
 
 int qw_w4_codes(const void* Wq, int64_t N, int64_t K, int8_t* codes, void* stream)

@@ -162,6 +162,27 @@ struct MfmaW8A16Args {
     int per, rem, nbmax;  // balanced variant (as in MfmaW4A8Args)
 };
 
+// Tiled matrix-core GEMM (gemm_tile.hip): one workgroup per output tile of BN rows of W
+// by BM rows of X, K walked in double-buffered stages through LDS.
+struct TileGemmArgs {
+    const void* X;          // W8A16: f16 [M][K]; W4A8: int8 codes [M][K] (workspace)
+    const uint8_t* Wq;
+    const void* w_scale;    // W8A16: f16 [N]; W4A8: fp32 [N]
+    void* Y;                // W8A16: f16 [M][N]; W4A8: fp32 [M][N]
+    const float* a_scale;   // W4A8: [M] (workspace)
+    int M, N, K;
+    int cg, nrg;
+    int mblocks;            // tiles along M (set by the launcher)
+};
+// Rows of X per tile of launch variant `variant` (0 when the variant does not exist).
+int tile_rows_m(int variant);
+hipError_t launch_gemm_w8a16_tile(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
+                                  const uint16_t* w_scale, uint16_t* Y, int variant, hipStream_t st);
+// Xq: row-major int8 codes [M][K] and a_scale [M] (launch_quant_act_rows)
+hipError_t launch_gemm_w4a8_tile(const int8_t* Xq, const float* a_scale, int M, int N, int K,
+                                 const uint8_t* Wq, const float* w_scale, float* Y, int variant,
+                                 hipStream_t st);
+
 size_t mfma_w4a8_workspace_bytes(int64_t M, int64_t K);
 // Launch shape of the matrix-core kernels: nw waves per workgroup (4 or 8), mb blocks
 // of 16 rows of X per workgroup, nbw blocks of 16 output rows per wave.

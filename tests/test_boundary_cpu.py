@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 31
+    assert len(names) == 33
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n

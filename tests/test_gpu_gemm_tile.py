@@ -1,0 +1,161 @@
+"""The tiled matrix-core GEMM (one workgroup per output tile of 128 rows of W by 64, 128
+or 256 rows of X, weights cast once per tile in on-chip memory) against the oracle, on
+an MI355X.
+
+W8A16 (ChatGLM2-6B W8A16 write-up, section 4): within relative L2 1e-3 of the fp64
+dequantize-then-multiply reference and per element within half an f16 ulp plus the
+fp32 summation bound.  W4A8 ("Jetson Orin AGX 上的 INT4 量化推理实践", sections 当前实现方式
+and 正确方向): the oracle's outputs bit for bit (exact int32 sums, the fixed epilogue).  Shapes: the top of the skinny-GEMM sweep (512 and 64 rows on
+4096 -> 27392, checked on sampled rows of W), and ragged M, N and K (a partial tile in
+each direction, K % 64 == 32, fewer rows than one tile)."""
+import numpy as np
+import pytest
+import torch
+
+import bit_weight_quantized_load_amd as qw
+import oracle
+import workloads as wl
+from bounds import check_w8a16
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    torch.cuda.set_device(0)
+    qw.lib()
+    yield
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+VARIANTS = (0, 1, 2, 3, 4, 5, 6)
+SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
+          (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_w8a16_tile_every_variant(M, N, K):
+    print("w8a16 tile", M, N, K, flush=True)
+    W = wl.weights(1500 + M, 1, N, K, outlier_rows=N >= 100)
+    W[min(3, N - 1)] = 0.0  # a zero row
+    X16 = wl.activations(1500 + M, 2, M, K, outlier_channels=4).astype(np.float16)
+    X16[M // 2] = 0  # a zero row of X
+    Wq, s16 = qw.quantize_pack_w8(dev(W))
+    q8, s16_o = oracle.quant_w8(W)
+    assert np.array_equal(host(s16).view(np.uint16), s16_o)
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    Xd = dev(X16)
+    for v in VARIANTS:
+        buf = torch.full((M * N + 64,), float("nan"), dtype=torch.float16, device="cuda")
+        Y = buf[:M * N].view(M, N)
+        qw.gemm_w8a16_tile(Xd, Wq, s16, v, out=Y)
+        y = host(Y)
+        assert np.all(np.isfinite(y.astype(np.float32))), v
+        assert np.all(np.isnan(host(buf[M * N:]).astype(np.float32))), v  # nothing past Y
+        check_w8a16(y, X16, q8, s16_o, y64)
+        assert not np.any(y[M // 2]) and not np.any(y[:, min(3, N - 1)])
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_w8a16_tile_sweep_shape_sampled(M):
+    c = wl.SKINNY
+    K, N = c["K"], c["N"]
+    print("w8a16 tile sweep shape", M, K, N, flush=True)
+    W = wl.weights(c["seed"], 1, N, K, outlier_rows=True)
+    X16 = wl.activations(c["seed"], 2, M, K, outlier_channels=4).astype(np.float16)
+    Wq, s16 = qw.quantize_pack_w8(dev(W))
+    rng = np.random.default_rng(M)
+    rows = np.unique(np.concatenate([np.arange(0, 160), np.arange(N - 160, N),
+                                     rng.choice(N, 400, replace=False)]))
+    q8, s16_o = oracle.quant_w8(W[rows])
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    ridx = torch.as_tensor(rows, device="cuda")
+    Xd = dev(X16)
+    for v in VARIANTS:
+        Y = qw.gemm_w8a16_tile(Xd, Wq, s16, v)
+        check_w8a16(host(Y[:, ridx]), X16, q8, s16_o, y64)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_w4a8_tile_every_variant(M, N, K):
+    print("w4a8 tile", M, N, K, flush=True)
+    W = wl.weights(1600 + M, 1, N, K, outlier_rows=N >= 100)
+    W[min(3, N - 1)] = 0.0
+    X = wl.activations(1600 + M, 2, M, K, outlier_channels=4)
+    X[M // 2] = 0.0
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    q, s_o = oracle.quant_w4(W)
+    assert np.array_equal(host(s).view(np.uint32), s_o.view(np.uint32))
+    ref = oracle.gemv_w4a8(X, q, s_o, nthreads=oracle.num_threads())
+    Xd = dev(X)
+    ws = torch.empty(int(qw.lib().qw_workspace_bytes(2, M, N, K)), dtype=torch.uint8, device="cuda")
+    for v in VARIANTS:
+        buf = torch.full((M * N + 64,), float("nan"), device="cuda")
+        Y = buf[:M * N].view(M, N)
+        qw.gemm_w4a8_tile(Xd, Wq, s, v, workspace=ws, out=Y)
+        y = host(Y)
+        assert np.all(np.isnan(host(buf[M * N:]))), v
+        assert np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32)), v
+
+
+@pytest.mark.parametrize("M", [64, 512])
+def test_w4a8_tile_sweep_shape_sampled(M):
+    c = wl.SKINNY
+    K, N = c["K"], c["N"]
+    print("w4a8 tile sweep shape", M, K, N, flush=True)
+    W = wl.weights(c["seed"], 1, N, K, outlier_rows=True)
+    X = wl.activations(c["seed"], 2, M, K, outlier_channels=4)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    rng = np.random.default_rng(M + 1)
+    rows = np.unique(np.concatenate([np.arange(0, 160), np.arange(N - 160, N),
+                                     rng.choice(N, 400, replace=False)]))
+    q, s_o = oracle.quant_w4(W[rows])
+    ref = oracle.gemv_w4a8(X, q, s_o, nthreads=oracle.num_threads())
+    ridx = torch.as_tensor(rows, device="cuda")
+    Xd = dev(X)
+    for v in VARIANTS:
+        Y = qw.gemm_w4a8_tile(Xd, Wq, s, v)
+        assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32)), v
+
+
+# The default entry points route to the tiled GEMM by rows of X where the output has at
+# least 128 tiles: W8A16 from 33 rows (128 x 64 tiles), 81 (128 x 128), 193 (256 x 128)
+# and 385 (256 x 256); W4A8 from 193 rows.  Checked on sampled rows of W.
+ROUTED = [(48, 20000, 1056), (150, 20000, 544), (300, 34000, 512), (520, 33000, 512),
+          (40, 3584, 4096)]
+
+
+@pytest.mark.parametrize("M,N,K", ROUTED)
+def test_default_paths_through_the_tiled_gemm(M, N, K):
+    print("default routed", M, N, K, flush=True)
+    W = wl.weights(1700 + M, 1, N, K, outlier_rows=True)
+    X = wl.activations(1700 + M, 2, M, K, outlier_channels=4)
+    X[M // 3] = 0.0
+    rng = np.random.default_rng(N)
+    rows = np.unique(np.concatenate([np.arange(0, 70), np.arange(N - 70, N),
+                                     rng.choice(N, 300, replace=False)]))
+    ridx = torch.as_tensor(rows, device="cuda")
+    Wd = dev(W)
+    Wq, s = qw.quantize_pack_w4(Wd)
+    q, s_o = oracle.quant_w4(W[rows])
+    ref = oracle.gemv_w4a8(X, q, s_o, nthreads=oracle.num_threads())
+    Y = qw.gemv_w4a8(dev(X), Wq, s, workspace=qw.make_workspace("w4a8", M, N, K))
+    assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32))
+    del Wq, s
+    X16 = X.astype(np.float16)
+    Wq8, s16 = qw.quantize_pack_w8(Wd)
+    q8, s16_o = oracle.quant_w8(W[rows])
+    y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
+    y = qw.gemv_w8a16(dev(X16), Wq8, s16)
+    check_w8a16(host(y[:, ridx]), X16, q8, s16_o, y64)
+    assert not np.any(host(y[M // 3]))

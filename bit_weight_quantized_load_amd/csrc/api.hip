@@ -407,26 +407,27 @@ int scratch_address(void** out)
 
 // Launch variant of the tiled matrix-core GEMM for M rows of X, or -1 where the other
 // kernels stay faster.  Measured on MI355X at K = 4096, N = 27392 (us, tile against the
-// kernel it replaces): W8A16 at 48 rows 38.6 / 54.2, 64 rows 38.5 / 58.7 (128 x 64
-// tile), 96 rows 52.1 / 84.8 and 128 rows 53.7 / 112.9 (128 x 128), 256 rows 78.7 / 192.8
-// (256 x 128), 512 rows 144.9 / 369.9 (256 x 256); from 32 rows down the balanced kernels
-// stay (30.5 against 37.7 at 32).  W4A8 at 256 rows 47.4 / 54.1, 512 rows 84.1 / 89.1;
-// below 193 rows the many-block kernel stays (24.9 against 25.6 at 64, 35.6 / 34.9 at
-// 128).  A tile grid needs at least 128 tiles (half the compute units) to be used: the
-// largest tile of the row range that reaches it is taken, else the other kernels.
+// kernel it replaces): W8A16 at 48 rows 36.7 / 44.2 and 64 rows 38.7 / 58.7 (64 x 64
+// tiles, four stages of loads in flight), 128 rows 48.0 / 112.9 (128 x 128, four
+// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 140.5 / 369.9 (256 x 256); from
+// 32 rows down the balanced kernels stay (30.5 against 37.7 at 32).  W4A8 at 128 rows
+// 32.4 / 34.5, 256 rows 47.4 / 54.1, 512 rows 81.5 / 89.1; below 113 rows the
+// many-block kernel stays (24.5 against 25.3 at 64, 30.0 against 33.3 at 96).  A tile
+// grid needs at least 128 tiles (half the compute units) to be used: the largest tile
+// of the row range that reaches it is taken, else the other kernels.
 int tile_variant(int bits, int64_t M, int64_t N)
 {
-    static const int v_lo[] = {2, -1}, v_mid[] = {0, 2, -1}, v_hi[] = {4, 0, 2, -1},
-                     v_top[] = {6, 4, 0, 2, -1};
+    static const int v_lo[] = {8, -1}, v_mid[] = {9, 8, -1}, v_hi[] = {4, 9, 8, -1},
+                     v_top[] = {6, 4, 9, 8, -1};
     const int* cand;
     if (bits == 8)
         cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 81 ? v_mid : M >= 33 ? v_lo : nullptr;
     else
-        cand = M >= 385 ? v_top : M >= 193 ? v_hi : nullptr;
+        cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 113 ? v_mid : nullptr;
     if (cand == nullptr)
         return -1;
     for (; *cand >= 0; ++cand) {
-        const int bm = qw::tile_rows_m(*cand), bn = *cand >= 4 ? 256 : 128;
+        const int bm = qw::tile_rows_m(*cand), bn = qw::tile_rows_n(*cand);
         if ((N + bn - 1) / bn * ((M + bm - 1) / bm) >= 128)
             return *cand;
     }

@@ -139,13 +139,13 @@ __device__ __forceinline__ void tile_gload(rsrc_t wr, rsrc_t xr, int s, int stag
     }
 }
 
-// Widens the weights of r and stores both operands of the stage in LDS buffer wl.
+// Widens piece q (q < PW: 16 bytes of weights; else 16 bytes of X) of register set r
+// and stores it in LDS buffer wl.
 template <class C, int BITS>
-__device__ __forceinline__ void tile_lstore(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r)
+__device__ __forceinline__ void tile_lstore_piece(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r,
+                                                  int q)
 {
-    uint8_t* xl = wl + C::WREG;
-#pragma unroll
-    for (int q = 0; q < C::PW; ++q) {
+    if (q < C::PW) {
         const int i = tid + C::T * q, row = i >> 2, j = i & 3;
         uint4 lo, hi;
         if constexpr (BITS == 8) {
@@ -163,20 +163,33 @@ __device__ __forceinline__ void tile_lstore(uint8_t* wl, int tid, const TileRegs
         }
         *reinterpret_cast<uint4*>(wl + swz(row, 2 * j)) = lo;
         *reinterpret_cast<uint4*>(wl + swz(row, 2 * j + 1)) = hi;
-    }
-#pragma unroll
-    for (int q = 0; q < C::PX; ++q) {
-        const int i = tid + C::T * q, row = i >> 3, c = i & 7;
-        *reinterpret_cast<uint4*>(xl + swz(row, c)) = BITS == 8 ? r.x[q] : perm16(r.x[q]);
+    } else {
+        const int qx = q - C::PW;
+        const int i = tid + C::T * qx, row = i >> 3, c = i & 7;
+        *reinterpret_cast<uint4*>(wl + C::WREG + swz(row, c)) = BITS == 8 ? r.x[qx] : perm16(r.x[qx]);
     }
 }
 
+template <class C, int BITS>
+__device__ __forceinline__ void tile_lstore(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r)
+{
+#pragma unroll
+    for (int q = 0; q < C::PW + C::PX; ++q)
+        tile_lstore_piece<C, BITS>(wl, tid, r, q);
+}
+
+// The multiplies of one stage from LDS buffer wl; the staging of the next stage into
+// buffer nl (from register set r) is spread over the four 16/32-k steps, after each
+// step's multiplies are issued: the MFMAs run asynchronously, so the cast and the LDS
+// stores issue while they execute instead of after them.
 template <class C, int BITS, class A>
-__device__ __forceinline__ void tile_compute(const uint8_t* wl, int wn, int wm, int rl, int half,
+__device__ __forceinline__ void tile_compute(const uint8_t* wl, uint8_t* nl, int tid, int wn, int wm,
+                                             int rl, int half, const TileRegs<C::PW, C::PX>& r,
                                              A (&acc)[C::IN][C::JM])
 {
     const uint8_t* xl = wl + C::WREG;
     constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
+    constexpr int NP = C::PW + C::PX;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         const int c = 2 * kk + half;
@@ -198,10 +211,13 @@ __device__ __forceinline__ void tile_compute(const uint8_t* wl, int wn, int wm, 
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
                         __builtin_bit_cast(v4i, a[i]), __builtin_bit_cast(v4i, b[j]), acc[i][j], 0, 0, 0);
             }
+#pragma unroll
+        for (int q = kk * NP / 4; q < (kk + 1) * NP / 4; ++q)
+            tile_lstore_piece<C, BITS>(nl, tid, r, q);
     }
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM>
+template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH>
 __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
 {
     using C = TileCfg<BITS, WN, WM, NWN, NWM>;
@@ -238,26 +254,25 @@ __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
                 acc[i][j][v] = 0;
 
     const int rl = lane & 31, half = lane >> 5;
-    // Two register sets: stage s + 1 is in flight while stage s is multiplied, and stage
-    // s + 2 is requested at the top of stage s.  Stages come in pairs (a last odd stage
-    // is paired with one past the end, which reads zeros and adds nothing).
-    Regs ra, rb;
-    tile_gload<C, BITS>(wr, xr, 0, stages, CG, xrow, tid, ra);
-    tile_gload<C, BITS>(wr, xr, 1, stages, CG, xrow, tid, rb);
-    tile_lstore<C, BITS>(lds, tid, ra);
-    // The loads of a stage are pinned above its multiplies (sched_barrier): left to the
-    // scheduler, they sink below the LDS stores and the prefetch is lost.
-    for (int s = 0; s < stages; s += 2) {
-        __syncthreads();  // stage s in buffer 0; every wave is done with buffer 1
-        tile_gload<C, BITS>(wr, xr, s + 2, stages, CG, xrow, tid, ra);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_compute<C, BITS>(lds, wn, wm, rl, half, acc);
-        tile_lstore<C, BITS>(lds + STAGE, tid, rb);
-        __syncthreads();  // stage s + 1 in buffer 1; every wave is done with buffer 0
-        tile_gload<C, BITS>(wr, xr, s + 3, stages, CG, xrow, tid, rb);
-        __builtin_amdgcn_sched_barrier(0);
-        tile_compute<C, BITS>(lds + STAGE, wn, wm, rl, half, acc);
-        tile_lstore<C, BITS>(lds, tid, ra);
+    // DEPTH register sets: at stage t, set t % DEPTH (stored to LDS during stage t - 1)
+    // takes the loads of stage t + DEPTH, and set (t + 1) % DEPTH, loaded DEPTH - 1 stages
+    // earlier, is staged into the other LDS buffer while stage t is multiplied.  The loop
+    // is unrolled DEPTH times so that buffers and register sets are static; stages past
+    // the last read zeros and add nothing.
+    Regs r[DEPTH];
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d)
+        tile_gload<C, BITS>(wr, xr, d, stages, CG, xrow, tid, r[d]);
+    tile_lstore<C, BITS>(lds, tid, r[0]);
+    for (int s = 0; s < stages; s += DEPTH) {
+#pragma unroll
+        for (int d = 0; d < DEPTH; ++d) {
+            __syncthreads();  // stage s + d in buffer d % 2; every wave is done with the other
+            tile_gload<C, BITS>(wr, xr, s + d + DEPTH, stages, CG, xrow, tid, r[d]);
+            __builtin_amdgcn_sched_barrier(0);
+            tile_compute<C, BITS>(lds + (d & 1) * STAGE, lds + ((d + 1) & 1) * STAGE, tid, wn, wm, rl,
+                                  half, r[(d + 1) % DEPTH], acc);
+        }
     }
 
     // Epilogue: lane (rl, half) of block (i, j) holds rows n = 8 g + 4 half + e of W
@@ -320,12 +335,12 @@ __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
     }
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM>
+template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH = 2>
 hipError_t go_tile(TileGemmArgs p, hipStream_t st)
 {
     using C = TileCfg<BITS, WN, WM, NWN, NWM>;
     const size_t lds = (size_t)2 * C::STAGE;
-    const void* kern = reinterpret_cast<const void*>(k_gemm_tile<BITS, WN, WM, NWN, NWM>);
+    const void* kern = reinterpret_cast<const void*>(k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH>);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
@@ -333,7 +348,7 @@ hipError_t go_tile(TileGemmArgs p, hipStream_t st)
     if (nbn * nbm > 0x7fffffff)
         return hipErrorInvalidValue;
     p.mblocks = (int)nbm;
-    hipLaunchKernelGGL((k_gemm_tile<BITS, WN, WM, NWN, NWM>), dim3((unsigned)(nbn * nbm)), dim3(C::T),
+    hipLaunchKernelGGL((k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH>), dim3((unsigned)(nbn * nbm)), dim3(C::T),
                        lds, st, p);
     return hipGetLastError();
 }
@@ -349,6 +364,9 @@ hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
     case 4: return go_tile<BITS, 64, 64, 4, 2>(p, st);   // 256 n x 128 m, 8 waves
     case 5: return go_tile<BITS, 128, 128, 2, 2>(p, st); // 256 n x 256 m, 4 waves
     case 6: return go_tile<BITS, 64, 128, 4, 2>(p, st);  // 256 n x 256 m, 8 waves
+    case 7: return go_tile<BITS, 64, 32, 2, 2, 4>(p, st); // variant 2, four stages in flight
+    case 8: return go_tile<BITS, 32, 32, 2, 2, 4>(p, st); // variant 3, four stages in flight
+    case 9: return go_tile<BITS, 64, 64, 2, 2, 4>(p, st); // variant 0, four stages in flight
     default: return hipErrorInvalidValue;
     }
 }
@@ -365,7 +383,19 @@ int tile_rows_m(int variant)
     case 4: return 128;
     case 5: return 256;
     case 6: return 256;
+    case 7: return 64;
+    case 8: return 64;
+    case 9: return 128;
     default: return 0;
+    }
+}
+
+int tile_rows_n(int variant)
+{
+    switch (variant) {
+    case 4: case 5: case 6: return 256;
+    case 3: case 8: return 64;
+    default: return 128;
     }
 }
 

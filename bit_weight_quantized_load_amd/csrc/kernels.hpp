@@ -176,6 +176,8 @@ struct TileGemmArgs {
 };
 // Rows of X per tile of launch variant `variant` (0 when the variant does not exist).
 int tile_rows_m(int variant);
+// Rows of W per tile of launch variant `variant`.
+int tile_rows_n(int variant);
 hipError_t launch_gemm_w8a16_tile(const uint16_t* X, int M, int N, int K, const uint8_t* Wq,
                                   const uint16_t* w_scale, uint16_t* Y, int variant, hipStream_t st);
 // Xq: row-major int8 codes [M][K] and a_scale [M] (launch_quant_act_rows)

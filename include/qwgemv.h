@@ -121,7 +121,7 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    what quant_act_i8 computes.  M == 1: one GEMV kernel with the activation
    quantization fused into its prologue; workspace may be NULL.  M >= 2: the
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
-   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 193 rows, where
+   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 113 rows, where
    the output has at least 128 tiles, the tiled GEMM of qw_gemm_w4a8_tile), or with
    K > 4096 and up to 8 rows (16 with packed weights below 24 MB) the balanced long-K
    GEMV kernel (qw_gemv_w4a8_long_k); results are the same bits as the GEMV's. */
@@ -294,8 +294,10 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
    section 4; gemv_w8a16's computation, Y = f16(s16[n] * sum_k q x) with the fp32 sum on
    the matrix cores) at an explicit launch variant: one workgroup of four waves per
    output tile of 128 rows of W by 128 (variant 0), 256 (variant 1) or 64 (variant 2)
-   rows of X, or of 64 by 64 (variant 3), or of eight waves per 256 by 128 (variant 4),
-   the INT8 weights cast to f16 once per tile in on-chip memory.  Same arguments and
+   rows of X, or of 64 by 64 (variant 3), or of eight waves per 256 by 128 (variant 4)
+   or 256 by 256 (variant 6), or of four waves with 128 by 128 each (variant 5); variants
+   7, 8 and 9 are 2, 3 and 0 with four stages of loads in flight instead of two; the
+   INT8 weights cast to f16 once per tile in on-chip memory.  Same arguments and
    limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another variant. */
 int qw_gemm_w8a16_tile(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int variant, void* stream);

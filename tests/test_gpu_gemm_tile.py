@@ -38,7 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-VARIANTS = (0, 1, 2, 3, 4, 5, 6)
+VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
 SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
           (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
 
@@ -129,10 +129,10 @@ def test_w4a8_tile_sweep_shape_sampled(M):
 
 
 # The default entry points route to the tiled GEMM by rows of X where the output has at
-# least 128 tiles: W8A16 from 33 rows (128 x 64 tiles), 81 (128 x 128), 193 (256 x 128)
-# and 385 (256 x 256); W4A8 from 193 rows.  Checked on sampled rows of W.
+# least 128 tiles: W8A16 from 33 rows (64 x 64 tiles), 81 (128 x 128), 193 (256 x 128)
+# and 385 (256 x 256); W4A8 from 113 rows.  Checked on sampled rows of W.
 ROUTED = [(48, 20000, 1056), (150, 20000, 544), (300, 34000, 512), (520, 33000, 512),
-          (40, 3584, 4096)]
+          (40, 3584, 4096), (120, 9000, 2080), (64, 3000, 18944)]
 
 
 @pytest.mark.parametrize("M,N,K", ROUTED)

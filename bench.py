@@ -37,6 +37,10 @@ if ROOT not in sys.path:
 METRIC = "W4A8/W8A16 GEMV µs and HBM GB/s (% of peak), M=1 K=3584 N=18944"
 PEAK_HBM_GBS = 8000.0
 ROTATE_BYTES = 1.5e9  # > 256 MB last-level cache, several times over
+# At most this many rotated copies of one buffer: shapes below 1.5 GB / 1024 (the tiny
+# and k/v linears, under 1.5 MB) are launch-bound, and a graph of tens of thousands of
+# launches per timing adds nothing.
+MAX_COPIES = 1024
 
 
 def bytes_w4a8(M, N, K):
@@ -153,6 +157,12 @@ def _pmc_per_dispatch(path, counter):
     return {k: list(v.values()) for k, v in per.items()}
 
 
+# The kernel instances the headline step runs (built-in launch shapes at M=1, K=3584,
+# N=18944); the counters are read for these names exactly.
+HEADLINE_KERNELS = {"gemv_w4a8": "k_gemv_w4a8_prod<7, 8, 2, 1, 0, false>",
+                    "gemv_w8a16": "k_gemv_w8a16_flight<7, 1, 4>"}
+
+
 def write_traffic(fetch_copy, write_copy, fetch_bench, write_bench, copy_bytes, commands):
     """HBM bytes per launch of both GEMVs from four rocprofv3 --pmc runs (FETCH_SIZE and
     WRITE_SIZE, KiB per dispatch, each on a plain device copy of copy_bytes and on this
@@ -175,8 +185,8 @@ def write_traffic(fetch_copy, write_copy, fetch_bench, write_bench, copy_bytes, 
     c = wl.HEADLINE
     M, K, N = c["M"], c["K"], c["N"]
     for kernel, algo in (("gemv_w4a8", bytes_w4a8(M, N, K)), ("gemv_w8a16", bytes_w8a16(M, N, K))):
-        fk = median_of(fetch_bench, "FETCH_SIZE", kernel)
-        wk = median_of(write_bench, "WRITE_SIZE", kernel)
+        fk = median_of(fetch_bench, "FETCH_SIZE", HEADLINE_KERNELS[kernel])
+        wk = median_of(write_bench, "WRITE_SIZE", HEADLINE_KERNELS[kernel])
         hbm = int(round((fk * f_scale + wk * w_scale) * 1024))
         out = {"kernel": kernel, "workload": c["workload"],
                "kernel_source_sha": kernel_source_hash(kernel),
@@ -240,7 +250,7 @@ class ReadPool:
         """Bare read of B bytes (rounded up to 16), rotated over the pool's slices."""
         B = -(-B // 16) * 16
         step = -(-B // 4096) * 4096
-        R = max(1, self.buf.numel() // step)
+        R = max(1, min(MAX_COPIES, self.buf.numel() // step))
         srcs = [self.buf[i * step:i * step + B] for i in range(R)]
         n = max(launches, R)
         return graph_us(self.torch, lambda i: qw.stream_read(srcs[i % R], self.sink), n), R
@@ -251,7 +261,7 @@ def w4_config_times(qw, torch, W, X, pool, launches):
     us of the same algorithmic bytes)."""
     N, K = W.shape
     Wq, s = qw.quantize_pack_w4(torch.from_numpy(W).cuda())
-    R = max(2, math.ceil(ROTATE_BYTES / Wq.numel()))
+    R = max(2, min(MAX_COPIES, math.ceil(ROTATE_BYTES / Wq.numel())))
     copies = [(Wq, s)] + [(Wq.clone(), s.clone()) for _ in range(R - 1)]
     Xd = torch.from_numpy(X).cuda()
     Y = torch.empty((1, N), dtype=torch.float32, device="cuda")
@@ -265,7 +275,7 @@ def w4_config_times(qw, torch, W, X, pool, launches):
 def w8_config_times(qw, torch, W, X16, pool, launches):
     N, K = W.shape
     Wq, s = qw.quantize_pack_w8(torch.from_numpy(W).cuda())
-    R = max(2, math.ceil(ROTATE_BYTES / Wq.numel()))
+    R = max(2, min(MAX_COPIES, math.ceil(ROTATE_BYTES / Wq.numel())))
     copies = [(Wq, s)] + [(Wq.clone(), s.clone()) for _ in range(R - 1)]
     Xd = torch.from_numpy(X16).cuda()
     Y = torch.empty((1, N), dtype=torch.float16, device="cuda")

@@ -409,9 +409,9 @@ int scratch_address(void** out)
 // kernels stay faster.  Measured on MI355X at K = 4096, N = 27392 (us, tile against the
 // kernel it replaces): W8A16 at 48 rows 36.7 / 44.2 and 64 rows 38.7 / 58.7 (64 x 64
 // tiles, four stages of loads in flight), 128 rows 48.0 / 112.9 (128 x 128, four
-// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 140.5 / 369.9 (256 x 256); from
+// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 127.5 / 369.9 (256 x 256); from
 // 32 rows down the balanced kernels stay (30.5 against 37.7 at 32).  W4A8 at 128 rows
-// 32.4 / 34.5, 256 rows 47.4 / 54.1, 512 rows 81.5 / 89.1; below 113 rows the
+// 32.4 / 34.5, 256 rows 47.4 / 54.1, 512 rows 74.4 / 89.1; below 113 rows the
 // many-block kernel stays (24.5 against 25.3 at 64, 30.0 against 33.3 at 96).  A tile
 // grid needs at least 128 tiles (half the compute units) to be used: the largest tile
 // of the row range that reaches it is taken, else the other kernels.

@@ -40,6 +40,11 @@
 // produces (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15); the X codes are
 // permuted the same way when staged, and the int32 dot over the group is unchanged.
 //
+// Epilogue: the multiplies take X as the A operand and the weights as B, so each
+// accumulator register holds one row of Y across 32 consecutive output columns and the
+// stores of a half-wave are contiguous (with the operands the other way round each
+// store scattered over 32 rows, and HBM write traffic was 2-3x the output).
+//
 // Grid: one workgroup per tile, numbered so that the tiles of X that share a block of
 // weights are neighbours on one XCD (dispatched together, the repeated weight reads
 // meet in that XCD's L2).
@@ -204,12 +209,15 @@ __device__ __forceinline__ void tile_compute(const uint8_t* wl, uint8_t* nl, int
         for (int i = 0; i < C::IN; ++i)
 #pragma unroll
             for (int j = 0; j < C::JM; ++j) {
+                // X is the A operand and the weights the B operand, so the result is Y
+                // itself (rows m, columns n) and a store instruction covers 32
+                // consecutive n of one row
                 if constexpr (BITS == 8)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(v8h, a[i]), __builtin_bit_cast(v8h, b[j]), acc[i][j], 0, 0, 0);
+                        __builtin_bit_cast(v8h, b[j]), __builtin_bit_cast(v8h, a[i]), acc[i][j], 0, 0, 0);
                 else
                     acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        __builtin_bit_cast(v4i, a[i]), __builtin_bit_cast(v4i, b[j]), acc[i][j], 0, 0, 0);
+                        __builtin_bit_cast(v4i, b[j]), __builtin_bit_cast(v4i, a[i]), acc[i][j], 0, 0, 0);
             }
 #pragma unroll
         for (int q = kk * NP / 4; q < (kk + 1) * NP / 4; ++q)
@@ -275,60 +283,42 @@ __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
         }
     }
 
-    // Epilogue: lane (rl, half) of block (i, j) holds rows n = 8 g + 4 half + e of W
-    // (g, e = 0..3: register 4 g + e) and row m = rl of X: four consecutive n per g.
+    // Epilogue: lane (rl, half) of block (i, j) holds rows m = 8 g + 4 half + e of X's
+    // block j (g, e = 0..3: register 4 g + e) and column n = rl of W's block i; the 32
+    // lanes of a half-wave store 32 consecutive n of one row.
     const rsrc_t sr = make_rsrc_u(p.w_scale, (uint32_t)N * (BITS == 8 ? 2u : 4u));
-    float av[JM];
-    if constexpr (BITS == 4) {
-        const rsrc_t ar = make_rsrc_u(p.a_scale, (uint32_t)M * 4u);
-#pragma unroll
-        for (int j = 0; j < JM; ++j)
-            av[j] = __uint_as_float(load4(ar, (uint32_t)(m0 + wm * WM + 32 * j + rl) * 4u));
-    }
+    const rsrc_t ar = make_rsrc_u(p.a_scale, BITS == 4 ? (uint32_t)M * 4u : 0u);
 #pragma unroll
     for (int i = 0; i < IN; ++i) {
+        const int n = n0 + wn * WN + 32 * i + rl;
+        const float sc = BITS == 8 ? __half2float(__ushort_as_half(load2(sr, (uint32_t)n * 2u)))
+                                   : __uint_as_float(load4(sr, (uint32_t)n * 4u));
+        if (n >= N)
+            continue;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const int n = n0 + wn * WN + 32 * i + 8 * g + 4 * half;
-            float sc[4];
+        for (int j = 0; j < JM; ++j) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                sc[e] = BITS == 8 ? __half2float(__ushort_as_half(load2(sr, (uint32_t)(n + e) * 2u)))
-                                  : __uint_as_float(load4(sr, (uint32_t)(n + e) * 4u));
+            for (int g = 0; g < 4; ++g) {
+                const int mb0 = m0 + wm * WM + 32 * j + 8 * g + 4 * half;
+                float av[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (BITS == 4) {
+                    const float4 a4 = load16f(ar, (uint32_t)mb0 * 4u);
+                    av[0] = a4.x;
+                    av[1] = a4.y;
+                    av[2] = a4.z;
+                    av[3] = a4.w;
+                }
 #pragma unroll
-            for (int j = 0; j < JM; ++j) {
-                const int m = m0 + wm * WM + 32 * j + rl;
-                if (m >= M)
-                    continue;
-                if constexpr (BITS == 8) {
-                    uint16_t h[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        h[e] = __half_as_ushort(__float2half_rn(sc[e] * acc[i][j][4 * g + e]));
-                    uint16_t* dst = static_cast<uint16_t*>(p.Y) + (size_t)m * N + n;
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        *reinterpret_cast<uint2*>(dst) = make_uint2(
-                            (uint32_t)h[0] | ((uint32_t)h[1] << 16), (uint32_t)h[2] | ((uint32_t)h[3] << 16));
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N)
-                                dst[e] = h[e];
-                    }
-                } else {
-                    float y[4];
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        y[e] = ((float)(acc[i][j][4 * g + e] >> 4) * sc[e]) * av[j];
-                    float* dst = static_cast<float*>(p.Y) + (size_t)m * N + n;
-                    if ((N & 3) == 0 && n + 3 < N) {
-                        *reinterpret_cast<float4*>(dst) = make_float4(y[0], y[1], y[2], y[3]);
-                    } else {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < N)
-                                dst[e] = y[e];
-                    }
+                for (int e = 0; e < 4; ++e) {
+                    const int m = mb0 + e;
+                    if (m >= M)
+                        continue;
+                    if constexpr (BITS == 8)
+                        static_cast<uint16_t*>(p.Y)[(size_t)m * N + n] =
+                            __half_as_ushort(__float2half_rn(sc * acc[i][j][4 * g + e]));
+                    else
+                        static_cast<float*>(p.Y)[(size_t)m * N + n] =
+                            ((float)(acc[i][j][4 * g + e] >> 4) * sc) * av[e];
                 }
             }
         }

@@ -60,13 +60,20 @@ def bytes_w8a16(M, N, K):
 
 
 def kernel_source_hash(kernel: str) -> str:
+    """Hash of the code (comments and whitespace removed) of the sources that define the
+    kernel and choose its launch shape."""
+    import re
+
     csrc = os.path.join(ROOT, "bit_weight_quantized_load_amd", "csrc")
     files = ["common.hpp", "kernels.hpp", "api.hip"]
     files += ["gemv_w4a8.hip", "w4a8_prod.hpp"] if kernel == "gemv_w4a8" else ["gemv_w8a16.hip"]
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(csrc, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(csrc, f)) as fh:
+            code = fh.read()
+        code = re.sub(r"/\*.*?\*/", " ", code, flags=re.S)
+        code = re.sub(r"//[^\n]*", " ", code)
+        h.update(" ".join(code.split()).encode())
     return h.hexdigest()[:16]
 
 

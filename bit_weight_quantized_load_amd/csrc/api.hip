@@ -295,13 +295,21 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     // 4 consumer and 4 producer waves on at most one workgroup per two row groups
     // (3584 -> 3584: 3.28 against 4.32 us; 3584 -> 512: 3.02 against 4.16 us; 3584 -> 4608:
     // 3.87 against 4.72 us)
+    // From 4096 to 16383 row groups (the fused gate|up projection 3584 -> 37888) two
+    // workgroups per CU of 6 consumer and 2 producer waves: 12.16 against 13.14 us.  From
+    // 1024 to 2047 row groups (the fused q|k|v 3584 -> 4608) 5 consumer and 3 producer
+    // waves: 3.60 against 3.79 us.  (Measured with the timing order varied.)
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG) {
         const int cus = device_cus();
+        if (nrg >= 4096 && nrg < 16384 && tiling_ok(bits, M, 5, 6, cus * 2 * 6, 2, L))
+            return make_tiling(bits, M, N, K, 5, 6, cus * 2 * 6, 2);
         if (nrg >= 2048) {
             if (tiling_ok(bits, M, 5, 8, cus * 8, 2, L))
                 return make_tiling(bits, M, N, K, 5, 8, cus * 8, 2);
         } else {
             const int blocks = (int)std::min<int64_t>(cus, std::max<int64_t>(1, nrg / 2));
+            if (nrg >= 1024 && tiling_ok(bits, M, 5, 5, blocks * 5, 3, L))
+                return make_tiling(bits, M, N, K, 5, 5, blocks * 5, 3);
             if (tiling_ok(bits, M, 5, 4, blocks * 4, 4, L))
                 return make_tiling(bits, M, N, K, 5, 4, blocks * 4, 4);
         }
@@ -1027,6 +1035,15 @@ int qw_gemv_w4a8_debug(const float* X, const void* Wq, const float* w_scale, int
     // producer, register and LDS variants), else from the register or LDS variant (every
     // variant gives the same bits)
     GemvTiling t = default_tiling(4, M, N, K);
+    if (t.u == 5 && !((t.nw == 8 && t.prod == 2) || (t.nw == 4 && t.prod == 4))) {
+        // producer shapes built with debug outputs: 8 + 2 waves (one workgroup per CU) or
+        // 4 + 4 (at most one workgroup per two row groups); the same bits as any shape
+        const qw::TileLayout L = qw::tile_layout(4, N, K);
+        const int cus = device_cus();
+        t = L.nrg >= 2048 ? make_tiling(4, M, N, K, 5, 8, cus * 8, 2)
+                          : make_tiling(4, M, N, K, 5, 4,
+                                        (int)std::min<int64_t>(cus, std::max<int64_t>(1, L.nrg / 2)) * 4, 4);
+    }
     if (t.u == 2 || t.u == 3) {
         const qw::TileLayout L = qw::tile_layout(4, N, K);
         t = L.cg <= qw::kRegCG && M == 1 ? make_tiling(4, M, N, K, 0, 4, L.nrg < 1600 ? L.nrg : 1600)

@@ -295,13 +295,14 @@ GemvTiling default_tiling(int bits, int64_t M, int64_t N, int64_t K)
     // 4 consumer and 4 producer waves on at most one workgroup per two row groups
     // (3584 -> 3584: 3.28 against 4.32 us; 3584 -> 512: 3.02 against 4.16 us; 3584 -> 4608:
     // 3.87 against 4.72 us)
-    // From 4096 to 16383 row groups (the fused gate|up projection 3584 -> 37888) two
-    // workgroups per CU of 6 consumer and 2 producer waves: 12.16 against 13.14 us.  From
+    // From 8192 to 16383 row groups (the fused gate|up projection 3584 -> 37888) two
+    // workgroups per CU of 6 consumer and 2 producer waves: 12.16 against 13.14 us (at
+    // 4736 row groups, 3584 -> 18944, slower: 7.38 against 7.10).  From
     // 1024 to 2047 row groups (the fused q|k|v 3584 -> 4608) 5 consumer and 3 producer
     // waves: 3.60 against 3.79 us.  (Measured with the timing order varied.)
     if (bits == 4 && M == 1 && L.cg <= qw::kRegCG) {
         const int cus = device_cus();
-        if (nrg >= 4096 && nrg < 16384 && tiling_ok(bits, M, 5, 6, cus * 2 * 6, 2, L))
+        if (nrg >= 8192 && nrg < 16384 && tiling_ok(bits, M, 5, 6, cus * 2 * 6, 2, L))
             return make_tiling(bits, M, N, K, 5, 6, cus * 2 * 6, 2);
         if (nrg >= 2048) {
             if (tiling_ok(bits, M, 5, 8, cus * 8, 2, L))

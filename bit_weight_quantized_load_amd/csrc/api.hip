@@ -418,7 +418,8 @@ int scratch_address(void** out)
 // kernels stay faster.  Measured on MI355X at K = 4096, N = 27392 (us, tile against the
 // kernel it replaces): W8A16 at 48 rows 36.7 / 44.2 and 64 rows 38.7 / 58.7 (64 x 64
 // tiles, four stages of loads in flight), 128 rows 48.0 / 112.9 (128 x 128, four
-// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 127.5 / 369.9 (256 x 256); from
+// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 122.1 / 369.9 (256 x 256, INT8
+// weights in LDS; 128.7 with them cast to f16 when staged); from
 // 32 rows down the balanced kernels stay (30.5 against 37.7 at 32).  W4A8 at 128 rows
 // 32.4 / 34.5, 256 rows 47.4 / 54.1, 512 rows 74.4 / 89.1; below 113 rows the
 // many-block kernel stays (24.5 against 25.3 at 64, 30.0 against 33.3 at 96).  A tile
@@ -427,10 +428,10 @@ int scratch_address(void** out)
 int tile_variant(int bits, int64_t M, int64_t N)
 {
     static const int v_lo[] = {8, -1}, v_mid[] = {9, 8, -1}, v_hi[] = {4, 9, 8, -1},
-                     v_top[] = {6, 4, 9, 8, -1};
+                     v_top[] = {6, 4, 9, 8, -1}, v_top8[] = {11, 4, 9, 8, -1};
     const int* cand;
     if (bits == 8)
-        cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 81 ? v_mid : M >= 33 ? v_lo : nullptr;
+        cand = M >= 385 ? v_top8 : M >= 193 ? v_hi : M >= 81 ? v_mid : M >= 33 ? v_lo : nullptr;
     else
         cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 113 ? v_mid : nullptr;
     if (cand == nullptr)

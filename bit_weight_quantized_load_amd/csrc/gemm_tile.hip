@@ -88,6 +88,26 @@ __device__ __forceinline__ uint4 perm16(uint4 x)
 
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowB + 16 * (c ^ ((r >> 1) & 7)); }
 
+// Narrow weight rows: 64 bytes, eight 8-byte units, unit u of row r at position
+// u ^ ((r / 4) % 8).  An operand read (8 bytes per lane, rows r..r+31 at one unit) puts
+// the eight rows that share a quarter of the 64 banks (rows r + 4t) on eight distinct
+// positions.
+__device__ __forceinline__ int swz_n(int r, int u) { return r * 64 + 8 * (u ^ ((r >> 2) & 7)); }
+
+// 8 bytes of narrow weights (one MFMA operand per lane) -> the wide operand: 8 f16
+// (INT8) or 16 int8 lanes of 16 q in the unpack order (INT4).
+template <int BITS>
+__device__ __forceinline__ uint4 widen8(uint2 w)
+{
+    if constexpr (BITS == 8) {
+        const uint2 a = cast4_f16(w.x), b = cast4_f16(w.y);
+        return make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+        return make_uint4((w.x << 4) & 0xF0F0F0F0u, w.x & 0xF0F0F0F0u, (w.y << 4) & 0xF0F0F0F0u,
+                          w.y & 0xF0F0F0F0u);
+    }
+}
+
 // Buffer resource from values that are uniform but may have been computed in vector
 // registers (a clamp becomes v_med3): taken through readfirstlane so that the resource
 // stays in scalar registers and each buffer load is a single instruction.
@@ -100,17 +120,24 @@ __device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t bytes)
                      __builtin_amdgcn_readfirstlane(bytes));
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM>
+// NARROW: the weights stay in LDS as stored in memory (INT8 or packed INT4, 64 bytes
+// per row per stage in both cases: 64 k of INT8, 128 k of INT4) and each wave widens
+// the operands it reads; otherwise they are widened once when staged (128 bytes per
+// row).  Narrow weights halve the weight bytes written to and read from LDS, the
+// bound of the many-row case, at the price of widening each operand in every wave
+// that reads it.
+template <int BITS, int WN, int WM, int NWN, int NWM, bool NARROW = false>
 struct TileCfg {
     static constexpr int NWN_ = NWN, NWM_ = NWM;
+    static constexpr bool NARROW_ = NARROW;
     static constexpr int T = 64 * NWN * NWM;
     static constexpr int BN = WN * NWN, BM = WM * NWM;
     static constexpr int BK = BITS == 8 ? 64 : 128;  // k per stage
     static constexpr int IN = WN / 32, JM = WM / 32;
     static constexpr int PW = BN * 4 / T;  // 16-byte weight loads per thread (64 B per row)
     static constexpr int PX = BM * 8 / T;  // 16-byte X loads per thread (128 B per row)
-    static constexpr int WREG = BN * kRowB;
-    static constexpr int STAGE = (BN + BM) * kRowB;
+    static constexpr int WREG = BN * (NARROW ? 64 : kRowB);
+    static constexpr int STAGE = WREG + BM * kRowB;
     static_assert(PW >= 1 && PX >= 1 && BN * 4 % T == 0 && BM * 8 % T == 0, "whole loads");
 };
 
@@ -150,7 +177,12 @@ template <class C, int BITS>
 __device__ __forceinline__ void tile_lstore_piece(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r,
                                                   int q)
 {
-    if (q < C::PW) {
+    if (q < C::PW && C::NARROW_) {
+        // 16 bytes = units 2j and 2j + 1 of the row, stored as they are
+        const int i = tid + C::T * q, row = i >> 2, j = i & 3;
+        *reinterpret_cast<uint2*>(wl + swz_n(row, 2 * j)) = make_uint2(r.w[q].x, r.w[q].y);
+        *reinterpret_cast<uint2*>(wl + swz_n(row, 2 * j + 1)) = make_uint2(r.w[q].z, r.w[q].w);
+    } else if (q < C::PW) {
         const int i = tid + C::T * q, row = i >> 2, j = i & 3;
         uint4 lo, hi;
         if constexpr (BITS == 8) {
@@ -200,8 +232,12 @@ __device__ __forceinline__ void tile_compute(const uint8_t* wl, uint8_t* nl, int
         const int c = 2 * kk + half;
         uint4 a[C::IN], b[C::JM];
 #pragma unroll
-        for (int i = 0; i < C::IN; ++i)
-            a[i] = *reinterpret_cast<const uint4*>(wl + swz(wn * WN + 32 * i + rl, c));
+        for (int i = 0; i < C::IN; ++i) {
+            if constexpr (C::NARROW_)
+                a[i] = widen8<BITS>(*reinterpret_cast<const uint2*>(wl + swz_n(wn * WN + 32 * i + rl, c)));
+            else
+                a[i] = *reinterpret_cast<const uint4*>(wl + swz(wn * WN + 32 * i + rl, c));
+        }
 #pragma unroll
         for (int j = 0; j < C::JM; ++j)
             b[j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, c));
@@ -225,10 +261,10 @@ __device__ __forceinline__ void tile_compute(const uint8_t* wl, uint8_t* nl, int
     }
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH>
+template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH, bool NARROW>
 __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
 {
-    using C = TileCfg<BITS, WN, WM, NWN, NWM>;
+    using C = TileCfg<BITS, WN, WM, NWN, NWM, NARROW>;
     constexpr int BN = C::BN, BM = C::BM, BK = C::BK, IN = C::IN, JM = C::JM;
     constexpr int STAGE = C::STAGE;
     constexpr int R = BITS == 8 ? 2 : 4;  // rows per tile of the weight layout
@@ -325,12 +361,12 @@ __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
     }
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH = 2>
+template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH = 2, bool NARROW = false>
 hipError_t go_tile(TileGemmArgs p, hipStream_t st)
 {
-    using C = TileCfg<BITS, WN, WM, NWN, NWM>;
+    using C = TileCfg<BITS, WN, WM, NWN, NWM, NARROW>;
     const size_t lds = (size_t)2 * C::STAGE;
-    const void* kern = reinterpret_cast<const void*>(k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH>);
+    const void* kern = reinterpret_cast<const void*>(k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH, NARROW>);
     hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess)
         return e;
@@ -338,7 +374,7 @@ hipError_t go_tile(TileGemmArgs p, hipStream_t st)
     if (nbn * nbm > 0x7fffffff)
         return hipErrorInvalidValue;
     p.mblocks = (int)nbm;
-    hipLaunchKernelGGL((k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH>), dim3((unsigned)(nbn * nbm)), dim3(C::T),
+    hipLaunchKernelGGL((k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH, NARROW>), dim3((unsigned)(nbn * nbm)), dim3(C::T),
                        lds, st, p);
     return hipGetLastError();
 }
@@ -357,6 +393,8 @@ hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
     case 7: return go_tile<BITS, 64, 32, 2, 2, 4>(p, st); // variant 2, four stages in flight
     case 8: return go_tile<BITS, 32, 32, 2, 2, 4>(p, st); // variant 3, four stages in flight
     case 9: return go_tile<BITS, 64, 64, 2, 2, 4>(p, st); // variant 0, four stages in flight
+    case 10: return go_tile<BITS, 128, 64, 2, 4, 2, true>(p, st);  // 256 x 256, narrow weights
+    case 11: return go_tile<BITS, 64, 128, 4, 2, 2, true>(p, st);  // variant 6, narrow weights
     default: return hipErrorInvalidValue;
     }
 }
@@ -376,6 +414,8 @@ int tile_rows_m(int variant)
     case 7: return 64;
     case 8: return 64;
     case 9: return 128;
+    case 10: return 256;
+    case 11: return 256;
     default: return 0;
     }
 }
@@ -383,7 +423,7 @@ int tile_rows_m(int variant)
 int tile_rows_n(int variant)
 {
     switch (variant) {
-    case 4: case 5: case 6: return 256;
+    case 4: case 5: case 6: case 10: case 11: return 256;
     case 3: case 8: return 64;
     default: return 128;
     }

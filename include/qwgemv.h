@@ -297,7 +297,9 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
    rows of X, or of 64 by 64 (variant 3), or of eight waves per 256 by 128 (variant 4)
    or 256 by 256 (variant 6), or of four waves with 128 by 128 each (variant 5); variants
    7, 8 and 9 are 2, 3 and 0 with four stages of loads in flight instead of two; the
-   INT8 weights cast to f16 once per tile in on-chip memory.  Same arguments and
+   INT8 weights cast to f16 once per tile in on-chip memory, except in variants 10
+   (eight waves of 128 by 64 on a 256 by 256 tile) and 11 (variant 6), which keep them
+   as INT8 in on-chip memory and cast each operand after reading it.  Same arguments and
    limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another variant. */
 int qw_gemm_w8a16_tile(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int variant, void* stream);

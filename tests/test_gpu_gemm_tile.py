@@ -38,7 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9)
+VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)
 SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
           (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
 

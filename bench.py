@@ -214,11 +214,17 @@ def progress(msg):
     print("bench: " + msg, file=sys.stderr, flush=True)
 
 
+# Untimed replays before each timed measurement run for at least this long: after host
+# work the GPU clock is low, and the first milliseconds of a measurement otherwise run
+# slower (the first of several kernels timed in a row read up to 15% slow).
+WARM_S = 0.02
+
+
 def graph_us(torch, fn, n, reps=3):
-    """Per-launch microseconds of fn(0), ..., fn(n - 1) captured in one HIP graph: one
-    untimed replay, then the median of `reps` replays timed with HIP events on the
-    stream the graph runs on.  Callers pass n >= the number of rotated copies, so every
-    copy is read in each replay."""
+    """Per-launch microseconds of fn(0), ..., fn(n - 1) captured in one HIP graph:
+    untimed replays for at least WARM_S seconds, then the median of `reps` replays timed
+    with HIP events on the stream the graph runs on.  Callers pass n >= the number of
+    rotated copies, so every copy is read in each replay."""
     import statistics
 
     fn(0)
@@ -227,8 +233,12 @@ def graph_us(torch, fn, n, reps=3):
     with torch.cuda.graph(g):
         for i in range(n):
             fn(i)
-    g.replay()
-    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while True:
+        g.replay()
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= WARM_S:
+            break
     ts = []
     for _ in range(reps):
         e0 = torch.cuda.Event(enable_timing=True)
@@ -402,8 +412,12 @@ def chain_measurement(qw, wl, torch, replays):
     for key, fused in (("unfused", False), ("fused_qkv_gate_up", True)):
         c = chain.DecodeChain(layer, lm, xh, xi, layers=wl.LAYERS, fused=fused)
         g = c.capture()
-        g.replay()
-        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        while True:  # untimed replays, at least WARM_S seconds
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_S:
+                break
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -441,21 +455,9 @@ def index_softmax_measurement(qw, torch, launches):
     n = max(20, launches // 20)
     qw.index_softmax(A, ci, out=P)
     torch.cuda.synchronize()
-    gr = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gr):
-        for i in range(n):
-            qw.index_softmax(copies[i % R], ci, out=P)
-    gr.replay()
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    gr.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / n
+    us = graph_us(torch, lambda i: qw.index_softmax(copies[i % R], ci, out=P), n)
     b = rows * L * 5
-    del gr, copies, A, P
+    del copies, A, P
     torch.cuda.empty_cache()
     return {"rows": rows, "L": L, "c_int": ci, "us": round(us, 2), "algo_bytes": b,
             "GB/s": round(b / us / 1e3, 1), "frac_of_peak": round(b / us / 1e3 / PEAK_HBM_GBS, 4)}
@@ -641,8 +643,13 @@ def main():
         with torch.cuda.graph(g):
             for i in range(K_steps):
                 fn(i)
-        g.replay()  # first replay outside the timed region
-        torch.cuda.synchronize()
+        # untimed replays (at least WARM_S seconds) outside the timed region
+        t0 = time.perf_counter()
+        while True:
+            g.replay()
+            torch.cuda.synchronize()
+            if time.perf_counter() - t0 >= WARM_S:
+                break
         return g
 
     progress("headline step")

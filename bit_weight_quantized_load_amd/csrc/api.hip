@@ -414,34 +414,48 @@ int scratch_address(void** out)
     return QW_OK;
 }
 
-// Launch variant of the tiled matrix-core GEMM for M rows of X, or -1 where the other
-// kernels stay faster.  Measured on MI355X at K = 4096, N = 27392 (us, tile against the
-// kernel it replaces): W8A16 at 48 rows 36.7 / 44.2 and 64 rows 38.7 / 58.7 (64 x 64
-// tiles, four stages of loads in flight), 128 rows 48.0 / 112.9 (128 x 128, four
-// stages), 256 rows 78.7 / 192.8 (256 x 128), 512 rows 122.1 / 369.9 (256 x 256, INT8
-// weights in LDS; 128.7 with them cast to f16 when staged); from
-// 32 rows down the balanced kernels stay (30.5 against 37.7 at 32).  W4A8 at 128 rows
-// 32.4 / 34.5, 256 rows 47.4 / 54.1, 512 rows 74.4 / 89.1; below 113 rows the
-// many-block kernel stays (24.5 against 25.3 at 64, 30.0 against 33.3 at 96).  A tile
-// grid needs at least 128 tiles (half the compute units) to be used: the largest tile
-// of the row range that reaches it is taken, else the other kernels.
+// Launch variant of the tiled matrix-core GEMM for M rows of X and N rows of W, or -1
+// where the balanced matrix-core kernels stay (fewer rows than kTileMinM, or fewer than
+// kTileMinTiles tiles).  Each candidate's time is modelled as the tiles on the busiest
+// CU times the tile's work over the variant's efficiency, and the least is taken.  The
+// efficiencies are fitted to sweeps of M = 33 .. 512 on 4096 -> 27392, 3584 -> 18944 and
+// 18944 -> 3584 (the choice is within 0.5% of the best variant on average, 10% at
+// worst).  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64 (30.2 us), 128
+// rows 128 x 128 in two k-groups (42.6), 256 rows 256 x 128 (66.9), 512 rows 256 x 256
+// (113); W4A8 96 rows 128 x 128 (29.0), 256 rows 256 x 128 (42.0), 512 rows 256 x 256
+// (68.5, the activation pre-pass included).  Below 33 (W8A16) or 65 (W4A8) rows the
+// balanced kernels are as fast or faster (W4A8 at 64 rows: 22.0 against 22.4 us).
+constexpr int64_t kTileMinM8 = 33, kTileMinM4 = 65, kTileMinTiles = 96;
+
 int tile_variant(int bits, int64_t M, int64_t N)
 {
-    static const int v_lo[] = {8, -1}, v_mid[] = {9, 8, -1}, v_hi[] = {4, 9, 8, -1},
-                     v_top[] = {6, 4, 9, 8, -1}, v_top8[] = {11, 4, 9, 8, -1};
-    const int* cand;
-    if (bits == 8)
-        cand = M >= 385 ? v_top8 : M >= 193 ? v_hi : M >= 81 ? v_mid : M >= 33 ? v_lo : nullptr;
-    else
-        cand = M >= 385 ? v_top : M >= 193 ? v_hi : M >= 113 ? v_mid : nullptr;
-    if (cand == nullptr)
+    struct Cand {
+        int v;
+        double eff;
+    };
+    static const Cand c8[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {3, 0.8}, {4, 0.4}, {5, 0.5}, {6, 0.3}};
+    static const Cand c4[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {4, 0.5}, {6, 0.4}};
+    if (M < (bits == 8 ? kTileMinM8 : kTileMinM4))
         return -1;
-    for (; *cand >= 0; ++cand) {
-        const int bm = qw::tile_rows_m(*cand), bn = qw::tile_rows_n(*cand);
-        if ((N + bn - 1) / bn * ((M + bm - 1) / bm) >= 128)
-            return *cand;
+    const Cand* c = bits == 8 ? c8 : c4;
+    const int nc = bits == 8 ? (int)(sizeof(c8) / sizeof(c8[0])) : (int)(sizeof(c4) / sizeof(c4[0]));
+    const int64_t cus = std::max<int64_t>(1, device_cus());
+    double best = 0.0;
+    int pick = -1;
+    for (int i = 0; i < nc; ++i) {
+        const int64_t bm = qw::tile_rows_m(c[i].v), bn = qw::tile_rows_n(c[i].v);
+        if (bm <= 0 || bn <= 0)
+            continue;
+        const int64_t tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
+        if (tiles < kTileMinTiles)
+            continue;
+        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bn * bm) / c[i].eff;
+        if (pick < 0 || cost < best * 0.999) {
+            best = cost;
+            pick = c[i].v;
+        }
     }
-    return -1;
+    return pick;
 }
 
 // One device int per GPU for the packers' non-finite flag.  A packer call holds the
@@ -721,7 +735,7 @@ int run_w4_tile(const float* X, const void* Wq, const float* w_scale, int64_t M,
     int8_t* xq = static_cast<int8_t*>(workspace);
     float* a = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + codes);
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    hipError_t e = qw::launch_quant_act_rows(X, (int)M, (int)K, xq, a, st);
+    hipError_t e = qw::launch_quant_act_rows(X, (int)M, (int)K, xq, a, st, true);
     if (e != hipSuccess)
         return hip_status(e);
     return hip_status(qw::launch_gemm_w4a8_tile(xq, a, (int)M, (int)N, (int)K,

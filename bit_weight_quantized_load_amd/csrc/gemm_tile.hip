@@ -12,38 +12,24 @@
 // acc * weight scale * activation scale):
 //   Y[m][n] = ((float)acc * w_scale[n]) * a_scale[m], acc = sum_k q[n][k] xq[m][k] in
 //   int32 on v_mfma_i32_32x32x32_i8, with xq and a_scale computed by a pre-pass into
-//   the workspace (the codes of quant_act_i8).  An INT4 weight enters the multiply as
-//   16 q (its nibble moved to the top of an int8 lane), so the sum is exactly 16 acc and
-//   acc = sum >> 4; the outputs equal every other W4A8 path's bit for bit.
+//   the workspace (the codes of quant_act_i8, each 16-byte group in the INT4 unpack
+//   order).  An INT4 weight enters the multiply as 16 q (its nibble moved to the top of
+//   an int8 lane), so the sum is exactly 16 acc and acc = sum >> 4; the outputs equal
+//   every other W4A8 path's bit for bit.
 //
 // Work split.  A workgroup owns an output tile of BN rows of W (n) by BM rows of X (m)
-// and walks K in stages (64 k for W8A16, 128 k for W4A8: 128 bytes of operand per row).
-// Its NWN x NWM waves each own WN x WM of the tile, (WN / 32) x (WM / 32) blocks of
-// 32 x 32 accumulators.  Each stage, the workgroup's threads load the stage's weights
-// (16-byte loads from the tile layout, in which a row's k are contiguous) and its rows
-// of X, widen the weights (INT8 -> f16 by the exact byte-permute cast: bytes q ^ 0x80
-// under a 0x64 byte read as 1024 + q + 128, minus 1152; INT4 -> int8 lanes of 16 q)
-// and store both in LDS, so each weight is widened once per workgroup and multiplied
-// against all BM rows of X.  LDS holds two stages; the global loads run two stages
-// ahead (two register sets), so a stage's memory latency overlaps two stages of
-// multiplies.  Loads past K, N or M read zeros (buffer loads out of range), which
-// keeps the loop free of branches around the loads.
+// and walks K in stages (64 k for W8A16, 128 k for W4A8: 64 bytes of weights and 128
+// bytes of X per row).  Its NWN x NWM waves each own WN x WM of the tile, (WN / 32) x
+// (WM / 32) blocks of 32 x 32 accumulators; with KS > 1 there are KS such groups of
+// waves, each taking part of every stage's k.  Each weight byte is read from memory once
+// per grid row of X tiles and multiplied against BM rows of X from LDS.
 //
-// LDS layout: rows of 128 bytes (eight 16-byte chunks), chunk c of row r at position
-// c ^ ((r / 2) % 8).  The LDS serves 16 lanes of a 16-byte access per cycle across 64
-// banks (256 bytes, two rows): an operand read (rows r..r+15 at one chunk) and a staging
-// write (two rows, or four rows at four chunks) each land on 16 distinct 16-byte slots
-// of that width.  (With chunk c at c ^ (r % 8), rows r and r + 8 met in one bank: the
-// bank-conflict counter read 1.36 conflict cycles per LDS-active cycle.)
-//
-// W4A8 operand order: a 16-byte group of 16 k holds them in the order the INT4 unpack
-// produces (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15); the X codes are
-// permuted the same way when staged, and the int32 dot over the group is unchanged.
-//
-// Epilogue: the multiplies take X as the A operand and the weights as B, so each
-// accumulator register holds one row of Y across 32 consecutive output columns and the
-// stores of a half-wave are contiguous (with the operands the other way round each
-// store scattered over 32 rows, and HBM write traffic was 2-3x the output).
+// Multiplies: X is the A operand and the weights the B operand, so each accumulator
+// register holds one row of Y across 32 consecutive output columns and the stores of a
+// half-wave are contiguous (with the operands the other way round each store scattered
+// over 32 rows, and HBM write traffic was 2-3x the output).  The INT8 -> f16 cast is the
+// exact byte-permute one (bytes q ^ 0x80 under a 0x64 byte read as 1024 + q + 128, minus
+// 1152); the INT4 widening moves each nibble to the top of an int8 lane.
 //
 // Grid: one workgroup per tile, numbered so that the tiles of X that share a block of
 // weights are neighbours on one XCD (dispatched together, the repeated weight reads
@@ -62,8 +48,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
-constexpr int kRowB = 128;  // LDS bytes per row of a stage
-
 // int8 x 4 -> f16 x 4, exact.
 __device__ __forceinline__ uint2 cast4_f16(uint32_t wd)
 {
@@ -76,26 +60,16 @@ __device__ __forceinline__ uint2 cast4_f16(uint32_t wd)
     return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-// 16 int8 codes in k order -> the INT4 unpack order (even k of each 8, then odd k).
-__device__ __forceinline__ uint4 perm16(uint4 x)
-{
-    // bytes of (hi:lo) = (x.y:x.x): selector byte i picks byte i (0..3 of x.x, 4..7 of x.y)
-    return make_uint4(__builtin_amdgcn_perm(x.y, x.x, 0x06040200u),
-                      __builtin_amdgcn_perm(x.y, x.x, 0x07050301u),
-                      __builtin_amdgcn_perm(x.w, x.z, 0x06040200u),
-                      __builtin_amdgcn_perm(x.w, x.z, 0x07050301u));
-}
+// Rows of X in LDS: 128 bytes (eight 16-byte chunks), chunk c of row r at position
+// c ^ ((r / 2) % 8).  The LDS serves 16 lanes of a 16-byte access per cycle across 64
+// banks (256 bytes, two rows): an operand read (rows r..r+15 at one chunk) lands on 16
+// distinct 16-byte slots of that width.  (With chunk c at c ^ (r % 8), rows r and r + 8
+// met in one bank: the bank-conflict counter read 1.36 conflict cycles per LDS-active
+// cycle.)
+__device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
-__device__ __forceinline__ int swz(int r, int c) { return r * kRowB + 16 * (c ^ ((r >> 1) & 7)); }
-
-// Narrow weight rows: 64 bytes, eight 8-byte units, unit u of row r at position
-// u ^ ((r / 4) % 8).  An operand read (8 bytes per lane, rows r..r+31 at one unit) puts
-// the eight rows that share a quarter of the 64 banks (rows r + 4t) on eight distinct
-// positions.
-__device__ __forceinline__ int swz_n(int r, int u) { return r * 64 + 8 * (u ^ ((r >> 2) & 7)); }
-
-// 8 bytes of narrow weights (one MFMA operand per lane) -> the wide operand: 8 f16
-// (INT8) or 16 int8 lanes of 16 q in the unpack order (INT4).
+// 8 bytes of weights as stored (one MFMA operand per lane) -> the operand: 8 f16 (INT8)
+// or 16 int8 lanes of 16 q in the unpack order (INT4).
 template <int BITS>
 __device__ __forceinline__ uint4 widen8(uint2 w)
 {
@@ -120,208 +94,14 @@ __device__ __forceinline__ rsrc_t make_rsrc_u(const void* base, uint32_t bytes)
                      __builtin_amdgcn_readfirstlane(bytes));
 }
 
-// NARROW: the weights stay in LDS as stored in memory (INT8 or packed INT4, 64 bytes
-// per row per stage in both cases: 64 k of INT8, 128 k of INT4) and each wave widens
-// the operands it reads; otherwise they are widened once when staged (128 bytes per
-// row).  Narrow weights halve the weight bytes written to and read from LDS, the
-// bound of the many-row case, at the price of widening each operand in every wave
-// that reads it.
-template <int BITS, int WN, int WM, int NWN, int NWM, bool NARROW = false>
-struct TileCfg {
-    static constexpr int NWN_ = NWN, NWM_ = NWM;
-    static constexpr bool NARROW_ = NARROW;
-    static constexpr int T = 64 * NWN * NWM;
-    static constexpr int BN = WN * NWN, BM = WM * NWM;
-    static constexpr int BK = BITS == 8 ? 64 : 128;  // k per stage
-    static constexpr int IN = WN / 32, JM = WM / 32;
-    static constexpr int PW = BN * 4 / T;  // 16-byte weight loads per thread (64 B per row)
-    static constexpr int PX = BM * 8 / T;  // 16-byte X loads per thread (128 B per row)
-    static constexpr int WREG = BN * (NARROW ? 64 : kRowB);
-    static constexpr int STAGE = WREG + BM * kRowB;
-    static_assert(PW >= 1 && PX >= 1 && BN * 4 % T == 0 && BM * 8 % T == 0, "whole loads");
-};
-
-template <int PW, int PX>
-struct TileRegs {
-    uint4 w[PW], x[PX];
-};
-
-// Stage s of the workgroup's weights and rows of X into r; a stage past the last reads
-// zeros (offsets out of range).  The buffer resources are passed by value: they are
-// uniform, and the loads stay single scalar-addressed buffer loads.
-template <class C, int BITS>
-__device__ __forceinline__ void tile_gload(rsrc_t wr, rsrc_t xr, int s, int stages, int CG, int xrow,
-                                           int tid, TileRegs<C::PW, C::PX>& r)
+// Epilogue: lane (rl, half) of block (i, j) holds rows m = 8 g + 4 half + e of X's block
+// j (g, e = 0..3: register 4 g + e) and column n = rl of W's block i; the 32 lanes of a
+// half-wave store 32 consecutive n of one row.
+template <int BITS, int IN, int JM, int WN, int WM, class A>
+__device__ __forceinline__ void tile_epilogue(const TileGemmArgs& p, const A (&acc)[IN][JM], int n0, int m0,
+                                              int wn, int wm, int rl, int half)
 {
-    constexpr int R = BITS == 8 ? 2 : 4;  // rows per tile of the weight layout
-    const bool live = s < stages;
-    const int k0 = s * C::BK;
-#pragma unroll
-    for (int q = 0; q < C::PW; ++q) {
-        const int i = tid + C::T * q, row = i >> 2, j = i & 3;
-        const uint32_t off = (uint32_t)(((row / R) * CG + (k0 >> 9)) * 1024 + (row % R) * (1024 / R) +
-                                        (k0 & 511) * BITS / 8 + 16 * j);
-        r.w[q] = load16_stream(wr, live ? off : 0x80000000u);
-    }
-#pragma unroll
-    for (int q = 0; q < C::PX; ++q) {
-        const int i = tid + C::T * q, row = i >> 3, c = i & 7;
-        const uint32_t off = (uint32_t)row * (uint32_t)xrow + (uint32_t)(k0 * (BITS == 8 ? 2 : 1) + 16 * c);
-        r.x[q] = load16(xr, live ? off : 0x80000000u);
-    }
-}
-
-// Widens piece q (q < PW: 16 bytes of weights; else 16 bytes of X) of register set r
-// and stores it in LDS buffer wl.
-template <class C, int BITS>
-__device__ __forceinline__ void tile_lstore_piece(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r,
-                                                  int q)
-{
-    if (q < C::PW && C::NARROW_) {
-        // 16 bytes = units 2j and 2j + 1 of the row, stored as they are
-        const int i = tid + C::T * q, row = i >> 2, j = i & 3;
-        *reinterpret_cast<uint2*>(wl + swz_n(row, 2 * j)) = make_uint2(r.w[q].x, r.w[q].y);
-        *reinterpret_cast<uint2*>(wl + swz_n(row, 2 * j + 1)) = make_uint2(r.w[q].z, r.w[q].w);
-    } else if (q < C::PW) {
-        const int i = tid + C::T * q, row = i >> 2, j = i & 3;
-        uint4 lo, hi;
-        if constexpr (BITS == 8) {
-            const uint2 a = cast4_f16(r.w[q].x), b = cast4_f16(r.w[q].y);
-            const uint2 c = cast4_f16(r.w[q].z), d = cast4_f16(r.w[q].w);
-            lo = make_uint4(a.x, a.y, b.x, b.y);
-            hi = make_uint4(c.x, c.y, d.x, d.y);
-        } else {
-            // 32 nibbles (k 32j .. 32j + 31) -> 32 int8 lanes of 16 q, unpack order
-            const uint32_t wd[4] = {r.w[q].x, r.w[q].y, r.w[q].z, r.w[q].w};
-            lo = make_uint4((wd[0] << 4) & 0xF0F0F0F0u, wd[0] & 0xF0F0F0F0u,
-                            (wd[1] << 4) & 0xF0F0F0F0u, wd[1] & 0xF0F0F0F0u);
-            hi = make_uint4((wd[2] << 4) & 0xF0F0F0F0u, wd[2] & 0xF0F0F0F0u,
-                            (wd[3] << 4) & 0xF0F0F0F0u, wd[3] & 0xF0F0F0F0u);
-        }
-        *reinterpret_cast<uint4*>(wl + swz(row, 2 * j)) = lo;
-        *reinterpret_cast<uint4*>(wl + swz(row, 2 * j + 1)) = hi;
-    } else {
-        const int qx = q - C::PW;
-        const int i = tid + C::T * qx, row = i >> 3, c = i & 7;
-        *reinterpret_cast<uint4*>(wl + C::WREG + swz(row, c)) = BITS == 8 ? r.x[qx] : perm16(r.x[qx]);
-    }
-}
-
-template <class C, int BITS>
-__device__ __forceinline__ void tile_lstore(uint8_t* wl, int tid, const TileRegs<C::PW, C::PX>& r)
-{
-#pragma unroll
-    for (int q = 0; q < C::PW + C::PX; ++q)
-        tile_lstore_piece<C, BITS>(wl, tid, r, q);
-}
-
-// The multiplies of one stage from LDS buffer wl; the staging of the next stage into
-// buffer nl (from register set r) is spread over the four 16/32-k steps, after each
-// step's multiplies are issued: the MFMAs run asynchronously, so the cast and the LDS
-// stores issue while they execute instead of after them.
-template <class C, int BITS, class A>
-__device__ __forceinline__ void tile_compute(const uint8_t* wl, uint8_t* nl, int tid, int wn, int wm,
-                                             int rl, int half, const TileRegs<C::PW, C::PX>& r,
-                                             A (&acc)[C::IN][C::JM])
-{
-    const uint8_t* xl = wl + C::WREG;
-    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
-    constexpr int NP = C::PW + C::PX;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        const int c = 2 * kk + half;
-        uint4 a[C::IN], b[C::JM];
-#pragma unroll
-        for (int i = 0; i < C::IN; ++i) {
-            if constexpr (C::NARROW_)
-                a[i] = widen8<BITS>(*reinterpret_cast<const uint2*>(wl + swz_n(wn * WN + 32 * i + rl, c)));
-            else
-                a[i] = *reinterpret_cast<const uint4*>(wl + swz(wn * WN + 32 * i + rl, c));
-        }
-#pragma unroll
-        for (int j = 0; j < C::JM; ++j)
-            b[j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, c));
-#pragma unroll
-        for (int i = 0; i < C::IN; ++i)
-#pragma unroll
-            for (int j = 0; j < C::JM; ++j) {
-                // X is the A operand and the weights the B operand, so the result is Y
-                // itself (rows m, columns n) and a store instruction covers 32
-                // consecutive n of one row
-                if constexpr (BITS == 8)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        __builtin_bit_cast(v8h, b[j]), __builtin_bit_cast(v8h, a[i]), acc[i][j], 0, 0, 0);
-                else
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                        __builtin_bit_cast(v4i, b[j]), __builtin_bit_cast(v4i, a[i]), acc[i][j], 0, 0, 0);
-            }
-#pragma unroll
-        for (int q = kk * NP / 4; q < (kk + 1) * NP / 4; ++q)
-            tile_lstore_piece<C, BITS>(nl, tid, r, q);
-    }
-}
-
-template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH, bool NARROW>
-__global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
-{
-    using C = TileCfg<BITS, WN, WM, NWN, NWM, NARROW>;
-    constexpr int BN = C::BN, BM = C::BM, BK = C::BK, IN = C::IN, JM = C::JM;
-    constexpr int STAGE = C::STAGE;
-    constexpr int R = BITS == 8 ? 2 : 4;  // rows per tile of the weight layout
-    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wn = wave % NWN, wm = wave / NWN;
-    const int L = xcd_block(blockIdx.x, gridDim.x);
-    const int nb = L / p.mblocks, mb = L - nb * p.mblocks;
-    const int n0 = nb * BN, m0 = mb * BM;
-    const int M = p.M, N = p.N, K = p.K, CG = p.cg;
-    const int stages = (K + BK - 1) / BK;
-    const int xrow = BITS == 8 ? K * 2 : K;  // bytes per row of X
-
-    const int rg0 = n0 / R;
-    const rsrc_t wr = make_rsrc_u(p.Wq + (size_t)rg0 * CG * 1024u,
-                                (uint32_t)max(0, min(BN / R, p.nrg - rg0)) * (uint32_t)CG * 1024u);
-    const rsrc_t xr = make_rsrc_u(static_cast<const uint8_t*>(p.X) + (size_t)m0 * xrow,
-                                (uint32_t)max(0, min(BM, M - m0)) * (uint32_t)xrow);
-    using Regs = TileRegs<C::PW, C::PX>;
-
-    typedef typename std::conditional<BITS == 8, v16f, v16i>::type acc_t;
-    acc_t acc[IN][JM];
-#pragma unroll
-    for (int i = 0; i < IN; ++i)
-#pragma unroll
-        for (int j = 0; j < JM; ++j)
-#pragma unroll
-            for (int v = 0; v < 16; ++v)
-                acc[i][j][v] = 0;
-
-    const int rl = lane & 31, half = lane >> 5;
-    // DEPTH register sets: at stage t, set t % DEPTH (stored to LDS during stage t - 1)
-    // takes the loads of stage t + DEPTH, and set (t + 1) % DEPTH, loaded DEPTH - 1 stages
-    // earlier, is staged into the other LDS buffer while stage t is multiplied.  The loop
-    // is unrolled DEPTH times so that buffers and register sets are static; stages past
-    // the last read zeros and add nothing.
-    Regs r[DEPTH];
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d)
-        tile_gload<C, BITS>(wr, xr, d, stages, CG, xrow, tid, r[d]);
-    tile_lstore<C, BITS>(lds, tid, r[0]);
-    for (int s = 0; s < stages; s += DEPTH) {
-#pragma unroll
-        for (int d = 0; d < DEPTH; ++d) {
-            __syncthreads();  // stage s + d in buffer d % 2; every wave is done with the other
-            tile_gload<C, BITS>(wr, xr, s + d + DEPTH, stages, CG, xrow, tid, r[d]);
-            __builtin_amdgcn_sched_barrier(0);
-            tile_compute<C, BITS>(lds + (d & 1) * STAGE, lds + ((d + 1) & 1) * STAGE, tid, wn, wm, rl,
-                                  half, r[(d + 1) % DEPTH], acc);
-        }
-    }
-
-    // Epilogue: lane (rl, half) of block (i, j) holds rows m = 8 g + 4 half + e of X's
-    // block j (g, e = 0..3: register 4 g + e) and column n = rl of W's block i; the 32
-    // lanes of a half-wave store 32 consecutive n of one row.
+    const int M = p.M, N = p.N;
     const rsrc_t sr = make_rsrc_u(p.w_scale, (uint32_t)N * (BITS == 8 ? 2u : 4u));
     const rsrc_t ar = make_rsrc_u(p.a_scale, BITS == 4 ? (uint32_t)M * 4u : 0u);
 #pragma unroll
@@ -361,40 +141,357 @@ __global__ __launch_bounds__(64 * NWN * NWM, 1) void k_gemm_tile(TileGemmArgs p)
     }
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM, int DEPTH = 2, bool NARROW = false>
-hipError_t go_tile(TileGemmArgs p, hipStream_t st)
+// Staging.  The stage's weights and rows of X go from memory straight into LDS (buffer
+// loads with the LDS destination: no registers, no VALU, no LDS store instructions),
+// NBUF stages in flight.  The weights stay in LDS as stored in memory (64 bytes per row
+// per stage, INT8 or packed INT4) and each wave widens the operands it reads; for W4A8
+// the activation codes arrive already in the unpack order.
+//
+// A load instruction of one wave writes 1 KB of LDS, lane l's 16 bytes at l * 16, so the
+// swizzle is applied on the memory side: the lane that fills LDS slot s loads the chunk
+// that belongs there.  Weight rows: 64 bytes = four 16-byte chunks, chunk c of row r at
+// position c ^ ((r / 4) % 4); an operand read (16 lanes, rows r..r+15 at one chunk)
+// covers the 64 banks once.  Rows of X as above.
+//
+// k assignment within a stage: lane half h reads weight chunks 2 h and 2 h + 1 of its row
+// (one 16-byte read each, two multiplies' operands); at step kk it multiplies chunk
+// 2 h + kk / 2, half kk % 2, against X chunk 4 h + kk.  Both operands of every multiply
+// then hold the same k (W8A16: k 32 h + 8 kk .. + 7; W4A8: 64 h + 16 kk .. + 15), and each
+// k of the stage is taken once.
+//
+// Pipeline, stage t in buffer t % NBUF: wait until this wave's loads of stage t have
+// landed (at most (NBUF - 2) stages of loads still in flight), barrier (every wave's
+// loads of stage t are in LDS, and every wave is done with buffer (t - 1) % NBUF), issue
+// the loads of stage t + NBUF - 1 into buffer (t - 1) % NBUF, multiply stage t.  Loads of
+// stages past the last are issued out of range (zeros) so that the count in flight is the
+// same at every stage.  Loads past K, N or M read zeros (buffer loads out of range), which
+// keeps the loop free of branches around the loads.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// KS > 1 splits each stage's k over KS groups of NWN x NWM waves (group g takes the
+// multiplies of steps kk = 4 g / KS .. 4 (g + 1) / KS - 1 of every stage, on its own
+// accumulators), so that a small tile still has several waves per SIMD to overlap one
+// wave's LDS latency and operand widening with another's multiplies.  The groups' sums
+// meet in LDS at the end (int32: exact; fp32: added in group order).
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS>
+struct DmaCfg {
+    static constexpr int NWN_ = NWN, NWM_ = NWM, KS_ = KS;
+    static constexpr int NWG = NWN * NWM;  // waves of one k-group
+    static constexpr int NWAVES = NWG * KS, T = 64 * NWAVES;
+    static constexpr int BN = WN * NWN, BM = WM * NWM;
+    static constexpr int BK = BITS == 8 ? 64 : 128;  // k per stage
+    static constexpr int SPT = 512 / BK;             // stages per 512-k tile of the weight layout
+    static constexpr int IN = WN / 32, JM = WM / 32;
+    // waves that issue the stage loads: all of them where the stage divides evenly
+    static constexpr int LW = (BN * 4 % T == 0 && BM * 8 % T == 0) ? NWAVES
+                            : (BN * 4 % (T / 2) == 0 && BM * 8 % (T / 2) == 0) ? NWAVES / 2 : NWG;
+    static constexpr int PW = BN * 4 / (64 * LW);  // 16-byte weight loads per loading thread
+    static constexpr int PX = BM * 8 / (64 * LW);  // 16-byte X loads per loading thread
+    static constexpr int WREG = BN * 64;
+    static constexpr int STAGE = WREG + BM * 128;
+    static constexpr int VM = (NBUF - 2) * (PW + PX);  // loads left in flight at a barrier
+    // the k-group sums meet in the stage buffers: 4 KB blocks (one 32 x 32 accumulator of
+    // one wave), BPB of them per buffer
+    static constexpr int BPB = STAGE / 4096;
+    static_assert(PW >= 1 && PX >= 1 && BN * 4 % (64 * LW) == 0 && BM * 8 % (64 * LW) == 0, "whole loads");
+    static_assert(NBUF >= 2 && NBUF <= 8 && VM <= 63, "wait count");
+    static_assert(NBUF * STAGE + 16 * 1024 <= 160 * 1024, "LDS");
+    static_assert(KS == 1 || KS == 2 || KS == 4, "k split");
+    static_assert(KS == 1 || (BPB >= 1 && (NWG * IN * JM + BPB - 1) / BPB <= NBUF), "room for one group's sums");
+};
+
+__device__ __forceinline__ int swz_w(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+
+// The bits of an accumulator element, taken by value (a bit cast applied to an element
+// of a vector-typed value in place reads element 0 with this compiler).
+template <class T>
+__device__ __forceinline__ uint32_t u32_of(T x)
 {
-    using C = TileCfg<BITS, WN, WM, NWN, NWM, NARROW>;
-    const size_t lds = (size_t)2 * C::STAGE;
-    const void* kern = reinterpret_cast<const void*>(k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH, NARROW>);
-    hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess)
-        return e;
+    return __builtin_bit_cast(uint32_t, x);
+}
+
+template <class C, int BITS>
+__device__ __forceinline__ void dma_stage(uint8_t* buf, rsrc_t wr, rsrc_t xr, const uint32_t (&vw)[C::PW],
+                                          const uint32_t (&vx)[C::PX], int t, int stages, int wave)
+{
+    if (C::LW < C::NWAVES && wave >= C::LW)
+        return;
+    const bool live = t < stages;
+    const uint32_t kw = (uint32_t)(t / C::SPT) * 1024u + (uint32_t)(t % C::SPT) * 64u;
+    const uint32_t kx = (uint32_t)t * 128u;
+#pragma unroll
+    for (int q = 0; q < C::PW; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(buf + 1024 * (wave + C::LW * q)), 16,
+                                                 live ? vw[q] + kw : 0x80000000u, 0, 0, 0);
+#pragma unroll
+    for (int q = 0; q < C::PX; ++q)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_ptr_t)(buf + C::WREG + 1024 * (wave + C::LW * q)),
+                                                 16, live ? vx[q] + kx : 0x80000000u, 0, 0, 0);
+}
+
+template <int BITS, class A>
+__device__ __forceinline__ void mfma_tile(A& acc, uint4 x, uint4 w)
+{
+    if constexpr (BITS == 8)
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, x), __builtin_bit_cast(v8h, w), acc, 0, 0, 0);
+    else
+        acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, x), __builtin_bit_cast(v4i, w), acc, 0, 0, 0);
+}
+
+// The multiplies of one stage from LDS buffer buf (one k-group): the operands of step
+// kk + 1 are read before the multiplies of step kk are issued, so their LDS latency
+// overlaps those multiplies.
+template <class C, int BITS, class A>
+__device__ __forceinline__ void dma_compute1(const uint8_t* buf, int wn, int wm, int rl, int h,
+                                             A (&acc)[C::IN][C::JM])
+{
+    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
+    const uint8_t* xl = buf + C::WREG;
+    uint4 w[2][C::IN], b[2][C::JM];
+#pragma unroll
+    for (int i = 0; i < C::IN; ++i)
+        w[0][i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h));
+#pragma unroll
+    for (int j = 0; j < C::JM; ++j)
+        b[0][j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h));
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+        if (kk < 3) {
+            if (kk == 1) {
+#pragma unroll
+                for (int i = 0; i < C::IN; ++i)
+                    w[1][i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h + 1));
+            }
+#pragma unroll
+            for (int j = 0; j < C::JM; ++j)
+                b[(kk + 1) & 1][j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h + kk + 1));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's multiplies
+#pragma unroll
+        for (int i = 0; i < C::IN; ++i) {
+            const uint4 wv = w[kk >> 1][i];
+            const uint4 a = widen8<BITS>((kk & 1) == 0 ? make_uint2(wv.x, wv.y) : make_uint2(wv.z, wv.w));
+#pragma unroll
+            for (int j = 0; j < C::JM; ++j)
+                mfma_tile<BITS>(acc[i][j], b[kk & 1][j], a);
+        }
+    }
+}
+
+// The multiplies of k-group kg of one stage from LDS buffer buf.
+template <class C, int BITS, class A>
+__device__ __forceinline__ void dma_compute(const uint8_t* buf, int wn, int wm, int kg, int rl, int h,
+                                            A (&acc)[C::IN][C::JM])
+{
+    if constexpr (C::KS_ == 1) {
+        dma_compute1<C, BITS>(buf, wn, wm, rl, h, acc);
+        return;
+    }
+    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
+    constexpr int NKP = C::KS_ == 4 ? 1 : 2 / C::KS_;  // 32-k pairs of steps of the group
+    const uint8_t* xl = buf + C::WREG;
+#pragma unroll
+    for (int p = 0; p < NKP; ++p) {
+        const int kp = C::KS_ == 1 ? p : C::KS_ == 2 ? kg : kg >> 1;
+        uint4 w[C::IN];
+#pragma unroll
+        for (int i = 0; i < C::IN; ++i)
+            w[i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h + kp));
+#pragma unroll
+        for (int e0 = 0; e0 < (C::KS_ == 4 ? 1 : 2); ++e0) {
+            const int e = C::KS_ == 4 ? (kg & 1) : e0;
+            const int kk = 2 * kp + e;
+            uint4 b[C::JM];
+#pragma unroll
+            for (int j = 0; j < C::JM; ++j)
+                b[j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h + kk));
+#pragma unroll
+            for (int i = 0; i < C::IN; ++i) {
+                const uint4 a = widen8<BITS>(e == 0 ? make_uint2(w[i].x, w[i].y) : make_uint2(w[i].z, w[i].w));
+#pragma unroll
+                for (int j = 0; j < C::JM; ++j) {
+                    if constexpr (BITS == 8)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            __builtin_bit_cast(v8h, b[j]), __builtin_bit_cast(v8h, a), acc[i][j], 0, 0, 0);
+                    else
+                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+                            __builtin_bit_cast(v4i, b[j]), __builtin_bit_cast(v4i, a), acc[i][j], 0, 0, 0);
+                }
+            }
+        }
+    }
+}
+
+// Wait for this wave's loads of the current stage, then the workgroup barrier.  The
+// compiler barriers keep LDS accesses on their side of it (the barrier instruction
+// itself is not a memory operation to the compiler).
+template <int VM>
+__device__ __forceinline__ void dma_barrier()
+{
+    // s_waitcnt vmcnt(VM) lgkmcnt(0): vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7
+    __builtin_amdgcn_s_waitcnt((VM & 15) | (7 << 4) | ((VM >> 4) << 14));
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS>
+__global__ __launch_bounds__(64 * NWN * NWM * KS) void k_gemm_dma(TileGemmArgs p)
+{
+    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS>;
+    constexpr int BN = C::BN, BM = C::BM, BK = C::BK, IN = C::IN, JM = C::JM;
+    constexpr int R = BITS == 8 ? 2 : 4;  // rows per tile of the weight layout
+    // one array per buffer: the compiler then knows which buffer a DMA writes and which
+    // one an LDS read reads, and does not wait for the later stages' loads before reads
+    __shared__ __attribute__((aligned(1024))) uint8_t lds0[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds1[C::STAGE];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds2[NBUF > 2 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds3[NBUF > 3 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds4[NBUF > 4 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds5[NBUF > 5 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds6[NBUF > 6 ? C::STAGE : 16];
+    __shared__ __attribute__((aligned(1024))) uint8_t lds7[NBUF > 7 ? C::STAGE : 16];
+    auto bufs = [&](int b) -> uint8_t* {
+        return b == 0 ? lds0 : b == 1 ? lds1 : b == 2 ? lds2 : b == 3 ? lds3 : b == 4 ? lds4 : b == 5 ? lds5
+             : b == 6 ? lds6 : lds7;
+    };
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wg = wave % C::NWG, kg = wave / C::NWG;  // position in the tile, k-group
+    const int wn = wg % NWN, wm = wg / NWN;
+    const int L = xcd_block(blockIdx.x, gridDim.x);
+    const int nb = L / p.mblocks, mb = L - nb * p.mblocks;
+    const int n0 = nb * BN, m0 = mb * BM;
+    const int M = p.M, K = p.K, CG = p.cg;
+    const int stages = (K + BK - 1) / BK;
+    const int xrow = BITS == 8 ? K * 2 : K;  // bytes per row of X
+
+    const int rg0 = n0 / R;
+    const rsrc_t wr = make_rsrc_u(p.Wq + (size_t)rg0 * CG * 1024u,
+                                (uint32_t)max(0, min(BN / R, p.nrg - rg0)) * (uint32_t)CG * 1024u);
+    const rsrc_t xr = make_rsrc_u(static_cast<const uint8_t*>(p.X) + (size_t)m0 * xrow,
+                                (uint32_t)max(0, min(BM, M - m0)) * (uint32_t)xrow);
+
+    // per-lane load offsets at stage 0: LDS slot i of a region holds the chunk that the
+    // swizzle puts there
+    uint32_t vw[C::PW], vx[C::PX];
+#pragma unroll
+    for (int q = 0; q < C::PW; ++q) {
+        const int i = tid + 64 * C::LW * q, r = i >> 2, c = (i & 3) ^ ((r >> 2) & 3);
+        vw[q] = (uint32_t)(((r / R) * CG) * 1024 + (r % R) * (1024 / R) + 16 * c);
+    }
+#pragma unroll
+    for (int q = 0; q < C::PX; ++q) {
+        const int i = tid + 64 * C::LW * q, r = i >> 3, c = (i & 7) ^ ((r >> 1) & 7);
+        vx[q] = (uint32_t)r * (uint32_t)xrow + 16u * (uint32_t)c;
+    }
+
+    typedef typename std::conditional<BITS == 8, v16f, v16i>::type acc_t;
+    acc_t acc[IN][JM];
+#pragma unroll
+    for (int i = 0; i < IN; ++i)
+#pragma unroll
+        for (int j = 0; j < JM; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[i][j][v] = 0;
+
+    const int rl = lane & 31, h = lane >> 5;
+#pragma unroll
+    for (int d = 0; d < NBUF - 1; ++d)
+        dma_stage<C, BITS>(bufs(d), wr, xr, vw, vx, d, stages, wave);
+    for (int s = 0; s < stages; s += NBUF) {
+#pragma unroll
+        for (int d = 0; d < NBUF; ++d) {
+            dma_barrier<C::VM>();
+            dma_stage<C, BITS>(bufs((d + NBUF - 1) % NBUF), wr, xr, vw, vx, s + d + NBUF - 1, stages, wave);
+            __builtin_amdgcn_sched_barrier(0);  // the loads go out before the multiplies
+            dma_compute<C, BITS>(bufs(d), wn, wm, kg, rl, h, acc);
+        }
+    }
+    // the loads of the stages past the last (zeros) may still be in flight
+    __builtin_amdgcn_s_waitcnt(0 | (7 << 4) | (15 << 8));
+
+    if constexpr (KS > 1) {
+        // k-groups KS - 1 .. 1 hand their sums to group 0 through LDS (the stage
+        // buffers, free once every wave is past its last multiply), one group at a time;
+        // block (wave wg, i, j) sits in buffer blk / BPB at 4 KB x (blk % BPB), register
+        // v of lane l at (v / 4) * 1 KB + 16 l + 4 (v % 4)
+#pragma unroll
+        for (int g = KS - 1; g >= 1; --g) {
+            dma_barrier<0>();
+#pragma unroll
+            for (int i = 0; i < IN; ++i)
+#pragma unroll
+                for (int j = 0; j < JM; ++j) {
+                    const int blk = (wg * IN + i) * JM + j;
+                    uint8_t* red = bufs(blk / C::BPB) + 4096 * (blk % C::BPB) + 16 * lane;
+                    if (kg == g) {
+#pragma unroll
+                        for (int v = 0; v < 16; v += 4)
+                            *reinterpret_cast<uint4*>(red + 256 * v) =
+                                make_uint4(u32_of(acc[i][j][v]), u32_of(acc[i][j][v + 1]), u32_of(acc[i][j][v + 2]),
+                                           u32_of(acc[i][j][v + 3]));
+                    }
+                }
+            dma_barrier<0>();
+#pragma unroll
+            for (int i = 0; i < IN; ++i)
+#pragma unroll
+                for (int j = 0; j < JM; ++j) {
+                    const int blk = (wg * IN + i) * JM + j;
+                    const uint8_t* red = bufs(blk / C::BPB) + 4096 * (blk % C::BPB) + 16 * lane;
+                    if (kg == 0) {
+#pragma unroll
+                        for (int v = 0; v < 16; v += 4) {
+                            const uint4 o = *reinterpret_cast<const uint4*>(red + 256 * v);
+                            const uint32_t ov[4] = {o.x, o.y, o.z, o.w};
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                if constexpr (BITS == 8)
+                                    acc[i][j][v + e] += __builtin_bit_cast(float, ov[e]);
+                                else
+                                    acc[i][j][v + e] += (int)ov[e];
+                            }
+                        }
+                    }
+                }
+        }
+        if (kg != 0)
+            return;
+    }
+
+    tile_epilogue<BITS, IN, JM, BN / NWN, BM / NWM>(p, acc, n0, m0, wn, wm, rl, h);
+}
+
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS = 1>
+hipError_t go_dma(TileGemmArgs p, hipStream_t st)
+{
+    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS>;
     const int64_t nbn = ((int64_t)p.N + C::BN - 1) / C::BN, nbm = ((int64_t)p.M + C::BM - 1) / C::BM;
     if (nbn * nbm > 0x7fffffff)
         return hipErrorInvalidValue;
     p.mblocks = (int)nbm;
-    hipLaunchKernelGGL((k_gemm_tile<BITS, WN, WM, NWN, NWM, DEPTH, NARROW>), dim3((unsigned)(nbn * nbm)), dim3(C::T),
-                       lds, st, p);
+    hipLaunchKernelGGL((k_gemm_dma<BITS, WN, WM, NWN, NWM, NBUF, KS>), dim3((unsigned)(nbn * nbm)), dim3(C::T), 0,
+                       st, p);
     return hipGetLastError();
 }
 
+// Launch variants: tile (BN x BM), waves, stages in flight, k split.  The LDS footprint
+// decides how many workgroups share a CU (variants 0, 1: one; 2 to 5: two; 6: three).
 template <int BITS>
 hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
 {
     switch (variant) {
-    case 0: return go_tile<BITS, 64, 64, 2, 2>(p, st);   // 128 n x 128 m, 4 waves
-    case 1: return go_tile<BITS, 64, 128, 2, 2>(p, st);  // 128 n x 256 m, 4 waves
-    case 2: return go_tile<BITS, 64, 32, 2, 2>(p, st);   // 128 n x 64 m, 4 waves
-    case 3: return go_tile<BITS, 32, 32, 2, 2>(p, st);   // 64 n x 64 m, 4 waves
-    case 4: return go_tile<BITS, 64, 64, 4, 2>(p, st);   // 256 n x 128 m, 8 waves
-    case 5: return go_tile<BITS, 128, 128, 2, 2>(p, st); // 256 n x 256 m, 4 waves
-    case 6: return go_tile<BITS, 64, 128, 4, 2>(p, st);  // 256 n x 256 m, 8 waves
-    case 7: return go_tile<BITS, 64, 32, 2, 2, 4>(p, st); // variant 2, four stages in flight
-    case 8: return go_tile<BITS, 32, 32, 2, 2, 4>(p, st); // variant 3, four stages in flight
-    case 9: return go_tile<BITS, 64, 64, 2, 2, 4>(p, st); // variant 0, four stages in flight
-    case 10: return go_tile<BITS, 128, 64, 2, 4, 2, true>(p, st);  // 256 x 256, narrow weights
-    case 11: return go_tile<BITS, 64, 128, 4, 2, 2, true>(p, st);  // variant 6, narrow weights
+    case 0: return go_dma<BITS, 64, 128, 4, 2, 3>(p, st);    // 256 n x 256 m, 8 waves
+    case 1: return go_dma<BITS, 64, 64, 4, 2, 4>(p, st);     // 256 n x 128 m, 8 waves
+    case 2: return go_dma<BITS, 64, 64, 2, 2, 3>(p, st);     // 128 n x 128 m, 4 waves
+    case 3: return go_dma<BITS, 64, 64, 2, 2, 3, 2>(p, st);  // 128 n x 128 m, 2 k-groups of 4 waves
+    case 4: return go_dma<BITS, 64, 32, 2, 2, 4>(p, st);     // 128 n x 64 m, 4 waves
+    case 5: return go_dma<BITS, 64, 32, 2, 2, 4, 2>(p, st);  // 128 n x 64 m, 2 k-groups of 4 waves
+    case 6: return go_dma<BITS, 32, 32, 2, 2, 4>(p, st);     // 64 n x 64 m, 4 waves
     default: return hipErrorInvalidValue;
     }
 }
@@ -404,18 +501,9 @@ hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
 int tile_rows_m(int variant)
 {
     switch (variant) {
-    case 0: return 128;
-    case 1: return 256;
-    case 2: return 64;
-    case 3: return 64;
-    case 4: return 128;
-    case 5: return 256;
-    case 6: return 256;
-    case 7: return 64;
-    case 8: return 64;
-    case 9: return 128;
-    case 10: return 256;
-    case 11: return 256;
+    case 0: return 256;
+    case 1: case 2: case 3: return 128;
+    case 4: case 5: case 6: return 64;
     default: return 0;
     }
 }
@@ -423,9 +511,10 @@ int tile_rows_m(int variant)
 int tile_rows_n(int variant)
 {
     switch (variant) {
-    case 4: case 5: case 6: case 10: case 11: return 256;
-    case 3: case 8: return 64;
-    default: return 128;
+    case 0: case 1: return 256;
+    case 2: case 3: case 4: case 5: return 128;
+    case 6: return 64;
+    default: return 0;
     }
 }
 

@@ -864,14 +864,18 @@ hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, 
 
 namespace {
 
-// Activation quantization for the long-K kernel: one workgroup of 1024 threads per row
-// of X, which loads the whole row into registers at once (NV float4 per thread, so a
-// single memory round trip), takes max|x| across the workgroup and writes the row-major
-// codes from the same registers.  The scale and the codes are computed exactly as by
-// the standalone quantization kernel.
+// Activation quantization for the long-K kernel and the tiled GEMM: one workgroup of
+// 1024 threads per row of X, which loads the whole row into registers at once (NV float4
+// per thread, so a single memory round trip), takes max|x| across the workgroup and
+// writes the row-major codes from the same registers.  The scale and the codes are
+// computed exactly as by the standalone quantization kernel.  With UNPACK, each 16-byte
+// group of codes (16 k) is written in the order the INT4 unpack presents the weights
+// (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15): the lane holding k 4j .. 4j + 3
+// of a group and its neighbour exchange their words, the even lane keeps the even k of
+// both and the odd lane the odd k, and each writes the word at its own position.
 constexpr int kQrThreads = 1024;
 
-template <int NV>
+template <int NV, bool UNPACK>
 __global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __restrict__ X, int K,
                                                                int8_t* __restrict__ Xq,
                                                                float* __restrict__ a_scale)
@@ -906,13 +910,20 @@ __global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __re
 #pragma unroll
     for (int t = 0; t < NV; ++t) {
         const int i = tid + kQrThreads * t;
-        if (i < K4) {
-            const float4 x = v[t];
-            out[i] = fast ? pack_i8x4(quant_code_fast(x.x, a, r, 127.f), quant_code_fast(x.y, a, r, 127.f),
-                                      quant_code_fast(x.z, a, r, 127.f), quant_code_fast(x.w, a, r, 127.f))
-                          : pack_i8x4(quant_code(x.x, a, 127.f), quant_code(x.y, a, 127.f),
-                                      quant_code(x.z, a, 127.f), quant_code(x.w, a, 127.f));
+        const float4 x = v[t];
+        uint32_t wd = fast ? pack_i8x4(quant_code_fast(x.x, a, r, 127.f), quant_code_fast(x.y, a, r, 127.f),
+                                       quant_code_fast(x.z, a, r, 127.f), quant_code_fast(x.w, a, r, 127.f))
+                           : pack_i8x4(quant_code(x.x, a, 127.f), quant_code(x.y, a, 127.f),
+                                       quant_code(x.z, a, 127.f), quant_code(x.w, a, 127.f));
+        if constexpr (UNPACK) {
+            // the neighbour's word (lanes 2 u and 2 u + 1 swap: quad permutation 1, 0, 3, 2);
+            // K is a multiple of 32, so both lanes of a pair are inside the row or both past it
+            const uint32_t nb = (uint32_t)__builtin_amdgcn_mov_dpp((int)wd, 0xB1, 0xF, 0xF, false);
+            wd = (tid & 1) == 0 ? __builtin_amdgcn_perm(nb, wd, 0x06040200u)   // own k 0, 2; its k 4, 6
+                                : __builtin_amdgcn_perm(wd, nb, 0x07050301u);  // its k 1, 3; own k 5, 7
         }
+        if (i < K4)
+            out[i] = wd;
     }
 }
 
@@ -1079,23 +1090,34 @@ hipError_t launch_w4_bsplit_t(const W4A8BsplitArgs& a, int blocks, int waves, in
 
 }  // namespace
 
-hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
+namespace {
+
+template <bool UNPACK>
+hipError_t launch_qar(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
 {
     const int nv = (K / 4 + kQrThreads - 1) / kQrThreads;  // float4 per thread
     const dim3 grid((unsigned)M), block(kQrThreads);
     if (nv <= 1)
-        hipLaunchKernelGGL(k_quant_act_rows<1>, grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<1, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 2)
-        hipLaunchKernelGGL(k_quant_act_rows<2>, grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<2, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 4)
-        hipLaunchKernelGGL(k_quant_act_rows<4>, grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<4, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 8)
-        hipLaunchKernelGGL(k_quant_act_rows<8>, grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<8, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 14)
-        hipLaunchKernelGGL(k_quant_act_rows<14>, grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<14, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st,
+                                 bool unpack_order)
+{
+    return unpack_order ? launch_qar<true>(X, M, K, Xq, a, st) : launch_qar<false>(X, M, K, Xq, a, st);
 }
 
 hipError_t launch_gemv_w4a8_bsplit(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st)

@@ -216,7 +216,10 @@ hipError_t launch_gemv_w8a16(const W8A16Args& a, const GemvTiling& t, hipStream_
 hipError_t launch_gemv_w4a8_bsplit(const W4A8BsplitArgs& a, int blocks, int waves, hipStream_t st);
 // row-major int8 codes and one scale per row of X, as launch_quant_act; one 1024-thread
 // workgroup per row holding the row in registers (K <= 57344)
-hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st);
+// With unpack_order, each 16-byte group of codes holds its 16 k in the INT4 unpack order
+// (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15), as the tiled GEMM takes them.
+hipError_t launch_quant_act_rows(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st,
+                                 bool unpack_order = false);
 // The INT4 page's ablations (M == 1, K <= 4096): FP16 GEMV on row-major f16 weights, and
 // weight-only INT4 (quantize_pack_w4 layout) with fp32 activations unpacked to float;
 // rpw rows (FP16) or row groups (INT4) per wave, 1, 2 or 4.

@@ -121,8 +121,9 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    what quant_act_i8 computes.  M == 1: one GEMV kernel with the activation
    quantization fused into its prologue; workspace may be NULL.  M >= 2: the
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
-   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 113 rows, where
-   the output has at least 128 tiles, the tiled GEMM of qw_gemm_w4a8_tile), or with
+   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 65 rows, where
+   the output has at least 96 tiles, the tiled GEMM of qw_gemm_w4a8_tile at the variant
+   a model of the tiles per CU picks), or with
    K > 4096 and up to 8 rows (16 with packed weights below 24 MB) the balanced long-K
    GEMV kernel (qw_gemv_w4a8_long_k); results are the same bits as the GEMV's. */
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
@@ -179,8 +180,8 @@ int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, 
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
    rounding.  M <= 2: GEMV kernel; M >= 3: f16 matrix-core GEMM on the exactly cast
-   weights (from 33 rows, where the output has at least 128 tiles, the tiled GEMM of
-   qw_gemm_w8a16_tile), except with K > 4096 and up to 8 rows (16 with weights below
+   weights (from 33 rows, where the output has at least 96 tiles, the tiled GEMM of
+   qw_gemm_w8a16_tile at the variant a model of the tiles per CU picks), except with K > 4096 and up to 8 rows (16 with weights below
    24 MB), where the balanced long-K GEMV variant runs (u = 7 of qw_gemv_w8a16_tiled).
    No workspace at any M (workspace may be NULL). */
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
@@ -292,23 +293,23 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
 
 /* The tiled f16 matrix-core GEMM for many rows of X (ChatGLM2-6B W8A16 write-up,
    section 4; gemv_w8a16's computation, Y = f16(s16[n] * sum_k q x) with the fp32 sum on
-   the matrix cores) at an explicit launch variant: one workgroup of four waves per
-   output tile of 128 rows of W by 128 (variant 0), 256 (variant 1) or 64 (variant 2)
-   rows of X, or of 64 by 64 (variant 3), or of eight waves per 256 by 128 (variant 4)
-   or 256 by 256 (variant 6), or of four waves with 128 by 128 each (variant 5); variants
-   7, 8 and 9 are 2, 3 and 0 with four stages of loads in flight instead of two; the
-   INT8 weights cast to f16 once per tile in on-chip memory, except in variants 10
-   (eight waves of 128 by 64 on a 256 by 256 tile) and 11 (variant 6), which keep them
-   as INT8 in on-chip memory and cast each operand after reading it.  Same arguments and
-   limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another variant. */
+   the matrix cores) at an explicit launch variant: one workgroup per output tile of
+   rows of W by rows of X, staged through LDS by direct loads and multiplied from there:
+   variant 0: 256 by 256, eight waves; 1: 256 by 128, eight waves; 2: 128 by 128, four
+   waves; 3: 128 by 128, two groups of four waves splitting each stage's k; 4: 128 by 64,
+   four waves; 5: 128 by 64, two groups of four waves; 6: 64 by 64, four waves.  The INT8
+   weights stay INT8 in LDS and each operand is cast to f16 after it is read.  Same
+   arguments and limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another
+   variant. */
 int qw_gemm_w8a16_tile(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16,
                        int64_t M, int64_t N, int64_t K, uint16_t* Y_f16, int variant, void* stream);
 
 /* The same tiled GEMM for W4A8 ("Jetson Orin AGX 上的 INT4 量化推理实践", sections
    当前实现方式 and 正确方向) on the int8 matrix cores: X is first quantized per row into
-   the workspace (row-major codes, as quant_act_i8), then each tile's INT4 weights are
-   widened to int8 lanes once per tile and multiplied against its rows of codes into
-   int32; outputs are gemv_w4a8's bits.  Arguments, limits and workspace as gemv_w4a8 at
+   the workspace (row-major codes, as quant_act_i8, each 16-byte group of codes in the
+   order the INT4 unpack presents the weights), then the packed INT4 weights are staged
+   in LDS as stored, each operand widened to int8 lanes after it is read and multiplied
+   against the tile's rows of codes into int32; outputs are gemv_w4a8's bits.  Arguments, limits and workspace as gemv_w4a8 at
    M >= 2 (qw_workspace_bytes(2, M, N, K) bytes at any M); variants as
    qw_gemm_w8a16_tile. */
 int qw_gemm_w4a8_tile(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,

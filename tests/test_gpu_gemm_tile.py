@@ -1,6 +1,6 @@
-"""The tiled matrix-core GEMM (one workgroup per output tile of 128 rows of W by 64, 128
-or 256 rows of X, weights cast once per tile in on-chip memory) against the oracle, on
-an MI355X.
+"""The tiled matrix-core GEMM (one workgroup per output tile of 64 to 256 rows of W by
+64 to 256 rows of X, staged through LDS by direct loads, every variant) against the
+oracle, on an MI355X.
 
 W8A16 (ChatGLM2-6B W8A16 write-up, section 4): within relative L2 1e-3 of the fp64
 dequantize-then-multiply reference and per element within half an f16 ulp plus the
@@ -38,7 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-VARIANTS = (0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11)
+VARIANTS = tuple(range(7))
 SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
           (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
 
@@ -55,15 +55,20 @@ def test_w8a16_tile_every_variant(M, N, K):
     assert np.array_equal(host(s16).view(np.uint16), s16_o)
     y64 = oracle.gemv_w8a16_ref64(X16, q8, s16_o, nthreads=oracle.num_threads())
     Xd = dev(X16)
+    bad = []
     for v in VARIANTS:
         buf = torch.full((M * N + 64,), float("nan"), dtype=torch.float16, device="cuda")
         Y = buf[:M * N].view(M, N)
         qw.gemm_w8a16_tile(Xd, Wq, s16, v, out=Y)
         y = host(Y)
-        assert np.all(np.isfinite(y.astype(np.float32))), v
-        assert np.all(np.isnan(host(buf[M * N:]).astype(np.float32))), v  # nothing past Y
-        check_w8a16(y, X16, q8, s16_o, y64)
-        assert not np.any(y[M // 2]) and not np.any(y[:, min(3, N - 1)])
+        try:
+            assert np.all(np.isfinite(y.astype(np.float32)))
+            assert np.all(np.isnan(host(buf[M * N:]).astype(np.float32)))  # nothing past Y
+            check_w8a16(y, X16, q8, s16_o, y64)
+            assert not np.any(y[M // 2]) and not np.any(y[:, min(3, N - 1)])
+        except AssertionError:
+            bad.append(v)
+    assert not bad, "variants %s" % bad
 
 
 @pytest.mark.parametrize("M", [64, 512])
@@ -99,13 +104,15 @@ def test_w4a8_tile_every_variant(M, N, K):
     ref = oracle.gemv_w4a8(X, q, s_o, nthreads=oracle.num_threads())
     Xd = dev(X)
     ws = torch.empty(int(qw.lib().qw_workspace_bytes(2, M, N, K)), dtype=torch.uint8, device="cuda")
+    bad = []
     for v in VARIANTS:
         buf = torch.full((M * N + 64,), float("nan"), device="cuda")
         Y = buf[:M * N].view(M, N)
         qw.gemm_w4a8_tile(Xd, Wq, s, v, workspace=ws, out=Y)
         y = host(Y)
-        assert np.all(np.isnan(host(buf[M * N:]))), v
-        assert np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32)), v
+        if not (np.all(np.isnan(host(buf[M * N:]))) and np.array_equal(y.view(np.uint32), ref["Y"].view(np.uint32))):
+            bad.append(v)
+    assert not bad, "variants %s" % bad
 
 
 @pytest.mark.parametrize("M", [64, 512])
@@ -128,11 +135,13 @@ def test_w4a8_tile_sweep_shape_sampled(M):
         assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32)), v
 
 
-# The default entry points route to the tiled GEMM by rows of X where the output has at
-# least 128 tiles: W8A16 from 33 rows (64 x 64 tiles), 81 (128 x 128), 193 (256 x 128)
-# and 385 (256 x 256); W4A8 from 113 rows.  Checked on sampled rows of W.
-ROUTED = [(48, 20000, 1056), (150, 20000, 544), (300, 34000, 512), (520, 33000, 512),
-          (40, 3584, 4096), (120, 9000, 2080), (64, 3000, 18944)]
+# The default entry points route to the tiled GEMM from 33 rows of X (W8A16) or 65
+# (W4A8) where the output has at least 96 tiles, choosing the variant by a model of the
+# tiles on the busiest CU.  These shapes reach every variant on the 256-CU MI355X
+# (W8A16 / W4A8): 6 / balanced, 5 / balanced, 3 / 6, 1 / 1, 0 / 0, 6 / 6, 5 / 4, 3 / 0,
+# 3 / 2, and the balanced kernels for both.  Checked on sampled rows of W.
+ROUTED = [(40, 9000, 1056), (40, 20000, 544), (70, 20000, 2080), (70, 34000, 512), (520, 20000, 512),
+          (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944)]
 
 
 @pytest.mark.parametrize("M,N,K", ROUTED)

@@ -309,6 +309,32 @@ def test_long_k_row_prepass_ties_and_near_ties(M, K):
     assert np.array_equal(bits(host(Y)), bits(ref["Y"]))
 
 
+UNPACK_ORDER = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]  # k offset of byte i
+
+
+@pytest.mark.parametrize("variant", [0, 4])
+@pytest.mark.parametrize("M,K", [(5, 4096), (3, 18944), (2, 512)])
+def test_tiled_gemm_prepass_ties_and_near_ties(variant, M, K):
+    """The row pre-pass of the tiled GEMM: row-major codes, each 16-byte group holding
+    its 16 k in the INT4 unpack order (byte i of group g = k 16 g + UNPACK_ORDER[i])."""
+    say("tiled GEMM pre-pass edges", variant, M, K)
+    X = _act_edges(6, K, 90 + K)[:M]
+    N = 40
+    rng = np.random.default_rng(K + 2)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    q_o, s_o = oracle.quant_w4(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o, nthreads=oracle.num_threads())
+    ws = torch.full((qw.lib().qw_workspace_bytes(2, M, N, K),), 0x55, dtype=torch.uint8,
+                    device="cuda")
+    Y = qw.gemm_w4a8_tile(dev(X), Wq, s, variant, workspace=ws)
+    codes, a = rows_ws_codes(ws, M, K)
+    codes = codes.reshape(M, K // 16, 16)[:, :, np.argsort(UNPACK_ORDER)].reshape(M, K)
+    assert np.array_equal(bits(a), bits(ref["a"]))
+    assert np.array_equal(codes, ref["xq"])
+    assert np.array_equal(bits(host(Y)), bits(ref["Y"]))
+
+
 @pytest.mark.parametrize("M,u", [(1, 0), (1, 2), (1, 4), (2, 1), (3, 8)])
 def test_gemv_variant_prologues_ties_and_near_ties(M, u):
     """The register, all-in-flight, eager and streaming GEMV variants quantize X in

@@ -104,6 +104,39 @@ __device__ __forceinline__ void tile_epilogue(const TileGemmArgs& p, const A (&a
     const int M = p.M, N = p.N;
     const rsrc_t sr = make_rsrc_u(p.w_scale, (uint32_t)N * (BITS == 8 ? 2u : 4u));
     const rsrc_t ar = make_rsrc_u(p.a_scale, BITS == 4 ? (uint32_t)M * 4u : 0u);
+    if constexpr (BITS == 8 && IN % 2 == 0) {
+        if ((N & 1) == 0) {
+            // f16 outputs two columns per lane: lanes 2t and 2t + 1 trade one scaled value,
+            // so that lane 2t holds columns 2t, 2t + 1 of block i and lane 2t + 1 those of
+            // block i + 1, and a half-wave stores 128 contiguous bytes of a row (one
+            // block's 64 would leave the rest of each 128-byte line to another store)
+            const bool odd = (rl & 1) != 0;
+#pragma unroll
+            for (int i = 0; i < IN; i += 2) {
+                const int na = n0 + wn * WN + 32 * i + rl;  // this lane's column in block i
+                const int nb = na + 32;                     // and in block i + 1
+                const float sa = __half2float(__ushort_as_half(load2(sr, (uint32_t)na * 2u)));
+                const float sb = __half2float(__ushort_as_half(load2(sr, (uint32_t)nb * 2u)));
+                const int nc = odd ? nb - 1 : na;  // first column of the lane's pair (even)
+#pragma unroll
+                for (int j = 0; j < JM; ++j) {
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int m = m0 + wm * WM + 32 * j + 8 * (v >> 2) + 4 * half + (v & 3);
+                        const float va = sa * acc[i][j][v], vb = sb * acc[i + 1][j][v];
+                        const float got = __int_as_float(
+                            __builtin_amdgcn_mov_dpp(__float_as_int(odd ? va : vb), 0xB1, 0xF, 0xF, false));
+                        const float lo = odd ? got : va, hi = odd ? vb : got;
+                        if (m < M && nc < N)  // N even: nc + 1 < N as well
+                            *reinterpret_cast<uint32_t*>(static_cast<uint16_t*>(p.Y) + (size_t)m * N + nc) =
+                                (uint32_t)__half_as_ushort(__float2half_rn(lo)) |
+                                ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
+                    }
+                }
+            }
+            return;
+        }
+    }
 #pragma unroll
     for (int i = 0; i < IN; ++i) {
         const int n = n0 + wn * WN + 32 * i + rl;

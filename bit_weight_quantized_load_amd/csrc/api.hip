@@ -420,10 +420,11 @@ int scratch_address(void** out)
 // CU times the tile's work over the variant's efficiency, and the least is taken.  The
 // efficiencies are fitted to sweeps of M = 33 .. 512 on 4096 -> 27392, 3584 -> 18944 and
 // 18944 -> 3584 (the choice is within 0.5% of the best variant on average, 10% at
-// worst).  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64 (30.2 us), 128
-// rows 128 x 128 in two k-groups (42.6), 256 rows 256 x 128 (66.9), 512 rows 256 x 256
-// (113); W4A8 96 rows 128 x 128 (29.0), 256 rows 256 x 128 (42.0), 512 rows 256 x 256
-// (68.5, the activation pre-pass included).  Below 33 (W8A16) or 65 (W4A8) rows the
+// worst; for W8A16 the 128 x 64 tile in two k-groups runs with stages twice as deep,
+// 5-10% faster at 33-64 rows).  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64
+// (27.5 us), 128 rows 128 x 128 in two k-groups (39.6), 256 rows 256 x 128 (63.4), 512
+// rows 256 x 256 (106-110); W4A8 96 rows 128 x 128 (28.9), 256 rows 256 x 128 (39.7),
+// 512 rows 256 x 256 (66.3, the activation pre-pass included).  Below 33 (W8A16) or 65 (W4A8) rows the
 // balanced kernels are as fast or faster (W4A8 at 64 rows: 22.0 against 22.4 us).
 constexpr int64_t kTileMinM8 = 33, kTileMinM4 = 65, kTileMinTiles = 96;
 
@@ -433,7 +434,7 @@ int tile_variant(int bits, int64_t M, int64_t N)
         int v;
         double eff;
     };
-    static const Cand c8[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {3, 0.8}, {4, 0.4}, {5, 0.5}, {6, 0.3}};
+    static const Cand c8[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {3, 0.8}, {4, 0.4}, {7, 0.5}, {6, 0.3}};
     static const Cand c4[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {4, 0.5}, {6, 0.4}};
     if (M < (bits == 8 ? kTileMinM8 : kTileMinM4))
         return -1;

@@ -60,13 +60,6 @@ __device__ __forceinline__ uint2 cast4_f16(uint32_t wd)
     return make_uint2(__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi));
 }
 
-// Rows of X in LDS: 128 bytes (eight 16-byte chunks), chunk c of row r at position
-// c ^ ((r / 2) % 8).  The LDS serves 16 lanes of a 16-byte access per cycle across 64
-// banks (256 bytes, two rows): an operand read (rows r..r+15 at one chunk) lands on 16
-// distinct 16-byte slots of that width.  (With chunk c at c ^ (r % 8), rows r and r + 8
-// met in one bank: the bank-conflict counter read 1.36 conflict cycles per LDS-active
-// cycle.)
-__device__ __forceinline__ int swz(int r, int c) { return r * 128 + 16 * (c ^ ((r >> 1) & 7)); }
 
 // 8 bytes of weights as stored (one MFMA operand per lane) -> the operand: 8 f16 (INT8)
 // or 16 int8 lanes of 16 q in the unpack order (INT4).
@@ -176,21 +169,23 @@ __device__ __forceinline__ void tile_epilogue(const TileGemmArgs& p, const A (&a
 
 // Staging.  The stage's weights and rows of X go from memory straight into LDS (buffer
 // loads with the LDS destination: no registers, no VALU, no LDS store instructions),
-// NBUF stages in flight.  The weights stay in LDS as stored in memory (64 bytes per row
-// per stage, INT8 or packed INT4) and each wave widens the operands it reads; for W4A8
-// the activation codes arrive already in the unpack order.
+// NBUF stages in flight.  The weights stay in LDS as stored in memory (16 CW bytes per
+// row per stage, INT8 or packed INT4) and each wave widens the operands it reads; for
+// W4A8 the activation codes arrive already in the unpack order.
 //
 // A load instruction of one wave writes 1 KB of LDS, lane l's 16 bytes at l * 16, so the
 // swizzle is applied on the memory side: the lane that fills LDS slot s loads the chunk
-// that belongs there.  Weight rows: 64 bytes = four 16-byte chunks, chunk c of row r at
-// position c ^ ((r / 4) % 4); an operand read (16 lanes, rows r..r+15 at one chunk)
-// covers the 64 banks once.  Rows of X as above.
+// that belongs there.  The LDS serves 16 lanes of a 16-byte access per cycle across 64
+// banks (256 bytes); the swizzles (swz_wc, swz_xc) put the 16 rows of an operand read on
+// 16 distinct 16-byte slots of that width.  (With X chunk c of a 128-byte row at
+// c ^ (r % 8), rows r and r + 8 met in one bank: the bank-conflict counter read 1.36
+// conflict cycles per LDS-active cycle.)
 //
-// k assignment within a stage: lane half h reads weight chunks 2 h and 2 h + 1 of its row
-// (one 16-byte read each, two multiplies' operands); at step kk it multiplies chunk
-// 2 h + kk / 2, half kk % 2, against X chunk 4 h + kk.  Both operands of every multiply
-// then hold the same k (W8A16: k 32 h + 8 kk .. + 7; W4A8: 64 h + 16 kk .. + 15), and each
-// k of the stage is taken once.
+// k assignment within a stage: lane half h reads weight chunks h CW / 2 .. h CW / 2 +
+// CW / 2 - 1 of its row (one 16-byte read each, two multiplies' operands); at step kk it
+// multiplies chunk h CW / 2 + kk / 2, half kk % 2, against X chunk h CW + kk.  Both
+// operands of every multiply then hold the same k (W8A16: k 8 (h CW + kk) .. + 7; W4A8:
+// 16 (h CW + kk) .. + 15), and each k of the stage is taken once.
 //
 // Pipeline, stage t in buffer t % NBUF: wait until this wave's loads of stage t have
 // landed (at most (NBUF - 2) stages of loads still in flight), barrier (every wave's
@@ -201,39 +196,57 @@ __device__ __forceinline__ void tile_epilogue(const TileGemmArgs& p, const A (&a
 // keeps the loop free of branches around the loads.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
+// CW: 16-byte chunks of weights per row per stage (4: 64 k of INT8 or 128 k of INT4, with
+// 128 bytes of X per row; 8: twice that).  Deeper stages halve the barriers and the
+// per-stage start for the same k, at twice the LDS per stage.
+//
 // KS > 1 splits each stage's k over KS groups of NWN x NWM waves (group g takes the
-// multiplies of steps kk = 4 g / KS .. 4 (g + 1) / KS - 1 of every stage, on its own
+// multiplies of steps kk = CW g / KS .. CW (g + 1) / KS - 1 of every stage, on its own
 // accumulators), so that a small tile still has several waves per SIMD to overlap one
 // wave's LDS latency and operand widening with another's multiplies.  The groups' sums
 // meet in LDS at the end (int32: exact; fp32: added in group order).
-template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS>
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS, int CW>
 struct DmaCfg {
-    static constexpr int NWN_ = NWN, NWM_ = NWM, KS_ = KS;
+    static constexpr int NWN_ = NWN, NWM_ = NWM, KS_ = KS, CW_ = CW;
     static constexpr int NWG = NWN * NWM;  // waves of one k-group
     static constexpr int NWAVES = NWG * KS, T = 64 * NWAVES;
     static constexpr int BN = WN * NWN, BM = WM * NWM;
-    static constexpr int BK = BITS == 8 ? 64 : 128;  // k per stage
-    static constexpr int SPT = 512 / BK;             // stages per 512-k tile of the weight layout
+    static constexpr int WRB = 16 * CW, XRB = 32 * CW;  // LDS bytes per row of W and of X
+    static constexpr int BK = (BITS == 8 ? 16 : 32) * CW;  // k per stage
+    static constexpr int SPT = 512 / BK;                   // stages per 512-k tile of the weight layout
     static constexpr int IN = WN / 32, JM = WM / 32;
     // waves that issue the stage loads: all of them where the stage divides evenly
-    static constexpr int LW = (BN * 4 % T == 0 && BM * 8 % T == 0) ? NWAVES
-                            : (BN * 4 % (T / 2) == 0 && BM * 8 % (T / 2) == 0) ? NWAVES / 2 : NWG;
-    static constexpr int PW = BN * 4 / (64 * LW);  // 16-byte weight loads per loading thread
-    static constexpr int PX = BM * 8 / (64 * LW);  // 16-byte X loads per loading thread
-    static constexpr int WREG = BN * 64;
-    static constexpr int STAGE = WREG + BM * 128;
+    static constexpr int LW = (BN * CW % T == 0 && BM * 2 * CW % T == 0) ? NWAVES
+                            : (BN * CW % (T / 2) == 0 && BM * 2 * CW % (T / 2) == 0) ? NWAVES / 2 : NWG;
+    static constexpr int PW = BN * CW / (64 * LW);      // 16-byte weight loads per loading thread
+    static constexpr int PX = BM * 2 * CW / (64 * LW);  // 16-byte X loads per loading thread
+    static constexpr int WREG = BN * WRB;
+    static constexpr int STAGE = WREG + BM * XRB;
     static constexpr int VM = (NBUF - 2) * (PW + PX);  // loads left in flight at a barrier
     // the k-group sums meet in the stage buffers: 4 KB blocks (one 32 x 32 accumulator of
     // one wave), BPB of them per buffer
     static constexpr int BPB = STAGE / 4096;
-    static_assert(PW >= 1 && PX >= 1 && BN * 4 % (64 * LW) == 0 && BM * 8 % (64 * LW) == 0, "whole loads");
+    static_assert(CW == 4 || CW == 8, "stage depth");
+    static_assert(PW >= 1 && PX >= 1 && BN * CW % (64 * LW) == 0 && BM * 2 * CW % (64 * LW) == 0, "whole loads");
     static_assert(NBUF >= 2 && NBUF <= 8 && VM <= 63, "wait count");
     static_assert(NBUF * STAGE + 16 * 1024 <= 160 * 1024, "LDS");
     static_assert(KS == 1 || KS == 2 || KS == 4, "k split");
     static_assert(KS == 1 || (BPB >= 1 && (NWG * IN * JM + BPB - 1) / BPB <= NBUF), "room for one group's sums");
 };
 
-__device__ __forceinline__ int swz_w(int r, int c) { return r * 64 + 16 * (c ^ ((r >> 2) & 3)); }
+// Chunk c of weight row r and of X row r in LDS.  Weight rows of 64 bytes: c ^ ((r / 4) % 4);
+// of 128 bytes: c ^ ((r / 2) % 8).  X rows of 128 bytes: c ^ ((r / 2) % 8); of 256 bytes:
+// c ^ (r % 16).  Sixteen consecutive rows at one chunk then fill the 64 banks once.
+template <int CW>
+__device__ __forceinline__ int swz_wc(int r, int c)
+{
+    return CW == 4 ? r * 64 + 16 * (c ^ ((r >> 2) & 3)) : r * 128 + 16 * (c ^ ((r >> 1) & 7));
+}
+template <int CW>
+__device__ __forceinline__ int swz_xc(int r, int c)
+{
+    return CW == 4 ? r * 128 + 16 * (c ^ ((r >> 1) & 7)) : r * 256 + 16 * (c ^ (r & 15));
+}
 
 // The bits of an accumulator element, taken by value (a bit cast applied to an element
 // of a vector-typed value in place reads element 0 with this compiler).
@@ -250,8 +263,8 @@ __device__ __forceinline__ void dma_stage(uint8_t* buf, rsrc_t wr, rsrc_t xr, co
     if (C::LW < C::NWAVES && wave >= C::LW)
         return;
     const bool live = t < stages;
-    const uint32_t kw = (uint32_t)(t / C::SPT) * 1024u + (uint32_t)(t % C::SPT) * 64u;
-    const uint32_t kx = (uint32_t)t * 128u;
+    const uint32_t kw = (uint32_t)(t / C::SPT) * 1024u + (uint32_t)(t % C::SPT) * (uint32_t)C::WRB;
+    const uint32_t kx = (uint32_t)t * (uint32_t)C::XRB;
 #pragma unroll
     for (int q = 0; q < C::PW; ++q)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_ptr_t)(buf + 1024 * (wave + C::LW * q)), 16,
@@ -271,42 +284,46 @@ __device__ __forceinline__ void mfma_tile(A& acc, uint4 x, uint4 w)
         acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(v4i, x), __builtin_bit_cast(v4i, w), acc, 0, 0, 0);
 }
 
-// The multiplies of one stage from LDS buffer buf (one k-group): the operands of step
-// kk + 1 are read before the multiplies of step kk are issued, so their LDS latency
-// overlaps those multiplies.
-template <class C, int BITS, class A>
-__device__ __forceinline__ void dma_compute1(const uint8_t* buf, int wn, int wm, int rl, int h,
-                                             A (&acc)[C::IN][C::JM])
+// The multiplies of NS steps of one stage from LDS buffer buf, from step kk0 (even unless
+// NS == 1): at step kk, lane half h multiplies weight chunk h CW / 2 + kk / 2 (its half
+// kk % 2) against X chunk h CW + kk.  The operands of step kk + 1 are read before the
+// multiplies of step kk are issued, so their LDS latency overlaps those multiplies.
+template <class C, int BITS, int NS, class A>
+__device__ __forceinline__ void dma_steps(const uint8_t* buf, int wn, int wm, int rl, int h, int kk0,
+                                          A (&acc)[C::IN][C::JM])
 {
-    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
+    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_, CW = C::CW_;
     const uint8_t* xl = buf + C::WREG;
+    const int wc0 = h * CW / 2 + (kk0 >> 1), xc0 = h * CW + kk0;
     uint4 w[2][C::IN], b[2][C::JM];
 #pragma unroll
     for (int i = 0; i < C::IN; ++i)
-        w[0][i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h));
+        w[0][i] = *reinterpret_cast<const uint4*>(buf + swz_wc<CW>(wn * WN + 32 * i + rl, wc0));
 #pragma unroll
     for (int j = 0; j < C::JM; ++j)
-        b[0][j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h));
+        b[0][j] = *reinterpret_cast<const uint4*>(xl + swz_xc<CW>(wm * WM + 32 * j + rl, xc0));
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        if (kk < 3) {
-            if (kk == 1) {
+    for (int st = 0; st < NS; ++st) {
+        if (st + 1 < NS) {
+            if (((st + 1) & 1) == 0) {
 #pragma unroll
                 for (int i = 0; i < C::IN; ++i)
-                    w[1][i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h + 1));
+                    w[((st + 1) >> 1) & 1][i] = *reinterpret_cast<const uint4*>(
+                        buf + swz_wc<CW>(wn * WN + 32 * i + rl, wc0 + (st + 1) / 2));
             }
 #pragma unroll
             for (int j = 0; j < C::JM; ++j)
-                b[(kk + 1) & 1][j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h + kk + 1));
+                b[(st + 1) & 1][j] = *reinterpret_cast<const uint4*>(xl + swz_xc<CW>(wm * WM + 32 * j + rl, xc0 + st + 1));
         }
         __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of this step's multiplies
+        const bool hi_half = NS == 1 ? (kk0 & 1) != 0 : (st & 1) != 0;
 #pragma unroll
         for (int i = 0; i < C::IN; ++i) {
-            const uint4 wv = w[kk >> 1][i];
-            const uint4 a = widen8<BITS>((kk & 1) == 0 ? make_uint2(wv.x, wv.y) : make_uint2(wv.z, wv.w));
+            const uint4 wv = w[(st >> 1) & 1][i];
+            const uint4 a = widen8<BITS>(hi_half ? make_uint2(wv.z, wv.w) : make_uint2(wv.x, wv.y));
 #pragma unroll
             for (int j = 0; j < C::JM; ++j)
-                mfma_tile<BITS>(acc[i][j], b[kk & 1][j], a);
+                mfma_tile<BITS>(acc[i][j], b[st & 1][j], a);
         }
     }
 }
@@ -316,43 +333,9 @@ template <class C, int BITS, class A>
 __device__ __forceinline__ void dma_compute(const uint8_t* buf, int wn, int wm, int kg, int rl, int h,
                                             A (&acc)[C::IN][C::JM])
 {
-    if constexpr (C::KS_ == 1) {
-        dma_compute1<C, BITS>(buf, wn, wm, rl, h, acc);
-        return;
-    }
-    constexpr int WN = C::BN / C::NWN_, WM = C::BM / C::NWM_;
-    constexpr int NKP = C::KS_ == 4 ? 1 : 2 / C::KS_;  // 32-k pairs of steps of the group
-    const uint8_t* xl = buf + C::WREG;
-#pragma unroll
-    for (int p = 0; p < NKP; ++p) {
-        const int kp = C::KS_ == 1 ? p : C::KS_ == 2 ? kg : kg >> 1;
-        uint4 w[C::IN];
-#pragma unroll
-        for (int i = 0; i < C::IN; ++i)
-            w[i] = *reinterpret_cast<const uint4*>(buf + swz_w(wn * WN + 32 * i + rl, 2 * h + kp));
-#pragma unroll
-        for (int e0 = 0; e0 < (C::KS_ == 4 ? 1 : 2); ++e0) {
-            const int e = C::KS_ == 4 ? (kg & 1) : e0;
-            const int kk = 2 * kp + e;
-            uint4 b[C::JM];
-#pragma unroll
-            for (int j = 0; j < C::JM; ++j)
-                b[j] = *reinterpret_cast<const uint4*>(xl + swz(wm * WM + 32 * j + rl, 4 * h + kk));
-#pragma unroll
-            for (int i = 0; i < C::IN; ++i) {
-                const uint4 a = widen8<BITS>(e == 0 ? make_uint2(w[i].x, w[i].y) : make_uint2(w[i].z, w[i].w));
-#pragma unroll
-                for (int j = 0; j < C::JM; ++j) {
-                    if constexpr (BITS == 8)
-                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                            __builtin_bit_cast(v8h, b[j]), __builtin_bit_cast(v8h, a), acc[i][j], 0, 0, 0);
-                    else
-                        acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
-                            __builtin_bit_cast(v4i, b[j]), __builtin_bit_cast(v4i, a), acc[i][j], 0, 0, 0);
-                }
-            }
-        }
-    }
+    constexpr int PER = C::CW_ / C::KS_;  // steps per k-group
+    static_assert(PER == 1 || PER % 2 == 0, "a k-group starts at an even step");
+    dma_steps<C, BITS, PER>(buf, wn, wm, rl, h, C::KS_ == 1 ? 0 : kg * PER, acc);
 }
 
 // Wait for this wave's loads of the current stage, then the workgroup barrier.  The
@@ -369,10 +352,10 @@ __device__ __forceinline__ void dma_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS>
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS, int CW>
 __global__ __launch_bounds__(64 * NWN * NWM * KS) void k_gemm_dma(TileGemmArgs p)
 {
-    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS>;
+    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS, CW>;
     constexpr int BN = C::BN, BM = C::BM, BK = C::BK, IN = C::IN, JM = C::JM;
     constexpr int R = BITS == 8 ? 2 : 4;  // rows per tile of the weight layout
     // one array per buffer: the compiler then knows which buffer a DMA writes and which
@@ -412,12 +395,14 @@ __global__ __launch_bounds__(64 * NWN * NWM * KS) void k_gemm_dma(TileGemmArgs p
     uint32_t vw[C::PW], vx[C::PX];
 #pragma unroll
     for (int q = 0; q < C::PW; ++q) {
-        const int i = tid + 64 * C::LW * q, r = i >> 2, c = (i & 3) ^ ((r >> 2) & 3);
+        const int i = tid + 64 * C::LW * q, r = i / CW;
+        const int c = (swz_wc<CW>(r, i % CW) - r * C::WRB) / 16;  // the chunk that lands in slot i
         vw[q] = (uint32_t)(((r / R) * CG) * 1024 + (r % R) * (1024 / R) + 16 * c);
     }
 #pragma unroll
     for (int q = 0; q < C::PX; ++q) {
-        const int i = tid + 64 * C::LW * q, r = i >> 3, c = (i & 7) ^ ((r >> 1) & 7);
+        const int i = tid + 64 * C::LW * q, r = i / (2 * CW);
+        const int c = (swz_xc<CW>(r, i % (2 * CW)) - r * C::XRB) / 16;
         vx[q] = (uint32_t)r * (uint32_t)xrow + 16u * (uint32_t)c;
     }
 
@@ -499,21 +484,22 @@ __global__ __launch_bounds__(64 * NWN * NWM * KS) void k_gemm_dma(TileGemmArgs p
     tile_epilogue<BITS, IN, JM, BN / NWN, BM / NWM>(p, acc, n0, m0, wn, wm, rl, h);
 }
 
-template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS = 1>
+template <int BITS, int WN, int WM, int NWN, int NWM, int NBUF, int KS = 1, int CW = 4>
 hipError_t go_dma(TileGemmArgs p, hipStream_t st)
 {
-    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS>;
+    using C = DmaCfg<BITS, WN, WM, NWN, NWM, NBUF, KS, CW>;
     const int64_t nbn = ((int64_t)p.N + C::BN - 1) / C::BN, nbm = ((int64_t)p.M + C::BM - 1) / C::BM;
     if (nbn * nbm > 0x7fffffff)
         return hipErrorInvalidValue;
     p.mblocks = (int)nbm;
-    hipLaunchKernelGGL((k_gemm_dma<BITS, WN, WM, NWN, NWM, NBUF, KS>), dim3((unsigned)(nbn * nbm)), dim3(C::T), 0,
+    hipLaunchKernelGGL((k_gemm_dma<BITS, WN, WM, NWN, NWM, NBUF, KS, CW>), dim3((unsigned)(nbn * nbm)), dim3(C::T), 0,
                        st, p);
     return hipGetLastError();
 }
 
-// Launch variants: tile (BN x BM), waves, stages in flight, k split.  The LDS footprint
-// decides how many workgroups share a CU (variants 0, 1: one; 2 to 5: two; 6: three).
+// Launch variants: tile (BN x BM), waves, stages in flight, k split, stage depth.  The LDS
+// footprint decides how many workgroups share a CU (variants 0, 1, 7: one; 2 to 5: two;
+// 6: three).
 template <int BITS>
 hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
 {
@@ -525,6 +511,7 @@ hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
     case 4: return go_dma<BITS, 64, 32, 2, 2, 4>(p, st);     // 128 n x 64 m, 4 waves
     case 5: return go_dma<BITS, 64, 32, 2, 2, 4, 2>(p, st);  // 128 n x 64 m, 2 k-groups of 4 waves
     case 6: return go_dma<BITS, 32, 32, 2, 2, 4>(p, st);     // 64 n x 64 m, 4 waves
+    case 7: return go_dma<BITS, 64, 32, 2, 2, 4, 2, 8>(p, st);  // variant 5 with stages twice as deep
     default: return hipErrorInvalidValue;
     }
 }
@@ -536,7 +523,7 @@ int tile_rows_m(int variant)
     switch (variant) {
     case 0: return 256;
     case 1: case 2: case 3: return 128;
-    case 4: case 5: case 6: return 64;
+    case 4: case 5: case 6: case 7: return 64;
     default: return 0;
     }
 }
@@ -545,7 +532,7 @@ int tile_rows_n(int variant)
 {
     switch (variant) {
     case 0: case 1: return 256;
-    case 2: case 3: case 4: case 5: return 128;
+    case 2: case 3: case 4: case 5: case 7: return 128;
     case 6: return 64;
     default: return 0;
     }

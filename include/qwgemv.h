@@ -297,7 +297,8 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
    rows of W by rows of X, staged through LDS by direct loads and multiplied from there:
    variant 0: 256 by 256, eight waves; 1: 256 by 128, eight waves; 2: 128 by 128, four
    waves; 3: 128 by 128, two groups of four waves splitting each stage's k; 4: 128 by 64,
-   four waves; 5: 128 by 64, two groups of four waves; 6: 64 by 64, four waves.  The INT8
+   four waves; 5: 128 by 64, two groups of four waves; 6: 64 by 64, four waves; 7: as 5
+   with stages of 128 bytes of weights per row instead of 64.  The INT8
    weights stay INT8 in LDS and each operand is cast to f16 after it is read.  Same
    arguments and limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another
    variant. */

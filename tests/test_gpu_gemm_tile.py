@@ -38,7 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-VARIANTS = tuple(range(7))
+VARIANTS = tuple(range(8))
 SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
           (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
 
@@ -138,7 +138,7 @@ def test_w4a8_tile_sweep_shape_sampled(M):
 # The default entry points route to the tiled GEMM from 33 rows of X (W8A16) or 65
 # (W4A8) where the output has at least 96 tiles, choosing the variant by a model of the
 # tiles on the busiest CU.  These shapes reach every variant on the 256-CU MI355X
-# (W8A16 / W4A8): 6 / balanced, 5 / balanced, 3 / 6, 1 / 1, 0 / 0, 6 / 6, 5 / 4, 3 / 0,
+# (W8A16 / W4A8): 6 / balanced, 7 / balanced, 3 / 6, 1 / 1, 0 / 0, 6 / 6, 7 / 4, 3 / 0,
 # 3 / 2, and the balanced kernels for both.  Checked on sampled rows of W.
 ROUTED = [(40, 9000, 1056), (40, 20000, 544), (70, 20000, 2080), (70, 34000, 512), (520, 20000, 512),
           (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944)]

@@ -415,45 +415,41 @@ int scratch_address(void** out)
 }
 
 // Launch variant of the tiled matrix-core GEMM for M rows of X and N rows of W, or -1
-// where the balanced matrix-core kernels stay (fewer rows than kTileMinM, or fewer than
-// kTileMinTiles tiles).  Each candidate's time is modelled as the tiles on the busiest
-// CU times the tile's work over the variant's efficiency, and the least is taken.  The
-// efficiencies are fitted to sweeps of M = 33 .. 512 on 4096 -> 27392, 3584 -> 18944 and
-// 18944 -> 3584 (the choice is within 0.5% of the best variant on average, 10% at
-// worst; for W8A16 the 128 x 64 tile in two k-groups runs with stages twice as deep,
-// 5-10% faster at 33-64 rows).  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64
-// (27.5 us), 128 rows 128 x 128 in two k-groups (39.6), 256 rows 256 x 128 (63.4), 512
-// rows 256 x 256 (106-110); W4A8 96 rows 128 x 128 (28.9), 256 rows 256 x 128 (39.7),
-// 512 rows 256 x 256 (66.3, the activation pre-pass included).  Below 33 (W8A16) or 65 (W4A8) rows the
-// balanced kernels are as fast or faster (W4A8 at 64 rows: 22.0 against 22.4 us).
-constexpr int64_t kTileMinM8 = 33, kTileMinM4 = 65, kTileMinTiles = 96;
+// where the balanced matrix-core kernels stay (fewer than 33 rows, or fewer than 96
+// tiles).  Each candidate's time is modelled as the tiles on the busiest CU times the
+// tile's work over the variant's efficiency, and the least is taken.  The efficiencies
+// (the same for W8A16 and W4A8) are fitted to sweeps of M = 33 .. 512 on 4096 -> 27392,
+// 3584 -> 18944 and 18944 -> 3584: the choice is within 0.6% of the best variant on
+// average and 7% at worst.  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64 in
+// two k-groups with deep stages (29.9 us), 128 rows 128 x 128 in two k-groups (41.1),
+// 256 rows 256 x 128 (64.0), 512 rows 256 x 256 (111); W4A8 33 rows 128 x 64 (18.9;
+// 20.3 for the balanced kernel), 128 rows 128 x 128 (27.3), 256 rows 256 x 128 (41.0),
+// 512 rows 256 x 256 (61.7, the activation pre-pass included).
+constexpr int64_t kTileMinM = 33, kTileMinTiles = 96;
 
-int tile_variant(int bits, int64_t M, int64_t N)
+int tile_variant(int /*bits*/, int64_t M, int64_t N)
 {
     struct Cand {
         int v;
         double eff;
     };
-    static const Cand c8[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {3, 0.8}, {4, 0.4}, {7, 0.5}, {6, 0.3}};
-    static const Cand c4[] = {{0, 1.0}, {1, 0.8}, {2, 0.5}, {4, 0.5}, {6, 0.4}};
-    if (M < (bits == 8 ? kTileMinM8 : kTileMinM4))
+    static const Cand cand[] = {{0, 1.0}, {1, 0.7}, {2, 0.4}, {3, 0.5}, {4, 0.3}, {5, 0.3}, {7, 0.4}, {6, 0.3}};
+    if (M < kTileMinM)
         return -1;
-    const Cand* c = bits == 8 ? c8 : c4;
-    const int nc = bits == 8 ? (int)(sizeof(c8) / sizeof(c8[0])) : (int)(sizeof(c4) / sizeof(c4[0]));
     const int64_t cus = std::max<int64_t>(1, device_cus());
     double best = 0.0;
     int pick = -1;
-    for (int i = 0; i < nc; ++i) {
-        const int64_t bm = qw::tile_rows_m(c[i].v), bn = qw::tile_rows_n(c[i].v);
+    for (const Cand& c : cand) {
+        const int64_t bm = qw::tile_rows_m(c.v), bn = qw::tile_rows_n(c.v);
         if (bm <= 0 || bn <= 0)
             continue;
         const int64_t tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
         if (tiles < kTileMinTiles)
             continue;
-        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bn * bm) / c[i].eff;
+        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bn * bm) / c.eff;
         if (pick < 0 || cost < best * 0.999) {
             best = cost;
-            pick = c[i].v;
+            pick = c.v;
         }
     }
     return pick;

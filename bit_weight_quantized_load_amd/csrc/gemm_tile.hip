@@ -167,6 +167,102 @@ __device__ __forceinline__ void tile_epilogue(const TileGemmArgs& p, const A (&a
     }
 }
 
+// W4A8 epilogue through LDS: the fp32 outputs of one 32 x 32 block go to a 4 KB LDS
+// scratch of the wave row by row, and come back as 16 bytes (4 columns) of one row per
+// lane, so that each store instruction writes 8 rows x 128 contiguous bytes with 16 bytes
+// per lane (storing straight from the accumulators, 4 bytes per lane, took 13.5 of 62
+// us at 512 rows on 4096 -> 27392; 16-byte stores of whole 128-byte row runs, 5 us).
+// Row r of the block sits at (r / 8) KB + (r % 4) * 256 + ((r / 4) % 2) * 128: the 64
+// lanes of a write (rows r and r + 4 of one column range) and the 16 lanes of an LDS read
+// cycle (rows r and r + 4) each cover the 64 banks once.  Needs N % 4 == 0 (aligned
+// 16-byte runs); scr is private to the wave.
+template <int IN, int JM, int WN, int WM, class A>
+__device__ __forceinline__ void tile_epilogue_w4_lds(const TileGemmArgs& p, const A (&acc)[IN][JM], int n0, int m0,
+                                                     int wn, int wm, int rl, int half, uint8_t* scr)
+{
+    const int M = p.M, N = p.N, lane = rl + 32 * half;
+    const rsrc_t sr = make_rsrc_u(p.w_scale, (uint32_t)N * 4u);
+    const rsrc_t ar = make_rsrc_u(p.a_scale, (uint32_t)M * 4u);
+    const int a8 = lane >> 3, c4 = lane & 7;
+    const int rr = ((a8 & 1) << 2) + (a8 >> 1);  // row (mod 8) this lane reads back
+#pragma unroll
+    for (int i = 0; i < IN; ++i) {
+        const float sc = __uint_as_float(load4(sr, (uint32_t)(n0 + wn * WN + 32 * i + rl) * 4u));
+        const int n = n0 + wn * WN + 32 * i + 4 * c4;  // first of the 4 columns this lane stores
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int mb = m0 + wm * WM + 32 * j;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 a4 = load16f(ar, (uint32_t)(mb + 8 * g + 4 * half) * 4u);
+                const float av[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    *reinterpret_cast<float*>(scr + g * 1024 + e * 256 + half * 128 + rl * 4) =
+                        ((float)(acc[i][j][4 * g + e] >> 4) * sc) * av[e];
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * q + rr;
+                const float4 v = *reinterpret_cast<const float4*>(scr + q * 1024 + (r & 3) * 256 +
+                                                                  ((r >> 2) & 1) * 128 + c4 * 16);
+                const int m = mb + r;
+                if (m < M && n < N)  // N % 4 == 0: the 4 columns are inside together
+                    *reinterpret_cast<float4*>(static_cast<float*>(p.Y) + (size_t)m * N + n) = v;
+            }
+        }
+    }
+}
+
+// W8A16 epilogue through LDS, the same way: blocks i and i + 1 (64 columns of f16, 128
+// bytes per row) go to the wave's 4 KB scratch, two adjacent columns per lane (lanes 2t
+// and 2t + 1 trade one scaled value first), and come back as 16 bytes (8 columns) per
+// lane, 8 rows x 128 contiguous bytes per store instruction.  Needs N % 8 == 0.
+template <int IN, int JM, int WN, int WM, class A>
+__device__ __forceinline__ void tile_epilogue_w8_lds(const TileGemmArgs& p, const A (&acc)[IN][JM], int n0, int m0,
+                                                     int wn, int wm, int rl, int half, uint8_t* scr)
+{
+    static_assert(IN % 2 == 0, "blocks in pairs");
+    const int M = p.M, N = p.N, lane = rl + 32 * half;
+    const rsrc_t sr = make_rsrc_u(p.w_scale, (uint32_t)N * 2u);
+    const bool odd = (rl & 1) != 0;
+    const int a8 = lane >> 3, c4 = lane & 7;
+    const int rr = ((a8 & 1) << 2) + (a8 >> 1);  // row (mod 8) this lane reads back
+#pragma unroll
+    for (int i = 0; i < IN; i += 2) {
+        const int na = n0 + wn * WN + 32 * i + rl;  // this lane's column in block i
+        const float sa = __half2float(__ushort_as_half(load2(sr, (uint32_t)na * 2u)));
+        const float sb = __half2float(__ushort_as_half(load2(sr, (uint32_t)(na + 32) * 2u)));
+        // lane 2t holds columns 2t, 2t + 1 of block i, lane 2t + 1 those of block i + 1
+        const int cb = odd ? 64 + 2 * (rl - 1) : 2 * rl;  // byte offset of the pair in the row
+        const int n = n0 + wn * WN + 32 * i + 8 * c4;     // first of the 8 columns this lane stores
+#pragma unroll
+        for (int j = 0; j < JM; ++j) {
+            const int mb = m0 + wm * WM + 32 * j;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const float va = sa * acc[i][j][v], vb = sb * acc[i + 1][j][v];
+                const float got = __int_as_float(
+                    __builtin_amdgcn_mov_dpp(__float_as_int(odd ? va : vb), 0xB1, 0xF, 0xF, false));
+                const float lo = odd ? got : va, hi = odd ? vb : got;
+                const int g = v >> 2, e = v & 3;
+                *reinterpret_cast<uint32_t*>(scr + g * 1024 + e * 256 + half * 128 + cb) =
+                    (uint32_t)__half_as_ushort(__float2half_rn(lo)) |
+                    ((uint32_t)__half_as_ushort(__float2half_rn(hi)) << 16);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = 8 * q + rr;
+                const uint4 o = *reinterpret_cast<const uint4*>(scr + q * 1024 + (r & 3) * 256 +
+                                                                ((r >> 2) & 1) * 128 + c4 * 16);
+                const int m = mb + r;
+                if (m < M && n < N)  // N % 8 == 0: the 8 columns are inside together
+                    *reinterpret_cast<uint4*>(static_cast<uint16_t*>(p.Y) + (size_t)m * N + n) = o;
+            }
+        }
+    }
+}
+
 // Staging.  The stage's weights and rows of X go from memory straight into LDS (buffer
 // loads with the LDS destination: no registers, no VALU, no LDS store instructions),
 // NBUF stages in flight.  The weights stay in LDS as stored in memory (16 CW bytes per
@@ -232,6 +328,7 @@ struct DmaCfg {
     static_assert(NBUF * STAGE + 16 * 1024 <= 160 * 1024, "LDS");
     static_assert(KS == 1 || KS == 2 || KS == 4, "k split");
     static_assert(KS == 1 || (BPB >= 1 && (NWG * IN * JM + BPB - 1) / BPB <= NBUF), "room for one group's sums");
+    static_assert(KS > 1 || (NWAVES + NBUF - 1) / NBUF * 4096 <= STAGE, "room for the epilogue scratch");
 };
 
 // Chunk c of weight row r and of X row r in LDS.  Weight rows of 64 bytes: c ^ ((r / 4) % 4);
@@ -481,6 +578,26 @@ __global__ __launch_bounds__(64 * NWN * NWM * KS) void k_gemm_dma(TileGemmArgs p
             return;
     }
 
+    if constexpr (BITS == 4 || IN % 2 == 0) {
+        if ((p.N & (BITS == 4 ? 3 : 7)) == 0) {
+            // a 4 KB scratch per wave: after the k-group hand-off, the wave's own first
+            // hand-off block (read back by this wave only); otherwise a slice of the stage
+            // buffers, once every wave is past its last multiply
+            uint8_t* scr;
+            if constexpr (KS > 1) {
+                const int blk = wg * IN * JM;
+                scr = bufs(blk / C::BPB) + 4096 * (blk % C::BPB);
+            } else {
+                dma_barrier<0>();
+                scr = bufs(wave % NBUF) + 4096 * (wave / NBUF);
+            }
+            if constexpr (BITS == 4)
+                tile_epilogue_w4_lds<IN, JM, BN / NWN, BM / NWM>(p, acc, n0, m0, wn, wm, rl, h, scr);
+            else
+                tile_epilogue_w8_lds<IN, JM, BN / NWN, BM / NWM>(p, acc, n0, m0, wn, wm, rl, h, scr);
+            return;
+        }
+    }
     tile_epilogue<BITS, IN, JM, BN / NWN, BM / NWM>(p, acc, n0, m0, wn, wm, rl, h);
 }
 

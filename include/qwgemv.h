@@ -121,7 +121,7 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    what quant_act_i8 computes.  M == 1: one GEMV kernel with the activation
    quantization fused into its prologue; workspace may be NULL.  M >= 2: the
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
-   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 65 rows, where
+   bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 33 rows, where
    the output has at least 96 tiles, the tiled GEMM of qw_gemm_w4a8_tile at the variant
    a model of the tiles per CU picks), or with
    K > 4096 and up to 8 rows (16 with packed weights below 24 MB) the balanced long-K

@@ -135,11 +135,10 @@ def test_w4a8_tile_sweep_shape_sampled(M):
         assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32)), v
 
 
-# The default entry points route to the tiled GEMM from 33 rows of X (W8A16) or 65
-# (W4A8) where the output has at least 96 tiles, choosing the variant by a model of the
-# tiles on the busiest CU.  These shapes reach every variant on the 256-CU MI355X
-# (W8A16 / W4A8): 6 / balanced, 7 / balanced, 3 / 6, 1 / 1, 0 / 0, 6 / 6, 7 / 4, 3 / 0,
-# 3 / 2, and the balanced kernels for both.  Checked on sampled rows of W.
+# The default entry points route to the tiled GEMM from 33 rows of X where the output
+# has at least 96 tiles, choosing the variant by a model of the tiles on the busiest CU.
+# These shapes reach variants 6, 7, 3, 1, 0, 6, 7, 0, 3 and the balanced kernels on the
+# 256-CU MI355X (the same for W8A16 and W4A8).  Checked on sampled rows of W.
 ROUTED = [(40, 9000, 1056), (40, 20000, 544), (70, 20000, 2080), (70, 34000, 512), (520, 20000, 512),
           (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944)]
 

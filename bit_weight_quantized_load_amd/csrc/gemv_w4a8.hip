@@ -864,8 +864,9 @@ hipError_t launch_gemv_w4a8(const W4A8Args& a, const GemvTiling& t, bool debug, 
 
 namespace {
 
-// Activation quantization for the long-K kernel and the tiled GEMM: one workgroup of
-// 1024 threads per row of X, which loads the whole row into registers at once (NV float4
+// Activation quantization for the long-K kernel and the tiled GEMM: one workgroup of T
+// threads per row of X (512 up to K = 4096: 0.3-0.6 us less than 1024 threads of one
+// float4 each; 1024 beyond), which loads the whole row into registers at once (NV float4
 // per thread, so a single memory round trip), takes max|x| across the workgroup and
 // writes the row-major codes from the same registers.  The scale and the codes are
 // computed exactly as by the standalone quantization kernel.  With UNPACK, each 16-byte
@@ -873,14 +874,11 @@ namespace {
 // (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15): the lane holding k 4j .. 4j + 3
 // of a group and its neighbour exchange their words, the even lane keeps the even k of
 // both and the odd lane the odd k, and each writes the word at its own position.
-constexpr int kQrThreads = 1024;
-
-template <int NV, bool UNPACK>
-__global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __restrict__ X, int K,
-                                                               int8_t* __restrict__ Xq,
-                                                               float* __restrict__ a_scale)
+template <int T, int NV, bool UNPACK>
+__global__ __launch_bounds__(T) void k_quant_act_rows(const float* __restrict__ X, int K, int8_t* __restrict__ Xq,
+                                                      float* __restrict__ a_scale)
 {
-    __shared__ float red[kQrThreads / 64];
+    __shared__ float red[T / 64];
     const int tid = threadIdx.x;
     const int m = blockIdx.x;
     const int K4 = K >> 2;
@@ -889,7 +887,7 @@ __global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __re
     float mx = 0.0f;
 #pragma unroll
     for (int t = 0; t < NV; ++t) {
-        const int i = tid + kQrThreads * t;
+        const int i = tid + T * t;
         v[t] = load16f(xr, i < K4 ? (uint32_t)i * 16u : 0x80000000u);
         mx = fmaxf(mx, max_abs4(v[t]));
     }
@@ -899,7 +897,7 @@ __global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __re
     __syncthreads();
     mx = red[0];
 #pragma unroll
-    for (int w = 1; w < kQrThreads / 64; ++w)
+    for (int w = 1; w < T / 64; ++w)
         mx = fmaxf(mx, red[w]);
     const float a = mx / 127.0f;
     const float r = 1.0f / a;
@@ -909,7 +907,7 @@ __global__ __launch_bounds__(kQrThreads) void k_quant_act_rows(const float* __re
     uint32_t* out = reinterpret_cast<uint32_t*>(Xq + (size_t)m * K);
 #pragma unroll
     for (int t = 0; t < NV; ++t) {
-        const int i = tid + kQrThreads * t;
+        const int i = tid + T * t;
         const float4 x = v[t];
         uint32_t wd = fast ? pack_i8x4(quant_code_fast(x.x, a, r, 127.f), quant_code_fast(x.y, a, r, 127.f),
                                        quant_code_fast(x.z, a, r, 127.f), quant_code_fast(x.w, a, r, 127.f))
@@ -1092,24 +1090,31 @@ hipError_t launch_w4_bsplit_t(const W4A8BsplitArgs& a, int blocks, int waves, in
 
 namespace {
 
-template <bool UNPACK>
-hipError_t launch_qar(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
+template <int T, bool UNPACK>
+hipError_t launch_qar_t(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
 {
-    const int nv = (K / 4 + kQrThreads - 1) / kQrThreads;  // float4 per thread
-    const dim3 grid((unsigned)M), block(kQrThreads);
+    const int nv = (K / 4 + T - 1) / T;  // float4 per thread
+    const dim3 grid((unsigned)M), block(T);
     if (nv <= 1)
-        hipLaunchKernelGGL((k_quant_act_rows<1, UNPACK>), grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<T, 1, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 2)
-        hipLaunchKernelGGL((k_quant_act_rows<2, UNPACK>), grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<T, 2, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 4)
-        hipLaunchKernelGGL((k_quant_act_rows<4, UNPACK>), grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<T, 4, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 8)
-        hipLaunchKernelGGL((k_quant_act_rows<8, UNPACK>), grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<T, 8, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else if (nv <= 14)
-        hipLaunchKernelGGL((k_quant_act_rows<14, UNPACK>), grid, block, 0, st, X, K, Xq, a);
+        hipLaunchKernelGGL((k_quant_act_rows<T, 14, UNPACK>), grid, block, 0, st, X, K, Xq, a);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
+}
+
+template <bool UNPACK>
+hipError_t launch_qar(const float* X, int M, int K, int8_t* Xq, float* a, hipStream_t st)
+{
+    return K / 4 <= 2 * 512 ? launch_qar_t<512, UNPACK>(X, M, K, Xq, a, st)
+                            : launch_qar_t<1024, UNPACK>(X, M, K, Xq, a, st);
 }
 
 }  // namespace

@@ -415,26 +415,30 @@ int scratch_address(void** out)
 }
 
 // Launch variant of the tiled matrix-core GEMM for M rows of X and N rows of W, or -1
-// where the balanced matrix-core kernels stay (fewer than 33 rows, or fewer than 96
-// tiles).  Each candidate's time is modelled as the tiles on the busiest CU times the
-// tile's work over the variant's efficiency, and the least is taken.  The efficiencies
-// (the same for W8A16 and W4A8) are fitted to sweeps of M = 33 .. 512 on 4096 -> 27392,
-// 3584 -> 18944 and 18944 -> 3584: the choice is within 0.6% of the best variant on
-// average and 7% at worst.  Measured choices on 4096 -> 27392: W8A16 64 rows 128 x 64 in
-// two k-groups with deep stages (29.9 us), 128 rows 128 x 128 in two k-groups (41.1),
-// 256 rows 256 x 128 (64.0), 512 rows 256 x 256 (111); W4A8 33 rows 128 x 64 (18.9;
-// 20.3 for the balanced kernel), 128 rows 128 x 128 (27.3), 256 rows 256 x 128 (41.0),
-// 512 rows 256 x 256 (61.7, the activation pre-pass included).
-constexpr int64_t kTileMinM = 33, kTileMinTiles = 96;
+// where the balanced matrix-core kernels stay (fewer than 17 rows for W8A16 or 33 for
+// W4A8, or fewer than 96 tiles).  Each candidate's time is modelled as the tiles on the
+// busiest CU times the tile's work over the variant's efficiency, and the least is taken.
+// The efficiencies are fitted to sweeps of M = 17 .. 512 on 4096 -> 27392, 3584 -> 18944
+// and 18944 -> 3584: the choice is within 0.4% (W8A16) and 0.5% (W4A8) of the best
+// variant on average and 8% at worst.  From 17 to 32 rows the tiled GEMM beats the
+// balanced W8A16 kernel by up to 14% (24.9 against 28.9 us at 32 rows on 4096 -> 27392)
+// and ties it at 17; for W4A8 the balanced kernel with its cheaper pre-pass stays ahead
+// on 3584 -> 18944 below 33 rows.  Measured choices on 4096 -> 27392: W8A16 64 rows
+// 128 x 64 in two k-groups with deep stages (27.1-27.5 us), 128 rows 128 x 128 in two
+// k-groups (39.5), 256 rows 256 x 128 (62), 512 rows 256 x 256 (101-107); W4A8 64 rows
+// 128 x 64 (20.3), 128 rows 128 x 128 (26.1), 256 rows 256 x 128 (36), 512 rows
+// 256 x 256 (59-61, the activation pre-pass included).
+constexpr int64_t kTileMinTiles = 96;
 
-int tile_variant(int /*bits*/, int64_t M, int64_t N)
+int tile_variant(int bits, int64_t M, int64_t N)
 {
     struct Cand {
         int v;
-        double eff;
+        double eff8, eff4;  // W8A16, W4A8
     };
-    static const Cand cand[] = {{0, 1.0}, {1, 0.7}, {2, 0.4}, {3, 0.5}, {4, 0.3}, {5, 0.3}, {7, 0.4}, {6, 0.3}};
-    if (M < kTileMinM)
+    static const Cand cand[] = {{0, 1.0, 1.0}, {1, 0.8, 0.8}, {2, 0.4, 0.5}, {3, 0.5, 0.5},
+                                {4, 0.3, 0.3}, {5, 0.3, 0.3}, {7, 0.4, 0.4}, {6, 0.3, 0.3}};
+    if (M < (bits == 8 ? 17 : 33))
         return -1;
     const int64_t cus = std::max<int64_t>(1, device_cus());
     double best = 0.0;
@@ -446,7 +450,7 @@ int tile_variant(int /*bits*/, int64_t M, int64_t N)
         const int64_t tiles = ((N + bn - 1) / bn) * ((M + bm - 1) / bm);
         if (tiles < kTileMinTiles)
             continue;
-        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bn * bm) / c.eff;
+        const double cost = (double)((tiles + cus - 1) / cus) * (double)(bn * bm) / (bits == 8 ? c.eff8 : c.eff4);
         if (pick < 0 || cost < best * 0.999) {
             best = cost;
             pick = c.v;

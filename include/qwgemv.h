@@ -180,7 +180,7 @@ int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, 
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
    rounding.  M <= 2: GEMV kernel; M >= 3: f16 matrix-core GEMM on the exactly cast
-   weights (from 33 rows, where the output has at least 96 tiles, the tiled GEMM of
+   weights (from 17 rows, where the output has at least 96 tiles, the tiled GEMM of
    qw_gemm_w8a16_tile at the variant a model of the tiles per CU picks), except with K > 4096 and up to 8 rows (16 with weights below
    24 MB), where the balanced long-K GEMV variant runs (u = 7 of qw_gemv_w8a16_tiled).
    No workspace at any M (workspace may be NULL). */

@@ -135,12 +135,14 @@ def test_w4a8_tile_sweep_shape_sampled(M):
         assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32)), v
 
 
-# The default entry points route to the tiled GEMM from 33 rows of X where the output
-# has at least 96 tiles, choosing the variant by a model of the tiles on the busiest CU.
-# These shapes reach variants 6, 7, 3, 1, 0, 6, 7, 0, 3 and the balanced kernels on the
-# 256-CU MI355X (the same for W8A16 and W4A8).  Checked on sampled rows of W.
+# The default entry points route to the tiled GEMM from 17 (W8A16) or 33 (W4A8) rows of
+# X where the output has at least 96 tiles, choosing the variant by a model of the tiles
+# on the busiest CU.  On the 256-CU MI355X these shapes reach variants 6, 7, 3 (W4A8: 2),
+# 1, 0, 6, 7, 0, 3 (W4A8: 2), the balanced kernels (3000 rows of W), and at 24 rows
+# variant 6 for W8A16 beside the balanced W4A8 kernel.  Checked on sampled rows of W.
 ROUTED = [(40, 9000, 1056), (40, 20000, 544), (70, 20000, 2080), (70, 34000, 512), (520, 20000, 512),
-          (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944)]
+          (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944),
+          (24, 9000, 1056)]
 
 
 @pytest.mark.parametrize("M,N,K", ROUTED)

@@ -425,9 +425,9 @@ def test_balanced_w8a16_two_block_kernel_matches_oracle(M, N, K):
         assert np.array_equal(y.view(np.uint16), y1.view(np.uint16))
     yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
     check_w8a16(yd, X16, q8, s16_o, y64)
-    # the default path at 17 to 64 rows is this kernel, except from 33 rows where the
-    # tiled GEMM has at least 96 tiles of its smallest variant (64 x 64)
-    tiled = M >= 33 and -(-N // 64) * -(-M // 64) >= 96
+    # the default path at 17 to 64 rows is this kernel, except where the tiled GEMM has
+    # at least 96 tiles of its smallest variant (64 x 64)
+    tiled = M >= 17 and -(-N // 64) * -(-M // 64) >= 96
     if M <= 64 and not tiled:
         assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 

@@ -408,10 +408,10 @@ def gemm_w8a16_mfma(X16, Wq, w_scale16, nw=4, mb=1, nbw=1, out=None, stream=None
 
 
 def gemm_w8a16_tile(X16, Wq, w_scale16, variant=0, out=None, stream=None):
-    """The tiled f16 matrix-core W8A16 GEMM at launch variant 0 to 7 (output tiles of
+    """The tiled f16 matrix-core W8A16 GEMM at launch variant 0 to 8 (output tiles of
     256 x 256, 256 x 128, 128 x 128, 128 x 128 in two k-groups, 128 x 64, 128 x 64 in
-    two k-groups, 64 x 64, and 128 x 64 in two k-groups with deeper stages: rows of W
-    by rows of X)."""
+    two k-groups, 64 x 64, 128 x 64 in two k-groups with deeper stages, and 128 x 32
+    with deeper stages: rows of W by rows of X)."""
     torch = _torch()
     M, K = X16.shape
     N = w_scale16.shape[0]

@@ -415,19 +415,23 @@ int scratch_address(void** out)
 }
 
 // Launch variant of the tiled matrix-core GEMM for M rows of X and N rows of W, or -1
-// where the balanced matrix-core kernels stay (fewer than 17 rows for W8A16 or 33 for
-// W4A8, or fewer than 96 tiles).  Each candidate's time is modelled as the tiles on the
-// busiest CU times the tile's work over the variant's efficiency, and the least is taken.
-// The efficiencies are fitted to sweeps of M = 17 .. 512 on 4096 -> 27392, 3584 -> 18944
-// and 18944 -> 3584: the choice is within 0.4% (W8A16) and 0.5% (W4A8) of the best
-// variant on average and 8% at worst.  From 17 to 32 rows the tiled GEMM beats the
-// balanced W8A16 kernel by up to 14% (24.9 against 28.9 us at 32 rows on 4096 -> 27392)
-// and ties it at 17; for W4A8 the balanced kernel with its cheaper pre-pass stays ahead
-// on 3584 -> 18944 below 33 rows.  Measured choices on 4096 -> 27392: W8A16 64 rows
-// 128 x 64 in two k-groups with deep stages (27.1-27.5 us), 128 rows 128 x 128 in two
-// k-groups (39.5), 256 rows 256 x 128 (62), 512 rows 256 x 256 (101-107); W4A8 64 rows
-// 128 x 64 (20.3), 128 rows 128 x 128 (26.1), 256 rows 256 x 128 (36), 512 rows
-// 256 x 256 (59-61, the activation pre-pass included).
+// where the balanced matrix-core kernels stay.  From 33 rows each candidate's time is
+// modelled as the tiles on the busiest CU times the tile's work over the variant's
+// efficiency, and the least is taken among the variants with at least 96 tiles.  The
+// efficiencies are fitted to sweeps of every variant at M = 9 .. 512 on 4096 -> 27392,
+// 3584 -> 18944, 4096 -> 9000 and 18944 -> 3584: the choice is within 0.5% of the best
+// variant on average and 8% at worst.  W8A16 at 12 to 32 rows takes the 128 x 32 tiles
+// where there are at least 128 of them (N >= 16257): 16.5-18.4 against 17.1-22.2 us for
+// the balanced kernel on 3584 -> 18944, 22.5-23.0 against 23.0-28.9 on 4096 -> 27392;
+// with fewer tiles the balanced kernel, which spreads any N over every CU, is faster
+// (4096 -> 9000 at 16 rows: 12.8 against 16.0 us).  W4A8 takes them from 20 rows on the
+// same condition (24 and 32 rows on 4096 -> 27392: 16.5 and 16.7 against 18.5 and 18.8
+// us; at 16 rows its balanced kernel with the cheaper pre-pass is still ahead, 15.5
+// against 16.2).  Measured choices on 4096 -> 27392: W8A16 16 rows
+// 128 x 32 (22.5 us), 64 rows 128 x 64 in two k-groups with deep stages (27.4), 128
+// rows 128 x 128 in two k-groups (39.3), 256 rows 256 x 128 (62), 512 rows 256 x 256
+// (101-107); W4A8 64 rows 128 x 64 (20.3), 128 rows 128 x 128 (26.1), 256 rows 256 x
+// 128 (36), 512 rows 256 x 256 (59-61, the activation pre-pass included).
 constexpr int64_t kTileMinTiles = 96;
 
 int tile_variant(int bits, int64_t M, int64_t N)
@@ -437,9 +441,13 @@ int tile_variant(int bits, int64_t M, int64_t N)
         double eff8, eff4;  // W8A16, W4A8
     };
     static const Cand cand[] = {{0, 1.0, 1.0}, {1, 0.8, 0.8}, {2, 0.4, 0.5}, {3, 0.5, 0.5},
-                                {4, 0.3, 0.3}, {5, 0.3, 0.3}, {7, 0.4, 0.4}, {6, 0.3, 0.3}};
-    if (M < (bits == 8 ? 17 : 33))
+                                {4, 0.3, 0.3}, {5, 0.3, 0.3}, {7, 0.4, 0.4}, {8, 0.35, 0.35},
+                                {6, 0.3, 0.3}};
+    if (M < 33) {
+        if (M >= (bits == 8 ? 12 : 20) && (N + 127) / 128 >= 128)
+            return 8;
         return -1;
+    }
     const int64_t cus = std::max<int64_t>(1, device_cus());
     double best = 0.0;
     int pick = -1;

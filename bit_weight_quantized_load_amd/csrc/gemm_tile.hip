@@ -655,8 +655,8 @@ hipError_t go_dma(TileGemmArgs p, hipStream_t st)
 }
 
 // Launch variants: tile (BN x BM), waves, stages in flight, k split, stage depth.  The LDS
-// footprint decides how many workgroups share a CU (variants 0, 1, 7: one; 2 to 5: two;
-// 6: three).
+// footprint decides how many workgroups share a CU (variants 0, 1, 7: one; 2 to 5 and 8:
+// two; 6: three).
 template <int BITS>
 hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
 {
@@ -669,6 +669,7 @@ hipError_t go_variant(const TileGemmArgs& p, int variant, hipStream_t st)
     case 5: return go_dma<BITS, 64, 32, 2, 2, 4, 2>(p, st);  // 128 n x 64 m, 2 k-groups of 4 waves
     case 6: return go_dma<BITS, 32, 32, 2, 2, 4>(p, st);     // 64 n x 64 m, 4 waves
     case 7: return go_dma<BITS, 64, 32, 2, 2, 4, 2, 8>(p, st);  // variant 5 with stages twice as deep
+    case 8: return go_dma<BITS, 32, 32, 4, 1, 4, 1, 8>(p, st);  // 128 n x 32 m, 4 waves, deep stages
     default: return hipErrorInvalidValue;
     }
 }
@@ -681,6 +682,7 @@ int tile_rows_m(int variant)
     case 0: return 256;
     case 1: case 2: case 3: return 128;
     case 4: case 5: case 6: case 7: return 64;
+    case 8: return 32;
     default: return 0;
     }
 }
@@ -689,7 +691,7 @@ int tile_rows_n(int variant)
 {
     switch (variant) {
     case 0: case 1: return 256;
-    case 2: case 3: case 4: case 5: case 7: return 128;
+    case 2: case 3: case 4: case 5: case 7: case 8: return 128;
     case 6: return 64;
     default: return 0;
     }

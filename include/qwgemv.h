@@ -123,7 +123,8 @@ int quant_act_i8(const float* X, int64_t M, int64_t K, int8_t* Xq, float* a_scal
    quantization runs once into `workspace` (at least qw_workspace_bytes(0, M, N, K)
    bytes, else QW_ERR_WORKSPACE), then an int8 matrix-core GEMM (from 33 rows, where
    the output has at least 96 tiles, the tiled GEMM of qw_gemm_w4a8_tile at the variant
-   a model of the tiles per CU picks), or with
+   a model of the tiles per CU picks; from 20 rows its 128 by 32 tiles where there are
+   at least 128 of them), or with
    K > 4096 and up to 8 rows (16 with packed weights below 24 MB) the balanced long-K
    GEMV kernel (qw_gemv_w4a8_long_k); results are the same bits as the GEMV's. */
 int gemv_w4a8(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
@@ -180,8 +181,10 @@ int gemv_w4a8g(const float* X, const void* Wq, const float* w_scale, int64_t M, 
    Y[m][n] = f16(w_scale[n] * sum_k q[n][k] * x[m][k]), the sum in fp32.  The per-channel
    scale is applied after the sum, which equals dequantize-then-multiply up to fp32
    rounding.  M <= 2: GEMV kernel; M >= 3: f16 matrix-core GEMM on the exactly cast
-   weights (from 17 rows, where the output has at least 96 tiles, the tiled GEMM of
-   qw_gemm_w8a16_tile at the variant a model of the tiles per CU picks), except with K > 4096 and up to 8 rows (16 with weights below
+   weights (from 33 rows, where the output has at least 96 tiles, the tiled GEMM of
+   qw_gemm_w8a16_tile at the variant a model of the tiles per CU picks; from 12 rows
+   its 128 by 32 tiles where there are at least 128 of them), except with K > 4096 and
+   up to 8 rows (16 with weights below
    24 MB), where the balanced long-K GEMV variant runs (u = 7 of qw_gemv_w8a16_tiled).
    No workspace at any M (workspace may be NULL). */
 int gemv_w8a16(const uint16_t* X_f16, const void* Wq, const uint16_t* w_scale_f16, int64_t M,
@@ -298,7 +301,8 @@ int qw_gemm_w8a16_mfma(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
    variant 0: 256 by 256, eight waves; 1: 256 by 128, eight waves; 2: 128 by 128, four
    waves; 3: 128 by 128, two groups of four waves splitting each stage's k; 4: 128 by 64,
    four waves; 5: 128 by 64, two groups of four waves; 6: 64 by 64, four waves; 7: as 5
-   with stages of 128 bytes of weights per row instead of 64.  The INT8
+   with stages of 128 bytes of weights per row instead of 64; 8: 128 by 32, four waves,
+   stages of 128 bytes.  The INT8
    weights stay INT8 in LDS and each operand is cast to f16 after it is read.  Same
    arguments and limits as gemv_w8a16; no workspace.  QW_ERR_TILING for another
    variant. */

@@ -38,7 +38,7 @@ def host(t):
     return t.cpu().numpy()
 
 
-VARIANTS = tuple(range(8))
+VARIANTS = tuple(range(9))
 SHAPES = [(130, 300, 1056), (64, 128, 4096), (1, 96, 512), (257, 1000, 2080), (300, 37, 96),
           (65, 4100, 3584), (200, 513, 544), (17, 2050, 18944)]
 
@@ -135,14 +135,15 @@ def test_w4a8_tile_sweep_shape_sampled(M):
         assert np.array_equal(host(Y[:, ridx]).view(np.uint32), ref["Y"].view(np.uint32)), v
 
 
-# The default entry points route to the tiled GEMM from 17 (W8A16) or 33 (W4A8) rows of
-# X where the output has at least 96 tiles, choosing the variant by a model of the tiles
-# on the busiest CU.  On the 256-CU MI355X these shapes reach variants 6, 7, 3 (W4A8: 2),
-# 1, 0, 6, 7, 0, 3 (W4A8: 2), the balanced kernels (3000 rows of W), and at 24 rows
-# variant 6 for W8A16 beside the balanced W4A8 kernel.  Checked on sampled rows of W.
+# The default entry points route to the tiled GEMM from 33 rows of X where the output has
+# at least 96 tiles, choosing the variant by a model of the tiles on the busiest CU, and
+# from 12 (W8A16) or 20 (W4A8) rows where there are at least 128 tiles of 128 x 32.  On
+# the 256-CU MI355X these shapes reach variants 8, 7, 8, 1, 0, 8, 8, 0, 3 (W4A8: 2), the
+# balanced kernels (3000 rows of W at 40 rows, 9000 at 24), and variant 8 at 24 rows.
+# Checked on sampled rows of W.
 ROUTED = [(40, 9000, 1056), (40, 20000, 544), (70, 20000, 2080), (70, 34000, 512), (520, 20000, 512),
           (70, 6000, 4096), (70, 9000, 1056), (130, 34000, 512), (520, 6000, 544), (40, 3000, 18944),
-          (24, 9000, 1056)]
+          (24, 9000, 1056), (24, 20000, 1056)]
 
 
 @pytest.mark.parametrize("M,N,K", ROUTED)

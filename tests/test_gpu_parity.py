@@ -39,6 +39,16 @@ def host(t):
     return t.cpu().numpy()
 
 
+def routed_to_tile(bits, M, N):
+    """Whether gemv_w4a8 / gemv_w8a16 send M rows to the tiled GEMM (its routing rule):
+    from 33 rows where some variant has at least 96 tiles (the most tiles: 64 x 64 or
+    128 x 32), below that from 12 (W8A16) or 20 (W4A8) rows where there are at least
+    128 tiles of 128 x 32."""
+    if M < 33:
+        return M >= (12 if bits == 8 else 20) and -(-N // 128) >= 128
+    return max(-(-N // 64) * -(-M // 64), -(-N // 128) * -(-M // 32)) >= 96
+
+
 def say(*a):
     print(*a, flush=True)
 
@@ -397,9 +407,13 @@ def test_balanced_w8a16_matrix_core_kernel_matches_oracle(M, N, K):
     assert np.all(np.isfinite(y.astype(np.float32)))
     ys = host(qw.gemm_w8a16_mfma(Xd, Wq8, s16, 8, 1, 1))
     check_w8a16(ys, X16, q8, s16_o, y64)
-    # the default path at these rows is the balanced kernel
+    # the default path at these rows is the balanced kernel, unless there are enough
+    # tiles of 128 x 32 for the tiled GEMM
     yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
-    assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
+    if routed_to_tile(8, M, N):
+        check_w8a16(yd, X16, q8, s16_o, y64)
+    else:
+        assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 
 
 W8_BALANCED_MULTI_SHAPES = [(17, 1000, 1056), (32, 27392, 4096), (40, 600, 544), (64, 4100, 3584),
@@ -425,9 +439,9 @@ def test_balanced_w8a16_two_block_kernel_matches_oracle(M, N, K):
         assert np.array_equal(y.view(np.uint16), y1.view(np.uint16))
     yd = host(qw.gemv_w8a16(Xd, Wq8, s16))
     check_w8a16(yd, X16, q8, s16_o, y64)
-    # the default path at 17 to 64 rows is this kernel, except where the tiled GEMM has
-    # at least 96 tiles of its smallest variant (64 x 64)
-    tiled = M >= 17 and -(-N // 64) * -(-M // 64) >= 96
+    # the default path at 17 to 64 rows is this kernel, except where the tiled GEMM
+    # takes the rows
+    tiled = routed_to_tile(8, M, N)
     if M <= 64 and not tiled:
         assert np.array_equal(yd.view(np.uint16), y.view(np.uint16))
 

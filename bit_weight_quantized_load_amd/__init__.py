@@ -55,6 +55,7 @@ SIGNATURES = {
     "qw_gemm_w8a16_mfma": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _I, _I, _P]),
     "qw_gemm_w8a16_tile": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "qw_gemm_w4a8_tile": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P, _SZ, _I, _P]),
+    "qw_tile_variant": (_I, [_I, _I64, _I64]),
     "qw_w4g_scale_bytes": (_SZ, [_I64, _I64, _I64]),
     "quantize_pack_w4g": (_I, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "qw_w4g_scales": (_I, [_P, _I64, _I64, _I64, _P, _P]),

@@ -1180,6 +1180,13 @@ int qw_gemm_w8a16_tile(const uint16_t* X_f16, const void* Wq, const uint16_t* w_
                                                  variant, static_cast<hipStream_t>(stream)));
 }
 
+int qw_tile_variant(int bits, int64_t M, int64_t N)
+{
+    if ((bits != 4 && bits != 8) || M < 1 || N < 1)
+        return -1;
+    return tile_variant(bits, M, N);
+}
+
 int qw_gemm_w4a8_tile(const float* X, const void* Wq, const float* w_scale, int64_t M, int64_t N,
                       int64_t K, float* Y, void* workspace, size_t ws_bytes, int variant,
                       void* stream)

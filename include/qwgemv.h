@@ -321,6 +321,13 @@ int qw_gemm_w4a8_tile(const float* X, const void* Wq, const float* w_scale, int6
                       int64_t K, float* Y, void* workspace, size_t ws_bytes, int variant,
                       void* stream);
 
+/* The launch variant of the tiled GEMM that gemv_w4a8 (bits 4) and gemv_w8a16 (bits 8)
+   take on their matrix-core path (M >= 2 for W4A8, M >= 3 for W8A16, outside the long-K
+   rows) for M rows of X and N rows of W on the current device, or -1 where the balanced
+   matrix-core kernels run instead.  With no device visible the model assumes 256 CUs.
+   A host-side query: no HIP call other than the device's CU count. */
+int qw_tile_variant(int bits, int64_t M, int64_t N);
+
 /* The two ablations the INT4 write-up times beside its INT4-weight / INT8-activation
    path ("Jetson Orin AGX 上的 INT4 量化推理实践", section 速度结果), as M == 1 GEMVs with
    K <= 4096 (QW_ERR_SHAPE otherwise); not part of the quantized linear itself.

@@ -33,7 +33,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 33
+    assert len(names) == 34
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -282,3 +282,30 @@ def test_noalloc_w4a8_checks_arguments_and_its_limit_on_the_host():
     assert L.qw_workspace_bytes(0, 512, 64, 16320) <= 8 << 20 < L.qw_workspace_bytes(0, 512, 64, 16384)
     assert f(A, A2, A3, 512, 64, 16384, A4, NULL) == qw.QW_ERR_WORKSPACE
     assert f(A, A2, A3, 4096, 64, 4096, A4, NULL) == qw.QW_ERR_WORKSPACE
+
+
+def test_tile_routing_choices():
+    """The tiled-GEMM routing (qw_tile_variant, the choice gemv_w4a8 / gemv_w8a16 make on
+    their matrix-core path) for the 256-CU model used without a visible device: the
+    documented choices and the shapes the GPU routing test relies on."""
+    v = L.qw_tile_variant
+    # W8A16 on 4096 -> 27392: 128 x 32 tiles from 12 rows, then by the tile model
+    assert [v(8, M, 27392) for M in (9, 11, 12, 16, 32)] == [-1, -1, 8, 8, 8]
+    assert [v(8, M, 27392) for M in (33, 64, 128, 256, 512)] == [7, 7, 3, 1, 0]
+    # W4A8: 128 x 32 tiles from 20 rows, the tile model from 33
+    assert [v(4, M, 27392) for M in (16, 19, 20, 32)] == [-1, -1, 8, 8]
+    assert [v(4, M, 27392) for M in (64, 128, 256, 512)] == [7, 2, 1, 0]
+    # fewer than 128 tiles of 128 x 32 below 33 rows: the balanced kernels
+    assert v(8, 16, 9000) == -1 and v(8, 24, 9000) == -1 and v(4, 24, 9000) == -1
+    assert v(8, 16, 16256) == -1 and v(8, 16, 16257) == 8
+    # 4096 -> 9000 from 33 rows, 3584 -> 18944 at 96 rows
+    assert [v(8, M, 9000) for M in (48, 64, 96, 128)] == [8, 8, 8, 7]
+    assert v(8, 96, 18944) == 8 and v(4, 96, 18944) == 8
+    # the default-path shapes of the GPU routing test
+    routed = [(40, 9000), (40, 20000), (70, 20000), (70, 34000), (520, 20000), (70, 6000),
+              (70, 9000), (130, 34000), (520, 6000), (40, 3000), (24, 9000), (24, 20000)]
+    assert [v(8, M, N) for M, N in routed] == [8, 7, 8, 1, 0, 8, 8, 0, 3, -1, -1, 8]
+    assert [v(4, M, N) for M, N in routed] == [8, 7, 8, 1, 0, 8, 8, 0, 2, -1, -1, 8]
+    # at least 96 tiles: narrow outputs stay on the balanced kernels at any M
+    assert v(8, 64, 3584) == -1 and v(4, 64, 3584) == -1
+    assert v(3, 64, 27392) == -1 and v(8, 0, 27392) == -1

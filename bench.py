@@ -65,7 +65,7 @@ def kernel_source_hash(kernel: str) -> str:
     import re
 
     csrc = os.path.join(ROOT, "bit_weight_quantized_load_amd", "csrc")
-    files = ["common.hpp", "kernels.hpp", "api.hip"]
+    files = ["common.hpp", "kernels.hpp", "gemv_shapes.hpp"]
     files += ["gemv_w4a8.hip", "w4a8_prod.hpp"] if kernel == "gemv_w4a8" else ["gemv_w8a16.hip"]
     h = hashlib.sha256()
     for f in files:

@@ -938,8 +938,8 @@ int qw_stream_read(const void* src, size_t bytes, uint32_t* sink, int waves, int
     if (!(waves == 1 || waves == 2 || waves == 4 || waves == 8 || waves == 16) || blocks < 1 ||
         blocks > 65535 || !(u == 1 || u == 2 || u == 4 || u == 8 || u == 16))
         return QW_ERR_TILING;
-    // each workgroup's share addressed by one buffer resource, below 2^31 bytes
-    if ((words + (size_t)blocks - 1) / (size_t)blocks * 16u >= ((size_t)1 << 31))
+    // the whole buffer addressed by one buffer resource, below 2^31 bytes
+    if (bytes >= ((size_t)1 << 31))
         return QW_ERR_SHAPE;
     return hip_status(qw::launch_stream_read(static_cast<const uint8_t*>(src), words, waves, blocks,
                                              u, sink, static_cast<hipStream_t>(stream)));

@@ -6,9 +6,12 @@
 // 16-byte loads (the non-temporal hint of the weight stream) and folds them into one
 // 32-bit word per workgroup, so the loads cannot be dropped; it computes nothing else.
 //
-// Work split: `blocks` workgroups of `waves` waves; workgroup b owns an even share of the
-// 16-byte words (the first `rem` get one more), read as batches of U loads per lane, all U
-// requested before any is used.  Past the end, buffer loads return zeros.
+// Work split: `blocks` workgroups of `waves` waves read batches of U loads per lane, all U
+// requested before any is used; batch i of workgroup b is the (i blocks + b)-th run of
+// U x (threads) 16-byte words, so that the grid sweeps the buffer as one moving window
+// (2-4% faster than an even contiguous share per workgroup: 34 MB in 7.05 against 7.20
+// us, 68 MB in 11.54 against 11.92, 112 MB in 17.7 against 18.5).  Past the end, buffer
+// loads return zeros.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -17,16 +20,15 @@ namespace qw {
 namespace {
 
 template <int U>
-__global__ __launch_bounds__(1024) void k_stream_read(const uint8_t* __restrict__ src, int per,
-                                                      int rem, uint32_t* __restrict__ sink)
+__global__ __launch_bounds__(1024) void k_stream_read(const uint8_t* __restrict__ src, int words,
+                                                      uint32_t* __restrict__ sink)
 {
     const int b = blockIdx.x;
-    const int w0 = rg_of(b, per, rem);              // first 16-byte word of the workgroup
-    const int nw = rg_of(b + 1, per, rem) - w0;     // words of the workgroup
-    const rsrc_t r = make_rsrc(src + (size_t)w0 * 16u, (uint32_t)nw * 16u);
     const int T = (int)blockDim.x;
+    const rsrc_t r = make_rsrc(src, (uint32_t)words * 16u);
+    const int step = (int)gridDim.x * U * T;  // words per sweep of the grid
     uint32_t acc = 0;
-    for (int base = 0; base < nw; base += U * T) {
+    for (int base = b * U * T; base < words; base += step) {
         uint4 v[U];
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -55,14 +57,14 @@ __global__ __launch_bounds__(1024) void k_stream_read(const uint8_t* __restrict_
 hipError_t launch_stream_read(const uint8_t* src, size_t words, int waves, int blocks, int u,
                               uint32_t* sink, hipStream_t st)
 {
-    const int per = (int)(words / (size_t)blocks), rem = (int)(words % (size_t)blocks);
+    const int w = (int)words;
     const dim3 g(blocks), t(64 * waves);
     switch (u) {
-    case 1: hipLaunchKernelGGL(k_stream_read<1>, g, t, 0, st, src, per, rem, sink); break;
-    case 2: hipLaunchKernelGGL(k_stream_read<2>, g, t, 0, st, src, per, rem, sink); break;
-    case 4: hipLaunchKernelGGL(k_stream_read<4>, g, t, 0, st, src, per, rem, sink); break;
-    case 8: hipLaunchKernelGGL(k_stream_read<8>, g, t, 0, st, src, per, rem, sink); break;
-    case 16: hipLaunchKernelGGL(k_stream_read<16>, g, t, 0, st, src, per, rem, sink); break;
+    case 1: hipLaunchKernelGGL(k_stream_read<1>, g, t, 0, st, src, w, sink); break;
+    case 2: hipLaunchKernelGGL(k_stream_read<2>, g, t, 0, st, src, w, sink); break;
+    case 4: hipLaunchKernelGGL(k_stream_read<4>, g, t, 0, st, src, w, sink); break;
+    case 8: hipLaunchKernelGGL(k_stream_read<8>, g, t, 0, st, src, w, sink); break;
+    case 16: hipLaunchKernelGGL(k_stream_read<16>, g, t, 0, st, src, w, sink); break;
     default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -366,9 +366,10 @@ int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k);
    bytes: decode is memory-bound and GEMV-dominated ("Jetson Orin AGX 上的 INT4
    量化推理实践", section 为什么这个结果有意义).  Launch shape: `blocks` workgroups
    (0: one per compute unit) of `waves` waves (1, 2, 4, 8 or 16; 0: 8), each lane with
-   `loads_in_flight` loads requested before use (1, 2, 4, 8 or 16; 0: 4); the bytes are
-   split evenly over the workgroups.  QW_ERR_SHAPE for 0 or a non-multiple of 16 bytes or
-   a workgroup share of 2 GiB or more, QW_ERR_TILING for another launch shape. */
+   `loads_in_flight` loads requested before use (1, 2, 4, 8 or 16; 0: 4); the grid reads
+   the buffer front to back as one moving window, each workgroup taking every blocks-th
+   run of loads.  QW_ERR_SHAPE for 0, a non-multiple of 16 bytes or 2 GiB or more,
+   QW_ERR_TILING for another launch shape. */
 int qw_stream_read(const void* src, size_t bytes, uint32_t* sink, int waves, int blocks,
                    int loads_in_flight, void* stream);
 

@@ -319,14 +319,25 @@ constexpr int kXAllMaxBytes = 64 * 1024;
 // area into A operands and multiplied against them, and the unit's int32 sums are
 // added into the workgroup's LDS totals (integer adds: exact in any order).  After one
 // more barrier the workgroup writes its outputs, consecutive threads on consecutive n.
+//
+// FR > 0 (fused quantization of up to FR rows of X, 8 waves): instead of reading codes
+// that a separate pre-pass launch wrote, the workgroup requests the rows of X itself
+// (fp32, before its first weights), takes each row's maximum (a wave reduction, one
+// value per wave in LDS, the maximum of those), and writes the codes straight into the LDS operand layout
+// with quant4_e, the same codes and scales as quant_act_i8.  Rows past M in the block
+// of 16 are left unwritten: they only reach outputs that are never stored.
 constexpr int kBalMaxBlocks = 40;      // output blocks per workgroup (LDS totals)
 constexpr int kBalSumPitch = 17;       // int32 per row of m in the LDS totals
+constexpr int kFqRows = 4;             // most rows of X the fused prologue takes
 
-template <int NW, int U>
+template <int NW, int U, int FR>
 __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
 {
     constexpr int kThreads = 64 * NW;
     constexpr int kXP = kXAllMaxBytes / 16 / kThreads;  // 16-byte X pieces per thread
+    constexpr bool FQ = FR > 0;
+    constexpr int kFV = 4096 / 4 / kThreads;            // FQ: float4 per thread per row (K <= 4096)
+    static_assert(!FQ || (NW == 8 && FR <= kFqRows), "the fused prologue: 8 waves, up to kFqRows rows");
     constexpr int kScales = 4 * 4 * kBalMaxBlocks;       // row scales of the workgroup
     constexpr int kSP = (kScales + kThreads - 1) / kThreads;
     // LDS: X [CG steps][8 KB], per wave 4 padded tiles, the int32 totals
@@ -357,6 +368,7 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
     int* s_sum = reinterpret_cast<int*>(s_mem + xbytes + NW * 4 * kW4TilePitch);
     float* s_sc = reinterpret_cast<float*>(s_sum + p.nbmax * 16 * kBalSumPitch);
     float* s_a = s_sc + 4 * 4 * p.nbmax;
+    float* s_wmax = s_a + 16;  // FQ: [wave][row] maxima
 
     // (step, block) of the wave's unit u, step-major: c = (u0 + u) / nb
     const int c0 = u0 / nb, blk0 = u0 - c0 * nb;
@@ -373,31 +385,89 @@ __global__ __launch_bounds__(64 * NW) void k_gemm_w4a8_bal(MfmaW4A8Args p)
                                                    : 0x80000000u);                               \
     }
 
-    uint4 xr[kXP];
+    uint4 xr[FQ ? 1 : kXP];
+    float4 xf[FQ ? FR : 1][FQ ? kFV : 1];  // FQ: float4 v of row m: k = 4 (v T + tid)
+    const int K4 = p.K >> 2;
+    if constexpr (FQ) {
+        const rsrc_t xfr = make_rsrc(p.X + (size_t)16 * mb * p.K, (uint32_t)(mv * p.K) * 4u);
 #pragma unroll
-    for (int v = 0; v < kXP; ++v) {
-        const int pc = v * kThreads + tid;
-        xr[v] = load16(xres, pc * 16 < xbytes ? (uint32_t)pc * 16u : 0x80000000u);
+        for (int m = 0; m < FR; ++m)
+#pragma unroll
+            for (int v = 0; v < kFV; ++v) {
+                const int f = v * kThreads + tid;
+                xf[m][v] = load16f(xfr, m < mv && f < K4 ? (uint32_t)(m * p.K + 4 * f) * 4u : 0x80000000u);
+            }
+    } else {
+#pragma unroll
+        for (int v = 0; v < kXP; ++v) {
+            const int pc = v * kThreads + tid;
+            xr[v] = load16(xres, pc * 16 < xbytes ? (uint32_t)pc * 16u : 0x80000000u);
+        }
     }
     uint32_t sr[kSP];
 #pragma unroll
     for (int v = 0; v < kSP; ++v)
         sr[v] = load4(sres, (uint32_t)(v * kThreads + tid) * 4u);
-    const uint32_t ar = load4(ares, (uint32_t)(tid & 15) * 4u);
+    const uint32_t ar = FQ ? 0u : load4(ares, (uint32_t)(tid & 15) * 4u);
     issue_barrier();
     QW_LOADU(0);
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (FQ) {
+        // each row's maximum |x|: per wave, then over the waves
 #pragma unroll
-    for (int v = 0; v < kXP; ++v) {
-        const int pc = v * kThreads + tid;
-        if (pc * 16 < xbytes)
-            *reinterpret_cast<uint4*>(s_x + (size_t)pc * 16) = xr[v];
+        for (int m = 0; m < FR; ++m) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int v = 0; v < kFV; ++v)
+                mx = fmaxf(mx, max_abs4(xf[m][v]));
+            mx = wave_max_dpp(mx);
+            if (lane == 0)
+                s_wmax[wave * FR + m] = mx;
+        }
+        __syncthreads();
+        // codes of 64-k step st, lane group g (16 k), row m at st 1024 + g 256 + m 16:
+        // bytes 0-3 the even k of its first 8, 4-7 their odd k, 8-15 the same for the
+        // next 8; a float4 (k = 4f .. 4f + 3, quarter h of the 16) gives two 16-bit pairs
+#pragma unroll
+        for (int m = 0; m < FR; ++m) {
+            if (m < mv) {
+                float mxm = s_wmax[m];
+#pragma unroll
+                for (int w = 1; w < NW; ++w)
+                    mxm = fmaxf(mxm, s_wmax[w * FR + m]);
+                const float a = mxm / 127.0f;
+                const float r = 1.0f / a;
+                const bool fast = r <= 3.0e38f;
+                if (tid == 0)
+                    s_a[m] = a;
+#pragma unroll
+                for (int v = 0; v < kFV; ++v) {
+                    const int f = v * kThreads + tid;
+                    if (f < CG * 128) {  // whole 512-k steps; past K, X read zeros
+                        uint32_t e[4];
+                        if (quant4_e(xf[m][v], r, e) || !fast)
+                            quant4_e_div(xf[m][v], a, e);
+                        const int st = f >> 4, g4 = (f >> 2) & 3, h = f & 3;
+                        uint8_t* d = s_x + (size_t)st * 1024 + g4 * 256 + m * 16 + (h & 1) * 2 + (h >> 1) * 8;
+                        *reinterpret_cast<uint16_t*>(d) = (uint16_t)__builtin_amdgcn_perm(e[2], e[0], 0x0C0C0602u);
+                        *reinterpret_cast<uint16_t*>(d + 4) = (uint16_t)__builtin_amdgcn_perm(e[3], e[1], 0x0C0C0602u);
+                    }
+                }
+            }
+        }
+    } else {
+#pragma unroll
+        for (int v = 0; v < kXP; ++v) {
+            const int pc = v * kThreads + tid;
+            if (pc * 16 < xbytes)
+                *reinterpret_cast<uint4*>(s_x + (size_t)pc * 16) = xr[v];
+        }
     }
 #pragma unroll
     for (int v = 0; v < kSP; ++v)
         if (v * kThreads + tid < 4 * 4 * p.nbmax)
             s_sc[v * kThreads + tid] = __uint_as_float(sr[v]);
-    if (tid < 16)
+    if (!FQ && tid < 16)
         s_a[tid] = __uint_as_float(ar);
     for (int e = tid; e < nb * 16 * kBalSumPitch; e += kThreads)
         s_sum[e] = 0;
@@ -1034,16 +1104,16 @@ hipError_t go_w4(const MfmaW4A8Args& p, hipStream_t st)
     return hipGetLastError();
 }
 
-template <int NW, int U>
+template <int NW, int U, int FR>
 hipError_t go_w4_bal_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t st)
 {
     // once per kernel, before its first launch
-    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bal<NW, U>),
+    static const hipError_t e = allow_lds(reinterpret_cast<const void*>(k_gemm_w4a8_bal<NW, U, FR>),
                                           (size_t)kXAllMaxBytes + (size_t)NW * 4 * kW4TilePitch +
-                                              (size_t)kBalMaxBlocks * (16 * kBalSumPitch + 16) * 4 + 64);
+                                              (size_t)kBalMaxBlocks * (16 * kBalSumPitch + 16) * 4 + 64 + 4 * NW * kFqRows);
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL((k_gemm_w4a8_bal<NW, U>), dim3((unsigned)nwg, (unsigned)p.mbtot),
+    hipLaunchKernelGGL((k_gemm_w4a8_bal<NW, U, FR>), dim3((unsigned)nwg, (unsigned)p.mbtot),
                        dim3(64 * NW), lds, st, p);
     return hipGetLastError();
 }
@@ -1051,10 +1121,12 @@ hipError_t go_w4_bal_u(const MfmaW4A8Args& p, int nwg, size_t lds, hipStream_t s
 // Units per wave the balanced kernel is built for.
 constexpr int kBalMaxUnits = 16;
 
-template <int NW>
+template <int NW, int FR = 0>
 hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
 {
     if ((size_t)p.cg * 8 * 1024 > (size_t)kXAllMaxBytes || p.mbtot > 65535)
+        return hipErrorInvalidValue;
+    if (FR > 0 && (p.M > FR || p.K > 4096 || p.X == nullptr))
         return hipErrorInvalidValue;
     // one workgroup per CU with at least four row groups each; more workgroups when a
     // wave would take more than kBalMaxUnits units or the totals more than
@@ -1068,12 +1140,12 @@ hipError_t go_w4_bal(MfmaW4A8Args p, int cus, hipStream_t st)
     p.mgroups = p.mbtot;
     const int umax = (p.nbmax * p.cg + NW - 1) / NW;
     const size_t lds = (size_t)p.cg * 8 * 1024 + (size_t)NW * 4 * kW4TilePitch +
-                       (size_t)p.nbmax * (16 * kBalSumPitch + 16) * 4 + 64;
+                       (size_t)p.nbmax * (16 * kBalSumPitch + 16) * 4 + 64 + 4 * NW * FR;
     if (umax <= 4)
-        return go_w4_bal_u<NW, 4>(p, nwg, lds, st);
+        return go_w4_bal_u<NW, 4, FR>(p, nwg, lds, st);
     if (umax <= 8)
-        return go_w4_bal_u<NW, 8>(p, nwg, lds, st);
-    return go_w4_bal_u<NW, 16>(p, nwg, lds, st);
+        return go_w4_bal_u<NW, 8, FR>(p, nwg, lds, st);
+    return go_w4_bal_u<NW, 16, FR>(p, nwg, lds, st);
 }
 
 template <int U, bool PAIR>
@@ -1241,6 +1313,26 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     uint8_t* xp = static_cast<uint8_t*>(workspace);
     const size_t xp_bytes = ((size_t)mbtot * ks * 1024u + 255u) & ~(size_t)255u;
     float* a = reinterpret_cast<float*>(xp + xp_bytes);
+    MfmaW4A8Args p;
+    p.X = X;
+    p.Xp = xp;
+    p.a_scale = a;
+    p.Wq = Wq;
+    p.w_scale = w_scale;
+    p.Y = Y;
+    p.M = M;
+    p.N = N;
+    p.K = K;
+    p.cg = L.cg;
+    p.nrg = L.nrg;
+    p.ks = ks;
+    p.mbtot = mbtot;
+    // up to 4 rows on the 8-wave balanced kernel: it quantizes X itself, no pre-pass
+    // launch (4096 -> 27392: 11.8 / 12.3 / 12.7 us at 2 / 3 / 4 rows against 14.5-14.8
+    // with the pre-pass, which took 4.3 us of them; 8 rows in the prologue measured
+    // slower than the pre-pass)
+    if (mb == 0 && nbw != 2 && nw == 8 && M <= kFqRows && K <= 4096)
+        return M <= 2 ? go_w4_bal<8, 2>(p, cus, st) : go_w4_bal<8, 4>(p, cus, st);
     const int qgrid = mbtot * 16 < 65536 ? mbtot * 16 : 65536;
     const int ns = (ks * 4 + kBlock - 1) / kBlock;  // 16-code slots per thread of 256
     const int ns_wide = (ks * 4 + 1023) / 1024;      // ... of 1024 (at most 4: K <= 65536)
@@ -1264,19 +1356,6 @@ hipError_t launch_gemm_w4a8(const float* X, int M, int N, int K, const uint8_t* 
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    MfmaW4A8Args p;
-    p.Xp = xp;
-    p.a_scale = a;
-    p.Wq = Wq;
-    p.w_scale = w_scale;
-    p.Y = Y;
-    p.M = M;
-    p.N = N;
-    p.K = K;
-    p.cg = L.cg;
-    p.nrg = L.nrg;
-    p.ks = ks;
-    p.mbtot = mbtot;
     if (mb == 0) {  // balanced: one workgroup per CU, X codes of one block resident in LDS
         if (nbw == 2)  // one wave per 512-k step, weights held in registers across the blocks
             return nw == 8 ? go_w4_bals(p, cus, st) : hipErrorInvalidValue;

@@ -136,6 +136,7 @@ constexpr int kMfmaMinM4 = 2;
 constexpr int kMfmaMinM8 = 3;
 
 struct MfmaW4A8Args {
+    const float* X;         // [M][K] fp32: read only by the balanced kernel's fused prologue
     const uint8_t* Xp;      // X codes in MFMA operand order (workspace)
     const float* a_scale;   // [M] (workspace)
     const uint8_t* Wq;

@@ -309,6 +309,29 @@ def test_long_k_row_prepass_ties_and_near_ties(M, K):
     assert np.array_equal(bits(host(Y)), bits(ref["Y"]))
 
 
+@pytest.mark.parametrize("M,K", [(2, 4096), (3, 3584), (4, 1056), (4, 4096), (1, 512)])
+def test_balanced_fused_prologue_ties_and_near_ties(M, K):
+    """Up to 4 rows, the balanced matrix-core kernel quantizes X in its own prologue
+    (no pre-pass launch): with tie and near-tie activations, and an all-zero row at 4
+    rows, its outputs (exact int32 sums, fixed epilogue) equal the oracle's bit for bit
+    on the default path and at an explicit launch shape."""
+    say("balanced fused prologue edges", M, K)
+    X = _act_edges(max(M, 6), K, 100 + K)[:M]
+    N = 300
+    rng = np.random.default_rng(K + 3)
+    W = (rng.standard_normal((N, K)) * 0.02).astype(np.float32)
+    Wq, s = qw.quantize_pack_w4(dev(W))
+    q_o, s_o = oracle.quant_w4(W)
+    ref = oracle.gemv_w4a8(X, q_o, s_o)
+    ws = qw.make_workspace("w4a8", M, N, K)
+    if M >= 2:
+        Y = qw.gemv_w4a8(dev(X), Wq, s, workspace=ws)
+        assert np.array_equal(bits(host(Y)), bits(ref["Y"]))
+    Y8 = qw.gemm_w4a8_mfma(dev(X), Wq, s, 8, 0, 1,
+                           workspace=ws if ws is not None else qw.make_workspace("w4a8", 2, N, K))
+    assert np.array_equal(bits(host(Y8)), bits(ref["Y"]))
+
+
 UNPACK_ORDER = [0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15]  # k offset of byte i
 
 

@@ -45,8 +45,11 @@ __device__ __forceinline__ uint32_t wave_sum_u32_dpp(uint32_t v)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// NW waves per row, V 16-byte loads (4 logits) per thread: L <= 256 * NW * V.
-template <int NW, int V>
+// NW waves per row, V 16-byte loads (4 logits) per thread: L <= 256 * NW * V.  MAG: the
+// index by one multiply-high (IndexSoftmaxArgs::magic) instead of the float estimate and
+// its threshold corrections (half the vector instructions and two thirds of the LDS reads
+// per logit).
+template <int NW, int V, bool MAG>
 __global__ __launch_bounds__(64 * NW) void k_index_softmax(const int32_t* __restrict__ A,
                                                            int64_t L, IndexSoftmaxArgs t,
                                                            uint8_t* __restrict__ P)
@@ -101,12 +104,17 @@ __global__ __launch_bounds__(64 * NW) void k_index_softmax(const int32_t* __rest
             // mx >= v: the difference is exact as an unsigned 32-bit number
             uint32_t d = (uint32_t)mx - (uint32_t)v4[u];
             d = d < cint ? d : cint;
-            uint32_t k = (uint32_t)((float)d * t.scale + 0.5f);
-            k = k < (uint32_t)n ? k : (uint32_t)n;
-            if (k > 0 && d < s_thr[k])
-                --k;
-            else if (k < (uint32_t)n && d >= s_thr[k + 1])
-                ++k;
+            uint32_t k;
+            if constexpr (MAG) {
+                k = __umulhi(__umul24(d, 2u * (uint32_t)n) + cint, t.magic) >> t.shift;
+            } else {
+                k = (uint32_t)((float)d * t.scale + 0.5f);
+                k = k < (uint32_t)n ? k : (uint32_t)n;
+                if (k > 0 && d < s_thr[k])
+                    --k;
+                else if (k < (uint32_t)n && d >= s_thr[k + 1])
+                    ++k;
+            }
             if (e + u < L)
                 sum += s_lut[k];
             packed |= k << (8 * u);
@@ -149,8 +157,12 @@ template <int NW, int V>
 hipError_t launch_is(const int32_t* A, int64_t rows, int64_t L, const IndexSoftmaxArgs& t,
                      uint8_t* P, hipStream_t st)
 {
-    hipLaunchKernelGGL((k_index_softmax<NW, V>), dim3((unsigned)rows), dim3(64 * NW), 0, st, A, L,
-                       t, P);
+    if (t.magic != 0)
+        hipLaunchKernelGGL((k_index_softmax<NW, V, true>), dim3((unsigned)rows), dim3(64 * NW), 0, st,
+                           A, L, t, P);
+    else
+        hipLaunchKernelGGL((k_index_softmax<NW, V, false>), dim3((unsigned)rows), dim3(64 * NW), 0,
+                           st, A, L, t, P);
     return hipGetLastError();
 }
 

@@ -231,6 +231,10 @@ struct IndexSoftmaxArgs {
     int32_t c_int;
     int b;
     float scale;  // n / c_int, for the index estimate
+    // exact index by multiplication: idx = mulhi(2 n D' + c_int, magic) >> shift, valid when
+    // c_int < 2^24 and c_int (2n + 1) < 2^31 (magic = 0 otherwise: the threshold path)
+    uint32_t magic;
+    int shift;
     uint32_t thr[64];
     uint32_t lut[64];
 };

@@ -2,7 +2,8 @@
 section 基准/方法设计) with the CPU oracle: integer work, so bit-exact, on logits over the
 whole int32 range (the row maximum minus a logit overflows int32 and must not wrap),
 attention-like peaked rows, constant rows, one-element rows, ragged lengths up to 16384,
-and b = 4, 5, 6 with thresholds from 1 to 2^31 - 1.
+and b = 4, 5, 6 with thresholds from 1 to 2^31 - 1 (on both sides of the bound of the
+exact multiply-high index, c_int < 2^24 and c_int (2n + 1) < 2^31, and a power of two).
 """
 import numpy as np
 import pytest
@@ -54,7 +55,8 @@ def test_index_softmax_bit_exact(rows, L, kind):
     print("index_softmax", kind, rows, L, flush=True)
     A = logits(kind, rows, L, rows * 1000 + L)
     Ad = dev(A)
-    for (b, ci) in ((5, 124451), (5, 1), (4, 62), (6, 2**31 - 1), (5, 3 * 10**6)):
+    for (b, ci) in ((5, 124451), (5, 1), (4, 62), (6, 2**31 - 1), (5, 3 * 10**6), (6, 2**20),
+                    (4, 2**24 - 1), (4, 2**24)):
         P = host(qw.index_softmax(Ad, ci, b=b, c=6.6))
         Po, rs = oracle.index_softmax(A, ci, b=b, c=6.6)
         assert np.array_equal(P, Po), (b, ci)

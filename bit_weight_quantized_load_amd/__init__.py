@@ -65,6 +65,7 @@ SIGNATURES = {
     "qw_gemv_w4f32": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _I, _P]),
     "index_softmax": (_I, [_P, _I64, _I64, ctypes.c_int32, _I, ctypes.c_double, _P, _P]),
     "qw_index_cint": (ctypes.c_int32, [ctypes.c_double, _I64, ctypes.c_double, ctypes.c_double]),
+    "qw_index_magic": (_I, [ctypes.c_int32, _I, _P, _P]),
     "qw_status_str": (ctypes.c_char_p, [_I]),
     "qw_last_hip_error": (_I, []),
     "qw_device_status": (_I, [_P, _I]),

@@ -624,6 +624,35 @@ int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k)
     return (int32_t)std::llround(v);
 }
 
+int qw_index_magic(int32_t c_int, int b, uint32_t* magic, int* shift)
+{
+    // idx = round(D' n / c_int) half up = floor(x / d), x = 2 n D' + c_int, d = 2 c_int.
+    // With s = floor(log2 d) and m = ceil(2^(32 + s) / d), m d = 2^(32 + s) + e, 0 <= e < d
+    // < 2^(s + 1), so for x < 2^31 the excess x e / 2^(32 + s) of x m / 2^(32 + s) over x / d
+    // stays below 1 / d and floor(mulhi(x, m) / 2^s) = floor(x / d); d a power of two takes
+    // m = 2^31 with s - 1.  x < 2^31 for every D' <= c_int when c_int (2n + 1) < 2^31, and
+    // the kernel forms 2 n D' with a 24-bit multiply (c_int < 2^24).
+    if (!magic || !shift || b < 4 || b > 6 || c_int < 1)
+        return 0;
+    const int n = (1 << b) - 1;
+    if (!(c_int < (1 << 24) && (int64_t)c_int * (2 * n + 1) < ((int64_t)1 << 31)))
+        return 0;
+    const uint64_t d = 2 * (uint64_t)c_int;
+    int sh = 0;
+    while ((d >> (sh + 1)) != 0)
+        ++sh;
+    const unsigned __int128 num = (unsigned __int128)1 << (32 + sh);
+    const uint64_t m = (uint64_t)((num + d - 1) / d);
+    if (m >= ((uint64_t)1 << 32)) {
+        *magic = 1u << 31;
+        *shift = sh - 1;
+    } else {
+        *magic = (uint32_t)m;
+        *shift = sh;
+    }
+    return 1;
+}
+
 int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b, double c,
                   uint8_t* P, void* stream)
 {
@@ -649,27 +678,9 @@ int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int 
         t.lut[i] = (uint32_t)std::lround(255.0 * std::exp(-c * (double)i / (double)n));
     for (int k = 1; k <= n; ++k)
         t.thr[k] = (uint32_t)(((int64_t)c_int * (2 * k - 1) + 2 * n - 1) / (2 * n));
-    // idx = round(D' n / c_int) half up = floor(x / d), x = 2 n D' + c_int, d = 2 c_int.
-    // With s = floor(log2 d) and m = ceil(2^(32 + s) / d), m d = 2^(32 + s) + e, 0 <= e < d
-    // < 2^(s + 1), so for x < 2^31 the excess x e / 2^(32 + s) of x m / 2^(32 + s) over x / d
-    // stays below 1 / d and floor(mulhi(x, m) / 2^s) = floor(x / d); d a power of two takes
-    // m = 2^31 with s - 1.
-    t.magic = 0;
-    t.shift = 0;
-    if (c_int < (1 << 24) && (int64_t)c_int * (2 * n + 1) < ((int64_t)1 << 31)) {
-        const uint64_t d = 2 * (uint64_t)c_int;
-        int sh = 0;
-        while ((d >> (sh + 1)) != 0)
-            ++sh;
-        const unsigned __int128 num = (unsigned __int128)1 << (32 + sh);
-        const uint64_t m = (uint64_t)((num + d - 1) / d);
-        if (m >= ((uint64_t)1 << 32)) {
-            t.magic = 1u << 31;
-            t.shift = sh - 1;
-        } else {
-            t.magic = (uint32_t)m;
-            t.shift = sh;
-        }
+    if (!qw_index_magic(c_int, b, &t.magic, &t.shift)) {
+        t.magic = 0;
+        t.shift = 0;
     }
     return hip_status(qw::launch_index_softmax(A, rows, L, t, P, static_cast<hipStream_t>(stream)));
 }

@@ -358,6 +358,13 @@ int qw_gemv_w4f32(const float* X, const void* Wq, const float* w_scale, int64_t 
 int index_softmax(const int32_t* A, int64_t rows, int64_t L, int32_t c_int, int b, double c,
                   uint8_t* P, void* stream);
 int32_t qw_index_cint(double c, int64_t d, double s_q, double s_k);
+/* Test helper: the table index the IndexSoftmax kernel computes without a division,
+   idx = (mulhi(2 n D' + c_int, magic) >> shift) = round(D' n / c_int) half up, exact for
+   0 <= D' <= c_int.  Writes magic and shift and returns 1 when c_int < 2^24 and
+   c_int (2n + 1) < 2^31 (the kernel then uses them); returns 0 otherwise (the kernel
+   then takes a float estimate corrected by thresholds) or for b outside 4..6, c_int < 1
+   or a NULL pointer. */
+int qw_index_magic(int32_t c_int, int b, uint32_t* magic, int* shift);
 
 /* Bandwidth reference (not part of the linear): a kernel that only streams `bytes`
    bytes (a multiple of 16) from src with 16-byte loads, each byte once, and writes one

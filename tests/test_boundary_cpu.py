@@ -4,6 +4,7 @@ import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 import bit_weight_quantized_load_amd as qw
@@ -33,7 +34,7 @@ def declared_functions():
 
 def test_every_declared_symbol_is_exported_and_bound():
     names = declared_functions()
-    assert len(names) == 34
+    assert len(names) == 35
     for n in names:
         assert hasattr(L, n), n
         assert n in qw.SIGNATURES, n
@@ -250,6 +251,44 @@ def test_index_softmax_checks_and_threshold():
     assert L.qw_index_cint(6.6, 128, 0.02, 0.03) == 124451      # 124450.79...
     assert L.qw_index_cint(6.6, 128, 0.0, 0.03) == -1
     assert L.qw_index_cint(6.6, 128, 1e-9, 1e-9) == -1          # beyond int32
+
+
+def test_index_magic_matches_the_rounded_ratio():
+    """The multiply-high table index of the IndexSoftmax kernel: for every c_int and b it
+    accepts, (mulhi(2 n D' + c_int, magic) >> shift) equals round(D' n / c_int) half up
+    (the integer definition) at D' = 0, c_int, both sides of every half-step and random
+    points; outside its bound it declines."""
+    rng = np.random.default_rng(7)
+    m = ctypes.c_uint32(0)
+    sh = ctypes.c_int(0)
+    cints = [1, 2, 3, 5, 62, 64, 1000, 124451, 2**20, 3 * 10**6, 2**24 - 1, 2**24, 2**31 - 1]
+    cints += [int(v) for v in rng.integers(1, 2**24, size=40)]
+    took = 0
+    for b in (4, 5, 6):
+        n = 2**b - 1
+        for ci in cints:
+            ok = L.qw_index_magic(ci, b, ctypes.byref(m), ctypes.byref(sh))
+            fits = ci < 2**24 and ci * (2 * n + 1) < 2**31
+            assert ok == (1 if fits else 0), (ci, b)
+            if not ok:
+                continue
+            took += 1
+            mag, s = m.value, sh.value
+            ds = {0, ci, ci - 1}
+            for k in range(1, n + 1):  # both sides of the half-step boundaries
+                t = -(-ci * (2 * k - 1) // (2 * n))
+                ds |= {t - 1, t, t + 1}
+            ds |= {int(v) for v in rng.integers(0, ci + 1, size=200)}
+            for d in ds:
+                if not 0 <= d <= ci:
+                    continue
+                want = (2 * n * d + ci) // (2 * ci)
+                got = (((2 * n * d + ci) * mag) >> 32) >> s
+                assert got == want, (ci, b, d)
+    assert took >= 100
+    assert L.qw_index_magic(100, 3, ctypes.byref(m), ctypes.byref(sh)) == 0
+    assert L.qw_index_magic(0, 5, ctypes.byref(m), ctypes.byref(sh)) == 0
+    assert L.qw_index_magic(100, 5, NULL, ctypes.byref(sh)) == 0
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -79,14 +79,15 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 // ---------------------------------------------------------------- W4A8 --------
 
 // Position p of the 16 codes of one B operand holds k = 16 g + kPerm[p] of its step:
-// the order in which the INT4 unpack presents the weights.
-__device__ __forceinline__ uint4 pack_perm16(const int (&q)[16])
+// the order in which the INT4 unpack presents the weights.  The code of k = 4 e + i is
+// byte 2 of c[e][i] (the four-value quantizer's form).
+__device__ __forceinline__ uint4 pack_perm16(const uint32_t (&c)[4][4])
 {
     uint4 o;
-    o.x = pack_i8x4(q[0], q[2], q[4], q[6]);
-    o.y = pack_i8x4(q[1], q[3], q[5], q[7]);
-    o.z = pack_i8x4(q[8], q[10], q[12], q[14]);
-    o.w = pack_i8x4(q[9], q[11], q[13], q[15]);
+    o.x = __builtin_amdgcn_perm(c[0][2], c[0][0], 0x0C0C0602u) | __builtin_amdgcn_perm(c[1][2], c[1][0], 0x06020C0Cu);
+    o.y = __builtin_amdgcn_perm(c[0][3], c[0][1], 0x0C0C0602u) | __builtin_amdgcn_perm(c[1][3], c[1][1], 0x06020C0Cu);
+    o.z = __builtin_amdgcn_perm(c[2][2], c[2][0], 0x0C0C0602u) | __builtin_amdgcn_perm(c[3][2], c[3][0], 0x06020C0Cu);
+    o.w = __builtin_amdgcn_perm(c[2][3], c[2][1], 0x0C0C0602u) | __builtin_amdgcn_perm(c[3][3], c[3][1], 0x06020C0Cu);
     return o;
 }
 
@@ -144,18 +145,14 @@ __global__ __launch_bounds__(NT) void k_quant_act_mfma(const float* __restrict__
         for (int t = 0; t < NS; ++t) {
             const int sl = (int)threadIdx.x + kBlock * t;
             if (sl < slots) {
-                int q[16];
+                uint32_t c[4][4];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const float xs[4] = {v[t][e].x, v[t][e].y, v[t][e].z, v[t][e].w};
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        q[4 * e + i] = fast ? quant_code_fast(xs[i], a, r, 127.f)
-                                            : quant_code(xs[i], a, 127.f);
-                }
+                for (int e = 0; e < 4; ++e)
+                    if (quant4_e(v[t][e], r, c[e]) || !fast)
+                        quant4_e_div(v[t][e], a, c[e]);
                 const int st = sl >> 2, g = sl & 3;
                 *reinterpret_cast<uint4*>(base + (size_t)st * 1024u + (size_t)g * 256u) =
-                    pack_perm16(q);
+                    pack_perm16(c);
             }
         }
     }

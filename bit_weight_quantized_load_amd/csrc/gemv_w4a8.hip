@@ -869,7 +869,9 @@ namespace {
 // float4 each; 1024 beyond), which loads the whole row into registers at once (NV float4
 // per thread, so a single memory round trip), takes max|x| across the workgroup and
 // writes the row-major codes from the same registers.  The scale and the codes are
-// computed exactly as by the standalone quantization kernel.  With UNPACK, each 16-byte
+// computed exactly as by the standalone quantization kernel (four values per step, by
+// the reciprocal, with the division taken for any four of which one lies near a
+// rounding boundary).  With UNPACK, each 16-byte
 // group of codes (16 k) is written in the order the INT4 unpack presents the weights
 // (k 0, 2, 4, 6, 1, 3, 5, 7, 8, 10, 12, 14, 9, 11, 13, 15): the lane holding k 4j .. 4j + 3
 // of a group and its neighbour exchange their words, the even lane keeps the even k of
@@ -908,11 +910,11 @@ __global__ __launch_bounds__(T) void k_quant_act_rows(const float* __restrict__ 
 #pragma unroll
     for (int t = 0; t < NV; ++t) {
         const int i = tid + T * t;
-        const float4 x = v[t];
-        uint32_t wd = fast ? pack_i8x4(quant_code_fast(x.x, a, r, 127.f), quant_code_fast(x.y, a, r, 127.f),
-                                       quant_code_fast(x.z, a, r, 127.f), quant_code_fast(x.w, a, r, 127.f))
-                           : pack_i8x4(quant_code(x.x, a, 127.f), quant_code(x.y, a, 127.f),
-                                       quant_code(x.z, a, 127.f), quant_code(x.w, a, 127.f));
+        // the four codes arrive in byte 2 of e[0 .. 3]; the word takes them in k order
+        uint32_t e[4];
+        if (quant4_e(v[t], r, e) || !fast)
+            quant4_e_div(v[t], a, e);
+        uint32_t wd = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0602u) | __builtin_amdgcn_perm(e[3], e[2], 0x06020C0Cu);
         if constexpr (UNPACK) {
             // the neighbour's word (lanes 2 u and 2 u + 1 swap: quad permutation 1, 0, 3, 2);
             // K is a multiple of 32, so both lanes of a pair are inside the row or both past it

@@ -162,60 +162,18 @@ __device__ __forceinline__ void issue_barrier()
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// The same code computed with one multiply by r = 1/scale instead of a division.
-// With r = fl(1/scale) and y = fl(x * r), |y - fl(x / scale)| <= 3 * 2^-24 * |x / scale|,
-// which is below 2^-15 for |x / scale| <= 128; so rint(y) equals rint(fl(x / scale))
-// unless y lies within 2^-15 of a half-integer, and then the division decides.
-// Callers pass r only when it is finite (scale >= 2^-126); otherwise they use
-// quant_code.  Verified bit for bit against quant_code over every fp32 x in
-// [-127 scale, 127 scale] for a spread of scales.
-__device__ __forceinline__ int quant_code_fast(float x, float scale, float r, float qmax)
-{
-    const float y = x * r;
-    float q = rintf(y);
-    if (0.5f - fabsf(y - q) <= 0x1p-15f)
-        q = rintf(x / scale);
-    q = fminf(fmaxf(q, -qmax), qmax);
-    return (int)q;
-}
-
-// Four INT8 codes at once with the same results as quant_code_fast/quant_code: the
-// multiply-by-reciprocal codes are kept unless one of the four values lies within
-// 2^-15 of a rounding boundary (or the reciprocal is not finite), in which case all
-// four are taken by division.  One branch per four values.
-__device__ __forceinline__ void quant4_i8(float4 x, float scale, float r, bool fast, int (&q)[4])
-{
-    const float xs[4] = {x.x, x.y, x.z, x.w};
-    float qf[4];
-    bool near = !fast;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float y = xs[i] * r;
-        qf[i] = rintf(y);
-        near |= 0.5f - fabsf(y - qf[i]) <= 0x1p-15f;
-    }
-    if (near) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            qf[i] = scale == 0.0f ? 0.0f : rintf(xs[i] / scale);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-        q[i] = (int)fminf(fmaxf(qf[i], -127.0f), 127.0f);
-}
-
-// Four INT8 activation codes in about half the instructions of quant4_i8, with the same
-// codes.  For a reciprocal r = fl(1/s) of s = fl(m/127), m = max |x|, every |x r| is
-// below 127.0001, so u = fl(x r + 384) (one fused rounding) lies in (256, 512), where
-// fp32 values are spaced 2^-15 apart.  e = (bits(u) << 1) + 0x8002 - (128 << 16) then
+// Four INT8 activation codes, equal to quant_code's, by one fused multiply-add per
+// value instead of a division.  For a reciprocal r = fl(1/s) of s = fl(m/127),
+// m = max |x|, every |x r| is below 127.0001, so u = fl(x r + 384) (one fused rounding)
+// lies in (256, 512), where fp32 values are spaced 2^-15 apart.  e = (bits(u) << 1) + 0x8002 - (128 << 16) then
 // holds in bits 16..23 the integer part of u minus 384, plus one when the fraction is at
 // least a half (the +0x8000 carry): rint(x r) modulo 256, the code's byte.  Bits 0..15
 // hold the fraction in units of 2^-16, offset so that the three spacings around a half
 // map to 0, 2 and 4.  When none of the four values lands there, each exact x r is more
 // than 3 * 2^-16 from a half-integer; x / s is within 2^-17 of x r and fl(x / s) within
 // 2^-18 of x / s, so rint(fl(x / s)), the definition, is the code found.  Returns true
-// when some value needs the division (quant4_e_div), as quant4_i8 does; callers pass r
-// only when it is finite.
+// when some value needs the division (quant4_e_div, then taken for all four); callers
+// pass r only when it is finite (s >= 2^-126), else take the division.
 __device__ __forceinline__ bool quant4_e(const float4 x, float r, uint32_t (&e)[4])
 {
     const float xs[4] = {x.x, x.y, x.z, x.w};

@@ -110,16 +110,18 @@ __device__ __forceinline__ void quantize_rows(const W4A8Args& p, float4 (&xv)[XV
             for (int i = 0; i < XV; ++i) {
                 const int f = blk * XV * kThreads + i * kThreads + tid;  // k = 4f .. 4f+3
                 if (f < K4) {
-                    int q[4];
-                    quant4_i8(xv[i], a, r, fast, q);
+                    uint32_t e[4];  // the codes in byte 2
+                    if (quant4_e(xv[i], r, e) || !fast)
+                        quant4_e_div(xv[i], a, e);
                     // chunk f/8, 8-group (f/2)%4, half f%2: even codes -> word 2d, odd -> 2d+1
                     const int c = f >> 3, d = (f >> 1) & 3, h = f & 1;
                     const int wi = (c * 8 + 2 * d) * 2 + h;  // halfword index in the even word
-                    act16[wi] = (uint16_t)((q[0] & 0xff) | ((q[2] & 0xff) << 8));
-                    act16[wi + 2] = (uint16_t)((q[1] & 0xff) | ((q[3] & 0xff) << 8));
+                    act16[wi] = (uint16_t)__builtin_amdgcn_perm(e[2], e[0], 0x0C0C0602u);
+                    act16[wi + 2] = (uint16_t)__builtin_amdgcn_perm(e[3], e[1], 0x0C0C0602u);
                     if (kDebug && p.dbg_xq != nullptr && blockIdx.x == 0 && mm < mt)
                         *reinterpret_cast<uint32_t*>(p.dbg_xq + (size_t)(m0 + mm) * p.K + 4 * f) =
-                            pack_i8x4(q[0], q[1], q[2], q[3]);
+                            __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0602u) |
+                            __builtin_amdgcn_perm(e[3], e[2], 0x06020C0Cu);
                 }
             }
         }

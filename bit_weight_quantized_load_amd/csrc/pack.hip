@@ -186,13 +186,13 @@ __global__ __launch_bounds__(kBlock) void k_quant_act(const float* __restrict__ 
             a_scale[m] = a;
         uint32_t* out = reinterpret_cast<uint32_t*>(Xq + (size_t)m * K);
         for (int i = threadIdx.x; i < K4; i += kBlock) {
-            float4 v = row[i];
-            if (fast)
-                out[i] = pack_i8x4(quant_code_fast(v.x, a, r, 127.f), quant_code_fast(v.y, a, r, 127.f),
-                                   quant_code_fast(v.z, a, r, 127.f), quant_code_fast(v.w, a, r, 127.f));
-            else
-                out[i] = pack_i8x4(quant_code(v.x, a, 127.f), quant_code(v.y, a, 127.f),
-                                   quant_code(v.z, a, 127.f), quant_code(v.w, a, 127.f));
+            // four codes per step in byte 2 of e[0 .. 3], by the reciprocal unless one of
+            // the four lies near a rounding boundary
+            const float4 v = row[i];
+            uint32_t e[4];
+            if (quant4_e(v, r, e) || !fast)
+                quant4_e_div(v, a, e);
+            out[i] = __builtin_amdgcn_perm(e[1], e[0], 0x0C0C0602u) | __builtin_amdgcn_perm(e[3], e[2], 0x06020C0Cu);
         }
     }
 }

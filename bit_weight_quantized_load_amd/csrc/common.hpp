@@ -165,8 +165,8 @@ __device__ __forceinline__ void issue_barrier()
 // Four INT8 activation codes, equal to quant_code's, by one fused multiply-add per
 // value instead of a division.  For a reciprocal r = fl(1/s) of s = fl(m/127),
 // m = max |x|, every |x r| is below 127.0001, so u = fl(x r + 384) (one fused rounding)
-// lies in (256, 512), where fp32 values are spaced 2^-15 apart.  e = (bits(u) << 1) + 0x8002 - (128 << 16) then
-// holds in bits 16..23 the integer part of u minus 384, plus one when the fraction is at
+// lies in (256, 512), where fp32 values are spaced 2^-15 apart.
+// e = (bits(u) << 1) + 0x8002 - (128 << 16) then holds in bits 16..23 the integer part of u minus 384, plus one when the fraction is at
 // least a half (the +0x8000 carry): rint(x r) modulo 256, the code's byte.  Bits 0..15
 // hold the fraction in units of 2^-16, offset so that the three spacings around a half
 // map to 0, 2 and 4.  When none of the four values lands there, each exact x r is more
